@@ -1,0 +1,437 @@
+"""Sort-based reference for filtered categorical sampling (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): nothing in the GPU
+library imports, links or runs this module.
+
+Pages cited (titles as they appear; sections by their headings):
+
+* [Blog]  FlashInfer blog, "Sorting-Free GPU Kernels for LLM Sampling"
+          (Chinese translation "面向 LLM 采样的免排序 GPU 内核").
+* [F4]    gpu-kernel-drills note "F4 讲解：不排序的 top-k / top-p".
+* [Expl]  charlestar explainer on FlashInfer Sorting-Free Sampling.
+
+Arithmetic
+----------
+Every float32 value x >= 0 is an integer multiple of 2**-149, so
+``X = x * 2**149`` is an exact Python integer and every mass below is an
+exact integer sum.  Parameters p and min_p are float32 numbers, hence exact
+rationals; comparisons against ``p * Z`` are done in integers.  There is no
+rounding anywhere in the decisions, so the kept sets are the mathematical
+ones.  Only reported probabilities and renormalised values are rounded (to
+float64 / float32) at the very end.
+
+Readings of the pages (each also listed in the design doc):
+
+* R1 ties: every filter is value-based and keeps all ties, so the kept set is
+  always an upper set {i : x_i >= tau}.  [F4 §⑥] states that a threshold keeps
+  every tied value; [Expl] "Tie 需要明确定义" asks only that the reference and
+  the predicate agree.
+* R2 top-p reference mass: the prefix is compared with p * Z_C, Z_C being the
+  exact mass of the set entering the top-p stage (the whole row, or the top-k
+  set under top-k-then-top-p).  [Expl] "Top-k 与 top-p 的组合顺序会改变分布"
+  applies top-p inside the top-k set; for rows that sum to one this equals the
+  raw rule of [F4 §②].
+* R3 the top-p prefix is the smallest r >= 1 with prefix_r >= p * Z_C
+  ([Expl] "Top-p"), so at least the maximum (with its ties) is kept.
+* R4 parameter domains: k <= 0 makes the output invalid, k >= V keeps every
+  token; p and min_p are clamped to [0, 1]; NaN p or min_p is invalid.
+* R5 degenerate rows ([Expl] "退化分布必须可报告"): any value with the sign bit
+  set (negative numbers and -0.0), NaN or +-inf, or a zero total, make the row
+  invalid; sampling reports token -1 with valid = 0, renorm reports a NaN row.
+* R6 min-p threshold is min_p * max as an exact product ([Blog] "Min-P",
+  [Expl] "Min-p"); kept set {x >= min_p * max}.
+"""
+
+from bisect import bisect_left, bisect_right
+from fractions import Fraction
+from itertools import accumulate
+
+import numpy as np
+
+SCALE_EXP = 149          # x * 2**149 is an integer for every float32 x >= 0
+
+OPS = ("none", "top_k", "top_p", "min_p", "top_k_top_p")
+
+
+# ----------------------------------------------------------------------------
+# exact arithmetic helpers
+# ----------------------------------------------------------------------------
+
+def exact_units(values):
+    """Exact integers x * 2**149 for a float32 array of finite x >= 0."""
+    scaled = np.ldexp(np.asarray(values, dtype=np.float32).astype(np.float64),
+                      SCALE_EXP)
+    return [int(t) for t in scaled]
+
+
+def fraction_of(value):
+    """Exact rational value of a float32 (or float64) number."""
+    return Fraction(*float(value).as_integer_ratio())
+
+
+def row_is_valid(row):
+    """R5: no sign bit set, no NaN/inf, and a positive total."""
+    row = np.asarray(row, dtype=np.float32)
+    bits = row.view(np.uint32)
+    if np.any(bits >= np.uint32(0x7F800000)):   # sign bit, inf or NaN
+        return False
+    return bool(np.any(bits != 0))
+
+
+# ----------------------------------------------------------------------------
+# thresholds (the kept set is {x >= tau}, R1)
+# ----------------------------------------------------------------------------
+
+def _sorted_desc(row):
+    return np.sort(np.asarray(row, dtype=np.float32))[::-1]
+
+
+def tau_top_k(row, k):
+    """k-th largest value [Expl "Top-k"]; k >= V keeps every token."""
+    s = _sorted_desc(row)
+    kk = min(int(k), s.size)
+    return float(s[kk - 1])
+
+
+def _count_at_least(sorted_desc, tau):
+    """Number of entries >= tau in a descending array."""
+    asc = sorted_desc[::-1]
+    return int(asc.size - np.searchsorted(asc, np.float32(tau), side="left"))
+
+
+def tau_top_p(sorted_desc, n_c, p):
+    """Top-p threshold on the first n_c entries of a descending row.
+
+    m = min{r >= 1 : sum_{j<=r} v_(j) >= p * Z_C} and tau = v_(m)
+    ([Expl] "Top-p"; R2, R3).  ``p`` must already be clamped to [0, 1].
+    """
+    units = exact_units(sorted_desc[:n_c])
+    prefix = list(accumulate(units))
+    z_c = prefix[-1]
+    num, den = fraction_of(p).as_integer_ratio()
+    # prefix_r * den >= num * z_c  <=>  prefix_r >= ceil(num * z_c / den)
+    need = -((-num * z_c) // den)
+    r = bisect_left(prefix, need)
+    r = max(0, min(r, n_c - 1))
+    return float(sorted_desc[r])
+
+
+def clamp01(v):
+    v = float(np.float32(v))
+    return min(max(v, 0.0), 1.0)
+
+
+def threshold(row, op, k=None, p=None, min_p=None):
+    """(valid, tau) for one row and one filter; kept set = {x >= tau}.
+
+    ``tau`` is returned as a float64 holding the exact threshold (for min-p,
+    the exact product of two float32 numbers, which float64 represents
+    exactly).
+    """
+    row = np.asarray(row, dtype=np.float32)
+    if not row_is_valid(row):
+        return False, None
+    if op == "none":
+        return True, 0.0
+    if op in ("top_k", "top_k_top_p") and int(k) <= 0:
+        return False, None
+    if op in ("top_p", "top_k_top_p") and np.isnan(np.float32(p)):
+        return False, None
+    if op == "min_p" and np.isnan(np.float32(min_p)):
+        return False, None
+    s = _sorted_desc(row)
+    if op == "top_k":
+        return True, tau_top_k(row, k)
+    if op == "top_p":
+        return True, tau_top_p(s, s.size, clamp01(p))
+    if op == "top_k_top_p":
+        tk = tau_top_k(row, k)
+        n_c = _count_at_least(s, tk)
+        return True, tau_top_p(s, n_c, clamp01(p))
+    if op == "min_p":
+        # exact: a product of two float32 numbers fits a float64 exactly
+        return True, float(np.float64(clamp01(min_p)) * np.float64(s[0]))
+    raise ValueError(op)
+
+
+def kept_mask(row, tau):
+    """{x >= tau} (R1)."""
+    return np.asarray(row, dtype=np.float32).astype(np.float64) >= float(tau)
+
+
+def support_mask(row, tau):
+    """Support of the filtered distribution: kept and strictly positive."""
+    r = np.asarray(row, dtype=np.float32)
+    return kept_mask(r, tau) & (r > 0)
+
+
+def target_distribution(row, tau):
+    """p~_i = p_i / sum_{j in S} p_j on S, else 0 ([Expl] "采样流水线究竟在计算什么")."""
+    r = np.asarray(row, dtype=np.float32)
+    sup = support_mask(r, tau)
+    z = sum(exact_units(r[sup]))
+    out = np.zeros(r.size, dtype=np.float64)
+    # x_i * 2**149 / Z, both exact before the one final rounding of each
+    out[sup] = np.ldexp(r[sup].astype(np.float64), SCALE_EXP) / float(z)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# renormalisation and logit masking
+# ----------------------------------------------------------------------------
+
+def renorm_row(row, tau):
+    """out_i = x_i / Z_S on the kept set, 0 elsewhere ([F4 §④] last two passes).
+
+    Z_S is exact; the quotient is formed in float64 from the correctly
+    rounded Z_S and rounded once more to float32.
+    """
+    r = np.asarray(row, dtype=np.float32)
+    keep = kept_mask(r, tau)
+    z = sum(exact_units(r[keep]))
+    zf = np.ldexp(float(z), -SCALE_EXP)
+    out = np.zeros(r.size, dtype=np.float32)
+    out[keep] = (r[keep].astype(np.float64) / zf).astype(np.float32)
+    return out
+
+
+def top_k_renorm(row, k):
+    valid, tau = threshold(row, "top_k", k=k)
+    if not valid:
+        return False, np.full(np.asarray(row).size, np.nan, dtype=np.float32)
+    return True, renorm_row(row, tau)
+
+
+def top_p_renorm(row, p):
+    valid, tau = threshold(row, "top_p", p=p)
+    if not valid:
+        return False, np.full(np.asarray(row).size, np.nan, dtype=np.float32)
+    return True, renorm_row(row, tau)
+
+
+def mask_logits_row(row, k):
+    """Keep the k largest logits (ties kept, R1), set the rest to -inf.
+
+    Logits may be negative, so the order is the numeric order of the values
+    ([F4 §⑧]: raw bit patterns of negative floats order backwards).  A NaN
+    logit or k <= 0 makes the row invalid (NaN-filled output).
+    """
+    r = np.asarray(row, dtype=np.float32)
+    if np.any(np.isnan(r)) or int(k) <= 0:
+        return False, np.full(r.size, np.nan, dtype=np.float32)
+    if int(k) >= r.size:
+        return True, r.copy()
+    tau = np.sort(r)[::-1][int(k) - 1]
+    return True, np.where(r >= tau, r, np.float32(-np.inf)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# inverse-transform draw
+# ----------------------------------------------------------------------------
+
+def inverse_transform(row, mask, a53):
+    """Index j with F_{j-1} <= u * Z < F_j over the masked entries, in index order.
+
+    [Blog] "逆变换采样" and [Expl] "不带过滤时：inverse transform sampling":
+    u ~ U[0, 1), F the prefix sums, return the first j with F_j > u.  Here
+    u = a53 / 2**53 and the prefix is scaled by the total Z of the masked
+    entries, so unnormalised rows are handled exactly.  Returns -1 if the
+    masked mass is zero.
+    """
+    r = np.asarray(row, dtype=np.float32)
+    idx = np.nonzero(mask)[0]
+    units = exact_units(r[idx])
+    prefix = list(accumulate(units))
+    if not prefix or prefix[-1] == 0:
+        return -1
+    thr = (int(a53) * prefix[-1]) >> 53          # floor(u * Z)
+    j = bisect_right(prefix, thr)                # first prefix > u * Z
+    return int(idx[j])
+
+
+def sample_by_cdf(row, op, a53, k=None, p=None, min_p=None):
+    """Sort-based filter then one CDF draw: the oracle's own sampler."""
+    valid, tau = threshold(row, op, k=k, p=p, min_p=min_p)
+    if not valid:
+        return -1
+    return inverse_transform(row, support_mask(row, tau), a53)
+
+
+# ----------------------------------------------------------------------------
+# the rejection predicate f and a plain model of dual-pivot rejection sampling
+# ----------------------------------------------------------------------------
+
+class Predicate:
+    """f(t) = 1 iff the threshold t already satisfies the filter.
+
+    [Blog] "双枢轴拒绝采样" defines f on probability values; "拒绝采样" says the
+    top-p check compares the mass above the pivot with top_p and the top-k
+    check counts the tokens above the pivot.  Written with strict
+    comparisons (x > t), as the draw range (low, inf) of the same section:
+
+      top_k:        #{x > t} < k
+      top_p:        sum_{x > t} x < p * Z_C   or  #{x > t} = 0
+      min_p:        t >= min_p * max
+      top_k_top_p:  top_k(t)  and  (sum_{x > t} x < p * Z_k  or  #{x > t} = 0)
+      none:         always 1
+
+    Z_C is the whole row's exact mass, Z_k that of {x >= tau_k} (R2).  The
+    "#{x > t} = 0" clause makes f(max) = 1 also when p = 0.
+    """
+
+    def __init__(self, row, op, k=None, p=None, min_p=None):
+        self.row = np.asarray(row, dtype=np.float32)
+        self.op = op
+        self.units = exact_units(self.row)
+        self.k = None if k is None else int(k)
+        if op in ("top_p", "top_k_top_p"):
+            self.p_num, self.p_den = fraction_of(clamp01(p)).as_integer_ratio()
+        if op == "top_p":
+            self.z_c = sum(self.units)
+        if op == "top_k_top_p":
+            tk = tau_top_k(self.row, self.k)
+            self.z_c = sum(u for u, x in zip(self.units, self.row) if x >= tk)
+        if op == "min_p":
+            self.minp_tau = float(np.float64(clamp01(min_p)) *
+                                  np.float64(self.row.max()))
+
+    def mass_count_above(self, t):
+        above = self.row > np.float32(t)
+        return sum(u for u, a in zip(self.units, above) if a), int(above.sum())
+
+    def __call__(self, t):
+        if self.op == "none":
+            return True
+        if self.op == "min_p":
+            return float(np.float32(t)) >= self.minp_tau
+        mass, count = self.mass_count_above(t)
+        ok_k = True if self.op == "top_p" else count < self.k
+        if self.op == "top_k":
+            return ok_k
+        ok_p = (mass * self.p_den < self.p_num * self.z_c) or count == 0
+        return ok_k and ok_p
+
+
+def pivot2_of(pivot1, high):
+    """(pivot1 + high) / 2 rounded once to float32 (reading of [Blog] "双枢轴拒绝采样").
+
+    The sum of two float32 numbers and its half are exact in float64, so
+    this is the correctly rounded midpoint with no overflow.
+    """
+    return np.float32((np.float64(pivot1) + np.float64(high)) / 2.0)
+
+
+def dual_pivot_sample(row, op, stream, k=None, p=None, min_p=None,
+                      max_rounds=100000, trace=None):
+    """One draw by dual-pivot rejection sampling, following [Blog] "双枢轴拒绝采样".
+
+      low <- 0, high <- max
+      repeat: draw j from the tokens with p_j > low by inverse transform;
+              pivot1 <- p_j; pivot2 <- (pivot1 + high) / 2
+              f(pivot1) = 1                -> return j
+              f(pivot1) = 0, f(pivot2) = 1 -> low, high <- pivot1, pivot2
+              f(pivot1) = 0, f(pivot2) = 0 -> low <- pivot2
+
+    ``stream.next()`` supplies one 53-bit uniform per draw.  Returns
+    (token, rounds); (-1, 0) for an invalid row or parameter.  If ``trace``
+    is a list, the (low, high) interval is appended to it at the start and
+    after every rejected round.
+    """
+    row = np.asarray(row, dtype=np.float32)
+    valid, _ = threshold(row, op, k=k, p=p, min_p=min_p)
+    if not valid:
+        return -1, 0
+    f = Predicate(row, op, k=k, p=p, min_p=min_p)
+    low, high = np.float32(0.0), np.float32(row.max())
+    if trace is not None:
+        trace.append((low, high))
+    for rounds in range(1, max_rounds + 1):
+        j = inverse_transform(row, row > low, stream.next())
+        pivot1 = row[j]
+        if f(pivot1):
+            return j, rounds
+        pivot2 = pivot2_of(pivot1, high)
+        if f(pivot2):
+            low, high = pivot1, pivot2
+        else:
+            low = pivot2
+        if trace is not None:
+            trace.append((low, high))
+    raise RuntimeError("dual-pivot model did not terminate")
+
+
+def dual_pivot_law(row, op, k=None, p=None, min_p=None):
+    """Exact output law and expected round count of ``dual_pivot_sample``.
+
+    Enumerates every draw from every reachable (low, high) state with exact
+    rationals (draw probability p_i / S(low), S(low) = mass above low, as in
+    the recurrence (★) of [Blog] "拒绝采样器正确性的理论证明").  For tiny
+    vocabularies only.  Returns ({token: Fraction}, Fraction expected_rounds).
+    """
+    row = np.asarray(row, dtype=np.float32)
+    f = Predicate(row, op, k=k, p=p, min_p=min_p)
+    units = f.units
+    memo = {}
+
+    def solve(low, high):
+        key = (float(low), float(high))
+        if key in memo:
+            return memo[key]
+        cand = [i for i in range(row.size) if row[i] > low]
+        s = sum(units[i] for i in cand)
+        law, rounds = {}, Fraction(1)
+        for i in cand:
+            w = Fraction(units[i], s)
+            if w == 0:
+                continue
+            pivot1 = row[i]
+            if f(pivot1):
+                law[i] = law.get(i, Fraction(0)) + w
+                continue
+            pivot2 = pivot2_of(pivot1, high)
+            sub_law, sub_rounds = (solve(pivot1, pivot2) if f(pivot2)
+                                   else solve(pivot2, high))
+            for j, q in sub_law.items():
+                law[j] = law.get(j, Fraction(0)) + w * q
+            rounds += w * sub_rounds
+        memo[key] = (law, rounds)
+        return law, rounds
+
+    return solve(np.float32(0.0), np.float32(row.max()))
+
+
+# ----------------------------------------------------------------------------
+# batch helpers mirroring the library's calling convention
+# ----------------------------------------------------------------------------
+
+def per_output(arr, scalar, n):
+    """Per-output parameter list: the array if given, else the scalar repeated."""
+    if arr is None:
+        return [scalar] * n
+    return list(np.asarray(arr).reshape(-1)[:n])
+
+
+def batch_thresholds(probs, op, indices=None, k=None, p=None, min_p=None,
+                     num_outputs=None):
+    """(valid, tau) per output; ``indices`` maps outputs onto rows.
+
+    ``k``, ``p``, ``min_p`` are scalars or per-output arrays.  An index
+    outside [0, rows) makes that output invalid.
+    """
+    probs = np.asarray(probs, dtype=np.float32)
+    rows = probs.shape[0]
+    n = rows if num_outputs is None else int(num_outputs)
+    rows_of = list(range(n)) if indices is None else [int(v) for v in indices]
+
+    def listify(v):
+        return list(np.asarray(v).reshape(-1)) if np.ndim(v) else [v] * n
+
+    ks, ps, ms = listify(k), listify(p), listify(min_p)
+    out = []
+    for i in range(n):
+        r = rows_of[i]
+        if r < 0 or r >= rows:
+            out.append((False, None))
+            continue
+        out.append(threshold(probs[r], op, k=ks[i], p=ps[i], min_p=ms[i]))
+    return out

@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle to things other than itself (runs without a GPU).
+
+Each test ties one oracle function to the pages' worked examples, to an
+independent definition (brute force on tiny vocabularies, the bisection
+definition of the F4 note, numpy's own Philox and sort), to a closed form or
+to an invariant stated on the pages.  Pages: FlashInfer blog "Sorting-Free
+GPU Kernels for LLM Sampling"; gpu-kernel-drills note "F4 讲解：不排序的
+top-k / top-p"; charlestar explainer on FlashInfer Sorting-Free Sampling.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import philox as ph
+from oracle import reference as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def f32(values):
+    return np.asarray(values, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Philox: numpy ships an independent Philox4x64-10 implementation.  numpy
+# increments its 256-bit counter before each block, so its first block for
+# counter c is the block for c + 1.
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key,ctr", [
+    ((0, 0), (0, 0, 0, 0)),
+    ((123456789, 987654321), (5, 0, 0, 0)),
+    ((2**64 - 1, 2**63 + 7), (11, 22, 33, 44)),
+    ((42, 0), (2**64 - 1, 0, 0, 0)),            # carry into word 1
+    ((7, 9), (2**64 - 1, 2**64 - 1, 3, 0)),     # carry into word 2
+])
+def test_philox_matches_numpy(key, ctr):
+    bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
+                          counter=np.array(ctr, dtype=np.uint64))
+    got = [int(v) for v in bg.random_raw(8)]
+    value = sum(int(c) << (64 * i) for i, c in enumerate(ctr)) + 1
+    nxt = [(value >> (64 * i)) & ph.MASK64 for i in range(4)]
+    assert got[:4] == list(ph.philox4x64_10(nxt, key))
+    value += 1
+    nxt = [(value >> (64 * i)) & ph.MASK64 for i in range(4)]
+    assert got[4:] == list(ph.philox4x64_10(nxt, key))
+
+
+def test_draws_are_uniform_and_streams_differ():
+    u = np.array([ph.draw_uniform(99, 3, 0, r) for r in range(20000)])
+    assert stats.kstest(u, "uniform").pvalue > 1e-3
+    assert 0.0 <= u.min() and u.max() < 1.0
+    # offset advance and output id give different streams
+    a = [ph.draw_bits53(99, 3, 0, r) for r in range(8)]
+    b = [ph.draw_bits53(99, 4, 0, r) for r in range(8)]
+    c = [ph.draw_bits53(99, 3, 1, r) for r in range(8)]
+    assert a != b and a != c and len(set(a)) == 8
+
+
+# ----------------------------------------------------------------------------
+# worked examples printed on the pages
+# ----------------------------------------------------------------------------
+
+def test_f4_hand_example_top_p():
+    g = golden("f4_hand_example.json")
+    row = f32(g["probs"])
+    valid, tau = ref.threshold(row, "top_p", p=g["top_p"])
+    assert valid and np.float32(tau) == np.float32(g["tau_top_p"])
+    assert list(np.nonzero(ref.kept_mask(row, tau))[0]) == g["kept_top_p"]
+    valid, tau = ref.threshold(row, "top_k", k=g["top_k"])
+    assert valid and np.float32(tau) == np.float32(g["tau_top_k"])
+    assert list(np.nonzero(ref.kept_mask(row, tau))[0]) == g["kept_top_k"]
+
+
+def test_expl_top2_example_law():
+    g = golden("expl_top2_example.json")
+    row = f32(g["probs"])
+    valid, tau = ref.threshold(row, "top_k", k=g["top_k"])
+    assert valid
+    assert list(np.nonzero(ref.support_mask(row, tau))[0]) == g["support"]
+    target = ref.target_distribution(row, tau)
+    expect = np.array(g["law_num"]) / g["law_den"]
+    # inputs are the float32 roundings of the printed decimals
+    assert np.allclose(target[g["support"]], expect, rtol=2e-7, atol=0)
+    law, _ = ref.dual_pivot_law(row, "top_k", k=g["top_k"])
+    assert set(law) == set(g["support"])
+    for j in g["support"]:
+        assert abs(float(law[j]) - target[j]) < 1e-15
+
+
+def test_expl_order_example():
+    g = golden("expl_order_example.json")
+    row = f32(g["probs"])
+    for p, kept in ((g["top_p"], g["kept"]),
+                    (g["derived_top_p"], g["derived_kept"])):
+        valid, tau = ref.threshold(row, "top_k_top_p", k=g["top_k"], p=p)
+        assert valid
+        assert list(np.nonzero(ref.kept_mask(row, tau))[0]) == kept
+    # the raw-mass reading (raw prefix of the top-3 compared with p itself,
+    # i.e. p / Z_k against the top-3 mass) keeps one more token here
+    top3 = row[:3]
+    valid, tau = ref.threshold(top3, "top_p",
+                               p=np.float32(g["derived_top_p"] / float(top3.sum())))
+    assert list(np.nonzero(ref.kept_mask(top3, tau))[0]) == g["raw_mass_reading_kept"]
+
+
+# ----------------------------------------------------------------------------
+# brute force on tiny vocabularies: the F4 note's bisection definition
+# ("largest t with count(x >= t) >= k" / "largest t with mass(x >= t) >= p")
+# against the explainer's sort-prefix definition used by the oracle
+# ----------------------------------------------------------------------------
+
+def _tiny_rows(seed, n_rows=300):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(n_rows):
+        v = int(rng.integers(1, 9))
+        if i % 3 == 0:      # tie-heavy: few distinct dyadic values, some zeros
+            row = rng.integers(0, 5, size=v).astype(np.float32) / 8
+            if not row.any():
+                row[0] = 0.25
+        else:
+            row = rng.dirichlet(np.ones(v)).astype(np.float32)
+        rows.append(f32(row))
+    return rows
+
+
+def _brute_top_k(row, k):
+    cands = sorted(set(float(x) for x in row))
+    ok = [t for t in cands if sum(1 for x in row if x >= t) >= k]
+    return max(ok) if ok else min(cands)
+
+
+def _brute_top_p(row, p, within=None):
+    vals = [Fraction(float(x)) for x in row]
+    members = [i for i in range(len(row)) if within is None or within[i]]
+    z = sum(vals[i] for i in members)
+    pf = Fraction(min(max(float(np.float32(p)), 0.0), 1.0))
+    cands = sorted(set(vals[i] for i in members))
+    ok = [t for t in cands if sum(vals[i] for i in members if vals[i] >= t) >= pf * z]
+    return float(max(ok))
+
+
+def test_tiny_brute_force_thresholds():
+    rng = np.random.default_rng(7)
+    for row in _tiny_rows(1):
+        v = row.size
+        k = int(rng.integers(1, v + 2))
+        p = float(np.float32(rng.choice([0.0, 0.3, 0.5, 0.77, 0.9, 1.0,
+                                         rng.uniform()])))
+        mp = float(np.float32(rng.uniform(0, 1)))
+        _, tk = ref.threshold(row, "top_k", k=k)
+        assert tk == _brute_top_k(row, k)
+        _, tp = ref.threshold(row, "top_p", p=p)
+        assert tp == _brute_top_p(row, p)
+        _, tkp = ref.threshold(row, "top_k_top_p", k=k, p=p)
+        assert tkp == _brute_top_p(row, p, within=row >= np.float32(_brute_top_k(row, k)))
+        _, tm = ref.threshold(row, "min_p", min_p=mp)
+        keep = [Fraction(float(x)) >= Fraction(mp) * Fraction(float(row.max()))
+                for x in row]
+        assert list(ref.kept_mask(row, tm)) == keep
+
+
+def test_predicate_equals_threshold_indicator():
+    """The rejection predicate f(t) of the blog is the indicator [t >= tau]."""
+    rng = np.random.default_rng(11)
+    for row in _tiny_rows(2, 120):
+        k = int(rng.integers(1, row.size + 1))
+        p = float(np.float32(rng.choice([0.0, 0.5, 0.8, 1.0, rng.uniform()])))
+        mp = float(np.float32(rng.uniform(0, 1)))
+        vals = sorted(set(float(x) for x in row) | {0.0})
+        probes = vals + [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+        for op in ("top_k", "top_p", "min_p", "top_k_top_p"):
+            _, tau = ref.threshold(row, op, k=k, p=p, min_p=mp)
+            f = ref.Predicate(row, op, k=k, p=p, min_p=mp)
+            for t in probes:
+                t32 = np.float32(t)
+                assert f(t32) == (float(t32) >= tau), (row, op, k, p, mp, t)
+
+
+def test_k_extremes_and_min_p_closed_form():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        row = f32(rng.dirichlet(np.ones(9)))
+        _, t1 = ref.threshold(row, "top_k", k=1)
+        assert list(np.nonzero(ref.kept_mask(row, t1))[0]) == [int(np.argmax(row))]
+        _, tv = ref.threshold(row, "top_k", k=row.size)
+        assert ref.kept_mask(row, tv).all()
+        _, tv = ref.threshold(row, "top_k", k=10 * row.size)
+        assert ref.kept_mask(row, tv).all()
+        _, tm = ref.threshold(row, "min_p", min_p=0.5)
+        assert np.array_equal(ref.kept_mask(row, tm),
+                              row.astype(np.float64) >= 0.5 * float(row.max()))
+        _, tp0 = ref.threshold(row, "top_p", p=0.0)
+        assert ref.kept_mask(row, tp0).sum() == 1
+        _, tp1 = ref.threshold(row, "top_p", p=1.0)
+        assert np.array_equal(ref.support_mask(row, tp1), row > 0)
+
+
+def test_invalid_rows_and_parameters():
+    good = f32([0.1, 0.2, 0.7])
+    for bad in ([0.1, np.nan, 0.9], [0.1, np.inf, 0.2], [0.5, -0.1, 0.6],
+                [0.0, 0.0, 0.0], [0.5, -0.0, 0.5]):
+        assert not ref.row_is_valid(f32(bad))
+        assert ref.threshold(f32(bad), "none") == (False, None)
+    assert ref.threshold(good, "top_k", k=0)[0] is False
+    assert ref.threshold(good, "top_k", k=-3)[0] is False
+    assert ref.threshold(good, "top_p", p=float("nan"))[0] is False
+    assert ref.threshold(good, "min_p", min_p=float("nan"))[0] is False
+    assert ref.threshold(good, "top_p", p=7.0) == ref.threshold(good, "top_p", p=1.0)
+    assert ref.threshold(good, "min_p", min_p=-1.0)[1] == 0.0
+
+
+# ----------------------------------------------------------------------------
+# distribution: p~ closed form, the blog's theorem (the rejection sampler's
+# output law equals p_j / Z), and the round-halving property
+# ----------------------------------------------------------------------------
+
+def test_target_distribution_closed_form():
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        row = f32(rng.dirichlet(np.ones(12)))
+        k = int(rng.integers(1, 13))
+        _, tau = ref.threshold(row, "top_k", k=k)
+        # numpy sort/argsort based top-k on tie-free rows
+        top = np.argsort(-row.astype(np.float64), kind="stable")[:k]
+        expect = np.zeros(row.size)
+        expect[top] = row[top].astype(np.float64) / math.fsum(row[top].astype(np.float64))
+        assert np.allclose(ref.target_distribution(row, tau), expect, rtol=1e-14, atol=0)
+
+
+def test_dual_pivot_law_equals_target():
+    """Exact enumeration of the dual-pivot procedure gives p~ exactly."""
+    rng = np.random.default_rng(8)
+    checked = 0
+    for row in _tiny_rows(3, 150):
+        if row.size > 7:
+            continue
+        k = int(rng.integers(1, row.size + 1))
+        p = float(np.float32(rng.choice([0.0, 0.4, 0.9, 1.0, rng.uniform()])))
+        mp = float(np.float32(rng.uniform(0, 1)))
+        for op in ref.OPS:
+            _, tau = ref.threshold(row, op, k=k, p=p, min_p=mp)
+            law, rounds = ref.dual_pivot_law(row, op, k=k, p=p, min_p=mp)
+            units = ref.exact_units(row)
+            sup = ref.support_mask(row, tau)
+            z = sum(u for u, s in zip(units, sup) if s)
+            expect = {i: Fraction(units[i], z) for i in range(row.size) if sup[i]}
+            assert law == expect, (row, op, k, p, mp)
+            assert rounds >= 1
+            checked += 1
+    assert checked > 300
+
+
+def test_round_halving():
+    """Each rejected round at least halves high - low (blog, Fig. 4 text)."""
+    rng = np.random.default_rng(9)
+    for i in range(40):
+        row = f32(rng.dirichlet(np.full(64, 0.3)))
+        k = int(rng.integers(1, 8))
+        trace = []
+        ref.dual_pivot_sample(row, "top_k", ph.Stream(i, 0, 0), k=k, trace=trace)
+        for (l0, h0), (l1, h1) in zip(trace, trace[1:]):
+            w0 = float(h0) - float(l0)
+            w1 = float(h1) - float(l1)
+            assert w1 <= w0 / 2 + 2 * np.spacing(np.float32(h0)), trace
+
+
+def test_dual_pivot_sampler_matches_target_empirically():
+    row = f32(golden("expl_top2_example.json")["probs"])
+    counts = np.zeros(row.size)
+    for i in range(4000):
+        j, _ = ref.dual_pivot_sample(row, "top_k", ph.Stream(1234, i, 0), k=2)
+        counts[j] += 1
+    assert counts[2:].sum() == 0
+    _, tau = ref.threshold(row, "top_k", k=2)
+    expect = ref.target_distribution(row, tau)[:2] * counts.sum()
+    assert stats.chisquare(counts[:2], expect).pvalue > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# inverse transform: exact quadrature on a dyadic row, boundary convention
+# F_{k-1} <= u < F_k (blog "逆变换采样")
+# ----------------------------------------------------------------------------
+
+def test_inverse_transform_quadrature_and_boundaries():
+    row = f32([1 / 8, 3 / 8, 0.0, 1 / 4, 1 / 4])
+    mask = row > 0
+    counts = np.zeros(row.size, dtype=int)
+    for i in range(64):
+        counts[ref.inverse_transform(row, mask, i << 47)] += 1    # u = i / 64
+    assert list(counts) == [8, 24, 0, 16, 16]
+    assert ref.inverse_transform(row, mask, 1 << 50) == 1          # u = F_0 = 1/8
+    assert ref.inverse_transform(row, mask, (1 << 50) - 1) == 0
+    assert ref.inverse_transform(row, mask, (1 << 53) - 1) == 4
+    # unnormalised row: scaling by the masked total
+    assert ref.inverse_transform(row * 4, mask, 1 << 50) == 1
+
+
+def test_plain_cdf_draw_frequencies():
+    rng = np.random.default_rng(21)
+    row = f32(rng.dirichlet(np.ones(6)))
+    n = 6000
+    counts = np.zeros(row.size)
+    for i in range(n):
+        counts[ref.sample_by_cdf(row, "none", ph.draw_bits53(5, i, 0, 0))] += 1
+    expect = row.astype(np.float64) / math.fsum(row.astype(np.float64)) * n
+    assert stats.chisquare(counts, expect).pvalue > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# renormalisation, logit masking, exact sums
+# ----------------------------------------------------------------------------
+
+def test_exact_units_sum_matches_fsum():
+    rng = np.random.default_rng(4)
+    for _ in range(20):
+        row = f32(rng.dirichlet(np.full(5000, 0.1)))
+        exact = sum(ref.exact_units(row))
+        assert np.ldexp(float(exact), -ref.SCALE_EXP) == math.fsum(row.astype(np.float64))
+
+
+def test_renorm_against_numpy_topk():
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        row = f32(rng.dirichlet(np.ones(200)))
+        k = int(rng.integers(1, 201))
+        valid, out = ref.top_k_renorm(row, k)
+        top = np.argsort(-row.astype(np.float64), kind="stable")[:k]
+        expect = np.zeros(row.size, dtype=np.float64)
+        expect[top] = row[top] / math.fsum(row[top].astype(np.float64))
+        assert valid and np.allclose(out, expect, rtol=1e-6, atol=0)
+        assert abs(math.fsum(out.astype(np.float64)) - 1.0) < 1e-5
+    g = golden("f4_hand_example.json")
+    valid, out = ref.top_p_renorm(f32(g["probs"]), g["top_p"])
+    x = np.array(g["probs"], dtype=np.float64)
+    expect = np.where(np.isin(np.arange(5), g["kept_top_p"]), x, 0) / x[g["kept_top_p"]].sum()
+    assert valid and np.allclose(out, expect, rtol=1e-6, atol=0)
+
+
+def test_renorm_then_plain_equals_filtered_target():
+    """renorm + plain sampling has the fused sampler's target distribution
+    (explainer, "当前 FlashInfer API 应怎样选择")."""
+    rng = np.random.default_rng(12)
+    for _ in range(20):
+        row = f32(rng.dirichlet(np.ones(50)))
+        p = float(np.float32(rng.uniform(0.3, 0.95)))
+        _, tau = ref.threshold(row, "top_p", p=p)
+        fused = ref.target_distribution(row, tau)
+        _, renormed = ref.top_p_renorm(row, p)
+        _, t0 = ref.threshold(renormed, "none")
+        assert np.allclose(ref.target_distribution(renormed, t0), fused,
+                           rtol=1e-6, atol=1e-12)
+
+
+def test_mask_logits_against_numpy():
+    rng = np.random.default_rng(13)
+    for _ in range(30):
+        row = f32(rng.standard_normal(300) * 3 - 2)      # many negative logits
+        k = int(rng.integers(1, 301))
+        valid, out = ref.mask_logits_row(row, k)
+        top = np.argpartition(-row, k - 1)[:k]
+        expect = np.full(row.size, -np.inf, dtype=np.float32)
+        expect[top] = row[top]
+        assert valid and np.array_equal(out, expect)
+    row = f32([-1.0, -3.0, -1.0, -2.0])
+    assert np.array_equal(ref.mask_logits_row(row, 1)[1],
+                          f32([-1.0, -np.inf, -1.0, -np.inf]))   # ties kept
+    assert np.array_equal(ref.mask_logits_row(row, 9)[1], row)
+    assert ref.mask_logits_row(f32([0.0, np.nan]), 1)[0] is False
+    assert ref.mask_logits_row(row, 0)[0] is False
+
+
+def test_batch_thresholds_indices():
+    probs = np.stack([f32([0.1, 0.2, 0.7]), f32([0.5, 0.25, 0.25])])
+    out = ref.batch_thresholds(probs, "top_k", indices=[1, 0, 2, -1], k=[1, 1, 1, 1],
+                               num_outputs=4)
+    assert out[0] == (True, 0.5) and out[1] == (True, np.float32(0.7))
+    assert out[2] == (False, None) and out[3] == (False, None)
