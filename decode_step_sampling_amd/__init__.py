@@ -1,0 +1,193 @@
+"""Sorting-free decode-step sampling for AMD Instinct MI355X (gfx950).
+
+Python binding of libdss.so: torch tensors in, device pointers and the
+current HIP stream out to the C ABI.  Every step of every op runs in the
+library's HIP kernels; this module only marshals arguments and allocates the
+output tensors.  Names follow the FlashInfer sampling API the pages list
+(charlestar explainer, "当前 FlashInfer API 应怎样选择").
+
+Tensors: ``probs`` / ``logits`` are float32 [rows, vocab] on a GPU.  Per
+output parameters (``top_k``, ``top_p``, ``min_p``) are Python scalars or
+1-D tensors (int32 / float32) with one entry per output.  ``seed`` and
+``offset`` are Python ints (one stream per output index) or int64 tensors
+with one value per output, read as unsigned 64-bit.
+"""
+
+import torch
+
+from . import _lib
+from ._lib import (DSS_FLAG_FROM_ZERO, DSS_FLAG_ORDER_JOINT, DSS_FLAG_STREAMING,  # noqa: F401
+                   DssError, OP_IDS)
+
+__all__ = [
+    "sampling_from_probs", "top_k_sampling_from_probs", "top_p_sampling_from_probs",
+    "min_p_sampling_from_probs", "top_k_top_p_sampling_from_probs",
+    "top_k_renorm_probs", "top_p_renorm_probs", "top_k_mask_logits",
+    "DssError", "DSS_FLAG_FROM_ZERO", "DSS_FLAG_STREAMING", "DSS_FLAG_ORDER_JOINT",
+]
+
+_U64_MASK = (1 << 64) - 1
+_workspaces = {}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(device, nbytes):
+    """Zero-filled scratch kept per device; the kernels leave it zeroed."""
+    if nbytes == 0:
+        return None, 0
+    buf = _workspaces.get(device)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[device] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+def _check_rows(x, name):
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.float32
+            and x.dim() == 2 and x.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous float32 [rows, vocab] GPU tensor")
+
+
+def _param(v, dtype, n, device, name):
+    """(device pointer or None, scalar) for a per-output parameter."""
+    if isinstance(v, torch.Tensor):
+        if v.dtype != dtype or v.device != device or v.numel() != n or not v.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor with {n} entries "
+                             f"on {device}")
+        return v, (0 if dtype == torch.int32 else 0.0)
+    return None, (int(v) if dtype == torch.int32 else float(v))
+
+
+def _rng(v, n, device, name):
+    if isinstance(v, torch.Tensor):
+        if v.dtype not in (torch.int64, torch.uint64) or v.device != device \
+                or v.numel() != n or not v.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 64-bit integer tensor with {n} "
+                             f"entries on {device}")
+        return v, 0
+    return None, int(v) & _U64_MASK
+
+
+def _sample(fn_name, probs, params, indices, seed, offset, return_valid, return_rounds,
+            flags):
+    _check_rows(probs, "probs")
+    device = probs.device
+    rows, vocab = probs.shape
+    if indices is not None:
+        if indices.dtype != torch.int32 or indices.device != device or indices.dim() != 1:
+            raise ValueError("indices must be a 1-D int32 tensor on the probs device")
+        indices = indices.contiguous()
+        n = indices.numel()
+    else:
+        n = rows
+    if seed is None:
+        seed = int(torch.randint(0, 2**62, (1,)).item())
+    seed_arr, seed_val = _rng(seed, n, device, "seed")
+    off_arr, off_val = _rng(offset, n, device, "offset")
+    samples = torch.empty(n, dtype=torch.int32, device=device)
+    valid = torch.empty(n, dtype=torch.uint8, device=device) if return_valid else None
+    rounds = torch.empty(n, dtype=torch.int32, device=device) if return_rounds else None
+    lib = _lib.load()
+    ws, ws_bytes = _workspace(device, lib.dss_workspace_size(
+        OP_IDS[fn_name], rows, vocab, n, flags))
+    args = [probs.data_ptr(), rows, vocab, _ptr(indices), n, _ptr(seed_arr), seed_val,
+            _ptr(off_arr), off_val]
+    keep = []
+    for value, dtype, name in params:
+        arr, scalar = _param(value, dtype, n, device, name)
+        keep.append(arr)
+        args += [_ptr(arr), scalar]
+    args += [samples.data_ptr(), _ptr(valid), _ptr(rounds), flags, ws, ws_bytes,
+             _stream(device)]
+    with torch.cuda.device(device):
+        _lib.check(getattr(lib, "dss_" + fn_name)(*args), fn_name)
+    out = [samples]
+    if return_valid:
+        out.append(valid)
+    if return_rounds:
+        out.append(rounds)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def sampling_from_probs(probs, *, indices=None, seed=None, offset=0, return_valid=False,
+                        return_rounds=False, flags=0):
+    """Inverse-transform sampling of one token per output."""
+    return _sample("sampling_from_probs", probs, [], indices, seed, offset, return_valid,
+                   return_rounds, flags)
+
+
+def top_k_sampling_from_probs(probs, top_k, *, indices=None, seed=None, offset=0,
+                              return_valid=False, return_rounds=False, flags=0):
+    return _sample("top_k_sampling_from_probs", probs, [(top_k, torch.int32, "top_k")],
+                   indices, seed, offset, return_valid, return_rounds, flags)
+
+
+def top_p_sampling_from_probs(probs, top_p, *, indices=None, seed=None, offset=0,
+                              return_valid=False, return_rounds=False, flags=0):
+    return _sample("top_p_sampling_from_probs", probs, [(top_p, torch.float32, "top_p")],
+                   indices, seed, offset, return_valid, return_rounds, flags)
+
+
+def min_p_sampling_from_probs(probs, min_p, *, indices=None, seed=None, offset=0,
+                              return_valid=False, return_rounds=False, flags=0):
+    return _sample("min_p_sampling_from_probs", probs, [(min_p, torch.float32, "min_p")],
+                   indices, seed, offset, return_valid, return_rounds, flags)
+
+
+def top_k_top_p_sampling_from_probs(probs, top_k, top_p, *, indices=None, seed=None,
+                                    offset=0, filter_apply_order="top_k_first",
+                                    return_valid=False, return_rounds=False, flags=0):
+    if filter_apply_order == "joint":
+        flags |= DSS_FLAG_ORDER_JOINT
+    elif filter_apply_order != "top_k_first":
+        raise ValueError("filter_apply_order must be 'top_k_first' or 'joint'")
+    return _sample("top_k_top_p_sampling_from_probs", probs,
+                   [(top_k, torch.int32, "top_k"), (top_p, torch.float32, "top_p")],
+                   indices, seed, offset, return_valid, return_rounds, flags)
+
+
+def _renorm(fn_name, x, value, dtype, name, out, return_status, flags):
+    _check_rows(x, "input")
+    device = x.device
+    rows, vocab = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_rows(out, "out")
+        if out.shape != x.shape or out.device != device:
+            raise ValueError("out must match the input's shape and device")
+    status = torch.empty(rows, dtype=torch.uint8, device=device) if return_status else None
+    arr, scalar = _param(value, dtype, rows, device, name)
+    lib = _lib.load()
+    ws, ws_bytes = _workspace(device, lib.dss_workspace_size(OP_IDS[fn_name], rows, vocab,
+                                                             rows, flags))
+    with torch.cuda.device(device):
+        _lib.check(getattr(lib, "dss_" + fn_name)(
+            x.data_ptr(), out.data_ptr(), rows, vocab, _ptr(arr), scalar,
+            _ptr(status), flags, ws, ws_bytes, _stream(device)), fn_name)
+    return (out, status) if return_status else out
+
+
+def top_k_renorm_probs(probs, top_k, *, out=None, return_status=False, flags=0):
+    """Keep the top-k probabilities of each row (ties kept) and renormalise."""
+    return _renorm("top_k_renorm_probs", probs, top_k, torch.int32, "top_k", out,
+                   return_status, flags)
+
+
+def top_p_renorm_probs(probs, top_p, *, out=None, return_status=False, flags=0):
+    """Keep each row's top-p nucleus (ties kept) and renormalise."""
+    return _renorm("top_p_renorm_probs", probs, top_p, torch.float32, "top_p", out,
+                   return_status, flags)
+
+
+def top_k_mask_logits(logits, top_k, *, out=None, return_status=False, flags=0):
+    """Keep the top-k logits of each row (ties kept), set the rest to -inf."""
+    return _renorm("top_k_mask_logits", logits, top_k, torch.int32, "top_k", out,
+                   return_status, flags)

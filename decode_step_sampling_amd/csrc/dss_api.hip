@@ -1,0 +1,220 @@
+// C ABI of libdss.so (declared in include/dss.h): argument validation on the
+// host, device check, choice of engine, launch on the caller's stream.
+// Validation happens before the first HIP runtime call, so every error path
+// can be exercised on a machine without a GPU.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/dss.h"
+#include "dss_internal.h"
+
+#define DSS_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSS_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DSS_ERR_DEVICE;
+  int st = g_device_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSS_ERR_HIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? DSS_OK : DSS_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const int32_t* indices,
+                  int32_t num_outputs, const uint64_t* seed_arr, uint64_t seed,
+                  const uint64_t* offset_arr, uint64_t offset, const int32_t* top_k_arr,
+                  int32_t top_k, const float* top_p_arr, float top_p, const float* min_p_arr,
+                  float min_p, int32_t* samples, uint8_t* valid, int32_t* rounds, uint32_t flags,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
+  if (flags & DSS_FLAG_ORDER_JOINT) return DSS_ERR_UNSUPPORTED;
+  if (rows < 0 || vocab <= 0 || num_outputs < 0) return DSS_ERR_INVALID_ARG;
+  if (vocab > DSS_MAX_VOCAB) return DSS_ERR_UNSUPPORTED;
+  if (!indices && num_outputs != rows) return DSS_ERR_INVALID_ARG;
+  if (num_outputs == 0) return DSS_OK;
+  if (!probs || !samples) return DSS_ERR_INVALID_ARG;
+  const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+
+  dss::SampleParams p;
+  p.probs = probs;
+  p.rows = rows;
+  p.vocab = vocab;
+  p.indices = indices;
+  p.num_outputs = num_outputs;
+  p.seed_arr = seed_arr;
+  p.seed = seed;
+  p.offset_arr = offset_arr;
+  p.offset = offset;
+  p.top_k_arr = top_k_arr;
+  p.top_k = top_k;
+  p.top_p_arr = top_p_arr;
+  p.top_p = top_p;
+  p.min_p_arr = min_p_arr;
+  p.min_p = min_p;
+  p.samples = samples;
+  p.valid = valid;
+  p.rounds = rounds;
+  p.vec_ok = (vocab % 4 == 0) && aligned16(probs);
+  const hipError_t e = dss::launch_stream_sample(op, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
+}
+
+int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows, int32_t vocab,
+                  const int32_t* top_k_arr, int32_t top_k, const float* top_p_arr, float top_p,
+                  uint8_t* row_status, uint32_t flags, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
+  if (flags & DSS_FLAG_ORDER_JOINT) return DSS_ERR_UNSUPPORTED;
+  if (rows < 0 || vocab <= 0) return DSS_ERR_INVALID_ARG;
+  if (vocab > DSS_MAX_VOCAB) return DSS_ERR_UNSUPPORTED;
+  if (rows == 0) return DSS_OK;
+  if (!in || !out) return DSS_ERR_INVALID_ARG;
+  const size_t need = dss_workspace_size(op_id, rows, vocab, rows, flags);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+
+  dss::RenormParams p;
+  p.in = in;
+  p.out = out;
+  p.rows = rows;
+  p.vocab = vocab;
+  p.top_k_arr = top_k_arr;
+  p.top_k = top_k;
+  p.top_p_arr = top_p_arr;
+  p.top_p = top_p;
+  p.row_status = row_status;
+  p.vec_ok = (vocab % 4 == 0) && aligned16(in) && aligned16(out);
+  const hipError_t e = dss::launch_stream_renorm(kind, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
+}
+
+}  // namespace
+
+DSS_EXPORT int dss_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                       const int32_t* indices, int32_t num_outputs,
+                                       const uint64_t* seed_arr, uint64_t seed,
+                                       const uint64_t* offset_arr, uint64_t offset,
+                                       int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                       uint32_t flags, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  return sample_common(dss::kOpNone, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
+                       offset_arr, offset, nullptr, 0, nullptr, 0.0f, nullptr, 0.0f, samples,
+                       valid, rounds, flags, workspace, workspace_bytes, stream);
+}
+
+DSS_EXPORT int dss_top_k_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                             const int32_t* indices, int32_t num_outputs,
+                                             const uint64_t* seed_arr, uint64_t seed,
+                                             const uint64_t* offset_arr, uint64_t offset,
+                                             const int32_t* top_k_arr, int32_t top_k,
+                                             int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                             uint32_t flags, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return sample_common(dss::kOpTopK, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
+                       offset_arr, offset, top_k_arr, top_k, nullptr, 0.0f, nullptr, 0.0f,
+                       samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+}
+
+DSS_EXPORT int dss_top_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                             const int32_t* indices, int32_t num_outputs,
+                                             const uint64_t* seed_arr, uint64_t seed,
+                                             const uint64_t* offset_arr, uint64_t offset,
+                                             const float* top_p_arr, float top_p,
+                                             int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                             uint32_t flags, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return sample_common(dss::kOpTopP, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
+                       offset_arr, offset, nullptr, 0, top_p_arr, top_p, nullptr, 0.0f,
+                       samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+}
+
+DSS_EXPORT int dss_min_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                             const int32_t* indices, int32_t num_outputs,
+                                             const uint64_t* seed_arr, uint64_t seed,
+                                             const uint64_t* offset_arr, uint64_t offset,
+                                             const float* min_p_arr, float min_p,
+                                             int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                             uint32_t flags, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return sample_common(dss::kOpMinP, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
+                       offset_arr, offset, nullptr, 0, nullptr, 0.0f, min_p_arr, min_p,
+                       samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+}
+
+DSS_EXPORT int dss_top_k_top_p_sampling_from_probs(
+    const float* probs, int32_t rows, int32_t vocab, const int32_t* indices, int32_t num_outputs,
+    const uint64_t* seed_arr, uint64_t seed, const uint64_t* offset_arr, uint64_t offset,
+    const int32_t* top_k_arr, int32_t top_k, const float* top_p_arr, float top_p,
+    int32_t* samples, uint8_t* valid, int32_t* rounds, uint32_t flags, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs, seed_arr,
+                       seed, offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p, nullptr,
+                       0.0f, samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+}
+
+DSS_EXPORT int dss_top_k_renorm_probs(const float* probs, float* out, int32_t rows, int32_t vocab,
+                                      const int32_t* top_k_arr, int32_t top_k,
+                                      uint8_t* row_status, uint32_t flags, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return renorm_common(dss::kRenormTopK, DSS_OP_TOP_K_RENORM, probs, out, rows, vocab, top_k_arr,
+                       top_k, nullptr, 0.0f, row_status, flags, workspace, workspace_bytes,
+                       stream);
+}
+
+DSS_EXPORT int dss_top_p_renorm_probs(const float* probs, float* out, int32_t rows, int32_t vocab,
+                                      const float* top_p_arr, float top_p, uint8_t* row_status,
+                                      uint32_t flags, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return renorm_common(dss::kRenormTopP, DSS_OP_TOP_P_RENORM, probs, out, rows, vocab, nullptr,
+                       0, top_p_arr, top_p, row_status, flags, workspace, workspace_bytes,
+                       stream);
+}
+
+DSS_EXPORT int dss_top_k_mask_logits(const float* logits, float* out, int32_t rows,
+                                     int32_t vocab, const int32_t* top_k_arr, int32_t top_k,
+                                     uint8_t* row_status, uint32_t flags, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return renorm_common(dss::kMaskLogits, DSS_OP_TOP_K_MASK_LOGITS, logits, out, rows, vocab,
+                       top_k_arr, top_k, nullptr, 0.0f, row_status, flags, workspace,
+                       workspace_bytes, stream);
+}
+
+DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
+                                     int32_t num_outputs, uint32_t flags) {
+  (void)op;
+  (void)rows;
+  (void)vocab;
+  (void)num_outputs;
+  (void)flags;
+  return 0;
+}
+
+DSS_EXPORT const char* dss_strerror(int32_t status) {
+  switch (status) {
+    case DSS_OK: return "ok";
+    case DSS_ERR_INVALID_ARG: return "invalid argument";
+    case DSS_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSS_ERR_HIP: return "HIP runtime error";
+    case DSS_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+DSS_EXPORT int32_t dss_version(void) { return 100; }

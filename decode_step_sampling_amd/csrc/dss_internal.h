@@ -1,0 +1,64 @@
+// Internal declarations shared by the host ABI and the kernel translation
+// units of libdss.so.  Not installed; the public interface is include/dss.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dss {
+
+// Filter ids used as template parameters by the sampling kernels.
+enum Op : int {
+  kOpNone = 0,      // plain inverse-transform sampling
+  kOpTopK = 1,
+  kOpTopP = 2,
+  kOpMinP = 3,
+  kOpTopKTopP = 4,  // top-k first, then top-p inside the top-k set
+};
+
+// Everything a sampling kernel reads or writes.  Pointer fields are device
+// memory; a NULL parameter array means "use the scalar".
+struct SampleParams {
+  const float* probs;
+  int32_t rows;
+  int32_t vocab;
+  const int32_t* indices;
+  int32_t num_outputs;
+  const uint64_t* seed_arr;
+  uint64_t seed;
+  const uint64_t* offset_arr;
+  uint64_t offset;
+  const int32_t* top_k_arr;
+  int32_t top_k;
+  const float* top_p_arr;
+  float top_p;
+  const float* min_p_arr;
+  float min_p;
+  int32_t* samples;
+  uint8_t* valid;
+  int32_t* rounds;
+  int32_t vec_ok;   // rows may be read with 16-byte loads
+};
+
+enum RenormKind : int { kRenormTopK = 0, kRenormTopP = 1, kMaskLogits = 2 };
+
+struct RenormParams {
+  const float* in;
+  float* out;
+  int32_t rows;
+  int32_t vocab;
+  const int32_t* top_k_arr;
+  int32_t top_k;
+  const float* top_p_arr;
+  float top_p;
+  uint8_t* row_status;
+  int32_t vec_ok;
+};
+
+// Streaming engine: one 1024-thread work-group per output (or row), every
+// pass reads the row from global memory.  Returns a hipError_t.
+hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s);
+hipError_t launch_stream_renorm(int kind, const RenormParams& p, hipStream_t s);
+
+}  // namespace dss

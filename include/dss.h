@@ -1,0 +1,215 @@
+/*
+ * dss.h -- sorting-free decode-step sampling on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libdss.so.  Plain pointers and sizes only.  Pages cited:
+ *   [Blog] FlashInfer blog "Sorting-Free GPU Kernels for LLM Sampling"
+ *          (Chinese translation "面向 LLM 采样的免排序 GPU 内核");
+ *   [F4]   gpu-kernel-drills note "F4 讲解：不排序的 top-k / top-p";
+ *   [Expl] charlestar explainer on FlashInfer Sorting-Free Sampling.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ * Memory.  Every array argument is DEVICE memory of the current HIP device:
+ *   probabilities / logits, outputs, per-output parameter arrays, index maps,
+ *   seed and offset arrays.  The caller allocates and owns all of them; the
+ *   library keeps no pointer after it returns and allocates nothing.
+ *   Row-major contiguous [rows, vocab] float32; row r starts at
+ *   probs + (int64)r * vocab.  Any alignment is accepted; 16-byte aligned rows
+ *   (vocab % 4 == 0 and a 16-byte aligned base) take the vector-load path.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Work is enqueued asynchronously; nothing synchronises the host.
+ *
+ * Workspace.  `workspace` / `workspace_bytes` is caller-owned device scratch
+ *   of at least dss_workspace_size(...) bytes (NULL is fine when that is 0).
+ *   It must be zero-filled once when it is allocated; every call leaves it
+ *   zero-filled again on return of its kernels, so a workspace can be reused
+ *   by later calls on the same stream without clearing.  Two calls that run
+ *   concurrently (different streams) need different workspaces.
+ *
+ * Outputs of the sampling ops (length num_outputs):
+ *   samples[i]  token id in [0, vocab), or -1 when output i is invalid;
+ *   valid[i]    1 / 0 (nullable: pass NULL to skip) [Expl "退化分布必须可报告"];
+ *   rounds[i]   number of draws the rejection loop used (nullable).
+ *
+ * Rows and outputs.  indices[i] maps output i to a probability row
+ *   ([Expl "动态 batch 中的 RNG 所有权": several outputs may share a row); with
+ *   indices == NULL, output i reads row i and num_outputs must equal rows.
+ *   Per-output parameters: if the array pointer (top_k_arr, top_p_arr,
+ *   min_p_arr) is non-NULL it holds num_outputs values (one per output,
+ *   not per row); otherwise the scalar applies to every output.
+ *
+ * Random numbers ([Expl "Seed、offset 与 deterministic 的边界"]).  Each output
+ *   owns the stream
+ *     key = (seed_i, 0), counter = (offset_i, sid_i, r / 4, 0),
+ *     u_r = (word[r % 4] of Philox4x64-10(counter, key)) >> 11, times 2^-53,
+ *   for draws r = 0, 1, 2, ... (Philox4x64-10: Salmon et al., SC'11).
+ *   seed_i = seed_arr ? seed_arr[i] : seed, offset_i likewise; sid_i = 0 when
+ *   seed_arr is given (the stream then depends only on the request's own
+ *   seed and offset, not on its batch position) and sid_i = i when one scalar
+ *   seed serves the call.  The library never advances offsets: the caller
+ *   must give every call a new offset.  Identical inputs and streams give
+ *   identical outputs (fixed reduction order, no floating-point atomics).
+ *
+ * Data problems are reported per output / row, never as an error status:
+ *   a row containing NaN, +-inf or any value with the sign bit set
+ *   (including -0.0), or whose total is zero; top_k <= 0; NaN top_p / min_p;
+ *   indices[i] outside [0, rows).  Sampling: samples[i] = -1, valid[i] = 0.
+ *   Renorm / mask: the output row is NaN-filled and row_status[r] = 1
+ *   (row_status nullable, 0 for good rows).
+ *
+ * Filter semantics (value-based, ties kept: the kept set is always the upper
+ * set {x >= tau}; [F4 §⑥], [Expl "Tie 需要明确定义"]):
+ *   top_k   tau = k-th largest value; k >= vocab keeps every token.
+ *   top_p   tau = v_(m), m = min{r >= 1 : v_(1) + ... + v_(r) >= p * Z},
+ *           v_(1) >= v_(2) >= ... the sorted row, Z its total
+ *           ([Expl "Top-p"], [F4 §①-②]); p clamped to [0, 1].
+ *   min_p   tau = min_p * max(row), exact product ([Blog "Min-P"]);
+ *           min_p clamped to [0, 1].
+ *   top_k_top_p (top-k first, [Blog] footnote 1, [Expl "Top-k 与 top-p 的组合
+ *           顺序会改变分布"]): top-p applied inside the top-k set, Z being the
+ *           top-k mass.
+ *   The sampled distribution is p~_i = x_i / sum_{x_j >= tau} x_j on the kept
+ *   set ([Expl "采样流水线究竟在计算什么"]); zero-probability tokens are never
+ *   drawn.  Rows need not sum to one.
+ *
+ * Status codes (host validation runs before any HIP call):
+ */
+#ifndef DSS_H
+#define DSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSS_OK                  0
+#define DSS_ERR_INVALID_ARG   (-1)  /* NULL required pointer, negative size, ... */
+#define DSS_ERR_WORKSPACE     (-2)  /* workspace smaller than dss_workspace_size */
+#define DSS_ERR_UNSUPPORTED   (-3)  /* vocab above DSS_MAX_VOCAB, joint order    */
+#define DSS_ERR_HIP           (-4)  /* a HIP runtime call or launch failed       */
+#define DSS_ERR_DEVICE        (-5)  /* current device is not gfx950             */
+
+#define DSS_MAX_VOCAB  (1 << 20)
+
+/* flags */
+#define DSS_FLAG_ORDER_JOINT   0x1u  /* joint top-k/top-p order: not built, returns
+                                        DSS_ERR_UNSUPPORTED ([Blog] footnote 1) */
+#define DSS_FLAG_FROM_ZERO     0x2u  /* run the rejection loop exactly as the
+                                        blog's listing starts it: low = 0,
+                                        high = max, whole row (no certified
+                                        starting interval, no split rows)     */
+#define DSS_FLAG_STREAMING     0x4u  /* force the one-work-group-per-row
+                                        streaming engine                       */
+#define DSS_FLAGS_ALL          0x7u
+
+/* op ids for dss_workspace_size */
+#define DSS_OP_SAMPLING          0
+#define DSS_OP_TOP_K_SAMPLING    1
+#define DSS_OP_TOP_P_SAMPLING    2
+#define DSS_OP_MIN_P_SAMPLING    3
+#define DSS_OP_TOP_K_TOP_P       4
+#define DSS_OP_TOP_K_RENORM      5
+#define DSS_OP_TOP_P_RENORM      6
+#define DSS_OP_TOP_K_MASK_LOGITS 7
+
+/* Inverse-transform sampling from each output's row ([Blog "逆变换采样"],
+ * [Expl "不带过滤时：inverse transform sampling"]): u ~ U[0,1) (draw r = 0),
+ * return the first token j with F_j > u * Z, F the prefix sums in index order,
+ * Z the row total.  rounds[i] = 1. */
+int dss_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                            const int32_t* indices, int32_t num_outputs,
+                            const uint64_t* seed_arr, uint64_t seed,
+                            const uint64_t* offset_arr, uint64_t offset,
+                            int32_t* samples, uint8_t* valid, int32_t* rounds,
+                            uint32_t flags, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Top-k sampling by dual-pivot rejection sampling ([Blog "双枢轴拒绝采样"],
+ * [Expl "Dual Pivot 怎样收缩范围"]); the output law is x_j / Z_k on the top-k
+ * set ([Blog "拒绝采样器正确性的理论证明"]). */
+int dss_top_k_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                  const int32_t* indices, int32_t num_outputs,
+                                  const uint64_t* seed_arr, uint64_t seed,
+                                  const uint64_t* offset_arr, uint64_t offset,
+                                  const int32_t* top_k_arr, int32_t top_k,
+                                  int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                  uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Top-p (nucleus) sampling by dual-pivot rejection sampling ([Blog "拒绝采样",
+ * "双枢轴拒绝采样"]). */
+int dss_top_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                  const int32_t* indices, int32_t num_outputs,
+                                  const uint64_t* seed_arr, uint64_t seed,
+                                  const uint64_t* offset_arr, uint64_t offset,
+                                  const float* top_p_arr, float top_p,
+                                  int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                  uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Min-p sampling ([Blog "Min-P"], [Expl "Min-p"]) through the same loop. */
+int dss_min_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                  const int32_t* indices, int32_t num_outputs,
+                                  const uint64_t* seed_arr, uint64_t seed,
+                                  const uint64_t* offset_arr, uint64_t offset,
+                                  const float* min_p_arr, float min_p,
+                                  int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                  uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Fused top-k-then-top-p sampling ([Blog] footnote 1 "Top-K First"; [Expl
+ * "Top-k 与 top-p 的组合顺序会改变分布"]).  DSS_FLAG_ORDER_JOINT is rejected. */
+int dss_top_k_top_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
+                                        const int32_t* indices, int32_t num_outputs,
+                                        const uint64_t* seed_arr, uint64_t seed,
+                                        const uint64_t* offset_arr, uint64_t offset,
+                                        const int32_t* top_k_arr, int32_t top_k,
+                                        const float* top_p_arr, float top_p,
+                                        int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                        uint32_t flags, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* Top-k renormalisation ([F4 §②-④], [Expl "只过滤/归一化"]):
+ * out[r, i] = x_i / Z_kept if x_i >= tau_k else 0.  top_k_arr has `rows`
+ * entries (per row).  out may equal probs (in place). */
+int dss_top_k_renorm_probs(const float* probs, float* out, int32_t rows, int32_t vocab,
+                           const int32_t* top_k_arr, int32_t top_k,
+                           uint8_t* row_status, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Top-p renormalisation by a monotone threshold search on the float32 bit
+ * pattern ([F4 §②-③, §⑤]).  top_p_arr has `rows` entries.  In place allowed. */
+int dss_top_p_renorm_probs(const float* probs, float* out, int32_t rows, int32_t vocab,
+                           const float* top_p_arr, float top_p,
+                           uint8_t* row_status, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Keep the k largest logits, set the rest to -inf ([Expl "只过滤/归一化"]);
+ * negative logits are ordered by value, not raw bits ([F4 §⑧]); ties at the
+ * k-th value are kept; -0.0 equals +0.0.  A NaN logit invalidates the row;
+ * +-inf logits are ordinary values.  top_k_arr has `rows` entries.  In place
+ * allowed. */
+int dss_top_k_mask_logits(const float* logits, float* out, int32_t rows, int32_t vocab,
+                          const int32_t* top_k_arr, int32_t top_k,
+                          uint8_t* row_status, uint32_t flags,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace an op needs for these sizes and flags (0 if none). */
+size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
+                          int32_t num_outputs, uint32_t flags);
+
+/* Static description of a status code. */
+const char* dss_strerror(int32_t status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t dss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSS_H */

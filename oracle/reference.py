@@ -116,6 +116,31 @@ def tau_top_p(sorted_desc, n_c, p):
     return float(sorted_desc[r])
 
 
+def top_p_boundary_margin(row, p, k=None):
+    """Relative distance of the top-p decision from a tie with p * Z_C.
+
+    min(|prefix_m - p Z_C|, |prefix_{m'} - p Z_C|) / Z_C, where m is the
+    chosen prefix length and m' the last prefix strictly below it; a float64
+    implementation that accumulates masses with relative error e decides
+    every boundary exactly when the margin exceeds e.  Reported by the GPU
+    tests; not used by any decision here.
+    """
+    s = _sorted_desc(row)
+    n_c = s.size if k is None else _count_at_least(s, tau_top_k(row, k))
+    units = exact_units(s[:n_c])
+    prefix = list(accumulate(units))
+    z_c = prefix[-1]
+    pf = fraction_of(clamp01(p)) * z_c
+    r = bisect_left(prefix, -((-pf.numerator) // pf.denominator))
+    r = max(0, min(r, n_c - 1))
+    gaps = [abs(prefix[r] - pf)]
+    tau = s[r]
+    below = _count_at_least(s[:n_c], np.nextafter(tau, np.float32(np.inf)))
+    if below > 0:
+        gaps.append(abs(prefix[below - 1] - pf))
+    return float(min(gaps) / z_c)
+
+
 def clamp01(v):
     v = float(np.float32(v))
     return min(max(v, 0.0), 1.0)
@@ -229,6 +254,27 @@ def mask_logits_row(row, k):
 # inverse-transform draw
 # ----------------------------------------------------------------------------
 
+class CdfTable:
+    """Exact prefix sums of the masked entries of one row, for repeated draws.
+
+    ``draw(a53)`` is the inverse-transform rule of ``inverse_transform``:
+    the first masked index j (index order) whose prefix exceeds u * Z, with
+    u = a53 / 2**53 and Z the masked total.
+    """
+
+    def __init__(self, row, mask):
+        r = np.asarray(row, dtype=np.float32)
+        self.idx = np.nonzero(mask)[0]
+        self.prefix = list(accumulate(exact_units(r[self.idx])))
+        self.total = self.prefix[-1] if self.prefix else 0
+
+    def draw(self, a53):
+        if self.total == 0:
+            return -1
+        thr = (int(a53) * self.total) >> 53       # floor(u * Z)
+        return int(self.idx[bisect_right(self.prefix, thr)])
+
+
 def inverse_transform(row, mask, a53):
     """Index j with F_{j-1} <= u * Z < F_j over the masked entries, in index order.
 
@@ -238,15 +284,7 @@ def inverse_transform(row, mask, a53):
     entries, so unnormalised rows are handled exactly.  Returns -1 if the
     masked mass is zero.
     """
-    r = np.asarray(row, dtype=np.float32)
-    idx = np.nonzero(mask)[0]
-    units = exact_units(r[idx])
-    prefix = list(accumulate(units))
-    if not prefix or prefix[-1] == 0:
-        return -1
-    thr = (int(a53) * prefix[-1]) >> 53          # floor(u * Z)
-    j = bisect_right(prefix, thr)                # first prefix > u * Z
-    return int(idx[j])
+    return CdfTable(row, mask).draw(a53)
 
 
 def sample_by_cdf(row, op, a53, k=None, p=None, min_p=None):

@@ -1,0 +1,126 @@
+"""C-ABI contract checks that need no GPU.
+
+libdss.so must load, export every function include/dss.h declares, and reject
+bad arguments with the documented status before making any HIP call (so
+these run on a machine without a GPU).  No compute call is made here.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_step_sampling_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dss.h")
+
+NULL = None
+FAKE = 0x1000          # never dereferenced: validation fails before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*|int32_t)\s+(dss_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def header_macro(name):
+    m = re.search(rf"#define\s+{name}\s+\(?\s*(-?\w+)", open(HEADER).read())
+    return int(m.group(1).rstrip("uU"), 0)
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_header_constants_match_binding():
+    for name in ("DSS_OK", "DSS_ERR_INVALID_ARG", "DSS_ERR_WORKSPACE", "DSS_ERR_UNSUPPORTED",
+                 "DSS_ERR_HIP", "DSS_ERR_DEVICE", "DSS_FLAG_ORDER_JOINT", "DSS_FLAG_FROM_ZERO",
+                 "DSS_FLAG_STREAMING"):
+        assert header_macro(name) == getattr(_lib, name), name
+    assert eval(re.search(r"#define\s+DSS_MAX_VOCAB\s+\((.*)\)", open(HEADER).read())
+                .group(1)) == _lib.DSS_MAX_VOCAB
+    for op, i in _lib.OP_IDS.items():
+        assert header_macro({
+            "sampling_from_probs": "DSS_OP_SAMPLING",
+            "top_k_sampling_from_probs": "DSS_OP_TOP_K_SAMPLING",
+            "top_p_sampling_from_probs": "DSS_OP_TOP_P_SAMPLING",
+            "min_p_sampling_from_probs": "DSS_OP_MIN_P_SAMPLING",
+            "top_k_top_p_sampling_from_probs": "DSS_OP_TOP_K_TOP_P",
+            "top_k_renorm_probs": "DSS_OP_TOP_K_RENORM",
+            "top_p_renorm_probs": "DSS_OP_TOP_P_RENORM",
+            "top_k_mask_logits": "DSS_OP_TOP_K_MASK_LOGITS"}[op]) == i
+
+
+def _plain(lib, probs=FAKE, rows=1, vocab=8, indices=NULL, n=1, samples=FAKE, flags=0,
+           ws=NULL, ws_bytes=0):
+    return lib.dss_sampling_from_probs(probs, rows, vocab, indices, n, NULL, 1, NULL, 0,
+                                       samples, NULL, NULL, flags, ws, ws_bytes, NULL)
+
+
+def _topk_topp(lib, flags=0, rows=1, vocab=8, n=1):
+    return lib.dss_top_k_top_p_sampling_from_probs(FAKE, rows, vocab, NULL, n, NULL, 1, NULL, 0,
+                                                   NULL, 5, NULL, 0.9, FAKE, NULL, NULL, flags,
+                                                   NULL, 0, NULL)
+
+
+def test_sampling_validation_before_any_hip_call():
+    lib = _lib.load()
+    assert _plain(lib, probs=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert _plain(lib, samples=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert _plain(lib, rows=-1) == _lib.DSS_ERR_INVALID_ARG
+    assert _plain(lib, vocab=0) == _lib.DSS_ERR_INVALID_ARG
+    assert _plain(lib, vocab=-5) == _lib.DSS_ERR_INVALID_ARG
+    assert _plain(lib, n=-1, indices=FAKE) == _lib.DSS_ERR_INVALID_ARG
+    assert _plain(lib, rows=2, n=3) == _lib.DSS_ERR_INVALID_ARG      # n != rows, no indices
+    assert _plain(lib, vocab=_lib.DSS_MAX_VOCAB + 1) == _lib.DSS_ERR_UNSUPPORTED
+    assert _plain(lib, flags=0x100) == _lib.DSS_ERR_INVALID_ARG
+    assert _topk_topp(lib, flags=_lib.DSS_FLAG_ORDER_JOINT) == _lib.DSS_ERR_UNSUPPORTED
+    # empty batches are a successful no-op and touch nothing
+    assert _plain(lib, probs=NULL, samples=NULL, rows=0, n=0) == _lib.DSS_OK
+    assert _plain(lib, probs=NULL, samples=NULL, rows=3, n=0, indices=FAKE) == _lib.DSS_OK
+    assert _topk_topp(lib, rows=0, n=0) == _lib.DSS_OK
+
+
+def test_renorm_and_mask_validation():
+    lib = _lib.load()
+    for fn, param in ((lib.dss_top_k_renorm_probs, 3), (lib.dss_top_p_renorm_probs, 0.5),
+                      (lib.dss_top_k_mask_logits, 3)):
+        assert fn(NULL, FAKE, 1, 8, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_ERR_INVALID_ARG
+        assert fn(FAKE, NULL, 1, 8, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, -1, 8, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, 1, 0, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, 1, _lib.DSS_MAX_VOCAB + 1, NULL, param, NULL, 0, NULL, 0,
+                  NULL) == _lib.DSS_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, 1, 8, NULL, param, NULL, 0x80, NULL, 0, NULL) == \
+            _lib.DSS_ERR_INVALID_ARG
+        assert fn(NULL, NULL, 0, 8, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_OK
+
+
+def test_workspace_size_and_strings():
+    lib = _lib.load()
+    for op in range(8):
+        for rows, vocab, n in ((1, 8, 1), (64, 151936, 64), (512, 256000, 512), (0, 1, 0)):
+            size = lib.dss_workspace_size(op, rows, vocab, n, 0)
+            assert size >= 0
+            assert lib.dss_workspace_size(op, rows, vocab, n, _lib.DSS_FLAG_STREAMING) == 0
+    for code in (0, -1, -2, -3, -4, -5):
+        assert _lib.strerror(code) not in ("", "unknown status")
+    assert _lib.strerror(7) == "unknown status"
+    assert lib.dss_version() >= 100
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import decode_step_sampling_amd as dss
+    with pytest.raises(ValueError):
+        dss.sampling_from_probs(torch.ones(2, 8))
+    with pytest.raises(ValueError):
+        dss.top_p_renorm_probs(torch.ones(2, 8), 0.5)

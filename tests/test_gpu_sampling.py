@@ -1,0 +1,331 @@
+"""GPU parity of the sampling ops against the CPU oracle (needs an MI355X).
+
+Three levels, as the task's correctness criteria ask:
+  * token-exact: plain inverse-transform sampling, and the rejection loop run
+    from low = 0 (DSS_FLAG_FROM_ZERO), consume the same Philox stream as the
+    oracle's exact models, so every token (and round count) must match;
+  * hard support: every draw lies in the oracle's kept set (sort-based);
+  * distribution: per-row chi-square at alpha = 1e-3 against the oracle's p~.
+Inputs come from synthetic_inputs (seeded); every RNG seed here is fixed, so
+the statistical tests are deterministic.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_step_sampling_amd as dss
+import synthetic_inputs as si
+from oracle import philox as ph
+from oracle import reference as ref
+from gpu_util import gpu, host, pooled_chi_square, u64
+
+pytestmark = pytest.mark.gpu
+
+OPS = {
+    "none": lambda P, prm, **kw: dss.sampling_from_probs(P, **kw),
+    "top_k": lambda P, prm, **kw: dss.top_k_sampling_from_probs(P, prm["k"], **kw),
+    "top_p": lambda P, prm, **kw: dss.top_p_sampling_from_probs(P, prm["p"], **kw),
+    "min_p": lambda P, prm, **kw: dss.min_p_sampling_from_probs(P, prm["mp"], **kw),
+    "top_k_top_p": lambda P, prm, **kw: dss.top_k_top_p_sampling_from_probs(
+        P, prm["k"], prm["p"], **kw),
+}
+
+FLAG_SETS = [0, dss.DSS_FLAG_FROM_ZERO, dss.DSS_FLAG_STREAMING]
+
+
+def _scalar_params(k=50, p=0.9, mp=0.1):
+    return {"k": k, "p": np.float32(p), "mp": np.float32(mp)}
+
+
+def _oracle_kw(op, prm, i=None):
+    def pick(v):
+        return v if (i is None or np.ndim(v) == 0) else v[i]
+    return {"k": pick(prm["k"]) if op in ("top_k", "top_k_top_p") else None,
+            "p": pick(prm["p"]) if op in ("top_p", "top_k_top_p") else None,
+            "min_p": pick(prm["mp"]) if op == "min_p" else None}
+
+
+@pytest.fixture(scope="module")
+def small():
+    w = si.small()
+    w["P"] = gpu(w["probs"])
+    return w
+
+
+# ----------------------------------------------------------------------------
+# token-exact
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_plain_sampling_token_exact(small, flags):
+    probs = small["probs"]
+    n = 4096
+    idx = (np.arange(n) % probs.shape[0]).astype(np.int32)
+    seed, offset = 987654321, 7
+    s, v, r = dss.sampling_from_probs(small["P"], indices=gpu(idx), seed=seed, offset=offset,
+                                      return_valid=True, return_rounds=True, flags=flags)
+    s, v, r = host(s), host(v), host(r)
+    tables = [ref.CdfTable(row, row > 0) for row in probs]
+    expect = np.array([tables[idx[i]].draw(ph.draw_bits53(seed, offset, i, 0))
+                       for i in range(n)])
+    assert (v == 1).all() and (r == 1).all()
+    assert np.array_equal(s, expect), np.nonzero(s != expect)[0][:10]
+
+
+def test_plain_sampling_token_exact_full_vocab():
+    w = si.renorm(rows=8)
+    probs = w["probs"]
+    n = 512
+    idx = (np.arange(n) % probs.shape[0]).astype(np.int32)
+    seeds = np.arange(1000, 1000 + n, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15)
+    offs = np.arange(n, dtype=np.uint64)
+    s = host(dss.sampling_from_probs(gpu(probs), indices=gpu(idx), seed=u64(seeds),
+                                     offset=u64(offs)))
+    tables = [ref.CdfTable(row, row > 0) for row in probs]
+    expect = np.array([tables[idx[i]].draw(ph.draw_bits53(int(seeds[i]), int(offs[i]), 0, 0))
+                       for i in range(n)])
+    assert np.array_equal(s, expect)
+
+
+@pytest.mark.parametrize("op", ["top_k", "top_p", "min_p", "top_k_top_p"])
+def test_rejection_loop_token_exact_from_zero(small, op):
+    """From low = 0 the GPU loop and the oracle's step-by-step model of the
+    blog's dual-pivot procedure draw the same tokens in the same rounds."""
+    probs = small["probs"]
+    n = 32
+    idx = (np.arange(n) % probs.shape[0]).astype(np.int32)
+    prm = _scalar_params(k=50, p=0.9, mp=0.1)
+    seed, offset = 4242, 3
+    s, v, r = OPS[op](small["P"], prm, indices=gpu(idx), seed=seed, offset=offset,
+                      return_valid=True, return_rounds=True, flags=dss.DSS_FLAG_FROM_ZERO)
+    s, v, r = host(s), host(v), host(r)
+    for i in range(n):
+        tok, rounds = ref.dual_pivot_sample(probs[idx[i]], op, ph.Stream(seed, offset, i),
+                                            **_oracle_kw(op, prm))
+        assert (s[i], r[i]) == (tok, rounds), (i, op)
+    assert (v == 1).all()
+
+
+# ----------------------------------------------------------------------------
+# support and distribution (small workload: B=4, V=32000, top_k=50, top_p=0.9)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("op", ["top_k_top_p", "top_k", "top_p", "min_p", "none"])
+@pytest.mark.parametrize("flags", [0, dss.DSS_FLAG_FROM_ZERO])
+def test_chi_square_per_row(small, op, flags):
+    probs = small["probs"]
+    rows = probs.shape[0]
+    draws = 20000
+    idx = np.repeat(np.arange(rows, dtype=np.int32), draws)
+    prm = _scalar_params(k=50, p=0.9, mp=0.02)
+    s = host(OPS[op](small["P"], prm, indices=gpu(idx), seed=2026, offset=11, flags=flags))
+    for row in range(rows):
+        _, tau = ref.threshold(probs[row], op, **_oracle_kw(op, prm))
+        support = ref.support_mask(probs[row], tau)
+        got = s[row * draws:(row + 1) * draws]
+        assert (got >= 0).all() and support[got].all(), "draw outside the kept set"
+        counts = np.bincount(got, minlength=probs.shape[1])
+        pval, tvd, cells = pooled_chi_square(counts[support],
+                                             ref.target_distribution(probs[row], tau)[support])
+        assert pval > 1e-3, (op, row, pval, tvd, cells)
+
+
+def test_chi_square_across_calls(small):
+    """20000 separate calls with offsets 0..19999, one output per row."""
+    probs = small["probs"]
+    rows, V = probs.shape
+    draws = 20000
+    prm = _scalar_params()
+    seeds = u64(np.array([11, 22, 33, 44], dtype=np.uint64))
+    out = torch.empty(draws, rows, dtype=torch.int32, device="cuda:0")
+    for t in range(draws):
+        out[t] = dss.top_k_top_p_sampling_from_probs(small["P"], prm["k"], prm["p"], seed=seeds,
+                                                     offset=t)
+    s = host(out)
+    for row in range(rows):
+        _, tau = ref.threshold(probs[row], "top_k_top_p", k=prm["k"], p=prm["p"])
+        support = ref.support_mask(probs[row], tau)
+        assert support[s[:, row]].all()
+        counts = np.bincount(s[:, row], minlength=V)
+        pval, tvd, _ = pooled_chi_square(counts[support],
+                                         ref.target_distribution(probs[row], tau)[support])
+        assert pval > 1e-3, (row, pval, tvd)
+
+
+# ----------------------------------------------------------------------------
+# full-size headline workload: B=64, V=151936, per-row top_k ~ U{1..1024},
+# top_p ~ U[0.5, 0.95]: every draw must lie in the oracle's kept set
+# ----------------------------------------------------------------------------
+
+def test_headline_support_full_size():
+    w = si.renorm()
+    probs = w["probs"]
+    rows = probs.shape[0]
+    P = gpu(probs)
+    k_t, p_t = gpu(w["top_k"]), gpu(w["top_p"])
+    seeds = u64(w["seeds"])
+    supports = []
+    for row in range(rows):
+        valid, tau = ref.threshold(probs[row], "top_k_top_p", k=w["top_k"][row], p=w["top_p"][row])
+        assert valid
+        supports.append(ref.support_mask(probs[row], tau))
+    rounds_all = []
+    for flags in (0, dss.DSS_FLAG_FROM_ZERO):
+        for call in range(40):
+            s, v, r = dss.top_k_top_p_sampling_from_probs(P, k_t, p_t, seed=seeds, offset=call,
+                                                          return_valid=True, return_rounds=True,
+                                                          flags=flags)
+            s, v, r = host(s), host(v), host(r)
+            assert (v == 1).all()
+            for row in range(rows):
+                assert supports[row][s[row]], (flags, call, row, s[row])
+            rounds_all.append(r)
+    rounds_all = np.concatenate(rounds_all)
+    assert rounds_all.min() >= 1 and rounds_all.max() < 64
+
+
+# ----------------------------------------------------------------------------
+# degenerate rows and parameters ("退化分布必须可报告")
+# ----------------------------------------------------------------------------
+
+def test_degenerate_rows_and_parameters():
+    V = 1000
+    rng = np.random.default_rng(3)
+    good = rng.dirichlet(np.ones(V)).astype(np.float32)
+    rows = [good.copy() for _ in range(7)]
+    rows[1][17] = np.nan
+    rows[2][5] = np.inf
+    rows[3][9] = -1e-3
+    rows[4][:] = 0.0
+    rows[5][3] = -0.0
+    rows[5][3] = np.float32(-0.0)
+    probs = np.stack(rows)
+    P = gpu(probs)
+    for op in ("none", "top_k", "top_p", "min_p", "top_k_top_p"):
+        for flags in FLAG_SETS:
+            s, v = OPS[op](P, _scalar_params(k=10, p=0.8, mp=0.1), seed=1, return_valid=True,
+                           flags=flags)
+            s, v = host(s), host(v)
+            assert list(v) == [1, 0, 0, 0, 0, 0, 1], (op, flags)
+            assert list(s[1:6]) == [-1] * 5
+            assert s[0] >= 0 and s[6] >= 0
+    # bad parameters and out-of-range indices make single outputs invalid
+    idx = gpu(np.array([0, 6, -1, 7, 0], dtype=np.int32))
+    k_arr = gpu(np.array([5, 0, 5, 5, -3], dtype=np.int32))
+    s, v = dss.top_k_sampling_from_probs(P, k_arr, indices=idx, seed=5, return_valid=True)
+    assert list(host(v)) == [1, 0, 0, 0, 0]
+    assert list(host(s))[1:] == [-1, -1, -1, -1]
+    p_arr = gpu(np.array([0.5, np.nan, 2.0, -1.0, 0.0], dtype=np.float32))
+    s, v = dss.top_p_sampling_from_probs(P, p_arr, indices=gpu(np.zeros(5, np.int32)), seed=5,
+                                         return_valid=True)
+    s, v = host(s), host(v)
+    assert list(v) == [1, 0, 1, 1, 1]
+    top = int(np.argmax(good))
+    assert s[3] == top and s[4] == top          # p <= 0 keeps only the maximum
+
+
+# ----------------------------------------------------------------------------
+# edge shapes: tiny vocabularies, ragged tiles, unaligned rows (token-exact)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 64, 2047, 2049, 4099, 10001])
+def test_edge_vocab_sizes_token_exact(V):
+    rng = np.random.default_rng(V)
+    rows = 3
+    probs = rng.dirichlet(np.full(V, 0.5), size=rows).astype(np.float32)
+    probs[0, ::3] = 0.0                         # zeros inside the row
+    if not probs[0].any():
+        probs[0, 0] = 1.0
+    buf = np.zeros(rows * V + 1, dtype=np.float32)
+    buf[1:] = probs.reshape(-1)
+    Pbuf = gpu(buf)
+    P = Pbuf[1:].view(rows, V)                  # misaligned by 4 bytes
+    P2 = gpu(probs)
+    n = 24
+    idx = (np.arange(n) % rows).astype(np.int32)
+    k = max(1, V // 3)
+    prm = _scalar_params(k=k, p=0.7, mp=0.2)
+    for Pt in (P, P2):
+        s = host(dss.sampling_from_probs(Pt, indices=gpu(idx), seed=9, offset=1))
+        tables = [ref.CdfTable(r_, r_ > 0) for r_ in probs]
+        assert [tables[idx[i]].draw(ph.draw_bits53(9, 1, i, 0)) for i in range(n)] == list(s)
+        for op in ("top_k", "top_p", "min_p", "top_k_top_p"):
+            s, r = OPS[op](Pt, prm, indices=gpu(idx), seed=9, offset=1, return_rounds=True,
+                           flags=dss.DSS_FLAG_FROM_ZERO)
+            s, r = host(s), host(r)
+            for i in range(n):
+                tok, rounds = ref.dual_pivot_sample(probs[idx[i]], op, ph.Stream(9, 1, i),
+                                                    **_oracle_kw(op, prm))
+                assert (s[i], r[i]) == (tok, rounds), (V, op, i)
+
+
+def test_parameter_extremes_support():
+    """k = 1 (greedy set), k >= V, p = 1, min_p = 0 and 1, per-output arrays."""
+    rng = np.random.default_rng(77)
+    V = 3000
+    probs = rng.dirichlet(np.full(V, 0.3), size=4).astype(np.float32)
+    probs[2, :10] = probs[2].max()              # ties at the maximum
+    P = gpu(probs)
+    n = 400
+    idx = (np.arange(n) % 4).astype(np.int32)
+    cases = [("top_k", {"k": 1}), ("top_k", {"k": V}), ("top_k", {"k": 10 * V}),
+             ("top_p", {"p": 1.0}), ("top_p", {"p": 0.0}), ("min_p", {"mp": 0.0}),
+             ("min_p", {"mp": 1.0}), ("top_k_top_p", {"k": V, "p": 1.0}),
+             ("top_k_top_p", {"k": 1, "p": 0.5})]
+    for op, kv in cases:
+        prm = _scalar_params()
+        prm.update({kk: (np.float32(vv) if kk != "k" else vv) for kk, vv in kv.items()})
+        for flags in FLAG_SETS:
+            s, v = OPS[op](P, prm, indices=gpu(idx), seed=3, return_valid=True, flags=flags)
+            s, v = host(s), host(v)
+            assert (v == 1).all()
+            for row in range(4):
+                _, tau = ref.threshold(probs[row], op, **_oracle_kw(op, prm))
+                sup = ref.support_mask(probs[row], tau)
+                assert sup[s[idx == row]].all(), (op, kv, flags, row)
+
+
+# ----------------------------------------------------------------------------
+# RNG ownership, replay, determinism, graph replay
+# ----------------------------------------------------------------------------
+
+def test_replay_offsets_and_batch_reorder():
+    w = si.renorm(rows=16, vocab=32000)
+    P = gpu(w["probs"])
+    k, p = gpu(w["top_k"]), gpu(w["top_p"])
+    seeds = w["seeds"]
+    a = host(dss.top_k_top_p_sampling_from_probs(P, k, p, seed=u64(seeds), offset=5))
+    for _ in range(5):
+        b = host(dss.top_k_top_p_sampling_from_probs(P, k, p, seed=u64(seeds), offset=5))
+        assert np.array_equal(a, b)
+    c = host(dss.top_k_top_p_sampling_from_probs(P, k, p, seed=u64(seeds), offset=6))
+    assert not np.array_equal(a, c)
+    perm = np.random.default_rng(1).permutation(16).astype(np.int32)
+    d = host(dss.top_k_top_p_sampling_from_probs(
+        P, gpu(w["top_k"][perm]), gpu(w["top_p"][perm]), indices=gpu(perm),
+        seed=u64(seeds[perm]), offset=5))
+    assert np.array_equal(d, a[perm])
+
+
+def test_graph_capture_with_device_offsets():
+    w = si.renorm(rows=8, vocab=32000)
+    P = gpu(w["probs"])
+    k, p = gpu(w["top_k"]), gpu(w["top_p"])
+    seeds = u64(w["seeds"])
+    offs = u64(np.zeros(8, dtype=np.uint64))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dss.top_k_top_p_sampling_from_probs(P, k, p, seed=seeds, offset=offs)  # warm-up
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            out = dss.top_k_top_p_sampling_from_probs(P, k, p, seed=seeds, offset=offs)
+    for step in range(1, 6):
+        offs.copy_(u64(np.full(8, step, dtype=np.uint64)))
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = dss.top_k_top_p_sampling_from_probs(P, k, p, seed=seeds,
+                                                    offset=u64(np.full(8, step, np.uint64)))
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), step
