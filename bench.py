@@ -86,7 +86,9 @@ def main():
     seeds = torch.from_numpy(w["seeds"].view(np.int64)).to(dev)
     samples = torch.empty(B, dtype=torch.int32, device=dev)
     lib = dss._lib.load()
-    assert lib.dss_workspace_size(4, B, V, B, flags) == 0
+    ws_bytes = lib.dss_workspace_size(dss.OP_IDS["top_k_top_p_sampling_from_probs"], B, V, B,
+                                      flags)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # zero-filled once
     fn = lib.dss_top_k_top_p_sampling_from_probs
     stream = torch.cuda.current_stream(dev).cuda_stream
     ptrs = [b.data_ptr() for b in bufs]
@@ -94,7 +96,8 @@ def main():
     def launch(i):
         # the C ABI directly: per-row seed array, scalar offset i (new stream per call)
         st = fn(ptrs[i % nbuf], B, V, None, B, seeds.data_ptr(), 0, None, i, k.data_ptr(), 0,
-                p.data_ptr(), 0.0, samples.data_ptr(), None, None, flags, None, 0, stream)
+                p.data_ptr(), 0.0, samples.data_ptr(), None, None, flags, ws.data_ptr(),
+                ws_bytes, stream)
         if st != 0:
             raise RuntimeError(dss._lib.strerror(st))
 
@@ -152,7 +155,7 @@ def main():
         "config": {
             "workload": "fused top_k_top_p_sampling_from_probs, B=64, V=151936, fp32 "
                         "softmax(N(0,2^2)), per-row top_k~U{1..1024}, top_p~U[0.5,0.95]",
-            "batch": B, "vocab": V, "engine": args.engine,
+            "batch": B, "vocab": V, "engine": args.engine, "workspace_bytes": ws_bytes,
             "cache": "warm (1 buffer)" if args.warm_cache else f"cold ({nbuf} rotating buffers)",
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -6,7 +6,6 @@
 #include <cmath>
 #include <cstring>
 
-#include "../../include/dss.h"
 #include "dss_internal.h"
 
 #define DSS_EXPORT extern "C" __attribute__((visibility("default")))
@@ -45,6 +44,8 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   if (!indices && num_outputs != rows) return DSS_ERR_INVALID_ARG;
   if (num_outputs == 0) return DSS_OK;
   if (!probs || !samples) return DSS_ERR_INVALID_ARG;
+  const int vec_ok = (vocab % 4 == 0) && aligned16(probs);
+  const dss::SplitPlan plan = dss::plan_split(op, rows, vocab, num_outputs, flags, vec_ok);
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   const int dev = check_device();
@@ -69,8 +70,10 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.samples = samples;
   p.valid = valid;
   p.rounds = rounds;
-  p.vec_ok = (vocab % 4 == 0) && aligned16(probs);
-  const hipError_t e = dss::launch_stream_sample(op, p, static_cast<hipStream_t>(stream));
+  p.vec_ok = vec_ok;
+  const hipError_t e =
+      plan.W > 0 ? dss::launch_split_sample(op, p, plan, workspace, static_cast<hipStream_t>(stream))
+                 : dss::launch_stream_sample(op, p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
@@ -197,12 +200,10 @@ DSS_EXPORT int dss_top_k_mask_logits(const float* logits, float* out, int32_t ro
 
 DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                                      int32_t num_outputs, uint32_t flags) {
-  (void)op;
-  (void)rows;
-  (void)vocab;
-  (void)num_outputs;
-  (void)flags;
-  return 0;
+  // sized for 16-byte aligned rows; an unaligned call runs the streaming
+  // engine, which needs none
+  if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || vocab <= 0 || num_outputs <= 0) return 0;
+  return dss::plan_split(op, rows, vocab, num_outputs, flags, vocab % 4 == 0).workspace;
 }
 
 DSS_EXPORT const char* dss_strerror(int32_t status) {

@@ -1,9 +1,10 @@
 // Device primitives for the gfx950 sampling kernels: wave64 reductions and
 // scans, the Philox4x64-10 generator, float32 order keys.
 //
-// Reductions use xor-butterflies, so every lane of a wave ends with the same
-// bits, and cross-wave combinations run in a fixed order through LDS: all
-// results are deterministic run to run (no floating-point atomics).
+// Wave reductions and scans run on DPP lane shifts with a fixed association
+// order, so every lane of a wave ends with the same bits, and cross-wave
+// combinations run in a fixed order through LDS: all results are
+// deterministic run to run (no floating-point atomics).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,47 +17,98 @@ constexpr int kBlock = 1024;
 constexpr int kWaves = kBlock / kWave;
 
 // ---------------------------------------------------------------------------
-// wave64 collectives
+// wave64 collectives on DPP (data-parallel primitives of GFX9)
 // ---------------------------------------------------------------------------
+//
+// An inclusive scan over the 64 lanes is four row shifts inside each row of
+// 16 lanes (row_shr:1,2,4,8) followed by two row broadcasts (row_bcast:15 into
+// rows 1 and 3, row_bcast:31 into rows 2 and 3); a reduction is the scan's
+// last lane read back as a scalar.  All lanes of a wave therefore agree
+// bit for bit, and the association order is fixed.  No LDS traffic.
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+namespace dpp {
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kWaveShr1 = 0x138;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// lanes whose DPP source is out of range or masked off receive `fill`
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t mov(uint32_t v, uint32_t fill) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double mov(double v, double fill) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v), f = (uint64_t)__double_as_longlong(fill);
+  const uint32_t lo = mov<CTRL, ROWS>((uint32_t)b, (uint32_t)f);
+  const uint32_t hi = mov<CTRL, ROWS>((uint32_t)(b >> 32), (uint32_t)(f >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+}  // namespace dpp
+
+struct OpSum {
+  template <class T> __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+struct OpMin {
+  __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+
+template <class T, class Op>
+__device__ __forceinline__ T wave_incl_scan(T v, T identity, Op op) {
+  v = op(v, dpp::mov<dpp::kRowShr1, 0xF>(v, identity));
+  v = op(v, dpp::mov<dpp::kRowShr2, 0xF>(v, identity));
+  v = op(v, dpp::mov<dpp::kRowShr4, 0xF>(v, identity));
+  v = op(v, dpp::mov<dpp::kRowShr8, 0xF>(v, identity));
+  v = op(v, dpp::mov<dpp::kRowBcast15, 0xA>(v, identity));
+  v = op(v, dpp::mov<dpp::kRowBcast31, 0xC>(v, identity));
   return v;
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+__device__ __forceinline__ double lane63(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, kWave - 1);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), kWave - 1);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Inclusive prefix sum across the 64 lanes.  Floating-point rounding can make
+// neighbouring prefixes non-monotone; callers that locate a token guard
+// against that explicitly.
+__device__ __forceinline__ double wave_incl_scan(double v) { return wave_incl_scan(v, 0.0, OpSum()); }
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) { return wave_incl_scan(v, 0u, OpSum()); }
+
+// Exclusive prefix: the inclusive prefix of the previous lane (0 in lane 0).
+__device__ __forceinline__ double wave_excl_from_incl(double incl) {
+  return dpp::mov<dpp::kWaveShr1, 0xF>(incl, 0.0);
+}
+
+// Value of lane `l` (wave-uniform) in every lane.
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ int lane_value(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ double lane_value(double v, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_sum(double v) { return lane63(wave_incl_scan(v)); }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return lane63(wave_incl_scan(v)); }
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor(v, m, kWave));
-  return v;
+  return lane63(wave_incl_scan(v, 0u, OpMax()));
 }
-
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor(v, m, kWave));
-  return v;
-}
-
-// Inclusive prefix sum across the 64 lanes (Hillis-Steele).  Floating-point
-// rounding can make neighbouring prefixes non-monotone; callers that locate a
-// token guard against that explicitly.
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    double y = __shfl_up(v, d, kWave);
-    if (lane >= d) v += y;
-  }
-  return v;
+  return lane63(wave_incl_scan(v, 0xFFFFFFFFu, OpMin()));
 }
 
 // ---------------------------------------------------------------------------

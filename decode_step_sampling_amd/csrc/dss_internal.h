@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dss.h"
+
 namespace dss {
 
 // Filter ids used as template parameters by the sampling kernels.
@@ -60,5 +62,19 @@ struct RenormParams {
 // pass reads the row from global memory.  Returns a hipError_t.
 hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s);
 hipError_t launch_stream_renorm(int kind, const RenormParams& p, hipStream_t s);
+
+// Split-row engine (top-k and top-k-then-top-p sampling): W work-groups per
+// output on one XCD, one HBM read of the row, candidates handed to the last
+// work-group through the caller's workspace.  W == 0 means "not eligible".
+struct SplitPlan {
+  int W;             // slices per output
+  int L;             // slice length (values, multiple of 4)
+  int nv;            // 16-byte loads per thread per slice
+  int chunk;         // outputs per launch
+  size_t workspace;  // bytes of workspace needed
+};
+SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flags, int vec_ok);
+hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& plan,
+                               void* workspace, hipStream_t s);
 
 }  // namespace dss

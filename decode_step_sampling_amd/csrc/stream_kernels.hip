@@ -17,468 +17,17 @@
 // tile with eight coalesced 16-byte loads per lane.  Every pivot pass leaves
 // the mass above each pivot per tile in LDS, so the next round's
 // inverse-transform draw scans the tile masses (one wave) and then one tile.
-#include "dss_device.h"
-#include "dss_internal.h"
+#include "stream_device.h"
 
 namespace dss {
 namespace {
 
-constexpr int kTile = 2048;
-constexpr int kTileChunks = kTile / (kWave * 4);  // 8 float4 per lane
-constexpr int kMaxTiles = (1 << 20) / kTile;      // vocab <= 2^20
-constexpr int kPreDraws = 4 * kWave;              // draws precomputed per output
-constexpr int kMaxRounds = 4096;                  // safety bound, never reached
-
-struct RowRef {
-  const float* x;
-  int V;
-  bool vec;
-};
-
-__device__ __forceinline__ void load4(const RowRef& r, int64_t idx, float (&v)[4]) {
-  if (r.vec && idx + 3 < r.V) {
-    const float4 q = *reinterpret_cast<const float4*>(r.x + idx);
-    v[0] = q.x;
-    v[1] = q.y;
-    v[2] = q.z;
-    v[3] = q.w;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (idx + e < r.V) ? r.x[idx + e] : 0.0f;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// block-wide reduction of a small record; every thread gets the same result
-// ---------------------------------------------------------------------------
-
-struct Red {
-  double d0, d1;
-  uint32_t s0, s1, mn, mx;
-};
-
-struct RedSmem {
-  double d[kWaves][2];
-  uint32_t u[kWaves][4];
-};
-
-__device__ Red block_reduce(Red v, RedSmem& sm) {
-  v.d0 = wave_sum(v.d0);
-  v.d1 = wave_sum(v.d1);
-  v.s0 = wave_sum(v.s0);
-  v.s1 = wave_sum(v.s1);
-  v.mn = wave_min(v.mn);
-  v.mx = wave_max(v.mx);
-  if (lane_id() == 0) {
-    const int w = wave_id();
-    sm.d[w][0] = v.d0;
-    sm.d[w][1] = v.d1;
-    sm.u[w][0] = v.s0;
-    sm.u[w][1] = v.s1;
-    sm.u[w][2] = v.mn;
-    sm.u[w][3] = v.mx;
-  }
-  __syncthreads();
-  Red out{0.0, 0.0, 0u, 0u, 0xFFFFFFFFu, 0u};
-  for (int w = 0; w < kWaves; ++w) {  // fixed order: deterministic
-    out.d0 += sm.d[w][0];
-    out.d1 += sm.d[w][1];
-    out.s0 += sm.u[w][0];
-    out.s1 += sm.u[w][1];
-    out.mn = min(out.mn, sm.u[w][2]);
-    out.mx = max(out.mx, sm.u[w][3]);
-  }
-  __syncthreads();
-  return out;
-}
-
-__device__ __forceinline__ Red red_zero() { return Red{0.0, 0.0, 0u, 0u, 0xFFFFFFFFu, 0u}; }
-
-// ---------------------------------------------------------------------------
-// threshold search on order keys (F4 note §②-③, §⑤)
-// ---------------------------------------------------------------------------
-//
-// Finds the largest key t with crit(t), where crit is count(key >= t) >= k
-// (MASS = false) or mass(key >= t) >= pz (MASS = true).  Invariant: crit(lo)
-// holds and crit(hi) fails.  Each pass evaluates crit at two pivots (1/3 and
-// 2/3 of [lo, hi)) and records the smallest key >= lo and the largest key
-// < hi; those two are themselves a satisfying and (plus one) a failing point,
-// and when they coincide only one distinct value is left: it is the answer.
-// KEYS selects signed-order keys (logits) instead of raw bits (x >= 0).
-template <bool MASS, bool KEYS>
-__device__ uint32_t threshold_search(const RowRef& r, uint32_t lo, uint32_t hi, uint32_t k,
-                                     double pz, RedSmem& sm) {
-  const int nvec = (r.V + 3) / 4;
-  while (hi - lo > 1u) {
-    const uint32_t d = hi - lo;
-    const uint32_t p1 = lo + max(1u, d / 3u);
-    const uint32_t p2 = lo + max(1u, (d / 3u) * 2u);
-    Red acc = red_zero();
-    for (int f = threadIdx.x; f < nvec; f += kBlock) {
-      const int64_t idx = 4ll * f;
-      float v[4];
-      load4(r, idx, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (idx + e >= r.V) continue;
-        const uint32_t key = KEYS ? signed_key(v[e]) : bits_of(v[e]);
-        if (key >= p1) {
-          acc.s0 += 1u;
-          if (MASS) acc.d0 += (double)v[e];
-        }
-        if (key >= p2) {
-          acc.s1 += 1u;
-          if (MASS) acc.d1 += (double)v[e];
-        }
-        if (key >= lo) acc.mn = min(acc.mn, key);
-        if (key < hi) acc.mx = max(acc.mx, key);
-      }
-    }
-    const Red t = block_reduce(acc, sm);
-    if (t.mn > t.mx) break;  // no value in [lo, hi): cannot happen; keep lo
-    if (t.mn == t.mx) return t.mn;
-    uint32_t nlo = t.mn, nhi = t.mx + 1u;
-    const bool ok1 = MASS ? (t.d0 >= pz) : (t.s0 >= k);
-    const bool ok2 = MASS ? (t.d1 >= pz) : (t.s1 >= k);
-    if (ok2) {
-      nlo = max(nlo, p2);
-    } else if (ok1) {
-      nlo = max(nlo, p1);
-      nhi = min(nhi, p2);
-    } else {
-      nhi = min(nhi, p1);
-    }
-    lo = nlo;
-    hi = nhi;
-  }
-  return lo;
-}
-
-// mass and count of {bits >= tau} (x >= 0)
-__device__ Red mass_at_least(const RowRef& r, uint32_t tau, RedSmem& sm) {
-  const int nvec = (r.V + 3) / 4;
-  Red acc = red_zero();
-  for (int f = threadIdx.x; f < nvec; f += kBlock) {
-    const int64_t idx = 4ll * f;
-    float v[4];
-    load4(r, idx, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (idx + e < r.V && bits_of(v[e]) >= tau) {
-        acc.d0 += (double)v[e];
-        acc.s0 += 1u;
-      }
-    }
-  }
-  return block_reduce(acc, sm);
-}
-
-__device__ __forceinline__ float clamp01(float v) { return fminf(fmaxf(v, 0.0f), 1.0f); }
-
-// ---------------------------------------------------------------------------
-// sampling
-// ---------------------------------------------------------------------------
-
-struct SampleSmem {
-  double tm[3][kMaxTiles];  // per-tile mass above: current low, pivot a, pivot b
-  double draws[kPreDraws];
-  RedSmem red;
-  double bc_d[2];
-  double extra_u;
-  int bc_tok;
-};
-
-// Sum of tm[0..n) in exactly the order the tile search of locate() uses, so
-// that S(low) computed here is the last prefix that search sees.  One wave.
-__device__ double tile_scan_total(const double* tm, int n) {
-  double carry = 0.0;
-  for (int base = 0; base < n; base += kWave) {
-    const int t = base + lane_id();
-    const double m = t < n ? tm[t] : 0.0;
-    const double incl = wave_incl_scan(m) + carry;
-    carry = __shfl(incl, kWave - 1, kWave);
-  }
-  return carry;
-}
-
-// Inverse-transform draw over the candidates {x > low} (blog, 逆变换采样;
-// explainer, "不带过滤时"): the first index j, in index order, whose
-// inclusive candidate prefix exceeds T.  Tiles first (tm = mass above low per
-// tile), then the one tile.  Guards (blog, 实现细节: a parallel prefix sum of
-// non-negative values need not be monotone): only candidates with nonzero
-// mass can be selected; the first hit in index order wins; if rounding puts T
-// at or past the scanned total, the last candidate is taken.  Wave 0 works,
-// the result is broadcast; every thread must call this.
-__device__ int locate(const RowRef& r, const double* tm, int n_tiles, double T, float low,
-                      SampleSmem& sm) {
-  if (wave_id() == 0) {
-    const int lane = lane_id();
-    double carry = 0.0, excl_hit = 0.0, excl_last = 0.0;
-    int tile = -1, last_nz = -1;
-    for (int base = 0; base < n_tiles; base += kWave) {
-      const int t = base + lane;
-      const double m = t < n_tiles ? tm[t] : 0.0;
-      const double incl = wave_incl_scan(m) + carry;
-      const double excl = incl - m;
-      const uint64_t hit = __ballot(m > 0.0 && incl > T);
-      const uint64_t nz = __ballot(m > 0.0);
-      if (nz) {
-        const int l = 63 - __clzll((long long)nz);
-        last_nz = base + l;
-        excl_last = __shfl(excl, l, kWave);
-      }
-      if (hit) {
-        const int l = __ffsll((long long)hit) - 1;
-        tile = base + l;
-        excl_hit = __shfl(excl, l, kWave);
-        break;
-      }
-      carry = __shfl(incl, kWave - 1, kWave);
-    }
-    double Tl = T - excl_hit;
-    if (tile < 0) {
-      tile = last_nz;
-      Tl = T - excl_last;
-    }
-    int found = -1;
-    if (tile >= 0) {
-      const int64_t tbase = (int64_t)tile * kTile;
-      double run_carry = 0.0;
-      int last_cand = -1;
-      for (int q = 0; q < kTileChunks; ++q) {
-        const int64_t idx = tbase + q * (kWave * 4) + lane * 4;
-        float v[4];
-        load4(r, idx, v);
-        double s = 0.0;
-        bool cand[4];
-        int my_last = -1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          cand[e] = (idx + e < r.V) && (v[e] > low);
-          if (cand[e]) {
-            s += (double)v[e];
-            my_last = (int)(idx + e);
-          }
-        }
-        const double incl = wave_incl_scan(s);
-        double excl = __shfl_up(incl, 1, kWave);
-        if (lane == 0) excl = 0.0;
-        double run = run_carry + excl;
-        int hit_e = -1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (cand[e]) {
-            run += (double)v[e];
-            if (hit_e < 0 && run > Tl) hit_e = e;
-          }
-        }
-        const uint64_t hm = __ballot(hit_e >= 0);
-        if (hm) {
-          const int l = __ffsll((long long)hm) - 1;
-          const int e = __shfl(hit_e, l, kWave);
-          found = (int)(tbase + q * (kWave * 4) + l * 4 + e);
-          break;
-        }
-        const uint64_t cm = __ballot(my_last >= 0);
-        if (cm) last_cand = __shfl(my_last, 63 - __clzll((long long)cm), kWave);
-        run_carry += __shfl(incl, kWave - 1, kWave);
-      }
-      if (found < 0) found = last_cand;
-    }
-    if (lane == 0) sm.bc_tok = found;
-  }
-  __syncthreads();
-  const int tok = sm.bc_tok;
-  __syncthreads();
-  return tok;
-}
-
-// One (mass, count) pass at pivots a <= b: per-tile masses above each pivot
-// into tma / tmb, per-lane counts of values above each pivot.
-__device__ void pivot_pass(const RowRef& r, int n_tiles, float a, float b, double* tma,
-                           double* tmb, uint32_t& ca, uint32_t& cb) {
-  const int lane = lane_id();
-  for (int t = wave_id(); t < n_tiles; t += kWaves) {
-    const int64_t base = (int64_t)t * kTile;
-    double sa = 0.0, sb = 0.0;
-#pragma unroll
-    for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
-      load4(r, base + q * (kWave * 4) + lane * 4, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // padding past the row end reads as 0, never above a pivot >= 0
-        if (v[e] > a) {
-          sa += (double)v[e];
-          ca += 1u;
-        }
-        if (v[e] > b) {
-          sb += (double)v[e];
-          cb += 1u;
-        }
-      }
-    }
-    sa = wave_sum(sa);
-    sb = wave_sum(sb);
-    if (lane == 0) {
-      tma[t] = sa;
-      tmb[t] = sb;
-    }
-  }
-}
-
-// f(t) of the blog's dual-pivot section: 1 iff threshold t already
-// satisfies the filter.  Top-k counts the values above t, top-p compares
-// their mass with p * Z_C (Z_C = row or top-k mass), min-p compares t with
-// min_p * max; "count == 0" makes f(max) = 1 also for p = 0.
-template <int OP>
-__device__ __forceinline__ bool predicate(float t, double mass_above, uint32_t count_above,
-                                          int k, double pz, double minp_thr) {
-  if (OP == kOpNone) return true;
-  if (OP == kOpMinP) return (double)t >= minp_thr;
-  const bool ok_k = (OP == kOpTopP) ? true : (count_above < (uint32_t)k);
-  if (OP == kOpTopK) return ok_k;
-  const bool ok_p = (mass_above < pz) || count_above == 0u;
-  return ok_k && ok_p;
-}
-
-__device__ __forceinline__ void write_sample(const SampleParams& P, int i, int tok, int rounds) {
-  P.samples[i] = tok;
-  if (P.valid) P.valid[i] = tok >= 0 ? 1 : 0;
-  if (P.rounds) P.rounds[i] = rounds;
-}
+using namespace stream;
 
 template <int OP>
 __global__ __launch_bounds__(kBlock) void stream_sample_kernel(SampleParams P) {
   __shared__ SampleSmem sm;
-  const int i = blockIdx.x;
-  const int lane = lane_id();
-  const int wave = wave_id();
-
-  const int row = P.indices ? P.indices[i] : i;
-  const int k = P.top_k_arr ? P.top_k_arr[i] : P.top_k;
-  const float pp = P.top_p_arr ? P.top_p_arr[i] : P.top_p;
-  const float mp = P.min_p_arr ? P.min_p_arr[i] : P.min_p;
-  bool ok = row >= 0 && row < P.rows;
-  if (OP == kOpTopK || OP == kOpTopKTopP) ok = ok && k > 0;
-  if (OP == kOpTopP || OP == kOpTopKTopP) ok = ok && !isnan(pp);
-  if (OP == kOpMinP) ok = ok && !isnan(mp);
-  if (!ok) {  // block-uniform
-    if (threadIdx.x == 0) write_sample(P, i, -1, 0);
-    return;
-  }
-  const uint64_t seed = P.seed_arr ? P.seed_arr[i] : P.seed;
-  const uint64_t offset = P.offset_arr ? P.offset_arr[i] : P.offset;
-  const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
-  if (wave == 0) {
-    if (OP == kOpNone) {
-      if (lane == 0) sm.draws[0] = draw_uniform(seed, offset, sid, 0u);
-    } else {
-      const Philox4x64 b = philox4x64_10(offset, sid, (uint64_t)lane, 0ull, seed, 0ull);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.draws[4 * lane + e] = (double)(b.w[e] >> 11) * 0x1p-53;
-    }
-  }
-
-  const RowRef r{P.probs + (int64_t)row * P.vocab, P.vocab, P.vec_ok != 0};
-  const int n_tiles = (P.vocab + kTile - 1) / kTile;
-
-  // pass 0: tile masses (mass above low = 0), max bits, validity
-  uint32_t mbits = 0u;
-  for (int t = wave; t < n_tiles; t += kWaves) {
-    const int64_t base = (int64_t)t * kTile;
-    double s = 0.0;
-#pragma unroll
-    for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
-      load4(r, base + q * (kWave * 4) + lane * 4, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mbits = max(mbits, bits_of(v[e]));
-        s += (double)v[e];
-      }
-    }
-    s = wave_sum(s);
-    if (lane == 0) sm.tm[0][t] = s;
-  }
-  Red red0 = red_zero();
-  red0.mx = mbits;
-  const uint32_t maxbits = block_reduce(red0, sm.red).mx;
-  if (wave == 0) {
-    const double z = tile_scan_total(sm.tm[0], n_tiles);
-    if (lane == 0) sm.bc_d[0] = z;
-  }
-  __syncthreads();
-  const double Z = sm.bc_d[0];
-  __syncthreads();
-  // sign bit, inf or NaN anywhere, or nothing positive: invalid row
-  if (maxbits >= 0x7F800000u || !(Z > 0.0)) {
-    if (threadIdx.x == 0) write_sample(P, i, -1, 0);
-    return;
-  }
-  const float M = __uint_as_float(maxbits);
-
-  double zc = Z;
-  if (OP == kOpTopKTopP && k < P.vocab) {
-    const uint32_t tau_k = threshold_search<false, false>(r, 0u, maxbits + 1u, (uint32_t)k, 0.0, sm.red);
-    zc = mass_at_least(r, tau_k, sm.red).d0;
-  }
-  const double pz = (OP == kOpTopP || OP == kOpTopKTopP) ? (double)clamp01(pp) * zc : 0.0;
-  const double minp_thr = (OP == kOpMinP) ? (double)clamp01(mp) * (double)M : 0.0;
-
-  float low = 0.0f, high = M;
-  double S = Z;
-  int cur = 0, rnd = 0, token = -1;
-  while (true) {
-    double u;
-    if (rnd < kPreDraws) {
-      u = sm.draws[rnd];
-    } else {
-      if (threadIdx.x == 0) sm.extra_u = draw_uniform(seed, offset, sid, (uint32_t)rnd);
-      __syncthreads();
-      u = sm.extra_u;
-      __syncthreads();
-    }
-    ++rnd;
-    token = locate(r, sm.tm[cur], n_tiles, u * S, low, sm);
-    if (OP == kOpNone || token < 0) break;
-    const float pivot1 = r.x[token];
-    const float pivot2 = (float)(((double)pivot1 + (double)high) * 0.5);
-    const int ia = (cur + 1) % 3, ib = (cur + 2) % 3;
-    uint32_t ca = 0u, cb = 0u;
-    pivot_pass(r, n_tiles, pivot1, pivot2, sm.tm[ia], sm.tm[ib], ca, cb);
-    Red cr = red_zero();
-    cr.s0 = ca;
-    cr.s1 = cb;
-    cr = block_reduce(cr, sm.red);
-    if (wave == 0) {
-      const double ma = tile_scan_total(sm.tm[ia], n_tiles);
-      const double mb = tile_scan_total(sm.tm[ib], n_tiles);
-      if (lane == 0) {
-        sm.bc_d[0] = ma;
-        sm.bc_d[1] = mb;
-      }
-    }
-    __syncthreads();
-    const double Ma = sm.bc_d[0], Mb = sm.bc_d[1];
-    __syncthreads();
-    if (predicate<OP>(pivot1, Ma, cr.s0, k, pz, minp_thr)) break;  // accept
-    if (predicate<OP>(pivot2, Mb, cr.s1, k, pz, minp_thr)) {
-      low = pivot1;
-      high = pivot2;
-      S = Ma;
-      cur = ia;
-    } else {
-      low = pivot2;
-      S = Mb;
-      cur = ib;
-    }
-    if (rnd >= kMaxRounds) {
-      token = -1;
-      break;
-    }
-  }
-  if (threadIdx.x == 0) write_sample(P, i, token, token >= 0 ? rnd : 0);
+  sample_row<OP>(P, blockIdx.x, sm);
 }
 
 // ---------------------------------------------------------------------------

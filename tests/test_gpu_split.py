@@ -1,0 +1,143 @@
+"""GPU tests aimed at the split-row engine (top-k and top-k-then-top-p).
+
+The engine reads each row once across W work-groups, hands the candidates
+to the last one and runs the rejection loop there; it falls back to the
+streaming engine when candidates overflow or k is above its cap.  Each test
+picks shapes that force one of those paths and checks draws against the
+oracle's kept set and distribution.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_step_sampling_amd as dss
+import synthetic_inputs as si
+from oracle import reference as ref
+from gpu_util import gpu, host, pooled_chi_square, u64
+
+pytestmark = pytest.mark.gpu
+
+
+def _supports(probs, op, ks, ps):
+    out = []
+    for r in range(probs.shape[0]):
+        k = ks[r] if np.ndim(ks) else ks
+        p = ps[r] if np.ndim(ps) else ps
+        valid, tau = ref.threshold(probs[r], op, k=k, p=p)
+        out.append(ref.support_mask(probs[r], tau) if valid else None)
+    return out
+
+
+def _call(op, P, k, p, **kw):
+    if op == "top_k":
+        return dss.top_k_sampling_from_probs(P, k, **kw)
+    return dss.top_k_top_p_sampling_from_probs(P, k, p, **kw)
+
+
+@pytest.mark.parametrize("op", ["top_k", "top_k_top_p"])
+@pytest.mark.parametrize("rows,vocab", [(64, 151936), (4, 32000), (1, 151936), (3, 8192)])
+def test_split_support_and_validity(op, rows, vocab):
+    w = si.renorm(rows=rows, vocab=vocab)
+    probs = w["probs"]
+    P = gpu(probs)
+    sup = _supports(probs, op, w["top_k"], w["top_p"])
+    k, p = gpu(w["top_k"]), gpu(w["top_p"])
+    seeds = u64(w["seeds"])
+    first = None
+    for call in range(30):
+        s, v, r = _call(op, P, k, p, seed=seeds, offset=call, return_valid=True,
+                        return_rounds=True)
+        s, v, r = host(s), host(v), host(r)
+        assert (v == 1).all() and (r >= 1).all()
+        for row in range(rows):
+            assert sup[row][s[row]], (op, rows, vocab, call, row)
+        if call == 0:
+            first = s
+    again = host(_call(op, P, k, p, seed=seeds, offset=0))
+    assert np.array_equal(first, again)             # deterministic replay
+
+
+@pytest.mark.parametrize("op", ["top_k", "top_k_top_p"])
+def test_split_chi_square_across_calls_w16(op):
+    """4 rows per call: 16 slices per row, so every draw crosses the hand-off."""
+    w = si.small()
+    probs = w["probs"]
+    rows, V = probs.shape
+    calls = 6000
+    k, p = 50, np.float32(0.9)
+    P = gpu(probs)
+    seeds = u64(np.array([7, 8, 9, 10], dtype=np.uint64))
+    out = torch.empty(calls, rows, dtype=torch.int32, device="cuda:0")
+    for t in range(calls):
+        out[t] = _call(op, P, k, p, seed=seeds, offset=t)
+    s = host(out)
+    for row in range(rows):
+        _, tau = ref.threshold(probs[row], op, k=k, p=p)
+        support = ref.support_mask(probs[row], tau)
+        assert support[s[:, row]].all()
+        counts = np.bincount(s[:, row], minlength=V)
+        pval, tvd, _ = pooled_chi_square(counts[support],
+                                         ref.target_distribution(probs[row], tau)[support])
+        assert pval > 1e-3, (op, row, pval, tvd)
+
+
+def test_split_adversarial_rows():
+    """Flat rows overflow the candidate buffers (streaming fallback); sorted
+    rows put the whole top-k in one slice; ties sit at the local bounds."""
+    V = 65536
+    rng = np.random.default_rng(5)
+    flat = (1.0 + rng.uniform(-1e-3, 1e-3, V)) / V
+    geo = (1.0 - 1e-4) ** np.arange(V, dtype=np.float64)
+    ties = np.repeat(rng.dirichlet(np.ones(V // 64)), 64)     # 64 copies of every value
+    peaked = np.full(V, 0.01 / (V - 1))
+    peaked[123] = 0.99
+    rows = np.stack([r / r.sum() for r in (flat, geo, ties, peaked)]).astype(np.float32)
+    P = gpu(rows)
+    for op in ("top_k", "top_k_top_p"):
+        for k, p in ((1, 0.5), (37, 0.9), (1000, 0.95), (1536, 0.3), (1537, 0.99), (V, 1.0)):
+            sup = _supports(rows, op, k, np.float32(p))
+            for n_out in (4, 64):           # few outputs: W > 1; many: more rows per call
+                idx = gpu((np.arange(n_out) % 4).astype(np.int32))
+                s, v = _call(op, P, k, np.float32(p), indices=idx, seed=k, offset=n_out,
+                             return_valid=True)
+                s, v = host(s), host(v)
+                assert (v == 1).all()
+                for o in range(n_out):
+                    assert sup[o % 4][s[o]], (op, k, p, n_out, o)
+
+
+def test_split_degenerate_rows():
+    V = 16384
+    rng = np.random.default_rng(9)
+    good = rng.dirichlet(np.ones(V)).astype(np.float32)
+    rows = np.stack([good] * 6)
+    rows[1, 9000] = np.nan
+    rows[2, 15] = -1e-6
+    rows[3] = 0.0
+    rows[4, 16383] = np.inf
+    P = gpu(rows)
+    for op in ("top_k", "top_k_top_p"):
+        for n_out in (6, 600):
+            idx = gpu((np.arange(n_out) % 6).astype(np.int32))
+            s, v = _call(op, P, 20, np.float32(0.8), indices=idx, seed=3, return_valid=True)
+            s, v = host(s), host(v)
+            expect = np.array([1, 0, 0, 0, 0, 1] * (n_out // 6))
+            assert np.array_equal(v, expect), (op, n_out)
+            assert (s[expect == 0] == -1).all() and (s[expect == 1] >= 0).all()
+
+
+def test_split_workspace_reuse_across_shapes():
+    """The arrival counters must be back at zero after every call."""
+    shapes = [(64, 151936), (2, 151936), (16, 50000), (64, 151936), (1, 200000)]
+    for rows, vocab in shapes:
+        w = si.renorm(rows=rows, vocab=vocab)
+        P = gpu(w["probs"])
+        sup = _supports(w["probs"], "top_k_top_p", w["top_k"], w["top_p"])
+        for call in range(3):
+            s, v = dss.top_k_top_p_sampling_from_probs(P, gpu(w["top_k"]), gpu(w["top_p"]),
+                                                       seed=u64(w["seeds"]), offset=call,
+                                                       return_valid=True)
+            s, v = host(s), host(v)
+            assert (v == 1).all()
+            assert all(sup[r][s[r]] for r in range(rows)), (rows, vocab, call)
