@@ -6,22 +6,29 @@
 // 拒绝采样器正确性的理论证明) holds from any starting pivot below every kept
 // value.  This engine therefore:
 //
-//  1. splits each row into W slices, one 1024-thread work-group per slice,
-//     and reads every slice from HBM exactly once into registers (16-byte
-//     loads);
-//  2. each slice finds a local bound t_s whose upper set holds at least k of
-//     its values, from a 2048-bin LDS histogram of the float32 bit patterns
-//     (bits >> 20: 1/8-binade bins) of the values within 8 binades of the
-//     slice maximum (all values if that is not enough), and publishes those
-//     few values with their indices.  The union over slices contains every
-//     value >= t* = max_s t_s of the row, and at least k of them;
+//  1. splits each row into W slices, one 1024-thread work-group per slice.
+//     Waves 1..15 read the slice from HBM exactly once into registers
+//     (16-byte loads, all issued up front); wave 0 clears the histogram and
+//     computes the row's first 256 Philox draws while the slice is in
+//     flight;
+//  2. from the first landed vector of every reading thread (3840 values) the
+//     slice takes a provisional bound: the edge of a 1/8-binade bin of the
+//     float32 bit patterns (bits >> 20) above which about 1.5 k + 64 of the
+//     slice's values should lie.  As each vector lands the reading waves
+//     append the values at or above that bound, with their indices, to
+//     per-wave LDS lists.  If the lists hold at least k values the bound
+//     stands (it is then at most the slice's k-th largest value); otherwise
+//     the slice is histogrammed in full and the exact 1/8-binade bound of
+//     its k-th largest value is used.  Each slice publishes its bound and
+//     its list.  The union over slices contains every value >= t* = max_s t_s
+//     of the row, and at least k of them;
 //  3. the last slice work-group of the row to finish (a relaxed arrival
-//     counter) gathers the candidates, finds the k-th largest tau_k with three
-//     histogram passes over the bit fields (the F4 note's threshold search on
-//     the float32 bit pattern, §③, done 2048 ways per pass instead of 2 or 3)
-//     and runs the dual-pivot loop on the candidates from just below tau_k,
-//     where f(low) = 0 still holds.  That tail runs on four waves, one per
-//     SIMD, so its serial steps are not shared four ways.
+//     counter) gathers the candidates into registers, finds the k-th largest
+//     tau_k with three histogram passes over the bit fields [30:20], [19:9]
+//     and [8:0] (the F4 note's threshold search on the float32 bit pattern,
+//     §③, done 2048 ways per pass instead of 2 or 3), compacts the values
+//     >= tau_k with their mass Z_k, and one wave runs the dual-pivot loop on
+//     them from just below tau_k, where f(low) = 0 still holds.
 //
 // All W work-groups of a row are placed on one XCD (work-groups are dispatched
 // to the eight XCDs round-robin, so block b runs on XCD b % 8), which lets the
@@ -36,15 +43,18 @@
 namespace dss {
 namespace {
 
+constexpr int kLoadWaves = kWaves - 1;             // waves 1..15 read the slice
+constexpr int kLoadThreads = kLoadWaves * kWave;   // 960
 constexpr int kHistBins = 2048;
+constexpr int kFineBins = 512;
 constexpr int kSliceCandMax = 4096;
-constexpr int kWaveCap = 512;  // per-wave append buffer during the read
+constexpr int kWaveCap = 512;  // per-wave append list during the read
 constexpr int kRowCandMax = 8192;
+constexpr int kPer = kRowCandMax / kBlock;  // gathered entries per thread
 constexpr int kSplitKCap = 1536;
 constexpr int kMaxSlices = 16;
 constexpr int kHdrWords = 8;
-constexpr int kTailWaves = 4;
-constexpr int kTailThreads = kTailWaves * kWave;
+constexpr uint32_t kNoList = 0xFFFFFFFFu;  // header count of a slice that published nothing
 
 struct SplitParams {
   int W;           // slices per output
@@ -57,32 +67,42 @@ struct SplitParams {
   uint64_t* cand;  // [n_out][W][kSliceCandMax]: bits | (index << 32)
 };
 
+// Histograms are stored in chunks of NB/64 bins (the bins one lane sums in
+// a search), each chunk padded by four words so that the 64 lanes' 16-byte
+// reads of their chunks fall in distinct LDS banks.
+template <int NB>
+struct Padded {
+  static constexpr int kChunk = NB / kWave;
+  static constexpr int kStride = kChunk + 4;
+  static constexpr int kWords = kWave * kStride;
+  static __device__ __forceinline__ uint32_t at(uint32_t b) { return b + 4u * (b / kChunk); }
+};
+using H1 = Padded<kHistBins>;
+using H3 = Padded<kFineBins>;
+
 struct SplitSmem {
   union {
+    uint64_t pw[kWaves][kWaveCap];  // per-wave appends during the read (bits | index << 32)
     struct {
-      uint32_t bits[kWaves][kWaveCap];
-      uint32_t idx[kWaves][kWaveCap];
-    } pw;                         // per-wave appends during the read
-    stream::SampleSmem stream;    // streaming fallback
+      alignas(16) uint32_t h2[H1::kWords];
+      alignas(16) uint32_t h3[H3::kWords];
+    } sel;                          // k-th largest, passes 2 and 3
+    stream::SampleSmem stream;      // streaming fallback
   } a;
-  struct {
-    uint32_t bits[kRowCandMax];
-    uint32_t idx[kRowCandMax];
-  } c;                            // candidates, compacted
-  uint32_t hist[kHistBins];
+  uint64_t cand[kRowCandMax];       // candidates (bits | index << 32)
+  alignas(16) uint32_t hist[H1::kWords];
   double draws[stream::kPreDraws];
-  double red_d[kWaves][2];
-  uint32_t red_u[kWaves][4];
+  double red_d[kWaves];
+  uint32_t red_u[kWaves];
   uint32_t wcnt[kWaves];
-  uint32_t hdr[kMaxSlices][kHdrWords];
+  uint32_t wmax[kWaves];
   uint32_t off[kMaxSlices + 1];
-  uint32_t gen;
-  int flag;
-  int hit_lane[kWaves];
-  int tok;
   uint32_t res[4];
-  double extra_u;
+  uint32_t fres[4];
+  uint32_t tprov;  // provisional bound | 1 once set (0 until then)
+  int flag;
 };
+static_assert(sizeof(SplitSmem) <= 160 * 1024, "LDS budget of one gfx950 work-group");
 
 __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
@@ -91,21 +111,29 @@ __device__ __forceinline__ uint32_t xcc_id() {
 // wave index as a scalar, so branches on it are scalar branches
 __device__ __forceinline__ int uwave() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+__device__ __forceinline__ int first_lane(uint64_t m) { return __ffsll((long long)m) - 1; }
+__device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll((long long)m); }
+
+template <int NB>
+__device__ __forceinline__ void clear_hist(uint32_t* h, int t, int nt) {
+  uint4* h4 = reinterpret_cast<uint4*>(h);
+  for (int q = t; q < Padded<NB>::kWords / 4; q += nt) h4[q] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // ---------------------------------------------------------------------------
-// work-group helpers over the first NW waves (every participating thread
-// must call; fixed association order, so results are deterministic)
+// work-group helpers (every thread of the work-group must call; fixed
+// association order, so results are deterministic)
 // ---------------------------------------------------------------------------
 
-template <int NW>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, SplitSmem& sm) {
   const int lane = lane_id(), w = uwave();
   const uint32_t incl = wave_incl_scan(v);
-  if (lane == kWave - 1) sm.red_u[w][0] = incl;
+  if (lane == kWave - 1) sm.red_u[w] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int q = 0; q < NW; ++q) {
-    const uint32_t t = sm.red_u[q][0];
+  for (int q = 0; q < kWaves; ++q) {
+    const uint32_t t = sm.red_u[q];
     base += q < w ? t : 0u;
     tot += t;
   }
@@ -114,130 +142,60 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, SplitSmem& sm) 
   return base + incl - v;
 }
 
-template <int NW>
-__device__ double block_excl_scan(double v, SplitSmem& sm) {
-  const int lane = lane_id(), w = uwave();
-  const double incl = wave_incl_scan(v);
-  const double excl = wave_excl_from_incl(incl);
-  if (lane == kWave - 1) sm.red_d[w][0] = incl;
-  __syncthreads();
-  double base = 0.0;
+// Largest bin b of the padded histogram hist (NB bins) whose suffix count
+// sum_{b' >= b} hist[b'] reaches need, the count strictly above b, and the
+// total (bin 0 and total - hist[0] if the total falls short).  One wave:
+// lane l sums the l-th chunk of bins from the top, a scan over the lanes
+// finds the chunk, a scan over that chunk's bins finds the bin.
+template <int NB>
+__device__ void wave_find(const uint32_t* hist, uint32_t need, uint32_t& bin, uint32_t& above,
+                          uint32_t& total) {
+  using H = Padded<NB>;
+  static_assert(H::kChunk % 4 == 0 && H::kChunk <= kWave, "chunk of whole 16-byte reads");
+  const int lane = lane_id();
+  const int chunk = kWave - 1 - lane;  // lane 0 holds the top chunk
+  uint32_t s = 0u;
 #pragma unroll
-  for (int q = 0; q < NW; ++q) base += q < w ? sm.red_d[q][0] : 0.0;
-  __syncthreads();
-  return base + excl;
+  for (int q = 0; q < H::kChunk; q += 4) {
+    const uint4 h = *reinterpret_cast<const uint4*>(hist + chunk * H::kStride + q);
+    s += h.x + h.y + h.z + h.w;
+  }
+  const uint32_t incl = wave_incl_scan(s);
+  total = lane63(incl);
+  const uint64_t m = __ballot(incl >= need);
+  if (m == 0ull) {
+    bin = 0u;
+    above = total - hist[0];
+    return;
+  }
+  const int L = first_lane(m);
+  const uint32_t excl_l = lane_value(incl - s, L);
+  const int c = kWave - 1 - L;
+  const uint32_t h = lane < H::kChunk ? hist[c * H::kStride + H::kChunk - 1 - lane] : 0u;
+  const uint32_t incl2 = excl_l + wave_incl_scan(h);
+  const int L2 = first_lane(__ballot(lane < H::kChunk && incl2 >= need));
+  bin = (uint32_t)(c * H::kChunk + H::kChunk - 1 - L2);
+  above = lane_value(incl2 - h, L2);
 }
 
-struct Pair {
-  double m0, m1;
-  uint32_t c0, c1;
-};
-
-template <int NW>
-__device__ Pair block_sum(Pair v, SplitSmem& sm) {
-  v.m0 = wave_sum(v.m0);
-  v.m1 = wave_sum(v.m1);
-  v.c0 = wave_sum(v.c0);
-  v.c1 = wave_sum(v.c1);
-  if (lane_id() == 0) {
-    const int w = uwave();
-    sm.red_d[w][0] = v.m0;
-    sm.red_d[w][1] = v.m1;
-    sm.red_u[w][0] = v.c0;
-    sm.red_u[w][1] = v.c1;
-  }
-  __syncthreads();
-  Pair out{0.0, 0.0, 0u, 0u};
-#pragma unroll
-  for (int q = 0; q < NW; ++q) {
-    out.m0 += sm.red_d[q][0];
-    out.m1 += sm.red_d[q][1];
-    out.c0 += sm.red_u[q][0];
-    out.c1 += sm.red_u[q][1];
-  }
-  __syncthreads();
-  return out;
-}
-
-template <int NW>
-__device__ uint32_t block_max(uint32_t v, SplitSmem& sm) {
-  v = wave_max(v);
-  if (lane_id() == 0) sm.red_u[uwave()][0] = v;
-  __syncthreads();
-  uint32_t out = 0;
-#pragma unroll
-  for (int q = 0; q < NW; ++q) out = max(out, sm.red_u[q][0]);
-  __syncthreads();
-  return out;
-}
-
-// Largest bin b of hist[0..nb) whose suffix count sum_{b' >= b} hist[b']
-// reaches need; returns b, the count strictly above b, and the total.  If
-// the total is below need, returns bin 0.  Thread t owns the bins
-// nb-1-t*BPT down to nb-(t+1)*BPT.
-template <int NW>
-__device__ void suffix_find(const uint32_t* hist, int nb, uint32_t need, uint32_t& bin,
-                            uint32_t& above, uint32_t& total, SplitSmem& sm) {
-  constexpr int T = NW * kWave;
-  const int bpt = (nb + T - 1) / T;
-  const int t = threadIdx.x;
-  const int top = nb - 1 - t * bpt;
-  uint32_t mine = 0u;
-  for (int q = 0; q < bpt; ++q) {
-    const int b = top - q;
-    if (b >= 0) mine += hist[b];
-  }
-  const uint32_t excl = block_excl_scan<NW>(mine, total, sm);
-  if (t == 0) {
-    sm.res[0] = 0u;
-    sm.res[1] = total - hist[0];
-  }
-  __syncthreads();
-  if (excl < need && excl + mine >= need) {
-    uint32_t run = excl;
-    for (int q = 0; q < bpt; ++q) {
-      const int b = top - q;
-      const uint32_t h = b >= 0 ? hist[b] : 0u;
-      if (run + h >= need) {
-        sm.res[0] = (uint32_t)b;
-        sm.res[1] = run;
-        break;
-      }
-      run += h;
+// The same, answered by wave 0 and handed to every thread.  The histogram
+// must be complete (a barrier before the call); consecutive calls must be
+// separated by a barrier.
+template <int NB>
+__device__ void block_find(const uint32_t* hist, uint32_t need, uint32_t& bin, uint32_t& above,
+                           uint32_t& total, SplitSmem& sm) {
+  if (uwave() == 0) {
+    wave_find<NB>(hist, need, bin, above, total);
+    if (lane_id() == 0) {
+      sm.fres[0] = bin;
+      sm.fres[1] = above;
+      sm.fres[2] = total;
     }
   }
   __syncthreads();
-  bin = sm.res[0];
-  above = sm.res[1];
-  __syncthreads();
-}
-
-// k-th largest bit pattern among bits[0..n) (1 <= k <= n; non-negative
-// floats, so bit 31 is clear): three histogram passes over bit fields
-// [30:20], [19:9] and [8:0], each keeping only the values that match the
-// bits fixed so far.
-template <int NW>
-__device__ uint32_t kth_largest(const uint32_t* bits, int n, uint32_t k, SplitSmem& sm) {
-  constexpr int T = NW * kWave;
-  uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = pass == 0 ? 20 : pass == 1 ? 9 : 0;
-    const int nb = pass == 2 ? 512 : 2048;
-    for (int q = threadIdx.x; q < nb; q += T) sm.hist[q] = 0u;
-    __syncthreads();
-    for (int c = threadIdx.x; c < n; c += T) {
-      const uint32_t x = bits[c];
-      if ((x & pmask) == prefix) atomicAdd(&sm.hist[(x >> sh) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    uint32_t bin, above, total;
-    suffix_find<NW>(sm.hist, nb, k, bin, above, total, sm);
-    k -= above;
-    prefix |= bin << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
-  }
-  return prefix;
+  bin = sm.fres[0];
+  above = sm.fres[1];
+  total = sm.fres[2];
 }
 
 template <int OP>
@@ -248,113 +206,122 @@ __device__ __forceinline__ bool split_predicate(double mass_above, uint32_t coun
   return ok_k && ((mass_above < pz) || count_above == 0u);
 }
 
-// The rejection loop on the candidates sm.c.bits/idx[0..n) (every value
-// above `low` of the row is among them), run by the first NW waves.  Thread
-// t owns the contiguous entries [t*E, t*E + E); the inverse-transform draw
-// runs over the entries in that order.  Returns the token (row index) or -1.
-template <int OP, int NW>
-__device__ int candidate_loop(SplitSmem& sm, int n, float low, float high, int k, double pz,
-                              uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
-  constexpr int T = NW * kWave;
-  const int E = (n + T - 1) / T;
-  const int c0 = min(n, (int)threadIdx.x * E), c1 = min(n, c0 + E);
-  const uint32_t* cb = sm.c.bits;
-  const int lane = lane_id(), w = uwave();
+// ---------------------------------------------------------------------------
+// The dual-pivot loop on one wave (no barriers).  cand[0..m) holds every
+// value of the row above `low` (and nothing at or below it); S is their
+// mass.  Lane l owns the contiguous entries [l*E, l*E + E), held in
+// registers when E <= kLoopRegs, and the inverse-transform draw runs over
+// the entries in that order (blog, 逆变换采样).  Guards as in the streaming
+// engine (blog, 实现细节): only entries with nonzero mass are chosen, the
+// first hit wins, and if rounding puts the target at or past every running
+// sum the last entry is taken.
+// ---------------------------------------------------------------------------
+constexpr int kLoopRegs = 32;
 
-  Pair acc{0.0, 0.0, 0u, 0u};
-  for (int c = c0; c < c1; ++c) {
-    const float x = __uint_as_float(cb[c]);
-    if (x > low) acc.m0 += (double)x;
+template <int OP, bool REG>
+__device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int k, double pz,
+                         double S, uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
+  const int lane = lane_id();
+  const int E = (m + kWave - 1) / kWave;
+  const int c0 = min(m, lane * E), c1 = min(m, c0 + E);
+  const uint64_t* cand = sm.cand;
+  constexpr int NR = REG ? kLoopRegs : 1;
+  float xr[NR];
+  if (REG) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) xr[j] = c0 + j < c1 ? __uint_as_float((uint32_t)cand[c0 + j]) : 0.0f;
   }
-  double S = block_sum<NW>(acc, sm).m0;  // S(low)
+  // x of this lane's j-th entry (0.0 past the end: never above a pivot)
+  auto X = [&](int j) -> float {
+    if (REG) return xr[j];
+    return c0 + j < c1 ? __uint_as_float((uint32_t)cand[c0 + j]) : 0.0f;
+  };
+  const int n = REG ? NR : E;
 
+  double part = 0.0;  // mass above low of this lane's entries
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    const float x = X(j);
+    if (x > low) part += (double)x;
+  }
   int rnd = 0;
   while (true) {
-    double u;
-    if (rnd < stream::kPreDraws) {
-      u = sm.draws[rnd];
-    } else {
-      if (threadIdx.x == 0) sm.extra_u = draw_uniform(seed, offset, sid, (uint32_t)rnd);
-      __syncthreads();
-      u = sm.extra_u;
-      __syncthreads();
-    }
+    const double u = rnd < stream::kPreDraws ? sm.draws[rnd]
+                                             : draw_uniform(seed, offset, sid, (uint32_t)rnd);
     ++rnd;
-    const double T_ = u * S;
-    // locate: the first candidate, in entry order, whose running sum exceeds
-    // T_; guards as in the streaming engine (first hit wins; if rounding puts
-    // T_ past every sum, the last candidate is taken)
-    double part = 0.0;
-    for (int c = c0; c < c1; ++c) {
-      const float x = __uint_as_float(cb[c]);
-      if (x > low) part += (double)x;
-    }
-    const double excl = block_excl_scan<NW>(part, sm);
-    const uint64_t hm = __ballot(part > 0.0 && excl + part > T_);
+    const double T = u * S;
+    const double incl = wave_incl_scan(part);
+    const double excl = wave_excl_from_incl(incl);
+    const uint64_t hit = __ballot(part > 0.0 && incl > T);
     const uint64_t nz = __ballot(part > 0.0);
-    if (lane == 0) {
-      sm.hit_lane[w] = hm ? (__ffsll((long long)hm) - 1) : -1;
-      sm.red_u[w][2] = nz ? (uint32_t)(64 - __clzll((long long)nz)) : 0u;
-    }
-    __syncthreads();
-    int win = -1, last = -1;
-#pragma unroll
-    for (int q = 0; q < NW; ++q) {
-      if (win < 0 && sm.hit_lane[q] >= 0) win = q * kWave + sm.hit_lane[q];
-      if (sm.red_u[q][2] > 0u) last = q * kWave + (int)sm.red_u[q][2] - 1;
-    }
-    const int owner = win >= 0 ? win : last;
-    if ((int)threadIdx.x == owner) {
-      int tok = -1, last_c = -1;
-      double run = excl;
-      for (int c = c0; c < c1; ++c) {
-        const float x = __uint_as_float(cb[c]);
-        if (x > low) {
-          run += (double)x;
-          last_c = c;
-          if (win >= 0 && run > T_) {
-            tok = c;
-            break;
-          }
-        }
-      }
-      sm.tok = tok >= 0 ? tok : last_c;
-    }
-    if (owner < 0 && threadIdx.x == 0) sm.tok = -1;
-    __syncthreads();
-    const int e = sm.tok;
-    __syncthreads();
-    if (e < 0) {
+    if (nz == 0ull) {
       rounds = rnd;
       return -1;
     }
-    const float pivot1 = __uint_as_float(cb[e]);
-    const int token = (int)sm.c.idx[e];
-    const float pivot2 = (float)(((double)pivot1 + (double)high) * 0.5);
-    Pair pv{0.0, 0.0, 0u, 0u};
-    for (int c = c0; c < c1; ++c) {
-      const float x = __uint_as_float(cb[c]);
-      if (x > pivot1) {
-        pv.m0 += (double)x;
-        pv.c0 += 1u;
-      }
-      if (x > pivot2) {
-        pv.m1 += (double)x;
-        pv.c1 += 1u;
+    const int owner = hit ? first_lane(hit) : last_lane(nz);
+    // the owner's entries, one per lane (a serial walk if a lane owns more
+    // than 64): first running sum past T, else the last entry above low
+    int e = -1;
+    const int o0 = min(m, owner * E), o1 = min(m, o0 + E);
+    const double base = lane_value(excl, owner);
+    if (o1 - o0 <= kWave) {
+      const int c = o0 + lane;
+      const float x = c < o1 ? __uint_as_float((uint32_t)cand[c]) : 0.0f;
+      const double xm = x > low ? (double)x : 0.0;
+      const double run = base + wave_incl_scan(xm);
+      const uint64_t h2 = __ballot(hit != 0ull && xm > 0.0 && run > T);
+      const uint64_t n2 = __ballot(xm > 0.0);
+      e = o0 + (h2 ? first_lane(h2) : last_lane(n2));
+    } else {
+      double run = base;
+      for (int c = o0; c < o1; ++c) {
+        const float x = __uint_as_float((uint32_t)cand[c]);
+        if (x > low) {
+          run += (double)x;
+          e = c;
+          if (hit != 0ull && run > T) break;
+        }
       }
     }
-    pv = block_sum<NW>(pv, sm);
-    if (split_predicate<OP>(pv.m0, pv.c0, k, pz)) {
+    e = min(max(e, 0), m - 1);  // part > 0 guarantees an entry; keep the read in bounds regardless
+    const uint64_t ent = cand[e];
+    const float pivot1 = __uint_as_float((uint32_t)ent);
+    const int token = (int)(ent >> 32);
+    if (OP == kOpTopK) {
+      // every entry is >= tau_k, so fewer than k values exceed pivot1
       rounds = rnd;
       return token;
     }
-    if (split_predicate<OP>(pv.m1, pv.c1, k, pz)) {
+    const float pivot2 = (float)(((double)pivot1 + (double)high) * 0.5);
+    double m0 = 0.0, m1 = 0.0;
+    uint32_t n0 = 0u, n1 = 0u;
+#pragma unroll
+    for (int j = 0; j < n; ++j) {
+      const float x = X(j);
+      if (x > pivot1) {
+        m0 += (double)x;
+        ++n0;
+      }
+      if (x > pivot2) {
+        m1 += (double)x;
+        ++n1;
+      }
+    }
+    const double M0 = wave_sum(m0), M1 = wave_sum(m1);
+    const uint32_t N0 = wave_sum(n0), N1 = wave_sum(n1);
+    if (split_predicate<OP>(M0, N0, k, pz)) {
+      rounds = rnd;
+      return token;
+    }
+    if (split_predicate<OP>(M1, N1, k, pz)) {
       low = pivot1;
       high = pivot2;
-      S = pv.m0;
+      S = M0;
+      part = m0;
     } else {
       low = pivot2;
-      S = pv.m1;
+      S = M1;
+      part = m1;
     }
     if (rnd >= stream::kMaxRounds) {
       rounds = rnd;
@@ -364,6 +331,18 @@ __device__ int candidate_loop(SplitSmem& sm, int n, float low, float high, int k
 }
 
 enum SplitMode : int { kDone = 0, kFallback = 1 };
+
+// Bounded wait for the provisional bound of wave 1.  Every wave gets out:
+// after the spin limit the bound 0 is used, which appends the whole slice,
+// overflows the lists and sends the slice down the full-histogram path.
+__device__ __forceinline__ uint32_t wait_tprov(SplitSmem& sm) {
+  for (int spin = 0; spin < (1 << 16); ++spin) {
+    const uint32_t t = __hip_atomic_load(&sm.tprov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (t & 1u) return t & ~1u;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return 0u;
+}
 
 // Everything but the streaming fallback; returns kFallback when the output
 // must be sampled by the streaming engine instead (one call site, below).
@@ -395,6 +374,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const uint64_t seed = P.seed_arr ? P.seed_arr[i] : P.seed;
   const uint64_t offset = P.offset_arr ? P.offset_arr[i] : P.offset;
   const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
+  if (tid == 0) sm.tprov = 0u;
+  __syncthreads();  // before any load: costs little, orders the clear before the polls
 
   // ---- phase A: one HBM read of the slice into registers --------------------
   const int V = P.vocab;
@@ -408,76 +389,91 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // bounds keeps every value of the row's top k.
   const uint32_t need = (uint32_t)k;
   const float4* src = reinterpret_cast<const float4*>(P.probs + (int64_t)row * V + s0);
+  const bool reader = wave > 0;
+  const int rt = tid - kWave;  // reader thread index
   // Loads are issued unconditionally (a lane past the end re-reads the last
   // vector and ignores it) so that they sit in one basic block and every
   // later use waits only for its own vector, not for the whole slice.
   float4 v[NV];
+  if (reader) {
 #pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = src[min(tid + j * kBlock, nvec - 1)];
-  // while the slice is in flight: the row's arrival generation (kept in a
-  // register until the header is written), the first 256 draws of the
-  // stream, and a cleared histogram
+    for (int j = 0; j < NV; ++j) v[j] = src[min(rt + j * kLoadThreads, nvec - 1)];
+  }
   uint32_t gen = 0u;
-  if (W > 1 && tid == 0)
-    gen = __hip_atomic_load(&S.gen[li], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (wave == 0) {
-    const Philox4x64 ph = philox4x64_10(offset, sid, (uint64_t)lane, 0ull, seed, 0ull);
+  if (reader) {
+    // Wave 1's loads go out first and land first: its values are the sample
+    // for the provisional bound, the edge of the 1/8-binade bin (bits >> 20)
+    // above which about 1.5 * need + 64 of the slice's values should lie.
+    uint32_t t_prov;
+    if (wave == 1) {
+      clear_hist<kHistBins>(sm.hist, lane, kWave);
+      uint32_t nsamp = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.draws[4 * lane + e] = (double)(ph.w[e] >> 11) * 0x1p-53;
-  }
-  for (int q = tid; q < kHistBins; q += kBlock) sm.hist[q] = 0u;
-  __syncthreads();  // histogram cleared (does not wait for the loads)
-
-  // Provisional bound from the first vector of every thread (the first
-  // 4096 values of the slice): the edge of the bin holding the r-th largest
-  // sample value, r sized for about 1.5 * need + 64 values over the slice.
-  {
-    const uint32_t q[4] = {bits_of(v[0].x), bits_of(v[0].y), bits_of(v[0].z), bits_of(v[0].w)};
-    if (tid < nvec) {
+      for (int j = 0; j < NV; ++j) {
+        if (rt + j * kLoadThreads < nvec) {
+          const uint32_t q[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&sm.hist[min(q[e] >> 20, (uint32_t)(kHistBins - 1))], 1u);
-    }
-  }
-  __syncthreads();
-  const uint32_t nsamp = 4u * (uint32_t)min(nvec, kBlock);
-  const uint32_t r = min(nsamp, max(1u, (uint32_t)(((1.5 * min(need, n_s) + 64.0) * nsamp) / n_s) + 1u));
-  uint32_t bin, above, total;
-  suffix_find<kWaves>(sm.hist, kHistBins, r, bin, above, total, sm);
-  const uint32_t t_prov = n_s <= need ? 0u : bin << 20;
-
-  // As each vector lands: slice maximum, and every value >= t_prov appended
-  // to this wave's LDS buffer in (vector, element, lane) order.
-  uint32_t mb = 0u;
-  uint32_t wcnt = 0u;  // wave-uniform
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int f = tid + j * kBlock;
-    const bool in = f < nvec;
-    const uint32_t q[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      mb = max(mb, in ? q[e] : 0u);
-      const bool sel = in && q[e] >= t_prov;
-      const uint64_t m = __ballot(sel);
-      if (m) {
-        if (sel) {
-          const uint32_t p =
-              wcnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          if (p < (uint32_t)kWaveCap) {
-            sm.a.pw.bits[wave][p] = q[e];
-            sm.a.pw.idx[wave][p] = (uint32_t)(s0 + 4 * f + e);
-          }
+          for (int e = 0; e < 4; ++e)
+            atomicAdd(&sm.hist[H1::at(min(q[e] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
         }
+        nsamp += 4u * (uint32_t)__popcll(__ballot(rt + j * kLoadThreads < nvec));
+      }
+      const uint32_t r =
+          min(nsamp, max(1u, (uint32_t)(((1.5 * min(need, n_s) + 64.0) * nsamp) / n_s) + 1u));
+      uint32_t bin, above, total;
+      wave_find<kHistBins>(sm.hist, r, bin, above, total);
+      t_prov = n_s <= need ? 0u : bin << 20;
+      if (lane == 0) __hip_atomic_store(&sm.tprov, t_prov | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      t_prov = wait_tprov(sm);
+    }
+
+    // As each vector lands: the slice maximum, and every value >= t_prov
+    // appended to this wave's list in (vector, element, lane) order.  Past
+    // the list's end the last slot is overwritten; the count still grows,
+    // which sends the slice down the full-histogram path.
+    uint32_t mb = 0u;
+    uint32_t wcnt = 0u;  // wave-uniform
+    uint64_t* list = sm.a.pw[wave];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int f = rt + j * kLoadThreads;
+      const bool in = f < nvec;
+      const uint32_t q[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mb = max(mb, in ? q[e] : 0u);
+        const bool sel = in && q[e] >= t_prov;
+        const uint64_t m = __ballot(sel);
+        const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, wcnt));
+        if (sel) list[min(p, (uint32_t)(kWaveCap - 1))] =
+            (uint64_t)q[e] | ((uint64_t)(uint32_t)(s0 + 4 * f + e) << 32);
         wcnt += (uint32_t)__popcll(m);
       }
     }
+    mb = wave_max(mb);
+    if (lane == 0) {
+      sm.wcnt[wave] = wcnt;
+      sm.wmax[wave] = mb;
+      if (wave == 1) sm.res[0] = t_prov;
+    }
+  } else {
+    // wave 0: the row's arrival generation and the first 256 draws of the
+    // output's stream, while the slice lands
+    if (W > 1 && lane == 0)
+      gen = __hip_atomic_load(&S.gen[li], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const Philox4x64 ph = philox4x64_10(offset, sid, (uint64_t)lane, 0ull, seed, 0ull);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.draws[4 * lane + e] = (double)(ph.w[e] >> 11) * 0x1p-53;
+    if (lane == 0) {
+      sm.wcnt[0] = 0u;
+      sm.wmax[0] = 0u;
+    }
   }
-  if (lane == 0) sm.wcnt[wave] = wcnt;
-  if (tid == 0) sm.gen = gen;
-  const uint32_t slice_max = block_max<kWaves>(mb, sm);  // also publishes wcnt[]
-  const bool bad = slice_max >= 0x7F800000u;             // sign bit, inf or NaN somewhere
-  uint32_t tot = 0u, wbase = 0u;
+  __syncthreads();
+  const uint32_t t_prov = sm.res[0];
+  uint32_t tot = 0u, wbase = 0u, slice_max = 0u;
   bool wave_ovf = false;
 #pragma unroll
   for (int q = 0; q < kWaves; ++q) {
@@ -485,29 +481,37 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     wbase += q < wave ? c : 0u;
     tot += c;
     wave_ovf |= c > (uint32_t)kWaveCap;
+    slice_max = max(slice_max, sm.wmax[q]);
   }
   const bool fast = !wave_ovf && (tot >= need || t_prov == 0u) && tot <= (uint32_t)kSliceCandMax;
 
-  // local bound t_s and the published list: the appended values (fast path),
-  // else a full histogram of the slice and a compaction from registers
+  // The slice's bound t_bits and its list: the appended values (fast path),
+  // else a full histogram of the slice and a compaction into sm.cand.  The
+  // full path re-reads the slice (from L2) rather than keeping it in
+  // registers: only flat rows take it, and freeing v[] keeps the common path
+  // free of spills.
   uint32_t t_bits, cnt;
   if (fast) {
     t_bits = t_prov;
     cnt = tot;
   } else {
-    for (int q = tid; q < kHistBins; q += kBlock) sm.hist[q] = 0u;
+    clear_hist<kHistBins>(sm.hist, tid, kBlock);
     __syncthreads();
-    // the slice is re-read (from L2) rather than kept in registers: this
-    // path is taken only by flat rows, and freeing v[] keeps the common
-    // path free of spills
+    uint32_t mx = 0u;
     for (int f = tid; f < nvec; f += kBlock) {
       const float4 x = src[f];
       const uint32_t q[4] = {bits_of(x.x), bits_of(x.y), bits_of(x.z), bits_of(x.w)};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&sm.hist[min(q[e] >> 20, (uint32_t)(kHistBins - 1))], 1u);
+      for (int e = 0; e < 4; ++e) {
+        mx = max(mx, q[e]);
+        atomicAdd(&sm.hist[H1::at(min(q[e] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
+      }
     }
-    __syncthreads();
-    suffix_find<kWaves>(sm.hist, kHistBins, need, bin, above, total, sm);
+    mx = wave_max(mx);
+    __syncthreads();  // histogram complete; wmax free
+    if (lane == 0) sm.wmax[wave] = mx;
+    uint32_t bin, above, total;
+    block_find<kHistBins>(sm.hist, need, bin, above, total, sm);  // its barrier publishes wmax[]
     t_bits = bin << 20;
     uint32_t mine = 0u;
     for (int f = tid; f < nvec; f += kBlock) {
@@ -515,35 +519,34 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       mine += (uint32_t)(bits_of(x.x) >= t_bits) + (uint32_t)(bits_of(x.y) >= t_bits) +
               (uint32_t)(bits_of(x.z) >= t_bits) + (uint32_t)(bits_of(x.w) >= t_bits);
     }
-    uint32_t pos = block_excl_scan<kWaves>(mine, cnt, sm);
-    if (cnt <= (uint32_t)kSliceCandMax && !bad) {  // compaction into sm.c, thread-major
+    uint32_t pos = block_excl_scan(mine, cnt, sm);
+    slice_max = 0u;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) slice_max = max(slice_max, sm.wmax[q]);
+    if (cnt <= (uint32_t)kSliceCandMax && slice_max < 0x7F800000u) {  // thread-major order
       for (int f = tid; f < nvec; f += kBlock) {
         const float4 x = src[f];
         const uint32_t q[4] = {bits_of(x.x), bits_of(x.y), bits_of(x.z), bits_of(x.w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (q[e] >= t_bits) {
-            sm.c.bits[pos] = q[e];
-            sm.c.idx[pos] = (uint32_t)(s0 + 4 * f + e);
+            sm.cand[pos] = (uint64_t)q[e] | ((uint64_t)(uint32_t)(s0 + 4 * f + e) << 32);
             ++pos;
           }
         }
       }
     }
   }
+  const bool bad = slice_max >= 0x7F800000u;  // a sign bit, an inf or a NaN somewhere
   const bool overflow = cnt > (uint32_t)kSliceCandMax;
   const bool publish = !bad && !overflow;
 
-  uint32_t gmax;
-  int n;
+  uint32_t gmax, tstar, ntot;
   if (W == 1) {
-    // the whole row is in this work-group: candidates into sm.c
-    if (fast && publish) {
-      const uint32_t c = min(sm.wcnt[wave], (uint32_t)kWaveCap);
-      for (uint32_t p = lane; p < c; p += kWave) {
-        sm.c.bits[wbase + p] = sm.a.pw.bits[wave][p];
-        sm.c.idx[wbase + p] = sm.a.pw.idx[wave][p];
-      }
+    // the whole row is in this work-group: candidates into sm.cand
+    if (fast && publish && wave > 0) {
+      const uint32_t c = sm.wcnt[wave];
+      for (uint32_t p = lane; p < c; p += kWave) sm.cand[wbase + p] = sm.a.pw[wave][p];
     }
     __syncthreads();
     if (bad || slice_max == 0u) {
@@ -552,27 +555,27 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
     if (overflow) return kFallback;
     gmax = slice_max;
-    n = (int)cnt;
-    if (wave >= kTailWaves) return kDone;
+    tstar = t_bits;
+    ntot = cnt;
   } else {
     uint64_t* dst = S.cand + ((int64_t)li * W + s) * kSliceCandMax;
     if (publish) {
       if (fast) {
-        const uint32_t c = min(sm.wcnt[wave], (uint32_t)kWaveCap);
-        for (uint32_t p = lane; p < c; p += kWave)
-          dst[wbase + p] = (uint64_t)sm.a.pw.bits[wave][p] | ((uint64_t)sm.a.pw.idx[wave][p] << 32);
+        if (wave > 0) {
+          const uint32_t c = sm.wcnt[wave];
+          for (uint32_t p = lane; p < c; p += kWave) dst[wbase + p] = sm.a.pw[wave][p];
+        }
       } else {
-        __syncthreads();  // compaction into sm.c complete
-        for (uint32_t c = tid; c < cnt; c += kBlock)
-          dst[c] = (uint64_t)sm.c.bits[c] | ((uint64_t)sm.c.idx[c] << 32);
+        __syncthreads();  // compaction into sm.cand complete
+        for (uint32_t c = tid; c < cnt; c += kBlock) dst[c] = sm.cand[c];
       }
     }
     if (tid == 0) {
       uint32_t* h = S.hdr + ((int64_t)li * W + s) * kHdrWords;
       h[0] = t_bits;
-      h[1] = publish ? cnt : 0xFFFFFFFFu;
+      h[1] = publish ? cnt : kNoList;
       h[2] = slice_max;
-      h[3] = sm.gen;
+      h[3] = gen;
       h[4] = xcc_id();
     }
     // hand-off: this work-group's stores reach the XCD's L2 before it arrives
@@ -588,98 +591,177 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     if (!sm.flag) return kDone;
 
     // ---- phase B: the last slice work-group of the row ----------------------
-    const uint32_t me = xcc_id();
-    if (tid == 0) {
-      __hip_atomic_store(&S.ctr[li], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&S.gen[li], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // wave 0 reads the W headers (lane q: slice q) and sums them up; every
+    // thread clears the selection histograms meanwhile
+    if (wave == 0) {
+      const uint32_t me = xcc_id();
+      const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
+      if (lane == 0) {
+        __hip_atomic_store(&S.ctr[li], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&S.gen[li], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const bool mine = lane < W;
+      uint32_t ht = 0u, hc = 0u, hm = 0u, hg = mygen, hx = me;
+      if (mine) {
+        const uint32_t* h = S.hdr + ((int64_t)li * W + lane) * kHdrWords;
+        ht = __hip_atomic_load(h + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hc = __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hm = __hip_atomic_load(h + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const bool foreign = __ballot(mine && (hg != mygen || hx != me)) != 0ull;
+      const bool ovf = __ballot(mine && hc > (uint32_t)kSliceCandMax) != 0ull;  // kNoList too
+      const uint32_t cc = (mine && hc <= (uint32_t)kSliceCandMax) ? hc : 0u;
+      const uint32_t incl = wave_incl_scan(cc);
+      const uint32_t all = lane63(incl);
+      const uint32_t gm = wave_max(hm);
+      const uint32_t ts = wave_max(ht);
+      if (lane <= kMaxSlices) sm.off[lane] = lane < W ? incl - cc : all;
+      if (lane == 0) {
+        uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back
+        if (foreign) status = 2u;
+        else if (gm >= 0x7F800000u || gm == 0u) status = 1u;
+        else if (ovf || all > (uint32_t)kRowCandMax) status = 2u;
+        sm.res[0] = ts;
+        sm.res[1] = all;
+        sm.res[2] = gm;
+        sm.res[3] = status;
+      }
     }
-    if (tid < W * kHdrWords) {
-      sm.hdr[tid / kHdrWords][tid % kHdrWords] =
-          __hip_atomic_load(S.hdr + (int64_t)li * W * kHdrWords + tid, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
-    }
+    clear_hist<kHistBins>(sm.hist, tid, kBlock);
     __syncthreads();
-    bool foreign = false, ovf = false;
-    uint32_t tstar = 0u, ntot = 0u;
-    gmax = 0u;
-    for (int q = 0; q < W; ++q) {
-      foreign |= sm.hdr[q][3] != sm.gen || sm.hdr[q][4] != me;
-      ovf |= sm.hdr[q][1] == 0xFFFFFFFFu;
-      gmax = max(gmax, sm.hdr[q][2]);
-      tstar = max(tstar, sm.hdr[q][0]);
-      if (sm.hdr[q][1] != 0xFFFFFFFFu) ntot += sm.hdr[q][1];
-    }
-    if (!foreign && (gmax >= 0x7F800000u || gmax == 0u)) {
+    if (sm.res[3] == 1u) {
       if (tid == 0) stream::write_sample(P, i, -1, 0);
       return kDone;
     }
-    if (foreign || ovf || ntot > (uint32_t)kRowCandMax) return kFallback;
+    if (sm.res[3] == 2u) return kFallback;
+    tstar = sm.res[0];
+    ntot = sm.res[1];
+    gmax = sm.res[2];
+  }
 
-    // gather: every thread issues its (up to 8) loads before using any, then
-    // keeps the entries >= t*; order (thread, slot), which is fixed
-    if (tid == 0) {
-      uint32_t acc = 0u;
-      for (int q = 0; q < W; ++q) {
-        sm.off[q] = acc;
-        acc += sm.hdr[q][1];
-      }
-      for (int q = W; q <= kMaxSlices; ++q) sm.off[q] = acc;
-    }
-    __syncthreads();
-    constexpr int kPer = kRowCandMax / kBlock;
-    uint64_t ent[kPer];
+  // ---- candidates into registers: thread t holds entries t + 1024 q ---------
+  uint64_t ent[kPer];
+  if (W == 1) {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const uint32_t g = (uint32_t)(tid + q * kBlock);
-      ent[q] = 0ull;
-      if (g < ntot) {
-        int sl = 0;  // slice holding entry g: sm.off is non-decreasing
-#pragma unroll
-        for (int step = kMaxSlices / 2; step >= 1; step >>= 1)
-          if (sl + step < W && sm.off[sl + step] <= g) sl += step;
-        ent[q] = __hip_atomic_load(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (g - sm.off[sl]),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      ent[q] = g < ntot ? sm.cand[g] : 0ull;
     }
-    uint32_t keep = 0u;
+    __syncthreads();  // sm.a.pw (read above) is dead; sm.cand is read
+    clear_hist<kHistBins>(sm.hist, tid, kBlock);
+    __syncthreads();
+  } else {
+    // the slice of entry g: the last q < W with off[q] <= g (off is
+    // non-decreasing); all offsets in registers, every load issued before
+    // any is used
+    uint32_t off[kMaxSlices];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      keep += (uint32_t)(tid + q * kBlock < (int)ntot && (uint32_t)ent[q] >= tstar);
-    uint32_t nstar;
-    uint32_t wpos = block_excl_scan<kWaves>(keep, nstar, sm);
+    for (int q = 0; q < kMaxSlices; ++q) off[q] = sm.off[q];
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      if (tid + q * kBlock < (int)ntot && (uint32_t)ent[q] >= tstar) {
-        sm.c.bits[wpos] = (uint32_t)ent[q];
-        sm.c.idx[wpos] = (uint32_t)(ent[q] >> 32);
-        ++wpos;
+      const uint32_t g = (uint32_t)(tid + q * kBlock);
+      int sl = 0;
+      uint32_t base = 0u;
+#pragma unroll
+      for (int t = 1; t < kMaxSlices; ++t) {
+        if (t < W && off[t] <= g) {
+          sl = t;
+          base = off[t];
+        }
       }
+      ent[q] = 0ull;
+      if (g < ntot)
+        ent[q] = __hip_atomic_load(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (g - base),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
-    if (tstar > 0u && nstar < (uint32_t)k) return kFallback;  // guard: not reached
-    n = (int)nstar;
-    if (wave >= kTailWaves) return kDone;
+  }
+  clear_hist<kHistBins>(sm.a.sel.h2, tid, kBlock);
+  clear_hist<kFineBins>(sm.a.sel.h3, tid, kBlock);
+  // an entry takes part if it exists and is >= t* (bits of valid values have
+  // bit 31 clear, so bits >> 20 is a bin of the 2048)
+  uint32_t live = 0u;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const uint32_t g = (uint32_t)(tid + q * kBlock);
+    if (g < ntot && (uint32_t)ent[q] >= tstar) live |= 1u << q;
   }
 
-  // ---- tail (four waves): k-th largest, top-k mass, dual-pivot loop --------
-  // The candidates are every value >= t* of the row, at least k of them (or
-  // the whole row).  tau_k is found exactly; the loop then starts just below
-  // it, where f(low) = 0 because at least k values exceed low.
-  const uint32_t tau_k =
-      ((uint32_t)k <= (uint32_t)n) ? kth_largest<kTailWaves>(sm.c.bits, n, (uint32_t)k, sm) : 0u;
-  double pz = 0.0;
-  if (OP == kOpTopKTopP) {
-    Pair z{0.0, 0.0, 0u, 0u};
-    for (int c = tid; c < n; c += kTailThreads)
-      if (sm.c.bits[c] >= tau_k) z.m0 += (double)__uint_as_float(sm.c.bits[c]);
-    z = block_sum<kTailWaves>(z, sm);
-    pz = (double)stream::clamp01(pp) * z.m0;
+  // ---- tau_k: the k-th largest candidate, three histogram passes ------------
+#pragma unroll
+  for (int q = 0; q < kPer; ++q)
+    if (live & (1u << q))
+      atomicAdd(&sm.hist[H1::at(((uint32_t)ent[q] >> 20) & (kHistBins - 1))], 1u);
+  __syncthreads();
+  uint32_t bin1, above1, nstar;
+  block_find<kHistBins>(sm.hist, (uint32_t)k, bin1, above1, nstar, sm);
+  uint32_t tau_k = 0u;
+  if (nstar >= (uint32_t)k) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if ((live & (1u << q)) && ((uint32_t)ent[q] >> 20) == bin1)
+        atomicAdd(&sm.a.sel.h2[H1::at(((uint32_t)ent[q] >> 9) & (kHistBins - 1))], 1u);
+    __syncthreads();
+    uint32_t bin2, above2, t2;
+    block_find<kHistBins>(sm.a.sel.h2, (uint32_t)k - above1, bin2, above2, t2, sm);
+    const uint32_t hi = (bin1 << 11) | bin2;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if ((live & (1u << q)) && ((uint32_t)ent[q] >> 9) == hi)
+        atomicAdd(&sm.a.sel.h3[H3::at((uint32_t)ent[q] & (kFineBins - 1))], 1u);
+    __syncthreads();
+    uint32_t bin3, above3, t3;
+    block_find<kFineBins>(sm.a.sel.h3, (uint32_t)k - above1 - above2, bin3, above3, t3, sm);
+    tau_k = (hi << 9) | bin3;
+  } else if (tstar > 0u) {
+    return kFallback;  // guard: fewer than k values at or above t* (not reached)
   }
+
+  // ---- the top-k set {x >= tau_k} into sm.cand, with its mass Z_k -----------
+  uint32_t keep = 0u, nk = 0u;
+  double zk = 0.0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const uint32_t x = (uint32_t)ent[q];
+    if ((live & (1u << q)) && x >= tau_k && x > 0u) {
+      keep |= 1u << q;
+      ++nk;
+      zk += (double)__uint_as_float(x);
+    }
+  }
+  const uint32_t incl = wave_incl_scan(nk);
+  zk = wave_sum(zk);
+  if (lane == kWave - 1) {
+    sm.red_u[wave] = incl;
+    sm.red_d[wave] = zk;
+  }
+  __syncthreads();
+  uint32_t pos = 0u, m = 0u;
+  double Z = 0.0;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    pos += q < wave ? sm.red_u[q] : 0u;
+    m += sm.red_u[q];
+    Z += sm.red_d[q];
+  }
+  pos += incl - nk;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q)
+    if (keep & (1u << q)) sm.cand[pos++] = ent[q];
+  __syncthreads();
+  if (wave != 0) return kDone;
+
+  // ---- the dual-pivot loop on wave 0 ----------------------------------------
+  const double pz = OP == kOpTopKTopP ? (double)stream::clamp01(pp) * Z : 0.0;
   const float low = tau_k > 0u ? __uint_as_float(tau_k - 1u) : 0.0f;
   int rounds = 0;
-  const int e = candidate_loop<OP, kTailWaves>(sm, n, low, __uint_as_float(gmax), k, pz, seed,
-                                               offset, sid, rounds);
-  if (tid == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
+  const int e = m <= kWave * kLoopRegs
+                    ? wave_loop<OP, true>(sm, (int)m, low, __uint_as_float(gmax), k, pz, Z, seed,
+                                          offset, sid, rounds)
+                    : wave_loop<OP, false>(sm, (int)m, low, __uint_as_float(gmax), k, pz, Z, seed,
+                                           offset, sid, rounds);
+  if (lane == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
   return kDone;
 }
 
@@ -711,7 +793,7 @@ void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, hipStream_t
 }
 
 constexpr int kChunk = 2048;     // outputs per launch (bounds the workspace)
-constexpr int kMaxSliceLen = 12 * 4 * kBlock;
+constexpr int kMaxSliceLen = 12 * 4 * kLoadThreads;
 
 // The arrival counters and generation numbers sit at fixed offsets for the
 // largest chunk, so calls of any shape can share one workspace: counters are
@@ -737,7 +819,7 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
     L = ((vocab + 4 * W - 1) / (4 * W)) * 4;
     if (W == 1 || (int64_t)(W - 1) * L < vocab) break;
   }
-  int nv = (L / 4 + kBlock - 1) / kBlock;
+  int nv = (L / 4 + kLoadThreads - 1) / kLoadThreads;
   nv = nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 6 ? 6 : nv <= 8 ? 8 : nv <= 10 ? 10 : 12;
   const int ch = min(num_outputs, kChunk);
   plan.W = W;
