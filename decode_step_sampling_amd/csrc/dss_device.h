@@ -160,6 +160,30 @@ __device__ __forceinline__ double draw_uniform(uint64_t seed, uint64_t offset, u
 }
 
 // ---------------------------------------------------------------------------
+// global-memory views of plain pointers
+// ---------------------------------------------------------------------------
+//
+// A pointer held in a parameter struct is generic (flat) to the compiler
+// unless it can prove otherwise, and flat loads count against the LDS wait
+// counter as well as the vector-memory one: every LDS wait would then also
+// wait for outstanding HBM reads.  These casts make the accesses
+// global-memory instructions.
+template <class T>
+using gptr = T __attribute__((address_space(1)))*;
+template <class T>
+__device__ __forceinline__ gptr<T> as_global(T* p) {
+  return (gptr<T>)p;
+}
+
+// 16-byte global load (HIP's float4 cannot be copied out of another
+// address space, the native vector type can)
+__device__ __forceinline__ float4 load_f4(gptr<const float4> p) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f x = *(gptr<const v4f>)p;
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
+// ---------------------------------------------------------------------------
 // float32 order keys
 // ---------------------------------------------------------------------------
 

@@ -48,7 +48,7 @@ constexpr int kLoadThreads = kLoadWaves * kWave;   // 960
 constexpr int kHistBins = 2048;
 constexpr int kFineBins = 512;
 constexpr int kSliceCandMax = 4096;
-constexpr int kWaveCap = 512;  // per-wave append list during the read
+constexpr int kWaveCap = 448;  // per-wave append list during the read
 constexpr int kRowCandMax = 8192;
 constexpr int kPer = kRowCandMax / kBlock;  // gathered entries per thread
 constexpr int kSplitKCap = 1536;
@@ -82,7 +82,10 @@ using H3 = Padded<kFineBins>;
 
 struct SplitSmem {
   union {
-    uint64_t pw[kWaves][kWaveCap];  // per-wave appends during the read (bits | index << 32)
+    struct {
+      uint32_t bits[kWaves][kWaveCap + kWave];  // per-wave appends during the read,
+      uint32_t idx[kWaves][kWaveCap + kWave];   // then one dummy slot per lane
+    } pw;
     struct {
       alignas(16) uint32_t h2[H1::kWords];
       alignas(16) uint32_t h3[H3::kWords];
@@ -209,24 +212,22 @@ __device__ __forceinline__ bool split_predicate(double mass_above, uint32_t coun
 // ---------------------------------------------------------------------------
 // The dual-pivot loop on one wave (no barriers).  cand[0..m) holds every
 // value of the row above `low` (and nothing at or below it); S is their
-// mass.  Lane l owns the contiguous entries [l*E, l*E + E), held in
-// registers when E <= kLoopRegs, and the inverse-transform draw runs over
+// mass.  Lane l owns the contiguous entries [l*E, l*E + E), held in NR
+// registers (NR >= E; NR = 0: read from LDS), and the inverse-transform draw runs over
 // the entries in that order (blog, 逆变换采样).  Guards as in the streaming
 // engine (blog, 实现细节): only entries with nonzero mass are chosen, the
 // first hit wins, and if rounding puts the target at or past every running
 // sum the last entry is taken.
 // ---------------------------------------------------------------------------
-constexpr int kLoopRegs = 32;
-
-template <int OP, bool REG>
+template <int OP, int NR>
 __device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int k, double pz,
                          double S, uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
+  constexpr bool REG = NR > 0;
   const int lane = lane_id();
   const int E = (m + kWave - 1) / kWave;
   const int c0 = min(m, lane * E), c1 = min(m, c0 + E);
   const uint64_t* cand = sm.cand;
-  constexpr int NR = REG ? kLoopRegs : 1;
-  float xr[NR];
+  float xr[REG ? NR : 1];
   if (REG) {
 #pragma unroll
     for (int j = 0; j < NR; ++j) xr[j] = c0 + j < c1 ? __uint_as_float((uint32_t)cand[c0 + j]) : 0.0f;
@@ -236,7 +237,7 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int 
     if (REG) return xr[j];
     return c0 + j < c1 ? __uint_as_float((uint32_t)cand[c0 + j]) : 0.0f;
   };
-  const int n = REG ? NR : E;
+  const int n = REG ? NR : E;  // entries past c1 read as 0.0
 
   double part = 0.0;  // mass above low of this lane's entries
 #pragma unroll
@@ -358,9 +359,10 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   out_i = i;
   const int tid = threadIdx.x, lane = lane_id(), wave = uwave();
 
-  const int row = P.indices ? P.indices[i] : i;
-  const int k = P.top_k_arr ? P.top_k_arr[i] : P.top_k;
-  const float pp = (OP == kOpTopKTopP) ? (P.top_p_arr ? P.top_p_arr[i] : P.top_p) : 0.0f;
+  const int row = P.indices ? as_global(P.indices)[i] : i;
+  const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
+  const float pp =
+      (OP == kOpTopKTopP) ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
   const bool ok = row >= 0 && row < P.rows && k > 0 && (OP != kOpTopKTopP || !isnan(pp));
   if (!ok || k > kSplitKCap) {
     // no hand-off for this output: slice 0 answers alone
@@ -371,8 +373,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
     return kFallback;
   }
-  const uint64_t seed = P.seed_arr ? P.seed_arr[i] : P.seed;
-  const uint64_t offset = P.offset_arr ? P.offset_arr[i] : P.offset;
+  const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
   if (tid == 0) sm.tprov = 0u;
   __syncthreads();  // before any load: costs little, orders the clear before the polls
@@ -388,7 +390,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // The row's k-th largest is at least every slice's, so the maximum of the
   // bounds keeps every value of the row's top k.
   const uint32_t need = (uint32_t)k;
-  const float4* src = reinterpret_cast<const float4*>(P.probs + (int64_t)row * V + s0);
+  const gptr<const float4> src =
+      as_global(reinterpret_cast<const float4*>(P.probs + (int64_t)row * V + s0));
   const bool reader = wave > 0;
   const int rt = tid - kWave;  // reader thread index
   // Loads are issued unconditionally (a lane past the end re-reads the last
@@ -397,7 +400,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   float4 v[NV];
   if (reader) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = src[min(rt + j * kLoadThreads, nvec - 1)];
+    for (int j = 0; j < NV; ++j) v[j] = load_f4(src + min(rt + j * kLoadThreads, nvec - 1));
   }
   uint32_t gen = 0u;
   if (reader) {
@@ -428,27 +431,40 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       t_prov = wait_tprov(sm);
     }
 
-    // As each vector lands: the slice maximum, and every value >= t_prov
-    // appended to this wave's list in (vector, element, lane) order.  Past
-    // the list's end the last slot is overwritten; the count still grows,
-    // which sends the slice down the full-histogram path.
+    // As each vector lands: the slice maximum (lanes past the end hold a
+    // copy of a real vector, so they may join in), and every value >= t_prov
+    // appended to this wave's list in (vector, element, lane) order.  Lanes
+    // with nothing to append write a dummy slot of their own, so the store
+    // needs no branch.  A list that could overflow with the next vector
+    // stops; its count is set past the cap, which sends the slice down the
+    // full-histogram path.
     uint32_t mb = 0u;
     uint32_t wcnt = 0u;  // wave-uniform
-    uint64_t* list = sm.a.pw[wave];
+    uint32_t* lbits = sm.a.pw.bits[wave];
+    uint32_t* lidx = sm.a.pw.idx[wave];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
+      if (wcnt > (uint32_t)(kWaveCap - 4 * kWave)) {
+        wcnt = kWaveCap + 1;
+        break;
+      }
       const int f = rt + j * kLoadThreads;
       const bool in = f < nvec;
+      // exec is full here, so the compare masks need no further masking
+      const uint64_t in_m = __builtin_amdgcn_uicmp((uint32_t)f, (uint32_t)nvec, 36);  // <
       const uint32_t q[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+      mb = max(max(mb, q[0]), q[1]);
+      mb = max(max(mb, q[2]), q[3]);
+      const uint32_t idx0 = (uint32_t)(s0 + 4 * f);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        mb = max(mb, in ? q[e] : 0u);
+        const uint64_t m = __builtin_amdgcn_uicmp(q[e], t_prov, 35) & in_m;  // >=
         const bool sel = in && q[e] >= t_prov;
-        const uint64_t m = __ballot(sel);
         const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, wcnt));
-        if (sel) list[min(p, (uint32_t)(kWaveCap - 1))] =
-            (uint64_t)q[e] | ((uint64_t)(uint32_t)(s0 + 4 * f + e) << 32);
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint32_t slot = sel ? wcnt + p : (uint32_t)(kWaveCap + lane);
+        lbits[slot] = q[e];
+        lidx[slot] = idx0 + (uint32_t)e;
         wcnt += (uint32_t)__popcll(m);
       }
     }
@@ -462,7 +478,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     // wave 0: the row's arrival generation and the first 256 draws of the
     // output's stream, while the slice lands
     if (W > 1 && lane == 0)
-      gen = __hip_atomic_load(&S.gen[li], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gen = __hip_atomic_load(as_global(S.gen + li), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const Philox4x64 ph = philox4x64_10(offset, sid, (uint64_t)lane, 0ull, seed, 0ull);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.draws[4 * lane + e] = (double)(ph.w[e] >> 11) * 0x1p-53;
@@ -499,7 +515,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     __syncthreads();
     uint32_t mx = 0u;
     for (int f = tid; f < nvec; f += kBlock) {
-      const float4 x = src[f];
+      const float4 x = load_f4(src + f);
       const uint32_t q[4] = {bits_of(x.x), bits_of(x.y), bits_of(x.z), bits_of(x.w)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -515,7 +531,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     t_bits = bin << 20;
     uint32_t mine = 0u;
     for (int f = tid; f < nvec; f += kBlock) {
-      const float4 x = src[f];
+      const float4 x = load_f4(src + f);
       mine += (uint32_t)(bits_of(x.x) >= t_bits) + (uint32_t)(bits_of(x.y) >= t_bits) +
               (uint32_t)(bits_of(x.z) >= t_bits) + (uint32_t)(bits_of(x.w) >= t_bits);
     }
@@ -525,7 +541,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     for (int q = 0; q < kWaves; ++q) slice_max = max(slice_max, sm.wmax[q]);
     if (cnt <= (uint32_t)kSliceCandMax && slice_max < 0x7F800000u) {  // thread-major order
       for (int f = tid; f < nvec; f += kBlock) {
-        const float4 x = src[f];
+        const float4 x = load_f4(src + f);
         const uint32_t q[4] = {bits_of(x.x), bits_of(x.y), bits_of(x.z), bits_of(x.w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -546,7 +562,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     // the whole row is in this work-group: candidates into sm.cand
     if (fast && publish && wave > 0) {
       const uint32_t c = sm.wcnt[wave];
-      for (uint32_t p = lane; p < c; p += kWave) sm.cand[wbase + p] = sm.a.pw[wave][p];
+      for (uint32_t p = lane; p < c; p += kWave)
+        sm.cand[wbase + p] = (uint64_t)sm.a.pw.bits[wave][p] | ((uint64_t)sm.a.pw.idx[wave][p] << 32);
     }
     __syncthreads();
     if (bad || slice_max == 0u) {
@@ -558,12 +575,13 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     tstar = t_bits;
     ntot = cnt;
   } else {
-    uint64_t* dst = S.cand + ((int64_t)li * W + s) * kSliceCandMax;
+    const gptr<uint64_t> dst = as_global(S.cand + ((int64_t)li * W + s) * kSliceCandMax);
     if (publish) {
       if (fast) {
         if (wave > 0) {
           const uint32_t c = sm.wcnt[wave];
-          for (uint32_t p = lane; p < c; p += kWave) dst[wbase + p] = sm.a.pw[wave][p];
+          for (uint32_t p = lane; p < c; p += kWave)
+            dst[wbase + p] = (uint64_t)sm.a.pw.bits[wave][p] | ((uint64_t)sm.a.pw.idx[wave][p] << 32);
         }
       } else {
         __syncthreads();  // compaction into sm.cand complete
@@ -571,7 +589,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       }
     }
     if (tid == 0) {
-      uint32_t* h = S.hdr + ((int64_t)li * W + s) * kHdrWords;
+      const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + s) * kHdrWords);
       h[0] = t_bits;
       h[1] = publish ? cnt : kNoList;
       h[2] = slice_max;
@@ -583,7 +601,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&S.ctr[li], 1u, __ATOMIC_RELAXED,
+      const uint32_t old = __hip_atomic_fetch_add(as_global(S.ctr + li), 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
       sm.flag = (old == (uint32_t)(W - 1));
     }
@@ -597,13 +615,13 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       const uint32_t me = xcc_id();
       const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
       if (lane == 0) {
-        __hip_atomic_store(&S.ctr[li], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(&S.gen[li], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(as_global(S.ctr + li), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const bool mine = lane < W;
       uint32_t ht = 0u, hc = 0u, hm = 0u, hg = mygen, hx = me;
       if (mine) {
-        const uint32_t* h = S.hdr + ((int64_t)li * W + lane) * kHdrWords;
+        const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + lane) * kHdrWords);
         ht = __hip_atomic_load(h + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         hc = __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         hm = __hip_atomic_load(h + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -654,11 +672,12 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     __syncthreads();
   } else {
     // the slice of entry g: the last q < W with off[q] <= g (off is
-    // non-decreasing); all offsets in registers, every load issued before
-    // any is used
+    // non-decreasing); the offsets in scalar registers, every load issued
+    // before any is used
     uint32_t off[kMaxSlices];
 #pragma unroll
-    for (int q = 0; q < kMaxSlices; ++q) off[q] = sm.off[q];
+    for (int q = 0; q < kMaxSlices; ++q)
+      off[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.off[q]);
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const uint32_t g = (uint32_t)(tid + q * kBlock);
@@ -673,8 +692,9 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       }
       ent[q] = 0ull;
       if (g < ntot)
-        ent[q] = __hip_atomic_load(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (g - base),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ent[q] = __hip_atomic_load(
+            as_global(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (g - base)),
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   clear_hist<kHistBins>(sm.a.sel.h2, tid, kBlock);
@@ -756,11 +776,17 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const double pz = OP == kOpTopKTopP ? (double)stream::clamp01(pp) * Z : 0.0;
   const float low = tau_k > 0u ? __uint_as_float(tau_k - 1u) : 0.0f;
   int rounds = 0;
-  const int e = m <= kWave * kLoopRegs
-                    ? wave_loop<OP, true>(sm, (int)m, low, __uint_as_float(gmax), k, pz, Z, seed,
-                                          offset, sid, rounds)
-                    : wave_loop<OP, false>(sm, (int)m, low, __uint_as_float(gmax), k, pz, Z, seed,
-                                           offset, sid, rounds);
+  const float high = __uint_as_float(gmax);
+  int e;
+  if (m <= 4 * kWave) {
+    e = wave_loop<OP, 4>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+  } else if (m <= 8 * kWave) {
+    e = wave_loop<OP, 8>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+  } else if (m <= 16 * kWave) {
+    e = wave_loop<OP, 16>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+  } else {  // (32 entries per lane in registers would spill the kernel)
+    e = wave_loop<OP, 0>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+  }
   if (lane == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
   return kDone;
 }
@@ -787,13 +813,13 @@ void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, hipStream_t
     case 4: launch_one<OP, 4>(p, sp, s); break;
     case 6: launch_one<OP, 6>(p, sp, s); break;
     case 8: launch_one<OP, 8>(p, sp, s); break;
-    case 10: launch_one<OP, 10>(p, sp, s); break;
-    default: launch_one<OP, 12>(p, sp, s); break;
+    default: launch_one<OP, 10>(p, sp, s); break;
   }
 }
 
 constexpr int kChunk = 2048;     // outputs per launch (bounds the workspace)
-constexpr int kMaxSliceLen = 12 * 4 * kLoadThreads;
+constexpr int kMaxNv = 10;  // vectors per reading thread (12 spills the kernel)
+constexpr int kMaxSliceLen = kMaxNv * 4 * kLoadThreads;
 
 // The arrival counters and generation numbers sit at fixed offsets for the
 // largest chunk, so calls of any shape can share one workspace: counters are
@@ -820,7 +846,7 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
     if (W == 1 || (int64_t)(W - 1) * L < vocab) break;
   }
   int nv = (L / 4 + kLoadThreads - 1) / kLoadThreads;
-  nv = nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 6 ? 6 : nv <= 8 ? 8 : nv <= 10 ? 10 : 12;
+  nv = nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 6 ? 6 : nv <= 8 ? 8 : 10;
   const int ch = min(num_outputs, kChunk);
   plan.W = W;
   plan.L = L;

@@ -16,14 +16,14 @@ constexpr int kPreDraws = 4 * kWave;              // draws precomputed per outpu
 constexpr int kMaxRounds = 4096;                  // safety bound, never reached
 
 struct RowRef {
-  const float* x;
+  gptr<const float> x;
   int V;
   bool vec;
 };
 
 __device__ __forceinline__ void load4(const RowRef& r, int64_t idx, float (&v)[4]) {
   if (r.vec && idx + 3 < r.V) {
-    const float4 q = *reinterpret_cast<const float4*>(r.x + idx);
+    const float4 q = load_f4((gptr<const float4>)(r.x + idx));
     v[0] = q.x;
     v[1] = q.y;
     v[2] = q.z;
@@ -328,9 +328,9 @@ __device__ __forceinline__ bool predicate(float t, double mass_above, uint32_t c
 }
 
 __device__ __forceinline__ void write_sample(const SampleParams& P, int i, int tok, int rounds) {
-  P.samples[i] = tok;
-  if (P.valid) P.valid[i] = tok >= 0 ? 1 : 0;
-  if (P.rounds) P.rounds[i] = rounds;
+  as_global(P.samples)[i] = tok;
+  if (P.valid) as_global(P.valid)[i] = tok >= 0 ? 1 : 0;
+  if (P.rounds) as_global(P.rounds)[i] = rounds;
 }
 
 
@@ -341,10 +341,10 @@ __device__ void sample_row(const SampleParams& P, int i, SampleSmem& sm) {
   const int lane = lane_id();
   const int wave = wave_id();
 
-  const int row = P.indices ? P.indices[i] : i;
-  const int k = P.top_k_arr ? P.top_k_arr[i] : P.top_k;
-  const float pp = P.top_p_arr ? P.top_p_arr[i] : P.top_p;
-  const float mp = P.min_p_arr ? P.min_p_arr[i] : P.min_p;
+  const int row = P.indices ? as_global(P.indices)[i] : i;
+  const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
+  const float pp = P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
+  const float mp = P.min_p_arr ? as_global(P.min_p_arr)[i] : P.min_p;
   bool ok = row >= 0 && row < P.rows;
   if (OP == kOpTopK || OP == kOpTopKTopP) ok = ok && k > 0;
   if (OP == kOpTopP || OP == kOpTopKTopP) ok = ok && !isnan(pp);
@@ -353,8 +353,8 @@ __device__ void sample_row(const SampleParams& P, int i, SampleSmem& sm) {
     if (threadIdx.x == 0) write_sample(P, i, -1, 0);
     return;
   }
-  const uint64_t seed = P.seed_arr ? P.seed_arr[i] : P.seed;
-  const uint64_t offset = P.offset_arr ? P.offset_arr[i] : P.offset;
+  const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
   if (wave == 0) {
     if (OP == kOpNone) {
@@ -366,7 +366,7 @@ __device__ void sample_row(const SampleParams& P, int i, SampleSmem& sm) {
     }
   }
 
-  const RowRef r{P.probs + (int64_t)row * P.vocab, P.vocab, P.vec_ok != 0};
+  const RowRef r{as_global(P.probs + (int64_t)row * P.vocab), P.vocab, P.vec_ok != 0};
   const int n_tiles = (P.vocab + kTile - 1) / kTile;
 
   // pass 0: tile masses (mass above low = 0), max bits, validity

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kBlock) void stream_renorm_kernel(RenormParams P) {
   __shared__ RedSmem red;
   const int row = blockIdx.x;
   const int V = P.vocab;
-  const RowRef r{P.in + (int64_t)row * V, V, P.vec_ok != 0};
+  const RowRef r{as_global(P.in + (int64_t)row * V), V, P.vec_ok != 0};
   float* out = P.out + (int64_t)row * V;
   const int nvec = (V + 3) / 4;
   const int k = P.top_k_arr ? P.top_k_arr[row] : P.top_k;
