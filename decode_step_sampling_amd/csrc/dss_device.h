@@ -156,7 +156,11 @@ __device__ __forceinline__ Philox4x64 philox4x64_10(uint64_t c0, uint64_t c1, ui
 __device__ __forceinline__ double draw_uniform(uint64_t seed, uint64_t offset, uint64_t sid,
                                                uint32_t r) {
   const Philox4x64 b = philox4x64_10(offset, sid, (uint64_t)(r >> 2), 0ull, seed, 0ull);
-  return (double)(b.w[r & 3] >> 11) * 0x1p-53;
+  // a select chain rather than b.w[r & 3]: a dynamic index would put the
+  // block in scratch memory, and any scratch slows every wave's launch
+  const uint32_t j = r & 3u;
+  const uint64_t w = j == 0u ? b.w[0] : j == 1u ? b.w[1] : j == 2u ? b.w[2] : b.w[3];
+  return (double)(w >> 11) * 0x1p-53;
 }
 
 // ---------------------------------------------------------------------------

@@ -86,10 +86,7 @@ struct SplitSmem {
       uint32_t bits[kWaves][kWaveCap + kWave];  // per-wave appends during the read,
       uint32_t idx[kWaves][kWaveCap + kWave];   // then one dummy slot per lane
     } pw;
-    struct {
-      alignas(16) uint32_t h2[H1::kWords];
-      alignas(16) uint32_t h3[H3::kWords];
-    } sel;                          // k-th largest, passes 2 and 3
+    uint64_t bnd[kRowCandMax];      // candidates in the bin of the k-th largest
     stream::SampleSmem stream;      // streaming fallback
   } a;
   uint64_t cand[kRowCandMax];       // candidates (bits | index << 32)
@@ -106,6 +103,7 @@ struct SplitSmem {
   int flag;
 };
 static_assert(sizeof(SplitSmem) <= 160 * 1024, "LDS budget of one gfx950 work-group");
+static_assert(kMaxSlices <= kWaves, "per-slice counts reuse the per-wave count slots");
 
 __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
@@ -211,8 +209,8 @@ __device__ __forceinline__ bool split_predicate(double mass_above, uint32_t coun
 
 // ---------------------------------------------------------------------------
 // The dual-pivot loop on one wave (no barriers).  cand[0..m) holds every
-// value of the row above `low` (and nothing at or below it); S is their
-// mass.  Lane l owns the contiguous entries [l*E, l*E + E), held in NR
+// value of the row above `low` (and nothing at or below it); their mass is
+// the kept mass Z_k, and the top-p bound is pfrac * Z_k.  Lane l owns the contiguous entries [l*E, l*E + E), held in NR
 // registers (NR >= E; NR = 0: read from LDS), and the inverse-transform draw runs over
 // the entries in that order (blog, 逆变换采样).  Guards as in the streaming
 // engine (blog, 实现细节): only entries with nonzero mass are chosen, the
@@ -220,8 +218,8 @@ __device__ __forceinline__ bool split_predicate(double mass_above, uint32_t coun
 // sum the last entry is taken.
 // ---------------------------------------------------------------------------
 template <int OP, int NR>
-__device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int k, double pz,
-                         double S, uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
+__device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int k, float pfrac,
+                         uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
   constexpr bool REG = NR > 0;
   const int lane = lane_id();
   const int E = (m + kWave - 1) / kWave;
@@ -245,6 +243,8 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int 
     const float x = X(j);
     if (x > low) part += (double)x;
   }
+  double S = wave_sum(part);  // mass above low: the kept mass Z_k at the start
+  const double pz = (double)pfrac * S;
   int rnd = 0;
   while (true) {
     const double u = rnd < stream::kPreDraws ? sm.draws[rnd]
@@ -503,24 +503,34 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 
   // The slice's bound t_bits and its list: the appended values (fast path),
   // else a full histogram of the slice and a compaction into sm.cand.  The
-  // full path re-reads the slice (from L2) rather than keeping it in
-  // registers: only flat rows take it, and freeing v[] keeps the common path
-  // free of spills.
+  // full path reads the slice again (it is in L2 now) into fresh registers,
+  // every reading thread's vectors in flight at once, rather than keeping
+  // v[] alive: only flat rows and rare short samples take it, and freeing
+  // v[] keeps the common path free of spills.
   uint32_t t_bits, cnt;
   if (fast) {
     t_bits = t_prov;
     cnt = tot;
   } else {
+    float4 w[NV];
+    if (reader) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) w[j] = load_f4(src + min(rt + j * kLoadThreads, nvec - 1));
+    }
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
     __syncthreads();
     uint32_t mx = 0u;
-    for (int f = tid; f < nvec; f += kBlock) {
-      const float4 x = load_f4(src + f);
-      const uint32_t q[4] = {bits_of(x.x), bits_of(x.y), bits_of(x.z), bits_of(x.w)};
+    if (reader) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mx = max(mx, q[e]);
-        atomicAdd(&sm.hist[H1::at(min(q[e] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
+      for (int j = 0; j < NV; ++j) {
+        if (rt + j * kLoadThreads < nvec) {
+          const uint32_t q[4] = {bits_of(w[j].x), bits_of(w[j].y), bits_of(w[j].z), bits_of(w[j].w)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            mx = max(mx, q[e]);
+            atomicAdd(&sm.hist[H1::at(min(q[e] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
+          }
+        }
       }
     }
     mx = wave_max(mx);
@@ -530,24 +540,32 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     block_find<kHistBins>(sm.hist, need, bin, above, total, sm);  // its barrier publishes wmax[]
     t_bits = bin << 20;
     uint32_t mine = 0u;
-    for (int f = tid; f < nvec; f += kBlock) {
-      const float4 x = load_f4(src + f);
-      mine += (uint32_t)(bits_of(x.x) >= t_bits) + (uint32_t)(bits_of(x.y) >= t_bits) +
-              (uint32_t)(bits_of(x.z) >= t_bits) + (uint32_t)(bits_of(x.w) >= t_bits);
+    if (reader) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        if (rt + j * kLoadThreads < nvec) {
+          mine += (uint32_t)(bits_of(w[j].x) >= t_bits) + (uint32_t)(bits_of(w[j].y) >= t_bits) +
+                  (uint32_t)(bits_of(w[j].z) >= t_bits) + (uint32_t)(bits_of(w[j].w) >= t_bits);
+        }
+      }
     }
     uint32_t pos = block_excl_scan(mine, cnt, sm);
     slice_max = 0u;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) slice_max = max(slice_max, sm.wmax[q]);
-    if (cnt <= (uint32_t)kSliceCandMax && slice_max < 0x7F800000u) {  // thread-major order
-      for (int f = tid; f < nvec; f += kBlock) {
-        const float4 x = load_f4(src + f);
-        const uint32_t q[4] = {bits_of(x.x), bits_of(x.y), bits_of(x.z), bits_of(x.w)};
+    if (reader && cnt <= (uint32_t)kSliceCandMax && slice_max < 0x7F800000u) {
+      // thread-major order
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (q[e] >= t_bits) {
-            sm.cand[pos] = (uint64_t)q[e] | ((uint64_t)(uint32_t)(s0 + 4 * f + e) << 32);
-            ++pos;
+      for (int j = 0; j < NV; ++j) {
+        const int f = rt + j * kLoadThreads;
+        if (f < nvec) {
+          const uint32_t q[4] = {bits_of(w[j].x), bits_of(w[j].y), bits_of(w[j].z), bits_of(w[j].w)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (q[e] >= t_bits) {
+              sm.cand[pos] = (uint64_t)q[e] | ((uint64_t)(uint32_t)(s0 + 4 * f + e) << 32);
+              ++pos;
+            }
           }
         }
       }
@@ -557,9 +575,11 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const bool overflow = cnt > (uint32_t)kSliceCandMax;
   const bool publish = !bad && !overflow;
 
-  uint32_t gmax, tstar, ntot;
+  uint32_t gmax, tstar;
+  uint64_t ent[kPer];  // thread t's candidates
+  uint32_t live = 0u;  // bit q: ent[q] is a candidate >= t*
   if (W == 1) {
-    // the whole row is in this work-group: candidates into sm.cand
+    // the whole row is in this work-group: candidates via sm.cand
     if (fast && publish && wave > 0) {
       const uint32_t c = sm.wcnt[wave];
       for (uint32_t p = lane; p < c; p += kWave)
@@ -573,7 +593,15 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     if (overflow) return kFallback;
     gmax = slice_max;
     tstar = t_bits;
-    ntot = cnt;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const uint32_t g = (uint32_t)(tid + q * kBlock);
+      ent[q] = g < cnt ? sm.cand[g] : 0ull;
+      if (g < cnt) live |= 1u << q;
+    }
+    __syncthreads();  // sm.cand is read (it is rewritten below)
+    clear_hist<kHistBins>(sm.hist, tid, kBlock);
+    __syncthreads();
   } else {
     const gptr<uint64_t> dst = as_global(S.cand + ((int64_t)li * W + s) * kSliceCandMax);
     if (publish) {
@@ -609,8 +637,24 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     if (!sm.flag) return kDone;
 
     // ---- phase B: the last slice work-group of the row ----------------------
-    // wave 0 reads the W headers (lane q: slice q) and sums them up; every
-    // thread clears the selection histograms meanwhile
+    // Every thread loads its slots of the slices' lists at once, without
+    // waiting for the counts: slot G = t + 1024 q is position G % win of
+    // slice G / win, win = 8192 / W.  Meanwhile wave 0 reads the W headers
+    // (lane q: slice q) and sums them up, and every thread clears the
+    // histogram.  A slot is a candidate if its position is below its
+    // slice's count; a slice whose list is longer than its window sends the
+    // row to an exact gather.
+    const uint32_t win = (uint32_t)(kRowCandMax / W);  // <= kSliceCandMax for W >= 2
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const uint32_t G = (uint32_t)(tid + q * kBlock);
+      const uint32_t sl = G / win;  // == W for the last slots when W does not divide 8192
+      ent[q] = 0ull;
+      if (sl < (uint32_t)W)
+        ent[q] = __hip_atomic_load(
+            as_global(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (G - sl * win)),
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (wave == 0) {
       const uint32_t me = xcc_id();
       const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
@@ -630,17 +674,20 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       }
       const bool foreign = __ballot(mine && (hg != mygen || hx != me)) != 0ull;
       const bool ovf = __ballot(mine && hc > (uint32_t)kSliceCandMax) != 0ull;  // kNoList too
+      const bool spill = __ballot(mine && hc <= (uint32_t)kSliceCandMax && hc > win) != 0ull;
       const uint32_t cc = (mine && hc <= (uint32_t)kSliceCandMax) ? hc : 0u;
       const uint32_t incl = wave_incl_scan(cc);
       const uint32_t all = lane63(incl);
       const uint32_t gm = wave_max(hm);
       const uint32_t ts = wave_max(ht);
       if (lane <= kMaxSlices) sm.off[lane] = lane < W ? incl - cc : all;
+      if (lane < kMaxSlices) sm.wcnt[lane] = cc;  // per-slice counts (0 past W)
       if (lane == 0) {
-        uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back
+        uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back, 3: exact gather
         if (foreign) status = 2u;
         else if (gm >= 0x7F800000u || gm == 0u) status = 1u;
         else if (ovf || all > (uint32_t)kRowCandMax) status = 2u;
+        else if (spill) status = 3u;
         sm.res[0] = ts;
         sm.res[1] = all;
         sm.res[2] = gm;
@@ -649,143 +696,175 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
     __syncthreads();
-    if (sm.res[3] == 1u) {
+    const uint32_t status = sm.res[3];
+    if (status == 1u) {
       if (tid == 0) stream::write_sample(P, i, -1, 0);
       return kDone;
     }
-    if (sm.res[3] == 2u) return kFallback;
+    if (status == 2u) return kFallback;
     tstar = sm.res[0];
-    ntot = sm.res[1];
     gmax = sm.res[2];
-  }
-
-  // ---- candidates into registers: thread t holds entries t + 1024 q ---------
-  uint64_t ent[kPer];
-  if (W == 1) {
+    if (status == 0u) {
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const uint32_t g = (uint32_t)(tid + q * kBlock);
-      ent[q] = g < ntot ? sm.cand[g] : 0ull;
-    }
-    __syncthreads();  // sm.a.pw (read above) is dead; sm.cand is read
-    clear_hist<kHistBins>(sm.hist, tid, kBlock);
-    __syncthreads();
-  } else {
-    // the slice of entry g: the last q < W with off[q] <= g (off is
-    // non-decreasing); the offsets in scalar registers, every load issued
-    // before any is used
-    uint32_t off[kMaxSlices];
+      for (int q = 0; q < kPer; ++q) {
+        const uint32_t G = (uint32_t)(tid + q * kBlock);
+        const uint32_t sl = G / win;
+        if (sl < (uint32_t)W && G - sl * win < sm.wcnt[sl]) live |= 1u << q;
+      }
+    } else {
+      // exact gather: entry g of the row's concatenated lists is position
+      // g - off[sl] of slice sl, the last slice with off[sl] <= g (the
+      // offsets in scalar registers; every load issued before any is used)
+      const uint32_t ntot = sm.res[1];
+      uint32_t off[kMaxSlices];
 #pragma unroll
-    for (int q = 0; q < kMaxSlices; ++q)
-      off[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.off[q]);
+      for (int q = 0; q < kMaxSlices; ++q)
+        off[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.off[q]);
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const uint32_t g = (uint32_t)(tid + q * kBlock);
-      int sl = 0;
-      uint32_t base = 0u;
+      for (int q = 0; q < kPer; ++q) {
+        const uint32_t g = (uint32_t)(tid + q * kBlock);
+        int sl = 0;
+        uint32_t base = 0u;
 #pragma unroll
-      for (int t = 1; t < kMaxSlices; ++t) {
-        if (t < W && off[t] <= g) {
-          sl = t;
-          base = off[t];
+        for (int t = 1; t < kMaxSlices; ++t) {
+          if (t < W && off[t] <= g) {
+            sl = t;
+            base = off[t];
+          }
+        }
+        ent[q] = 0ull;
+        if (g < ntot) {
+          ent[q] = __hip_atomic_load(
+              as_global(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (g - base)),
+              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          live |= 1u << q;
         }
       }
-      ent[q] = 0ull;
-      if (g < ntot)
-        ent[q] = __hip_atomic_load(
-            as_global(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (g - base)),
-            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  clear_hist<kHistBins>(sm.a.sel.h2, tid, kBlock);
-  clear_hist<kFineBins>(sm.a.sel.h3, tid, kBlock);
-  // an entry takes part if it exists and is >= t* (bits of valid values have
-  // bit 31 clear, so bits >> 20 is a bin of the 2048)
-  uint32_t live = 0u;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const uint32_t g = (uint32_t)(tid + q * kBlock);
-    if (g < ntot && (uint32_t)ent[q] >= tstar) live |= 1u << q;
-  }
-
-  // ---- tau_k: the k-th largest candidate, three histogram passes ------------
+  // candidates below t* take no part (bits of valid values have bit 31
+  // clear, so bits >> 20 is a bin of the 2048)
 #pragma unroll
   for (int q = 0; q < kPer; ++q)
-    if (live & (1u << q))
-      atomicAdd(&sm.hist[H1::at(((uint32_t)ent[q] >> 20) & (kHistBins - 1))], 1u);
+    if ((uint32_t)ent[q] < tstar) live &= ~(1u << q);
+
+  // ---- tau_k, first pass: a histogram of bits [30:20] ------------------------
+  // Most candidates sit in the few bins just above t*: the four bins from
+  // t*'s are counted in 8-bit register fields and added once per wave, the
+  // rest go straight to LDS.
+  const uint32_t b0 = tstar >> 20;
+  uint32_t packed = 0u;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (live & (1u << q)) {
+      const uint32_t bq = ((uint32_t)ent[q] >> 20) & (kHistBins - 1);
+      const uint32_t d = bq - b0;
+      if (d < 4u) packed += 1u << (8u * d);
+      else atomicAdd(&sm.hist[H1::at(bq)], 1u);
+    }
+  }
+  {
+    const uint32_t even = wave_sum(packed & 0x00FF00FFu);         // fields 0 and 2
+    const uint32_t odd = wave_sum((packed >> 8) & 0x00FF00FFu);   // fields 1 and 3
+    if (lane == 0) {
+      const uint32_t c4[4] = {even & 0xFFFFu, odd & 0xFFFFu, even >> 16, odd >> 16};
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        if (c4[d] != 0u && b0 + d < (uint32_t)kHistBins) atomicAdd(&sm.hist[H1::at(b0 + d)], c4[d]);
+    }
+  }
   __syncthreads();
   uint32_t bin1, above1, nstar;
   block_find<kHistBins>(sm.hist, (uint32_t)k, bin1, above1, nstar, sm);
-  uint32_t tau_k = 0u;
-  if (nstar >= (uint32_t)k) {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if ((live & (1u << q)) && ((uint32_t)ent[q] >> 20) == bin1)
-        atomicAdd(&sm.a.sel.h2[H1::at(((uint32_t)ent[q] >> 9) & (kHistBins - 1))], 1u);
-    __syncthreads();
-    uint32_t bin2, above2, t2;
-    block_find<kHistBins>(sm.a.sel.h2, (uint32_t)k - above1, bin2, above2, t2, sm);
-    const uint32_t hi = (bin1 << 11) | bin2;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if ((live & (1u << q)) && ((uint32_t)ent[q] >> 9) == hi)
-        atomicAdd(&sm.a.sel.h3[H3::at((uint32_t)ent[q] & (kFineBins - 1))], 1u);
-    __syncthreads();
-    uint32_t bin3, above3, t3;
-    block_find<kFineBins>(sm.a.sel.h3, (uint32_t)k - above1 - above2, bin3, above3, t3, sm);
-    tau_k = (hi << 9) | bin3;
-  } else if (tstar > 0u) {
-    return kFallback;  // guard: fewer than k values at or above t* (not reached)
-  }
+  if (nstar < (uint32_t)k && tstar > 0u) return kFallback;  // guard: fewer than k at or above t*
+  const bool all_kept = nstar < (uint32_t)k;  // t* = 0 and k above the row's nonzero count
 
-  // ---- the top-k set {x >= tau_k} into sm.cand, with its mass Z_k -----------
-  uint32_t keep = 0u, nk = 0u;
-  double zk = 0.0;
+  // ---- the candidates above bin1 into sm.cand, those in bin1 into a side
+  // list (both in (thread, slot) order, one packed scan) -----------------------
+  uint32_t na = 0u, nb = 0u, ma = 0u, mb2 = 0u;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    const uint32_t x = (uint32_t)ent[q];
-    if ((live & (1u << q)) && x >= tau_k && x > 0u) {
-      keep |= 1u << q;
-      ++nk;
-      zk += (double)__uint_as_float(x);
+    if (live & (1u << q)) {
+      const uint32_t x = (uint32_t)ent[q];
+      const uint32_t bq = (x >> 20) & (kHistBins - 1);
+      if (all_kept ? x > 0u : bq > bin1) {
+        ma |= 1u << q;
+        ++na;
+      } else if (!all_kept && bq == bin1) {
+        mb2 |= 1u << q;
+        ++nb;
+      }
     }
   }
-  const uint32_t incl = wave_incl_scan(nk);
-  zk = wave_sum(zk);
-  if (lane == kWave - 1) {
-    sm.red_u[wave] = incl;
-    sm.red_d[wave] = zk;
-  }
+  const uint32_t pk = na | (nb << 16);  // each field stays below 2^14
+  const uint32_t pincl = wave_incl_scan(pk);
+  if (lane == kWave - 1) sm.red_u[wave] = pincl;
   __syncthreads();
-  uint32_t pos = 0u, m = 0u;
-  double Z = 0.0;
+  uint32_t pbase = 0u, ptot = 0u;
 #pragma unroll
   for (int q = 0; q < kWaves; ++q) {
-    pos += q < wave ? sm.red_u[q] : 0u;
-    m += sm.red_u[q];
-    Z += sm.red_d[q];
+    const uint32_t t = sm.red_u[q];
+    pbase += q < wave ? t : 0u;
+    ptot += t;
   }
-  pos += incl - nk;
+  uint32_t pa = (pbase + pincl - pk) & 0xFFFFu, pb = (pbase + pincl - pk) >> 16;
+  uint64_t* bnd = sm.a.bnd;
 #pragma unroll
-  for (int q = 0; q < kPer; ++q)
-    if (keep & (1u << q)) sm.cand[pos++] = ent[q];
+  for (int q = 0; q < kPer; ++q) {
+    if (ma & (1u << q)) sm.cand[pa++] = ent[q];
+    if (mb2 & (1u << q)) bnd[pb++] = ent[q];
+  }
   __syncthreads();
   if (wave != 0) return kDone;
 
+  // ---- wave 0 from here on: tau_k inside bin1, the top-k list, the loop -----
+  uint32_t m = ptot & 0xFFFFu;
+  uint32_t tau_k = 0u;
+  if (!all_kept) {
+    const uint32_t nbt = ptot >> 16;
+    const uint32_t need2 = (uint32_t)k - above1;  // 1 <= need2 <= nbt
+    // bits [19:9] then [8:0] of the boundary entries, in sm.hist (one wave:
+    // its LDS operations are ordered, no barrier needed)
+    uint32_t bin2, above2, t2, bin3, above3, t3;
+    clear_hist<kHistBins>(sm.hist, lane, kWave);
+    for (uint32_t c = lane; c < nbt; c += kWave)
+      atomicAdd(&sm.hist[H1::at(((uint32_t)bnd[c] >> 9) & (kHistBins - 1))], 1u);
+    wave_find<kHistBins>(sm.hist, need2, bin2, above2, t2);
+    const uint32_t hi = (bin1 << 11) | bin2;
+    clear_hist<kFineBins>(sm.hist, lane, kWave);
+    for (uint32_t c = lane; c < nbt; c += kWave) {
+      const uint32_t x = (uint32_t)bnd[c];
+      if ((x >> 9) == hi) atomicAdd(&sm.hist[H3::at(x & (kFineBins - 1))], 1u);
+    }
+    wave_find<kFineBins>(sm.hist, need2 - above2, bin3, above3, t3);
+    tau_k = (hi << 9) | bin3;
+    // the boundary entries >= tau_k follow the others, in list order
+    for (uint32_t c0 = 0; c0 < nbt; c0 += kWave) {
+      const uint32_t c = c0 + lane;
+      const uint64_t en = c < nbt ? bnd[c] : 0ull;
+      const bool take = c < nbt && (uint32_t)en >= tau_k && (uint32_t)en > 0u;
+      const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
+      const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(tm >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)tm, 0u));
+      if (take) sm.cand[m + pos] = en;
+      m += (uint32_t)__popcll(tm);
+    }
+  }
+
   // ---- the dual-pivot loop on wave 0 ----------------------------------------
-  const double pz = OP == kOpTopKTopP ? (double)stream::clamp01(pp) * Z : 0.0;
+  const float pfrac = OP == kOpTopKTopP ? stream::clamp01(pp) : 0.0f;
   const float low = tau_k > 0u ? __uint_as_float(tau_k - 1u) : 0.0f;
   int rounds = 0;
   const float high = __uint_as_float(gmax);
   int e;
   if (m <= 4 * kWave) {
-    e = wave_loop<OP, 4>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+    e = wave_loop<OP, 4>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
   } else if (m <= 8 * kWave) {
-    e = wave_loop<OP, 8>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+    e = wave_loop<OP, 8>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
   } else if (m <= 16 * kWave) {
-    e = wave_loop<OP, 16>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+    e = wave_loop<OP, 16>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
   } else {  // (32 entries per lane in registers would spill the kernel)
-    e = wave_loop<OP, 0>(sm, (int)m, low, high, k, pz, Z, seed, offset, sid, rounds);
+    e = wave_loop<OP, 0>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
   }
   if (lane == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
   return kDone;

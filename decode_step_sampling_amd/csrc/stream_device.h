@@ -337,7 +337,7 @@ __device__ __forceinline__ void write_sample(const SampleParams& P, int i, int t
 // Sample output i with the streaming engine; every thread of the
 // work-group must call this (it contains barriers).
 template <int OP>
-__device__ void sample_row(const SampleParams& P, int i, SampleSmem& sm) {
+__device__ __forceinline__ void sample_row(const SampleParams& P, int i, SampleSmem& sm) {
   const int lane = lane_id();
   const int wave = wave_id();
 

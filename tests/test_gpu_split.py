@@ -36,7 +36,10 @@ def _call(op, P, k, p, **kw):
 
 
 @pytest.mark.parametrize("op", ["top_k", "top_k_top_p"])
-@pytest.mark.parametrize("rows,vocab", [(64, 151936), (4, 32000), (1, 151936), (3, 8192)])
+# 86, 52 and 37 outputs give 3, 5 and 7 slices per row: windows of the
+# candidate gather that do not divide the 8192 slots evenly
+@pytest.mark.parametrize("rows,vocab", [(64, 151936), (4, 32000), (1, 151936), (3, 8192),
+                                        (86, 16384), (52, 50000), (37, 32000)])
 def test_split_support_and_validity(op, rows, vocab):
     w = si.renorm(rows=rows, vocab=vocab)
     probs = w["probs"]
