@@ -4,67 +4,64 @@
 // Kernels for LLM Sampling", section 双枢轴拒绝采样) only ever draws from the
 // values above the current `low`, and its correctness proof (section
 // 拒绝采样器正确性的理论证明) holds from any starting pivot below every kept
-// value.  This engine therefore:
+// value.  The engine therefore reads each row from HBM exactly once and runs
+// the loop on the row's top-k set only:
 //
-//  1. splits each row into W slices, one 1024-thread work-group per slice.
-//     Waves 1..15 read the slice from HBM exactly once into registers
-//     (16-byte loads, all issued up front); wave 0 clears the histogram and
-//     computes the row's first 256 Philox draws while the slice is in
-//     flight;
-//  2. from the first landed vector of every reading thread (3840 values) the
-//     slice takes a provisional bound: the edge of a 1/8-binade bin of the
-//     float32 bit patterns (bits >> 20) above which about 1.5 k + 64 of the
-//     slice's values should lie.  As each vector lands the reading waves
-//     append the values at or above that bound, with their indices, to
-//     per-wave LDS lists.  If the lists hold at least k values the bound
-//     stands (it is then at most the slice's k-th largest value); otherwise
-//     the slice is histogrammed in full and the exact 1/8-binade bound of
-//     its k-th largest value is used.  Each slice publishes its bound and
-//     its list.  The union over slices contains every value >= t* = max_s t_s
-//     of the row, and at least k of them;
-//  3. the last slice work-group of the row to finish (a relaxed arrival
-//     counter) gathers the candidates into registers, finds the k-th largest
-//     tau_k with three histogram passes over the bit fields [30:20], [19:9]
-//     and [8:0] (the F4 note's threshold search on the float32 bit pattern,
-//     §③, done 2048 ways per pass instead of 2 or 3), compacts the values
-//     >= tau_k with their mass Z_k, and one wave runs the dual-pivot loop on
-//     them from just below tau_k, where f(low) = 0 still holds.
+//  1. Each row is cut into W slices, one 1024-thread work-group per slice;
+//     every thread issues all of its 16-byte loads of the slice at once.  As
+//     each vector lands the thread takes its maximum (on the float32 bit
+//     pattern, which orders non-negative values like the values, F4 note §③)
+//     and counts it in a 2048-bin LDS histogram of the top eleven bits.
+//  2. The slice bound b is the lower edge of the histogram bin holding the
+//     k-th largest vector maximum.  At least k vectors, hence at least k
+//     values, are >= b, so b never exceeds the slice's k-th largest value and
+//     therefore never exceeds the row's: every value of the row's top-k set
+//     lies at or above the bound of its slice.  No estimate is involved.
+//  3. Vectors holding a value >= b are staged in LDS (one block scan), their
+//     elements >= b are extracted (a second scan) and published as
+//     (bits | index << 32) entries.
+//  4. The last work-group of the row to arrive (a relaxed arrival counter)
+//     loads every slice's entries, keeps those >= t* = max_s b_s (the row's
+//     top-k set lies above t*, and at least k entries do), finds the k-th
+//     largest tau_k with a histogram on a key relative to t* followed by an
+//     exact rank inside the boundary bin, and one wave runs the dual-pivot
+//     loop on the values >= tau_k, starting just below tau_k, where f(low) = 0
+//     still holds.
 //
 // All W work-groups of a row are placed on one XCD (work-groups are dispatched
 // to the eight XCDs round-robin, so block b runs on XCD b % 8), which lets the
 // hand-off use the XCD's shared L2 with relaxed atomics instead of
-// device-wide acquire/release fences (measured at several microseconds each
-// on gfx950).  Every published header carries the row's generation number and
-// the writer's XCC id; the finishing work-group checks both and falls back to
-// the streaming engine (stream_device.h) if anything looks foreign, if a
-// slice overflowed its candidate buffer, or if k is too large to bound.
+// device-wide acquire/release fences.  Every published header carries the
+// row's generation number and the writer's XCC id; the finishing work-group
+// checks both and falls back to the streaming engine (stream_device.h) if
+// anything looks foreign, or if a list overflows its capacity (flat rows).
 #include "stream_device.h"
 
 namespace dss {
 namespace {
 
-constexpr int kLoadWaves = kWaves - 1;             // waves 1..15 read the slice
-constexpr int kLoadThreads = kLoadWaves * kWave;   // 960
 constexpr int kHistBins = 2048;
-constexpr int kFineBins = 512;
-constexpr int kSliceCandMax = 4096;
-constexpr int kWaveCap = 448;  // per-wave append list during the read
-constexpr int kRowCandMax = 8192;
-constexpr int kPer = kRowCandMax / kBlock;  // gathered entries per thread
-constexpr int kSplitKCap = 1536;
-constexpr int kMaxSlices = 16;
+constexpr int kStageMax = 2048;   // vectors a slice stages in LDS
+constexpr int kListMax = 4096;    // entries a slice publishes
+constexpr int kRowCandMax = 8192; // entries of all slices of a row (the merge's LDS copy)
+constexpr int kKeptMax = 4096;    // entries of the top-k set (ties included)
+constexpr int kBndMax = 4096;     // entries in the boundary bin
+constexpr int kSplitKCap = 2048;
+constexpr int kMaxSlices = 16;    // a power of two
 constexpr int kHdrWords = 8;
+constexpr int kLoadBatch = 8;     // list loads a merge thread keeps in flight
 constexpr uint32_t kNoList = 0xFFFFFFFFu;  // header count of a slice that published nothing
 
 struct SplitParams {
-  int W;           // slices per output
+  int W;           // slices per output (a power of two)
+  int wlog;        // log2(W)
   int L;           // slice length in values (multiple of 4)
   int out0;        // first output handled by this launch
   int n_out;       // outputs handled by this launch
   uint32_t* ctr;   // [kChunk] arrival counters (zero between calls)
   uint32_t* gen;   // [kChunk] generation numbers
   uint32_t* hdr;   // [n_out][W][kHdrWords]
-  uint64_t* cand;  // [n_out][W][kSliceCandMax]: bits | (index << 32)
+  uint64_t* list;  // [n_out][W][kListMax]: bits | (index << 32)
 };
 
 // Histograms are stored in chunks of NB/64 bins (the bins one lane sums in
@@ -78,32 +75,31 @@ struct Padded {
   static __device__ __forceinline__ uint32_t at(uint32_t b) { return b + 4u * (b / kChunk); }
 };
 using H1 = Padded<kHistBins>;
-using H3 = Padded<kFineBins>;
 
 struct SplitSmem {
+  uint64_t full[kRowCandMax];     // every slice's entries, in (slice, position) order
   union {
     struct {
-      uint32_t bits[kWaves][kWaveCap + kWave];  // per-wave appends during the read,
-      uint32_t idx[kWaves][kWaveCap + kWave];   // then one dummy slot per lane
-    } pw;
-    uint64_t bnd[kRowCandMax];      // candidates in the bin of the k-th largest
-    stream::SampleSmem stream;      // streaming fallback
-  } a;
-  uint64_t cand[kRowCandMax];       // candidates (bits | index << 32)
+      float4 vec[kStageMax];     // staged vectors
+      uint32_t vidx[kStageMax];  // their vector index inside the slice
+    } a;
+    struct {
+      uint64_t cand[kKeptMax];   // the top-k set, in candidate order
+      uint64_t bnd[kBndMax];     // entries in the boundary bin
+    } b;
+    stream::SampleSmem stream;   // streaming fallback
+  } u;
   alignas(16) uint32_t hist[H1::kWords];
   double draws[stream::kPreDraws];
-  double red_d[kWaves];
-  uint32_t red_u[kWaves];
-  uint32_t wcnt[kWaves];
+  uint32_t red[4][kWaves];        // per-wave partials of the block scans
   uint32_t wmax[kWaves];
   uint32_t off[kMaxSlices + 1];
-  uint32_t res[4];
+  uint32_t sel[kWave];
+  uint32_t res[8];
   uint32_t fres[4];
-  uint32_t tprov;  // provisional bound | 1 once set (0 until then)
   int flag;
 };
 static_assert(sizeof(SplitSmem) <= 160 * 1024, "LDS budget of one gfx950 work-group");
-static_assert(kMaxSlices <= kWaves, "per-slice counts reuse the per-wave count slots");
 
 __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
@@ -114,6 +110,15 @@ __device__ __forceinline__ int uwave() { return __builtin_amdgcn_readfirstlane(t
 
 __device__ __forceinline__ int first_lane(uint64_t m) { return __ffsll((long long)m) - 1; }
 __device__ __forceinline__ int last_lane(uint64_t m) { return 63 - __clzll((long long)m); }
+
+// position of this lane among the lanes set in m that are below it
+__device__ __forceinline__ uint32_t rank_in(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint32_t max4_bits(const float4& x) {
+  return max(max(bits_of(x.x), bits_of(x.y)), max(bits_of(x.z), bits_of(x.w)));
+}
 
 template <int NB>
 __device__ __forceinline__ void clear_hist(uint32_t* h, int t, int nt) {
@@ -126,21 +131,26 @@ __device__ __forceinline__ void clear_hist(uint32_t* h, int t, int nt) {
 // association order, so results are deterministic)
 // ---------------------------------------------------------------------------
 
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, SplitSmem& sm) {
+// Exclusive prefix of v over the work-group in thread order, and the total.
+// `red` must not be reused by another scan before every thread has returned
+// from this one.  Waves with `active` false (wave-uniform) contribute zeros
+// without computing anything.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* red,
+                                                    bool active = true) {
   const int lane = lane_id(), w = uwave();
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == kWave - 1) sm.red_u[w] = incl;
+  uint32_t incl = 0u;
+  if (active) incl = wave_incl_scan(v);
+  if (lane == kWave - 1) red[w] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int q = 0; q < kWaves; ++q) {
-    const uint32_t t = sm.red_u[q];
+    const uint32_t t = red[q];
     base += q < w ? t : 0u;
     tot += t;
   }
-  __syncthreads();
   total = tot;
-  return base + incl - v;
+  return active ? base + incl - v : 0u;
 }
 
 // Largest bin b of the padded histogram hist (NB bins) whose suffix count
@@ -179,69 +189,94 @@ __device__ void wave_find(const uint32_t* hist, uint32_t need, uint32_t& bin, ui
   above = lane_value(incl2 - h, L2);
 }
 
-// The same, answered by wave 0 and handed to every thread.  The histogram
-// must be complete (a barrier before the call); consecutive calls must be
-// separated by a barrier.
-template <int NB>
-__device__ void block_find(const uint32_t* hist, uint32_t need, uint32_t& bin, uint32_t& above,
-                           uint32_t& total, SplitSmem& sm) {
-  if (uwave() == 0) {
-    wave_find<NB>(hist, need, bin, above, total);
-    if (lane_id() == 0) {
-      sm.fres[0] = bin;
-      sm.fres[1] = above;
-      sm.fres[2] = total;
+// ---------------------------------------------------------------------------
+// The k-th largest value among the entries of bnd[0..n) whose bits lie in
+// [base, base + 2^sh), need of them counting from the top (1 <= need <= the
+// number in range).  One wave, no barriers: while more than 64 entries are
+// in range, a 2048-way histogram of the next bit field narrows the range
+// (the F4 note's threshold search on the bit pattern, §③); then every lane
+// takes one entry and counts the entries >= its own (an exact rank).
+// ---------------------------------------------------------------------------
+__device__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, uint32_t base, uint32_t sh,
+                             uint32_t need, uint32_t* hist, uint32_t* sel) {
+  const int lane = lane_id();
+  while (true) {
+    // entries in range, and (if at most 64) their bits in sel[]
+    uint32_t cnt = 0u;
+    for (uint32_t c0 = 0; c0 < n; c0 += kWave) {
+      const uint32_t c = c0 + lane;
+      const uint32_t x = c < n ? (uint32_t)bnd[c] : 0u;
+      const bool in = c < n && x - base < (1u << sh) && x >= base;
+      const uint64_t m = __ballot(in);
+      const uint32_t p = cnt + rank_in(m);
+      if (in && p < (uint32_t)kWave) sel[p] = x;
+      cnt += (uint32_t)__popcll(m);
     }
+    if (cnt <= (uint32_t)kWave || sh == 0u) {
+      if (sh == 0u) return base;  // one bit pattern left: every entry in range equals it
+      const uint32_t x = lane < (int)cnt ? sel[lane] : 0u;
+      uint32_t ge = 0u;
+      for (uint32_t j = 0; j < cnt; ++j) ge += (uint32_t)(sel[j] >= x);
+      const uint32_t cand = (lane < (int)cnt && ge >= need) ? x : 0u;
+      return wave_max(cand);
+    }
+    const uint32_t sh2 = sh > 11u ? sh - 11u : 0u;
+    clear_hist<kHistBins>(hist, lane, kWave);
+    for (uint32_t c = lane; c < n; c += kWave) {
+      const uint32_t x = (uint32_t)bnd[c];
+      if (x >= base && x - base < (1u << sh)) atomicAdd(&hist[H1::at((x - base) >> sh2)], 1u);
+    }
+    uint32_t bin, above, total;
+    wave_find<kHistBins>(hist, need, bin, above, total);
+    base += bin << sh2;
+    sh = sh2;
+    need -= above;
   }
-  __syncthreads();
-  bin = sm.fres[0];
-  above = sm.fres[1];
-  total = sm.fres[2];
-}
-
-template <int OP>
-__device__ __forceinline__ bool split_predicate(double mass_above, uint32_t count_above, int k,
-                                                double pz) {
-  const bool ok_k = count_above < (uint32_t)k;
-  if (OP == kOpTopK) return ok_k;
-  return ok_k && ((mass_above < pz) || count_above == 0u);
 }
 
 // ---------------------------------------------------------------------------
 // The dual-pivot loop on one wave (no barriers).  cand[0..m) holds every
-// value of the row above `low` (and nothing at or below it); their mass is
-// the kept mass Z_k, and the top-p bound is pfrac * Z_k.  Lane l owns the contiguous entries [l*E, l*E + E), held in NR
-// registers (NR >= E; NR = 0: read from LDS), and the inverse-transform draw runs over
-// the entries in that order (blog, 逆变换采样).  Guards as in the streaming
-// engine (blog, 实现细节): only entries with nonzero mass are chosen, the
-// first hit wins, and if rounding puts the target at or past every running
-// sum the last entry is taken.
+// value of the row above `low` and nothing at or below it, each > 0; their
+// mass is the kept mass Z_k, and the top-p bound is pfrac * Z_k.  Lane l
+// owns the contiguous entries [l*E, l*E + E), held in NR registers as
+// float64 (NR >= E; NR = 0: read from LDS), and the inverse-transform draw
+// runs over the entries in that order (blog, 逆变换采样).  Guards as in the
+// streaming engine (blog, 实现细节): only entries with nonzero mass are
+// chosen, the first hit wins, and if rounding puts the target at or past
+// every running sum the last entry is taken.
+//
+// Every pivot is one of the entries, so it is >= tau_k and fewer than k
+// values exceed it: the top-k half of f(t) always holds here, and f(t) of
+// top-k-then-top-p reduces to "the mass above t is below p * Z_k" (or no
+// value is above t).
 // ---------------------------------------------------------------------------
 template <int OP, int NR>
-__device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int k, float pfrac,
+__device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, float pfrac,
                          uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
   constexpr bool REG = NR > 0;
   const int lane = lane_id();
   const int E = (m + kWave - 1) / kWave;
   const int c0 = min(m, lane * E), c1 = min(m, c0 + E);
-  const uint64_t* cand = sm.cand;
-  float xr[REG ? NR : 1];
+  const uint64_t* cand = sm.u.b.cand;
+  double xr[REG ? NR : 1];
   if (REG) {
 #pragma unroll
-    for (int j = 0; j < NR; ++j) xr[j] = c0 + j < c1 ? __uint_as_float((uint32_t)cand[c0 + j]) : 0.0f;
+    for (int j = 0; j < NR; ++j)
+      xr[j] = c0 + j < c1 ? (double)__uint_as_float((uint32_t)cand[c0 + j]) : 0.0;
   }
-  // x of this lane's j-th entry (0.0 past the end: never above a pivot)
-  auto X = [&](int j) -> float {
+  // x of this lane's j-th entry (0 past the end: never above a pivot)
+  auto X = [&](int j) -> double {
     if (REG) return xr[j];
-    return c0 + j < c1 ? __uint_as_float((uint32_t)cand[c0 + j]) : 0.0f;
+    return c0 + j < c1 ? (double)__uint_as_float((uint32_t)cand[c0 + j]) : 0.0;
   };
-  const int n = REG ? NR : E;  // entries past c1 read as 0.0
+  const int n = REG ? NR : E;
 
+  double lo = (double)low;
   double part = 0.0;  // mass above low of this lane's entries
 #pragma unroll
   for (int j = 0; j < n; ++j) {
-    const float x = X(j);
-    if (x > low) part += (double)x;
+    const double x = X(j);
+    part += x > lo ? x : 0.0;
   }
   double S = wave_sum(part);  // mass above low: the kept mass Z_k at the start
   const double pz = (double)pfrac * S;
@@ -260,67 +295,52 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int 
       return -1;
     }
     const int owner = hit ? first_lane(hit) : last_lane(nz);
-    // the owner's entries, one per lane (a serial walk if a lane owns more
-    // than 64): first running sum past T, else the last entry above low
-    int e = -1;
-    const int o0 = min(m, owner * E), o1 = min(m, o0 + E);
-    const double base = lane_value(excl, owner);
-    if (o1 - o0 <= kWave) {
-      const int c = o0 + lane;
-      const float x = c < o1 ? __uint_as_float((uint32_t)cand[c]) : 0.0f;
-      const double xm = x > low ? (double)x : 0.0;
-      const double run = base + wave_incl_scan(xm);
-      const uint64_t h2 = __ballot(hit != 0ull && xm > 0.0 && run > T);
-      const uint64_t n2 = __ballot(xm > 0.0);
-      e = o0 + (h2 ? first_lane(h2) : last_lane(n2));
-    } else {
-      double run = base;
-      for (int c = o0; c < o1; ++c) {
-        const float x = __uint_as_float((uint32_t)cand[c]);
-        if (x > low) {
-          run += (double)x;
-          e = c;
-          if (hit != 0ull && run > T) break;
+    // The owner walks its own entries: the first running sum past T, else
+    // its last entry above low.
+    int pick = 0;
+    if (lane == owner) {
+      double run = excl;
+      int last = -1, found = -1;
+#pragma unroll
+      for (int j = 0; j < n; ++j) {
+        const double x = X(j);
+        if (x > lo) {
+          run += x;
+          last = j;
+          if (found < 0 && hit != 0ull && run > T) found = j;
         }
       }
+      pick = found >= 0 ? found : last;
     }
-    e = min(max(e, 0), m - 1);  // part > 0 guarantees an entry; keep the read in bounds regardless
+    // part > 0 guarantees the owner an entry; the clamp keeps reads in bounds regardless
+    const int e = min(max(__builtin_amdgcn_readlane(c0 + pick, owner), 0), m - 1);
     const uint64_t ent = cand[e];
-    const float pivot1 = __uint_as_float((uint32_t)ent);
-    const int token = (int)(ent >> 32);
     if (OP == kOpTopK) {
-      // every entry is >= tau_k, so fewer than k values exceed pivot1
       rounds = rnd;
-      return token;
+      return (int)(ent >> 32);
     }
+    const float pivot1 = __uint_as_float((uint32_t)ent);
     const float pivot2 = (float)(((double)pivot1 + (double)high) * 0.5);
+    const double p1 = (double)pivot1, p2 = (double)pivot2;
     double m0 = 0.0, m1 = 0.0;
-    uint32_t n0 = 0u, n1 = 0u;
 #pragma unroll
     for (int j = 0; j < n; ++j) {
-      const float x = X(j);
-      if (x > pivot1) {
-        m0 += (double)x;
-        ++n0;
-      }
-      if (x > pivot2) {
-        m1 += (double)x;
-        ++n1;
-      }
+      const double x = X(j);
+      m0 += x > p1 ? x : 0.0;
+      m1 += x > p2 ? x : 0.0;
     }
     const double M0 = wave_sum(m0), M1 = wave_sum(m1);
-    const uint32_t N0 = wave_sum(n0), N1 = wave_sum(n1);
-    if (split_predicate<OP>(M0, N0, k, pz)) {
+    if (M0 < pz || M0 == 0.0) {  // f(pivot1) = 1: accept
       rounds = rnd;
-      return token;
+      return (int)(ent >> 32);
     }
-    if (split_predicate<OP>(M1, N1, k, pz)) {
-      low = pivot1;
+    if (M1 < pz || M1 == 0.0) {  // f(pivot2) = 1: the kept set lies in (pivot1, pivot2]
+      lo = p1;
       high = pivot2;
       S = M0;
       part = m0;
     } else {
-      low = pivot2;
+      lo = p2;
       S = M1;
       part = m1;
     }
@@ -332,18 +352,6 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, int 
 }
 
 enum SplitMode : int { kDone = 0, kFallback = 1 };
-
-// Bounded wait for the provisional bound of wave 1.  Every wave gets out:
-// after the spin limit the bound 0 is used, which appends the whole slice,
-// overflows the lists and sends the slice down the full-histogram path.
-__device__ __forceinline__ uint32_t wait_tprov(SplitSmem& sm) {
-  for (int spin = 0; spin < (1 << 16); ++spin) {
-    const uint32_t t = __hip_atomic_load(&sm.tprov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (t & 1u) return t & ~1u;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  return 0u;
-}
 
 // Everything but the streaming fallback; returns kFallback when the output
 // must be sampled by the streaming engine instead (one call site, below).
@@ -376,251 +384,150 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
   const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
-  if (tid == 0) sm.tprov = 0u;
-  __syncthreads();  // before any load: costs little, orders the clear before the polls
 
   // ---- phase A: one HBM read of the slice into registers --------------------
   const int V = P.vocab;
   const int s0 = s * S.L;
   const int s1 = min(s0 + S.L, V);
   const int nvec = (s1 - s0) / 4;
-  const uint32_t n_s = (uint32_t)(s1 - s0);
-  // The slice's bound must not exceed its own k-th largest value; a slice
-  // shorter than k has none, and its bound is 0 (all of it is a candidate).
-  // The row's k-th largest is at least every slice's, so the maximum of the
-  // bounds keeps every value of the row's top k.
-  const uint32_t need = (uint32_t)k;
   const gptr<const float4> src =
       as_global(reinterpret_cast<const float4*>(P.probs + (int64_t)row * V + s0));
-  const bool reader = wave > 0;
-  const int rt = tid - kWave;  // reader thread index
-  // Loads are issued unconditionally (a lane past the end re-reads the last
-  // vector and ignores it) so that they sit in one basic block and every
+  // Loads are issued unconditionally (a thread past the end re-reads the
+  // last vector and ignores it) so that they sit in one basic block and every
   // later use waits only for its own vector, not for the whole slice.
   float4 v[NV];
-  if (reader) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = load_f4(src + min(rt + j * kLoadThreads, nvec - 1));
-  }
-  uint32_t gen = 0u;
-  if (reader) {
-    // Wave 1's loads go out first and land first: its values are the sample
-    // for the provisional bound, the edge of the 1/8-binade bin (bits >> 20)
-    // above which about 1.5 * need + 64 of the slice's values should lie.
-    uint32_t t_prov;
-    if (wave == 1) {
-      clear_hist<kHistBins>(sm.hist, lane, kWave);
-      uint32_t nsamp = 0u;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        if (rt + j * kLoadThreads < nvec) {
-          const uint32_t q[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            atomicAdd(&sm.hist[H1::at(min(q[e] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
-        }
-        nsamp += 4u * (uint32_t)__popcll(__ballot(rt + j * kLoadThreads < nvec));
-      }
-      const uint32_t r =
-          min(nsamp, max(1u, (uint32_t)(((1.5 * min(need, n_s) + 64.0) * nsamp) / n_s) + 1u));
-      uint32_t bin, above, total;
-      wave_find<kHistBins>(sm.hist, r, bin, above, total);
-      t_prov = n_s <= need ? 0u : bin << 20;
-      if (lane == 0) __hip_atomic_store(&sm.tprov, t_prov | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else {
-      t_prov = wait_tprov(sm);
-    }
+  for (int j = 0; j < NV; ++j) v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1));
 
-    // As each vector lands: the slice maximum (lanes past the end hold a
-    // copy of a real vector, so they may join in), and every value >= t_prov
-    // appended to this wave's list in (vector, element, lane) order.  Lanes
-    // with nothing to append write a dummy slot of their own, so the store
-    // needs no branch.  A list that could overflow with the next vector
-    // stops; its count is set past the cap, which sends the slice down the
-    // full-histogram path.
-    uint32_t mb = 0u;
-    uint32_t wcnt = 0u;  // wave-uniform
-    uint32_t* lbits = sm.a.pw.bits[wave];
-    uint32_t* lidx = sm.a.pw.idx[wave];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      if (wcnt > (uint32_t)(kWaveCap - 4 * kWave)) {
-        wcnt = kWaveCap + 1;
-        break;
-      }
-      const int f = rt + j * kLoadThreads;
-      const bool in = f < nvec;
-      // exec is full here, so the compare masks need no further masking
-      const uint64_t in_m = __builtin_amdgcn_uicmp((uint32_t)f, (uint32_t)nvec, 36);  // <
-      const uint32_t q[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
-      mb = max(max(mb, q[0]), q[1]);
-      mb = max(max(mb, q[2]), q[3]);
-      const uint32_t idx0 = (uint32_t)(s0 + 4 * f);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint64_t m = __builtin_amdgcn_uicmp(q[e], t_prov, 35) & in_m;  // >=
-        const bool sel = in && q[e] >= t_prov;
-        const uint32_t p = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        const uint32_t slot = sel ? wcnt + p : (uint32_t)(kWaveCap + lane);
-        lbits[slot] = q[e];
-        lidx[slot] = idx0 + (uint32_t)e;
-        wcnt += (uint32_t)__popcll(m);
-      }
-    }
-    mb = wave_max(mb);
-    if (lane == 0) {
-      sm.wcnt[wave] = wcnt;
-      sm.wmax[wave] = mb;
-      if (wave == 1) sm.res[0] = t_prov;
-    }
-  } else {
-    // wave 0: the row's arrival generation and the first 256 draws of the
-    // output's stream, while the slice lands
+  // while they are in flight: clear the histogram; wave 0 reads the row's
+  // generation and computes the first 256 draws of the output's stream
+  clear_hist<kHistBins>(sm.hist, tid, kBlock);
+  uint32_t gen = 0u;
+  if (wave == 0) {
     if (W > 1 && lane == 0)
       gen = __hip_atomic_load(as_global(S.gen + li), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const Philox4x64 ph = philox4x64_10(offset, sid, (uint64_t)lane, 0ull, seed, 0ull);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.draws[4 * lane + e] = (double)(ph.w[e] >> 11) * 0x1p-53;
+  }
+  __syncthreads();
+
+  // As each vector lands: its maximum, counted in the histogram of bits
+  // [30:20] (bin 2047 collects the patterns with the sign bit set).
+  uint32_t m4[NV];
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const bool in = tid + j * kBlock < nvec;
+    m4[j] = max4_bits(v[j]);
+    if (in) {
+      mx = max(mx, m4[j]);
+      atomicAdd(&sm.hist[H1::at(min(m4[j] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
+    }
+  }
+  mx = wave_max(mx);
+  if (lane == 0) sm.wmax[wave] = mx;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t bin, above, total;
+    wave_find<kHistBins>(sm.hist, (uint32_t)k, bin, above, total);
+    const uint32_t smax = wave_max(lane < kWaves ? sm.wmax[lane] : 0u);
     if (lane == 0) {
-      sm.wcnt[0] = 0u;
-      sm.wmax[0] = 0u;
+      sm.res[0] = total < (uint32_t)k ? 0u : bin << 20;  // fewer than k vectors: all of it
+      sm.res[1] = smax;
     }
   }
   __syncthreads();
-  const uint32_t t_prov = sm.res[0];
-  uint32_t tot = 0u, wbase = 0u, slice_max = 0u;
-  bool wave_ovf = false;
-#pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
-    const uint32_t c = sm.wcnt[q];
-    wbase += q < wave ? c : 0u;
-    tot += c;
-    wave_ovf |= c > (uint32_t)kWaveCap;
-    slice_max = max(slice_max, sm.wmax[q]);
-  }
-  const bool fast = !wave_ovf && (tot >= need || t_prov == 0u) && tot <= (uint32_t)kSliceCandMax;
+  const uint32_t bnd = sm.res[0];
+  const uint32_t smax = sm.res[1];
+  const bool bad = smax >= 0x7F800000u;  // a sign bit, an inf or a NaN somewhere
 
-  // The slice's bound t_bits and its list: the appended values (fast path),
-  // else a full histogram of the slice and a compaction into sm.cand.  The
-  // full path reads the slice again (it is in L2 now) into fresh registers,
-  // every reading thread's vectors in flight at once, rather than keeping
-  // v[] alive: only flat rows and rare short samples take it, and freeing
-  // v[] keeps the common path free of spills.
-  uint32_t t_bits, cnt;
-  if (fast) {
-    t_bits = t_prov;
-    cnt = tot;
-  } else {
-    float4 w[NV];
-    if (reader) {
+  // vectors with a value >= bnd, staged in thread order
+  uint32_t nv_hit = 0u;
 #pragma unroll
-      for (int j = 0; j < NV; ++j) w[j] = load_f4(src + min(rt + j * kLoadThreads, nvec - 1));
-    }
-    clear_hist<kHistBins>(sm.hist, tid, kBlock);
-    __syncthreads();
-    uint32_t mx = 0u;
-    if (reader) {
+  for (int j = 0; j < NV; ++j) nv_hit += (uint32_t)(tid + j * kBlock < nvec && m4[j] >= bnd);
+  uint32_t nstage;
+  uint32_t pos = block_excl_scan(nv_hit, nstage, sm.red[0]);
+  const bool stage_ok = !bad && nstage <= (uint32_t)kStageMax;
+  if (stage_ok) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        if (rt + j * kLoadThreads < nvec) {
-          const uint32_t q[4] = {bits_of(w[j].x), bits_of(w[j].y), bits_of(w[j].z), bits_of(w[j].w)};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            mx = max(mx, q[e]);
-            atomicAdd(&sm.hist[H1::at(min(q[e] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
-          }
-        }
-      }
-    }
-    mx = wave_max(mx);
-    __syncthreads();  // histogram complete; wmax free
-    if (lane == 0) sm.wmax[wave] = mx;
-    uint32_t bin, above, total;
-    block_find<kHistBins>(sm.hist, need, bin, above, total, sm);  // its barrier publishes wmax[]
-    t_bits = bin << 20;
-    uint32_t mine = 0u;
-    if (reader) {
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        if (rt + j * kLoadThreads < nvec) {
-          mine += (uint32_t)(bits_of(w[j].x) >= t_bits) + (uint32_t)(bits_of(w[j].y) >= t_bits) +
-                  (uint32_t)(bits_of(w[j].z) >= t_bits) + (uint32_t)(bits_of(w[j].w) >= t_bits);
-        }
-      }
-    }
-    uint32_t pos = block_excl_scan(mine, cnt, sm);
-    slice_max = 0u;
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) slice_max = max(slice_max, sm.wmax[q]);
-    if (reader && cnt <= (uint32_t)kSliceCandMax && slice_max < 0x7F800000u) {
-      // thread-major order
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int f = rt + j * kLoadThreads;
-        if (f < nvec) {
-          const uint32_t q[4] = {bits_of(w[j].x), bits_of(w[j].y), bits_of(w[j].z), bits_of(w[j].w)};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (q[e] >= t_bits) {
-              sm.cand[pos] = (uint64_t)q[e] | ((uint64_t)(uint32_t)(s0 + 4 * f + e) << 32);
-              ++pos;
-            }
-          }
-        }
+    for (int j = 0; j < NV; ++j) {
+      if (tid + j * kBlock < nvec && m4[j] >= bnd) {
+        sm.u.a.vec[pos] = v[j];
+        sm.u.a.vidx[pos] = (uint32_t)(tid + j * kBlock);
+        ++pos;
       }
     }
   }
-  const bool bad = slice_max >= 0x7F800000u;  // a sign bit, an inf or a NaN somewhere
-  const bool overflow = cnt > (uint32_t)kSliceCandMax;
-  const bool publish = !bad && !overflow;
+  __syncthreads();
 
-  uint32_t gmax, tstar;
-  uint64_t ent[kPer];  // thread t's candidates
-  uint32_t live = 0u;  // bit q: ent[q] is a candidate >= t*
+  // their elements >= bnd, in staging order, as (bits | index << 32)
+  constexpr int kSt = kStageMax / kBlock;
+  float4 sv[kSt];
+  uint32_t sidx[kSt];
+  uint32_t ne = 0u;
+#pragma unroll
+  for (int q = 0; q < kSt; ++q) {
+    const uint32_t g = (uint32_t)(tid + q * kBlock);
+    sv[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    sidx[q] = 0u;
+    if (stage_ok && g < nstage) {
+      sv[q] = sm.u.a.vec[g];
+      sidx[q] = sm.u.a.vidx[g];
+      ne += (uint32_t)(bits_of(sv[q].x) >= bnd) + (uint32_t)(bits_of(sv[q].y) >= bnd) +
+            (uint32_t)(bits_of(sv[q].z) >= bnd) + (uint32_t)(bits_of(sv[q].w) >= bnd);
+    }
+  }
+  uint32_t nlist;
+  uint32_t epos = block_excl_scan(ne, nlist, sm.red[1]);
+  const bool publish = stage_ok && nlist <= (uint32_t)kListMax;
+
+  uint32_t tstar, gmax, ntot;
   if (W == 1) {
-    // the whole row is in this work-group: candidates via sm.cand
-    if (fast && publish && wave > 0) {
-      const uint32_t c = sm.wcnt[wave];
-      for (uint32_t p = lane; p < c; p += kWave)
-        sm.cand[wbase + p] = (uint64_t)sm.a.pw.bits[wave][p] | ((uint64_t)sm.a.pw.idx[wave][p] << 32);
+    // the whole row is in this work-group: the list goes straight to full[]
+    if (publish && nlist <= (uint32_t)kRowCandMax) {
+#pragma unroll
+      for (int q = 0; q < kSt; ++q) {
+        const float xs[4] = {sv[q].x, sv[q].y, sv[q].z, sv[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (bits_of(xs[e]) >= bnd && (q * kBlock + tid) < (int)nstage) {
+            sm.full[epos] = (uint64_t)bits_of(xs[e]) | ((uint64_t)(uint32_t)(s0 + 4 * sidx[q] + e) << 32);
+            ++epos;
+          }
+        }
+      }
     }
-    __syncthreads();
-    if (bad || slice_max == 0u) {
+    if (bad || smax == 0u) {
       if (tid == 0) stream::write_sample(P, i, -1, 0);
       return kDone;
     }
-    if (overflow) return kFallback;
-    gmax = slice_max;
-    tstar = t_bits;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const uint32_t g = (uint32_t)(tid + q * kBlock);
-      ent[q] = g < cnt ? sm.cand[g] : 0ull;
-      if (g < cnt) live |= 1u << q;
-    }
-    __syncthreads();  // sm.cand is read (it is rewritten below)
+    if (!publish || nlist > (uint32_t)kRowCandMax) return kFallback;
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
-    __syncthreads();
+    __syncthreads();  // list complete, histogram clear
+    tstar = bnd;
+    gmax = smax;
+    ntot = nlist;
   } else {
-    const gptr<uint64_t> dst = as_global(S.cand + ((int64_t)li * W + s) * kSliceCandMax);
+    const gptr<uint64_t> dst = as_global(S.list + ((int64_t)li * W + s) * kListMax);
     if (publish) {
-      if (fast) {
-        if (wave > 0) {
-          const uint32_t c = sm.wcnt[wave];
-          for (uint32_t p = lane; p < c; p += kWave)
-            dst[wbase + p] = (uint64_t)sm.a.pw.bits[wave][p] | ((uint64_t)sm.a.pw.idx[wave][p] << 32);
+#pragma unroll
+      for (int q = 0; q < kSt; ++q) {
+        const float xs[4] = {sv[q].x, sv[q].y, sv[q].z, sv[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (bits_of(xs[e]) >= bnd && (q * kBlock + tid) < (int)nstage) {
+            dst[epos] = (uint64_t)bits_of(xs[e]) | ((uint64_t)(uint32_t)(s0 + 4 * sidx[q] + e) << 32);
+            ++epos;
+          }
         }
-      } else {
-        __syncthreads();  // compaction into sm.cand complete
-        for (uint32_t c = tid; c < cnt; c += kBlock) dst[c] = sm.cand[c];
       }
     }
     if (tid == 0) {
       const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + s) * kHdrWords);
-      h[0] = t_bits;
-      h[1] = publish ? cnt : kNoList;
-      h[2] = slice_max;
+      h[0] = bnd;
+      h[1] = publish ? nlist : kNoList;
+      h[2] = smax;
       h[3] = gen;
       h[4] = xcc_id();
     }
@@ -637,23 +544,23 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     if (!sm.flag) return kDone;
 
     // ---- phase B: the last slice work-group of the row ----------------------
-    // Every thread loads its slots of the slices' lists at once, without
-    // waiting for the counts: slot G = t + 1024 q is position G % win of
-    // slice G / win, win = 8192 / W.  Meanwhile wave 0 reads the W headers
-    // (lane q: slice q) and sums them up, and every thread clears the
-    // histogram.  A slot is a candidate if its position is below its
-    // slice's count; a slice whose list is longer than its window sends the
-    // row to an exact gather.
-    const uint32_t win = (uint32_t)(kRowCandMax / W);  // <= kSliceCandMax for W >= 2
+    // Wave 0 reads the W headers (lane q: slice q).  At the same time every
+    // thread loads, speculatively, a batch of positions of one slice's list:
+    // the threads form W groups of 1024 / W, group q reading slice q, as far
+    // as about twice this work-group's own count (lists of one row have
+    // similar lengths); the headers then say which positions are real.
+    const int gsz = kBlock >> S.wlog;
+    const int sl = tid >> (10 - S.wlog);
+    const int lt = tid & (gsz - 1);
+    const gptr<uint64_t> lst = as_global(S.list + ((int64_t)li * W + sl) * kListMax);
+    // positions [0, spec) of every list are loaded now (spec <= one batch)
+    const uint32_t spec = min((uint32_t)(kLoadBatch * gsz), 2u * (publish ? nlist : 0u) + 128u);
+    uint64_t e8[kLoadBatch];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const uint32_t G = (uint32_t)(tid + q * kBlock);
-      const uint32_t sl = G / win;  // == W for the last slots when W does not divide 8192
-      ent[q] = 0ull;
-      if (sl < (uint32_t)W)
-        ent[q] = __hip_atomic_load(
-            as_global(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (G - sl * win)),
-            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 0; q < kLoadBatch; ++q) {
+      const uint32_t pos = (uint32_t)(lt + q * gsz);
+      e8[q] = pos < spec ? __hip_atomic_load(lst + pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0ull;
     }
     if (wave == 0) {
       const uint32_t me = xcc_id();
@@ -673,180 +580,157 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
         hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const bool foreign = __ballot(mine && (hg != mygen || hx != me)) != 0ull;
-      const bool ovf = __ballot(mine && hc > (uint32_t)kSliceCandMax) != 0ull;  // kNoList too
-      const bool spill = __ballot(mine && hc <= (uint32_t)kSliceCandMax && hc > win) != 0ull;
-      const uint32_t cc = (mine && hc <= (uint32_t)kSliceCandMax) ? hc : 0u;
+      const bool ovf = __ballot(mine && hc > (uint32_t)kListMax) != 0ull;  // kNoList too
+      const uint32_t cc = (mine && hc <= (uint32_t)kListMax) ? hc : 0u;
       const uint32_t incl = wave_incl_scan(cc);
       const uint32_t all = lane63(incl);
       const uint32_t gm = wave_max(hm);
       const uint32_t ts = wave_max(ht);
+      const uint32_t nmax = wave_max(cc);
       if (lane <= kMaxSlices) sm.off[lane] = lane < W ? incl - cc : all;
-      if (lane < kMaxSlices) sm.wcnt[lane] = cc;  // per-slice counts (0 past W)
       if (lane == 0) {
-        uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back, 3: exact gather
+        uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back
         if (foreign) status = 2u;
         else if (gm >= 0x7F800000u || gm == 0u) status = 1u;
         else if (ovf || all > (uint32_t)kRowCandMax) status = 2u;
-        else if (spill) status = 3u;
-        sm.res[0] = ts;
-        sm.res[1] = all;
-        sm.res[2] = gm;
-        sm.res[3] = status;
+        sm.res[2] = ts;
+        sm.res[3] = all;
+        sm.res[4] = gm;
+        sm.res[5] = status;
+        sm.res[6] = nmax;
       }
     }
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
     __syncthreads();
-    const uint32_t status = sm.res[3];
+    const uint32_t status = sm.res[5];
     if (status == 1u) {
       if (tid == 0) stream::write_sample(P, i, -1, 0);
       return kDone;
     }
     if (status == 2u) return kFallback;
-    tstar = sm.res[0];
-    gmax = sm.res[2];
-    if (status == 0u) {
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const uint32_t G = (uint32_t)(tid + q * kBlock);
-        const uint32_t sl = G / win;
-        if (sl < (uint32_t)W && G - sl * win < sm.wcnt[sl]) live |= 1u << q;
-      }
-    } else {
-      // exact gather: entry g of the row's concatenated lists is position
-      // g - off[sl] of slice sl, the last slice with off[sl] <= g (the
-      // offsets in scalar registers; every load issued before any is used)
-      const uint32_t ntot = sm.res[1];
-      uint32_t off[kMaxSlices];
-#pragma unroll
-      for (int q = 0; q < kMaxSlices; ++q)
-        off[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.off[q]);
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const uint32_t g = (uint32_t)(tid + q * kBlock);
-        int sl = 0;
-        uint32_t base = 0u;
-#pragma unroll
-        for (int t = 1; t < kMaxSlices; ++t) {
-          if (t < W && off[t] <= g) {
-            sl = t;
-            base = off[t];
-          }
-        }
-        ent[q] = 0ull;
-        if (g < ntot) {
-          ent[q] = __hip_atomic_load(
-              as_global(S.cand + ((int64_t)li * W + sl) * kSliceCandMax + (g - base)),
-              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          live |= 1u << q;
-        }
-      }
-    }
-  }
-  // candidates below t* take no part (bits of valid values have bit 31
-  // clear, so bits >> 20 is a bin of the 2048)
-#pragma unroll
-  for (int q = 0; q < kPer; ++q)
-    if ((uint32_t)ent[q] < tstar) live &= ~(1u << q);
+    tstar = sm.res[2];
+    ntot = sm.res[3];
+    gmax = sm.res[4];
+    const uint32_t nmax = sm.res[6];
 
-  // ---- tau_k, first pass: a histogram of bits [30:20] ------------------------
-  // Most candidates sit in the few bins just above t*: the four bins from
-  // t*'s are counted in 8-bit register fields and added once per wave, the
-  // rest go straight to LDS.
-  const uint32_t b0 = tstar >> 20;
-  uint32_t packed = 0u;
+    // the real positions into full[], in (slice, position) order; positions
+    // past the speculative batch (rare) in further batches
+    const uint32_t n_sl = sm.off[sl + 1] - sm.off[sl];
+    uint64_t* out = sm.full + sm.off[sl];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    if (live & (1u << q)) {
-      const uint32_t bq = ((uint32_t)ent[q] >> 20) & (kHistBins - 1);
-      const uint32_t d = bq - b0;
-      if (d < 4u) packed += 1u << (8u * d);
-      else atomicAdd(&sm.hist[H1::at(bq)], 1u);
+    for (int q = 0; q < kLoadBatch; ++q) {
+      const uint32_t pos = (uint32_t)(lt + q * gsz);
+      if (pos < n_sl && pos < spec) out[pos] = e8[q];
+    }
+    for (uint32_t p0 = 0; nmax > spec && p0 < nmax; p0 += (uint32_t)(kLoadBatch * gsz)) {
+#pragma unroll
+      for (int q = 0; q < kLoadBatch; ++q) {
+        const uint32_t pos = p0 + (uint32_t)(lt + q * gsz);
+        e8[q] = (pos < n_sl && pos >= spec)
+                    ? __hip_atomic_load(lst + pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0ull;
+      }
+#pragma unroll
+      for (int q = 0; q < kLoadBatch; ++q) {
+        const uint32_t pos = p0 + (uint32_t)(lt + q * gsz);
+        if (pos < n_sl && pos >= spec) out[pos] = e8[q];
+      }
+    }
+    __syncthreads();
+  }
+
+  // From here on waves 0..7 (two per SIMD) hold the entries, slot q of
+  // thread t being entry t + 512 q, all in registers; the other waves take
+  // part in the barriers only, so the fixed per-thread cost of the merge is
+  // paid by 8 waves instead of 16.
+  constexpr int kMw = 8, kMt = kMw * kWave, kSlots = kRowCandMax / kMt;
+  const bool worker = wave < kMw;
+  uint64_t en[kSlots];
+  uint32_t valid = 0u;  // bit q: slot q holds an entry >= t*
+  if (worker) {
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      en[q] = 0ull;
+      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
+      const uint32_t g = (uint32_t)(tid + q * kMt);
+      en[q] = g < ntot ? sm.full[g] : 0ull;
+      if (g < ntot && (uint32_t)en[q] >= tstar) valid |= 1u << q;
     }
   }
-  {
-    const uint32_t even = wave_sum(packed & 0x00FF00FFu);         // fields 0 and 2
-    const uint32_t odd = wave_sum((packed >> 8) & 0x00FF00FFu);   // fields 1 and 3
+
+  // ---- tau_k: a histogram of the entries >= t* on the key (bits - t*) >> sh,
+  // sh chosen so that the keys up to the row maximum fit 2048 bins ----------
+  const uint32_t range = gmax - tstar;
+  const uint32_t sh = range < (uint32_t)kHistBins ? 0u : 21u - (uint32_t)__clz((int)range);
+  if (worker) {
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
+      if (valid & (1u << q)) atomicAdd(&sm.hist[H1::at(((uint32_t)en[q] - tstar) >> sh)], 1u);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t bin, above, total;
+    wave_find<kHistBins>(sm.hist, (uint32_t)k, bin, above, total);
     if (lane == 0) {
-      const uint32_t c4[4] = {even & 0xFFFFu, odd & 0xFFFFu, even >> 16, odd >> 16};
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        if (c4[d] != 0u && b0 + d < (uint32_t)kHistBins) atomicAdd(&sm.hist[H1::at(b0 + d)], c4[d]);
+      sm.fres[0] = bin;
+      sm.fres[1] = above;
+      sm.fres[2] = total;
     }
   }
   __syncthreads();
-  uint32_t bin1, above1, nstar;
-  block_find<kHistBins>(sm.hist, (uint32_t)k, bin1, above1, nstar, sm);
+  const uint32_t bin1 = sm.fres[0], above1 = sm.fres[1], nstar = sm.fres[2];
   if (nstar < (uint32_t)k && tstar > 0u) return kFallback;  // guard: fewer than k at or above t*
-  const bool all_kept = nstar < (uint32_t)k;  // t* = 0 and k above the row's nonzero count
+  const bool all_kept = nstar < (uint32_t)k;  // t* = 0 and k above the row's entry count
 
-  // ---- the candidates above bin1 into sm.cand, those in bin1 into a side
-  // list (both in (thread, slot) order, one packed scan) -----------------------
-  uint32_t na = 0u, nb = 0u, ma = 0u, mb2 = 0u;
+  // ---- the entries above bin1 into cand, those in bin1 into bnd (both in
+  // (slot, thread) order, one packed scan) --------------------------------------
+  uint32_t ma = 0u, mb = 0u;  // bit q: slot q above bin1 (kept for sure) / in bin1
+  if (worker) {
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    if (live & (1u << q)) {
-      const uint32_t x = (uint32_t)ent[q];
-      const uint32_t bq = (x >> 20) & (kHistBins - 1);
-      if (all_kept ? x > 0u : bq > bin1) {
-        ma |= 1u << q;
-        ++na;
-      } else if (!all_kept && bq == bin1) {
-        mb2 |= 1u << q;
-        ++nb;
-      }
+    for (int q = 0; q < kSlots; ++q) {
+      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
+      const uint32_t x = (uint32_t)en[q];
+      const uint32_t key = (x - tstar) >> sh;
+      const bool v = valid & (1u << q);
+      if (v && (all_kept ? x > 0u : key > bin1)) ma |= 1u << q;
+      if (v && !all_kept && key == bin1) mb |= 1u << q;
     }
   }
-  const uint32_t pk = na | (nb << 16);  // each field stays below 2^14
-  const uint32_t pincl = wave_incl_scan(pk);
-  if (lane == kWave - 1) sm.red_u[wave] = pincl;
-  __syncthreads();
-  uint32_t pbase = 0u, ptot = 0u;
+  uint32_t ptot;
+  const uint32_t pk = block_excl_scan((uint32_t)__popc(ma) | ((uint32_t)__popc(mb) << 16), ptot,
+                                      sm.red[2], worker);  // both fields stay below 2^14
+  const uint32_t n_above = ptot & 0xFFFFu, n_bnd = ptot >> 16;
+  // the top-k set (above-bin entries and the boundary entries >= tau_k) must
+  // fit cand[]; decided here, while every wave is still present
+  if (n_above + n_bnd > (uint32_t)kKeptMax || n_bnd > (uint32_t)kBndMax) return kFallback;
+  uint32_t pa = pk & 0xFFFFu, pb = pk >> 16;
+  if (worker) {
 #pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
-    const uint32_t t = sm.red_u[q];
-    pbase += q < wave ? t : 0u;
-    ptot += t;
-  }
-  uint32_t pa = (pbase + pincl - pk) & 0xFFFFu, pb = (pbase + pincl - pk) >> 16;
-  uint64_t* bnd = sm.a.bnd;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    if (ma & (1u << q)) sm.cand[pa++] = ent[q];
-    if (mb2 & (1u << q)) bnd[pb++] = ent[q];
+    for (int q = 0; q < kSlots; ++q) {
+      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
+      if (ma & (1u << q)) sm.u.b.cand[pa++] = en[q];
+      if (mb & (1u << q)) sm.u.b.bnd[pb++] = en[q];
+    }
   }
   __syncthreads();
   if (wave != 0) return kDone;
 
   // ---- wave 0 from here on: tau_k inside bin1, the top-k list, the loop -----
-  uint32_t m = ptot & 0xFFFFu;
+  uint32_t m = n_above;
   uint32_t tau_k = 0u;
   if (!all_kept) {
-    const uint32_t nbt = ptot >> 16;
-    const uint32_t need2 = (uint32_t)k - above1;  // 1 <= need2 <= nbt
-    // bits [19:9] then [8:0] of the boundary entries, in sm.hist (one wave:
-    // its LDS operations are ordered, no barrier needed)
-    uint32_t bin2, above2, t2, bin3, above3, t3;
-    clear_hist<kHistBins>(sm.hist, lane, kWave);
-    for (uint32_t c = lane; c < nbt; c += kWave)
-      atomicAdd(&sm.hist[H1::at(((uint32_t)bnd[c] >> 9) & (kHistBins - 1))], 1u);
-    wave_find<kHistBins>(sm.hist, need2, bin2, above2, t2);
-    const uint32_t hi = (bin1 << 11) | bin2;
-    clear_hist<kFineBins>(sm.hist, lane, kWave);
-    for (uint32_t c = lane; c < nbt; c += kWave) {
-      const uint32_t x = (uint32_t)bnd[c];
-      if ((x >> 9) == hi) atomicAdd(&sm.hist[H3::at(x & (kFineBins - 1))], 1u);
-    }
-    wave_find<kFineBins>(sm.hist, need2 - above2, bin3, above3, t3);
-    tau_k = (hi << 9) | bin3;
+    tau_k = wave_kth(sm.u.b.bnd, n_bnd, tstar + (bin1 << sh), sh, (uint32_t)k - above1, sm.hist,
+                     sm.sel);
     // the boundary entries >= tau_k follow the others, in list order
-    for (uint32_t c0 = 0; c0 < nbt; c0 += kWave) {
+    for (uint32_t c0 = 0; c0 < n_bnd; c0 += kWave) {
       const uint32_t c = c0 + lane;
-      const uint64_t en = c < nbt ? bnd[c] : 0ull;
-      const bool take = c < nbt && (uint32_t)en >= tau_k && (uint32_t)en > 0u;
-      const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
-      const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(tm >> 32),
-                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)tm, 0u));
-      if (take) sm.cand[m + pos] = en;
+      const uint64_t en = c < n_bnd ? sm.u.b.bnd[c] : 0ull;
+      const bool take = c < n_bnd && (uint32_t)en >= tau_k && (uint32_t)en > 0u;
+      const uint64_t tm = __ballot(take);
+      const uint32_t p = m + rank_in(tm);
+      if (take) sm.u.b.cand[p] = en;  // p < n_above + n_bnd <= kKeptMax
       m += (uint32_t)__popcll(tm);
     }
   }
@@ -858,13 +742,13 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const float high = __uint_as_float(gmax);
   int e;
   if (m <= 4 * kWave) {
-    e = wave_loop<OP, 4>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 4>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
   } else if (m <= 8 * kWave) {
-    e = wave_loop<OP, 8>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 8>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
   } else if (m <= 16 * kWave) {
-    e = wave_loop<OP, 16>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
-  } else {  // (32 entries per lane in registers would spill the kernel)
-    e = wave_loop<OP, 0>(sm, (int)m, low, high, k, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 16>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
+  } else {  // (32 float64 entries per lane in registers would spill the kernel)
+    e = wave_loop<OP, 0>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
   }
   if (lane == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
   return kDone;
@@ -875,7 +759,7 @@ __global__ __launch_bounds__(kBlock) void split_sample_kernel(SampleParams P, Sp
   __shared__ SplitSmem sm;
   int i = 0;
   const int mode = split_sample<OP, NV>(P, S, sm, i);
-  if (mode == kFallback) stream::sample_row<OP>(P, i, sm.a.stream);
+  if (mode == kFallback) stream::sample_row<OP>(P, i, sm.u.stream);
 }
 
 template <int OP, int NV>
@@ -888,7 +772,9 @@ void launch_one(const SampleParams& p, const SplitParams& sp, hipStream_t s) {
 template <int OP>
 void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, hipStream_t s) {
   switch (nv) {
+    case 1: launch_one<OP, 1>(p, sp, s); break;
     case 2: launch_one<OP, 2>(p, sp, s); break;
+    case 3: launch_one<OP, 3>(p, sp, s); break;
     case 4: launch_one<OP, 4>(p, sp, s); break;
     case 6: launch_one<OP, 6>(p, sp, s); break;
     case 8: launch_one<OP, 8>(p, sp, s); break;
@@ -897,8 +783,8 @@ void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, hipStream_t
 }
 
 constexpr int kChunk = 2048;     // outputs per launch (bounds the workspace)
-constexpr int kMaxNv = 10;  // vectors per reading thread (12 spills the kernel)
-constexpr int kMaxSliceLen = kMaxNv * 4 * kLoadThreads;
+constexpr int kMaxNv = 10;  // vectors per thread
+constexpr int kMaxSliceLen = kMaxNv * 4 * kBlock;
 
 // The arrival counters and generation numbers sit at fixed offsets for the
 // largest chunk, so calls of any shape can share one workspace: counters are
@@ -917,15 +803,19 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
   if (!vec_ok || vocab < 1024 || num_outputs <= 0) return plan;
   const int wmin = (vocab + kMaxSliceLen - 1) / kMaxSliceLen;
   const int wt = (256 + num_outputs - 1) / num_outputs;
-  int W = max(wmin, min(wt, kMaxSlices));
-  if (W > kMaxSlices) return plan;
+  if (wmin > kMaxSlices) return plan;
+  // W: a power of two, at least wmin, about 256 work-groups in all, at most
+  // kMaxSlices, and no empty slice
+  int W = 1;
+  while (W < wmin || (W * 2 <= kMaxSlices && W * 2 <= wt)) W *= 2;
   int L = 0;
-  for (;; --W) {  // largest W <= chosen one whose slices are all non-empty
+  for (;; W /= 2) {
     L = ((vocab + 4 * W - 1) / (4 * W)) * 4;
     if (W == 1 || (int64_t)(W - 1) * L < vocab) break;
   }
-  int nv = (L / 4 + kLoadThreads - 1) / kLoadThreads;
-  nv = nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 6 ? 6 : nv <= 8 ? 8 : 10;
+  if (W < wmin) return plan;
+  int nv = (L / 4 + kBlock - 1) / kBlock;
+  nv = nv <= 4 ? nv : nv <= 6 ? 6 : nv <= 8 ? 8 : 10;
   const int ch = min(num_outputs, kChunk);
   plan.W = W;
   plan.L = L;
@@ -933,7 +823,7 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
   plan.chunk = ch;
   plan.workspace = W == 1 ? 0
                           : kCtlBytes + align256((size_t)ch * W * kHdrWords * 4) +
-                                (size_t)ch * W * kSliceCandMax * 8;
+                                (size_t)ch * W * kListMax * 8;
   return plan;
 }
 
@@ -943,11 +833,13 @@ hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& p
   const size_t ch = (size_t)plan.chunk;
   SplitParams sp;
   sp.W = plan.W;
+  sp.wlog = 0;
+  while ((1 << sp.wlog) < plan.W) ++sp.wlog;
   sp.L = plan.L;
   sp.ctr = reinterpret_cast<uint32_t*>(ws);
   sp.gen = sp.ctr + kChunk;
   sp.hdr = reinterpret_cast<uint32_t*>(ws + kCtlBytes);
-  sp.cand = reinterpret_cast<uint64_t*>(ws + kCtlBytes + align256(ch * plan.W * kHdrWords * 4));
+  sp.list = reinterpret_cast<uint64_t*>(ws + kCtlBytes + align256(ch * plan.W * kHdrWords * 4));
   for (int out0 = 0; out0 < p.num_outputs; out0 += plan.chunk) {
     sp.out0 = out0;
     sp.n_out = min(plan.chunk, p.num_outputs - out0);
