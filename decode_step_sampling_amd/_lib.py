@@ -56,6 +56,7 @@ SIGNATURES = {
     "dss_workspace_size": ([_I32, _I32, _I32, _I32, _U32], ctypes.c_size_t),
     "dss_strerror": ([_I32], ctypes.c_char_p),
     "dss_version": ([], ctypes.c_int32),
+    "dss_set_timing_events": ([_P, _P], ctypes.c_int32),
 }
 
 _lib = None

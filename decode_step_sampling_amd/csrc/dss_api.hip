@@ -14,6 +14,12 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<void*> g_ev_start{nullptr}, g_ev_stop{nullptr};  // dss_set_timing_events
+
+dss::LaunchEvents timing_events() {
+  return dss::LaunchEvents{static_cast<hipEvent_t>(g_ev_start.load(std::memory_order_relaxed)),
+                           static_cast<hipEvent_t>(g_ev_stop.load(std::memory_order_relaxed))};
+}
 
 int check_device() {
   int dev = 0;
@@ -72,8 +78,9 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.rounds = rounds;
   p.vec_ok = vec_ok;
   const hipError_t e =
-      plan.W > 0 ? dss::launch_split_sample(op, p, plan, workspace, static_cast<hipStream_t>(stream))
-                 : dss::launch_stream_sample(op, p, static_cast<hipStream_t>(stream));
+      plan.W > 0 ? dss::launch_split_sample(op, p, plan, workspace, static_cast<hipStream_t>(stream),
+                                            timing_events())
+                 : dss::launch_stream_sample(op, p, static_cast<hipStream_t>(stream), timing_events());
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
@@ -103,7 +110,8 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
   p.top_p = top_p;
   p.row_status = row_status;
   p.vec_ok = (vocab % 4 == 0) && aligned16(in) && aligned16(out);
-  const hipError_t e = dss::launch_stream_renorm(kind, p, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      dss::launch_stream_renorm(kind, p, static_cast<hipStream_t>(stream), timing_events());
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
@@ -204,6 +212,13 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
   // engine, which needs none
   if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || vocab <= 0 || num_outputs <= 0) return 0;
   return dss::plan_split(op, rows, vocab, num_outputs, flags, vocab % 4 == 0).workspace;
+}
+
+DSS_EXPORT int32_t dss_set_timing_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return DSS_ERR_INVALID_ARG;
+  g_ev_start.store(start, std::memory_order_relaxed);
+  g_ev_stop.store(stop, std::memory_order_relaxed);
+  return DSS_OK;
 }
 
 DSS_EXPORT const char* dss_strerror(int32_t status) {

@@ -2,6 +2,7 @@
 // units of libdss.so.  Not installed; the public interface is include/dss.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -58,10 +59,32 @@ struct RenormParams {
   int32_t vec_ok;
 };
 
+// Optional kernel-timing events (dss_set_timing_events): the first kernel of
+// a call records `start` when it begins executing and the last records
+// `stop` when it ends (hipExtLaunchKernel dispatch events).  NULL: none.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+// Launch kernel on stream s, attaching the dispatch events of ev that apply
+// (start if first, stop if last).
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t s, const LaunchEvents& ev,
+                          bool first, bool last, Args... args) {
+  hipEvent_t a = first ? ev.start : nullptr, b = last ? ev.stop : nullptr;
+  if (a || b) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+}
+
 // Streaming engine: one 1024-thread work-group per output (or row), every
 // pass reads the row from global memory.  Returns a hipError_t.
-hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s);
-hipError_t launch_stream_renorm(int kind, const RenormParams& p, hipStream_t s);
+hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_stream_renorm(int kind, const RenormParams& p, hipStream_t s,
+                                const LaunchEvents& ev);
 
 // Split-row engine (top-k and top-k-then-top-p sampling): W work-groups per
 // output on one XCD, one HBM read of the row, candidates handed to the last
@@ -75,6 +98,6 @@ struct SplitPlan {
 };
 SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flags, int vec_ok);
 hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& plan,
-                               void* workspace, hipStream_t s);
+                               void* workspace, hipStream_t s, const LaunchEvents& ev);
 
 }  // namespace dss

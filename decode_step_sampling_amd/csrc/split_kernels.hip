@@ -763,22 +763,24 @@ __global__ __launch_bounds__(kBlock) void split_sample_kernel(SampleParams P, Sp
 }
 
 template <int OP, int NV>
-void launch_one(const SampleParams& p, const SplitParams& sp, hipStream_t s) {
+void launch_one(const SampleParams& p, const SplitParams& sp, hipStream_t s, const LaunchEvents& ev,
+                bool first, bool last) {
   const int groups = (sp.n_out + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * sp.W)), block(kBlock);
-  hipLaunchKernelGGL((split_sample_kernel<OP, NV>), grid, block, 0, s, p, sp);
+  launch_kernel(split_sample_kernel<OP, NV>, grid, block, s, ev, first, last, p, sp);
 }
 
 template <int OP>
-void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, hipStream_t s) {
+void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, hipStream_t s,
+               const LaunchEvents& ev, bool first, bool last) {
   switch (nv) {
-    case 1: launch_one<OP, 1>(p, sp, s); break;
-    case 2: launch_one<OP, 2>(p, sp, s); break;
-    case 3: launch_one<OP, 3>(p, sp, s); break;
-    case 4: launch_one<OP, 4>(p, sp, s); break;
-    case 6: launch_one<OP, 6>(p, sp, s); break;
-    case 8: launch_one<OP, 8>(p, sp, s); break;
-    default: launch_one<OP, 10>(p, sp, s); break;
+    case 1: launch_one<OP, 1>(p, sp, s, ev, first, last); break;
+    case 2: launch_one<OP, 2>(p, sp, s, ev, first, last); break;
+    case 3: launch_one<OP, 3>(p, sp, s, ev, first, last); break;
+    case 4: launch_one<OP, 4>(p, sp, s, ev, first, last); break;
+    case 6: launch_one<OP, 6>(p, sp, s, ev, first, last); break;
+    case 8: launch_one<OP, 8>(p, sp, s, ev, first, last); break;
+    default: launch_one<OP, 10>(p, sp, s, ev, first, last); break;
   }
 }
 
@@ -828,7 +830,7 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
 }
 
 hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& plan,
-                               void* workspace, hipStream_t s) {
+                               void* workspace, hipStream_t s, const LaunchEvents& ev) {
   char* ws = static_cast<char*>(workspace);
   const size_t ch = (size_t)plan.chunk;
   SplitParams sp;
@@ -843,10 +845,11 @@ hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& p
   for (int out0 = 0; out0 < p.num_outputs; out0 += plan.chunk) {
     sp.out0 = out0;
     sp.n_out = min(plan.chunk, p.num_outputs - out0);
+    const bool first = out0 == 0, last = out0 + plan.chunk >= p.num_outputs;
     if (op == kOpTopK) {
-      launch_nv<kOpTopK>(plan.nv, p, sp, s);
+      launch_nv<kOpTopK>(plan.nv, p, sp, s, ev, first, last);
     } else {
-      launch_nv<kOpTopKTopP>(plan.nv, p, sp, s);
+      launch_nv<kOpTopKTopP>(plan.nv, p, sp, s, ev, first, last);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -133,27 +133,28 @@ __global__ __launch_bounds__(kBlock) void stream_renorm_kernel(RenormParams P) {
 
 }  // namespace
 
-hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s) {
+hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s, const LaunchEvents& ev) {
   const dim3 grid((unsigned)p.num_outputs), block(kBlock);
   switch (op) {
-    case kOpNone: hipLaunchKernelGGL(stream_sample_kernel<kOpNone>, grid, block, 0, s, p); break;
-    case kOpTopK: hipLaunchKernelGGL(stream_sample_kernel<kOpTopK>, grid, block, 0, s, p); break;
-    case kOpTopP: hipLaunchKernelGGL(stream_sample_kernel<kOpTopP>, grid, block, 0, s, p); break;
-    case kOpMinP: hipLaunchKernelGGL(stream_sample_kernel<kOpMinP>, grid, block, 0, s, p); break;
+    case kOpNone: launch_kernel(stream_sample_kernel<kOpNone>, grid, block, s, ev, true, true, p); break;
+    case kOpTopK: launch_kernel(stream_sample_kernel<kOpTopK>, grid, block, s, ev, true, true, p); break;
+    case kOpTopP: launch_kernel(stream_sample_kernel<kOpTopP>, grid, block, s, ev, true, true, p); break;
+    case kOpMinP: launch_kernel(stream_sample_kernel<kOpMinP>, grid, block, s, ev, true, true, p); break;
     case kOpTopKTopP:
-      hipLaunchKernelGGL(stream_sample_kernel<kOpTopKTopP>, grid, block, 0, s, p);
+      launch_kernel(stream_sample_kernel<kOpTopKTopP>, grid, block, s, ev, true, true, p);
       break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_stream_renorm(int kind, const RenormParams& p, hipStream_t s) {
+hipError_t launch_stream_renorm(int kind, const RenormParams& p, hipStream_t s,
+                                const LaunchEvents& ev) {
   const dim3 grid((unsigned)p.rows), block(kBlock);
   switch (kind) {
-    case kRenormTopK: hipLaunchKernelGGL(stream_renorm_kernel<kRenormTopK>, grid, block, 0, s, p); break;
-    case kRenormTopP: hipLaunchKernelGGL(stream_renorm_kernel<kRenormTopP>, grid, block, 0, s, p); break;
-    case kMaskLogits: hipLaunchKernelGGL(stream_renorm_kernel<kMaskLogits>, grid, block, 0, s, p); break;
+    case kRenormTopK: launch_kernel(stream_renorm_kernel<kRenormTopK>, grid, block, s, ev, true, true, p); break;
+    case kRenormTopP: launch_kernel(stream_renorm_kernel<kRenormTopP>, grid, block, s, ev, true, true, p); break;
+    case kMaskLogits: launch_kernel(stream_renorm_kernel<kMaskLogits>, grid, block, s, ev, true, true, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -202,6 +202,17 @@ int dss_top_k_mask_logits(const float* logits, float* out, int32_t rows, int32_t
 size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                           int32_t num_outputs, uint32_t flags);
 
+/* Profiling hook (not part of the sampling path).  With two hipEvent_t
+ * handles (passed as void*, both non-NULL), every later call of this process
+ * attaches them to its kernels as dispatch events (hipExtLaunchKernel): the
+ * first kernel of the call records `start` when it begins executing, the
+ * last records `stop` when it ends, so hipEventElapsedTime(start, stop) is
+ * the call's kernel time as a kernel-trace profiler reports it.  (NULL,
+ * NULL) switches the hook off.  Process-wide; the caller owns the events
+ * and must keep them alive while the hook is on.  Returns DSS_ERR_INVALID_ARG
+ * if exactly one handle is NULL. */
+int32_t dss_set_timing_events(void* start, void* stop);
+
 /* Static description of a status code. */
 const char* dss_strerror(int32_t status);
 

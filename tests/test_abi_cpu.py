@@ -34,7 +34,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -115,6 +115,9 @@ def test_workspace_size_and_strings():
         assert _lib.strerror(code) not in ("", "unknown status")
     assert _lib.strerror(7) == "unknown status"
     assert lib.dss_version() >= 100
+    # the timing hook takes both event handles or neither; no HIP call is made
+    assert lib.dss_set_timing_events(ctypes.c_void_p(16), None) == _lib.DSS_ERR_INVALID_ARG
+    assert lib.dss_set_timing_events(None, None) == _lib.DSS_OK
 
 
 def test_binding_refuses_cpu_tensors():
