@@ -77,15 +77,16 @@ struct Padded {
 using H1 = Padded<kHistBins>;
 
 struct SplitSmem {
-  uint64_t full[kRowCandMax];     // every slice's entries, in (slice, position) order
+  uint64_t full[kRowCandMax + kWave];  // every slice's entries, in (slice, position) order;
+                                       // the last kWave slots take branch-free dummy writes
   union {
     struct {
-      float4 vec[kStageMax];     // staged vectors
-      uint32_t vidx[kStageMax];  // their vector index inside the slice
+      float4 vec[kStageMax + kWave];     // staged vectors (+ per-lane dummy slots)
+      uint32_t vidx[kStageMax + kWave];  // their vector index inside the slice
     } a;
     struct {
-      uint64_t cand[kKeptMax];   // the top-k set, in candidate order
-      uint64_t bnd[kBndMax];     // entries in the boundary bin
+      uint64_t cand[kKeptMax + kWave];  // the top-k set, in candidate order (+ dummies)
+      uint64_t bnd[kBndMax + kWave];    // entries in the boundary bin (+ dummies)
     } b;
     stream::SampleSmem stream;   // streaming fallback
   } u;
@@ -368,10 +369,27 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const int tid = threadIdx.x, lane = lane_id(), wave = uwave();
 
   const int row = P.indices ? as_global(P.indices)[i] : i;
+  const bool row_ok = row >= 0 && row < P.rows;
+
+  // ---- phase A: one HBM read of the slice into registers --------------------
+  // The loads go out before anything else is read (they depend on the row
+  // only).  They are unconditional (a thread past the end re-reads the last
+  // vector and ignores it) so that they sit in one basic block and every
+  // later use waits only for its own vector, not for the whole slice.
+  const int V = P.vocab;
+  const int s0 = s * S.L;
+  const int s1 = min(s0 + S.L, V);
+  const int nvec = (s1 - s0) / 4;
+  const gptr<const float4> src = as_global(
+      reinterpret_cast<const float4*>(P.probs + (int64_t)(row_ok ? row : 0) * V + s0));
+  float4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1));
+
   const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
   const float pp =
       (OP == kOpTopKTopP) ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
-  const bool ok = row >= 0 && row < P.rows && k > 0 && (OP != kOpTopKTopP || !isnan(pp));
+  const bool ok = row_ok && k > 0 && (OP != kOpTopKTopP || !isnan(pp));
   if (!ok || k > kSplitKCap) {
     // no hand-off for this output: slice 0 answers alone
     if (s != 0) return kDone;
@@ -381,27 +399,13 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
     return kFallback;
   }
+
+  // while the slice is in flight: clear the histogram; wave 0 reads the
+  // row's generation and computes the first 256 draws of the output's stream
+  clear_hist<kHistBins>(sm.hist, tid, kBlock);
   const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
   const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
-
-  // ---- phase A: one HBM read of the slice into registers --------------------
-  const int V = P.vocab;
-  const int s0 = s * S.L;
-  const int s1 = min(s0 + S.L, V);
-  const int nvec = (s1 - s0) / 4;
-  const gptr<const float4> src =
-      as_global(reinterpret_cast<const float4*>(P.probs + (int64_t)row * V + s0));
-  // Loads are issued unconditionally (a thread past the end re-reads the
-  // last vector and ignores it) so that they sit in one basic block and every
-  // later use waits only for its own vector, not for the whole slice.
-  float4 v[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1));
-
-  // while they are in flight: clear the histogram; wave 0 reads the row's
-  // generation and computes the first 256 draws of the output's stream
-  clear_hist<kHistBins>(sm.hist, tid, kBlock);
   uint32_t gen = 0u;
   if (wave == 0) {
     if (W > 1 && lane == 0)
@@ -412,18 +416,23 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   }
   __syncthreads();
 
-  // As each vector lands: its maximum, counted in the histogram of bits
-  // [30:20] (bin 2047 collects the patterns with the sign bit set).
-  uint32_t m4[NV];
+  // As each vector lands: its maximum (float32 bits) counted in the
+  // histogram of bits [30:20] (bin 2047 also takes the patterns with the sign
+  // bit set), and its staging key, the maximum + 1, or 0 for a thread past
+  // the end.  Everything below is branch-free per lane (selects, and stores
+  // to dummy slots), because every divergent branch costs scalar
+  // instructions and one scalar unit serves all waves of a CU: a lane past
+  // the end counts into a padding word of the histogram that no search reads.
+  const uint32_t pad = (uint32_t)lane * H1::kStride + H1::kChunk;
+  uint32_t key[NV];
   uint32_t mx = 0u;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const bool in = tid + j * kBlock < nvec;
-    m4[j] = max4_bits(v[j]);
-    if (in) {
-      mx = max(mx, m4[j]);
-      atomicAdd(&sm.hist[H1::at(min(m4[j] >> 20, (uint32_t)(kHistBins - 1)))], 1u);
-    }
+    const uint32_t m = max4_bits(v[j]);
+    key[j] = in ? m + 1u : 0u;
+    mx = max(mx, in ? m : 0u);
+    atomicAdd(&sm.hist[in ? H1::at(min(m >> 20, (uint32_t)(kHistBins - 1))) : pad], 1u);
   }
   mx = wave_max(mx);
   if (lane == 0) sm.wmax[wave] = mx;
@@ -442,86 +451,80 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const uint32_t smax = sm.res[1];
   const bool bad = smax >= 0x7F800000u;  // a sign bit, an inf or a NaN somewhere
 
-  // vectors with a value >= bnd, staged in thread order
+  // the vectors with a value >= bnd (key > bnd), staged in thread order
   uint32_t nv_hit = 0u;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) nv_hit += (uint32_t)(tid + j * kBlock < nvec && m4[j] >= bnd);
+  for (int j = 0; j < NV; ++j) nv_hit += key[j] > bnd ? 1u : 0u;
   uint32_t nstage;
   uint32_t pos = block_excl_scan(nv_hit, nstage, sm.red[0]);
   const bool stage_ok = !bad && nstage <= (uint32_t)kStageMax;
   if (stage_ok) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      if (tid + j * kBlock < nvec && m4[j] >= bnd) {
-        sm.u.a.vec[pos] = v[j];
-        sm.u.a.vidx[pos] = (uint32_t)(tid + j * kBlock);
-        ++pos;
-      }
+      const bool hit = key[j] > bnd;
+      const uint32_t slot = hit ? pos : (uint32_t)(kStageMax + lane);
+      sm.u.a.vec[slot] = v[j];
+      sm.u.a.vidx[slot] = (uint32_t)(tid + j * kBlock);
+      pos += hit ? 1u : 0u;
     }
   }
   __syncthreads();
 
-  // their elements >= bnd, in staging order, as (bits | index << 32)
+  // their positive elements >= bnd, in staging order, as (bits | index << 32),
+  // into full[] (the row's list when W == 1, a staging copy otherwise)
+  const uint32_t bthr = max(bnd, 1u);
   constexpr int kSt = kStageMax / kBlock;
-  float4 sv[kSt];
+  uint32_t xb[kSt][4];
   uint32_t sidx[kSt];
   uint32_t ne = 0u;
 #pragma unroll
   for (int q = 0; q < kSt; ++q) {
     const uint32_t g = (uint32_t)(tid + q * kBlock);
-    sv[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    sidx[q] = 0u;
-    if (stage_ok && g < nstage) {
-      sv[q] = sm.u.a.vec[g];
-      sidx[q] = sm.u.a.vidx[g];
-      ne += (uint32_t)(bits_of(sv[q].x) >= bnd) + (uint32_t)(bits_of(sv[q].y) >= bnd) +
-            (uint32_t)(bits_of(sv[q].z) >= bnd) + (uint32_t)(bits_of(sv[q].w) >= bnd);
-    }
+    const bool live = stage_ok && g < nstage;
+    const uint32_t gg = live ? g : (uint32_t)(kStageMax + lane);
+    const float4 x = sm.u.a.vec[gg];
+    sidx[q] = sm.u.a.vidx[gg];
+    xb[q][0] = live ? bits_of(x.x) : 0u;
+    xb[q][1] = live ? bits_of(x.y) : 0u;
+    xb[q][2] = live ? bits_of(x.z) : 0u;
+    xb[q][3] = live ? bits_of(x.w) : 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ne += xb[q][e] >= bthr ? 1u : 0u;
   }
   uint32_t nlist;
   uint32_t epos = block_excl_scan(ne, nlist, sm.red[1]);
   const bool publish = stage_ok && nlist <= (uint32_t)kListMax;
+  if (publish) {
+#pragma unroll
+    for (int q = 0; q < kSt; ++q) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool take = xb[q][e] >= bthr;
+        const uint32_t slot = take ? epos : (uint32_t)(kRowCandMax + lane);
+        sm.full[slot] = (uint64_t)xb[q][e] | ((uint64_t)(uint32_t)(s0 + 4 * sidx[q] + e) << 32);
+        epos += take ? 1u : 0u;
+      }
+    }
+  }
+  __syncthreads();
 
   uint32_t tstar, gmax, ntot;
   if (W == 1) {
-    // the whole row is in this work-group: the list goes straight to full[]
-    if (publish && nlist <= (uint32_t)kRowCandMax) {
-#pragma unroll
-      for (int q = 0; q < kSt; ++q) {
-        const float xs[4] = {sv[q].x, sv[q].y, sv[q].z, sv[q].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (bits_of(xs[e]) >= bnd && (q * kBlock + tid) < (int)nstage) {
-            sm.full[epos] = (uint64_t)bits_of(xs[e]) | ((uint64_t)(uint32_t)(s0 + 4 * sidx[q] + e) << 32);
-            ++epos;
-          }
-        }
-      }
-    }
+    // the whole row is in this work-group: full[] holds its list
     if (bad || smax == 0u) {
       if (tid == 0) stream::write_sample(P, i, -1, 0);
       return kDone;
     }
-    if (!publish || nlist > (uint32_t)kRowCandMax) return kFallback;
+    if (!publish) return kFallback;
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
-    __syncthreads();  // list complete, histogram clear
+    __syncthreads();  // histogram clear
     tstar = bnd;
     gmax = smax;
     ntot = nlist;
   } else {
     const gptr<uint64_t> dst = as_global(S.list + ((int64_t)li * W + s) * kListMax);
     if (publish) {
-#pragma unroll
-      for (int q = 0; q < kSt; ++q) {
-        const float xs[4] = {sv[q].x, sv[q].y, sv[q].z, sv[q].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (bits_of(xs[e]) >= bnd && (q * kBlock + tid) < (int)nstage) {
-            dst[epos] = (uint64_t)bits_of(xs[e]) | ((uint64_t)(uint32_t)(s0 + 4 * sidx[q] + e) << 32);
-            ++epos;
-          }
-        }
-      }
+      for (uint32_t g = tid; g < nlist; g += kBlock) dst[g] = sm.full[g];
     }
     if (tid == 0) {
       const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + s) * kHdrWords);
@@ -616,12 +619,13 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     // the real positions into full[], in (slice, position) order; positions
     // past the speculative batch (rare) in further batches
     const uint32_t n_sl = sm.off[sl + 1] - sm.off[sl];
-    uint64_t* out = sm.full + sm.off[sl];
+    const uint32_t o_sl = sm.off[sl];
 #pragma unroll
     for (int q = 0; q < kLoadBatch; ++q) {
       const uint32_t pos = (uint32_t)(lt + q * gsz);
-      if (pos < n_sl && pos < spec) out[pos] = e8[q];
+      sm.full[pos < n_sl && pos < spec ? o_sl + pos : (uint32_t)(kRowCandMax + lane)] = e8[q];
     }
+    uint64_t* out = sm.full + o_sl;
     for (uint32_t p0 = 0; nmax > spec && p0 < nmax; p0 += (uint32_t)(kLoadBatch * gsz)) {
 #pragma unroll
       for (int q = 0; q < kLoadBatch; ++q) {
@@ -641,32 +645,37 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 
   // From here on waves 0..7 (two per SIMD) hold the entries, slot q of
   // thread t being entry t + 512 q, all in registers; the other waves take
-  // part in the barriers only, so the fixed per-thread cost of the merge is
-  // paid by 8 waves instead of 16.
-  constexpr int kMw = 8, kMt = kMw * kWave, kSlots = kRowCandMax / kMt;
+  // part in the barriers only.  Slots are visited in groups of four behind
+  // one wave-uniform test, and everything inside is branch-free.
+  constexpr int kMw = 8, kMt = kMw * kWave, kSlots = kRowCandMax / kMt, kGrp = 4;
   const bool worker = wave < kMw;
+  const uint32_t range = gmax - tstar;
+  const uint32_t sh = range < (uint32_t)kHistBins ? 0u : 21u - (uint32_t)__clz((int)range);
   uint64_t en[kSlots];
-  uint32_t valid = 0u;  // bit q: slot q holds an entry >= t*
+  uint32_t kq[kSlots];  // (bits - t*) >> sh for an entry >= t*, 0xFFFFFFFF for none
   if (worker) {
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
-      en[q] = 0ull;
-      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
-      const uint32_t g = (uint32_t)(tid + q * kMt);
-      en[q] = g < ntot ? sm.full[g] : 0ull;
-      if (g < ntot && (uint32_t)en[q] >= tstar) valid |= 1u << q;
+    for (int q0 = 0; q0 < kSlots; q0 += kGrp) {
+      if ((uint32_t)(q0 * kMt) >= ntot) continue;  // wave-uniform
+#pragma unroll
+      for (int q = q0; q < q0 + kGrp; ++q) {
+        const uint32_t g = (uint32_t)(tid + q * kMt);
+        en[q] = sm.full[g < ntot ? g : (uint32_t)(kRowCandMax + lane)];
+        const uint32_t x = (uint32_t)en[q];
+        kq[q] = (g < ntot && x >= tstar) ? (x - tstar) >> sh : 0xFFFFFFFFu;
+      }
     }
   }
 
   // ---- tau_k: a histogram of the entries >= t* on the key (bits - t*) >> sh,
   // sh chosen so that the keys up to the row maximum fit 2048 bins ----------
-  const uint32_t range = gmax - tstar;
-  const uint32_t sh = range < (uint32_t)kHistBins ? 0u : 21u - (uint32_t)__clz((int)range);
   if (worker) {
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
-      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
-      if (valid & (1u << q)) atomicAdd(&sm.hist[H1::at(((uint32_t)en[q] - tstar) >> sh)], 1u);
+    for (int q0 = 0; q0 < kSlots; q0 += kGrp) {
+      if ((uint32_t)(q0 * kMt) >= ntot) continue;
+#pragma unroll
+      for (int q = q0; q < q0 + kGrp; ++q)
+        atomicAdd(&sm.hist[kq[q] != 0xFFFFFFFFu ? H1::at(kq[q]) : pad], 1u);
     }
   }
   __syncthreads();
@@ -686,21 +695,25 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 
   // ---- the entries above bin1 into cand, those in bin1 into bnd (both in
   // (slot, thread) order, one packed scan) --------------------------------------
-  uint32_t ma = 0u, mb = 0u;  // bit q: slot q above bin1 (kept for sure) / in bin1
+  // above: kept for sure (every positive entry when all are kept); in bin1:
+  // the boundary.  Entries are positive, so "above" is key > bin1 or, when
+  // all are kept, key != none.
+  const uint32_t hi_cut = all_kept ? 0xFFFFFFFEu : bin1;  // key > hi_cut and != none: above
+  uint32_t na = 0u, nb = 0u;
   if (worker) {
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
-      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
-      const uint32_t x = (uint32_t)en[q];
-      const uint32_t key = (x - tstar) >> sh;
-      const bool v = valid & (1u << q);
-      if (v && (all_kept ? x > 0u : key > bin1)) ma |= 1u << q;
-      if (v && !all_kept && key == bin1) mb |= 1u << q;
+    for (int q0 = 0; q0 < kSlots; q0 += kGrp) {
+      if ((uint32_t)(q0 * kMt) >= ntot) continue;
+#pragma unroll
+      for (int q = q0; q < q0 + kGrp; ++q) {
+        const bool some = kq[q] != 0xFFFFFFFFu;
+        na += (some && (all_kept || kq[q] > hi_cut)) ? 1u : 0u;
+        nb += (some && !all_kept && kq[q] == bin1) ? 1u : 0u;
+      }
     }
   }
   uint32_t ptot;
-  const uint32_t pk = block_excl_scan((uint32_t)__popc(ma) | ((uint32_t)__popc(mb) << 16), ptot,
-                                      sm.red[2], worker);  // both fields stay below 2^14
+  const uint32_t pk = block_excl_scan(na | (nb << 16), ptot, sm.red[2], worker);  // fields < 2^14
   const uint32_t n_above = ptot & 0xFFFFu, n_bnd = ptot >> 16;
   // the top-k set (above-bin entries and the boundary entries >= tau_k) must
   // fit cand[]; decided here, while every wave is still present
@@ -708,10 +721,18 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   uint32_t pa = pk & 0xFFFFu, pb = pk >> 16;
   if (worker) {
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
-      if ((uint32_t)(q * kMt) >= ntot) continue;  // wave-uniform
-      if (ma & (1u << q)) sm.u.b.cand[pa++] = en[q];
-      if (mb & (1u << q)) sm.u.b.bnd[pb++] = en[q];
+    for (int q0 = 0; q0 < kSlots; q0 += kGrp) {
+      if ((uint32_t)(q0 * kMt) >= ntot) continue;
+#pragma unroll
+      for (int q = q0; q < q0 + kGrp; ++q) {
+        const bool some = kq[q] != 0xFFFFFFFFu;
+        const bool ta = some && (all_kept || kq[q] > hi_cut);
+        const bool tb = some && !all_kept && kq[q] == bin1;
+        sm.u.b.cand[ta ? pa : (uint32_t)(kKeptMax + lane)] = en[q];
+        sm.u.b.bnd[tb ? pb : (uint32_t)(kBndMax + lane)] = en[q];
+        pa += ta ? 1u : 0u;
+        pb += tb ? 1u : 0u;
+      }
     }
   }
   __syncthreads();
