@@ -21,6 +21,7 @@ struct RowRef {
   bool vec;
 };
 
+// Values x[idx .. idx+3]; positions past the row end read as 0.
 __device__ __forceinline__ void load4(const RowRef& r, int64_t idx, float (&v)[4]) {
   if (r.vec && idx + 3 < r.V) {
     const float4 q = load_f4((gptr<const float4>)(r.x + idx));
@@ -31,6 +32,42 @@ __device__ __forceinline__ void load4(const RowRef& r, int64_t idx, float (&v)[4
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (idx + e < r.V) ? r.x[idx + e] : 0.0f;
+  }
+}
+
+// Calls body(idx, v, valid) for every group of four values v = x[idx ..
+// idx+3] of the row, thread t taking the groups t, t + kBlock, ...  Each
+// thread keeps kBatch 16-byte loads in flight (all issued before the first is
+// used), so a pass over a row is bound by bandwidth rather than by one load
+// latency per group.  Lanes past the last group get valid = false together
+// with a copy of the last group (same idx), so a body stays branch-free:
+// reductions must ignore invalid groups, stores may repeat the last group's.
+// Values past the row end inside the last group read as 0.
+constexpr int kBatch = 8;
+template <class F>
+__device__ __forceinline__ void for_each4(const RowRef& r, F&& body) {
+  const int nvec = (r.V + 3) / 4;
+  for (int f0 = threadIdx.x; f0 < nvec; f0 += kBlock * kBatch) {
+    float v[kBatch][4];
+    if (r.vec) {
+      // V % 4 == 0 and a 16-byte aligned row: every clamped group is whole
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float4 q = load_f4((gptr<const float4>)(r.x + 4ll * min(f0 + u * kBlock, nvec - 1)));
+        v[u][0] = q.x;
+        v[u][1] = q.y;
+        v[u][2] = q.z;
+        v[u][3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) load4(r, 4ll * min(f0 + u * kBlock, nvec - 1), v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int f = f0 + u * kBlock;
+      body(4ll * min(f, nvec - 1), v[u], f < nvec);
+    }
   }
 }
 
@@ -94,32 +131,29 @@ __device__ __forceinline__ Red red_zero() { return Red{0.0, 0.0, 0u, 0u, 0xFFFFF
 template <bool MASS, bool KEYS>
 __device__ uint32_t threshold_search(const RowRef& r, uint32_t lo, uint32_t hi, uint32_t k,
                                      double pz, RedSmem& sm) {
-  const int nvec = (r.V + 3) / 4;
   while (hi - lo > 1u) {
     const uint32_t d = hi - lo;
     const uint32_t p1 = lo + max(1u, d / 3u);
     const uint32_t p2 = lo + max(1u, (d / 3u) * 2u);
     Red acc = red_zero();
-    for (int f = threadIdx.x; f < nvec; f += kBlock) {
-      const int64_t idx = 4ll * f;
-      float v[4];
-      load4(r, idx, v);
+    for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (idx + e >= r.V) continue;
-        const uint32_t key = KEYS ? signed_key(v[e]) : bits_of(v[e]);
-        if (key >= p1) {
-          acc.s0 += 1u;
-          if (MASS) acc.d0 += (double)v[e];
+        // key 0 stands for "no value": it is below every pivot (p1, p2 >= 1)
+        // and leaves the trackers' results unchanged but for the early exit
+        const bool in = valid && idx + e < r.V;
+        const uint32_t key = in ? (KEYS ? signed_key(v[e]) : bits_of(v[e])) : 0u;
+        const bool a1 = key >= p1, a2 = key >= p2;
+        acc.s0 += a1 ? 1u : 0u;
+        acc.s1 += a2 ? 1u : 0u;
+        if (MASS) {
+          acc.d0 += a1 ? (double)v[e] : 0.0;
+          acc.d1 += a2 ? (double)v[e] : 0.0;
         }
-        if (key >= p2) {
-          acc.s1 += 1u;
-          if (MASS) acc.d1 += (double)v[e];
-        }
-        if (key >= lo) acc.mn = min(acc.mn, key);
-        if (key < hi) acc.mx = max(acc.mx, key);
+        acc.mn = min(acc.mn, key >= lo ? key : 0xFFFFFFFFu);
+        acc.mx = max(acc.mx, key < hi ? key : 0u);
       }
-    }
+    });
     const Red t = block_reduce(acc, sm);
     if (t.mn > t.mx) break;  // no value in [lo, hi): cannot happen; keep lo
     if (t.mn == t.mx) return t.mn;
@@ -142,20 +176,15 @@ __device__ uint32_t threshold_search(const RowRef& r, uint32_t lo, uint32_t hi, 
 
 // mass and count of {bits >= tau} (x >= 0)
 __device__ inline Red mass_at_least(const RowRef& r, uint32_t tau, RedSmem& sm) {
-  const int nvec = (r.V + 3) / 4;
   Red acc = red_zero();
-  for (int f = threadIdx.x; f < nvec; f += kBlock) {
-    const int64_t idx = 4ll * f;
-    float v[4];
-    load4(r, idx, v);
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (idx + e < r.V && bits_of(v[e]) >= tau) {
-        acc.d0 += (double)v[e];
-        acc.s0 += 1u;
-      }
+      const bool t = valid && idx + e < r.V && bits_of(v[e]) >= tau;
+      acc.d0 += t ? (double)v[e] : 0.0;
+      acc.s0 += t ? 1u : 0u;
     }
-  }
+  });
   return block_reduce(acc, sm);
 }
 
@@ -231,20 +260,21 @@ __device__ inline int locate(const RowRef& r, const double* tm, int n_tiles, dou
       const int64_t tbase = (int64_t)tile * kTile;
       double run_carry = 0.0;
       int last_cand = -1;
+      float vt[kTileChunks][4];  // the whole tile in flight at once
+#pragma unroll
+      for (int q = 0; q < kTileChunks; ++q) load4(r, tbase + q * (kWave * 4) + lane * 4, vt[q]);
+#pragma unroll
       for (int q = 0; q < kTileChunks; ++q) {
         const int64_t idx = tbase + q * (kWave * 4) + lane * 4;
-        float v[4];
-        load4(r, idx, v);
+        const float (&v)[4] = vt[q];
         double s = 0.0;
         bool cand[4];
         int my_last = -1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           cand[e] = (idx + e < r.V) && (v[e] > low);
-          if (cand[e]) {
-            s += (double)v[e];
-            my_last = (int)(idx + e);
-          }
+          s += cand[e] ? (double)v[e] : 0.0;
+          my_last = cand[e] ? (int)(idx + e) : my_last;
         }
         const double incl = wave_incl_scan(s);
         const double excl = wave_excl_from_incl(incl);
@@ -252,10 +282,8 @@ __device__ inline int locate(const RowRef& r, const double* tm, int n_tiles, dou
         int hit_e = -1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (cand[e]) {
-            run += (double)v[e];
-            if (hit_e < 0 && run > Tl) hit_e = e;
-          }
+          run += cand[e] ? (double)v[e] : 0.0;
+          hit_e = (hit_e < 0 && cand[e] && run > Tl) ? e : hit_e;
         }
         const uint64_t hm = __ballot(hit_e >= 0);
         if (hm) {
@@ -293,14 +321,11 @@ __device__ inline void pivot_pass(const RowRef& r, int n_tiles, float a, float b
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // padding past the row end reads as 0, never above a pivot >= 0
-        if (v[e] > a) {
-          sa += (double)v[e];
-          ca += 1u;
-        }
-        if (v[e] > b) {
-          sb += (double)v[e];
-          cb += 1u;
-        }
+        const bool ga = v[e] > a, gb = v[e] > b;
+        sa += ga ? (double)v[e] : 0.0;
+        ca += ga ? 1u : 0u;
+        sb += gb ? (double)v[e] : 0.0;
+        cb += gb ? 1u : 0u;
       }
     }
     sa = wave_sum(sa);

@@ -34,9 +34,18 @@ __global__ __launch_bounds__(kBlock) void stream_sample_kernel(SampleParams P) {
 // renormalisation and logit masking
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void store4(float* out, int V, bool vec, int64_t idx, const float (&o)[4]) {
-  if (vec && idx + 3 < V) {
-    *reinterpret_cast<float4*>(out + idx) = make_float4(o[0], o[1], o[2], o[3]);
+// (vec: V % 4 == 0 and 16-byte aligned rows, so every group is whole; the
+// stores are global-memory instructions, not flat ones)
+__device__ __forceinline__ void store4(gptr<float> out, int V, bool vec, int64_t idx,
+                                       const float (&o)[4]) {
+  if (vec) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    v4f q;
+    q.x = o[0];
+    q.y = o[1];
+    q.z = o[2];
+    q.w = o[3];
+    *(gptr<v4f>)(out + idx) = q;
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -50,29 +59,26 @@ __global__ __launch_bounds__(kBlock) void stream_renorm_kernel(RenormParams P) {
   const int row = blockIdx.x;
   const int V = P.vocab;
   const RowRef r{as_global(P.in + (int64_t)row * V), V, P.vec_ok != 0};
-  float* out = P.out + (int64_t)row * V;
+  const gptr<float> out = as_global(P.out + (int64_t)row * V);
   const int nvec = (V + 3) / 4;
   const int k = P.top_k_arr ? P.top_k_arr[row] : P.top_k;
   const float pp = P.top_p_arr ? P.top_p_arr[row] : P.top_p;
 
   // pass 0: max key, total mass, NaN (logits) / sign-inf-NaN (probs) check
   Red acc = red_zero();
-  for (int f = threadIdx.x; f < nvec; f += kBlock) {
-    const int64_t idx = 4ll * f;
-    float v[4];
-    load4(r, idx, v);
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (idx + e >= V) continue;
+      const bool in = valid && idx + e < V;
       if (KIND == kMaskLogits) {
-        acc.mx = max(acc.mx, signed_key(v[e]));
-        if ((bits_of(v[e]) & 0x7FFFFFFFu) > 0x7F800000u) acc.s0 += 1u;
+        acc.mx = max(acc.mx, in ? signed_key(v[e]) : 0u);
+        acc.s0 += (in && (bits_of(v[e]) & 0x7FFFFFFFu) > 0x7F800000u) ? 1u : 0u;
       } else {
-        acc.mx = max(acc.mx, bits_of(v[e]));
-        acc.d0 += (double)v[e];
+        acc.mx = max(acc.mx, in ? bits_of(v[e]) : 0u);
+        acc.d0 += in ? (double)v[e] : 0.0;
       }
     }
-  }
+  });
   const Red s0 = block_reduce(acc, red);
   bool ok;
   if (KIND == kMaskLogits) {
@@ -108,25 +114,23 @@ __global__ __launch_bounds__(kBlock) void stream_renorm_kernel(RenormParams P) {
 
   if (KIND == kMaskLogits) {
     const float ninf = __uint_as_float(0xFF800000u);
-    for (int f = threadIdx.x; f < nvec; f += kBlock) {
-      const int64_t idx = 4ll * f;
-      float v[4], o[4];
-      load4(r, idx, v);
+    // invalid groups are copies of the last one: never stored (the op may
+    // run in place, where a repeated store could write a value twice renormalised)
+    for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+      float o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = signed_key(v[e]) >= tau ? v[e] : ninf;
-      store4(out, V, P.vec_ok != 0, idx, o);
-    }
+      if (valid) store4(out, V, P.vec_ok != 0, idx, o);
+    });
   } else {
     const double zk = mass_at_least(r, tau, red).d0;
     const double inv = 1.0 / zk;
-    for (int f = threadIdx.x; f < nvec; f += kBlock) {
-      const int64_t idx = 4ll * f;
-      float v[4], o[4];
-      load4(r, idx, v);
+    for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+      float o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = bits_of(v[e]) >= tau ? (float)((double)v[e] * inv) : 0.0f;
-      store4(out, V, P.vec_ok != 0, idx, o);
-    }
+      if (valid) store4(out, V, P.vec_ok != 0, idx, o);
+    });
   }
   if (P.row_status && threadIdx.x == 0) P.row_status[row] = 0;
 }
