@@ -94,6 +94,8 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
   if (vocab > DSS_MAX_VOCAB) return DSS_ERR_UNSUPPORTED;
   if (rows == 0) return DSS_OK;
   if (!in || !out) return DSS_ERR_INVALID_ARG;
+  const int vec_ok = (vocab % 4 == 0) && aligned16(in) && aligned16(out);
+  const dss::SplitPlan plan = dss::plan_split_renorm(kind, rows, vocab, flags, vec_ok);
   const size_t need = dss_workspace_size(op_id, rows, vocab, rows, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   const int dev = check_device();
@@ -109,9 +111,12 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
   p.top_p_arr = top_p_arr;
   p.top_p = top_p;
   p.row_status = row_status;
-  p.vec_ok = (vocab % 4 == 0) && aligned16(in) && aligned16(out);
+  p.vec_ok = vec_ok;
   const hipError_t e =
-      dss::launch_stream_renorm(kind, p, static_cast<hipStream_t>(stream), timing_events());
+      plan.W > 0 ? dss::launch_split_renorm(kind, p, plan, workspace,
+                                            static_cast<hipStream_t>(stream), timing_events())
+                 : dss::launch_stream_renorm(kind, p, static_cast<hipStream_t>(stream),
+                                             timing_events());
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
@@ -210,7 +215,13 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                                      int32_t num_outputs, uint32_t flags) {
   // sized for 16-byte aligned rows; an unaligned call runs the streaming
   // engine, which needs none
-  if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || vocab <= 0 || num_outputs <= 0) return 0;
+  if (vocab <= 0) return 0;
+  if (op == DSS_OP_TOP_K_RENORM || op == DSS_OP_TOP_K_MASK_LOGITS) {
+    if (rows <= 0) return 0;
+    const int kind = op == DSS_OP_TOP_K_RENORM ? dss::kRenormTopK : dss::kMaskLogits;
+    return dss::plan_split_renorm(kind, rows, vocab, flags, vocab % 4 == 0).workspace;
+  }
+  if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || num_outputs <= 0) return 0;
   return dss::plan_split(op, rows, vocab, num_outputs, flags, vocab % 4 == 0).workspace;
 }
 

@@ -94,10 +94,18 @@ struct SplitPlan {
   int L;             // slice length (values, multiple of 4)
   int nv;            // 16-byte loads per thread per slice
   int chunk;         // outputs per launch
-  size_t workspace;  // bytes of workspace needed
+  size_t handoff;    // bytes of the hand-off area (counters, headers, lists)
+  size_t workspace;  // bytes of workspace needed in all (hand-off + results)
 };
 SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flags, int vec_ok);
 hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& plan,
+                               void* workspace, hipStream_t s, const LaunchEvents& ev);
+
+// Split-row top-k renormalisation / logit masking (kind kRenormTopK or
+// kMaskLogits): the split engine finds tau_k and Z_k per row, a second kernel
+// writes the rows.  W == 0 means "not eligible" (streaming engine instead).
+SplitPlan plan_split_renorm(int kind, int rows, int vocab, uint32_t flags, int vec_ok);
+hipError_t launch_split_renorm(int kind, const RenormParams& p, const SplitPlan& plan,
                                void* workspace, hipStream_t s, const LaunchEvents& ev);
 
 }  // namespace dss

@@ -61,8 +61,22 @@ struct SplitParams {
   uint32_t* ctr;   // [kChunk] arrival counters (zero between calls)
   uint32_t* gen;   // [kChunk] generation numbers
   uint32_t* hdr;   // [n_out][W][kHdrWords]
-  uint64_t* list;  // [n_out][W][kListMax]: bits | (index << 32)
+  uint64_t* list;  // [n_out][W][kListMax]: key | (index << 32)
+  uint32_t* r_tau;    // renorm / mask: [n_out] tau_k as an order key
+  double* r_z;        // renorm: [n_out] kept mass Z_k
+  uint8_t* r_status;  // renorm / mask: [n_out] 0 ok, 1 invalid row, 2 written already
 };
+
+// What the split engine computes: a sample, or tau_k (and Z_k) for a top-k
+// renormalisation or a top-k logit mask, written by a second kernel.
+enum SplitKind : int { kKindSample = 0, kKindRenorm = 1, kKindMask = 2 };
+
+// Order key of a value: the float32 bits for probabilities (non-negative,
+// F4 note §③), the signed-order key for logits (F4 note §⑧).
+template <bool KEYS>
+__device__ __forceinline__ uint32_t key_of(float x) {
+  return KEYS ? signed_key(x) : bits_of(x);
+}
 
 // Histograms are stored in chunks of NB/64 bins (the bins one lane sums in
 // a search), each chunk padded by four words so that the 64 lanes' 16-byte
@@ -94,6 +108,7 @@ struct SplitSmem {
   double draws[stream::kPreDraws];
   uint32_t red[4][kWaves];        // per-wave partials of the block scans
   uint32_t wmax[kWaves];
+  uint32_t wnan[kWaves];
   uint32_t off[kMaxSlices + 1];
   uint32_t sel[kWave];
   uint32_t res[8];
@@ -117,8 +132,9 @@ __device__ __forceinline__ uint32_t rank_in(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint32_t max4_bits(const float4& x) {
-  return max(max(bits_of(x.x), bits_of(x.y)), max(bits_of(x.z), bits_of(x.w)));
+template <bool KEYS>
+__device__ __forceinline__ uint32_t max4_key(const float4& x) {
+  return max(max(key_of<KEYS>(x.x), key_of<KEYS>(x.y)), max(key_of<KEYS>(x.z), key_of<KEYS>(x.w)));
 }
 
 template <int NB>
@@ -356,9 +372,19 @@ enum SplitMode : int { kDone = 0, kFallback = 1 };
 
 // Everything but the streaming fallback; returns kFallback when the output
 // must be sampled by the streaming engine instead (one call site, below).
-template <int OP, int NV>
+// Reports output i (chunk-local li) invalid.
+template <int KIND>
+__device__ __forceinline__ void split_invalid(const SampleParams& P, const SplitParams& S, int i,
+                                              int li) {
+  if (KIND == kKindSample) stream::write_sample(P, i, -1, 0);
+  else as_global(S.r_status)[li] = 1;
+}
+
+template <int KIND, int OP, int NV>
 __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitParams& S,
                                            SplitSmem& sm, int& out_i) {
+  constexpr bool KEYS = KIND == kKindMask;    // logits: signed-order keys
+  constexpr uint32_t kSh = KEYS ? 21u : 20u;  // top eleven bits of a key
   const int W = S.W;
   const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
   const int li = (local / W) * 8 + xcd;  // the W slices of an output share b % 8
@@ -394,7 +420,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     // no hand-off for this output: slice 0 answers alone
     if (s != 0) return kDone;
     if (!ok) {
-      if (tid == 0) stream::write_sample(P, i, -1, 0);
+      if (tid == 0) split_invalid<KIND>(P, S, i, li);
       return kDone;
     }
     return kFallback;
@@ -403,16 +429,20 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // while the slice is in flight: clear the histogram; wave 0 reads the
   // row's generation and computes the first 256 draws of the output's stream
   clear_hist<kHistBins>(sm.hist, tid, kBlock);
-  const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
-  const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
+  const uint64_t seed =
+      KIND != kKindSample ? 0ull : P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset =
+      KIND != kKindSample ? 0ull : P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
   uint32_t gen = 0u;
   if (wave == 0) {
     if (W > 1 && lane == 0)
       gen = __hip_atomic_load(as_global(S.gen + li), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const Philox4x64 ph = philox4x64_10(offset, sid, (uint64_t)lane, 0ull, seed, 0ull);
+    if (KIND == kKindSample) {
+      const Philox4x64 ph = philox4x64_10(offset, sid, (uint64_t)lane, 0ull, seed, 0ull);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.draws[4 * lane + e] = (double)(ph.w[e] >> 11) * 0x1p-53;
+      for (int e = 0; e < 4; ++e) sm.draws[4 * lane + e] = (double)(ph.w[e] >> 11) * 0x1p-53;
+    }
   }
   __syncthreads();
 
@@ -426,30 +456,40 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const uint32_t pad = (uint32_t)lane * H1::kStride + H1::kChunk;
   uint32_t key[NV];
   uint32_t mx = 0u;
+  bool nan_seen = false;  // logits: a NaN invalidates the row
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const bool in = tid + j * kBlock < nvec;
-    const uint32_t m = max4_bits(v[j]);
+    const uint32_t m = max4_key<KEYS>(v[j]);
     key[j] = in ? m + 1u : 0u;
     mx = max(mx, in ? m : 0u);
-    atomicAdd(&sm.hist[in ? H1::at(min(m >> 20, (uint32_t)(kHistBins - 1))) : pad], 1u);
+    atomicAdd(&sm.hist[in ? H1::at(min(m >> kSh, (uint32_t)(kHistBins - 1))) : pad], 1u);
+    if (KEYS)
+      nan_seen = nan_seen || (in && (isnan(v[j].x) || isnan(v[j].y) || isnan(v[j].z) || isnan(v[j].w)));
   }
   mx = wave_max(mx);
   if (lane == 0) sm.wmax[wave] = mx;
+  if (KEYS) {
+    const bool wn = __ballot(nan_seen) != 0ull;
+    if (lane == 0) sm.wnan[wave] = wn ? 1u : 0u;
+  }
   __syncthreads();
   if (wave == 0) {
     uint32_t bin, above, total;
     wave_find<kHistBins>(sm.hist, (uint32_t)k, bin, above, total);
     const uint32_t smax = wave_max(lane < kWaves ? sm.wmax[lane] : 0u);
+    const bool anynan = KEYS && __ballot(lane < kWaves && sm.wnan[lane] != 0u) != 0ull;
     if (lane == 0) {
-      sm.res[0] = total < (uint32_t)k ? 0u : bin << 20;  // fewer than k vectors: all of it
+      sm.res[0] = total < (uint32_t)k ? 0u : bin << kSh;  // fewer than k vectors: all of it
       sm.res[1] = smax;
+      sm.res[2] = anynan ? 1u : 0u;
     }
   }
   __syncthreads();
   const uint32_t bnd = sm.res[0];
   const uint32_t smax = sm.res[1];
-  const bool bad = smax >= 0x7F800000u;  // a sign bit, an inf or a NaN somewhere
+  // probabilities: a sign bit, an inf or a NaN somewhere; logits: a NaN
+  const bool bad = KEYS ? sm.res[2] != 0u : smax >= 0x7F800000u;
 
   // the vectors with a value >= bnd (key > bnd), staged in thread order
   uint32_t nv_hit = 0u;
@@ -470,7 +510,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   }
   __syncthreads();
 
-  // their positive elements >= bnd, in staging order, as (bits | index << 32),
+  // their positive elements >= bnd, in staging order, as (key | index << 32),
   // into full[] (the row's list when W == 1, a staging copy otherwise)
   const uint32_t bthr = max(bnd, 1u);
   constexpr int kSt = kStageMax / kBlock;
@@ -484,10 +524,10 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     const uint32_t gg = live ? g : (uint32_t)(kStageMax + lane);
     const float4 x = sm.u.a.vec[gg];
     sidx[q] = sm.u.a.vidx[gg];
-    xb[q][0] = live ? bits_of(x.x) : 0u;
-    xb[q][1] = live ? bits_of(x.y) : 0u;
-    xb[q][2] = live ? bits_of(x.z) : 0u;
-    xb[q][3] = live ? bits_of(x.w) : 0u;
+    xb[q][0] = live ? key_of<KEYS>(x.x) : 0u;
+    xb[q][1] = live ? key_of<KEYS>(x.y) : 0u;
+    xb[q][2] = live ? key_of<KEYS>(x.z) : 0u;
+    xb[q][3] = live ? key_of<KEYS>(x.w) : 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ne += xb[q][e] >= bthr ? 1u : 0u;
   }
@@ -512,7 +552,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   if (W == 1) {
     // the whole row is in this work-group: full[] holds its list
     if (bad || smax == 0u) {
-      if (tid == 0) stream::write_sample(P, i, -1, 0);
+      if (tid == 0) split_invalid<KIND>(P, S, i, li);
       return kDone;
     }
     if (!publish) return kFallback;
@@ -533,6 +573,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       h[2] = smax;
       h[3] = gen;
       h[4] = xcc_id();
+      h[5] = bad ? 1u : 0u;
     }
     // hand-off: this work-group's stores reach the XCD's L2 before it arrives
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -573,7 +614,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
         __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const bool mine = lane < W;
-      uint32_t ht = 0u, hc = 0u, hm = 0u, hg = mygen, hx = me;
+      uint32_t ht = 0u, hc = 0u, hm = 0u, hg = mygen, hx = me, hb = 0u;
       if (mine) {
         const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + lane) * kHdrWords);
         ht = __hip_atomic_load(h + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -581,7 +622,9 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
         hm = __hip_atomic_load(h + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hb = __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      const bool anybad = __ballot(mine && hb != 0u) != 0ull;
       const bool foreign = __ballot(mine && (hg != mygen || hx != me)) != 0ull;
       const bool ovf = __ballot(mine && hc > (uint32_t)kListMax) != 0ull;  // kNoList too
       const uint32_t cc = (mine && hc <= (uint32_t)kListMax) ? hc : 0u;
@@ -594,7 +637,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       if (lane == 0) {
         uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back
         if (foreign) status = 2u;
-        else if (gm >= 0x7F800000u || gm == 0u) status = 1u;
+        else if (anybad || (!KEYS && gm == 0u)) status = 1u;
         else if (ovf || all > (uint32_t)kRowCandMax) status = 2u;
         sm.res[2] = ts;
         sm.res[3] = all;
@@ -607,7 +650,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     __syncthreads();
     const uint32_t status = sm.res[5];
     if (status == 1u) {
-      if (tid == 0) stream::write_sample(P, i, -1, 0);
+      if (tid == 0) split_invalid<KIND>(P, S, i, li);
       return kDone;
     }
     if (status == 2u) return kFallback;
@@ -756,6 +799,22 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
   }
 
+  if (KIND != kKindSample) {
+    // renormalisation / masking: tau_k, and the kept mass Z_k in a fixed order
+    double zs = 0.0;
+    if (KIND == kKindRenorm) {
+      for (uint32_t c = lane; c < m; c += kWave)
+        zs += (double)__uint_as_float((uint32_t)sm.u.b.cand[c]);
+      zs = wave_sum(zs);
+    }
+    if (lane == 0) {
+      as_global(S.r_tau)[li] = tau_k;
+      as_global(S.r_z)[li] = zs;
+      as_global(S.r_status)[li] = 0;
+    }
+    return kDone;
+  }
+
   // ---- the dual-pivot loop on wave 0 ----------------------------------------
   const float pfrac = OP == kOpTopKTopP ? stream::clamp01(pp) : 0.0f;
   const float low = tau_k > 0u ? __uint_as_float(tau_k - 1u) : 0.0f;
@@ -775,33 +834,81 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   return kDone;
 }
 
-template <int OP, int NV>
-__global__ __launch_bounds__(kBlock) void split_sample_kernel(SampleParams P, SplitParams S) {
+template <int KIND, int OP, int NV>
+__global__ __launch_bounds__(kBlock) void split_kernel(SampleParams P, SplitParams S,
+                                                       RenormParams RP) {
   __shared__ SplitSmem sm;
   int i = 0;
-  const int mode = split_sample<OP, NV>(P, S, sm, i);
-  if (mode == kFallback) stream::sample_row<OP>(P, i, sm.u.stream);
+  const int mode = split_sample<KIND, OP, NV>(P, S, sm, i);
+  if (mode == kFallback) {
+    if constexpr (KIND == kKindSample) {
+      stream::sample_row<OP>(P, i, sm.u.stream);
+    } else {
+      // the whole row by the streaming engine, output written here
+      stream::renorm_row<KIND == kKindRenorm ? kRenormTopK : kMaskLogits>(RP, i, sm.u.stream.red);
+      if (threadIdx.x == 0) as_global(S.r_status)[i - S.out0] = 2;
+    }
+  }
 }
 
-template <int OP, int NV>
-void launch_one(const SampleParams& p, const SplitParams& sp, hipStream_t s, const LaunchEvents& ev,
-                bool first, bool last) {
+// The write pass of a split renormalisation / mask: work-group c of output
+// li covers vectors [c * kBlock * kWB, (c + 1) * kBlock * kWB) of its row,
+// kWB 16-byte loads in flight per thread.  out = x / Z_k (renorm) or x (mask)
+// where key(x) >= tau_k, else 0 or -inf; invalid rows are NaN-filled.
+constexpr int kWB = 8;
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void split_write_kernel(RenormParams P, SplitParams S,
+                                                             int nchunk) {
+  constexpr bool KEYS = KIND == kKindMask;
+  const int li = blockIdx.x / nchunk, c = blockIdx.x - li * nchunk;
+  const int row = S.out0 + li;
+  const uint32_t st = as_global(S.r_status)[li];
+  if (st == 2u) return;
+  const int V = P.vocab, nvec = V / 4;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const gptr<const v4f> src = (gptr<const v4f>)as_global(P.in + (int64_t)row * V);
+  const gptr<v4f> dst = (gptr<v4f>)as_global(P.out + (int64_t)row * V);
+  const int f0 = c * kBlock * kWB + threadIdx.x;
+  v4f x[kWB];
+#pragma unroll
+  for (int u = 0; u < kWB; ++u) x[u] = src[min(f0 + u * kBlock, nvec - 1)];
+  const uint32_t tau = as_global(S.r_tau)[li];
+  const double inv = KIND == kKindRenorm ? 1.0 / as_global(S.r_z)[li] : 0.0;
+  const float qnan = __uint_as_float(0x7FC00000u), ninf = __uint_as_float(0xFF800000u);
+#pragma unroll
+  for (int u = 0; u < kWB; ++u) {
+    v4f o;
+    for (int e = 0; e < 4; ++e) {
+      const float v = x[u][e];
+      const bool keep = key_of<KEYS>(v) >= tau;
+      o[e] = st == 1u ? qnan
+             : KEYS   ? (keep ? v : ninf)
+                      : (keep ? (float)((double)v * inv) : 0.0f);
+    }
+    if (f0 + u * kBlock < nvec) dst[f0 + u * kBlock] = o;
+  }
+  if (c == 0 && threadIdx.x == 0 && P.row_status) as_global(P.row_status)[row] = st == 1u ? 1 : 0;
+}
+
+template <int KIND, int OP, int NV>
+void launch_one(const SampleParams& p, const SplitParams& sp, const RenormParams& rp,
+                hipStream_t s, const LaunchEvents& ev, bool first, bool last) {
   const int groups = (sp.n_out + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * sp.W)), block(kBlock);
-  launch_kernel(split_sample_kernel<OP, NV>, grid, block, s, ev, first, last, p, sp);
+  launch_kernel(split_kernel<KIND, OP, NV>, grid, block, s, ev, first, last, p, sp, rp);
 }
 
-template <int OP>
-void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, hipStream_t s,
-               const LaunchEvents& ev, bool first, bool last) {
+template <int KIND, int OP>
+void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, const RenormParams& rp,
+               hipStream_t s, const LaunchEvents& ev, bool first, bool last) {
   switch (nv) {
-    case 1: launch_one<OP, 1>(p, sp, s, ev, first, last); break;
-    case 2: launch_one<OP, 2>(p, sp, s, ev, first, last); break;
-    case 3: launch_one<OP, 3>(p, sp, s, ev, first, last); break;
-    case 4: launch_one<OP, 4>(p, sp, s, ev, first, last); break;
-    case 6: launch_one<OP, 6>(p, sp, s, ev, first, last); break;
-    case 8: launch_one<OP, 8>(p, sp, s, ev, first, last); break;
-    default: launch_one<OP, 10>(p, sp, s, ev, first, last); break;
+    case 1: launch_one<KIND, OP, 1>(p, sp, rp, s, ev, first, last); break;
+    case 2: launch_one<KIND, OP, 2>(p, sp, rp, s, ev, first, last); break;
+    case 3: launch_one<KIND, OP, 3>(p, sp, rp, s, ev, first, last); break;
+    case 4: launch_one<KIND, OP, 4>(p, sp, rp, s, ev, first, last); break;
+    case 6: launch_one<KIND, OP, 6>(p, sp, rp, s, ev, first, last); break;
+    case 8: launch_one<KIND, OP, 8>(p, sp, rp, s, ev, first, last); break;
+    default: launch_one<KIND, OP, 10>(p, sp, rp, s, ev, first, last); break;
   }
 }
 
@@ -819,7 +926,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flags, int vec_ok) {
-  SplitPlan plan{0, 0, 0, 0, 0};
+  SplitPlan plan{0, 0, 0, 0, 0, 0};
   (void)rows;
   if (op != kOpTopK && op != kOpTopKTopP) return plan;
   if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO)) return plan;
@@ -844,14 +951,22 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
   plan.L = L;
   plan.nv = nv;
   plan.chunk = ch;
-  plan.workspace = W == 1 ? 0
-                          : kCtlBytes + align256((size_t)ch * W * kHdrWords * 4) +
-                                (size_t)ch * W * kListMax * 8;
+  plan.handoff = W == 1 ? 0
+                        : align256(kCtlBytes + align256((size_t)ch * W * kHdrWords * 4) +
+                                   (size_t)ch * W * kListMax * 8);
+  plan.workspace = plan.handoff;
   return plan;
 }
 
-hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& plan,
-                               void* workspace, hipStream_t s, const LaunchEvents& ev) {
+namespace {
+// the hand-off region of a plan, then (renorm / mask) the per-output results.
+// The results never overlap the control words (arrival counters, generation
+// numbers at fixed offsets), which every op sharing a workspace relies on,
+// even when the plan itself needs no hand-off (W == 1).
+size_t result_bytes(size_t ch) { return align256(ch * 4) + align256(ch * 8) + align256(ch); }
+size_t results_offset(const SplitPlan& plan) { return max(plan.handoff, align256(kCtlBytes)); }
+
+SplitParams split_params(const SplitPlan& plan, void* workspace) {
   char* ws = static_cast<char*>(workspace);
   const size_t ch = (size_t)plan.chunk;
   SplitParams sp;
@@ -863,14 +978,68 @@ hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& p
   sp.gen = sp.ctr + kChunk;
   sp.hdr = reinterpret_cast<uint32_t*>(ws + kCtlBytes);
   sp.list = reinterpret_cast<uint64_t*>(ws + kCtlBytes + align256(ch * plan.W * kHdrWords * 4));
+  char* res = ws + results_offset(plan);
+  sp.r_tau = reinterpret_cast<uint32_t*>(res);
+  sp.r_z = reinterpret_cast<double*>(res + align256(ch * 4));
+  sp.r_status = reinterpret_cast<uint8_t*>(res + align256(ch * 4) + align256(ch * 8));
+  return sp;
+}
+}  // namespace
+
+SplitPlan plan_split_renorm(int kind, int rows, int vocab, uint32_t flags, int vec_ok) {
+  SplitPlan plan{0, 0, 0, 0, 0, 0};
+  if (kind != kRenormTopK && kind != kMaskLogits) return plan;
+  plan = plan_split(kOpTopK, rows, vocab, rows, flags, vec_ok);
+  if (plan.W > 0) plan.workspace = results_offset(plan) + result_bytes((size_t)plan.chunk);
+  return plan;
+}
+
+hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& plan,
+                               void* workspace, hipStream_t s, const LaunchEvents& ev) {
+  SplitParams sp = split_params(plan, workspace);
+  const RenormParams rp{};
   for (int out0 = 0; out0 < p.num_outputs; out0 += plan.chunk) {
     sp.out0 = out0;
     sp.n_out = min(plan.chunk, p.num_outputs - out0);
     const bool first = out0 == 0, last = out0 + plan.chunk >= p.num_outputs;
     if (op == kOpTopK) {
-      launch_nv<kOpTopK>(plan.nv, p, sp, s, ev, first, last);
+      launch_nv<kKindSample, kOpTopK>(plan.nv, p, sp, rp, s, ev, first, last);
     } else {
-      launch_nv<kOpTopKTopP>(plan.nv, p, sp, s, ev, first, last);
+      launch_nv<kKindSample, kOpTopKTopP>(plan.nv, p, sp, rp, s, ev, first, last);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_split_renorm(int kind, const RenormParams& rp, const SplitPlan& plan,
+                               void* workspace, hipStream_t s, const LaunchEvents& ev) {
+  // the results must lie inside the workspace the plan sized
+  if (results_offset(plan) + result_bytes((size_t)plan.chunk) > plan.workspace)
+    return hipErrorInvalidValue;
+  SplitParams sp = split_params(plan, workspace);
+  SampleParams p{};
+  p.probs = rp.in;
+  p.rows = rp.rows;
+  p.vocab = rp.vocab;
+  p.num_outputs = rp.rows;
+  p.top_k_arr = rp.top_k_arr;
+  p.top_k = rp.top_k;
+  p.vec_ok = 1;
+  const int nvec = rp.vocab / 4;
+  const int nchunk = (nvec + kBlock * kWB - 1) / (kBlock * kWB);
+  for (int out0 = 0; out0 < p.num_outputs; out0 += plan.chunk) {
+    sp.out0 = out0;
+    sp.n_out = min(plan.chunk, p.num_outputs - out0);
+    const bool first = out0 == 0, last = out0 + plan.chunk >= p.num_outputs;
+    const dim3 wgrid((unsigned)(sp.n_out * nchunk)), block(kBlock);
+    if (kind == kRenormTopK) {
+      launch_nv<kKindRenorm, kOpTopK>(plan.nv, p, sp, rp, s, ev, first, false);
+      launch_kernel(split_write_kernel<kKindRenorm>, wgrid, block, s, ev, false, last, rp, sp, nchunk);
+    } else {
+      launch_nv<kKindMask, kOpTopK>(plan.nv, p, sp, rp, s, ev, first, false);
+      launch_kernel(split_write_kernel<kKindMask>, wgrid, block, s, ev, false, last, rp, sp, nchunk);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

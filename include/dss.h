@@ -22,10 +22,13 @@
  *   stream).  Work is enqueued asynchronously; nothing synchronises the host.
  *
  * Workspace.  `workspace` / `workspace_bytes` is caller-owned device scratch
- *   of at least dss_workspace_size(...) bytes (NULL is fine when that is 0).
- *   It must be zero-filled once when it is allocated; every call leaves it
- *   zero-filled again on return of its kernels, so a workspace can be reused
- *   by later calls on the same stream without clearing.  Two calls that run
+ *   of at least dss_workspace_size(...) bytes (NULL is fine when that is 0):
+ *   the split-row engine's hand-off area (top-k and top-k-then-top-p
+ *   sampling) and its per-row results (top-k renormalisation and top-k logit
+ *   masking).  It must be zero-filled once when it is allocated; every call
+ *   leaves its arrival counters at zero again when its kernels end (the rest
+ *   is written before it is read), so a workspace can be reused by later
+ *   calls on the same stream without clearing.  Two calls that run
  *   concurrently (different streams) need different workspaces.
  *
  * Outputs of the sampling ops (length num_outputs):

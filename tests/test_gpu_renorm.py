@@ -132,3 +132,60 @@ def test_mask_logits():
                 assert np.array_equal(out[r], expect), r
             else:
                 assert np.isnan(out[r]).all()
+
+
+# Shapes for the split-row renorm / mask path (V % 4 == 0, V >= 1024): several
+# slices per row, one slice per row (W = 1), and more rows than one launch
+# chunk takes (2048).
+@pytest.mark.parametrize("rows,V", [(3, 8192), (64, 16384), (300, 4096), (2100, 1024)])
+def test_split_renorm_and_mask_edges(rows, V):
+    rng = np.random.default_rng(rows * 7 + V)
+    probs = rng.dirichlet(np.full(V, 0.3), size=rows).astype(np.float32)
+    probs[0, : V // 8] = probs[0].max()                  # ties across the top-k boundary
+    ks = rng.integers(1, 1500, size=rows).astype(np.int32)
+    ks[0] = 200
+    special = {}
+    if rows > 6:
+        probs[1, 5] = np.nan
+        probs[2, 7] = -1e-3
+        probs[3] = 0.0
+        probs[4, 9] = np.inf
+        ks[5] = 0                                         # invalid parameter
+        ks[6] = 3000                                      # above the split engine's cap
+        special = {1, 2, 3, 4, 5}
+    P = gpu(probs)
+    K = gpu(ks)
+    out, st = dss.top_k_renorm_probs(P, K, return_status=True)
+    out, st = host(out), host(st)
+    P2 = gpu(probs)
+    dss.top_k_renorm_probs(P2, K, out=P2)                # in place
+    inplace = host(P2)
+    for r in range(rows):
+        valid, expect = ref.top_k_renorm(probs[r], ks[r])
+        assert valid == (r not in special), r
+        assert st[r] == (0 if valid else 1), r
+        if valid:
+            _check_renorm(out[r], probs[r], valid, expect)
+            assert np.array_equal(inplace[r], out[r]), r
+        else:
+            assert np.isnan(out[r]).all() and np.isnan(inplace[r]).all(), r
+
+    logits = si.logits_rows(rng, rows, V)
+    logits[0, : V // 8] = logits[0].max()                # ties at the top
+    if rows > 6:
+        logits[1, 3] = np.nan                             # invalid row
+        logits[2, ::3] = -np.inf
+        logits[3, 1] = np.inf
+        logits[4, :] = np.float32(-2.0)
+        logits[4, 10] = np.float32(-0.0)
+        logits[4, 11] = np.float32(0.0)                   # -0.0 == +0.0
+    L = gpu(logits)
+    out, st = dss.top_k_mask_logits(L, K, return_status=True)
+    out, st = host(out), host(st)
+    for r in range(rows):
+        valid, expect = ref.mask_logits_row(logits[r], ks[r])
+        assert st[r] == (0 if valid else 1), r
+        if valid:
+            assert np.array_equal(out[r], expect), r
+        else:
+            assert np.isnan(out[r]).all(), r

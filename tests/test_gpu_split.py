@@ -144,3 +144,23 @@ def test_split_workspace_reuse_across_shapes():
             s, v = host(s), host(v)
             assert (v == 1).all()
             assert all(sup[r][s[r]] for r in range(rows)), (rows, vocab, call)
+
+
+def test_workspace_shared_by_renorm_and_sampling():
+    """The binding keeps one workspace per device for every op: the per-row
+    results of a split renorm or mask of any shape (one slice per row, several
+    slices, many rows) must leave the sampler's arrival counters at zero."""
+    rng = np.random.default_rng(77)
+    w = si.small()
+    P = gpu(w["probs"])
+    sup = _supports(w["probs"], "top_k_top_p", 50, np.float32(0.9))
+    for rows, V in ((2100, 1024), (64, 16384), (3, 8192)):
+        probs = rng.dirichlet(np.full(V, 0.3), size=rows).astype(np.float32)
+        dss.top_k_renorm_probs(gpu(probs), 100)
+        dss.top_k_mask_logits(gpu(np.log(probs)), 100)
+        for call in range(3):
+            s, v = dss.top_k_top_p_sampling_from_probs(P, 50, np.float32(0.9), seed=5,
+                                                       offset=call, return_valid=True)
+            s, v = host(s), host(v)
+            assert (v == 1).all(), (rows, V, call)
+            assert all(sup[r][s[r]] for r in range(4)), (rows, V, call)
