@@ -91,6 +91,112 @@ def cpu_baseline(w, budget_s=10.0):
                       f"prefix + CDF draw per row), {dt:.1f} s single-threaded Python/numpy"}
 
 
+def kernel_times(lib, fn, reps, warm=2):
+    """Per-call kernel time in us of fn() (dispatch-event hook), reps calls."""
+    import torch
+    for _ in range(warm):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        lib.dss_set_timing_events(a.cuda_event, b.cuda_event)
+        fn()
+    lib.dss_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+
+def extra_configs(dss, si, lib, dev):
+    """The other workloads of the sampling path, one line each: kernel time
+    per call (mean, and p50/p99 where the workload is a latency case) and the
+    fraction of the 8 TB/s roofline for the op's algorithmic bytes (one read
+    of each output's row; read + write for renorm and masking)."""
+    import torch
+
+    def g(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def entry(t, nbytes, **kw):
+        d = {"kernel_us": float(t.mean()), "algorithmic_bytes": int(nbytes),
+             "hbm_frac": nbytes / (t.mean() * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+        d.update(kw)
+        return d
+
+    out = {}
+    w = si.small()
+    P = g(w["probs"])
+    B, V = P.shape
+    t = kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_probs(P, 50, 0.9, seed=1, offset=0),
+                     200)
+    out["small B=4 V=32000 top_k_top_p (k=50, p=0.9)"] = entry(
+        t, B * V * 4, p50_us=float(np.percentile(t, 50)), p99_us=float(np.percentile(t, 99)))
+    w = si.renorm()
+    P = g(w["probs"])
+    B, V = P.shape
+    k, p = g(w["top_k"]), g(w["top_p"])
+    out["renorm B=64 V=151936 top_p_renorm_probs"] = entry(
+        kernel_times(lib, lambda: dss.top_p_renorm_probs(P, p), 10), 2 * B * V * 4)
+    out["renorm B=64 V=151936 top_k_renorm_probs"] = entry(
+        kernel_times(lib, lambda: dss.top_k_renorm_probs(P, k), 50), 2 * B * V * 4)
+    L = g(si.logits_rows(np.random.default_rng(1), B, V))
+    out["logits B=64 V=151936 top_k_mask_logits"] = entry(
+        kernel_times(lib, lambda: dss.top_k_mask_logits(L, k), 50), 2 * B * V * 4)
+    out["probs B=64 V=151936 sampling_from_probs"] = entry(
+        kernel_times(lib, lambda: dss.sampling_from_probs(P, seed=1, offset=0), 50), B * V * 4)
+    out["probs B=64 V=151936 top_p_sampling_from_probs"] = entry(
+        kernel_times(lib, lambda: dss.top_p_sampling_from_probs(P, p, seed=1, offset=0), 10),
+        B * V * 4)
+    out["probs B=64 V=151936 min_p_sampling_from_probs (0.05)"] = entry(
+        kernel_times(lib, lambda: dss.min_p_sampling_from_probs(P, 0.05, seed=1, offset=0), 10),
+        B * V * 4)
+    w = si.latency()
+    P = g(w["probs"])
+    t = kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_probs(P, 50, 0.9, seed=3,
+                                                                       offset=0), 1000, 20)
+    out["latency B=1 V=151936 top_k_top_p (k=50, p=0.9), 1000 calls"] = entry(
+        t, 151936 * 4, p50_us=float(np.percentile(t, 50)), p95_us=float(np.percentile(t, 95)),
+        p99_us=float(np.percentile(t, 99)))
+    w = si.hetero()
+    P = g(w["probs"])
+    B, V = P.shape
+    idx, op, seeds = w["indices"], w["op_of_output"], w["seeds"]
+    step, parts = 0.0, {}
+    for o, name in enumerate(("top_k_top_p", "min_p", "plain")):
+        sel = np.nonzero(op == o)[0]
+        I, S = g(idx[sel]), g(seeds[sel].view(np.int64))
+        K, Pp, M = g(w["top_k"][idx[sel]]), g(w["top_p"][idx[sel]]), g(w["min_p"][idx[sel]])
+        fn = {0: lambda: dss.top_k_top_p_sampling_from_probs(P, K, Pp, indices=I, seed=S, offset=0),
+              1: lambda: dss.min_p_sampling_from_probs(P, M, indices=I, seed=S, offset=0),
+              2: lambda: dss.sampling_from_probs(P, indices=I, seed=S, offset=0)}[o]
+        t = kernel_times(lib, fn, 5, 1)
+        parts[name] = {"outputs": int(len(sel)), "kernel_us": float(t.mean())}
+        step += float(t.mean())
+    out["hetero B=256 V=128256, 512 outputs, three calls per step"] = {
+        "kernel_us": step, "algorithmic_bytes": 512 * V * 4,
+        "hbm_frac": 512 * V * 4 / (step * 1e-6) / (HBM_PEAK_GBS * 1e9), "calls": parts}
+    w = si.stress()
+    P = g(w["probs"])
+    B, V = P.shape
+    seeds = g(w["seeds"].view(np.int64))
+    t = kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_probs(P, 1000, 0.95, seed=seeds,
+                                                                       offset=0), 3, 1)
+    _, _, r = dss.top_k_top_p_sampling_from_probs(P, 1000, 0.95, seed=seeds, offset=7,
+                                                  return_valid=True, return_rounds=True)
+    r = r.cpu().numpy()
+    hist = {}
+    for gi, name in enumerate(("near-uniform", "peaked", "geometric")):
+        x = r[w["groups"] == gi]
+        hist[name] = {"mean": float(x.mean()), "p95": float(np.percentile(x, 95)),
+                      "p99": float(np.percentile(x, 99)), "max": int(x.max())}
+    out["stress B=512 V=256000 top_k_top_p (k=1000, p=0.95)"] = entry(t, B * V * 4,
+                                                                      rounds=hist)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +205,8 @@ def main():
     ap.add_argument("--engine", default="auto", choices=["auto", "streaming", "from_zero"])
     ap.add_argument("--warm-cache", action="store_true", help="time one buffer only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (other_configs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -213,6 +321,10 @@ def main():
                      "algorithmic_bytes": bytes_per_launch},
         "rounds_histogram": {str(kk): vv for kk, vv in sorted(hist.items())},
     }
+    if not args.no_extra and args.engine == "auto" and not args.warm_cache:
+        del bufs
+        torch.cuda.empty_cache()
+        out["other_configs"] = extra_configs(dss, si, lib, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
