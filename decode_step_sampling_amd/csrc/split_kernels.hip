@@ -49,6 +49,7 @@ constexpr int kBndMax = 4096;     // entries in the boundary bin
 constexpr int kSplitKCap = 2048;
 constexpr int kMaxSlices = 16;    // a power of two
 constexpr int kHdrWords = 8;
+constexpr int kMassBins = 512;    // top-p start search: one mass bin per 4 histogram bins
 constexpr int kLoadBatch = 8;     // list loads a merge thread keeps in flight
 constexpr uint32_t kNoList = 0xFFFFFFFFu;  // header count of a slice that published nothing
 
@@ -105,6 +106,9 @@ struct SplitSmem {
     stream::SampleSmem stream;   // streaming fallback
   } u;
   alignas(16) uint32_t hist[H1::kWords];
+  // fixed-point masses of the top-k entries above the boundary bin, per
+  // group of four histogram bins (+ per-lane dummy slots)
+  alignas(16) unsigned long long mh[kMassBins + kWave];
   double draws[stream::kPreDraws];
   uint32_t red[4][kWaves];        // per-wave partials of the block scans
   uint32_t wmax[kWaves];
@@ -214,7 +218,7 @@ __device__ void wave_find(const uint32_t* hist, uint32_t need, uint32_t& bin, ui
 // (the F4 note's threshold search on the bit pattern, §③); then every lane
 // takes one entry and counts the entries >= its own (an exact rank).
 // ---------------------------------------------------------------------------
-__device__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, uint32_t base, uint32_t sh,
+__device__ __forceinline__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, uint32_t base, uint32_t sh,
                              uint32_t need, uint32_t* hist, uint32_t* sel) {
   const int lane = lane_id();
   while (true) {
@@ -222,7 +226,8 @@ __device__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, uint32_t base, uin
     uint32_t cnt = 0u;
     for (uint32_t c0 = 0; c0 < n; c0 += kWave) {
       const uint32_t c = c0 + lane;
-      const uint32_t x = c < n ? (uint32_t)bnd[c] : 0u;
+      uint32_t x = (uint32_t)bnd[min(c, n - 1u)];  // unconditional read, n >= 1 here
+      asm volatile("" : "+v"(x));
       const bool in = c < n && x - base < (1u << sh) && x >= base;
       const uint64_t m = __ballot(in);
       const uint32_t p = cnt + rank_in(m);
@@ -231,9 +236,11 @@ __device__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, uint32_t base, uin
     }
     if (cnt <= (uint32_t)kWave || sh == 0u) {
       if (sh == 0u) return base;  // one bit pattern left: every entry in range equals it
+      // lane j holds the j-th entry in range; each lane counts the entries
+      // >= its own, the other lanes' values read as scalars
       const uint32_t x = lane < (int)cnt ? sel[lane] : 0u;
       uint32_t ge = 0u;
-      for (uint32_t j = 0; j < cnt; ++j) ge += (uint32_t)(sel[j] >= x);
+      for (uint32_t j = 0; j < cnt; ++j) ge += (uint32_t)(lane_value(x, (int)j) >= x);
       const uint32_t cand = (lane < (int)cnt && ge >= need) ? x : 0u;
       return wave_max(cand);
     }
@@ -255,11 +262,13 @@ __device__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, uint32_t base, uin
 // The dual-pivot loop on one wave (no barriers).  cand[0..m) holds every
 // value of the row above `low` and nothing at or below it, each > 0; their
 // mass is the kept mass Z_k, and the top-p bound is pfrac * Z_k.  Lane l
-// owns the contiguous entries [l*E, l*E + E), held in NR registers as
-// float64 (NR >= E; NR = 0: read from LDS), and the inverse-transform draw
-// runs over the entries in that order (blog, 逆变换采样).  Guards as in the
-// streaming engine (blog, 实现细节): only entries with nonzero mass are
-// chosen, the first hit wins, and if rounding puts the target at or past
+// owns the entries l, l + 64, l + 128, ... (NR of them in registers as
+// float64, or E = ceil(m / 64) read from LDS when NR = 0), so every LDS read
+// of the entries is one conflict-free row.  The inverse-transform draw
+// (blog, 逆变换采样) runs over lane 0's entries, then lane 1's, and so on: a
+// fixed order of the candidates, which is all the method needs.  Guards as
+// in the streaming engine (blog, 实现细节): only entries with nonzero mass
+// are chosen, the first hit wins, and if rounding puts the target at or past
 // every running sum the last entry is taken.
 //
 // Every pivot is one of the entries, so it is >= tau_k and fewer than k
@@ -267,71 +276,130 @@ __device__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, uint32_t base, uin
 // top-k-then-top-p reduces to "the mass above t is below p * Z_k" (or no
 // value is above t).
 // ---------------------------------------------------------------------------
+// x (float32 bits b, x >= 0, finite, at most the value with exponent field
+// eg) in units of 2^(eg - 176), rounded down: mant * 2^(e + 26 - eg) for a
+// normal x, which is below 2^50, so 4096 of them sum below 2^62.  The
+// integer sums are exact and independent of the order of the additions.
+__device__ __forceinline__ unsigned long long fixed_mass(uint32_t b, uint32_t eg) {
+  const uint32_t e = b >> 23;
+  const unsigned long long mant = (unsigned long long)((b & 0x7FFFFFu) | 0x800000u);
+  const int d = (int)e + 26 - (int)eg;
+  const unsigned long long up = mant << (uint32_t)max(d, 0);
+  const unsigned long long dn = mant >> (uint32_t)min(-d, 63);
+  return e == 0u ? 0ull : d >= 0 ? up : dn;
+}
+
+// A starting pivot for the dual-pivot loop above tau_k: the largest key L
+// below one of the mass bins such that the top-k mass above L provably
+// reaches pfrac * Z_k, so that f(L) is false and no value at or below L can
+// be kept (the blog's proof then holds from L).  The mass histogram holds
+// lower bounds of the above-bin masses (fixed_mass, unit 2^(eg - 176)); Z_k
+// is bounded above by those sums plus one unit per entry plus zb, the mass
+// of the boundary entries kept; the test carries a 1e-9 relative margin,
+// far above every rounding error of the float64 sums here and in the loop.
+// Returns 0 when no bin qualifies.  One wave.
+__device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_above, double zb,
+                                                uint32_t eg, float pfrac, uint32_t tstar,
+                                                uint32_t sh) {
+  constexpr int kPer = kMassBins / kWave;  // bins per lane, the top ones in lane 0
+  const int lane = lane_id();
+  const int c = kWave - 1 - lane;
+  unsigned long long t = 0ull;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) t += sm.mh[c * kPer + q];
+  const double unit = __longlong_as_double((long long)((unsigned long long)(eg + 1023u - 176u) << 52));
+  const double sd = (double)t * unit;
+  const double incl = wave_incl_scan(sd);
+  const double excl = wave_excl_from_incl(incl);
+  const double zhi = lane63(incl) * (1.0 + 1e-12) + (double)n_above * unit + zb;
+  const double target = (double)pfrac * zhi * (1.0 + 1e-9);
+  const uint64_t m = __ballot(incl > 0.0 && incl * (1.0 - 1e-12) >= target);
+  if (m == 0ull) return 0u;
+  const int l1 = first_lane(m);
+  const int c1 = kWave - 1 - l1;
+  const double h = lane < kPer ? (double)sm.mh[c1 * kPer + kPer - 1 - lane] * unit : 0.0;
+  const double incl2 = lane_value(excl, l1) + wave_incl_scan(h);
+  const uint64_t m2 = __ballot(lane < kPer && incl2 > 0.0 && incl2 * (1.0 - 1e-12) >= target);
+  if (m2 == 0ull) return 0u;
+  const uint32_t b = (uint32_t)(c1 * kPer + kPer - 1 - first_lane(m2));
+  const uint32_t edge = tstar + ((b << 2) << sh);
+  return edge > 0u ? edge - 1u : 0u;
+}
+
 template <int OP, int NR>
-__device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, float pfrac,
-                         uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
+__device__ int wave_loop(const SplitSmem& sm, int m, float low, float start, float high,
+                         float pfrac, uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
   constexpr bool REG = NR > 0;
   const int lane = lane_id();
-  const int E = (m + kWave - 1) / kWave;
-  const int c0 = min(m, lane * E), c1 = min(m, c0 + E);
+  const int E = (m + kWave - 1) / kWave;  // entries of the busiest lane (<= 64)
   const uint64_t* cand = sm.u.b.cand;
+  if (m <= 0) {  // no value above low (callers never pass this)
+    rounds = 0;
+    return -1;
+  }
+  // x of entry c, 0 past the end (never above a pivot).  The read is
+  // clamped and pinned by an empty asm so that the compiler cannot sink it
+  // into a branch: all reads go out together and one wait covers them.
+  auto ld = [&](int c) -> double {
+    uint32_t b = (uint32_t)cand[min(c, m - 1)];
+    asm volatile("" : "+v"(b));
+    return c < m ? (double)__uint_as_float(b) : 0.0;
+  };
   double xr[REG ? NR : 1];
   if (REG) {
 #pragma unroll
-    for (int j = 0; j < NR; ++j)
-      xr[j] = c0 + j < c1 ? (double)__uint_as_float((uint32_t)cand[c0 + j]) : 0.0;
+    for (int j = 0; j < NR; ++j) xr[j] = ld(lane + kWave * j);
   }
-  // x of this lane's j-th entry (0 past the end: never above a pivot)
-  auto X = [&](int j) -> double {
-    if (REG) return xr[j];
-    return c0 + j < c1 ? (double)__uint_as_float((uint32_t)cand[c0 + j]) : 0.0;
-  };
-  const int n = REG ? NR : E;
-
-  double lo = (double)low;
-  double part = 0.0;  // mass above low of this lane's entries
+  // f(x) for each of this lane's entries
+  auto each = [&](auto&& f) {
+    if constexpr (REG) {
 #pragma unroll
-  for (int j = 0; j < n; ++j) {
-    const double x = X(j);
+      for (int j = 0; j < NR; ++j) f(xr[j]);
+    } else {
+      for (int j = 0; j < E; ++j) f(ld(lane + kWave * j));
+    }
+  };
+
+  // Z_k: the mass above low (every entry); the loop starts at `start`
+  // (>= low), which leaves every value that top-p can keep above it
+  const double lk = (double)low;
+  double lo = (double)start;
+  double zk = 0.0, part = 0.0;  // this lane's mass above low, above lo
+  each([&](double x) {
+    zk += x > lk ? x : 0.0;
     part += x > lo ? x : 0.0;
-  }
-  double S = wave_sum(part);  // mass above low: the kept mass Z_k at the start
-  const double pz = (double)pfrac * S;
+  });
+  const double pz = (double)pfrac * wave_sum(zk);
+  double incl = wave_incl_scan(part);  // prefix over lanes of the mass above lo
+  double S = lane63(incl);
   int rnd = 0;
   while (true) {
     const double u = rnd < stream::kPreDraws ? sm.draws[rnd]
                                              : draw_uniform(seed, offset, sid, (uint32_t)rnd);
     ++rnd;
     const double T = u * S;
-    const double incl = wave_incl_scan(part);
     const double excl = wave_excl_from_incl(incl);
-    const uint64_t hit = __ballot(part > 0.0 && incl > T);
     const uint64_t nz = __ballot(part > 0.0);
     if (nz == 0ull) {
       rounds = rnd;
       return -1;
     }
+    const uint64_t hit = __ballot(part > 0.0 && incl > T);
     const int owner = hit ? first_lane(hit) : last_lane(nz);
-    // The owner walks its own entries: the first running sum past T, else
-    // its last entry above low.
-    int pick = 0;
-    if (lane == owner) {
-      double run = excl;
-      int last = -1, found = -1;
-#pragma unroll
-      for (int j = 0; j < n; ++j) {
-        const double x = X(j);
-        if (x > lo) {
-          run += x;
-          last = j;
-          if (found < 0 && hit != 0ull && run > T) found = j;
-        }
-      }
-      pick = found >= 0 ? found : last;
-    }
+    // The owner's entries, its j-th in lane j, and their running sums from
+    // the owner's exclusive prefix: the first past T, else the last entry
+    // above low.
+    const int c = owner + kWave * lane;
+    const bool mine = lane < E && c < m;
+    const uint64_t oe = cand[mine ? c : m - 1];
+    const double ox = (double)__uint_as_float((uint32_t)oe);
+    const double xm = (mine && ox > lo) ? ox : 0.0;
+    const double run = lane_value(excl, owner) + wave_incl_scan(xm);
+    const uint64_t nz2 = __ballot(xm > 0.0);
+    const uint64_t h2 = hit ? __ballot(xm > 0.0 && run > T) : 0ull;
     // part > 0 guarantees the owner an entry; the clamp keeps reads in bounds regardless
-    const int e = min(max(__builtin_amdgcn_readlane(c0 + pick, owner), 0), m - 1);
-    const uint64_t ent = cand[e];
+    const int pl = h2 ? first_lane(h2) : nz2 ? last_lane(nz2) : 0;
+    const uint64_t ent = lane_value(oe, pl);
     if (OP == kOpTopK) {
       rounds = rnd;
       return (int)(ent >> 32);
@@ -340,13 +408,12 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, floa
     const float pivot2 = (float)(((double)pivot1 + (double)high) * 0.5);
     const double p1 = (double)pivot1, p2 = (double)pivot2;
     double m0 = 0.0, m1 = 0.0;
-#pragma unroll
-    for (int j = 0; j < n; ++j) {
-      const double x = X(j);
+    each([&](double x) {
       m0 += x > p1 ? x : 0.0;
       m1 += x > p2 ? x : 0.0;
-    }
-    const double M0 = wave_sum(m0), M1 = wave_sum(m1);
+    });
+    const double i0 = wave_incl_scan(m0), i1 = wave_incl_scan(m1);
+    const double M0 = lane63(i0), M1 = lane63(i1);
     if (M0 < pz || M0 == 0.0) {  // f(pivot1) = 1: accept
       rounds = rnd;
       return (int)(ent >> 32);
@@ -356,10 +423,12 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float high, floa
       high = pivot2;
       S = M0;
       part = m0;
+      incl = i0;
     } else {
       lo = p2;
       S = M1;
       part = m1;
+      incl = i1;
     }
     if (rnd >= stream::kMaxRounds) {
       rounds = rnd;
@@ -384,6 +453,9 @@ template <int KIND, int OP, int NV>
 __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitParams& S,
                                            SplitSmem& sm, int& out_i) {
   constexpr bool KEYS = KIND == kKindMask;    // logits: signed-order keys
+  // top-k-then-top-p sampling keeps a mass histogram for the loop's start
+  constexpr bool kMass = KIND == kKindSample && OP == kOpTopKTopP;
+  static_assert(kMassBins + kWave <= kBlock, "one clearing store per thread");
   constexpr uint32_t kSh = KEYS ? 21u : 20u;  // top eleven bits of a key
   const int W = S.W;
   const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
@@ -557,7 +629,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
     if (!publish) return kFallback;
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
-    __syncthreads();  // histogram clear
+    if (kMass && tid < kMassBins + kWave) sm.mh[tid] = 0ull;
+    __syncthreads();  // histogram clears
     tstar = bnd;
     gmax = smax;
     ntot = nlist;
@@ -647,6 +720,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       }
     }
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
+    if (kMass && tid < kMassBins + kWave) sm.mh[tid] = 0ull;
     __syncthreads();
     const uint32_t status = sm.res[5];
     if (status == 1u) {
@@ -771,8 +845,15 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
         const bool some = kq[q] != 0xFFFFFFFFu;
         const bool ta = some && (all_kept || kq[q] > hi_cut);
         const bool tb = some && !all_kept && kq[q] == bin1;
-        sm.u.b.cand[ta ? pa : (uint32_t)(kKeptMax + lane)] = en[q];
-        sm.u.b.bnd[tb ? pb : (uint32_t)(kBndMax + lane)] = en[q];
+        // one store per entry: into cand, into bnd, or a dummy slot
+        uint64_t* const dst = ta   ? sm.u.b.cand + pa
+                              : tb ? sm.u.b.bnd + pb
+                                   : sm.u.b.cand + (kKeptMax + lane);
+        *dst = en[q];
+        if (kMass) {
+          const uint32_t mb = ta ? kq[q] >> 2 : (uint32_t)(kMassBins + lane);
+          atomicAdd(&sm.mh[mb], ta ? fixed_mass((uint32_t)en[q], gmax >> 23) : 0ull);
+        }
         pa += ta ? 1u : 0u;
         pb += tb ? 1u : 0u;
       }
@@ -784,6 +865,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // ---- wave 0 from here on: tau_k inside bin1, the top-k list, the loop -----
   uint32_t m = n_above;
   uint32_t tau_k = 0u;
+  double zb = 0.0;  // mass of the boundary entries kept (per lane, then summed)
   if (!all_kept) {
     tau_k = wave_kth(sm.u.b.bnd, n_bnd, tstar + (bin1 << sh), sh, (uint32_t)k - above1, sm.hist,
                      sm.sel);
@@ -796,6 +878,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       const uint32_t p = m + rank_in(tm);
       if (take) sm.u.b.cand[p] = en;  // p < n_above + n_bnd <= kKeptMax
       m += (uint32_t)__popcll(tm);
+      zb += take ? (double)__uint_as_float((uint32_t)en) : 0.0;
     }
   }
 
@@ -817,18 +900,24 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 
   // ---- the dual-pivot loop on wave 0 ----------------------------------------
   const float pfrac = OP == kOpTopKTopP ? stream::clamp01(pp) : 0.0f;
-  const float low = tau_k > 0u ? __uint_as_float(tau_k - 1u) : 0.0f;
+  const uint32_t lowk = tau_k > 0u ? tau_k - 1u : 0u;
+  uint32_t startk = lowk;
+  if (kMass) {
+    const uint32_t L = top_p_start(sm, n_above, wave_sum(zb), gmax >> 23, pfrac, tstar, sh);
+    startk = max(startk, L);
+  }
+  const float low = __uint_as_float(lowk), start = __uint_as_float(startk);
   int rounds = 0;
   const float high = __uint_as_float(gmax);
   int e;
   if (m <= 4 * kWave) {
-    e = wave_loop<OP, 4>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 4>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
   } else if (m <= 8 * kWave) {
-    e = wave_loop<OP, 8>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 8>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
   } else if (m <= 16 * kWave) {
-    e = wave_loop<OP, 16>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 16>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
   } else {  // (32 float64 entries per lane in registers would spill the kernel)
-    e = wave_loop<OP, 0>(sm, (int)m, low, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 0>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
   }
   if (lane == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
   return kDone;

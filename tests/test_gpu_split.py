@@ -85,6 +85,36 @@ def test_split_chi_square_across_calls_w16(op):
         assert pval > 1e-3, (op, row, pval, tvd)
 
 
+# 4 rows: 16 slices per row; 64 rows: 4 slices, so that large k stays on the
+# split path (16 lists of at least k entries would overflow the merge)
+@pytest.mark.parametrize("rows,k,p", [(4, 300, 0.95), (4, 50, 0.0), (64, 1000, 0.6),
+                                      (64, 2048, 0.3), (64, 700, 0.0), (64, 1024, 0.95)])
+def test_split_chi_square_top_p_start(rows, k, p):
+    """Top-p cuts far above tau_k: the loop starts from a pivot taken from the
+    merge's mass histogram, which must never exclude a kept token."""
+    probs = si.small()["probs"] if rows == 4 else si.renorm(rows=rows, vocab=32000)["probs"]
+    V = probs.shape[1]
+    calls = 4000
+    P = gpu(probs)
+    seeds = u64(np.arange(11, 11 + rows, dtype=np.uint64))
+    out = torch.empty(calls, rows, dtype=torch.int32, device="cuda:0")
+    rounds = torch.empty(calls, rows, dtype=torch.int32, device="cuda:0")
+    for t in range(calls):
+        out[t], _, rounds[t] = dss.top_k_top_p_sampling_from_probs(
+            P, k, np.float32(p), seed=seeds, offset=t, return_valid=True, return_rounds=True)
+    s, r = host(out), host(rounds)
+    assert (r >= 1).all()
+    for row in range(4):
+        _, tau = ref.threshold(probs[row], "top_k_top_p", k=k, p=np.float32(p))
+        support = ref.support_mask(probs[row], tau)
+        assert support[s[:, row]].all(), (k, p, row)
+        counts = np.bincount(s[:, row], minlength=V)
+        if support.sum() > 1:
+            pval, tvd, _ = pooled_chi_square(counts[support],
+                                             ref.target_distribution(probs[row], tau)[support])
+            assert pval > 1e-3, (k, p, row, pval, tvd)
+
+
 def test_split_adversarial_rows():
     """Flat rows overflow the candidate buffers (streaming fallback); sorted
     rows put the whole top-k in one slice; ties sit at the local bounds."""
