@@ -338,12 +338,11 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float start, flo
     return -1;
   }
   // x of entry c, 0 past the end (never above a pivot).  The read is
-  // clamped and pinned by an empty asm so that the compiler cannot sink it
-  // into a branch: all reads go out together and one wait covers them.
+  // clamped and its bits masked rather than selected, so that the compiler
+  // keeps it unconditional: all reads go out together under one wait.
   auto ld = [&](int c) -> double {
-    uint32_t b = (uint32_t)cand[min(c, m - 1)];
-    asm volatile("" : "+v"(b));
-    return c < m ? (double)__uint_as_float(b) : 0.0;
+    const uint32_t b = (uint32_t)cand[min(c, m - 1)];
+    return (double)__uint_as_float(b & (c < m ? 0xFFFFFFFFu : 0u));
   };
   double xr[REG ? NR : 1];
   if (REG) {
