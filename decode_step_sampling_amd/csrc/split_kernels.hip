@@ -669,32 +669,35 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     const int sl = tid >> (10 - S.wlog);
     const int lt = tid & (gsz - 1);
     const gptr<uint64_t> lst = as_global(S.list + ((int64_t)li * W + sl) * kListMax);
-    // positions [0, spec) of every list are loaded now (spec <= one batch)
+    // positions [0, spec) of every list are loaded now (spec <= one batch).
+    // Wave 0's header reads go out first (a wave's loads return in order),
+    // then every thread's list reads.  All reads are unconditional, at
+    // clamped addresses, so that they leave back to back and no wait for
+    // one of them sits inside a branch; what they return is masked later.
     const uint32_t spec = min((uint32_t)(kLoadBatch * gsz), 2u * (publish ? nlist : 0u) + 128u);
+    const bool mine = wave == 0 && lane < W;
+    uint32_t ht = 0u, hc = 0u, hm = 0u, hg = 0u, hx = 0u, hb = 0u;
+    if (wave == 0) {
+      const gptr<uint32_t> h =
+          as_global(S.hdr + ((int64_t)li * W + (lane & (W - 1))) * kHdrWords);
+      ht = __hip_atomic_load(h + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hc = __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hm = __hip_atomic_load(h + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hb = __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     uint64_t e8[kLoadBatch];
 #pragma unroll
-    for (int q = 0; q < kLoadBatch; ++q) {
-      const uint32_t pos = (uint32_t)(lt + q * gsz);
-      e8[q] = pos < spec ? __hip_atomic_load(lst + pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : 0ull;
-    }
+    for (int q = 0; q < kLoadBatch; ++q)
+      e8[q] = __hip_atomic_load(lst + min((uint32_t)(lt + q * gsz), spec - 1u), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
     if (wave == 0) {
       const uint32_t me = xcc_id();
       const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
       if (lane == 0) {
         __hip_atomic_store(as_global(S.ctr + li), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      const bool mine = lane < W;
-      uint32_t ht = 0u, hc = 0u, hm = 0u, hg = mygen, hx = me, hb = 0u;
-      if (mine) {
-        const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + lane) * kHdrWords);
-        ht = __hip_atomic_load(h + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hc = __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hm = __hip_atomic_load(h + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hb = __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const bool anybad = __ballot(mine && hb != 0u) != 0ull;
       const bool foreign = __ballot(mine && (hg != mygen || hx != me)) != 0ull;
