@@ -483,9 +483,15 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 #pragma unroll
   for (int j = 0; j < NV; ++j) v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1));
 
+  // (read before any store of the kernel, so that they are scalar loads and
+  // no wait for them waits for the slice's vector loads)
   const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
   const float pp =
       (OP == kOpTopKTopP) ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
+  const uint64_t seed =
+      KIND != kKindSample ? 0ull : P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset =
+      KIND != kKindSample ? 0ull : P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const bool ok = row_ok && k > 0 && (OP != kOpTopKTopP || !isnan(pp));
   if (!ok || k > kSplitKCap) {
     // no hand-off for this output: slice 0 answers alone
@@ -500,10 +506,6 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // while the slice is in flight: clear the histogram; wave 0 reads the
   // row's generation and computes the first 256 draws of the output's stream
   clear_hist<kHistBins>(sm.hist, tid, kBlock);
-  const uint64_t seed =
-      KIND != kKindSample ? 0ull : P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
-  const uint64_t offset =
-      KIND != kKindSample ? 0ull : P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
   uint32_t gen = 0u;
   if (wave == 0) {
