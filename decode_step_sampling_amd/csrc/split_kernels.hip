@@ -41,7 +41,8 @@ namespace dss {
 namespace {
 
 constexpr int kHistBins = 2048;
-constexpr int kStageMax = 2048;   // vectors a slice stages in LDS
+constexpr int kStageMax = 3072;   // vectors a slice stages in LDS
+constexpr int kRegion = kStageMax / 16;  // staging region of one wave (provisional bound)
 constexpr int kListMax = 4096;    // entries a slice publishes
 constexpr int kRowCandMax = 8192; // entries of all slices of a row (the merge's LDS copy)
 constexpr int kKeptMax = 4096;    // entries of the top-k set (ties included)
@@ -117,6 +118,8 @@ struct SplitSmem {
   uint32_t sel[kWave];
   uint32_t res[8];
   uint32_t fres[4];
+  uint32_t tp;                    // provisional slice bound
+  uint32_t wcnt[kWaves];          // vectors each wave staged (0xFFFFFFFF: overflow)
   int flag;
 };
 static_assert(sizeof(SplitSmem) <= 160 * 1024, "LDS budget of one gfx950 work-group");
@@ -522,16 +525,25 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // As each vector lands: its maximum (float32 bits) counted in the
   // histogram of bits [30:20] (bin 2047 also takes the patterns with the sign
   // bit set), and its staging key, the maximum + 1, or 0 for a thread past
-  // the end.  Everything below is branch-free per lane (selects, and stores
-  // to dummy slots), because every divergent branch costs scalar
-  // instructions and one scalar unit serves all waves of a CU: a lane past
-  // the end counts into a padding word of the histogram that no search reads.
+  // the end.  A lane past the end counts into a padding word of the
+  // histogram that no search reads.
+  //
+  // The first J0 slots of every thread (about 30% of the slice) are a
+  // sample: once they are counted, wave 0 takes from the histogram a
+  // provisional bound tp, the edge of the bin holding the r-th largest
+  // sample maximum, r well above the sample's expected share of k.  From then
+  // on every vector with a value >= tp is staged in LDS as it lands, in its
+  // wave's region at a position taken from ballots, so that the staging
+  // stores fall inside the landing window.  After the last vector, if
+  // tp <= bnd and no region overflowed, the staged vectors include every
+  // vector with a value >= bnd; otherwise the slice stages again from its
+  // registers with bnd itself (the general path).
+  constexpr int J0 = NV >= 4 ? (3 * NV + 5) / 10 : 0;
   const uint32_t pad = (uint32_t)lane * H1::kStride + H1::kChunk;
   uint32_t key[NV];
   uint32_t mx = 0u;
   bool nan_seen = false;  // logits: a NaN invalidates the row
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
+  auto count = [&](int j) {
     const bool in = tid + j * kBlock < nvec;
     const uint32_t m = max4_key<KEYS>(v[j]);
     key[j] = in ? m + 1u : 0u;
@@ -539,9 +551,51 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     atomicAdd(&sm.hist[in ? H1::at(min(m >> kSh, (uint32_t)(kHistBins - 1))) : pad], 1u);
     if (KEYS)
       nan_seen = nan_seen || (in && (isnan(v[j].x) || isnan(v[j].y) || isnan(v[j].z) || isnan(v[j].w)));
+  };
+  uint32_t tp = 0xFFFFFFFFu;
+  uint32_t wp = 0u;  // vectors this wave has staged (wave-uniform)
+  bool wovf = false;
+  auto stage = [&](int j) {
+    const bool hit = key[j] > tp;
+    const uint64_t hm = __ballot(hit);
+    const uint32_t c = (uint32_t)__popcll(hm);
+    if (wp + c <= (uint32_t)kRegion) {
+      if (hit) {
+        const uint32_t slot = (uint32_t)(wave * kRegion) + wp + rank_in(hm);
+        sm.u.a.vec[slot] = v[j];
+        sm.u.a.vidx[slot] = (uint32_t)(tid + j * kBlock);
+      }
+    } else {
+      wovf = true;
+    }
+    wp += c;
+  };
+#pragma unroll
+  for (int j = 0; j < J0; ++j) count(j);
+  if (J0 > 0) {
+    __syncthreads();
+    if (wave == 0) {
+      const float fk = (float)k * ((float)J0 / (float)NV);
+      const uint32_t r = (uint32_t)(fk + 3.0f * __builtin_sqrtf(fk) + 2.0f);
+      uint32_t bin, above, total;
+      wave_find<kHistBins>(sm.hist, r, bin, above, total);
+      if (lane == 0) sm.tp = total < r ? 0u : bin << kSh;
+    }
+    __syncthreads();
+    tp = sm.tp;
+#pragma unroll
+    for (int j = 0; j < J0; ++j) stage(j);
+  }
+#pragma unroll
+  for (int j = J0; j < NV; ++j) {
+    count(j);
+    if (J0 > 0) stage(j);
   }
   mx = wave_max(mx);
-  if (lane == 0) sm.wmax[wave] = mx;
+  if (lane == 0) {
+    sm.wmax[wave] = mx;
+    sm.wcnt[wave] = wovf ? 0xFFFFFFFFu : wp;
+  }
   if (KEYS) {
     const bool wn = __ballot(nan_seen) != 0ull;
     if (lane == 0) sm.wnan[wave] = wn ? 1u : 0u;
@@ -552,10 +606,13 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     wave_find<kHistBins>(sm.hist, (uint32_t)k, bin, above, total);
     const uint32_t smax = wave_max(lane < kWaves ? sm.wmax[lane] : 0u);
     const bool anynan = KEYS && __ballot(lane < kWaves && sm.wnan[lane] != 0u) != 0ull;
+    const uint32_t bnd = total < (uint32_t)k ? 0u : bin << kSh;  // fewer than k vectors: all of it
+    const bool ovf = __ballot(lane < kWaves && sm.wcnt[lane] == 0xFFFFFFFFu) != 0ull;
     if (lane == 0) {
-      sm.res[0] = total < (uint32_t)k ? 0u : bin << kSh;  // fewer than k vectors: all of it
+      sm.res[0] = bnd;
       sm.res[1] = smax;
       sm.res[2] = anynan ? 1u : 0u;
+      sm.res[3] = (J0 > 0 && tp <= bnd && !ovf) ? 1u : 0u;
     }
   }
   __syncthreads();
@@ -563,40 +620,55 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const uint32_t smax = sm.res[1];
   // probabilities: a sign bit, an inf or a NaN somewhere; logits: a NaN
   const bool bad = KEYS ? sm.res[2] != 0u : smax >= 0x7F800000u;
+  const bool fast = sm.res[3] != 0u;
 
-  // the vectors with a value >= bnd (key > bnd), staged in thread order
-  uint32_t nv_hit = 0u;
+  // The general path: the vectors with a value >= bnd (key > bnd), staged
+  // in thread order, branch-free (stores to per-lane dummy slots).
+  uint32_t nstage = 0u;
+  bool stage_ok = !bad;
+  if (!fast) {
+    uint32_t nv_hit = 0u;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) nv_hit += key[j] > bnd ? 1u : 0u;
-  uint32_t nstage;
-  uint32_t pos = block_excl_scan(nv_hit, nstage, sm.red[0]);
-  const bool stage_ok = !bad && nstage <= (uint32_t)kStageMax;
-  if (stage_ok) {
+    for (int j = 0; j < NV; ++j) nv_hit += key[j] > bnd ? 1u : 0u;
+    uint32_t pos = block_excl_scan(nv_hit, nstage, sm.red[0]);
+    stage_ok = !bad && nstage <= (uint32_t)kStageMax;
+    if (stage_ok) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const bool hit = key[j] > bnd;
-      const uint32_t slot = hit ? pos : (uint32_t)(kStageMax + lane);
-      sm.u.a.vec[slot] = v[j];
-      sm.u.a.vidx[slot] = (uint32_t)(tid + j * kBlock);
-      pos += hit ? 1u : 0u;
+      for (int j = 0; j < NV; ++j) {
+        const bool hit = key[j] > bnd;
+        const uint32_t slot = hit ? pos : (uint32_t)(kStageMax + lane);
+        sm.u.a.vec[slot] = v[j];
+        sm.u.a.vidx[slot] = (uint32_t)(tid + j * kBlock);
+        pos += hit ? 1u : 0u;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // their positive elements >= bnd, in staging order, as (key | index << 32),
-  // into full[] (the row's list when W == 1, a staging copy otherwise)
+  // The staged vectors' positive elements >= bnd as (key | index << 32) into
+  // full[] (the row's list when W == 1, a staging copy otherwise), in
+  // (thread, slot, element) order.  Slot q of a thread is the q-th vector of
+  // its wave's region (provisional bound) or staged vector tid + q * 1024.
   const uint32_t bthr = max(bnd, 1u);
   constexpr int kSt = kStageMax / kBlock;
+  static_assert(kSt == kRegion / kWave, "three staging slots per thread either way");
   uint32_t xb[kSt][4];
   uint32_t sidx[kSt];
   uint32_t ne = 0u;
 #pragma unroll
   for (int q = 0; q < kSt; ++q) {
-    const uint32_t g = (uint32_t)(tid + q * kBlock);
-    const bool live = stage_ok && g < nstage;
-    const uint32_t gg = live ? g : (uint32_t)(kStageMax + lane);
-    const float4 x = sm.u.a.vec[gg];
-    sidx[q] = sm.u.a.vidx[gg];
+    const uint32_t first = fast ? (uint32_t)(q * kWave) : (uint32_t)(q * kBlock);
+    const uint32_t n = fast ? wp : nstage;
+    xb[q][0] = xb[q][1] = xb[q][2] = xb[q][3] = 0u;
+    sidx[q] = 0u;
+    if (!stage_ok || first >= n) continue;  // wave-uniform
+    const uint32_t g = fast ? (uint32_t)(lane + q * kWave) : (uint32_t)(tid + q * kBlock);
+    const bool live = g < n;
+    const uint32_t slot = !live ? (uint32_t)(kStageMax + lane)
+                          : fast ? (uint32_t)(wave * kRegion) + g
+                                 : g;
+    const float4 x = sm.u.a.vec[slot];
+    sidx[q] = sm.u.a.vidx[slot];
     xb[q][0] = live ? key_of<KEYS>(x.x) : 0u;
     xb[q][1] = live ? key_of<KEYS>(x.y) : 0u;
     xb[q][2] = live ? key_of<KEYS>(x.z) : 0u;
@@ -610,6 +682,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   if (publish) {
 #pragma unroll
     for (int q = 0; q < kSt; ++q) {
+      const uint32_t first = fast ? (uint32_t)(q * kWave) : (uint32_t)(q * kBlock);
+      if (first >= (fast ? wp : nstage)) continue;  // wave-uniform
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool take = xb[q][e] >= bthr;
