@@ -52,6 +52,7 @@ constexpr int kMaxSlices = 16;    // a power of two
 constexpr int kHdrWords = 8;
 constexpr int kMassBins = 512;    // top-p start search: one mass bin per 4 histogram bins
 constexpr int kLoadBatch = 8;     // list loads a merge thread keeps in flight
+constexpr int kDepth = 5;         // slice loads a thread keeps in flight
 constexpr uint32_t kNoList = 0xFFFFFFFFu;  // header count of a slice that published nothing
 
 struct SplitParams {
@@ -482,9 +483,15 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const int nvec = (s1 - s0) / 4;
   const gptr<const float4> src = as_global(
       reinterpret_cast<const float4*>(P.probs + (int64_t)(row_ok ? row : 0) * V + s0));
+  // Only kInFlight loads per thread go out now; each later one leaves as an
+  // earlier vector is processed.  A wave stalls while the CU cannot accept
+  // another load, so issuing all of them at once would leave every wave
+  // stuck at its last load until most of the slice had landed.
+  constexpr int kInFlight = NV < kDepth ? NV : kDepth;
   float4 v[NV];
+  auto issue = [&](int j) { v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1)); };
 #pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1));
+  for (int j = 0; j < kInFlight; ++j) issue(j);
 
   // (read before any store of the kernel, so that they are scalar loads and
   // no wait for them waits for the slice's vector loads)
@@ -570,8 +577,18 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
     wp += c;
   };
+  auto next = [&](int j) {  // the load that takes slot j's place in flight
+    if (j + kInFlight < NV) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j + kInFlight);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 #pragma unroll
-  for (int j = 0; j < J0; ++j) count(j);
+  for (int j = 0; j < J0; ++j) {
+    count(j);
+    next(j);
+  }
   if (J0 > 0) {
     __syncthreads();
     if (wave == 0) {
@@ -589,6 +606,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 #pragma unroll
   for (int j = J0; j < NV; ++j) {
     count(j);
+    next(j);
     if (J0 > 0) stage(j);
   }
   mx = wave_max(mx);
