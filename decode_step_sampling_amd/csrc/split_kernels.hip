@@ -50,7 +50,8 @@ constexpr int kBndMax = 4096;     // entries in the boundary bin
 constexpr int kSplitKCap = 2048;
 constexpr int kMaxSlices = 16;    // a power of two
 constexpr int kHdrWords = 8;
-constexpr int kMassBins = 512;    // top-p start search: one mass bin per 4 histogram bins
+constexpr int kMassBins = 256;    // top-p start search: one mass bin per 8 histogram bins
+constexpr int kMassShift = 3;
 constexpr int kLoadBatch = 8;     // list loads a merge thread keeps in flight
 constexpr int kDepth = 5;         // slice loads a thread keeps in flight
 constexpr uint32_t kNoList = 0xFFFFFFFFu;  // header count of a slice that published nothing
@@ -109,7 +110,7 @@ struct SplitSmem {
   } u;
   alignas(16) uint32_t hist[H1::kWords];
   // fixed-point masses of the top-k entries above the boundary bin, per
-  // group of four histogram bins (+ per-lane dummy slots)
+  // group of eight histogram bins (+ per-lane dummy slots)
   alignas(16) unsigned long long mh[kMassBins + kWave];
   double draws[stream::kPreDraws];
   uint32_t red[4][kWaves];        // per-wave partials of the block scans
@@ -306,27 +307,33 @@ __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_
                                                 uint32_t eg, float pfrac, uint32_t tstar,
                                                 uint32_t sh) {
   constexpr int kPer = kMassBins / kWave;  // bins per lane, the top ones in lane 0
+  static_assert(kPer == 4, "two 16-byte reads per lane");
   const int lane = lane_id();
   const int c = kWave - 1 - lane;
-  unsigned long long t = 0ull;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) t += sm.mh[c * kPer + q];
+  // this lane's bins from the top down, and their running sums
+  const ulonglong2 lo = *reinterpret_cast<const ulonglong2*>(sm.mh + c * kPer);
+  const ulonglong2 hi = *reinterpret_cast<const ulonglong2*>(sm.mh + c * kPer + 2);
   const double unit = __longlong_as_double((long long)((unsigned long long)(eg + 1023u - 176u) << 52));
-  const double sd = (double)t * unit;
-  const double incl = wave_incl_scan(sd);
+  const double r0 = (double)hi.y * unit;
+  const double r1 = r0 + (double)hi.x * unit;
+  const double r2 = r1 + (double)lo.y * unit;
+  const double r3 = r2 + (double)lo.x * unit;
+  const double incl = wave_incl_scan(r3);
   const double excl = wave_excl_from_incl(incl);
   const double zhi = lane63(incl) * (1.0 + 1e-12) + (double)n_above * unit + zb;
   const double target = (double)pfrac * zhi * (1.0 + 1e-9);
-  const uint64_t m = __ballot(incl > 0.0 && incl * (1.0 - 1e-12) >= target);
+  // suffix mass down to each of this lane's bins; the first (highest) bin
+  // whose suffix provably reaches the target
+  auto ok = [&](double r) {
+    const double sfx = excl + r;
+    return sfx > 0.0 && sfx * (1.0 - 1e-12) >= target;
+  };
+  const int j = ok(r0) ? 0 : ok(r1) ? 1 : ok(r2) ? 2 : ok(r3) ? 3 : 4;
+  const uint64_t m = __ballot(j < 4);
   if (m == 0ull) return 0u;
   const int l1 = first_lane(m);
-  const int c1 = kWave - 1 - l1;
-  const double h = lane < kPer ? (double)sm.mh[c1 * kPer + kPer - 1 - lane] * unit : 0.0;
-  const double incl2 = lane_value(excl, l1) + wave_incl_scan(h);
-  const uint64_t m2 = __ballot(lane < kPer && incl2 > 0.0 && incl2 * (1.0 - 1e-12) >= target);
-  if (m2 == 0ull) return 0u;
-  const uint32_t b = (uint32_t)(c1 * kPer + kPer - 1 - first_lane(m2));
-  const uint32_t edge = tstar + ((b << 2) << sh);
+  const uint32_t b = (uint32_t)(kMassBins - 1 - (kPer * l1 + lane_value(j, l1)));
+  const uint32_t edge = tstar + ((b << kMassShift) << sh);
   return edge > 0u ? edge - 1u : 0u;
 }
 
@@ -947,8 +954,9 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
                                    : sm.u.b.cand + (kKeptMax + lane);
         *dst = en[q];
         if (kMass) {
-          const uint32_t mb = ta ? kq[q] >> 2 : (uint32_t)(kMassBins + lane);
-          atomicAdd(&sm.mh[mb], ta ? fixed_mass((uint32_t)en[q], gmax >> 23) : 0ull);
+          // (masked rather than selected, so that no branch forms around it)
+          const uint32_t mb = ta ? kq[q] >> kMassShift : (uint32_t)(kMassBins + lane);
+          atomicAdd(&sm.mh[mb], fixed_mass((uint32_t)en[q], gmax >> 23) & (ta ? ~0ull : 0ull));
         }
         pa += ta ? 1u : 0u;
         pb += tb ? 1u : 0u;
