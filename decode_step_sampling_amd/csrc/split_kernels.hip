@@ -842,6 +842,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     const uint32_t o_sl = sm.off[sl];
 #pragma unroll
     for (int q = 0; q < kLoadBatch; ++q) {
+      if ((uint32_t)(q * gsz) >= min(spec, nmax)) continue;  // wave-uniform
       const uint32_t pos = (uint32_t)(lt + q * gsz);
       sm.full[pos < n_sl && pos < spec ? o_sl + pos : (uint32_t)(kRowCandMax + lane)] = e8[q];
     }
@@ -865,9 +866,9 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 
   // From here on waves 0..7 (two per SIMD) hold the entries, slot q of
   // thread t being entry t + 512 q, all in registers; the other waves take
-  // part in the barriers only.  Slots are visited in groups of four behind
+  // part in the barriers only.  Slots are visited in pairs behind
   // one wave-uniform test, and everything inside is branch-free.
-  constexpr int kMw = 8, kMt = kMw * kWave, kSlots = kRowCandMax / kMt, kGrp = 4;
+  constexpr int kMw = 8, kMt = kMw * kWave, kSlots = kRowCandMax / kMt, kGrp = 2;
   const bool worker = wave < kMw;
   const uint32_t range = gmax - tstar;
   const uint32_t sh = range < (uint32_t)kHistBins ? 0u : 21u - (uint32_t)__clz((int)range);
