@@ -864,11 +864,10 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     __syncthreads();
   }
 
-  // From here on waves 0..7 (two per SIMD) hold the entries, slot q of
-  // thread t being entry t + 512 q, all in registers; the other waves take
-  // part in the barriers only.  Slots are visited in pairs behind
+  // From here on every thread holds entries, slot q of thread t being entry
+  // t + 1024 q, all in registers.  Slots are visited in pairs behind
   // one wave-uniform test, and everything inside is branch-free.
-  constexpr int kMw = 8, kMt = kMw * kWave, kSlots = kRowCandMax / kMt, kGrp = 2;
+  constexpr int kMw = 16, kMt = kMw * kWave, kSlots = kRowCandMax / kMt, kGrp = 2;
   const bool worker = wave < kMw;
   const uint32_t range = gmax - tstar;
   const uint32_t sh = range < (uint32_t)kHistBins ? 0u : 21u - (uint32_t)__clz((int)range);
