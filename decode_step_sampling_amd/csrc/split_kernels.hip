@@ -111,7 +111,7 @@ struct SplitSmem {
   alignas(16) uint32_t hist[H1::kWords];
   // fixed-point masses of the top-k entries above the boundary bin, per
   // group of eight histogram bins (+ per-lane dummy slots)
-  alignas(16) unsigned long long mh[kMassBins + kWave];
+  alignas(16) uint32_t mh[kMassBins + kWave];
   double draws[stream::kPreDraws];
   uint32_t red[4][kWaves];        // per-wave partials of the block scans
   uint32_t wmax[kWaves];
@@ -282,23 +282,20 @@ __device__ __forceinline__ uint32_t wave_kth(const uint64_t* bnd, uint32_t n, ui
 // value is above t).
 // ---------------------------------------------------------------------------
 // x (float32 bits b, x >= 0, finite, at most the value with exponent field
-// eg) in units of 2^(eg - 176), rounded down: mant * 2^(e + 26 - eg) for a
-// normal x, which is below 2^50, so 4096 of them sum below 2^62.  The
+// eg) in units of 2^(eg - 145), rounded down: mant >> (eg - e + 5) for a
+// normal x, which is below 2^19, so 4096 of them sum below 2^31.  The
 // integer sums are exact and independent of the order of the additions.
-__device__ __forceinline__ unsigned long long fixed_mass(uint32_t b, uint32_t eg) {
+__device__ __forceinline__ uint32_t fixed_mass(uint32_t b, uint32_t eg) {
   const uint32_t e = b >> 23;
-  const unsigned long long mant = (unsigned long long)((b & 0x7FFFFFu) | 0x800000u);
-  const int d = (int)e + 26 - (int)eg;
-  const unsigned long long up = mant << (uint32_t)max(d, 0);
-  const unsigned long long dn = mant >> (uint32_t)min(-d, 63);
-  return e == 0u ? 0ull : d >= 0 ? up : dn;
+  const uint32_t mant = (b & 0x7FFFFFu) | 0x800000u;
+  return e == 0u ? 0u : mant >> min(eg - e + 5u, 31u);
 }
 
 // A starting pivot for the dual-pivot loop above tau_k: the largest key L
 // below one of the mass bins such that the top-k mass above L provably
 // reaches pfrac * Z_k, so that f(L) is false and no value at or below L can
 // be kept (the blog's proof then holds from L).  The mass histogram holds
-// lower bounds of the above-bin masses (fixed_mass, unit 2^(eg - 176)); Z_k
+// lower bounds of the above-bin masses (fixed_mass, unit 2^(eg - 145)); Z_k
 // is bounded above by those sums plus one unit per entry plus zb, the mass
 // of the boundary entries kept; the test carries a 1e-9 relative margin,
 // far above every rounding error of the float64 sums here and in the loop.
@@ -307,17 +304,16 @@ __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_
                                                 uint32_t eg, float pfrac, uint32_t tstar,
                                                 uint32_t sh) {
   constexpr int kPer = kMassBins / kWave;  // bins per lane, the top ones in lane 0
-  static_assert(kPer == 4, "two 16-byte reads per lane");
+  static_assert(kPer == 4, "one 16-byte read per lane");
   const int lane = lane_id();
   const int c = kWave - 1 - lane;
   // this lane's bins from the top down, and their running sums
-  const ulonglong2 lo = *reinterpret_cast<const ulonglong2*>(sm.mh + c * kPer);
-  const ulonglong2 hi = *reinterpret_cast<const ulonglong2*>(sm.mh + c * kPer + 2);
-  const double unit = __longlong_as_double((long long)((unsigned long long)(eg + 1023u - 176u) << 52));
-  const double r0 = (double)hi.y * unit;
-  const double r1 = r0 + (double)hi.x * unit;
-  const double r2 = r1 + (double)lo.y * unit;
-  const double r3 = r2 + (double)lo.x * unit;
+  const uint4 mb = *reinterpret_cast<const uint4*>(sm.mh + c * kPer);
+  const double unit = __longlong_as_double((long long)((unsigned long long)(eg + 1023u - 145u) << 52));
+  const double r0 = (double)mb.w * unit;
+  const double r1 = r0 + (double)mb.z * unit;
+  const double r2 = r1 + (double)mb.y * unit;
+  const double r3 = r2 + (double)mb.x * unit;
   const double incl = wave_incl_scan(r3);
   const double excl = wave_excl_from_incl(incl);
   const double zhi = lane63(incl) * (1.0 + 1e-12) + (double)n_above * unit + zb;
@@ -729,7 +725,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
     if (!publish) return kFallback;
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
-    if (kMass && tid < kMassBins + kWave) sm.mh[tid] = 0ull;
+    if (kMass && tid < kMassBins + kWave) sm.mh[tid] = 0u;
     __syncthreads();  // histogram clears
     tstar = bnd;
     gmax = smax;
@@ -823,7 +819,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       }
     }
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
-    if (kMass && tid < kMassBins + kWave) sm.mh[tid] = 0ull;
+    if (kMass && tid < kMassBins + kWave) sm.mh[tid] = 0u;
     __syncthreads();
     const uint32_t status = sm.res[5];
     if (status == 1u) {
@@ -956,7 +952,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
         if (kMass) {
           // (masked rather than selected, so that no branch forms around it)
           const uint32_t mb = ta ? kq[q] >> kMassShift : (uint32_t)(kMassBins + lane);
-          atomicAdd(&sm.mh[mb], fixed_mass((uint32_t)en[q], gmax >> 23) & (ta ? ~0ull : 0ull));
+          atomicAdd(&sm.mh[mb], fixed_mass((uint32_t)en[q], gmax >> 23) & (ta ? ~0u : 0u));
         }
         pa += ta ? 1u : 0u;
         pb += tb ? 1u : 0u;
