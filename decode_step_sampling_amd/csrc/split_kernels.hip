@@ -300,9 +300,20 @@ __device__ __forceinline__ uint32_t fixed_mass(uint32_t b, uint32_t eg) {
 // of the boundary entries kept; the test carries a 1e-9 relative margin,
 // far above every rounding error of the float64 sums here and in the loop.
 // Returns 0 when no bin qualifies.  One wave.
+// What wave 0 keeps of the mass histogram for the loop: per lane, the
+// suffix mass above its bins (excl) and down to each of them (excl + r[j]),
+// lower bounds in float64 with a relative error below 1e-12; slack bounds
+// what the rounding down of every entry's mass can have lost.
+struct MassView {
+  double excl, r[4];
+  double slack;
+  uint32_t tstar, sh, mb1;  // bin geometry, and the mass bin of the boundary bin
+  bool on;
+};
+
 __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_above, double zb,
                                                 uint32_t eg, float pfrac, uint32_t tstar,
-                                                uint32_t sh) {
+                                                uint32_t sh, uint32_t bin1, MassView& mv) {
   constexpr int kPer = kMassBins / kWave;  // bins per lane, the top ones in lane 0
   static_assert(kPer == 4, "one 16-byte read per lane");
   const int lane = lane_id();
@@ -310,21 +321,26 @@ __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_
   // this lane's bins from the top down, and their running sums
   const uint4 mb = *reinterpret_cast<const uint4*>(sm.mh + c * kPer);
   const double unit = __longlong_as_double((long long)((unsigned long long)(eg + 1023u - 145u) << 52));
-  const double r0 = (double)mb.w * unit;
-  const double r1 = r0 + (double)mb.z * unit;
-  const double r2 = r1 + (double)mb.y * unit;
-  const double r3 = r2 + (double)mb.x * unit;
-  const double incl = wave_incl_scan(r3);
-  const double excl = wave_excl_from_incl(incl);
-  const double zhi = lane63(incl) * (1.0 + 1e-12) + (double)n_above * unit + zb;
+  mv.r[0] = (double)mb.w * unit;
+  mv.r[1] = mv.r[0] + (double)mb.z * unit;
+  mv.r[2] = mv.r[1] + (double)mb.y * unit;
+  mv.r[3] = mv.r[2] + (double)mb.x * unit;
+  const double incl = wave_incl_scan(mv.r[3]);
+  mv.excl = wave_excl_from_incl(incl);
+  mv.slack = (double)n_above * unit;
+  mv.tstar = tstar;
+  mv.sh = sh;
+  mv.mb1 = bin1 >> kMassShift;
+  mv.on = true;
+  const double zhi = lane63(incl) * (1.0 + 1e-12) + mv.slack + zb;
   const double target = (double)pfrac * zhi * (1.0 + 1e-9);
   // suffix mass down to each of this lane's bins; the first (highest) bin
   // whose suffix provably reaches the target
   auto ok = [&](double r) {
-    const double sfx = excl + r;
+    const double sfx = mv.excl + r;
     return sfx > 0.0 && sfx * (1.0 - 1e-12) >= target;
   };
-  const int j = ok(r0) ? 0 : ok(r1) ? 1 : ok(r2) ? 2 : ok(r3) ? 3 : 4;
+  const int j = ok(mv.r[0]) ? 0 : ok(mv.r[1]) ? 1 : ok(mv.r[2]) ? 2 : ok(mv.r[3]) ? 3 : 4;
   const uint64_t m = __ballot(j < 4);
   if (m == 0ull) return 0u;
   const int l1 = first_lane(m);
@@ -335,7 +351,8 @@ __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_
 
 template <int OP, int NR>
 __device__ int wave_loop(const SplitSmem& sm, int m, float low, float start, float high,
-                         float pfrac, uint64_t seed, uint64_t offset, uint64_t sid, int& rounds) {
+                         float pfrac, uint64_t seed, uint64_t offset, uint64_t sid,
+                         const MassView& mv, int& rounds) {
   constexpr bool REG = NR > 0;
   const int lane = lane_id();
   const int E = (m + kWave - 1) / kWave;  // entries of the busiest lane (<= 64)
@@ -409,6 +426,23 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float start, flo
     if (OP == kOpTopK) {
       rounds = rnd;
       return (int)(ent >> 32);
+    }
+    // When pivot1 lies in a mass bin above the boundary bin's, the mass of
+    // the bins from its own up bounds the mass above it from above; if that
+    // bound is already below p * Z_k, f(pivot1) holds and the exact sums
+    // would accept too, so the draw is accepted without them.
+    if (OP == kOpTopKTopP && mv.on) {
+      const uint32_t mb = (((uint32_t)ent - mv.tstar) >> mv.sh) >> kMassShift;  // wave-uniform
+      if (mb > mv.mb1 && mb < (uint32_t)kMassBins) {
+        const uint32_t d = (uint32_t)kMassBins - 1u - mb;
+        const uint32_t jj = d & 3u;
+        const double r = jj == 0u ? mv.r[0] : jj == 1u ? mv.r[1] : jj == 2u ? mv.r[2] : mv.r[3];
+        const double sfx = lane_value(mv.excl + r, (int)(d >> 2));
+        if ((sfx * (1.0 + 1e-12) + mv.slack) * (1.0 + 1e-9) < pz) {
+          rounds = rnd;
+          return (int)(ent >> 32);
+        }
+      }
     }
     const float pivot1 = __uint_as_float((uint32_t)ent);
     const float pivot2 = (float)(((double)pivot1 + (double)high) * 0.5);
@@ -1002,8 +1036,11 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const float pfrac = OP == kOpTopKTopP ? stream::clamp01(pp) : 0.0f;
   const uint32_t lowk = tau_k > 0u ? tau_k - 1u : 0u;
   uint32_t startk = lowk;
+  MassView mv;
+  mv.on = false;
   if (kMass) {
-    const uint32_t L = top_p_start(sm, n_above, wave_sum(zb), gmax >> 23, pfrac, tstar, sh);
+    const uint32_t L =
+        top_p_start(sm, n_above, wave_sum(zb), gmax >> 23, pfrac, tstar, sh, bin1, mv);
     startk = max(startk, L);
   }
   const float low = __uint_as_float(lowk), start = __uint_as_float(startk);
@@ -1011,13 +1048,13 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const float high = __uint_as_float(gmax);
   int e;
   if (m <= 4 * kWave) {
-    e = wave_loop<OP, 4>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 4>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
   } else if (m <= 8 * kWave) {
-    e = wave_loop<OP, 8>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 8>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
   } else if (m <= 16 * kWave) {
-    e = wave_loop<OP, 16>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 16>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
   } else {  // (32 float64 entries per lane in registers would spill the kernel)
-    e = wave_loop<OP, 0>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, rounds);
+    e = wave_loop<OP, 0>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
   }
   if (lane == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
   return kDone;
