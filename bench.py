@@ -110,6 +110,47 @@ def kernel_times(lib, fn, reps, warm=2):
     return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
 
 
+def reference_points(lib, bufs, steps):
+    """Context beside the headline, on the same cold rotating buffers: a plain
+    HIP streaming read of the batch (dss_stream_read_reference: one pass,
+    38.9 MB per step, five 16-byte loads in flight per thread) as the read
+    rate this GPU reaches at this size, and torch.sort of one batch (the sort
+    the sorting-free method avoids)."""
+    import torch
+    nb = len(bufs)
+    out = torch.zeros(1, dtype=torch.int32, device=bufs[0].device)
+    stream = torch.cuda.current_stream(bufs[0].device).cuda_stream
+    n = bufs[0].numel()
+
+    def read(i):
+        if lib.dss_stream_read_reference(bufs[i % nb].data_ptr(), n, out.data_ptr(), stream) != 0:
+            raise RuntimeError("stream read reference failed")
+
+    # kernel time through the dispatch-event hook, like the headline's kernel_us
+    # (back-to-back calls from Python would be launch-bound for a read this short)
+    cnt = [0]
+
+    def step():
+        read(cnt[0])
+        cnt[0] += 1
+
+    us = float(kernel_times(lib, step, steps, warm=10).mean())
+    nbytes = n * 4
+    for _ in range(3):
+        torch.sort(bufs[0], dim=-1, descending=True)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(10):
+        torch.sort(bufs[i % nb], dim=-1, descending=True)
+    s1.record()
+    torch.cuda.synchronize()
+    return {"stream_read": {"op": "dss_stream_read_reference over the batch, cold rotating buffers",
+                            "kernel_us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+                            "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "torch_sort_us": s0.elapsed_time(s1) * 1e3 / 10}
+
+
 def extra_configs(dss, si, lib, dev):
     """The other workloads of the sampling path, one line each: kernel time
     per call (mean, and p50/p99 where the workload is a latency case) and the
@@ -322,6 +363,7 @@ def main():
         "rounds_histogram": {str(kk): vv for kk, vv in sorted(hist.items())},
     }
     if not args.no_extra and args.engine == "auto" and not args.warm_cache:
+        out["reference"] = reference_points(lib, bufs, K)
         del bufs
         torch.cuda.empty_cache()
         out["other_configs"] = extra_configs(dss, si, lib, dev)

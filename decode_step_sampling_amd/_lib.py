@@ -57,6 +57,7 @@ SIGNATURES = {
     "dss_strerror": ([_I32], ctypes.c_char_p),
     "dss_version": ([], ctypes.c_int32),
     "dss_set_timing_events": ([_P, _P], ctypes.c_int32),
+    "dss_stream_read_reference": ([_P, ctypes.c_int64, _P, _P], ctypes.c_int32),
 }
 
 _lib = None

@@ -232,6 +232,18 @@ DSS_EXPORT int32_t dss_set_timing_events(void* start, void* stop) {
   return DSS_OK;
 }
 
+DSS_EXPORT int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max,
+                                             void* stream) {
+  if (n < 0 || (n % 4) != 0 || (n > 0 && (x == nullptr || !aligned16(x))) || out_max == nullptr)
+    return DSS_ERR_INVALID_ARG;
+  const int dst = check_device();
+  if (dst != DSS_OK) return dst;
+  return dss::launch_stream_read(x, n, out_max, static_cast<hipStream_t>(stream),
+                                timing_events()) == hipSuccess
+             ? DSS_OK
+             : DSS_ERR_HIP;
+}
+
 DSS_EXPORT const char* dss_strerror(int32_t status) {
   switch (status) {
     case DSS_OK: return "ok";

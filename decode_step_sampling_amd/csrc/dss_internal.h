@@ -108,4 +108,9 @@ SplitPlan plan_split_renorm(int kind, int rows, int vocab, uint32_t flags, int v
 hipError_t launch_split_renorm(int kind, const RenormParams& p, const SplitPlan& plan,
                                void* workspace, hipStream_t s, const LaunchEvents& ev);
 
+// plain streaming read of n floats (n a multiple of 4, x 16-byte aligned);
+// folds their maximum bit pattern into *out
+hipError_t launch_stream_read(const float* x, int64_t n, uint32_t* out, hipStream_t s,
+                              const LaunchEvents& ev);
+
 }  // namespace dss

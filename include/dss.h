@@ -216,6 +216,15 @@ size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
  * if exactly one handle is NULL. */
 int32_t dss_set_timing_events(void* start, void* stop);
 
+/* Measurement aid (not part of the sampling path): one plain streaming read
+ * of n floats at x (device, 16-byte aligned, n a multiple of 4), five
+ * 16-byte loads in flight per thread, folding the largest float32 bit
+ * pattern into *out_max (device uint32, caller-initialised; atomicMax).
+ * Its time is the read rate this GPU reaches for that many bytes, the
+ * reference beside the sampling kernels' HBM fraction.  Enqueued on
+ * `stream`.  DSS_ERR_INVALID_ARG for a bad size, pointer or alignment. */
+int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max, void* stream);
+
 /* Static description of a status code. */
 const char* dss_strerror(int32_t status);
 

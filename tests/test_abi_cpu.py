@@ -34,7 +34,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -118,6 +118,12 @@ def test_workspace_size_and_strings():
     # the timing hook takes both event handles or neither; no HIP call is made
     assert lib.dss_set_timing_events(ctypes.c_void_p(16), None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_set_timing_events(None, None) == _lib.DSS_OK
+    # the streaming-read reference checks its arguments before touching HIP
+    out = ctypes.c_void_p(16)
+    assert lib.dss_stream_read_reference(None, 4, out, None) == _lib.DSS_ERR_INVALID_ARG
+    assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 6, out, None) == _lib.DSS_ERR_INVALID_ARG
+    assert lib.dss_stream_read_reference(ctypes.c_void_p(18), 8, out, None) == _lib.DSS_ERR_INVALID_ARG
+    assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 8, None, None) == _lib.DSS_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():
