@@ -52,6 +52,8 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   if (!probs || !samples) return DSS_ERR_INVALID_ARG;
   const int vec_ok = (vocab % 4 == 0) && aligned16(probs);
   const dss::SplitPlan plan = dss::plan_split(op, rows, vocab, num_outputs, flags, vec_ok);
+  const dss::SplitPlan rplan = plan.W > 0 ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
+                                          : dss::plan_resident(op, vocab, num_outputs, flags, vec_ok);
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   const int dev = check_device();
@@ -77,10 +79,11 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.valid = valid;
   p.rounds = rounds;
   p.vec_ok = vec_ok;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      plan.W > 0 ? dss::launch_split_sample(op, p, plan, workspace, static_cast<hipStream_t>(stream),
-                                            timing_events())
-                 : dss::launch_stream_sample(op, p, static_cast<hipStream_t>(stream), timing_events());
+      plan.W > 0    ? dss::launch_split_sample(op, p, plan, workspace, st, timing_events())
+      : rplan.W > 0 ? dss::launch_resident_sample(op, p, rplan, workspace, st, timing_events())
+                    : dss::launch_stream_sample(op, p, st, timing_events());
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
@@ -96,6 +99,9 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
   if (!in || !out) return DSS_ERR_INVALID_ARG;
   const int vec_ok = (vocab % 4 == 0) && aligned16(in) && aligned16(out);
   const dss::SplitPlan plan = dss::plan_split_renorm(kind, rows, vocab, flags, vec_ok);
+  const dss::SplitPlan rplan = kind == dss::kRenormTopP
+                                   ? dss::plan_resident(dss::kOpTopP, vocab, rows, flags, vec_ok)
+                                   : dss::SplitPlan{0, 0, 0, 0, 0, 0};
   const size_t need = dss_workspace_size(op_id, rows, vocab, rows, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   const int dev = check_device();
@@ -112,11 +118,11 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
   p.top_p = top_p;
   p.row_status = row_status;
   p.vec_ok = vec_ok;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      plan.W > 0 ? dss::launch_split_renorm(kind, p, plan, workspace,
-                                            static_cast<hipStream_t>(stream), timing_events())
-                 : dss::launch_stream_renorm(kind, p, static_cast<hipStream_t>(stream),
-                                             timing_events());
+      plan.W > 0    ? dss::launch_split_renorm(kind, p, plan, workspace, st, timing_events())
+      : rplan.W > 0 ? dss::launch_resident_renorm(p, rplan, workspace, st, timing_events())
+                    : dss::launch_stream_renorm(kind, p, st, timing_events());
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
@@ -216,13 +222,20 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
   // sized for 16-byte aligned rows; an unaligned call runs the streaming
   // engine, which needs none
   if (vocab <= 0) return 0;
+  const int vec = vocab % 4 == 0;
   if (op == DSS_OP_TOP_K_RENORM || op == DSS_OP_TOP_K_MASK_LOGITS) {
     if (rows <= 0) return 0;
     const int kind = op == DSS_OP_TOP_K_RENORM ? dss::kRenormTopK : dss::kMaskLogits;
-    return dss::plan_split_renorm(kind, rows, vocab, flags, vocab % 4 == 0).workspace;
+    return dss::plan_split_renorm(kind, rows, vocab, flags, vec).workspace;
+  }
+  if (op == DSS_OP_TOP_P_RENORM) {
+    if (rows <= 0) return 0;
+    return dss::plan_resident(dss::kOpTopP, vocab, rows, flags, vec).workspace;
   }
   if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || num_outputs <= 0) return 0;
-  return dss::plan_split(op, rows, vocab, num_outputs, flags, vocab % 4 == 0).workspace;
+  const dss::SplitPlan plan = dss::plan_split(op, rows, vocab, num_outputs, flags, vec);
+  if (plan.W > 0) return plan.workspace;
+  return dss::plan_resident(op, vocab, num_outputs, flags, vec).workspace;
 }
 
 DSS_EXPORT int32_t dss_set_timing_events(void* start, void* stop) {

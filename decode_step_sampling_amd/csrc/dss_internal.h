@@ -108,6 +108,25 @@ SplitPlan plan_split_renorm(int kind, int rows, int vocab, uint32_t flags, int v
 hipError_t launch_split_renorm(int kind, const RenormParams& p, const SplitPlan& plan,
                                void* workspace, hipStream_t s, const LaunchEvents& ev);
 
+// Workspace layout shared by every op, so that calls of any kind can use one
+// workspace: [0, kCtlRegionBytes) the split engine's arrival counters and
+// generation numbers; then kResidentSlots per-output slots of the resident
+// engine (zero between calls); then the split engine's hand-off area and
+// per-row results (written before they are read).
+constexpr size_t kCtlRegionBytes = 16384;
+constexpr int kResidentSlots = 256;  // outputs of one resident launch at most
+constexpr size_t kResidentSlotBytes = 35072;
+constexpr size_t kFixedRegionBytes = kCtlRegionBytes + (size_t)kResidentSlots * kResidentSlotBytes;
+
+// Resident-slice engine (plain, top-p and min-p sampling; top-p
+// renormalisation): W work-groups per output on one XCD keep the row in
+// registers and meet at row barriers.  W == 0 means "not eligible".
+SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok);
+hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan& plan,
+                                  void* workspace, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_resident_renorm(const RenormParams& p, const SplitPlan& plan, void* workspace,
+                                  hipStream_t s, const LaunchEvents& ev);
+
 // plain streaming read of n floats (n a multiple of 4, x 16-byte aligned);
 // folds their maximum bit pattern into *out
 hipError_t launch_stream_read(const float* x, int64_t n, uint32_t* out, hipStream_t s,

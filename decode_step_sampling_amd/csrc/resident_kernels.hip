@@ -1,0 +1,730 @@
+// Resident-slice engine: plain, top-p and min-p sampling, top-p
+// renormalisation.
+//
+// Top-p needs the row's total mass before any value can be classified, so a
+// slice cannot bound its candidates alone the way the split engine does for
+// top-k.  Here the W work-groups of a row keep their slices in registers for
+// the whole kernel and meet at row barriers (a counter in the XCD's L2 and a
+// bounded spin), so the row is read from HBM exactly once:
+//
+//  1. As each 16-byte vector lands, its values go into an LDS mass histogram
+//     on the top ten bits of the float32 pattern (F4 note §③: for x >= 0 the
+//     bits order like the values).  Every bin holds one binade quarter, so
+//     the bin's mass is an exact integer sum of 24-bit significands times one
+//     power of two: sums are exact and their order does not matter.
+//  2. The slices add their histograms into the row's (global atomics, integer
+//     adds), meet, and every work-group finds the same bin where the mass
+//     from the top crosses p * Z (the F4 note's threshold search on the bit
+//     pattern, section ⑤, with 1023 pivots per pass instead of two).  Two
+//     more levels (the next eleven bits, then the last ten) pin the exact
+//     threshold tau = the largest pattern t with mass(bits >= t) >= p * Z.
+//  3. Renormalisation writes x / Z_kept or 0 straight from the registers.
+//     Sampling publishes the kept mass of every wave's values; the wave whose
+//     range holds u * Z_kept walks its values (blog, 逆变换采样: the first
+//     value whose inclusive prefix exceeds the target).  This is the
+//     dual-pivot loop of the blog's 双枢轴拒绝采样 section started at
+//     low = the largest value below tau: every draw is then a value >= tau,
+//     which f accepts, so it ends after one round.
+//
+// Plain sampling uses tau = the smallest positive pattern and min-p the
+// smallest float >= min_p * max (blog, min-p section), both known without a
+// histogram.  The walk visits values in a fixed order (slice, wave, load,
+// lane, element), not index order; every fixed order gives value x_i the
+// probability x_i / Z_kept.
+//
+// Work-group b runs on XCD b % 8, so the W work-groups of output li are the
+// blocks with equal b % 8 (as in the split engine), and the row's counters
+// live in that XCD's L2.  Every launch holds at most as many work-groups as
+// the device keeps resident at once, so no work-group waits on one that
+// cannot start; a spin that still runs out of time marks the output invalid
+// instead of hanging.
+#include "stream_device.h"
+
+namespace dss {
+namespace {
+
+constexpr int kRMaxW = 16;
+constexpr int kRMaxNv = 12;  // 16-byte loads per thread (48 values; more run out of registers)
+constexpr int kRB1 = 1024;   // level 1: bits [30:21]
+constexpr int kRB2 = 2048;   // level 2: bits [20:10]
+constexpr int kRB3 = 1024;   // level 3: bits [9:0]
+constexpr int kRHistWords = 8192;  // LDS histogram words: bins x copies
+constexpr uint64_t kSpinTicks = 5000000ull;  // 50 ms of the 100 MHz constant clock
+
+// Per-output control block in the workspace, zero between calls.
+struct RowSlot {
+  uint32_t ctl[64];  // 0 barrier arrivals, 1 XCC ids (bit mask), 2 maximum pattern, 3 bad value
+  uint64_t h1[kRB1];
+  uint64_t h2[kRB2];
+  uint64_t h3[kRB3];
+  double chunk[kRMaxW * 16];  // kept mass of every (slice, load): W * NV <= 16 * 12
+};
+
+struct ResidentParams {
+  int W;      // slices per output (a power of two)
+  int L;      // slice length in values (multiple of 4)
+  int out0;   // first output of this launch
+  int n_out;  // outputs of this launch
+  RowSlot* slots;
+};
+
+enum ResKind : int { kResSample = 0, kResRenorm = 1 };
+
+struct ResSmem {
+  alignas(16) uint64_t hh[kRHistWords];  // histogram copies (lanes spread over copies)
+  double md[kRB2];                       // bin masses of the level being searched
+  double wm[kRMaxNv * kWaves];           // kept mass per (load, wave)
+  double cm[kRMaxW * kRMaxNv];           // kept mass per (slice, load), all slices
+  uint32_t wmax[kWaves];
+  uint32_t wbad[kWaves];
+  uint32_t res[4];
+  double resd[4];
+  int flag;
+};
+static_assert(sizeof(ResSmem) <= 96 * 1024, "LDS of the resident kernel");
+
+__device__ __forceinline__ int r_uwave() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ uint32_t r_xcc_id() {
+  return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
+}
+
+__device__ __forceinline__ int r_first_lane(uint64_t m) { return __ffsll((long long)m) - 1; }
+__device__ __forceinline__ int r_last_lane(uint64_t m) { return 63 - __clzll((long long)m); }
+
+// 24-bit significand of a non-negative float32 pattern (hidden bit for
+// normal numbers); value = sig * 2^(max(exponent, 1) - 150)
+__device__ __forceinline__ uint32_t sig_of(uint32_t key) {
+  return (key & 0x7FFFFFu) | (key >= 0x800000u ? 0x800000u : 0u);
+}
+__device__ __forceinline__ double bin_mass(uint64_t s, uint32_t exponent) {
+  return ldexp((double)s, (int)max(exponent, 1u) - 150);
+}
+
+__device__ __forceinline__ uint32_t max4(const float4& x) {
+  return max(max(bits_of(x.x), bits_of(x.y)), max(bits_of(x.z), bits_of(x.w)));
+}
+
+// Arrive at the row barrier and wait until `target` arrivals are counted.
+// Every thread must call; each thread's earlier global stores and atomics are
+// complete (vmcnt 0) before thread 0 arrives.  False if the wait timed out.
+__device__ __forceinline__ bool row_barrier(gptr<uint32_t> ctr, uint32_t target, ResSmem& sm) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    int ok = 1;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+        ok = 0;
+        break;
+      }
+    }
+    sm.flag = ok;
+  }
+  __syncthreads();
+  return sm.flag != 0;
+}
+
+// Leave the row after the last read of its slot.  The work-group that
+// leaves last (all W have passed `passed` barriers and then left) clears what
+// the row used and finally the arrival counter, so the slot is zero for the
+// next launch.  Every thread must call.
+__device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, int W, bool used_hist, ResSmem& sm) {
+  __syncthreads();
+  const gptr<uint32_t> ctr = (gptr<uint32_t>)slot->ctl;
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.flag = old == passed * (uint32_t)W + (uint32_t)W - 1u;
+  }
+  __syncthreads();
+  if (!sm.flag) return;
+  const int t = threadIdx.x;
+  if (used_hist) {
+    const gptr<uint64_t> h = (gptr<uint64_t>)slot->h1;  // h1, h2, h3 are contiguous
+    for (int q = t; q < kRB1 + kRB2 + kRB3; q += kBlock) h[q] = 0ull;
+  }
+  if (t < kRMaxW * kWaves) ((gptr<double>)slot->chunk)[t] = 0.0;
+  if (t >= 1 && t < 64) ctr[t] = 0u;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (t == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum the LDS histogram copies of every bin and add the non-zero sums into
+// the row's global histogram g (NB bins, kRHistWords / NB copies per bin).
+template <int NB>
+__device__ __forceinline__ void publish_hist(const ResSmem& sm, gptr<uint64_t> g) {
+  constexpr int C = kRHistWords / NB;
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    uint64_t s = 0ull;
+#pragma unroll
+    for (int c = 0; c < C; ++c) s += sm.hh[b * C + c];
+    if (s != 0ull) __hip_atomic_fetch_add(g + b, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ void clear_lds_hist(ResSmem& sm) {
+  uint4* h4 = reinterpret_cast<uint4*>(sm.hh);
+  for (int q = threadIdx.x; q < kRHistWords / 2; q += kBlock) h4[q] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Load the row's histogram g (NB bins) as masses into sm.md; `exponent` < 0:
+// level 1, bin b holds exponent b >> 2.
+template <int NB>
+__device__ __forceinline__ void load_masses(gptr<uint64_t> g, int exponent, ResSmem& sm) {
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    const uint64_t s = __hip_atomic_load(g + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.md[b] = bin_mass(s, exponent < 0 ? (uint32_t)b >> 2 : (uint32_t)exponent);
+  }
+}
+
+// One wave: the largest bin b of md[0, NB) whose mass from the top,
+// M(b) = sum_{b' >= b} md[b'], reaches `need` (need = pfrac * total when
+// pfrac >= 0) and is positive; `above` = M(b + 1).  If rounding leaves every
+// M(b) below need, the lowest bin with mass is taken (everything kept).
+// Lane l sums the chunk of NB / 64 bins that is l-th from the top; a scan
+// over lanes finds the chunk and a scan over that chunk's bins the bin.
+template <int NB>
+__device__ __forceinline__ void mass_find(const double* md, double need, double pfrac, uint32_t& bin,
+                          double& above, double& total) {
+  constexpr int C = NB / kWave;
+  const int lane = lane_id();
+  const int c = kWave - 1 - lane;
+  double s = 0.0;
+#pragma unroll
+  for (int q = C - 1; q >= 0; --q) {
+    if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // four reads in flight at a time
+    s += md[c * C + q];
+  }
+  const double incl = wave_incl_scan(s);
+  const double excl = wave_excl_from_incl(incl);
+  total = lane63(incl);
+  if (pfrac >= 0.0) need = pfrac * total;
+  uint64_t hit = __ballot(incl >= need && incl > 0.0);
+  int L = hit ? r_first_lane(hit) : r_last_lane(__ballot(s > 0.0) | 1ull);
+  const bool fallback = hit == 0ull;
+  const int cc = kWave - 1 - L;
+  const double ex = lane_value(excl, L);
+  const double m = lane < C ? md[cc * C + C - 1 - lane] : 0.0;
+  const double incl2 = wave_incl_scan(m) + ex;
+  const double sh = wave_excl_from_incl(incl2);
+  const double excl2 = lane == 0 ? ex : sh;
+  uint64_t hit2 = fallback ? 0ull : __ballot(lane < C && incl2 >= need && incl2 > 0.0);
+  if (hit2 == 0ull) hit2 = 1ull << r_last_lane(__ballot(lane < C && m > 0.0) | 1ull);
+  const int Q = r_first_lane(hit2);
+  bin = (uint32_t)(cc * C + C - 1 - Q);
+  above = lane_value(excl2, Q);
+}
+
+// Kept mass (patterns >= tau) of every load j of this wave's threads, into
+// wm[j * kWaves + wave]: per lane a sequential sum of its four values, over
+// the lanes a wave scan.  Load j of the whole work-group is the contiguous
+// index range [s0 + 4096 j, s0 + 4096 (j + 1)), lanes in index order, so
+// (slice, load, wave, lane, element) is index order.
+template <int NV>
+__device__ __forceinline__ void wave_load_masses(const float4 (&v)[NV], int nvec, uint32_t tau,
+                                                 double* wm) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    // one load at a time: the slice stays live in registers meanwhile
+    __builtin_amdgcn_sched_barrier(0);
+    const bool in = tid + j * kBlock < nvec;
+    const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += (in && bits_of(x[e]) >= tau) ? (double)x[e] : 0.0;
+    const double m = lane63(wave_incl_scan(s));
+    if (lane == 0) wm[j * kWaves + wave] = m;
+  }
+}
+
+// Inverse transform inside one 64-lane group of values x (four per lane,
+// index order): the first kept value whose inclusive prefix exceeds T, with
+// the same lane sums and scan as wave_load_masses, so T below the group's
+// mass always stops inside it; otherwise (rounding) the last kept value.
+// Returns the position 0..255 in the group, in every lane; -1 if none is kept.
+__device__ __forceinline__ int wave_pick(const float4& xv, bool in, uint32_t tau, double T) {
+  const int lane = lane_id();
+  const float x[4] = {xv.x, xv.y, xv.z, xv.w};
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += (in && bits_of(x[e]) >= tau) ? (double)x[e] : 0.0;
+  const double incl = wave_incl_scan(s);
+  const double excl = wave_excl_from_incl(incl);
+  const uint64_t nz = __ballot(s > 0.0);
+  if (nz == 0ull) return -1;
+  const uint64_t hit = __ballot(s > 0.0 && incl > T);
+  const int l = hit ? r_first_lane(hit) : r_last_lane(nz);
+  int e_out = -1;
+  if (lane == l) {
+    double acc = excl;
+    int pick = -1, lastk = -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool k = in && bits_of(x[e]) >= tau && x[e] > 0.0f;
+      lastk = k ? e : lastk;
+      acc += k ? (double)x[e] : 0.0;
+      pick = (k && pick < 0 && acc > T) ? e : pick;
+    }
+    e_out = (hit && pick >= 0) ? pick : lastk;
+  }
+  return __builtin_amdgcn_readlane(4 * l + e_out, l);
+}
+
+// Sequential inverse transform over n masses m[0..n) (one thread): the first
+// positive entry whose running sum exceeds T, and T minus the sum before it;
+// if rounding leaves none, the last positive entry with a target beyond its
+// mass (its last kept value is then taken).  -1 if all are zero.
+__device__ __forceinline__ int seq_pick(const double* m, int n, double T, double& Tl) {
+  double acc = 0.0;
+  int last = -1;
+  double mlast = 0.0;
+  for (int q = 0; q < n; ++q) {
+    const double before = acc, mq = m[q];
+    acc += mq;
+    if (mq > 0.0) {
+      if (acc > T) {
+        Tl = T - before;
+        return q;
+      }
+      last = q;
+      mlast = mq;
+    }
+  }
+  Tl = 2.0 * mlast;
+  return last;
+}
+
+typedef float r_v4f __attribute__((ext_vector_type(4)));
+
+// An empty asm that "changes" the slice's registers: values the compiler
+// derived from them earlier are not kept live past this point for reuse
+// (with the slice itself live, such reuse runs the kernel out of registers).
+template <int NV>
+__device__ __forceinline__ void fence_values(float4 (&v)[NV]) {
+#pragma unroll
+  for (int j = 0; j < NV; ++j) asm volatile("" : "+v"(v[j].x), "+v"(v[j].y), "+v"(v[j].z), "+v"(v[j].w));
+}
+
+// An invalid output: sample -1 (sampling), or the slice NaN-filled and the
+// row's status set by slice 0 (renormalisation).
+template <int KIND, int NV>
+__device__ __forceinline__ void res_invalid(const SampleParams& P, const RenormParams& RP, int i,
+                                            int row, int s, int nvec, gptr<r_v4f> dst) {
+  const int tid = threadIdx.x;
+  if (KIND == kResSample) {
+    if (s == 0 && tid == 0) stream::write_sample(P, i, -1, 0);
+  } else {
+    const float qnan = __uint_as_float(0x7FC00000u);
+    r_v4f o;
+    o.x = o.y = o.z = o.w = qnan;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (tid + j * kBlock < nvec) dst[tid + j * kBlock] = o;
+    if (s == 0 && tid == 0 && RP.row_status) as_global(RP.row_status)[row] = 1;
+  }
+}
+
+template <int KIND, int OP, int NV>
+__global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, RenormParams RP,
+                                                          ResidentParams R) {
+  __shared__ ResSmem sm;
+  constexpr bool kTopP = OP == kOpTopP;
+  const int W = R.W;
+  const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
+  const int li = (local / W) * 8 + xcd;  // the W slices of an output share b % 8
+  const int s = local % W;
+  if (li >= R.n_out) return;
+  const int i = R.out0 + li;
+  const int tid = threadIdx.x, lane = lane_id(), wave = r_uwave();
+
+  const int rows = KIND == kResSample ? P.rows : RP.rows;
+  const int V = KIND == kResSample ? P.vocab : RP.vocab;
+  const int row = KIND == kResSample ? (P.indices ? as_global(P.indices)[i] : i) : i;
+  const bool row_ok = row >= 0 && row < rows;
+  const float* base = KIND == kResSample ? P.probs : RP.in;
+
+  // ---- one HBM read of the slice into registers ------------------------------
+  const int s0 = s * R.L;
+  const int s1 = min(s0 + R.L, V);
+  const int nvec = (s1 - s0) / 4;
+  const gptr<const float4> src =
+      as_global(reinterpret_cast<const float4*>(base + (int64_t)(row_ok ? row : 0) * V + s0));
+  constexpr int kInFlight = NV < 5 ? NV : 5;
+  float4 v[NV];
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1));
+  };
+#pragma unroll
+  for (int j = 0; j < kInFlight; ++j) issue(j);
+
+  // parameters (read before any store, so they are scalar loads)
+  float prm = 0.0f;
+  if (KIND == kResRenorm) prm = RP.top_p_arr ? as_global(RP.top_p_arr)[i] : RP.top_p;
+  else if (OP == kOpTopP) prm = P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
+  else if (OP == kOpMinP) prm = P.min_p_arr ? as_global(P.min_p_arr)[i] : P.min_p;
+  const uint64_t seed = KIND != kResSample ? 0ull : P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset =
+      KIND != kResSample ? 0ull : P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
+  const uint64_t sid = (KIND == kResSample && P.seed_arr) ? 0ull : (uint64_t)i;
+  const float pc = stream::clamp01(prm);
+
+  const gptr<r_v4f> dst = KIND == kResRenorm
+                              ? (gptr<r_v4f>)as_global(RP.out + (int64_t)row * V + s0)
+                              : (gptr<r_v4f>)nullptr;
+
+  if (!row_ok || isnan(prm)) {  // the same decision in every slice of the output
+    res_invalid<KIND, NV>(P, RP, i, row, s, nvec, dst);
+    return;
+  }
+
+  if (kTopP) clear_lds_hist(sm);
+  __syncthreads();
+
+  // as each vector lands: its maximum pattern, and (top-p) its values'
+  // significands added into bin bits[30:21] of the LDS histogram, copy
+  // lane % 8, so that lanes hitting one bin mostly hit different words
+  uint32_t mx = 0u;
+  auto next = [&](int j) __attribute__((always_inline)) {
+    if (j + kInFlight < NV) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j + kInFlight);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const bool in = tid + j * kBlock < nvec;
+    const uint32_t m = max4(v[j]);
+    mx = max(mx, in ? m : 0u);
+    if (kTopP && in) {
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        atomicAdd(&sm.hh[min(k4[e] >> 21, (uint32_t)(kRB1 - 1)) * 8u + (uint32_t)(lane & 7)],
+                  (unsigned long long)sig_of(k4[e]));
+    }
+    next(j);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) sm.wmax[wave] = mx;
+  __syncthreads();
+
+  const gptr<RowSlot> slot = as_global(R.slots + li);
+  const gptr<uint32_t> ctl = (gptr<uint32_t>)slot->ctl;
+  if (tid == 0) {
+    uint32_t smax = 0u;
+    for (int w = 0; w < kWaves; ++w) smax = max(smax, sm.wmax[w]);
+    // a sign bit, an inf or a NaN shows as a pattern >= 0x7F800000
+    __hip_atomic_fetch_max(ctl + 2, smax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(ctl + 1, 1u << r_xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // plain sampling: tau is the smallest positive pattern, known now, so the
+  // kept masses go out with the first arrival
+  uint32_t tau = 1u;
+  // publish the kept mass of every load of this slice (chunk s * NV + j)
+  auto publish_chunks = [&]() __attribute__((always_inline)) {
+    wave_load_masses<NV>(v, nvec, tau, sm.wm);
+    __syncthreads();
+    if (tid < NV) {
+      double m = 0.0;
+      for (int w = 0; w < kWaves; ++w) m += sm.wm[tid * kWaves + w];
+      ((gptr<double>)slot->chunk)[s * NV + tid] = m;
+    }
+  };
+  if (OP == kOpNone && KIND == kResSample) publish_chunks();
+  if (kTopP) publish_hist<kRB1>(sm, (gptr<uint64_t>)slot->h1);
+
+  uint32_t passed = 0u;
+  // a wait that timed out: the output is reported invalid (every slice of
+  // it times out too, its counters never reach the target)
+  if (kTopP) {
+    __syncthreads();
+    clear_lds_hist(sm);
+  }
+  if (!row_barrier(ctl, (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+  passed = 1u;
+  const uint32_t gmax = __hip_atomic_load(ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t xm = __hip_atomic_load(ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool bad = gmax >= 0x7F800000u || gmax == 0u || __popc(xm) != 1;
+
+  double zkept = 0.0;
+  if (bad) {
+    res_invalid<KIND, NV>(P, RP, i, row, s, nvec, dst);
+    row_leave(slot, passed, W, kTopP, sm);
+    return;
+  }
+
+  if (kTopP) {
+    // ---- threshold search, three levels --------------------------------------
+    load_masses<kRB1>((gptr<uint64_t>)slot->h1, -1, sm);
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t b1;
+      double above, total;
+      mass_find<kRB1>(sm.md, 0.0, (double)pc, b1, above, total);
+      if (lane == 0) {
+        sm.res[0] = b1;
+        sm.resd[0] = above;
+        sm.resd[1] = total;
+        sm.resd[2] = (double)pc * total;
+      }
+    }
+    __syncthreads();
+    const uint32_t b1 = sm.res[0];
+    const double above1 = sm.resd[0], ztot = sm.resd[1], need = sm.resd[2];
+    if (pc >= 1.0f) {
+      tau = 1u;  // every positive value
+      zkept = ztot;
+    } else {
+      // level 2: values in bin b1, by bits [20:10], copy lane % 4
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const bool in = tid + j * kBlock < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (in && (k4[e] >> 21) == b1)
+            atomicAdd(&sm.hh[((k4[e] >> 10) & (uint32_t)(kRB2 - 1)) * 4u + (uint32_t)(lane & 3)],
+                      (unsigned long long)sig_of(k4[e]));
+      }
+      __syncthreads();
+      publish_hist<kRB2>(sm, (gptr<uint64_t>)slot->h2);
+      __syncthreads();
+      clear_lds_hist(sm);
+      if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+      passed = 2u;
+      load_masses<kRB2>((gptr<uint64_t>)slot->h2, (int)(b1 >> 2), sm);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t b2;
+        double above, total;
+        mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+        if (lane == 0) {
+          sm.res[1] = b2;
+          sm.resd[0] = above;
+        }
+      }
+      __syncthreads();
+      const uint32_t pre2 = (b1 << 11) | sm.res[1];
+      const double above2 = sm.resd[0];
+      // level 3: values with bits [30:10] == pre2, by bits [9:0], copy lane % 8
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const bool in = tid + j * kBlock < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (in && (k4[e] >> 10) == pre2)
+            atomicAdd(&sm.hh[(k4[e] & (uint32_t)(kRB3 - 1)) * 8u + (uint32_t)(lane & 7)],
+                      (unsigned long long)sig_of(k4[e]));
+      }
+      __syncthreads();
+      publish_hist<kRB3>(sm, (gptr<uint64_t>)slot->h3);
+      if (!row_barrier(ctl, 3u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+      passed = 3u;
+      load_masses<kRB3>((gptr<uint64_t>)slot->h3, (int)(b1 >> 2), sm);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t b3;
+        double above, total;
+        mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
+        if (lane == 0) {
+          sm.res[2] = b3;
+          sm.resd[0] = above1 + above2 + (above + sm.md[b3]);
+        }
+      }
+      __syncthreads();
+      tau = (pre2 << 10) | sm.res[2];
+      zkept = sm.resd[0];
+    }
+  } else if (OP == kOpMinP) {
+    // the smallest float32 >= min_p * max (an exact double product)
+    const double thr = (double)pc * (double)__uint_as_float(gmax);
+    float f = (float)thr;
+    if ((double)f < thr) f = __uint_as_float(bits_of(f) + 1u);
+    tau = max(bits_of(f), 1u);
+  }
+
+  if (KIND == kResRenorm) {
+    if (kTopP) row_leave(slot, passed, W, true, sm);
+    const double inv = 1.0 / zkept;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      r_v4f o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = bits_of(x[e]) >= tau ? (float)((double)x[e] * inv) : 0.0f;
+      if (tid + j * kBlock < nvec) dst[tid + j * kBlock] = o;
+    }
+    if (s == 0 && tid == 0 && RP.row_status) as_global(RP.row_status)[row] = 0;
+    return;
+  }
+
+  // ---- sampling: kept mass per (slice, load), one draw, the owner walks -----
+  if (OP != kOpNone) {
+    publish_chunks();
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm))
+      return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+    ++passed;
+  }
+  // every work-group: the chunk holding u * (total kept mass), index order
+  const int nch = W * NV;
+  for (int c = tid; c < nch; c += kBlock)
+    sm.cm[c] = __hip_atomic_load((gptr<double>)slot->chunk + c, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  row_leave(slot, passed, W, kTopP, sm);
+  if (tid == 0) {
+    double tot = 0.0;
+    for (int c = 0; c < nch; ++c) tot += sm.cm[c];
+    const double u = draw_uniform(seed, offset, sid, 0u);
+    double Tl = 0.0;
+    const int c = seq_pick(sm.cm, nch, u * tot, Tl);
+    sm.res[3] = (uint32_t)c;
+    sm.resd[3] = Tl;
+    // this slice's chunk: the wave inside it
+    if (c >= 0 && c / NV == s) {
+      double Tw = 0.0;
+      const int w = seq_pick(sm.wm + (c % NV) * kWaves, kWaves, Tl, Tw);
+      sm.res[2] = (uint32_t)w;
+      sm.resd[2] = Tw;
+    }
+  }
+  __syncthreads();
+  const int c = (int)sm.res[3];
+  if (c < 0) {  // cannot happen for a valid row (its maximum is kept)
+    if (s == 0 && tid == 0) stream::write_sample(P, i, -1, 0);
+    return;
+  }
+  if (c / NV != s || (int)sm.res[2] != wave) return;
+  const int jstar = c % NV;
+  const double Tw = sm.resd[2];
+  fence_values<NV>(v);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    if (j != jstar) continue;  // wave-uniform
+    const int pos = wave_pick(v[j], tid + j * kBlock < nvec, tau, Tw);
+    if (lane == 0) {
+      const int tok = pos < 0 ? -1 : s0 + 4 * (j * kBlock + wave * kWave) + pos;
+      stream::write_sample(P, i, tok, tok >= 0 ? 1 : 0);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace dss
+
+namespace dss {
+namespace {
+
+static_assert(sizeof(RowSlot) == kResidentSlotBytes, "workspace layout of the resident engine");
+
+
+template <int KIND, int OP, int NV>
+hipError_t launch_res_one(const SampleParams& p, const RenormParams& rp, const SplitPlan& plan,
+                          void* workspace, hipStream_t s, const LaunchEvents& ev) {
+  // work-groups the device keeps resident at once, asked once per process
+  static int cap = -1;
+  if (cap < 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(resident_kernel<KIND, OP, NV>), kBlock, 0);
+    if (e != hipSuccess) return e;
+    cap = cus * per_cu;
+  }
+  ResidentParams R;
+  R.W = plan.W;
+  R.L = plan.L;
+  R.slots = reinterpret_cast<RowSlot*>(static_cast<char*>(workspace) + kCtlRegionBytes);
+  // outputs per launch: whole groups of eight (one per XCD), all resident
+  const int per = min(plan.chunk, (cap / (8 * plan.W)) * 8);
+  const int total = KIND == kResSample ? p.num_outputs : rp.rows;
+  if (per <= 0) return hipErrorInvalidConfiguration;
+  for (int out0 = 0; out0 < total; out0 += per) {
+    R.out0 = out0;
+    R.n_out = min(per, total - out0);
+    const bool first = out0 == 0, last = out0 + per >= total;
+    const dim3 grid((unsigned)(((R.n_out + 7) / 8) * 8 * plan.W)), block(kBlock);
+    launch_kernel(resident_kernel<KIND, OP, NV>, grid, block, s, ev, first, last, p, rp, R);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int KIND, int OP>
+hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const SplitPlan& plan,
+                         void* ws, hipStream_t s, const LaunchEvents& ev) {
+  switch (plan.nv) {
+    case 1: return launch_res_one<KIND, OP, 1>(p, rp, plan, ws, s, ev);
+    case 2: return launch_res_one<KIND, OP, 2>(p, rp, plan, ws, s, ev);
+    case 4: return launch_res_one<KIND, OP, 4>(p, rp, plan, ws, s, ev);
+    case 8: return launch_res_one<KIND, OP, 8>(p, rp, plan, ws, s, ev);
+    case 10: return launch_res_one<KIND, OP, 10>(p, rp, plan, ws, s, ev);
+    default: return launch_res_one<KIND, OP, 12>(p, rp, plan, ws, s, ev);
+  }
+}
+
+}  // namespace
+
+SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok) {
+  SplitPlan plan{0, 0, 0, 0, 0, 0};
+  if (op != kOpNone && op != kOpTopP && op != kOpMinP) return plan;
+  if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO)) return plan;
+  if (!vec_ok || vocab < 1024 || num_outputs <= 0) return plan;
+  constexpr int kMaxSlice = kRMaxNv * 4 * kBlock;
+  const int wmin = (vocab + kMaxSlice - 1) / kMaxSlice;
+  if (wmin > kRMaxW) return plan;
+  const int wt = (kResidentSlots + num_outputs - 1) / num_outputs;
+  // W: a power of two, at least wmin, about 256 work-groups in all, no empty slice
+  int W = 1;
+  while (W < wmin || (W * 2 <= kRMaxW && W * 2 <= wt)) W *= 2;
+  int L = 0;
+  for (;; W /= 2) {
+    L = ((vocab + 4 * W - 1) / (4 * W)) * 4;
+    if (W == 1 || (int64_t)(W - 1) * L < vocab) break;
+  }
+  if (W < wmin) return plan;
+  int nv = (L / 4 + kBlock - 1) / kBlock;
+  nv = nv <= 2 ? nv : nv <= 4 ? 4 : nv <= 8 ? 8 : nv <= 10 ? 10 : 12;
+  plan.W = W;
+  plan.L = L;
+  plan.nv = nv;
+  plan.chunk = min(num_outputs, kResidentSlots / W);
+  plan.handoff = kFixedRegionBytes;
+  plan.workspace = kFixedRegionBytes;
+  return plan;
+}
+
+hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan& plan,
+                                  void* workspace, hipStream_t s, const LaunchEvents& ev) {
+  const RenormParams rp{};
+  hipError_t e;
+  if (op == kOpNone) e = launch_res_nv<kResSample, kOpNone>(p, rp, plan, workspace, s, ev);
+  else if (op == kOpTopP) e = launch_res_nv<kResSample, kOpTopP>(p, rp, plan, workspace, s, ev);
+  else e = launch_res_nv<kResSample, kOpMinP>(p, rp, plan, workspace, s, ev);
+  // a device that cannot hold one group of work-groups at once: streaming engine
+  if (e == hipErrorInvalidConfiguration) e = launch_stream_sample(op, p, s, ev);
+  return e;
+}
+
+hipError_t launch_resident_renorm(const RenormParams& rp, const SplitPlan& plan, void* workspace,
+                                  hipStream_t s, const LaunchEvents& ev) {
+  const SampleParams p{};
+  hipError_t e = launch_res_nv<kResRenorm, kOpTopP>(p, rp, plan, workspace, s, ev);
+  if (e == hipErrorInvalidConfiguration) e = launch_stream_renorm(kRenormTopP, rp, s, ev);
+  return e;
+}
+
+}  // namespace dss

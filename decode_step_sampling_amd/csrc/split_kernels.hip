@@ -1146,6 +1146,7 @@ constexpr int kMaxSliceLen = kMaxNv * 4 * kBlock;
 // largest chunk, so calls of any shape can share one workspace: counters are
 // zero between calls, generations only ever grow.
 constexpr size_t kCtlBytes = 2 * (size_t)kChunk * 4;
+static_assert(kCtlBytes == kCtlRegionBytes, "workspace layout shared with the resident engine");
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1178,7 +1179,7 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
   plan.nv = nv;
   plan.chunk = ch;
   plan.handoff = W == 1 ? 0
-                        : align256(kCtlBytes + align256((size_t)ch * W * kHdrWords * 4) +
+                        : align256(kFixedRegionBytes + align256((size_t)ch * W * kHdrWords * 4) +
                                    (size_t)ch * W * kListMax * 8);
   plan.workspace = plan.handoff;
   return plan;
@@ -1190,7 +1191,7 @@ namespace {
 // numbers at fixed offsets), which every op sharing a workspace relies on,
 // even when the plan itself needs no hand-off (W == 1).
 size_t result_bytes(size_t ch) { return align256(ch * 4) + align256(ch * 8) + align256(ch); }
-size_t results_offset(const SplitPlan& plan) { return max(plan.handoff, align256(kCtlBytes)); }
+size_t results_offset(const SplitPlan& plan) { return max(plan.handoff, align256(kFixedRegionBytes)); }
 
 SplitParams split_params(const SplitPlan& plan, void* workspace) {
   char* ws = static_cast<char*>(workspace);
@@ -1202,8 +1203,8 @@ SplitParams split_params(const SplitPlan& plan, void* workspace) {
   sp.L = plan.L;
   sp.ctr = reinterpret_cast<uint32_t*>(ws);
   sp.gen = sp.ctr + kChunk;
-  sp.hdr = reinterpret_cast<uint32_t*>(ws + kCtlBytes);
-  sp.list = reinterpret_cast<uint64_t*>(ws + kCtlBytes + align256(ch * plan.W * kHdrWords * 4));
+  sp.hdr = reinterpret_cast<uint32_t*>(ws + kFixedRegionBytes);
+  sp.list = reinterpret_cast<uint64_t*>(ws + kFixedRegionBytes + align256(ch * plan.W * kHdrWords * 4));
   char* res = ws + results_offset(plan);
   sp.r_tau = reinterpret_cast<uint32_t*>(res);
   sp.r_z = reinterpret_cast<double*>(res + align256(ch * 4));
