@@ -57,7 +57,7 @@ struct RowSlot {
   uint64_t h1[kRB1];
   uint64_t h2[kRB2];
   uint64_t h3[kRB3];
-  double chunk[kRMaxW * 16];  // kept mass of every (slice, load): W * NV <= 16 * 12
+  double chunk[kRMaxW * kWaves];  // kept mass of every (slice, wave) range
 };
 
 struct ResidentParams {
@@ -73,8 +73,6 @@ enum ResKind : int { kResSample = 0, kResRenorm = 1 };
 struct ResSmem {
   alignas(16) uint64_t hh[kRHistWords];  // histogram copies (lanes spread over copies)
   double md[kRB2];                       // bin masses of the level being searched
-  double wm[kRMaxNv * kWaves];           // kept mass per (load, wave)
-  double cm[kRMaxW * kRMaxNv];           // kept mass per (slice, load), all slices
   uint32_t wmax[kWaves];
   uint32_t wbad[kWaves];
   uint32_t res[4];
@@ -221,84 +219,111 @@ __device__ __forceinline__ void mass_find(const double* md, double need, double 
   above = lane_value(excl2, Q);
 }
 
-// Kept mass (patterns >= tau) of every load j of this wave's threads, into
-// wm[j * kWaves + wave]: per lane a sequential sum of its four values, over
-// the lanes a wave scan.  Load j of the whole work-group is the contiguous
-// index range [s0 + 4096 j, s0 + 4096 (j + 1)), lanes in index order, so
-// (slice, load, wave, lane, element) is index order.
+// The slice is loaded so that wave w owns the contiguous vector range
+// [w * 64 * NV, (w + 1) * 64 * NV): its load j covers vectors
+// w * 64 * NV + 64 j + lane (64 consecutive 16-byte vectors, one coalesced
+// 1 KB read per instruction).  Thread position of load j: vbase + 64 j with
+// vbase = w * 64 * NV + lane.  Index order inside the slice is therefore
+// (wave, load, lane, element).
+
+// An empty asm that "changes" one vector together with a loop's running
+// value: the vector's arithmetic cannot start before the previous
+// iteration's result exists (scheduling barriers do not hold back pure
+// arithmetic), which keeps loops over the loads from converting every value
+// at once and running out of registers.
+template <class T>
+__device__ __forceinline__ void fence_vec(float4& x, T& chain) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w), "+v"(chain));
+}
+
+// Kept mass (patterns >= tau) of this wave's values: per lane a sequential
+// sum, over the lanes a wave scan.  Lane-uniform.
 template <int NV>
-__device__ __forceinline__ void wave_load_masses(const float4 (&v)[NV], int nvec, uint32_t tau,
-                                                 double* wm) {
-  const int tid = threadIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
+__device__ __forceinline__ double wave_mass(float4 (&v)[NV], int vbase, int nvec, uint32_t tau) {
+  double acc = 0.0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    // one load at a time: the slice stays live in registers meanwhile
-    __builtin_amdgcn_sched_barrier(0);
-    const bool in = tid + j * kBlock < nvec;
+    fence_vec(v[j], acc);  // one load at a time (register pressure)
+    const bool in = vbase + j * kWave < nvec;
+    const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += (in && bits_of(x[e]) >= tau) ? (double)x[e] : 0.0;
+  }
+  return lane63(wave_incl_scan(acc));
+}
+
+// Where the owner wave's walk stopped: load j, lane l, the mass before that
+// lane's values in the walk, and whether a prefix really exceeded the target
+// (otherwise (j, l) is the last lane holding kept mass).  Wave-uniform.
+struct WalkPick {
+  int j;
+  int l;
+  double excl;
+  bool hit;
+};
+
+// Inverse transform over the wave's kept values in index order (load j,
+// lane, element): per load a wave scan of the lanes' sums, carried over the
+// loads; pk = the first lane whose inclusive prefix exceeds T.
+template <int NV>
+__device__ __forceinline__ void wave_walk(float4 (&v)[NV], int vbase, int nvec, uint32_t tau,
+                                          double T, WalkPick& pk) {
+  const int lane = lane_id();
+  double carry = 0.0;
+  pk = WalkPick{-1, -1, 0.0, false};
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    fence_vec(v[j], carry);  // one load at a time (register pressure)
+    const bool in = vbase + j * kWave < nvec;
     const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
     double s = 0.0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) s += (in && bits_of(x[e]) >= tau) ? (double)x[e] : 0.0;
-    const double m = lane63(wave_incl_scan(s));
-    if (lane == 0) wm[j * kWaves + wave] = m;
+    const double incl = wave_incl_scan(s) + carry;
+    if (!pk.hit) {
+      const double sh = wave_excl_from_incl(incl);
+      const double excl = lane == 0 ? carry : sh;
+      const uint64_t nz = __ballot(s > 0.0);
+      const uint64_t hit = __ballot(s > 0.0 && incl > T);
+      if (hit) {
+        const int l = r_first_lane(hit);
+        pk = WalkPick{j, l, lane_value(excl, l), true};
+      } else if (nz) {
+        const int l = r_last_lane(nz);
+        pk = WalkPick{j, l, lane_value(excl, l), false};
+      }
+    }
+    carry = lane63(incl);
   }
 }
 
-// Inverse transform inside one 64-lane group of values x (four per lane,
-// index order): the first kept value whose inclusive prefix exceeds T, with
-// the same lane sums and scan as wave_load_masses, so T below the group's
-// mass always stops inside it; otherwise (rounding) the last kept value.
-// Returns the position 0..255 in the group, in every lane; -1 if none is kept.
-__device__ __forceinline__ int wave_pick(const float4& xv, bool in, uint32_t tau, double T) {
-  const int lane = lane_id();
-  const float x[4] = {xv.x, xv.y, xv.z, xv.w};
-  double s = 0.0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s += (in && bits_of(x[e]) >= tau) ? (double)x[e] : 0.0;
-  const double incl = wave_incl_scan(s);
-  const double excl = wave_excl_from_incl(incl);
-  const uint64_t nz = __ballot(s > 0.0);
-  if (nz == 0ull) return -1;
-  const uint64_t hit = __ballot(s > 0.0 && incl > T);
-  const int l = hit ? r_first_lane(hit) : r_last_lane(nz);
+// The value the walk picked, decided by lane pk.l: the first kept value of
+// its load pk.j whose prefix exceeds T, or its last kept one when rounding
+// leaves none.  Returns the value's position in the slice in lane pk.l, -1
+// elsewhere.  (Every load is examined and only load pk.j's result kept:
+// selecting the vector by a run-time index would move v to scratch memory.)
+template <int NV>
+__device__ __forceinline__ int pick_value(float4 (&v)[NV], int vbase, uint32_t tau, double T,
+                                          const WalkPick& pk) {
+  if (pk.j < 0 || lane_id() != pk.l) return -1;
   int e_out = -1;
-  if (lane == l) {
-    double acc = excl;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    fence_vec(v[j], e_out);
+    const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    double acc = pk.excl;
     int pick = -1, lastk = -1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool k = in && bits_of(x[e]) >= tau && x[e] > 0.0f;
+      const bool k = bits_of(x[e]) >= tau && x[e] > 0.0f;
       lastk = k ? e : lastk;
       acc += k ? (double)x[e] : 0.0;
       pick = (k && pick < 0 && acc > T) ? e : pick;
     }
-    e_out = (hit && pick >= 0) ? pick : lastk;
+    const int e = (pk.hit && pick >= 0) ? pick : lastk;
+    e_out = j == pk.j ? e : e_out;
   }
-  return __builtin_amdgcn_readlane(4 * l + e_out, l);
-}
-
-// Sequential inverse transform over n masses m[0..n) (one thread): the first
-// positive entry whose running sum exceeds T, and T minus the sum before it;
-// if rounding leaves none, the last positive entry with a target beyond its
-// mass (its last kept value is then taken).  -1 if all are zero.
-__device__ __forceinline__ int seq_pick(const double* m, int n, double T, double& Tl) {
-  double acc = 0.0;
-  int last = -1;
-  double mlast = 0.0;
-  for (int q = 0; q < n; ++q) {
-    const double before = acc, mq = m[q];
-    acc += mq;
-    if (mq > 0.0) {
-      if (acc > T) {
-        Tl = T - before;
-        return q;
-      }
-      last = q;
-      mlast = mq;
-    }
-  }
-  Tl = 2.0 * mlast;
-  return last;
+  return e_out < 0 ? -1 : 4 * (vbase + pk.j * kWave) + e_out;
 }
 
 typedef float r_v4f __attribute__((ext_vector_type(4)));
@@ -316,7 +341,7 @@ __device__ __forceinline__ void fence_values(float4 (&v)[NV]) {
 // row's status set by slice 0 (renormalisation).
 template <int KIND, int NV>
 __device__ __forceinline__ void res_invalid(const SampleParams& P, const RenormParams& RP, int i,
-                                            int row, int s, int nvec, gptr<r_v4f> dst) {
+                                            int row, int s, int vbase, int nvec, gptr<r_v4f> dst) {
   const int tid = threadIdx.x;
   if (KIND == kResSample) {
     if (s == 0 && tid == 0) stream::write_sample(P, i, -1, 0);
@@ -326,7 +351,7 @@ __device__ __forceinline__ void res_invalid(const SampleParams& P, const RenormP
     o.x = o.y = o.z = o.w = qnan;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-      if (tid + j * kBlock < nvec) dst[tid + j * kBlock] = o;
+      if (vbase + j * kWave < nvec) dst[vbase + j * kWave] = o;
     if (s == 0 && tid == 0 && RP.row_status) as_global(RP.row_status)[row] = 1;
   }
 }
@@ -358,8 +383,9 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       as_global(reinterpret_cast<const float4*>(base + (int64_t)(row_ok ? row : 0) * V + s0));
   constexpr int kInFlight = NV < 5 ? NV : 5;
   float4 v[NV];
+  const int vbase = wave * (kWave * NV) + lane;  // this thread's vector of load 0
   auto issue = [&](int j) __attribute__((always_inline)) {
-    v[j] = load_f4(src + min(tid + j * kBlock, nvec - 1));
+    v[j] = load_f4(src + min(vbase + j * kWave, nvec - 1));
   };
 #pragma unroll
   for (int j = 0; j < kInFlight; ++j) issue(j);
@@ -374,13 +400,16 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       KIND != kResSample ? 0ull : P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
   const uint64_t sid = (KIND == kResSample && P.seed_arr) ? 0ull : (uint64_t)i;
   const float pc = stream::clamp01(prm);
+  // the output's draw, while the slice is in flight (only thread 0 uses it)
+  double u = 0.0;
+  if (KIND == kResSample && wave == 0) u = draw_uniform(seed, offset, sid, 0u);
 
   const gptr<r_v4f> dst = KIND == kResRenorm
                               ? (gptr<r_v4f>)as_global(RP.out + (int64_t)row * V + s0)
                               : (gptr<r_v4f>)nullptr;
 
   if (!row_ok || isnan(prm)) {  // the same decision in every slice of the output
-    res_invalid<KIND, NV>(P, RP, i, row, s, nvec, dst);
+    res_invalid<KIND, NV>(P, RP, i, row, s, vbase, nvec, dst);
     return;
   }
 
@@ -400,7 +429,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   };
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const bool in = tid + j * kBlock < nvec;
+    const bool in = vbase + j * kWave < nvec;
     const uint32_t m = max4(v[j]);
     mx = max(mx, in ? m : 0u);
     if (kTopP && in) {
@@ -429,15 +458,11 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   // plain sampling: tau is the smallest positive pattern, known now, so the
   // kept masses go out with the first arrival
   uint32_t tau = 1u;
-  // publish the kept mass of every load of this slice (chunk s * NV + j)
+  // publish the kept mass of this wave's range (chunk s * 16 + wave)
   auto publish_chunks = [&]() __attribute__((always_inline)) {
-    wave_load_masses<NV>(v, nvec, tau, sm.wm);
-    __syncthreads();
-    if (tid < NV) {
-      double m = 0.0;
-      for (int w = 0; w < kWaves; ++w) m += sm.wm[tid * kWaves + w];
-      ((gptr<double>)slot->chunk)[s * NV + tid] = m;
-    }
+    fence_values<NV>(v);
+    const double m = wave_mass<NV>(v, vbase, nvec, tau);
+    if (lane == 0) ((gptr<double>)slot->chunk)[s * kWaves + wave] = m;
   };
   if (OP == kOpNone && KIND == kResSample) publish_chunks();
   if (kTopP) publish_hist<kRB1>(sm, (gptr<uint64_t>)slot->h1);
@@ -449,7 +474,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     __syncthreads();
     clear_lds_hist(sm);
   }
-  if (!row_barrier(ctl, (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+  if (!row_barrier(ctl, (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
   passed = 1u;
   const uint32_t gmax = __hip_atomic_load(ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t xm = __hip_atomic_load(ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -457,7 +482,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
 
   double zkept = 0.0;
   if (bad) {
-    res_invalid<KIND, NV>(P, RP, i, row, s, nvec, dst);
+    res_invalid<KIND, NV>(P, RP, i, row, s, vbase, nvec, dst);
     row_leave(slot, passed, W, kTopP, sm);
     return;
   }
@@ -487,7 +512,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       // level 2: values in bin b1, by bits [20:10], copy lane % 4
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const bool in = tid + j * kBlock < nvec;
+        const bool in = vbase + j * kWave < nvec;
         const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -499,7 +524,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       publish_hist<kRB2>(sm, (gptr<uint64_t>)slot->h2);
       __syncthreads();
       clear_lds_hist(sm);
-      if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+      if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
       passed = 2u;
       load_masses<kRB2>((gptr<uint64_t>)slot->h2, (int)(b1 >> 2), sm);
       __syncthreads();
@@ -518,7 +543,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       // level 3: values with bits [30:10] == pre2, by bits [9:0], copy lane % 8
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const bool in = tid + j * kBlock < nvec;
+        const bool in = vbase + j * kWave < nvec;
         const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -528,7 +553,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       }
       __syncthreads();
       publish_hist<kRB3>(sm, (gptr<uint64_t>)slot->h3);
-      if (!row_barrier(ctl, 3u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+      if (!row_barrier(ctl, 3u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
       passed = 3u;
       load_masses<kRB3>((gptr<uint64_t>)slot->h3, (int)(b1 >> 2), sm);
       __syncthreads();
@@ -554,7 +579,6 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   }
 
   if (KIND == kResRenorm) {
-    if (kTopP) row_leave(slot, passed, W, true, sm);
     const double inv = 1.0 / zkept;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -562,61 +586,82 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       r_v4f o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = bits_of(x[e]) >= tau ? (float)((double)x[e] * inv) : 0.0f;
-      if (tid + j * kBlock < nvec) dst[tid + j * kBlock] = o;
+      if (vbase + j * kWave < nvec) dst[vbase + j * kWave] = o;
     }
     if (s == 0 && tid == 0 && RP.row_status) as_global(RP.row_status)[row] = 0;
+    row_leave(slot, passed, W, true, sm);
     return;
   }
 
-  // ---- sampling: kept mass per (slice, load), one draw, the owner walks -----
+  // ---- sampling: kept mass per (slice, wave), one draw, the owner walks -----
   if (OP != kOpNone) {
     publish_chunks();
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm))
-      return res_invalid<KIND, NV>(P, RP, i, row, 0, nvec, dst);
+      return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
     ++passed;
   }
-  // every work-group: the chunk holding u * (total kept mass), index order
-  const int nch = W * NV;
-  for (int c = tid; c < nch; c += kBlock)
-    sm.cm[c] = __hip_atomic_load((gptr<double>)slot->chunk + c, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  row_leave(slot, passed, W, kTopP, sm);
-  if (tid == 0) {
-    double tot = 0.0;
-    for (int c = 0; c < nch; ++c) tot += sm.cm[c];
-    const double u = draw_uniform(seed, offset, sid, 0u);
-    double Tl = 0.0;
-    const int c = seq_pick(sm.cm, nch, u * tot, Tl);
-    sm.res[3] = (uint32_t)c;
-    sm.resd[3] = Tl;
-    // this slice's chunk: the wave inside it
-    if (c >= 0 && c / NV == s) {
-      double Tw = 0.0;
-      const int w = seq_pick(sm.wm + (c % NV) * kWaves, kWaves, Tl, Tw);
-      sm.res[2] = (uint32_t)w;
-      sm.resd[2] = Tw;
-    }
-  }
-  __syncthreads();
-  const int c = (int)sm.res[3];
-  if (c < 0) {  // cannot happen for a valid row (its maximum is kept)
-    if (s == 0 && tid == 0) stream::write_sample(P, i, -1, 0);
-    return;
-  }
-  if (c / NV != s || (int)sm.res[2] != wave) return;
-  const int jstar = c % NV;
-  const double Tw = sm.resd[2];
-  fence_values<NV>(v);
+  // every work-group, wave 0: the chunk holding u * (total kept mass);
+  // lane l holds chunks [4l, 4l + 4) (slice-major, index order)
+  if (wave == 0) {
+    const int nch = W * kWaves;
+    double cmq[4];
+    double ls = 0.0;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    if (j != jstar) continue;  // wave-uniform
-    const int pos = wave_pick(v[j], tid + j * kBlock < nvec, tau, Tw);
-    if (lane == 0) {
-      const int tok = pos < 0 ? -1 : s0 + 4 * (j * kBlock + wave * kWave) + pos;
-      stream::write_sample(P, i, tok, tok >= 0 ? 1 : 0);
+    for (int q = 0; q < 4; ++q) {
+      const int c = 4 * lane + q;
+      cmq[q] = c < nch ? __hip_atomic_load((gptr<double>)slot->chunk + c, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.0;
+      ls += cmq[q];
+    }
+    const double incl = wave_incl_scan(ls);
+    const double T = u * lane63(incl);
+    const uint64_t hit = __ballot(ls > 0.0 && incl > T);
+    const bool fallback = hit == 0ull;
+    const int L = fallback ? r_last_lane(__ballot(ls > 0.0) | 1ull) : r_first_lane(hit);
+    if (lane == L) {
+      double acc = incl - ls;
+      int pick = -1, lastc = -1;
+      double ex_pick = 0.0, mlast = 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double before = acc;
+        acc += cmq[q];
+        if (cmq[q] > 0.0) {
+          lastc = q;
+          mlast = cmq[q];
+          if (pick < 0 && !fallback && acc > T) {
+            pick = q;
+            ex_pick = before;
+          }
+        }
+      }
+      const int q = pick >= 0 ? pick : lastc;
+      sm.res[3] = q < 0 ? 0xFFFFFFFFu : (uint32_t)(4 * L + q);
+      // no prefix beyond T (rounding): a target past the chunk's mass makes
+      // the owner wave take its last kept value
+      sm.resd[3] = pick >= 0 ? T - ex_pick : 2.0 * mlast;
     }
   }
+  __syncthreads();
+  const uint32_t c = sm.res[3];
+  if (c == 0xFFFFFFFFu) {  // cannot happen for a valid row (its maximum is kept)
+    if (s == 0 && tid == 0) stream::write_sample(P, i, -1, 0);
+  } else if ((int)c / kWaves == s && (int)c % kWaves == wave) {
+    // the owner wave; the slot is left afterwards, off this path
+    const double Tl = sm.resd[3];
+    fence_values<NV>(v);
+    WalkPick pk;
+    wave_walk<NV>(v, vbase, nvec, tau, Tl, pk);
+    fence_values<NV>(v);
+    const int pos = pick_value<NV>(v, vbase, tau, Tl, pk);
+    if (pk.j < 0) {
+      if (lane == 0) stream::write_sample(P, i, -1, 0);
+    } else if (lane == pk.l) {
+      stream::write_sample(P, i, pos >= 0 ? s0 + pos : -1, pos >= 0 ? 1 : 0);
+    }
+  }
+  row_leave(slot, passed, W, kTopP, sm);
 }
 
 }  // namespace
