@@ -114,9 +114,11 @@ hipError_t launch_split_renorm(int kind, const RenormParams& p, const SplitPlan&
 // engine (zero between calls); then the split engine's hand-off area and
 // per-row results (written before they are read).
 constexpr size_t kCtlRegionBytes = 16384;
-constexpr int kResidentSlots = 256;  // outputs of one resident launch at most
+constexpr int kResidentSlots = 256;  // outputs (and work-groups) of one resident launch at most
 constexpr size_t kResidentSlotBytes = 35072;
-constexpr size_t kFixedRegionBytes = kCtlRegionBytes + (size_t)kResidentSlots * kResidentSlotBytes;
+constexpr int kResidentSegKeys = 8192;  // boundary-bin keys one work-group may publish
+constexpr size_t kFixedRegionBytes = kCtlRegionBytes + (size_t)kResidentSlots * kResidentSlotBytes +
+                                     (size_t)kResidentSlots * kResidentSegKeys * 4;
 
 // Resident-slice engine (plain, top-p and min-p sampling; top-p
 // renormalisation): W work-groups per output on one XCD keep the row in

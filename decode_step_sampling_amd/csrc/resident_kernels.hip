@@ -66,6 +66,7 @@ struct ResidentParams {
   int out0;   // first output of this launch
   int n_out;  // outputs of this launch
   RowSlot* slots;
+  uint32_t* lists;  // [n_out * W][kResidentSegKeys] boundary-bin keys per work-group
 };
 
 enum ResKind : int { kResSample = 0, kResRenorm = 1 };
@@ -75,6 +76,8 @@ struct ResSmem {
   double md[kRB2];                       // bin masses of the level being searched
   uint32_t wmax[kWaves];
   uint32_t wbad[kWaves];
+  uint32_t wsc[kWaves];           // per-wave totals of a block scan
+  uint32_t off[kRMaxW + 1];       // list offsets of the slices
   uint32_t res[4];
   double resd[4];
   int flag;
@@ -263,38 +266,74 @@ struct WalkPick {
 };
 
 // Inverse transform over the wave's kept values in index order (load j,
-// lane, element): per load a wave scan of the lanes' sums, carried over the
-// loads; pk = the first lane whose inclusive prefix exceeds T.
+// lane, element).  The lane sums of every load go to LDS at j * 64 + lane
+// (index order); lane l then takes the NV consecutive entries
+// [l * NV, (l + 1) * NV), so one wave scan of the lanes' totals finds the
+// lane whose entries cross T, and that lane walks its entries.  Sets pk to
+// the crossing entry's (load, lane) with excl = 0 and returns the target
+// left inside that entry (or a target past its mass when rounding leaves
+// no crossing, so that its last kept value is taken).  lds: NV * 64 doubles
+// used by this wave alone.
 template <int NV>
-__device__ __forceinline__ void wave_walk(float4 (&v)[NV], int vbase, int nvec, uint32_t tau,
-                                          double T, WalkPick& pk) {
+__device__ __forceinline__ double wave_walk(float4 (&v)[NV], int vbase, int nvec, uint32_t tau,
+                                            double T, double* lds, WalkPick& pk) {
   const int lane = lane_id();
-  double carry = 0.0;
-  pk = WalkPick{-1, -1, 0.0, false};
+  double chain = 0.0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    fence_vec(v[j], carry);  // one load at a time (register pressure)
+    fence_vec(v[j], chain);  // one load at a time (register pressure)
     const bool in = vbase + j * kWave < nvec;
     const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
     double s = 0.0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) s += (in && bits_of(x[e]) >= tau) ? (double)x[e] : 0.0;
-    const double incl = wave_incl_scan(s) + carry;
-    if (!pk.hit) {
-      const double sh = wave_excl_from_incl(incl);
-      const double excl = lane == 0 ? carry : sh;
-      const uint64_t nz = __ballot(s > 0.0);
-      const uint64_t hit = __ballot(s > 0.0 && incl > T);
-      if (hit) {
-        const int l = r_first_lane(hit);
-        pk = WalkPick{j, l, lane_value(excl, l), true};
-      } else if (nz) {
-        const int l = r_last_lane(nz);
-        pk = WalkPick{j, l, lane_value(excl, l), false};
+    lds[j * kWave + lane] = s;
+    chain = s;
+  }
+  __builtin_amdgcn_wave_barrier();
+  double q[NV];
+  double t = 0.0;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    q[k] = lds[lane * NV + k];
+    t += q[k];
+  }
+  const double incl = wave_incl_scan(t);
+  const uint64_t hit = __ballot(t > 0.0 && incl > T);
+  const uint64_t nz = __ballot(t > 0.0);
+  pk = WalkPick{-1, -1, 0.0, false};
+  if (nz == 0ull) return 0.0;
+  const int L = hit ? r_first_lane(hit) : r_last_lane(nz);
+  // lane L: its entries in order
+  int ent = -1;
+  double tl = 0.0;
+  if (lane == L) {
+    double run = incl - t;
+    int lastk = -1;
+    double mlast = 0.0;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const double before = run;
+      run += q[k];
+      const bool pos = q[k] > 0.0;
+      lastk = pos ? k : lastk;
+      mlast = pos ? q[k] : mlast;
+      if (hit && ent < 0 && pos && run > T) {
+        ent = k;
+        tl = T - before;
       }
     }
-    carry = lane63(incl);
+    if (ent < 0) {
+      ent = lastk;
+      tl = 2.0 * mlast;
+    }
+    ent += L * NV;
   }
+  const int e = __builtin_amdgcn_readlane(ent, L);
+  // the entry's own values decide: the first whose prefix exceeds the target
+  // left in it, else (rounding, or the no-crossing target) its last kept one
+  pk = WalkPick{e / kWave, e % kWave, 0.0, true};
+  return lane_value(tl, L);
 }
 
 // The value the walk picked, decided by lane pk.l: the first kept value of
@@ -335,6 +374,37 @@ template <int NV>
 __device__ __forceinline__ void fence_values(float4 (&v)[NV]) {
 #pragma unroll
   for (int j = 0; j < NV; ++j) asm volatile("" : "+v"(v[j].x), "+v"(v[j].y), "+v"(v[j].z), "+v"(v[j].w));
+}
+
+// Exclusive prefix of v over the work-group in thread order, and the total.
+// Every thread must call.
+__device__ __forceinline__ uint32_t res_block_scan(uint32_t v, uint32_t& total, ResSmem& sm) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == kWave - 1) sm.wsc[w] = incl;
+  __syncthreads();
+  uint32_t base = 0u, tot = 0u;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    const uint32_t t = sm.wsc[q];
+    base += q < w ? t : 0u;
+    tot += t;
+  }
+  total = tot;
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Fold the LDS histogram copies of NB bins into masses md (exponent e).
+template <int NB>
+__device__ __forceinline__ void fold_masses(ResSmem& sm, uint32_t exponent) {
+  constexpr int C = kRHistWords / NB;
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    uint64_t s = 0ull;
+#pragma unroll
+    for (int c = 0; c < C; ++c) s += sm.hh[b * C + c];
+    sm.md[b] = bin_mass(s, exponent);
+  }
 }
 
 // An invalid output: sample -1 (sampling), or the slice NaN-filled and the
@@ -505,9 +575,105 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     __syncthreads();
     const uint32_t b1 = sm.res[0];
     const double above1 = sm.resd[0], ztot = sm.resd[1], need = sm.resd[2];
+    const uint32_t e1 = b1 >> 2;
+    // the row's values in bin b1 number at most its significand sum / 2^23
+    // (normal numbers): a small bin goes out as a key list instead of two
+    // more rounds of row histograms
+    const bool use_list = e1 >= 1u && ldexp(sm.md[b1], 127 - (int)e1) <= (double)kResidentSegKeys;
     if (pc >= 1.0f) {
       tau = 1u;  // every positive value
       zkept = ztot;
+    } else if (use_list) {
+      // this slice's keys in bin b1, in thread order, to its segment
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const bool in = vbase + j * kWave < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cnt += (in && (k4[e] >> 21) == b1) ? 1u : 0u;
+      }
+      uint32_t mine;
+      uint32_t pos = res_block_scan(cnt, mine, sm);
+      const gptr<uint32_t> seg = as_global(R.lists + (size_t)(li * W + s) * kResidentSegKeys);
+      if (cnt != 0u) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const bool in = vbase + j * kWave < nvec;
+          const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (in && (k4[e] >> 21) == b1) seg[pos++] = k4[e];
+        }
+      }
+      if (tid == 0) __hip_atomic_store(ctl + 8 + s, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+      passed = 2u;
+      // every work-group: all of the row's keys in bin b1 (at most kResidentSegKeys)
+      if (wave == 0) {
+        const uint32_t c = lane < W ? __hip_atomic_load(ctl + 8 + lane, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0u;
+        const uint32_t incl = wave_incl_scan(c);
+        if (lane <= kRMaxW) sm.off[lane] = incl - c;
+      }
+      __syncthreads();
+      const uint32_t n = sm.off[W];
+      constexpr int kPer = kResidentSegKeys / kBlock;
+      uint32_t kk[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const uint32_t g = (uint32_t)tid + (uint32_t)(q * kBlock);
+        int sl = 0;
+        for (int t = 1; t < W; ++t) sl = g >= sm.off[t] ? t : sl;
+        const uint32_t at = min(g - sm.off[sl], (uint32_t)(kResidentSegKeys - 1));
+        const uint32_t k = __hip_atomic_load(R.lists + (size_t)(li * W + sl) * kResidentSegKeys + at,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        kk[q] = g < n ? k : 0u;
+      }
+      // level 2 in LDS: bits [20:10], copy lane % 4
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (kk[q] != 0u)
+          atomicAdd(&sm.hh[((kk[q] >> 10) & (uint32_t)(kRB2 - 1)) * 4u + (uint32_t)(lane & 3)],
+                    (unsigned long long)sig_of(kk[q]));
+      __syncthreads();
+      fold_masses<kRB2>(sm, e1);
+      __syncthreads();
+      clear_lds_hist(sm);
+      if (wave == 0) {
+        uint32_t b2;
+        double above, total;
+        mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+        if (lane == 0) {
+          sm.res[1] = b2;
+          sm.resd[0] = above;
+        }
+      }
+      __syncthreads();
+      const uint32_t pre2 = (b1 << 11) | sm.res[1];
+      const double above2 = sm.resd[0];
+      // level 3 in LDS: bits [9:0] of the keys with bits [30:10] == pre2
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (kk[q] != 0u && (kk[q] >> 10) == pre2)
+          atomicAdd(&sm.hh[(kk[q] & (uint32_t)(kRB3 - 1)) * 8u + (uint32_t)(lane & 7)],
+                    (unsigned long long)sig_of(kk[q]));
+      __syncthreads();
+      fold_masses<kRB3>(sm, e1);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t b3;
+        double above, total;
+        mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
+        if (lane == 0) {
+          sm.res[2] = b3;
+          sm.resd[0] = above1 + above2 + (above + sm.md[b3]);
+        }
+      }
+      __syncthreads();
+      tau = (pre2 << 10) | sm.res[2];
+      zkept = sm.resd[0];
     } else {
       // level 2: values in bin b1, by bits [20:10], copy lane % 4
 #pragma unroll
@@ -652,9 +818,9 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     const double Tl = sm.resd[3];
     fence_values<NV>(v);
     WalkPick pk;
-    wave_walk<NV>(v, vbase, nvec, tau, Tl, pk);
+    const double Te = wave_walk<NV>(v, vbase, nvec, tau, Tl, sm.md, pk);
     fence_values<NV>(v);
-    const int pos = pick_value<NV>(v, vbase, tau, Tl, pk);
+    const int pos = pick_value<NV>(v, vbase, tau, Te, pk);
     if (pk.j < 0) {
       if (lane == 0) stream::write_sample(P, i, -1, 0);
     } else if (lane == pk.l) {
@@ -692,6 +858,8 @@ hipError_t launch_res_one(const SampleParams& p, const RenormParams& rp, const S
   R.W = plan.W;
   R.L = plan.L;
   R.slots = reinterpret_cast<RowSlot*>(static_cast<char*>(workspace) + kCtlRegionBytes);
+  R.lists = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kCtlRegionBytes +
+                                        (size_t)kResidentSlots * kResidentSlotBytes);
   // outputs per launch: whole groups of eight (one per XCD), all resident
   const int per = min(plan.chunk, (cap / (8 * plan.W)) * 8);
   const int total = KIND == kResSample ? p.num_outputs : rp.rows;

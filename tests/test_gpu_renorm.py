@@ -72,6 +72,28 @@ def test_renorm_small_and_edge_parameters():
             _check_renorm(out[r], probs[r], *ref.top_p_renorm(probs[r], p))
 
 
+@pytest.mark.parametrize("p", [0.3, 0.95])
+def test_top_p_dense_boundary_bins(p):
+    """Near-uniform and slowly decaying rows put thousands of values into the
+    bin where the top-p mass crosses p * Z (more than a work-group's key list
+    holds), peaked rows put one: both ways of finding tau, for renormalisation
+    and for sampling."""
+    w = si.stress(rows=6, vocab=65536)
+    probs = w["probs"]
+    P = gpu(probs)
+    out = host(dss.top_p_renorm_probs(P, p))
+    for r in range(probs.shape[0]):
+        _check_renorm(out[r], probs[r], *ref.top_p_renorm(probs[r], p))
+    n = 2000
+    idx = np.repeat(np.arange(probs.shape[0], dtype=np.int32), n)
+    s = host(dss.top_p_sampling_from_probs(P, p, indices=gpu(idx), seed=5, offset=1))
+    for r in range(probs.shape[0]):
+        _, tau = ref.threshold(probs[r], "top_p", k=None, p=np.float32(p), min_p=None)
+        support = ref.support_mask(probs[r], tau)
+        got = s[r * n:(r + 1) * n]
+        assert (got >= 0).all() and support[got].all(), r
+
+
 @pytest.mark.parametrize("V", [1, 3, 7, 2049, 4101])
 def test_renorm_ragged_and_in_place(V):
     rng = np.random.default_rng(V + 5)
