@@ -44,16 +44,19 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
                   float min_p, int32_t* samples, uint8_t* valid, int32_t* rounds, uint32_t flags,
                   void* workspace, size_t workspace_bytes, void* stream) {
   if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
-  if (flags & DSS_FLAG_ORDER_JOINT) return DSS_ERR_UNSUPPORTED;
+  // the joint order only exists for the combined filter; the engines know it
+  // as an op of its own (the public op id still sizes the workspace)
+  if ((flags & DSS_FLAG_ORDER_JOINT) && op != dss::kOpTopKTopP) return DSS_ERR_UNSUPPORTED;
+  const int eop = (flags & DSS_FLAG_ORDER_JOINT) ? dss::kOpTopKTopPJoint : op;
   if (rows < 0 || vocab <= 0 || num_outputs < 0) return DSS_ERR_INVALID_ARG;
   if (vocab > DSS_MAX_VOCAB) return DSS_ERR_UNSUPPORTED;
   if (!indices && num_outputs != rows) return DSS_ERR_INVALID_ARG;
   if (num_outputs == 0) return DSS_OK;
   if (!probs || !samples) return DSS_ERR_INVALID_ARG;
   const int vec_ok = (vocab % 4 == 0) && aligned16(probs);
-  const dss::SplitPlan plan = dss::plan_split(op, rows, vocab, num_outputs, flags, vec_ok);
+  const dss::SplitPlan plan = dss::plan_split(eop, rows, vocab, num_outputs, flags, vec_ok);
   const dss::SplitPlan rplan = plan.W > 0 ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
-                                          : dss::plan_resident(op, vocab, num_outputs, flags, vec_ok);
+                                          : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok);
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   const int dev = check_device();
@@ -81,9 +84,9 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.vec_ok = vec_ok;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      plan.W > 0    ? dss::launch_split_sample(op, p, plan, workspace, st, timing_events())
-      : rplan.W > 0 ? dss::launch_resident_sample(op, p, rplan, workspace, st, timing_events())
-                    : dss::launch_stream_sample(op, p, st, timing_events());
+      plan.W > 0    ? dss::launch_split_sample(eop, p, plan, workspace, st, timing_events())
+      : rplan.W > 0 ? dss::launch_resident_sample(eop, p, rplan, workspace, st, timing_events())
+                    : dss::launch_stream_sample(eop, p, st, timing_events());
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 

@@ -18,6 +18,7 @@ enum Op : int {
   kOpTopP = 2,
   kOpMinP = 3,
   kOpTopKTopP = 4,  // top-k first, then top-p inside the top-k set
+  kOpTopKTopPJoint = 5,  // both checks in every round, top-p against the row's mass
 };
 
 // Everything a sampling kernel reads or writes.  Pointer fields are device

@@ -121,6 +121,8 @@ struct SplitSmem {
   uint32_t res[8];
   uint32_t fres[4];
   uint32_t tp;                    // provisional slice bound
+  double wz[kWaves];              // joint order: per-wave totals of the slice
+  double zs;                      // joint order: the slice's total, then the row's
   uint32_t wcnt[kWaves];          // vectors each wave staged (0xFFFFFFFF: overflow)
   int flag;
 };
@@ -312,8 +314,9 @@ struct MassView {
 };
 
 __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_above, double zb,
-                                                uint32_t eg, float pfrac, uint32_t tstar,
-                                                uint32_t sh, uint32_t bin1, MassView& mv) {
+                                                uint32_t eg, float pfrac, double zref,
+                                                uint32_t tstar, uint32_t sh, uint32_t bin1,
+                                                MassView& mv) {
   constexpr int kPer = kMassBins / kWave;  // bins per lane, the top ones in lane 0
   static_assert(kPer == 4, "one 16-byte read per lane");
   const int lane = lane_id();
@@ -332,7 +335,9 @@ __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_
   mv.sh = sh;
   mv.mb1 = bin1 >> kMassShift;
   mv.on = true;
-  const double zhi = lane63(incl) * (1.0 + 1e-12) + mv.slack + zb;
+  // an upper bound of the mass top-p compares with: Z_k, or (joint order,
+  // zref >= 0) the row's mass
+  const double zhi = zref >= 0.0 ? zref * (1.0 + 1e-12) : lane63(incl) * (1.0 + 1e-12) + mv.slack + zb;
   const double target = (double)pfrac * zhi * (1.0 + 1e-9);
   // suffix mass down to each of this lane's bins; the first (highest) bin
   // whose suffix provably reaches the target
@@ -351,7 +356,7 @@ __device__ __forceinline__ uint32_t top_p_start(const SplitSmem& sm, uint32_t n_
 
 template <int OP, int NR>
 __device__ int wave_loop(const SplitSmem& sm, int m, float low, float start, float high,
-                         float pfrac, uint64_t seed, uint64_t offset, uint64_t sid,
+                         float pfrac, double zrow, uint64_t seed, uint64_t offset, uint64_t sid,
                          const MassView& mv, int& rounds) {
   constexpr bool REG = NR > 0;
   const int lane = lane_id();
@@ -392,7 +397,8 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float start, flo
     zk += x > lk ? x : 0.0;
     part += x > lo ? x : 0.0;
   });
-  const double pz = (double)pfrac * wave_sum(zk);
+  // top-p against Z_k, or against the row's mass Z under the joint order
+  const double pz = (double)pfrac * (OP == kOpTopKTopPJoint ? zrow : wave_sum(zk));
   double incl = wave_incl_scan(part);  // prefix over lanes of the mass above lo
   double S = lane63(incl);
   int rnd = 0;
@@ -431,7 +437,7 @@ __device__ int wave_loop(const SplitSmem& sm, int m, float low, float start, flo
     // the bins from its own up bounds the mass above it from above; if that
     // bound is already below p * Z_k, f(pivot1) holds and the exact sums
     // would accept too, so the draw is accepted without them.
-    if (OP == kOpTopKTopP && mv.on) {
+    if ((OP == kOpTopKTopP || OP == kOpTopKTopPJoint) && mv.on) {
       const uint32_t mb = (((uint32_t)ent - mv.tstar) >> mv.sh) >> kMassShift;  // wave-uniform
       if (mb > mv.mb1 && mb < (uint32_t)kMassBins) {
         const uint32_t d = (uint32_t)kMassBins - 1u - mb;
@@ -494,7 +500,9 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
                                            SplitSmem& sm, int& out_i) {
   constexpr bool KEYS = KIND == kKindMask;    // logits: signed-order keys
   // top-k-then-top-p sampling keeps a mass histogram for the loop's start
-  constexpr bool kMass = KIND == kKindSample && OP == kOpTopKTopP;
+  constexpr bool kJoint = OP == kOpTopKTopPJoint;
+  constexpr bool kTopPPart = OP == kOpTopKTopP || kJoint;
+  constexpr bool kMass = KIND == kKindSample && kTopPPart;
   static_assert(kMassBins + kWave <= kBlock, "one clearing store per thread");
   constexpr uint32_t kSh = KEYS ? 21u : 20u;  // top eleven bits of a key
   const int W = S.W;
@@ -534,12 +542,12 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // no wait for them waits for the slice's vector loads)
   const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
   const float pp =
-      (OP == kOpTopKTopP) ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
+      kTopPPart ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
   const uint64_t seed =
       KIND != kKindSample ? 0ull : P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
   const uint64_t offset =
       KIND != kKindSample ? 0ull : P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
-  const bool ok = row_ok && k > 0 && (OP != kOpTopKTopP || !isnan(pp));
+  const bool ok = row_ok && k > 0 && (!kTopPPart || !isnan(pp));
   if (!ok || k > kSplitKCap) {
     // no hand-off for this output: slice 0 answers alone
     if (s != 0) return kDone;
@@ -587,8 +595,11 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   uint32_t key[NV];
   uint32_t mx = 0u;
   bool nan_seen = false;  // logits: a NaN invalidates the row
+  double zsum = 0.0;      // joint order: this thread's values, summed in a fixed order
   auto count = [&](int j) {
     const bool in = tid + j * kBlock < nvec;
+    if constexpr (kJoint)
+      zsum += in ? ((double)v[j].x + (double)v[j].y) + ((double)v[j].z + (double)v[j].w) : 0.0;
     const uint32_t m = max4_key<KEYS>(v[j]);
     key[j] = in ? m + 1u : 0u;
     mx = max(mx, in ? m : 0u);
@@ -651,6 +662,10 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     sm.wmax[wave] = mx;
     sm.wcnt[wave] = wovf ? 0xFFFFFFFFu : wp;
   }
+  if constexpr (kJoint) {
+    const double wz = wave_sum(zsum);
+    if (lane == 0) sm.wz[wave] = wz;
+  }
   if (KEYS) {
     const bool wn = __ballot(nan_seen) != 0ull;
     if (lane == 0) sm.wnan[wave] = wn ? 1u : 0u;
@@ -668,6 +683,11 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       sm.res[1] = smax;
       sm.res[2] = anynan ? 1u : 0u;
       sm.res[3] = (J0 > 0 && tp <= bnd && !ovf) ? 1u : 0u;
+      if (kJoint) {
+        double z = 0.0;
+        for (int w = 0; w < kWaves; ++w) z += sm.wz[w];
+        sm.zs = z;
+      }
     }
   }
   __syncthreads();
@@ -777,6 +797,11 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       h[3] = gen;
       h[4] = xcc_id();
       h[5] = bad ? 1u : 0u;
+      if (kJoint) {
+        const uint64_t zb = (uint64_t)__double_as_longlong(sm.zs);
+        h[6] = (uint32_t)zb;
+        h[7] = (uint32_t)(zb >> 32);
+      }
     }
     // hand-off: this work-group's stores reach the XCD's L2 before it arrives
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -807,7 +832,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     // one of them sits inside a branch; what they return is masked later.
     const uint32_t spec = min((uint32_t)(kLoadBatch * gsz), 2u * (publish ? nlist : 0u) + 128u);
     const bool mine = wave == 0 && lane < W;
-    uint32_t ht = 0u, hc = 0u, hm = 0u, hg = 0u, hx = 0u, hb = 0u;
+    uint32_t ht = 0u, hc = 0u, hm = 0u, hg = 0u, hx = 0u, hb = 0u, hz0 = 0u, hz1 = 0u;
     if (wave == 0) {
       const gptr<uint32_t> h =
           as_global(S.hdr + ((int64_t)li * W + (lane & (W - 1))) * kHdrWords);
@@ -817,6 +842,10 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       hb = __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (kJoint) {
+        hz0 = __hip_atomic_load(h + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hz1 = __hip_atomic_load(h + 7, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     uint64_t e8[kLoadBatch];
 #pragma unroll
@@ -840,6 +869,12 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       const uint32_t ts = wave_max(ht);
       const uint32_t nmax = wave_max(cc);
       if (lane <= kMaxSlices) sm.off[lane] = lane < W ? incl - cc : all;
+      if (kJoint) {  // the row's mass: the slices' totals in slice order
+        const double z =
+            mine ? __longlong_as_double((long long)(((uint64_t)hz1 << 32) | hz0)) : 0.0;
+        const double zr = lane63(wave_incl_scan(z));
+        if (lane == 0) sm.zs = zr;
+      }
       if (lane == 0) {
         uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back
         if (foreign) status = 2u;
@@ -1033,28 +1068,30 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   }
 
   // ---- the dual-pivot loop on wave 0 ----------------------------------------
-  const float pfrac = OP == kOpTopKTopP ? stream::clamp01(pp) : 0.0f;
+  const float pfrac = kTopPPart ? stream::clamp01(pp) : 0.0f;
   const uint32_t lowk = tau_k > 0u ? tau_k - 1u : 0u;
   uint32_t startk = lowk;
   MassView mv;
   mv.on = false;
   if (kMass) {
     const uint32_t L =
-        top_p_start(sm, n_above, wave_sum(zb), gmax >> 23, pfrac, tstar, sh, bin1, mv);
+        top_p_start(sm, n_above, wave_sum(zb), gmax >> 23, pfrac, kJoint ? sm.zs : -1.0, tstar,
+                    sh, bin1, mv);
     startk = max(startk, L);
   }
   const float low = __uint_as_float(lowk), start = __uint_as_float(startk);
   int rounds = 0;
   const float high = __uint_as_float(gmax);
+  const double zrow = kJoint ? sm.zs : 0.0;
   int e;
   if (m <= 4 * kWave) {
-    e = wave_loop<OP, 4>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
+    e = wave_loop<OP, 4>(sm, (int)m, low, start, high, pfrac, zrow, seed, offset, sid, mv, rounds);
   } else if (m <= 8 * kWave) {
-    e = wave_loop<OP, 8>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
+    e = wave_loop<OP, 8>(sm, (int)m, low, start, high, pfrac, zrow, seed, offset, sid, mv, rounds);
   } else if (m <= 16 * kWave) {
-    e = wave_loop<OP, 16>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
+    e = wave_loop<OP, 16>(sm, (int)m, low, start, high, pfrac, zrow, seed, offset, sid, mv, rounds);
   } else {  // (32 float64 entries per lane in registers would spill the kernel)
-    e = wave_loop<OP, 0>(sm, (int)m, low, start, high, pfrac, seed, offset, sid, mv, rounds);
+    e = wave_loop<OP, 0>(sm, (int)m, low, start, high, pfrac, zrow, seed, offset, sid, mv, rounds);
   }
   if (lane == 0) stream::write_sample(P, i, e, e >= 0 ? rounds : 0);
   return kDone;
@@ -1155,7 +1192,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flags, int vec_ok) {
   SplitPlan plan{0, 0, 0, 0, 0, 0};
   (void)rows;
-  if (op != kOpTopK && op != kOpTopKTopP) return plan;
+  if (op != kOpTopK && op != kOpTopKTopP && op != kOpTopKTopPJoint) return plan;
   if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO)) return plan;
   if (!vec_ok || vocab < 1024 || num_outputs <= 0) return plan;
   const int wmin = (vocab + kMaxSliceLen - 1) / kMaxSliceLen;
@@ -1231,6 +1268,8 @@ hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& p
     const bool first = out0 == 0, last = out0 + plan.chunk >= p.num_outputs;
     if (op == kOpTopK) {
       launch_nv<kKindSample, kOpTopK>(plan.nv, p, sp, rp, s, ev, first, last);
+    } else if (op == kOpTopKTopPJoint) {
+      launch_nv<kKindSample, kOpTopKTopPJoint>(plan.nv, p, sp, rp, s, ev, first, last);
     } else {
       launch_nv<kKindSample, kOpTopKTopP>(plan.nv, p, sp, rp, s, ev, first, last);
     }

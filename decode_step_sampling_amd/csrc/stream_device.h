@@ -339,7 +339,8 @@ __device__ inline void pivot_pass(const RowRef& r, int n_tiles, float a, float b
 
 // f(t) of the blog's dual-pivot section: 1 iff threshold t already
 // satisfies the filter.  Top-k counts the values above t, top-p compares
-// their mass with p * Z_C (Z_C = row or top-k mass), min-p compares t with
+// their mass with p * Z_C (Z_C = the row's mass for top-p and for the joint
+// order, the top-k set's for top-k-then-top-p), min-p compares t with
 // min_p * max; "count == 0" makes f(max) = 1 also for p = 0.
 template <int OP>
 __device__ __forceinline__ bool predicate(float t, double mass_above, uint32_t count_above,
@@ -371,8 +372,8 @@ __device__ __forceinline__ void sample_row(const SampleParams& P, int i, SampleS
   const float pp = P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
   const float mp = P.min_p_arr ? as_global(P.min_p_arr)[i] : P.min_p;
   bool ok = row >= 0 && row < P.rows;
-  if (OP == kOpTopK || OP == kOpTopKTopP) ok = ok && k > 0;
-  if (OP == kOpTopP || OP == kOpTopKTopP) ok = ok && !isnan(pp);
+  if (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint) ok = ok && k > 0;
+  if (OP == kOpTopP || OP == kOpTopKTopP || OP == kOpTopKTopPJoint) ok = ok && !isnan(pp);
   if (OP == kOpMinP) ok = ok && !isnan(mp);
   if (!ok) {  // block-uniform
     if (threadIdx.x == 0) write_sample(P, i, -1, 0);
@@ -434,7 +435,10 @@ __device__ __forceinline__ void sample_row(const SampleParams& P, int i, SampleS
     const uint32_t tau_k = threshold_search<false, false>(r, 0u, maxbits + 1u, (uint32_t)k, 0.0, sm.red);
     zc = mass_at_least(r, tau_k, sm.red).d0;
   }
-  const double pz = (OP == kOpTopP || OP == kOpTopKTopP) ? (double)clamp01(pp) * zc : 0.0;
+  // (the joint order compares with the row's own mass: zc stays Z)
+  const double pz = (OP == kOpTopP || OP == kOpTopKTopP || OP == kOpTopKTopPJoint)
+                        ? (double)clamp01(pp) * zc
+                        : 0.0;
   const double minp_thr = (OP == kOpMinP) ? (double)clamp01(mp) * (double)M : 0.0;
 
   float low = 0.0f, high = M;

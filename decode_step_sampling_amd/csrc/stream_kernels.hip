@@ -48,6 +48,9 @@ hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s, co
     case kOpTopKTopP:
       launch_kernel(stream_sample_kernel<kOpTopKTopP>, grid, block, s, ev, true, true, p);
       break;
+    case kOpTopKTopPJoint:
+      launch_kernel(stream_sample_kernel<kOpTopKTopPJoint>, grid, block, s, ev, true, true, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

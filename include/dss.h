@@ -99,8 +99,9 @@ extern "C" {
 #define DSS_MAX_VOCAB  (1 << 20)
 
 /* flags */
-#define DSS_FLAG_ORDER_JOINT   0x1u  /* joint top-k/top-p order: not built, returns
-                                        DSS_ERR_UNSUPPORTED ([Blog] footnote 1) */
+#define DSS_FLAG_ORDER_JOINT   0x1u  /* joint top-k/top-p order ([Blog] footnote 1):
+                                        top_k_top_p sampling only, any other op
+                                        returns DSS_ERR_UNSUPPORTED */
 #define DSS_FLAG_FROM_ZERO     0x2u  /* run the rejection loop exactly as the
                                         blog's listing starts it: low = 0,
                                         high = max, whole row (no certified
@@ -165,7 +166,11 @@ int dss_min_p_sampling_from_probs(const float* probs, int32_t rows, int32_t voca
                                   size_t workspace_bytes, void* stream);
 
 /* Fused top-k-then-top-p sampling ([Blog] footnote 1 "Top-K First"; [Expl
- * "Top-k 与 top-p 的组合顺序会改变分布"]).  DSS_FLAG_ORDER_JOINT is rejected. */
+ * "Top-k 与 top-p 的组合顺序会改变分布"]): top-p applies inside the top-k set,
+ * its mass target p * Z_k.  With DSS_FLAG_ORDER_JOINT both checks run
+ * together in every rejection round ([Blog] footnote 1 "Joint"; [Expl], same
+ * section) and the top-p target is p times the whole row's mass: the kept
+ * set is {x >= max(tau_k, tau_p)}, tau_p the top-p threshold of the row. */
 int dss_top_k_top_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
                                         const int32_t* indices, int32_t num_outputs,
                                         const uint64_t* seed_arr, uint64_t seed,

@@ -40,6 +40,12 @@ Readings of the pages (each also listed in the design doc):
   invalid; sampling reports token -1 with valid = 0, renorm reports a NaN row.
 * R6 min-p threshold is min_p * max as an exact product ([Blog] "Min-P",
   [Expl] "Min-p"); kept set {x >= min_p * max}.
+* R17 the "joint" order ([Blog] footnote on the filter options; [Expl]
+  "Top-k 与 top-p 的组合顺序会改变分布") checks the top-k and the top-p
+  condition together in every rejection round; the top-p condition then
+  refers to the whole row's mass (there is no top-k stage before it), so the
+  kept set is where both hold: {x >= max(tau_k, tau_p)} with tau_p taken on
+  the whole row.
 """
 
 from bisect import bisect_left, bisect_right
@@ -50,7 +56,9 @@ import numpy as np
 
 SCALE_EXP = 149          # x * 2**149 is an integer for every float32 x >= 0
 
-OPS = ("none", "top_k", "top_p", "min_p", "top_k_top_p")
+OPS = ("none", "top_k", "top_p", "min_p", "top_k_top_p", "top_k_top_p_joint")
+K_OPS = ("top_k", "top_k_top_p", "top_k_top_p_joint")
+P_OPS = ("top_p", "top_k_top_p", "top_k_top_p_joint")
 
 
 # ----------------------------------------------------------------------------
@@ -158,9 +166,9 @@ def threshold(row, op, k=None, p=None, min_p=None):
         return False, None
     if op == "none":
         return True, 0.0
-    if op in ("top_k", "top_k_top_p") and int(k) <= 0:
+    if op in K_OPS and int(k) <= 0:
         return False, None
-    if op in ("top_p", "top_k_top_p") and np.isnan(np.float32(p)):
+    if op in P_OPS and np.isnan(np.float32(p)):
         return False, None
     if op == "min_p" and np.isnan(np.float32(min_p)):
         return False, None
@@ -173,6 +181,10 @@ def threshold(row, op, k=None, p=None, min_p=None):
         tk = tau_top_k(row, k)
         n_c = _count_at_least(s, tk)
         return True, tau_top_p(s, n_c, clamp01(p))
+    if op == "top_k_top_p_joint":
+        # both conditions at once (R17): the larger of the two thresholds,
+        # the top-p one against the whole row
+        return True, max(tau_top_k(row, k), tau_top_p(s, s.size, clamp01(p)))
     if op == "min_p":
         # exact: a product of two float32 numbers fits a float64 exactly
         return True, float(np.float64(clamp01(min_p)) * np.float64(s[0]))
@@ -311,10 +323,12 @@ class Predicate:
       top_p:        sum_{x > t} x < p * Z_C   or  #{x > t} = 0
       min_p:        t >= min_p * max
       top_k_top_p:  top_k(t)  and  (sum_{x > t} x < p * Z_k  or  #{x > t} = 0)
+      top_k_top_p_joint:
+                    top_k(t)  and  (sum_{x > t} x < p * Z_C  or  #{x > t} = 0)
       none:         always 1
 
-    Z_C is the whole row's exact mass, Z_k that of {x >= tau_k} (R2).  The
-    "#{x > t} = 0" clause makes f(max) = 1 also when p = 0.
+    Z_C is the whole row's exact mass, Z_k that of {x >= tau_k} (R2, R17).
+    The "#{x > t} = 0" clause makes f(max) = 1 also when p = 0.
     """
 
     def __init__(self, row, op, k=None, p=None, min_p=None):
@@ -322,9 +336,9 @@ class Predicate:
         self.op = op
         self.units = exact_units(self.row)
         self.k = None if k is None else int(k)
-        if op in ("top_p", "top_k_top_p"):
+        if op in P_OPS:
             self.p_num, self.p_den = fraction_of(clamp01(p)).as_integer_ratio()
-        if op == "top_p":
+        if op in ("top_p", "top_k_top_p_joint"):
             self.z_c = sum(self.units)
         if op == "top_k_top_p":
             tk = tau_top_k(self.row, self.k)

@@ -82,7 +82,12 @@ def test_sampling_validation_before_any_hip_call():
     assert _plain(lib, rows=2, n=3) == _lib.DSS_ERR_INVALID_ARG      # n != rows, no indices
     assert _plain(lib, vocab=_lib.DSS_MAX_VOCAB + 1) == _lib.DSS_ERR_UNSUPPORTED
     assert _plain(lib, flags=0x100) == _lib.DSS_ERR_INVALID_ARG
-    assert _topk_topp(lib, flags=_lib.DSS_FLAG_ORDER_JOINT) == _lib.DSS_ERR_UNSUPPORTED
+    # the joint order belongs to the combined filter only; there it is
+    # validated and sized like top-k-first
+    assert _plain(lib, flags=_lib.DSS_FLAG_ORDER_JOINT) == _lib.DSS_ERR_UNSUPPORTED
+    assert _topk_topp(lib, flags=_lib.DSS_FLAG_ORDER_JOINT, vocab=0) == _lib.DSS_ERR_INVALID_ARG
+    assert _topk_topp(lib, flags=_lib.DSS_FLAG_ORDER_JOINT, vocab=4096) == _lib.DSS_ERR_WORKSPACE
+    assert _topk_topp(lib, vocab=4096) == _lib.DSS_ERR_WORKSPACE
     # empty batches are a successful no-op and touch nothing
     assert _plain(lib, probs=NULL, samples=NULL, rows=0, n=0) == _lib.DSS_OK
     assert _plain(lib, probs=NULL, samples=NULL, rows=3, n=0, indices=FAKE) == _lib.DSS_OK

@@ -29,6 +29,8 @@ OPS = {
     "min_p": lambda P, prm, **kw: dss.min_p_sampling_from_probs(P, prm["mp"], **kw),
     "top_k_top_p": lambda P, prm, **kw: dss.top_k_top_p_sampling_from_probs(
         P, prm["k"], prm["p"], **kw),
+    "top_k_top_p_joint": lambda P, prm, **kw: dss.top_k_top_p_sampling_from_probs(
+        P, prm["k"], prm["p"], filter_apply_order="joint", **kw),
 }
 
 FLAG_SETS = [0, dss.DSS_FLAG_FROM_ZERO, dss.DSS_FLAG_STREAMING]
@@ -41,8 +43,8 @@ def _scalar_params(k=50, p=0.9, mp=0.1):
 def _oracle_kw(op, prm, i=None):
     def pick(v):
         return v if (i is None or np.ndim(v) == 0) else v[i]
-    return {"k": pick(prm["k"]) if op in ("top_k", "top_k_top_p") else None,
-            "p": pick(prm["p"]) if op in ("top_p", "top_k_top_p") else None,
+    return {"k": pick(prm["k"]) if op in ref.K_OPS else None,
+            "p": pick(prm["p"]) if op in ref.P_OPS else None,
             "min_p": pick(prm["mp"]) if op == "min_p" else None}
 
 
@@ -88,7 +90,7 @@ def test_plain_sampling_token_exact_full_vocab():
     assert np.array_equal(s, expect)
 
 
-@pytest.mark.parametrize("op", ["top_k", "top_p", "min_p", "top_k_top_p"])
+@pytest.mark.parametrize("op", ["top_k", "top_p", "min_p", "top_k_top_p", "top_k_top_p_joint"])
 def test_rejection_loop_token_exact_from_zero(small, op):
     """From low = 0 the GPU loop and the oracle's step-by-step model of the
     blog's dual-pivot procedure draw the same tokens in the same rounds."""
@@ -111,7 +113,8 @@ def test_rejection_loop_token_exact_from_zero(small, op):
 # support and distribution (small workload: B=4, V=32000, top_k=50, top_p=0.9)
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("op", ["top_k_top_p", "top_k", "top_p", "min_p", "none"])
+@pytest.mark.parametrize("op", ["top_k_top_p", "top_k_top_p_joint", "top_k", "top_p", "min_p",
+                                "none"])
 @pytest.mark.parametrize("flags", [0, dss.DSS_FLAG_FROM_ZERO])
 def test_chi_square_per_row(small, op, flags):
     probs = small["probs"]
@@ -158,7 +161,8 @@ def test_chi_square_across_calls(small):
 # top_p ~ U[0.5, 0.95]: every draw must lie in the oracle's kept set
 # ----------------------------------------------------------------------------
 
-def test_headline_support_full_size():
+@pytest.mark.parametrize("order", ["top_k_first", "joint"])
+def test_headline_support_full_size(order):
     w = si.renorm()
     probs = w["probs"]
     rows = probs.shape[0]
@@ -166,8 +170,9 @@ def test_headline_support_full_size():
     k_t, p_t = gpu(w["top_k"]), gpu(w["top_p"])
     seeds = u64(w["seeds"])
     supports = []
+    op = "top_k_top_p" if order == "top_k_first" else "top_k_top_p_joint"
     for row in range(rows):
-        valid, tau = ref.threshold(probs[row], "top_k_top_p", k=w["top_k"][row], p=w["top_p"][row])
+        valid, tau = ref.threshold(probs[row], op, k=w["top_k"][row], p=w["top_p"][row])
         assert valid
         supports.append(ref.support_mask(probs[row], tau))
     rounds_all = []
@@ -175,7 +180,7 @@ def test_headline_support_full_size():
         for call in range(40):
             s, v, r = dss.top_k_top_p_sampling_from_probs(P, k_t, p_t, seed=seeds, offset=call,
                                                           return_valid=True, return_rounds=True,
-                                                          flags=flags)
+                                                          flags=flags, filter_apply_order=order)
             s, v, r = host(s), host(v), host(r)
             assert (v == 1).all()
             for row in range(rows):

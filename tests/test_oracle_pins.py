@@ -113,6 +113,14 @@ def test_expl_order_example():
     valid, tau = ref.threshold(top3, "top_p",
                                p=np.float32(g["derived_top_p"] / float(top3.sum())))
     assert list(np.nonzero(ref.kept_mask(top3, tau))[0]) == g["raw_mass_reading_kept"]
+    # the joint order (R17) checks both conditions against the whole row: with
+    # p = 0.75 the row prefix .4 + .3 = .7 is still short of .75, so C stays
+    # (the raw-mass set); with p = 0.6 the prefix .7 reaches .6 at B, and top-3
+    # is looser, so {A, B}.  Derived from the definitions, not printed.
+    for p, kept in ((g["derived_top_p"], g["raw_mass_reading_kept"]), (g["top_p"], [0, 1])):
+        valid, tau = ref.threshold(row, "top_k_top_p_joint", k=g["top_k"], p=p)
+        assert valid
+        assert list(np.nonzero(ref.kept_mask(row, tau))[0]) == kept
 
 
 # ----------------------------------------------------------------------------
@@ -181,12 +189,30 @@ def test_predicate_equals_threshold_indicator():
         mp = float(np.float32(rng.uniform(0, 1)))
         vals = sorted(set(float(x) for x in row) | {0.0})
         probes = vals + [(a + b) / 2 for a, b in zip(vals, vals[1:])]
-        for op in ("top_k", "top_p", "min_p", "top_k_top_p"):
+        for op in ("top_k", "top_p", "min_p", "top_k_top_p", "top_k_top_p_joint"):
             _, tau = ref.threshold(row, op, k=k, p=p, min_p=mp)
             f = ref.Predicate(row, op, k=k, p=p, min_p=mp)
             for t in probes:
                 t32 = np.float32(t)
                 assert f(t32) == (float(t32) >= tau), (row, op, k, p, mp, t)
+
+
+def test_joint_order_special_cases():
+    """Joint with k >= V is top-p on the row; with p >= 1 it is top-k; joint
+    keeps a superset of top-k-then-top-p (its top-p mass target p * Z_C is at
+    least p * Z_k)."""
+    rng = np.random.default_rng(21)
+    for row in _tiny_rows(5, 150):
+        k = int(rng.integers(1, row.size + 1))
+        p = float(np.float32(rng.choice([0.0, 0.3, 0.7, 1.0, rng.uniform()])))
+        _, tj = ref.threshold(row, "top_k_top_p_joint", k=row.size + 3, p=p)
+        assert tj == ref.threshold(row, "top_p", p=p)[1]
+        _, tj = ref.threshold(row, "top_k_top_p_joint", k=k, p=1.0)
+        assert set(np.nonzero(ref.support_mask(row, tj))[0]) == \
+            set(np.nonzero(ref.support_mask(row, ref.threshold(row, "top_k", k=k)[1]))[0])
+        _, tj = ref.threshold(row, "top_k_top_p_joint", k=k, p=p)
+        _, tf = ref.threshold(row, "top_k_top_p", k=k, p=p)
+        assert ref.kept_mask(row, tj)[ref.kept_mask(row, tf)].all()
 
 
 def test_k_extremes_and_min_p_closed_form():
