@@ -235,6 +235,20 @@ def extra_configs(dss, si, lib, dev):
                       "p99": float(np.percentile(x, 99)), "max": int(x.max())}
     out["stress B=512 V=256000 top_k_top_p (k=1000, p=0.95)"] = entry(t, B * V * 4,
                                                                       rounds=hist)
+    # the pages' tail argument: rounds of the loop run from low = 0 with the
+    # second pivot (dual) and without it (single), same rows, same streams
+    cmp = {}
+    for name, fl in (("dual_pivot", dss.DSS_FLAG_FROM_ZERO), ("single_pivot", dss.DSS_FLAG_SINGLE_PIVOT)):
+        _, _, r = dss.top_k_top_p_sampling_from_probs(P, 1000, 0.95, seed=seeds, offset=7,
+                                                      return_valid=True, return_rounds=True,
+                                                      flags=fl)
+        r = r.cpu().numpy()
+        cmp[name] = {}
+        for gi, gname in enumerate(("near-uniform", "peaked", "geometric")):
+            x = r[w["groups"] == gi]
+            cmp[name][gname] = {"mean": float(x.mean()), "p99": float(np.percentile(x, 99)),
+                                "max": int(x.max())}
+    out["stress rounds from low = 0: dual vs single pivot"] = cmp
     return out
 
 

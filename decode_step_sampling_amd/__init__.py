@@ -16,7 +16,8 @@ with one value per output, read as unsigned 64-bit.
 import torch
 
 from . import _lib
-from ._lib import (DSS_FLAG_FROM_ZERO, DSS_FLAG_ORDER_JOINT, DSS_FLAG_STREAMING,  # noqa: F401
+from ._lib import (DSS_FLAG_FROM_ZERO, DSS_FLAG_ORDER_JOINT, DSS_FLAG_SINGLE_PIVOT,  # noqa: F401
+                   DSS_FLAG_STREAMING,
                    DssError, OP_IDS)
 
 __all__ = [
@@ -24,6 +25,7 @@ __all__ = [
     "min_p_sampling_from_probs", "top_k_top_p_sampling_from_probs",
     "top_k_renorm_probs", "top_p_renorm_probs", "top_k_mask_logits",
     "DssError", "DSS_FLAG_FROM_ZERO", "DSS_FLAG_STREAMING", "DSS_FLAG_ORDER_JOINT",
+    "DSS_FLAG_SINGLE_PIVOT",
 ]
 
 _U64_MASK = (1 << 64) - 1

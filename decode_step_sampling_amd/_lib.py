@@ -21,6 +21,7 @@ DSS_MAX_VOCAB = 1 << 20
 DSS_FLAG_ORDER_JOINT = 0x1
 DSS_FLAG_FROM_ZERO = 0x2
 DSS_FLAG_STREAMING = 0x4
+DSS_FLAG_SINGLE_PIVOT = 0x8
 
 OP_IDS = {
     "sampling_from_probs": 0,

@@ -82,6 +82,7 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.valid = valid;
   p.rounds = rounds;
   p.vec_ok = vec_ok;
+  p.single_pivot = (flags & DSS_FLAG_SINGLE_PIVOT) ? 1 : 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
       plan.W > 0    ? dss::launch_split_sample(eop, p, plan, workspace, st, timing_events())

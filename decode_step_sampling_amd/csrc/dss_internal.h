@@ -43,6 +43,7 @@ struct SampleParams {
   uint8_t* valid;
   int32_t* rounds;
   int32_t vec_ok;   // rows may be read with 16-byte loads
+  int32_t single_pivot;  // streaming loop: low <- pivot1 after each rejection
 };
 
 enum RenormKind : int { kRenormTopK = 0, kRenormTopP = 1, kMaskLogits = 2 };

@@ -894,7 +894,7 @@ hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const Sp
 SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok) {
   SplitPlan plan{0, 0, 0, 0, 0, 0};
   if (op != kOpNone && op != kOpTopP && op != kOpMinP) return plan;
-  if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO)) return plan;
+  if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO | DSS_FLAG_SINGLE_PIVOT)) return plan;
   if (!vec_ok || vocab < 1024 || num_outputs <= 0) return plan;
   constexpr int kMaxSlice = kRMaxNv * 4 * kBlock;
   const int wmin = (vocab + kMaxSlice - 1) / kMaxSlice;

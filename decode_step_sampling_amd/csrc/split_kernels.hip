@@ -1193,7 +1193,7 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
   SplitPlan plan{0, 0, 0, 0, 0, 0};
   (void)rows;
   if (op != kOpTopK && op != kOpTopKTopP && op != kOpTopKTopPJoint) return plan;
-  if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO)) return plan;
+  if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO | DSS_FLAG_SINGLE_PIVOT)) return plan;
   if (!vec_ok || vocab < 1024 || num_outputs <= 0) return plan;
   const int wmin = (vocab + kMaxSliceLen - 1) / kMaxSliceLen;
   const int wt = (256 + num_outputs - 1) / num_outputs;

@@ -478,7 +478,11 @@ __device__ __forceinline__ void sample_row(const SampleParams& P, int i, SampleS
     const double Ma = sm.bc_d[0], Mb = sm.bc_d[1];
     __syncthreads();
     if (predicate<OP>(pivot1, Ma, cr.s0, k, pz, minp_thr)) break;  // accept
-    if (predicate<OP>(pivot2, Mb, cr.s1, k, pz, minp_thr)) {
+    if (P.single_pivot) {  // single pivot: only the rejected value moves low
+      low = pivot1;
+      S = Ma;
+      cur = ia;
+    } else if (predicate<OP>(pivot2, Mb, cr.s1, k, pz, minp_thr)) {
       low = pivot1;
       high = pivot2;
       S = Ma;

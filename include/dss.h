@@ -108,7 +108,14 @@ extern "C" {
                                         starting interval, no split rows)     */
 #define DSS_FLAG_STREAMING     0x4u  /* force the one-work-group-per-row
                                         streaming engine                       */
-#define DSS_FLAGS_ALL          0x7u
+#define DSS_FLAG_SINGLE_PIVOT  0x8u  /* sampling ops: single-pivot rounds
+                                        ([Blog] "拒绝采样"; [Expl] "如何在不知道
+                                        top-k 边界时拒绝错误样本"): from low = 0,
+                                        low <- the rejected value, streaming
+                                        engine; for comparing round counts
+                                        with the dual-pivot loop.  Ignored by
+                                        the renorm / mask ops                 */
+#define DSS_FLAGS_ALL          0xFu
 
 /* op ids for dss_workspace_size */
 #define DSS_OP_SAMPLING          0

@@ -412,6 +412,63 @@ def dual_pivot_sample(row, op, stream, k=None, p=None, min_p=None,
     raise RuntimeError("dual-pivot model did not terminate")
 
 
+def single_pivot_sample(row, op, stream, k=None, p=None, min_p=None, max_rounds=1000000):
+    """One draw by single-pivot rejection sampling ([Blog] "拒绝采样"; [Expl]
+    "如何在不知道 top-k 边界时拒绝错误样本"):
+
+      low <- 0
+      repeat: draw j from the tokens with p_j > low by inverse transform;
+              f(p_j) = 1 -> return j;  otherwise low <- p_j
+
+    Same stream, predicate and draw rule as ``dual_pivot_sample``; returns
+    (token, rounds), (-1, 0) for an invalid row or parameter.
+    """
+    row = np.asarray(row, dtype=np.float32)
+    valid, _ = threshold(row, op, k=k, p=p, min_p=min_p)
+    if not valid:
+        return -1, 0
+    f = Predicate(row, op, k=k, p=p, min_p=min_p)
+    low = np.float32(0.0)
+    for rounds in range(1, max_rounds + 1):
+        j = inverse_transform(row, row > low, stream.next())
+        if f(row[j]):
+            return j, rounds
+        low = row[j]
+    raise RuntimeError("single-pivot model did not terminate")
+
+
+def single_pivot_law(row, op, k=None, p=None, min_p=None):
+    """Exact output law and expected round count of ``single_pivot_sample``
+    (enumeration over every reachable low with exact rationals; tiny rows)."""
+    row = np.asarray(row, dtype=np.float32)
+    f = Predicate(row, op, k=k, p=p, min_p=min_p)
+    units = f.units
+    memo = {}
+
+    def solve(low):
+        key = float(low)
+        if key in memo:
+            return memo[key]
+        cand = [i for i in range(row.size) if row[i] > low]
+        s = sum(units[i] for i in cand)
+        law, rounds = {}, Fraction(1)
+        for i in cand:
+            w = Fraction(units[i], s)
+            if w == 0:
+                continue
+            if f(row[i]):
+                law[i] = law.get(i, Fraction(0)) + w
+                continue
+            sub_law, sub_rounds = solve(row[i])
+            for j, q in sub_law.items():
+                law[j] = law.get(j, Fraction(0)) + w * q
+            rounds += w * sub_rounds
+        memo[key] = (law, rounds)
+        return law, rounds
+
+    return solve(np.float32(0.0))
+
+
 def dual_pivot_law(row, op, k=None, p=None, min_p=None):
     """Exact output law and expected round count of ``dual_pivot_sample``.
 

@@ -109,6 +109,25 @@ def test_rejection_loop_token_exact_from_zero(small, op):
     assert (v == 1).all()
 
 
+@pytest.mark.parametrize("op", ["top_k", "top_p", "min_p", "top_k_top_p", "top_k_top_p_joint"])
+def test_single_pivot_token_exact(small, op):
+    """The single-pivot variant (low <- the rejected value) against the
+    oracle's model of the same procedure: same tokens, same round counts."""
+    probs = small["probs"]
+    n = 32
+    idx = (np.arange(n) % probs.shape[0]).astype(np.int32)
+    prm = _scalar_params(k=50, p=0.9, mp=0.1)
+    seed, offset = 777, 5
+    s, v, r = OPS[op](small["P"], prm, indices=gpu(idx), seed=seed, offset=offset,
+                      return_valid=True, return_rounds=True, flags=dss.DSS_FLAG_SINGLE_PIVOT)
+    s, v, r = host(s), host(v), host(r)
+    for i in range(n):
+        tok, rounds = ref.single_pivot_sample(probs[idx[i]], op, ph.Stream(seed, offset, i),
+                                              **_oracle_kw(op, prm))
+        assert (s[i], r[i]) == (tok, rounds), (i, op)
+    assert (v == 1).all()
+
+
 # ----------------------------------------------------------------------------
 # support and distribution (small workload: B=4, V=32000, top_k=50, top_p=0.9)
 # ----------------------------------------------------------------------------

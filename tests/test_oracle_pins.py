@@ -289,6 +289,29 @@ def test_dual_pivot_law_equals_target():
     assert checked > 300
 
 
+def test_single_pivot_law_equals_target():
+    """Exact enumeration of the single-pivot procedure also gives p~ exactly
+    (every rejection only removes values below the kept set)."""
+    rng = np.random.default_rng(9)
+    checked = 0
+    for row in _tiny_rows(4, 120):
+        if row.size > 7:
+            continue
+        k = int(rng.integers(1, row.size + 1))
+        p = float(np.float32(rng.choice([0.0, 0.4, 0.9, 1.0, rng.uniform()])))
+        mp = float(np.float32(rng.uniform(0, 1)))
+        for op in ref.OPS:
+            _, tau = ref.threshold(row, op, k=k, p=p, min_p=mp)
+            law, rounds = ref.single_pivot_law(row, op, k=k, p=p, min_p=mp)
+            units = ref.exact_units(row)
+            sup = ref.support_mask(row, tau)
+            z = sum(u for u, s_ in zip(units, sup) if s_)
+            assert law == {i: Fraction(units[i], z) for i in range(row.size) if sup[i]}
+            assert rounds >= 1
+            checked += 1
+    assert checked > 200
+
+
 def test_round_halving():
     """Each rejected round at least halves high - low (blog, Fig. 4 text)."""
     rng = np.random.default_rng(9)
