@@ -25,11 +25,23 @@
  *   of at least dss_workspace_size(...) bytes (NULL is fine when that is 0):
  *   the split-row engine's hand-off area (top-k and top-k-then-top-p
  *   sampling) and its per-row results (top-k renormalisation and top-k logit
- *   masking).  It must be zero-filled once when it is allocated; every call
- *   leaves its arrival counters at zero again when its kernels end (the rest
- *   is written before it is read), so a workspace can be reused by later
- *   calls on the same stream without clearing.  Two calls that run
- *   concurrently (different streams) need different workspaces.
+ *   masking), and the resident engine's per-output control blocks and key
+ *   lists (plain, top-p and min-p sampling, top-p renormalisation).  It must
+ *   be zero-filled once when it is allocated; every call leaves its counters
+ *   and control blocks at zero again when its kernels end (the rest is
+ *   written before it is read), so a workspace can be reused by later calls
+ *   on the same stream without clearing.  Two calls that run concurrently
+ *   (different streams) need different workspaces.
+ *
+ * Co-residency.  The resident engine's work-groups of one output wait for
+ *   each other inside the kernel, so each of its launches holds no more
+ *   work-groups than the device keeps resident at once.  Work that runs
+ *   concurrently on other streams can still hold compute units; a
+ *   work-group that waits more than 50 ms reports its output invalid
+ *   (sample -1, valid 0; renorm rows NaN) instead of hanging, and leaves its
+ *   control block dirty (zero the workspace again before reusing it).
+ *   Callers that overlap other kernels with these ops can pass
+ *   DSS_FLAG_STREAMING, whose engine never waits.
  *
  * Outputs of the sampling ops (length num_outputs):
  *   samples[i]  token id in [0, vocab), or -1 when output i is invalid;
