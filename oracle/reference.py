@@ -40,6 +40,10 @@ Readings of the pages (each also listed in the design doc):
   invalid; sampling reports token -1 with valid = 0, renorm reports a NaN row.
 * R6 min-p threshold is min_p * max as an exact product ([Blog] "Min-P",
   [Expl] "Min-p"); kept set {x >= min_p * max}.
+* R18 logits with a temperature: the max is subtracted before the exponent
+  (an identity of the formula, needed for range); differences, scaling by
+  1/T, exponentials and their sum in float64, each probability rounded once
+  to float32; the probabilities then enter the filters like any input row.
 * R17 the "joint" order ([Blog] footnote on the filter options; [Expl]
   "Top-k 与 top-p 的组合顺序会改变分布") checks the top-k and the top-p
   condition together in every rejection round; the top-p condition then
@@ -305,6 +309,36 @@ def sample_by_cdf(row, op, a53, k=None, p=None, min_p=None):
     if not valid:
         return -1
     return inverse_transform(row, support_mask(row, tau), a53)
+
+
+# ----------------------------------------------------------------------------
+# probabilities from logits with a temperature (the step before the filters)
+# ----------------------------------------------------------------------------
+
+def softmax_row(z, temperature):
+    """p_i = exp(z_i / T) / sum_j exp(z_j / T) ([Expl] "采样流水线究竟在计算什么").
+
+    Written out in the order the library fixes (R18): m = max_i z_i,
+    t_i = (z_i - m) * (1 / T) in float64 (the difference of two float32 is
+    exact there), e_i = exp(t_i) in float64, S = sum_i e_i rounded once
+    (math.fsum), and p_i = float32(e_i / S).  Returns (valid, p): a NaN or
+    +inf logit, no finite logit, or T not a finite positive number make the
+    row invalid.
+    """
+    import math
+    z = np.asarray(z, dtype=np.float32)
+    t32 = np.float32(temperature)
+    if np.isnan(z).any() or np.isposinf(z).any() or not np.isfinite(z).any():
+        return False, None
+    if not (np.isfinite(t32) and t32 > 0):
+        return False, None
+    m = np.float64(z.max())
+    inv_t = 1.0 / np.float64(t32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        t = (z.astype(np.float64) - m) * inv_t
+    e = np.exp(t)                                # -inf -> 0
+    total = math.fsum(e.tolist())
+    return True, (e / total).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------

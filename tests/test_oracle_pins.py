@@ -215,6 +215,38 @@ def test_joint_order_special_cases():
         assert ref.kept_mask(row, tj)[ref.kept_mask(row, tf)].all()
 
 
+def test_softmax_row_closed_forms_and_scipy():
+    """Probabilities from logits: closed forms, shift invariance, the
+    temperature as a scale of the logits, and scipy's softmax."""
+    from scipy.special import softmax as sp_softmax
+    ok, p = ref.softmax_row(f32([0.0, 0.0]), 1.0)
+    assert ok and p.tolist() == [0.5, 0.5]
+    ok, p = ref.softmax_row(f32([1.0, 0.0]), 1.0)
+    e = np.e
+    assert np.allclose(p, [e / (1 + e), 1 / (1 + e)], rtol=2 ** -23, atol=0)
+    ok, p = ref.softmax_row(f32([3.0, 1.0, -np.inf]), 2.0)   # -inf has probability 0
+    assert p[2] == 0 and np.allclose(p[:2], [np.e / (1 + np.e), 1 / (1 + np.e)], rtol=2 ** -23)
+    rng = np.random.default_rng(31)
+    for _ in range(50):
+        z = f32(rng.normal(0, 3, size=int(rng.integers(2, 300))))
+        T = float(np.float32(rng.choice([0.25, 0.5, 1.0, 2.0])))   # powers of two: 1/T exact
+        ok, p = ref.softmax_row(z, T)
+        assert ok and abs(float(p.astype(np.float64).sum()) - 1.0) < z.size * 2 ** -24
+        # integer shift: every difference z_i - m is unchanged, so p is too
+        ok2, p2 = ref.softmax_row(z + np.float32(8.0), T) if np.abs(z).max() < 1e3 else (True, p)
+        assert ok2 and np.array_equal(p, p2) or not np.array_equal(np.float32(z + 8.0) - 8.0, z)
+        q = sp_softmax(z.astype(np.float64) / T)
+        # one float32 rounding (absolute below the normal range)
+        assert np.allclose(p, q, rtol=2 ** -23, atol=2.0 ** -149)
+
+
+def test_softmax_row_invalid_inputs():
+    for z, T in ((f32([np.nan, 0.0]), 1.0), (f32([np.inf, 0.0]), 1.0),
+                 (f32([-np.inf, -np.inf]), 1.0), (f32([0.0, 1.0]), 0.0),
+                 (f32([0.0, 1.0]), -1.0), (f32([0.0, 1.0]), np.nan), (f32([0.0, 1.0]), np.inf)):
+        assert ref.softmax_row(z, T) == (False, None)
+
+
 def test_k_extremes_and_min_p_closed_form():
     rng = np.random.default_rng(3)
     for _ in range(50):
