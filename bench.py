@@ -194,6 +194,12 @@ def extra_configs(dss, si, lib, dev):
     out["probs B=64 V=151936 min_p_sampling_from_probs (0.05)"] = entry(
         kernel_times(lib, lambda: dss.min_p_sampling_from_probs(P, 0.05, seed=1, offset=0), 10),
         B * V * 4)
+    Lg = g(si.logits_rows(np.random.default_rng(2), B, V, 2.0))
+    out["logits B=64 V=151936 softmax (T=0.8)"] = entry(
+        kernel_times(lib, lambda: dss.softmax(Lg, 0.8), 50), 2 * B * V * 4)
+    out["logits B=64 V=151936 top_k_top_p_sampling_from_logits (T=0.8; softmax + sampling kernels)"] = entry(
+        kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_logits(Lg, k, p, 0.8, seed=1, offset=0), 50),
+        B * V * 4)
     w = si.latency()
     P = g(w["probs"])
     t = kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_probs(P, 50, 0.9, seed=3,

@@ -24,6 +24,7 @@ __all__ = [
     "sampling_from_probs", "top_k_sampling_from_probs", "top_p_sampling_from_probs",
     "min_p_sampling_from_probs", "top_k_top_p_sampling_from_probs",
     "top_k_renorm_probs", "top_p_renorm_probs", "top_k_mask_logits",
+    "softmax", "top_k_top_p_sampling_from_logits",
     "DssError", "DSS_FLAG_FROM_ZERO", "DSS_FLAG_STREAMING", "DSS_FLAG_ORDER_JOINT",
     "DSS_FLAG_SINGLE_PIVOT",
 ]
@@ -102,8 +103,8 @@ def _sample(fn_name, probs, params, indices, seed, offset, return_valid, return_
     args = [probs.data_ptr(), rows, vocab, _ptr(indices), n, _ptr(seed_arr), seed_val,
             _ptr(off_arr), off_val]
     keep = []
-    for value, dtype, name in params:
-        arr, scalar = _param(value, dtype, n, device, name)
+    for value, dtype, name, *count in params:   # count: entries of an array (default n)
+        arr, scalar = _param(value, dtype, count[0] if count else n, device, name)
         keep.append(arr)
         args += [_ptr(arr), scalar]
     args += [samples.data_ptr(), _ptr(valid), _ptr(rounds), flags, ws, ws_bytes,
@@ -187,6 +188,29 @@ def top_p_renorm_probs(probs, top_p, *, out=None, return_status=False, flags=0):
     """Keep each row's top-p nucleus (ties kept) and renormalise."""
     return _renorm("top_p_renorm_probs", probs, top_p, torch.float32, "top_p", out,
                    return_status, flags)
+
+
+def softmax(logits, temperature=1.0, *, out=None, return_status=False, flags=0):
+    """Probabilities exp(z / T) / sum exp(z / T) per row (temperature: scalar
+    or one value per row); invalid rows come out NaN with status 1."""
+    return _renorm("softmax", logits, temperature, torch.float32, "temperature", out,
+                   return_status, flags)
+
+
+def top_k_top_p_sampling_from_logits(logits, top_k, top_p, temperature=1.0, *, indices=None,
+                                     seed=None, offset=0, filter_apply_order="top_k_first",
+                                     return_valid=False, return_rounds=False, flags=0):
+    """softmax(logits / temperature) per row, then top_k_top_p_sampling_from_probs;
+    the temperature is per row (scalar or `rows` values), k and p per output."""
+    if filter_apply_order == "joint":
+        flags |= DSS_FLAG_ORDER_JOINT
+    elif filter_apply_order != "top_k_first":
+        raise ValueError("filter_apply_order must be 'top_k_first' or 'joint'")
+    rows = logits.shape[0] if isinstance(logits, torch.Tensor) and logits.dim() == 2 else 0
+    return _sample("top_k_top_p_sampling_from_logits", logits,
+                   [(top_k, torch.int32, "top_k"), (top_p, torch.float32, "top_p"),
+                    (temperature, torch.float32, "temperature", rows)],
+                   indices, seed, offset, return_valid, return_rounds, flags)
 
 
 def top_k_mask_logits(logits, top_k, *, out=None, return_status=False, flags=0):

@@ -42,7 +42,8 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
                   const uint64_t* offset_arr, uint64_t offset, const int32_t* top_k_arr,
                   int32_t top_k, const float* top_p_arr, float top_p, const float* min_p_arr,
                   float min_p, int32_t* samples, uint8_t* valid, int32_t* rounds, uint32_t flags,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream,
+                  const dss::LaunchEvents& ev, bool check_only = false) {
   if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
   // the joint order only exists for the combined filter; the engines know it
   // as an op of its own (the public op id still sizes the workspace)
@@ -59,6 +60,7 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
                                           : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok);
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
+  if (check_only) return DSS_OK;
   const int dev = check_device();
   if (dev != DSS_OK) return dev;
 
@@ -85,10 +87,20 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.single_pivot = (flags & DSS_FLAG_SINGLE_PIVOT) ? 1 : 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      plan.W > 0    ? dss::launch_split_sample(eop, p, plan, workspace, st, timing_events())
-      : rplan.W > 0 ? dss::launch_resident_sample(eop, p, rplan, workspace, st, timing_events())
-                    : dss::launch_stream_sample(eop, p, st, timing_events());
+      plan.W > 0    ? dss::launch_split_sample(eop, p, plan, workspace, st, ev)
+      : rplan.W > 0 ? dss::launch_resident_sample(eop, p, rplan, workspace, st, ev)
+                    : dss::launch_stream_sample(eop, p, st, ev);
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the logits path: the engines' area (the softmax kernel's and
+// the sampling call's share one), then the probabilities.
+size_t logits_engine_bytes(int32_t rows, int32_t vocab, int32_t num_outputs, uint32_t flags) {
+  const size_t a = dss_workspace_size(DSS_OP_TOP_K_TOP_P, rows, vocab, num_outputs, flags);
+  const size_t b = dss::plan_softmax(rows, vocab, flags, vocab % 4 == 0).workspace;
+  return align256(a > b ? a : b);
 }
 
 int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows, int32_t vocab,
@@ -141,7 +153,7 @@ DSS_EXPORT int dss_sampling_from_probs(const float* probs, int32_t rows, int32_t
                                        void* stream) {
   return sample_common(dss::kOpNone, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
                        offset_arr, offset, nullptr, 0, nullptr, 0.0f, nullptr, 0.0f, samples,
-                       valid, rounds, flags, workspace, workspace_bytes, stream);
+                       valid, rounds, flags, workspace, workspace_bytes, stream, timing_events());
 }
 
 DSS_EXPORT int dss_top_k_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
@@ -154,7 +166,7 @@ DSS_EXPORT int dss_top_k_sampling_from_probs(const float* probs, int32_t rows, i
                                              size_t workspace_bytes, void* stream) {
   return sample_common(dss::kOpTopK, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
                        offset_arr, offset, top_k_arr, top_k, nullptr, 0.0f, nullptr, 0.0f,
-                       samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+                       samples, valid, rounds, flags, workspace, workspace_bytes, stream, timing_events());
 }
 
 DSS_EXPORT int dss_top_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
@@ -167,7 +179,7 @@ DSS_EXPORT int dss_top_p_sampling_from_probs(const float* probs, int32_t rows, i
                                              size_t workspace_bytes, void* stream) {
   return sample_common(dss::kOpTopP, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
                        offset_arr, offset, nullptr, 0, top_p_arr, top_p, nullptr, 0.0f,
-                       samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+                       samples, valid, rounds, flags, workspace, workspace_bytes, stream, timing_events());
 }
 
 DSS_EXPORT int dss_min_p_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
@@ -180,7 +192,7 @@ DSS_EXPORT int dss_min_p_sampling_from_probs(const float* probs, int32_t rows, i
                                              size_t workspace_bytes, void* stream) {
   return sample_common(dss::kOpMinP, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
                        offset_arr, offset, nullptr, 0, nullptr, 0.0f, min_p_arr, min_p,
-                       samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+                       samples, valid, rounds, flags, workspace, workspace_bytes, stream, timing_events());
 }
 
 DSS_EXPORT int dss_top_k_top_p_sampling_from_probs(
@@ -191,7 +203,7 @@ DSS_EXPORT int dss_top_k_top_p_sampling_from_probs(
     size_t workspace_bytes, void* stream) {
   return sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs, seed_arr,
                        seed, offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p, nullptr,
-                       0.0f, samples, valid, rounds, flags, workspace, workspace_bytes, stream);
+                       0.0f, samples, valid, rounds, flags, workspace, workspace_bytes, stream, timing_events());
 }
 
 DSS_EXPORT int dss_top_k_renorm_probs(const float* probs, float* out, int32_t rows, int32_t vocab,
@@ -221,6 +233,69 @@ DSS_EXPORT int dss_top_k_mask_logits(const float* logits, float* out, int32_t ro
                        workspace_bytes, stream);
 }
 
+DSS_EXPORT int dss_softmax(const float* logits, float* probs, int32_t rows, int32_t vocab,
+                           const float* temperature_arr, float temperature, uint8_t* row_status,
+                           uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
+  if (rows < 0 || vocab <= 0) return DSS_ERR_INVALID_ARG;
+  if (vocab > DSS_MAX_VOCAB) return DSS_ERR_UNSUPPORTED;
+  if (rows == 0) return DSS_OK;
+  if (!logits || !probs) return DSS_ERR_INVALID_ARG;
+  const int vec_ok = (vocab % 4 == 0) && aligned16(logits) && aligned16(probs);
+  const size_t need = dss_workspace_size(DSS_OP_SOFTMAX, rows, vocab, rows, flags);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+  const dss::SoftmaxParams q{logits, probs, rows, vocab, temperature_arr, temperature, row_status,
+                             vec_ok};
+  return dss::launch_softmax(q, dss::plan_softmax(rows, vocab, flags, vec_ok), workspace,
+                             static_cast<hipStream_t>(stream), timing_events()) == hipSuccess
+             ? DSS_OK
+             : DSS_ERR_HIP;
+}
+
+DSS_EXPORT int dss_top_k_top_p_sampling_from_logits(
+    const float* logits, int32_t rows, int32_t vocab, const int32_t* indices, int32_t num_outputs,
+    const uint64_t* seed_arr, uint64_t seed, const uint64_t* offset_arr, uint64_t offset,
+    const int32_t* top_k_arr, int32_t top_k, const float* top_p_arr, float top_p,
+    const float* temperature_arr, float temperature, int32_t* samples, uint8_t* valid,
+    int32_t* rounds, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
+  if (rows < 0 || vocab <= 0 || num_outputs < 0) return DSS_ERR_INVALID_ARG;
+  if (vocab > DSS_MAX_VOCAB) return DSS_ERR_UNSUPPORTED;
+  if (!indices && num_outputs != rows) return DSS_ERR_INVALID_ARG;
+  if (num_outputs == 0) return DSS_OK;
+  if (!logits || !samples) return DSS_ERR_INVALID_ARG;
+  const size_t eng = logits_engine_bytes(rows, vocab, num_outputs, flags);
+  const size_t need = dss_workspace_size(DSS_OP_TOP_K_TOP_P_FROM_LOGITS, rows, vocab, num_outputs,
+                                         flags);
+  if (workspace_bytes < need || !workspace) return DSS_ERR_WORKSPACE;
+  float* probs = reinterpret_cast<float*>(static_cast<char*>(workspace) + eng);
+  // every check of the sampling call before anything is enqueued
+  const dss::LaunchEvents ev = timing_events();
+  const int chk = sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs, seed_arr,
+                                seed, offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p,
+                                nullptr, 0.0f, samples, valid, rounds, flags, workspace, eng,
+                                stream, ev, true);
+  if (chk != DSS_OK) return chk;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+  // probabilities into the workspace (invalid rows come out NaN-filled, which
+  // the sampling call reports as invalid outputs), then the sampling call;
+  // the timing events span both kernels
+  const int vec_ok = (vocab % 4 == 0) && aligned16(logits);
+  const dss::SoftmaxParams q{logits, probs, rows, vocab, temperature_arr, temperature, nullptr,
+                             vec_ok};
+  const hipError_t e = dss::launch_softmax(q, dss::plan_softmax(rows, vocab, flags, vec_ok),
+                                           workspace, static_cast<hipStream_t>(stream),
+                                           dss::LaunchEvents{ev.start, nullptr});
+  if (e != hipSuccess) return DSS_ERR_HIP;
+  return sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
+                       offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p, nullptr, 0.0f,
+                       samples, valid, rounds, flags, workspace, eng, stream,
+                       dss::LaunchEvents{nullptr, ev.stop});
+}
+
 DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                                      int32_t num_outputs, uint32_t flags) {
   // sized for 16-byte aligned rows; an unaligned call runs the streaming
@@ -235,6 +310,15 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
   if (op == DSS_OP_TOP_P_RENORM) {
     if (rows <= 0) return 0;
     return dss::plan_resident(dss::kOpTopP, vocab, rows, flags, vec).workspace;
+  }
+  if (op == DSS_OP_SOFTMAX) {
+    if (rows <= 0) return 0;
+    return dss::plan_softmax(rows, vocab, flags, vec).workspace;
+  }
+  if (op == DSS_OP_TOP_K_TOP_P_FROM_LOGITS) {
+    if (rows <= 0 || num_outputs <= 0) return 0;
+    return logits_engine_bytes(rows, vocab, num_outputs, flags) +
+           align256((size_t)rows * (size_t)vocab * 4);
   }
   if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || num_outputs <= 0) return 0;
   const dss::SplitPlan plan = dss::plan_split(op, rows, vocab, num_outputs, flags, vec);

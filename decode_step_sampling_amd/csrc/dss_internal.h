@@ -131,6 +131,24 @@ hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan
 hipError_t launch_resident_renorm(const RenormParams& p, const SplitPlan& plan, void* workspace,
                                   hipStream_t s, const LaunchEvents& ev);
 
+// Probabilities from logits with a temperature, p = softmax(z / T) per row
+// (T per row or one scalar); invalid rows are NaN-filled with status 1.
+struct SoftmaxParams {
+  const float* in;
+  float* out;
+  int32_t rows;
+  int32_t vocab;
+  const float* temp_arr;
+  float temp;
+  uint8_t* row_status;
+  int32_t vec_ok;
+};
+// W == 0: the one-work-group-per-row streaming kernel runs instead
+SplitPlan plan_softmax(int rows, int vocab, uint32_t flags, int vec_ok);
+hipError_t launch_softmax(const SoftmaxParams& p, const SplitPlan& plan, void* workspace,
+                          hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_stream_softmax(const SoftmaxParams& p, hipStream_t s, const LaunchEvents& ev);
+
 // plain streaming read of n floats (n a multiple of 4, x 16-byte aligned);
 // folds their maximum bit pattern into *out
 hipError_t launch_stream_read(const float* x, int64_t n, uint32_t* out, hipStream_t s,

@@ -830,6 +830,150 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   row_leave(slot, passed, W, kTopP, sm);
 }
 
+// ---------------------------------------------------------------------------
+// Probabilities from logits with a temperature (explainer, 采样流水线究竟在
+// 计算什么: p_i = exp(z_i / T) / sum_j exp(z_j / T)).  The W work-groups of a
+// row keep its slices in registers: the row's maximum m at the first
+// barrier, the sum S of exp((z_i - m) / T) at the second, then every slice
+// writes float32(exp((z_i - m) / T) / S).  Differences, scaling, exponentials
+// and sums are float64 (the maximum is subtracted for range only); a NaN or
+// +inf logit, no finite logit, or T not a finite positive number make the
+// row invalid (NaN-filled, status 1).
+// ---------------------------------------------------------------------------
+
+// float32 value of a signed-order key (the inverse of signed_key)
+__device__ __forceinline__ float from_signed_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int NV>
+__global__ __launch_bounds__(kBlock) void softmax_kernel(SoftmaxParams Q, ResidentParams R) {
+  __shared__ ResSmem sm;
+  const int W = R.W;
+  const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
+  const int li = (local / W) * 8 + xcd;
+  const int s = local % W;
+  if (li >= R.n_out) return;
+  const int row = R.out0 + li;
+  const int tid = threadIdx.x, lane = lane_id(), wave = r_uwave();
+  const int V = Q.vocab;
+  const int s0 = s * R.L;
+  const int s1 = min(s0 + R.L, V);
+  const int nvec = (s1 - s0) / 4;
+  const gptr<const float4> src =
+      as_global(reinterpret_cast<const float4*>(Q.in + (int64_t)row * V + s0));
+  constexpr int kInFlight = NV < 5 ? NV : 5;
+  const int vbase = wave * (kWave * NV) + lane;
+  float4 v[NV];
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    v[j] = load_f4(src + min(vbase + j * kWave, nvec - 1));
+  };
+#pragma unroll
+  for (int j = 0; j < kInFlight; ++j) issue(j);
+  const float T = Q.temp_arr ? as_global(Q.temp_arr)[row] : Q.temp;
+  const gptr<r_v4f> dst = (gptr<r_v4f>)as_global(Q.out + (int64_t)row * V + s0);
+
+  // as the slice lands: its largest signed-order key, and NaN / +inf
+  uint32_t mk = 0u;
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const bool in = vbase + j * kWave < nvec;
+    const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mk = max(mk, in ? signed_key(x[e]) : 0u);
+      bad = bad || (in && (isnan(x[e]) || x[e] == __builtin_inff()));
+    }
+    if (j + kInFlight < NV) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j + kInFlight);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  mk = wave_max(mk);
+  const bool wb = __ballot(bad) != 0ull;
+  if (lane == 0) {
+    sm.wmax[wave] = mk;
+    sm.wbad[wave] = wb ? 1u : 0u;
+  }
+  __syncthreads();
+  const gptr<RowSlot> slot = as_global(R.slots + li);
+  const gptr<uint32_t> ctl = (gptr<uint32_t>)slot->ctl;
+  if (tid == 0) {
+    uint32_t smax = 0u, sbad = 0u;
+    for (int w = 0; w < kWaves; ++w) {
+      smax = max(smax, sm.wmax[w]);
+      sbad |= sm.wbad[w];
+    }
+    __hip_atomic_fetch_max(ctl + 2, smax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sbad) __hip_atomic_fetch_or(ctl + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(ctl + 1, 1u << r_xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  auto invalid = [&]() __attribute__((always_inline)) {
+    r_v4f o;
+    o.x = o.y = o.z = o.w = __uint_as_float(0x7FC00000u);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (vbase + j * kWave < nvec) dst[vbase + j * kWave] = o;
+    if (s == 0 && tid == 0 && Q.row_status) as_global(Q.row_status)[row] = 1;
+  };
+  if (!row_barrier(ctl, (uint32_t)W, sm)) return invalid();
+  const uint32_t gk = __hip_atomic_load(ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t gb = __hip_atomic_load(ctl + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t xm = __hip_atomic_load(ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float zmax = from_signed_key(gk);
+  if (gb != 0u || __popc(xm) != 1 || !(T > 0.0f) || T == __builtin_inff() ||
+      zmax == -__builtin_inff()) {
+    invalid();
+    row_leave(slot, 1u, W, false, sm);
+    return;
+  }
+  const double m = (double)zmax, it = 1.0 / (double)T;
+
+  // the slice's sum of exponentials, in a fixed order
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    fence_vec(v[j], acc);
+    const bool in = vbase + j * kWave < nvec;
+    const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += in ? exp(((double)x[e] - m) * it) : 0.0;
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) sm.md[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double z = 0.0;
+    for (int w = 0; w < kWaves; ++w) z += sm.md[w];
+    __hip_atomic_store((gptr<double>)slot->chunk + s, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return invalid();
+  if (wave == 0) {
+    const double z = lane < W ? __hip_atomic_load((gptr<double>)slot->chunk + lane, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.0;
+    const double tot = lane63(wave_incl_scan(z));
+    if (lane == 0) sm.resd[0] = tot;
+  }
+  __syncthreads();
+  const double S = sm.resd[0];
+  double chain = 0.0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    fence_vec(v[j], chain);
+    const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    r_v4f o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)(exp(((double)x[e] - m) * it) / S);
+    if (vbase + j * kWave < nvec) dst[vbase + j * kWave] = o;
+    chain = (double)o[0];
+  }
+  if (s == 0 && tid == 0 && Q.row_status) as_global(Q.row_status)[row] = 0;
+  row_leave(slot, 2u, W, false, sm);
+}
+
 }  // namespace
 }  // namespace dss
 
@@ -929,6 +1073,64 @@ hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan
   else e = launch_res_nv<kResSample, kOpMinP>(p, rp, plan, workspace, s, ev);
   // a device that cannot hold one group of work-groups at once: streaming engine
   if (e == hipErrorInvalidConfiguration) e = launch_stream_sample(op, p, s, ev);
+  return e;
+}
+
+SplitPlan plan_softmax(int rows, int vocab, uint32_t flags, int vec_ok) {
+  // the same slicing as the resident sampling kernels (a plain op id)
+  if (flags & DSS_FLAG_STREAMING) return SplitPlan{0, 0, 0, 0, 0, 0};
+  return plan_resident(kOpNone, vocab, rows, 0u, vec_ok);
+}
+
+namespace {
+template <int NV>
+hipError_t launch_softmax_nv(const SoftmaxParams& q, const SplitPlan& plan, void* workspace,
+                             hipStream_t s, const LaunchEvents& ev) {
+  static int cap = -1;
+  if (cap < 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(softmax_kernel<NV>), kBlock, 0);
+    if (e != hipSuccess) return e;
+    cap = cus * per_cu;
+  }
+  ResidentParams R;
+  R.W = plan.W;
+  R.L = plan.L;
+  R.slots = reinterpret_cast<RowSlot*>(static_cast<char*>(workspace) + kCtlRegionBytes);
+  R.lists = nullptr;
+  const int per = min(plan.chunk, (cap / (8 * plan.W)) * 8);
+  if (per <= 0) return hipErrorInvalidConfiguration;
+  for (int out0 = 0; out0 < q.rows; out0 += per) {
+    R.out0 = out0;
+    R.n_out = min(per, q.rows - out0);
+    const bool first = out0 == 0, last = out0 + per >= q.rows;
+    const dim3 grid((unsigned)(((R.n_out + 7) / 8) * 8 * plan.W)), block(kBlock);
+    launch_kernel(softmax_kernel<NV>, grid, block, s, ev, first, last, q, R);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_softmax(const SoftmaxParams& q, const SplitPlan& plan, void* workspace,
+                          hipStream_t s, const LaunchEvents& ev) {
+  hipError_t e = hipErrorInvalidConfiguration;
+  if (plan.W > 0) {
+    switch (plan.nv) {
+      case 1: e = launch_softmax_nv<1>(q, plan, workspace, s, ev); break;
+      case 2: e = launch_softmax_nv<2>(q, plan, workspace, s, ev); break;
+      case 4: e = launch_softmax_nv<4>(q, plan, workspace, s, ev); break;
+      case 8: e = launch_softmax_nv<8>(q, plan, workspace, s, ev); break;
+      case 10: e = launch_softmax_nv<10>(q, plan, workspace, s, ev); break;
+      default: e = launch_softmax_nv<12>(q, plan, workspace, s, ev); break;
+    }
+  }
+  if (e == hipErrorInvalidConfiguration) e = launch_stream_softmax(q, s, ev);
   return e;
 }
 

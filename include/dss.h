@@ -138,6 +138,8 @@ extern "C" {
 #define DSS_OP_TOP_K_RENORM      5
 #define DSS_OP_TOP_P_RENORM      6
 #define DSS_OP_TOP_K_MASK_LOGITS 7
+#define DSS_OP_TOP_K_TOP_P_FROM_LOGITS 8
+#define DSS_OP_SOFTMAX           9
 
 /* Inverse-transform sampling from each output's row ([Blog "逆变换采样"],
  * [Expl "不带过滤时：inverse transform sampling"]): u ~ U[0,1) (draw r = 0),
@@ -224,6 +226,39 @@ int dss_top_k_mask_logits(const float* logits, float* out, int32_t rows, int32_t
                           const int32_t* top_k_arr, int32_t top_k,
                           uint8_t* row_status, uint32_t flags,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Probabilities from logits with a temperature ([Expl "采样流水线究竟在计算什么"]):
+ * probs[r, i] = exp(z_i / T_r) / sum_j exp(z_j / T_r), computed as
+ * float32((exp((z_i - m) / T) / S)) with m the row's largest logit and the
+ * differences, exponentials and their sum S in float64 (subtracting m keeps
+ * the exponentials in range; the formula is unchanged).  temperature_arr has
+ * `rows` entries (NULL: the scalar for every row).  A NaN or +inf logit, a
+ * row without a finite logit, or a temperature that is not a finite positive
+ * number give a NaN row with row_status 1 (nullable); -inf logits get
+ * probability 0.  probs may equal logits (in place).  The workspace is the
+ * one of dss_workspace_size(DSS_OP_SOFTMAX, rows, vocab, rows, flags); only
+ * DSS_FLAG_STREAMING changes anything (one work-group per row). */
+int dss_softmax(const float* logits, float* probs, int32_t rows, int32_t vocab,
+                const float* temperature_arr, float temperature, uint8_t* row_status,
+                uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused top-k-then-top-p sampling from logits: dss_softmax with the given
+ * temperature (temperature_arr per ROW, `rows` entries), then
+ * dss_top_k_top_p_sampling_from_probs on those probabilities with the same
+ * indices, seeds, parameters and flags.  The probabilities live in the
+ * workspace (dss_workspace_size(DSS_OP_TOP_K_TOP_P_FROM_LOGITS, ...) bytes,
+ * zero-filled once like every workspace).  Rows the softmax rejects give
+ * invalid outputs. */
+int dss_top_k_top_p_sampling_from_logits(const float* logits, int32_t rows, int32_t vocab,
+                                         const int32_t* indices, int32_t num_outputs,
+                                         const uint64_t* seed_arr, uint64_t seed,
+                                         const uint64_t* offset_arr, uint64_t offset,
+                                         const int32_t* top_k_arr, int32_t top_k,
+                                         const float* top_p_arr, float top_p,
+                                         const float* temperature_arr, float temperature,
+                                         int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                         uint32_t flags, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace an op needs for these sizes and flags (0 if none). */
 size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,

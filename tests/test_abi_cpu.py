@@ -34,7 +34,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function():
 def test_header_constants_match_binding():
     for name in ("DSS_OK", "DSS_ERR_INVALID_ARG", "DSS_ERR_WORKSPACE", "DSS_ERR_UNSUPPORTED",
                  "DSS_ERR_HIP", "DSS_ERR_DEVICE", "DSS_FLAG_ORDER_JOINT", "DSS_FLAG_FROM_ZERO",
-                 "DSS_FLAG_STREAMING"):
+                 "DSS_FLAG_STREAMING", "DSS_FLAG_SINGLE_PIVOT"):
         assert header_macro(name) == getattr(_lib, name), name
     assert eval(re.search(r"#define\s+DSS_MAX_VOCAB\s+\((.*)\)", open(HEADER).read())
                 .group(1)) == _lib.DSS_MAX_VOCAB
@@ -56,7 +56,9 @@ def test_header_constants_match_binding():
             "top_k_top_p_sampling_from_probs": "DSS_OP_TOP_K_TOP_P",
             "top_k_renorm_probs": "DSS_OP_TOP_K_RENORM",
             "top_p_renorm_probs": "DSS_OP_TOP_P_RENORM",
-            "top_k_mask_logits": "DSS_OP_TOP_K_MASK_LOGITS"}[op]) == i
+            "top_k_mask_logits": "DSS_OP_TOP_K_MASK_LOGITS",
+            "top_k_top_p_sampling_from_logits": "DSS_OP_TOP_K_TOP_P_FROM_LOGITS",
+            "softmax": "DSS_OP_SOFTMAX"}[op]) == i
 
 
 def _plain(lib, probs=FAKE, rows=1, vocab=8, indices=NULL, n=1, samples=FAKE, flags=0,
@@ -97,7 +99,7 @@ def test_sampling_validation_before_any_hip_call():
 def test_renorm_and_mask_validation():
     lib = _lib.load()
     for fn, param in ((lib.dss_top_k_renorm_probs, 3), (lib.dss_top_p_renorm_probs, 0.5),
-                      (lib.dss_top_k_mask_logits, 3)):
+                      (lib.dss_top_k_mask_logits, 3), (lib.dss_softmax, 1.0)):
         assert fn(NULL, FAKE, 1, 8, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_ERR_INVALID_ARG
         assert fn(FAKE, NULL, 1, 8, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_ERR_INVALID_ARG
         assert fn(FAKE, FAKE, -1, 8, NULL, param, NULL, 0, NULL, 0, NULL) == _lib.DSS_ERR_INVALID_ARG
@@ -111,11 +113,13 @@ def test_renorm_and_mask_validation():
 
 def test_workspace_size_and_strings():
     lib = _lib.load()
-    for op in range(8):
+    for op in range(10):
         for rows, vocab, n in ((1, 8, 1), (64, 151936, 64), (512, 256000, 512), (0, 1, 0)):
             size = lib.dss_workspace_size(op, rows, vocab, n, 0)
             assert size >= 0
-            assert lib.dss_workspace_size(op, rows, vocab, n, _lib.DSS_FLAG_STREAMING) == 0
+            # the streaming engine needs none; the logits path still holds its probabilities
+            probs_bytes = ((rows * vocab * 4 + 255) // 256) * 256 if op == 8 and n > 0 else 0
+            assert lib.dss_workspace_size(op, rows, vocab, n, _lib.DSS_FLAG_STREAMING) == probs_bytes
     for code in (0, -1, -2, -3, -4, -5):
         assert _lib.strerror(code) not in ("", "unknown status")
     assert _lib.strerror(7) == "unknown status"
@@ -129,6 +133,27 @@ def test_workspace_size_and_strings():
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 6, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(18), 8, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 8, None, None) == _lib.DSS_ERR_INVALID_ARG
+
+
+def test_logits_sampling_validation():
+    lib = _lib.load()
+
+    def call(logits=FAKE, rows=1, vocab=8, indices=NULL, n=1, samples=FAKE, flags=0, ws=NULL,
+             ws_bytes=0):
+        return lib.dss_top_k_top_p_sampling_from_logits(
+            logits, rows, vocab, indices, n, NULL, 1, NULL, 0, NULL, 5, NULL, 0.9, NULL, 1.0,
+            samples, NULL, NULL, flags, ws, ws_bytes, NULL)
+    assert call(logits=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(samples=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(vocab=0) == _lib.DSS_ERR_INVALID_ARG
+    assert call(rows=2, n=3) == _lib.DSS_ERR_INVALID_ARG
+    assert call(flags=0x100) == _lib.DSS_ERR_INVALID_ARG
+    assert call(vocab=_lib.DSS_MAX_VOCAB + 1) == _lib.DSS_ERR_UNSUPPORTED
+    assert call() == _lib.DSS_ERR_WORKSPACE                        # probabilities need room
+    need = lib.dss_workspace_size(8, 1, 8, 1, 0)
+    assert need >= 32
+    assert call(ws=FAKE, ws_bytes=need - 1) == _lib.DSS_ERR_WORKSPACE
+    assert call(logits=NULL, samples=NULL, rows=0, n=0) == _lib.DSS_OK
 
 
 def test_binding_refuses_cpu_tensors():
