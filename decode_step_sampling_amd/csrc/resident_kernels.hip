@@ -255,14 +255,11 @@ __device__ __forceinline__ double wave_mass(float4 (&v)[NV], int vbase, int nvec
   return lane63(wave_incl_scan(acc));
 }
 
-// Where the owner wave's walk stopped: load j, lane l, the mass before that
-// lane's values in the walk, and whether a prefix really exceeded the target
-// (otherwise (j, l) is the last lane holding kept mass).  Wave-uniform.
+// The (load j, lane l) group of four values the owner wave's walk stopped
+// at; j = -1 if the wave holds no kept mass.  Wave-uniform.
 struct WalkPick {
   int j;
   int l;
-  double excl;
-  bool hit;
 };
 
 // Inverse transform over the wave's kept values in index order (load j,
@@ -270,10 +267,10 @@ struct WalkPick {
 // (index order); lane l then takes the NV consecutive entries
 // [l * NV, (l + 1) * NV), so one wave scan of the lanes' totals finds the
 // lane whose entries cross T, and that lane walks its entries.  Sets pk to
-// the crossing entry's (load, lane) with excl = 0 and returns the target
-// left inside that entry (or a target past its mass when rounding leaves
-// no crossing, so that its last kept value is taken).  lds: NV * 64 doubles
-// used by this wave alone.
+// the crossing entry's (load, lane) and returns the target left inside that
+// entry (or a target past its mass when rounding leaves no crossing, so
+// that its last kept value is taken).  lds: NV * 64 doubles used by this
+// wave alone.
 template <int NV>
 __device__ __forceinline__ double wave_walk(float4 (&v)[NV], int vbase, int nvec, uint32_t tau,
                                             double T, double* lds, WalkPick& pk) {
@@ -301,7 +298,7 @@ __device__ __forceinline__ double wave_walk(float4 (&v)[NV], int vbase, int nvec
   const double incl = wave_incl_scan(t);
   const uint64_t hit = __ballot(t > 0.0 && incl > T);
   const uint64_t nz = __ballot(t > 0.0);
-  pk = WalkPick{-1, -1, 0.0, false};
+  pk = WalkPick{-1, -1};
   if (nz == 0ull) return 0.0;
   const int L = hit ? r_first_lane(hit) : r_last_lane(nz);
   // lane L: its entries in order
@@ -330,15 +327,13 @@ __device__ __forceinline__ double wave_walk(float4 (&v)[NV], int vbase, int nvec
     ent += L * NV;
   }
   const int e = __builtin_amdgcn_readlane(ent, L);
-  // the entry's own values decide: the first whose prefix exceeds the target
-  // left in it, else (rounding, or the no-crossing target) its last kept one
-  pk = WalkPick{e / kWave, e % kWave, 0.0, true};
+  pk = WalkPick{e / kWave, e % kWave};
   return lane_value(tl, L);
 }
 
 // The value the walk picked, decided by lane pk.l: the first kept value of
-// its load pk.j whose prefix exceeds T, or its last kept one when rounding
-// leaves none.  Returns the value's position in the slice in lane pk.l, -1
+// its load pk.j whose prefix (from 0 inside the group) exceeds T, or its
+// last kept one when none does (rounding, or the no-crossing target).  Returns the value's position in the slice in lane pk.l, -1
 // elsewhere.  (Every load is examined and only load pk.j's result kept:
 // selecting the vector by a run-time index would move v to scratch memory.)
 template <int NV>
@@ -350,7 +345,7 @@ __device__ __forceinline__ int pick_value(float4 (&v)[NV], int vbase, uint32_t t
   for (int j = 0; j < NV; ++j) {
     fence_vec(v[j], e_out);
     const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-    double acc = pk.excl;
+    double acc = 0.0;
     int pick = -1, lastk = -1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -359,7 +354,7 @@ __device__ __forceinline__ int pick_value(float4 (&v)[NV], int vbase, uint32_t t
       acc += k ? (double)x[e] : 0.0;
       pick = (k && pick < 0 && acc > T) ? e : pick;
     }
-    const int e = (pk.hit && pick >= 0) ? pick : lastk;
+    const int e = pick >= 0 ? pick : lastk;
     e_out = j == pk.j ? e : e_out;
   }
   return e_out < 0 ? -1 : 4 * (vbase + pk.j * kWave) + e_out;
