@@ -44,6 +44,9 @@ Readings of the pages (each also listed in the design doc):
   (an identity of the formula, needed for range); differences, scaling by
   1/T, exponentials and their sum in float64, each probability rounded once
   to float32; the probabilities then enter the filters like any input row.
+* R19 top-k selection ([Expl] "选择 top-k 值本身": values and indices, not a
+  sample): the k largest values of a row in descending order, equal values
+  by ascending index, -0.0 equal to +0.0; a NaN makes the row invalid.
 * R17 the "joint" order ([Blog] footnote on the filter options; [Expl]
   "Top-k 与 top-p 的组合顺序会改变分布") checks the top-k and the top-p
   condition together in every rejection round; the top-p condition then
@@ -339,6 +342,21 @@ def softmax_row(z, temperature):
     e = np.exp(t)                                # -inf -> 0
     total = math.fsum(e.tolist())
     return True, (e / total).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# top-k selection: values and indices (R19)
+# ----------------------------------------------------------------------------
+
+def top_k_select(row, k):
+    """(valid, values, indices) of the k largest entries of a float32 row,
+    values descending, equal values by ascending index (R19); NaN: invalid."""
+    row = np.asarray(row, dtype=np.float32)
+    if np.isnan(row).any():
+        return False, None, None
+    key = row.astype(np.float64) + 0.0            # -0.0 -> +0.0
+    order = np.lexsort((np.arange(row.size), -key))[:int(k)]
+    return True, row[order], order.astype(np.int32)
 
 
 # ----------------------------------------------------------------------------

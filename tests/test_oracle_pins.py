@@ -247,6 +247,32 @@ def test_softmax_row_invalid_inputs():
         assert ref.softmax_row(z, T) == (False, None)
 
 
+def test_top_k_select_against_sorted_and_heapq():
+    """Top-k selection (R19) against Python's sorted() with an explicit key and
+    heapq.nlargest, on rows with ties, signed zeros and infinities."""
+    import heapq
+    rng = np.random.default_rng(41)
+    for trial in range(200):
+        v = int(rng.integers(1, 60))
+        if trial % 3 == 0:
+            row = f32(rng.integers(-3, 4, size=v) / 2.0)       # many ties
+            row[rng.integers(0, v)] = -0.0
+        else:
+            row = f32(rng.normal(0, 2, size=v))
+            if trial % 7 == 0:
+                row[rng.integers(0, v)] = np.inf
+                row[rng.integers(0, v)] = -np.inf
+        k = int(rng.integers(1, v + 1))
+        ok, vals, idx = ref.top_k_select(row, k)
+        assert ok
+        want = sorted(range(v), key=lambda i: (-(float(row[i]) + 0.0), i))[:k]
+        assert list(idx) == want
+        assert [float(x) for x in vals] == [float(row[i]) for i in want]
+        big = heapq.nlargest(k, ((float(row[i]) + 0.0, -i) for i in range(v)))
+        assert [-b for _, b in big] == want
+    assert ref.top_k_select(f32([1.0, np.nan]), 1) == (False, None, None)
+
+
 def test_k_extremes_and_min_p_closed_form():
     rng = np.random.default_rng(3)
     for _ in range(50):
