@@ -24,7 +24,7 @@ __all__ = [
     "sampling_from_probs", "top_k_sampling_from_probs", "top_p_sampling_from_probs",
     "min_p_sampling_from_probs", "top_k_top_p_sampling_from_probs",
     "top_k_renorm_probs", "top_p_renorm_probs", "top_k_mask_logits",
-    "softmax", "top_k_top_p_sampling_from_logits",
+    "softmax", "top_k_top_p_sampling_from_logits", "top_k",
     "DssError", "DSS_FLAG_FROM_ZERO", "DSS_FLAG_STREAMING", "DSS_FLAG_ORDER_JOINT",
     "DSS_FLAG_SINGLE_PIVOT",
 ]
@@ -211,6 +211,22 @@ def top_k_top_p_sampling_from_logits(logits, top_k, top_p, temperature=1.0, *, i
                    [(top_k, torch.int32, "top_k"), (top_p, torch.float32, "top_p"),
                     (temperature, torch.float32, "temperature", rows)],
                    indices, seed, offset, return_valid, return_rounds, flags)
+
+
+def top_k(x, k, *, return_status=False):
+    """The k largest entries of every row: (values, indices), each [rows, k],
+    values descending, equal values by ascending index."""
+    _check_rows(x, "input")
+    device = x.device
+    rows, vocab = x.shape
+    values = torch.empty(rows, k, dtype=torch.float32, device=device)
+    indices = torch.empty(rows, k, dtype=torch.int32, device=device)
+    status = torch.empty(rows, dtype=torch.uint8, device=device) if return_status else None
+    lib = _lib.load()
+    with torch.cuda.device(device):
+        _lib.check(lib.dss_top_k(x.data_ptr(), rows, vocab, int(k), values.data_ptr(),
+                                 indices.data_ptr(), _ptr(status), 0, _stream(device)), "top_k")
+    return (values, indices, status) if return_status else (values, indices)
 
 
 def top_k_mask_logits(logits, top_k, *, out=None, return_status=False, flags=0):

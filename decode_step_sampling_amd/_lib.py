@@ -57,6 +57,7 @@ SIGNATURES = {
     "dss_top_p_renorm_probs": ([_P, _P, _I32, _I32, _P, _F32] + _RENORM_TAIL, ctypes.c_int),
     "dss_top_k_mask_logits": ([_P, _P, _I32, _I32, _P, _I32] + _RENORM_TAIL, ctypes.c_int),
     "dss_softmax": ([_P, _P, _I32, _I32, _P, _F32] + _RENORM_TAIL, ctypes.c_int),
+    "dss_top_k": ([_P, _I32, _I32, _I32, _P, _P, _P, _U32, _P], ctypes.c_int),
     "dss_top_k_top_p_sampling_from_logits": (_HEAD + [_P, _I32, _P, _F32, _P, _F32] + _TAIL,
                                              ctypes.c_int),
     "dss_workspace_size": ([_I32, _I32, _I32, _I32, _U32], ctypes.c_size_t),

@@ -296,6 +296,22 @@ DSS_EXPORT int dss_top_k_top_p_sampling_from_logits(
                        dss::LaunchEvents{nullptr, ev.stop});
 }
 
+DSS_EXPORT int dss_top_k(const float* x, int32_t rows, int32_t vocab, int32_t k, float* values,
+                         int32_t* indices, uint8_t* row_status, uint32_t flags, void* stream) {
+  if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
+  if (rows < 0 || vocab <= 0 || k < 1 || k > vocab) return DSS_ERR_INVALID_ARG;
+  if (vocab > DSS_MAX_VOCAB || k > dss::kSelectMax) return DSS_ERR_UNSUPPORTED;
+  if (rows == 0) return DSS_OK;
+  if (!x || !values || !indices) return DSS_ERR_INVALID_ARG;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+  const dss::SelectParams q{x, values, indices, rows, vocab, k, row_status,
+                            (vocab % 4 == 0) && aligned16(x)};
+  return dss::launch_select(q, static_cast<hipStream_t>(stream), timing_events()) == hipSuccess
+             ? DSS_OK
+             : DSS_ERR_HIP;
+}
+
 DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                                      int32_t num_outputs, uint32_t flags) {
   // sized for 16-byte aligned rows; an unaligned call runs the streaming

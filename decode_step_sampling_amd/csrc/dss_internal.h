@@ -149,6 +149,21 @@ hipError_t launch_softmax(const SoftmaxParams& p, const SplitPlan& plan, void* w
                           hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_stream_softmax(const SoftmaxParams& p, hipStream_t s, const LaunchEvents& ev);
 
+// Top-k selection: per row the k largest values (descending, equal values by
+// ascending index) and their indices; one work-group per row.
+constexpr int kSelectMax = 4096;
+struct SelectParams {
+  const float* in;
+  float* values;    // [rows][k]
+  int32_t* indices; // [rows][k]
+  int32_t rows;
+  int32_t vocab;
+  int32_t k;
+  uint8_t* row_status;
+  int32_t vec_ok;
+};
+hipError_t launch_select(const SelectParams& p, hipStream_t s, const LaunchEvents& ev);
+
 // plain streaming read of n floats (n a multiple of 4, x 16-byte aligned);
 // folds their maximum bit pattern into *out
 hipError_t launch_stream_read(const float* x, int64_t n, uint32_t* out, hipStream_t s,

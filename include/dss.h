@@ -260,6 +260,18 @@ int dss_top_k_top_p_sampling_from_logits(const float* logits, int32_t rows, int3
                                          uint32_t flags, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/* Top-k selection ([Expl "选择 top-k 值本身"]: the values and indices, not a
+ * sample): for every row the k largest entries, values[r, 0..k) in
+ * descending order with equal values by ascending index (-0.0 equals +0.0),
+ * indices[r, 0..k) their positions in the row; values and indices are
+ * [rows, k] device arrays.  Any float32 input (probabilities or logits,
+ * +-inf allowed); a NaN makes the row invalid (NaN values, index -1,
+ * row_status 1, nullable).  1 <= k <= vocab, else DSS_ERR_INVALID_ARG;
+ * k > 4096 is DSS_ERR_UNSUPPORTED.  No workspace; flags are reserved (pass
+ * 0).  One work-group per row. */
+int dss_top_k(const float* x, int32_t rows, int32_t vocab, int32_t k, float* values,
+              int32_t* indices, uint8_t* row_status, uint32_t flags, void* stream);
+
 /* Bytes of workspace an op needs for these sizes and flags (0 if none). */
 size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                           int32_t num_outputs, uint32_t flags);

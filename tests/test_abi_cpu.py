@@ -34,7 +34,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -133,6 +133,22 @@ def test_workspace_size_and_strings():
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 6, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(18), 8, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 8, None, None) == _lib.DSS_ERR_INVALID_ARG
+
+
+def test_top_k_selection_validation():
+    lib = _lib.load()
+
+    def call(x=FAKE, rows=1, vocab=8, k=3, values=FAKE, indices=FAKE, flags=0):
+        return lib.dss_top_k(x, rows, vocab, k, values, indices, NULL, flags, NULL)
+    assert call(x=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(values=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(indices=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(k=0) == _lib.DSS_ERR_INVALID_ARG
+    assert call(k=9) == _lib.DSS_ERR_INVALID_ARG               # k > vocab
+    assert call(rows=-1) == _lib.DSS_ERR_INVALID_ARG
+    assert call(flags=0x100) == _lib.DSS_ERR_INVALID_ARG
+    assert call(vocab=10000, k=4097) == _lib.DSS_ERR_UNSUPPORTED
+    assert call(x=NULL, values=NULL, indices=NULL, rows=0) == _lib.DSS_OK
 
 
 def test_logits_sampling_validation():
