@@ -200,6 +200,9 @@ def extra_configs(dss, si, lib, dev):
     out["logits B=64 V=151936 top_k_top_p_sampling_from_logits (T=0.8; softmax + sampling kernels)"] = entry(
         kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_logits(Lg, k, p, 0.8, seed=1, offset=0), 50),
         B * V * 4)
+    for kk in (50, 1024):
+        out[f"logits B=64 V=151936 top_k selection (k={kk}; values + indices)"] = entry(
+            kernel_times(lib, lambda: dss.top_k(Lg, kk), 50), B * V * 4 + B * kk * 8)
     w = si.latency()
     P = g(w["probs"])
     t = kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_probs(P, 50, 0.9, seed=3,

@@ -213,7 +213,7 @@ def top_k_top_p_sampling_from_logits(logits, top_k, top_p, temperature=1.0, *, i
                    indices, seed, offset, return_valid, return_rounds, flags)
 
 
-def top_k(x, k, *, return_status=False):
+def top_k(x, k, *, return_status=False, flags=0):
     """The k largest entries of every row: (values, indices), each [rows, k],
     values descending, equal values by ascending index."""
     _check_rows(x, "input")
@@ -223,9 +223,12 @@ def top_k(x, k, *, return_status=False):
     indices = torch.empty(rows, k, dtype=torch.int32, device=device)
     status = torch.empty(rows, dtype=torch.uint8, device=device) if return_status else None
     lib = _lib.load()
+    ws, ws_bytes = _workspace(device, lib.dss_workspace_size(OP_IDS["top_k"], rows, vocab,
+                                                             rows, flags))
     with torch.cuda.device(device):
         _lib.check(lib.dss_top_k(x.data_ptr(), rows, vocab, int(k), values.data_ptr(),
-                                 indices.data_ptr(), _ptr(status), 0, _stream(device)), "top_k")
+                                 indices.data_ptr(), _ptr(status), flags, ws, ws_bytes,
+                                 _stream(device)), "top_k")
     return (values, indices, status) if return_status else (values, indices)
 
 

@@ -34,6 +34,7 @@ OP_IDS = {
     "top_k_mask_logits": 7,
     "top_k_top_p_sampling_from_logits": 8,
     "softmax": 9,
+    "top_k": 10,
 }
 
 _P = ctypes.c_void_p
@@ -57,7 +58,7 @@ SIGNATURES = {
     "dss_top_p_renorm_probs": ([_P, _P, _I32, _I32, _P, _F32] + _RENORM_TAIL, ctypes.c_int),
     "dss_top_k_mask_logits": ([_P, _P, _I32, _I32, _P, _I32] + _RENORM_TAIL, ctypes.c_int),
     "dss_softmax": ([_P, _P, _I32, _I32, _P, _F32] + _RENORM_TAIL, ctypes.c_int),
-    "dss_top_k": ([_P, _I32, _I32, _I32, _P, _P, _P, _U32, _P], ctypes.c_int),
+    "dss_top_k": ([_P, _I32, _I32, _I32, _P, _P, _P, _U32, _P, _SZ, _P], ctypes.c_int),
     "dss_top_k_top_p_sampling_from_logits": (_HEAD + [_P, _I32, _P, _F32, _P, _F32] + _TAIL,
                                              ctypes.c_int),
     "dss_workspace_size": ([_I32, _I32, _I32, _I32, _U32], ctypes.c_size_t),

@@ -297,19 +297,28 @@ DSS_EXPORT int dss_top_k_top_p_sampling_from_logits(
 }
 
 DSS_EXPORT int dss_top_k(const float* x, int32_t rows, int32_t vocab, int32_t k, float* values,
-                         int32_t* indices, uint8_t* row_status, uint32_t flags, void* stream) {
+                         int32_t* indices, uint8_t* row_status, uint32_t flags, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
   if (rows < 0 || vocab <= 0 || k < 1 || k > vocab) return DSS_ERR_INVALID_ARG;
   if (vocab > DSS_MAX_VOCAB || k > dss::kSelectMax) return DSS_ERR_UNSUPPORTED;
   if (rows == 0) return DSS_OK;
   if (!x || !values || !indices) return DSS_ERR_INVALID_ARG;
+  const int vec = (vocab % 4 == 0) && aligned16(x);
+  const dss::SplitPlan plan = dss::plan_split_select(rows, vocab, k, flags, vec);
+  if (workspace_bytes < plan.workspace || (plan.workspace > 0 && !workspace))
+    return DSS_ERR_WORKSPACE;
   const int dev = check_device();
   if (dev != DSS_OK) return dev;
-  const dss::SelectParams q{x, values, indices, rows, vocab, k, row_status,
-                            (vocab % 4 == 0) && aligned16(x)};
-  return dss::launch_select(q, static_cast<hipStream_t>(stream), timing_events()) == hipSuccess
-             ? DSS_OK
-             : DSS_ERR_HIP;
+  const dss::SelectParams q{x, values, indices, rows, vocab, k, row_status, vec};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (plan.W > 0) {
+    e = dss::launch_split_select(q, plan, workspace, s, timing_events());
+  } else {
+    e = dss::launch_select(q, s, timing_events());
+  }
+  return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
 DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
@@ -322,6 +331,10 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
     if (rows <= 0) return 0;
     const int kind = op == DSS_OP_TOP_K_RENORM ? dss::kRenormTopK : dss::kMaskLogits;
     return dss::plan_split_renorm(kind, rows, vocab, flags, vec).workspace;
+  }
+  if (op == DSS_OP_TOP_K_SELECT) {
+    if (rows <= 0) return 0;
+    return dss::plan_split_select(rows, vocab, 1, flags, vec).workspace;
   }
   if (op == DSS_OP_TOP_P_RENORM) {
     if (rows <= 0) return 0;

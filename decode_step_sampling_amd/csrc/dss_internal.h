@@ -163,6 +163,12 @@ struct SelectParams {
   int32_t vec_ok;
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t s, const LaunchEvents& ev);
+// Top-k selection on the split engine (k <= 2048): the top-k set that the
+// engine gathers, sorted; rows whose lists overflow fall back to the
+// one-work-group selection inside the same kernel.  W == 0: not eligible.
+SplitPlan plan_split_select(int rows, int vocab, int k, uint32_t flags, int vec_ok);
+hipError_t launch_split_select(const SelectParams& q, const SplitPlan& plan, void* workspace,
+                               hipStream_t s, const LaunchEvents& ev);
 
 // plain streaming read of n floats (n a multiple of 4, x 16-byte aligned);
 // folds their maximum bit pattern into *out

@@ -71,9 +71,11 @@ struct SplitParams {
   uint8_t* r_status;  // renorm / mask: [n_out] 0 ok, 1 invalid row, 2 written already
 };
 
-// What the split engine computes: a sample, or tau_k (and Z_k) for a top-k
-// renormalisation or a top-k logit mask, written by a second kernel.
-enum SplitKind : int { kKindSample = 0, kKindRenorm = 1, kKindMask = 2 };
+// What the split engine computes: a sample; tau_k (and Z_k) for a top-k
+// renormalisation or a top-k logit mask, written by a second kernel; or the
+// top-k values and indices themselves (selection: the top-k set, already in
+// LDS, sorted by key and index).
+enum SplitKind : int { kKindSample = 0, kKindRenorm = 1, kKindMask = 2, kKindSelect = 3 };
 
 // Order key of a value: the float32 bits for probabilities (non-negative,
 // F4 note §③), the signed-order key for logits (F4 note §⑧).
@@ -107,6 +109,7 @@ struct SplitSmem {
       uint64_t bnd[kBndMax + kWave];    // entries in the boundary bin (+ dummies)
     } b;
     stream::SampleSmem stream;   // streaming fallback
+    stream::SelectSmem sel;      // streaming fallback of a selection
   } u;
   alignas(16) uint32_t hist[H1::kWords];
   // fixed-point masses of the top-k entries above the boundary bin, per
@@ -487,18 +490,24 @@ enum SplitMode : int { kDone = 0, kFallback = 1 };
 
 // Everything but the streaming fallback; returns kFallback when the output
 // must be sampled by the streaming engine instead (one call site, below).
-// Reports output i (chunk-local li) invalid.
+// Reports output i (chunk-local li) invalid; every thread calls it.
 template <int KIND>
-__device__ __forceinline__ void split_invalid(const SampleParams& P, const SplitParams& S, int i,
-                                              int li) {
+__device__ __forceinline__ void split_invalid(const SampleParams& P, const SplitParams& S,
+                                              const SelectParams& Q, int i, int li) {
+  if (KIND == kKindSelect) {
+    stream::select_invalid(Q, i);
+    return;
+  }
+  if (threadIdx.x != 0) return;
   if (KIND == kKindSample) stream::write_sample(P, i, -1, 0);
   else as_global(S.r_status)[li] = 1;
 }
 
 template <int KIND, int OP, int NV>
 __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitParams& S,
-                                           SplitSmem& sm, int& out_i) {
-  constexpr bool KEYS = KIND == kKindMask;    // logits: signed-order keys
+                                           const SelectParams& Q, SplitSmem& sm, int& out_i) {
+  // logits, and any values to select from: signed-order keys
+  constexpr bool KEYS = KIND == kKindMask || KIND == kKindSelect;
   // top-k-then-top-p sampling keeps a mass histogram for the loop's start
   constexpr bool kJoint = OP == kOpTopKTopPJoint;
   constexpr bool kTopPPart = OP == kOpTopKTopP || kJoint;
@@ -552,7 +561,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     // no hand-off for this output: slice 0 answers alone
     if (s != 0) return kDone;
     if (!ok) {
-      if (tid == 0) split_invalid<KIND>(P, S, i, li);
+      split_invalid<KIND>(P, S, Q, i, li);
       return kDone;
     }
     return kFallback;
@@ -774,7 +783,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   if (W == 1) {
     // the whole row is in this work-group: full[] holds its list
     if (bad || smax == 0u) {
-      if (tid == 0) split_invalid<KIND>(P, S, i, li);
+      split_invalid<KIND>(P, S, Q, i, li);
       return kDone;
     }
     if (!publish) return kFallback;
@@ -892,7 +901,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     __syncthreads();
     const uint32_t status = sm.res[5];
     if (status == 1u) {
-      if (tid == 0) split_invalid<KIND>(P, S, i, li);
+      split_invalid<KIND>(P, S, Q, i, li);
       return kDone;
     }
     if (status == 2u) return kFallback;
@@ -1029,13 +1038,14 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
   }
   __syncthreads();
-  if (wave != 0) return kDone;
+  if (KIND != kKindSelect && wave != 0) return kDone;
 
   // ---- wave 0 from here on: tau_k inside bin1, the top-k list, the loop -----
+  // (a selection keeps every wave for the sort)
   uint32_t m = n_above;
   uint32_t tau_k = 0u;
   double zb = 0.0;  // mass of the boundary entries kept (per lane, then summed)
-  if (!all_kept) {
+  if (wave == 0 && !all_kept) {
     tau_k = wave_kth(sm.u.b.bnd, n_bnd, tstar + (bin1 << sh), sh, (uint32_t)k - above1, sm.hist,
                      sm.sel);
     // the boundary entries >= tau_k follow the others, in list order
@@ -1051,6 +1061,19 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
   }
 
+  if constexpr (KIND == kKindSelect) {
+    // cand[0, m) holds every entry >= tau_k (m >= k, more where tau_k is
+    // tied); sorted by descending key, equal keys by ascending index, its
+    // first k entries are the output
+    if (wave == 0 && lane == 0) sm.res[7] = m;
+    __syncthreads();
+    const uint32_t ms = sm.res[7];
+    uint32_t P2 = 1u;
+    while (P2 < ms) P2 <<= 1;
+    stream::sort_desc<true>(sm.u.b.cand, ms, P2);
+    stream::select_write(Q, i, sm.u.b.cand);
+    return kDone;
+  }
   if (KIND != kKindSample) {
     // renormalisation / masking: tau_k, and the kept mass Z_k in a fixed order
     double zs = 0.0;
@@ -1099,13 +1122,15 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
 
 template <int KIND, int OP, int NV>
 __global__ __launch_bounds__(kBlock) void split_kernel(SampleParams P, SplitParams S,
-                                                       RenormParams RP) {
+                                                       RenormParams RP, SelectParams Q) {
   __shared__ SplitSmem sm;
   int i = 0;
-  const int mode = split_sample<KIND, OP, NV>(P, S, sm, i);
+  const int mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
   if (mode == kFallback) {
     if constexpr (KIND == kKindSample) {
       stream::sample_row<OP>(P, i, sm.u.stream);
+    } else if constexpr (KIND == kKindSelect) {
+      stream::select_row(Q, i, sm.u.sel);
     } else {
       // the whole row by the streaming engine, output written here
       stream::renorm_row<KIND == kKindRenorm ? kRenormTopK : kMaskLogits>(RP, i, sm.u.stream.red);
@@ -1155,23 +1180,25 @@ __global__ __launch_bounds__(kBlock) void split_write_kernel(RenormParams P, Spl
 
 template <int KIND, int OP, int NV>
 void launch_one(const SampleParams& p, const SplitParams& sp, const RenormParams& rp,
-                hipStream_t s, const LaunchEvents& ev, bool first, bool last) {
+                const SelectParams& q, hipStream_t s, const LaunchEvents& ev, bool first,
+                bool last) {
   const int groups = (sp.n_out + 7) / 8;
   const dim3 grid((unsigned)(groups * 8 * sp.W)), block(kBlock);
-  launch_kernel(split_kernel<KIND, OP, NV>, grid, block, s, ev, first, last, p, sp, rp);
+  launch_kernel(split_kernel<KIND, OP, NV>, grid, block, s, ev, first, last, p, sp, rp, q);
 }
 
 template <int KIND, int OP>
 void launch_nv(int nv, const SampleParams& p, const SplitParams& sp, const RenormParams& rp,
-               hipStream_t s, const LaunchEvents& ev, bool first, bool last) {
+               hipStream_t s, const LaunchEvents& ev, bool first, bool last,
+               const SelectParams& q = SelectParams{}) {
   switch (nv) {
-    case 1: launch_one<KIND, OP, 1>(p, sp, rp, s, ev, first, last); break;
-    case 2: launch_one<KIND, OP, 2>(p, sp, rp, s, ev, first, last); break;
-    case 3: launch_one<KIND, OP, 3>(p, sp, rp, s, ev, first, last); break;
-    case 4: launch_one<KIND, OP, 4>(p, sp, rp, s, ev, first, last); break;
-    case 6: launch_one<KIND, OP, 6>(p, sp, rp, s, ev, first, last); break;
-    case 8: launch_one<KIND, OP, 8>(p, sp, rp, s, ev, first, last); break;
-    default: launch_one<KIND, OP, 10>(p, sp, rp, s, ev, first, last); break;
+    case 1: launch_one<KIND, OP, 1>(p, sp, rp, q, s, ev, first, last); break;
+    case 2: launch_one<KIND, OP, 2>(p, sp, rp, q, s, ev, first, last); break;
+    case 3: launch_one<KIND, OP, 3>(p, sp, rp, q, s, ev, first, last); break;
+    case 4: launch_one<KIND, OP, 4>(p, sp, rp, q, s, ev, first, last); break;
+    case 6: launch_one<KIND, OP, 6>(p, sp, rp, q, s, ev, first, last); break;
+    case 8: launch_one<KIND, OP, 8>(p, sp, rp, q, s, ev, first, last); break;
+    default: launch_one<KIND, OP, 10>(p, sp, rp, q, s, ev, first, last); break;
   }
 }
 
@@ -1307,6 +1334,34 @@ hipError_t launch_split_renorm(int kind, const RenormParams& rp, const SplitPlan
       launch_nv<kKindMask, kOpTopK>(plan.nv, p, sp, rp, s, ev, first, false);
       launch_kernel(split_write_kernel<kKindMask>, wgrid, block, s, ev, false, last, rp, sp, nchunk);
     }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+SplitPlan plan_split_select(int rows, int vocab, int k, uint32_t flags, int vec_ok) {
+  SplitPlan plan{0, 0, 0, 0, 0, 0};
+  if (k < 1 || k > kSplitKCap) return plan;
+  return plan_split(kOpTopK, rows, vocab, rows, flags & DSS_FLAG_STREAMING, vec_ok);
+}
+
+hipError_t launch_split_select(const SelectParams& q, const SplitPlan& plan, void* workspace,
+                               hipStream_t s, const LaunchEvents& ev) {
+  SplitParams sp = split_params(plan, workspace);
+  const RenormParams rp{};
+  SampleParams p{};
+  p.probs = q.in;
+  p.rows = q.rows;
+  p.vocab = q.vocab;
+  p.num_outputs = q.rows;
+  p.top_k = q.k;
+  p.vec_ok = 1;
+  for (int out0 = 0; out0 < p.num_outputs; out0 += plan.chunk) {
+    sp.out0 = out0;
+    sp.n_out = min(plan.chunk, p.num_outputs - out0);
+    const bool first = out0 == 0, last = out0 + plan.chunk >= p.num_outputs;
+    launch_nv<kKindSelect, kOpTopK>(plan.nv, p, sp, rp, s, ev, first, last, q);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -605,5 +605,267 @@ __device__ __forceinline__ void renorm_row(const RenormParams& P, int row, RedSm
   if (P.row_status && threadIdx.x == 0) P.row_status[row] = 0;
 }
 
+// ---- top-k selection (explainer, 选择 top-k 值本身) ----------------------
+
+// A row with no top-k set (a NaN in it): NaN values, index -1, status 1.
+__device__ __forceinline__ void select_invalid(const SelectParams& Q, int row) {
+  const gptr<float> vo = as_global(Q.values + (int64_t)row * Q.k);
+  const gptr<int32_t> io = as_global(Q.indices + (int64_t)row * Q.k);
+  for (int j = threadIdx.x; j < Q.k; j += kBlock) {
+    vo[j] = __uint_as_float(0x7FC00000u);
+    io[j] = -1;
+  }
+  if (Q.row_status && threadIdx.x == 0) Q.row_status[row] = 1;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Compare-exchange of the entries at positions i < j: ascending (i takes the
+// smaller) when `up`, else descending.
+__device__ __forceinline__ void cmp_swap(uint64_t& a, uint64_t& b, bool up) {
+  const uint64_t lo = a < b ? a : b, hi = a < b ? b : a;
+  a = up ? lo : hi;
+  b = up ? hi : lo;
+}
+
+// One step of a bitonic network on the 256 entries one wave holds, entry
+// base + 64 r + lane in x[r]: the pairs `stride` apart, ascending inside a
+// block of `size` entries whose `size` bit is set, descending otherwise.
+__device__ __forceinline__ void chunk_step(uint64_t (&x)[4], uint32_t base, uint32_t size,
+                                           uint32_t stride, uint32_t lane) {
+  if (stride == 128u) {
+    cmp_swap(x[0], x[2], ((base + lane) & size) != 0u);
+    cmp_swap(x[1], x[3], ((base + 64u + lane) & size) != 0u);
+  } else if (stride == 64u) {
+    cmp_swap(x[0], x[1], ((base + lane) & size) != 0u);
+    cmp_swap(x[2], x[3], ((base + 128u + lane) & size) != 0u);
+  } else {
+    const bool lower = (lane & stride) == 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint64_t y = shfl_xor_u64(x[r], (int)stride);
+      const bool up = ((base + 64u * r + lane) & size) != 0u;
+      x[r] = (lower == up) ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
+    }
+  }
+}
+
+// Sorts ent[0, P) into descending order: P a power of two <= kSelectMax,
+// the first n <= P entries given, the rest taken as 0 (below every real
+// entry).  A bitonic network in which every wave keeps a chunk of 256
+// entries in registers and runs all strides below 256 with lane shuffles;
+// only the strides of 256 and more go through LDS, one barrier each (18
+// barriers for 4096 entries instead of 78).  With CONV the entries arrive
+// as key | index << 32 and are sorted as key << 32 | ~index: descending
+// keys, equal keys by ascending index.  Every thread of the work-group
+// calls it; it ends with a barrier.
+template <bool CONV>
+__device__ __forceinline__ void sort_desc(uint64_t* ent, uint32_t n, uint32_t P) {
+  const uint32_t tid = threadIdx.x, lane = (uint32_t)lane_id();
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6)) * 256u;
+  const bool act = base < P;  // wave-uniform
+  uint64_t x[4];
+  if (act) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t p = base + 64u * r + lane;
+      const uint64_t e = p < n ? ent[p] : 0ull;
+      x[r] = (CONV && p < n) ? ((e << 32) | (uint64_t)(~(uint32_t)(e >> 32))) : e;
+    }
+    const uint32_t top = P < 256u ? P : 256u;
+    for (uint32_t size = 2u; size <= top; size <<= 1)
+      for (uint32_t stride = size >> 1; stride > 0u; stride >>= 1)
+        chunk_step(x, base, size, stride, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t p = base + 64u * r + lane;
+      if (p < P) ent[p] = x[r];
+    }
+  }
+  for (uint32_t size = 512u; size <= P; size <<= 1) {
+    __syncthreads();
+    for (uint32_t stride = size >> 1; stride >= 256u; stride >>= 1) {
+      for (uint32_t t = tid; t < P / 2u; t += kBlock) {
+        const uint32_t i = 2u * t - (t & (stride - 1u)), j = i + stride;
+        const uint64_t a = ent[i], b = ent[j];
+        const bool up = (i & size) != 0u;
+        if (up ? (a > b) : (a < b)) {
+          ent[i] = b;
+          ent[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+    if (act) {  // P >= 512 here: every active wave's chunk lies inside [0, P)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = ent[base + 64u * r + lane];
+      for (uint32_t stride = 128u; stride > 0u; stride >>= 1) chunk_step(x, base, size, stride, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ent[base + 64u * r + lane] = x[r];
+    }
+  }
+  __syncthreads();
+}
+
+// The row's first k sorted entries (key << 32 | ~index): indices, and the
+// values read back by index (the key folds -0.0 into +0.0); status 0.
+__device__ __forceinline__ void select_write(const SelectParams& Q, int row, const uint64_t* ent) {
+  const int k = Q.k;
+  const gptr<const float> x = as_global(Q.in + (int64_t)row * Q.vocab);
+  const gptr<float> vo = as_global(Q.values + (int64_t)row * k);
+  const gptr<int32_t> io = as_global(Q.indices + (int64_t)row * k);
+  for (int j = threadIdx.x; j < k; j += kBlock) {
+    const uint32_t ix = ~(uint32_t)ent[j];
+    // (always a position of the row; the test keeps any read inside it)
+    const bool in = ix < (uint32_t)Q.vocab;
+    vo[j] = in ? x[ix] : __uint_as_float(0x7FC00000u);
+    io[j] = in ? (int32_t)ix : -1;
+  }
+  if (Q.row_status && threadIdx.x == 0) Q.row_status[row] = 0;
+}
+
+// Top-k selection (explainer, 选择 top-k 值本身: values and indices rather
+// than a sample), one work-group per row: tau = the k-th largest signed-order
+// key by the F4 threshold search; one pass counts, per 2048-value tile, the
+// values above tau and those equal to it, which fixes where the ties still
+// needed end (in index order); a second pass gathers exactly k entries
+// (key << 32 | ~index) into LDS; sort_desc puts them in descending key
+// order, equal keys by ascending index; the row's values and indices are
+// written.  A NaN makes the row invalid (NaN values, index -1, status 1).
+struct SelectSmem {
+  RedSmem red;
+  uint64_t ent[kSelectMax];
+  uint32_t ties[kMaxTiles];
+  uint32_t n;
+  uint32_t cut_tile;
+  uint32_t cut_need;
+};
+
+__device__ __forceinline__ void select_row(const SelectParams& Q, int row, SelectSmem& sm) {
+  const int V = Q.vocab, k = Q.k;
+  const int lane = lane_id(), wave = wave_id();
+  const RowRef r{as_global(Q.in + (int64_t)row * V), V, Q.vec_ok != 0};
+  Red acc = red_zero();
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = valid && idx + e < V;
+      acc.mx = max(acc.mx, in ? signed_key(v[e]) : 0u);
+      acc.s0 += (in && isnan(v[e])) ? 1u : 0u;
+    }
+  });
+  const Red s0 = block_reduce(acc, sm.red);
+  if (s0.s0 != 0u) {
+    select_invalid(Q, row);
+    return;
+  }
+  // the k-th largest key (k <= V); keys of real values are >= 1
+  const uint32_t tau = threshold_search<false, true>(r, 0u, s0.mx + 1u, (uint32_t)k, 0.0, sm.red);
+
+  // per tile: values equal to tau; above tau over the row
+  const int n_tiles = (V + kTile - 1) / kTile;
+  uint32_t gt = 0u;
+  for (int t = wave; t < n_tiles; t += kWaves) {
+    const int64_t base = (int64_t)t * kTile;
+    uint32_t eq = 0u;
+#pragma unroll
+    for (int q = 0; q < kTileChunks; ++q) {
+      float v[4];
+      const int64_t idx = base + q * (kWave * 4) + lane * 4;
+      load4(r, idx, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = idx + e < V ? signed_key(v[e]) : 0u;
+        eq += key == tau ? 1u : 0u;
+        gt += key > tau ? 1u : 0u;
+      }
+    }
+    eq = wave_sum(eq);
+    if (lane == 0) sm.ties[t] = eq;
+  }
+  Red cg = red_zero();
+  cg.s0 = gt;
+  const uint32_t above = block_reduce(cg, sm.red).s0;  // (its barriers also publish ties[])
+  if (wave == 0) {
+    // the tile where the ties still needed (k - above, in index order) end
+    const uint32_t need = (uint32_t)k - above;
+    uint32_t carry = 0u;
+    bool found = false;
+    for (int base = 0; base < n_tiles && !found; base += kWave) {
+      const int t = base + lane;
+      const uint32_t c = t < n_tiles ? sm.ties[t] : 0u;
+      const uint32_t incl = wave_incl_scan(c) + carry;
+      const uint64_t hit = __ballot(t < n_tiles && incl >= need && c > 0u);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        if (lane == 0) {
+          sm.cut_tile = (uint32_t)(base + l);
+          sm.cut_need = need - (lane_value(incl, l) - lane_value(c, l));
+        }
+        found = true;
+      }
+      carry = lane63(incl);
+    }
+    if (!found && lane == 0) {  // need == 0 cannot happen (count(key >= tau) >= k > above)
+      sm.cut_tile = 0u;
+      sm.cut_need = 0u;
+    }
+    if (lane == 0) sm.n = 0u;
+  }
+  __syncthreads();
+  const uint32_t cut = sm.cut_tile, cneed = sm.cut_need;
+
+  // gather: every value above tau; the ties of tiles before the cut; the
+  // first cneed ties (index order) of the cut tile
+  for (int t = wave; t < n_tiles; t += kWaves) {
+    const int64_t base = (int64_t)t * kTile;
+    uint32_t tie_carry = 0u;
+#pragma unroll
+    for (int q = 0; q < kTileChunks; ++q) {
+      float v[4];
+      const int64_t idx = base + q * (kWave * 4) + lane * 4;
+      load4(r, idx, v);
+      uint32_t key[4];
+      uint32_t my_ties = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[e] = idx + e < V ? signed_key(v[e]) : 0u;
+        my_ties += key[e] == tau ? 1u : 0u;
+      }
+      const uint32_t tincl = wave_incl_scan(my_ties);
+      uint32_t trank = tie_carry + tincl - my_ties;  // ties before this lane's first value
+      bool take[4];
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool tie = key[e] == tau;
+        take[e] = key[e] > tau || (tie && ((uint32_t)t < cut || ((uint32_t)t == cut && trank < cneed)));
+        trank += tie ? 1u : 0u;
+        cnt += take[e] ? 1u : 0u;
+      }
+      tie_carry += lane63(tincl);
+      const uint32_t cincl = wave_incl_scan(cnt);
+      uint32_t pos = 0u;
+      if (lane == kWave - 1 && cincl > 0u) pos = atomicAdd(&sm.n, cincl);
+      pos = __shfl(pos, kWave - 1) + cincl - cnt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (take[e] && pos < (uint32_t)kSelectMax)
+          sm.ent[pos] = ((uint64_t)key[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(idx + e));
+        pos += take[e] ? 1u : 0u;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t P = 1u;
+  while (P < (uint32_t)k) P <<= 1;
+  sort_desc<false>(sm.ent, (uint32_t)k, P);
+  select_write(Q, row, sm.ent);
+}
+
 }  // namespace stream
 }  // namespace dss

@@ -36,173 +36,10 @@ __global__ __launch_bounds__(kBlock) void stream_renorm_kernel(RenormParams P) {
   renorm_row<KIND>(P, blockIdx.x, red);
 }
 
-// Top-k selection (explainer, 选择 top-k 值本身: values and indices rather
-// than a sample), one work-group per row: tau = the k-th largest signed-order
-// key by the F4 threshold search; one pass counts, per 2048-value tile, the
-// values above tau and those equal to it, which fixes where the ties still
-// needed end (in index order); a second pass gathers exactly k entries
-// (key << 32 | ~index) into LDS; a bitonic sort puts them in descending key
-// order, equal keys by ascending index; the row's values and indices are
-// written.  A NaN makes the row invalid (NaN values, index -1, status 1).
-struct SelectSmem {
-  RedSmem red;
-  uint64_t ent[kSelectMax];
-  uint32_t ties[kMaxTiles];
-  uint32_t n;
-  uint32_t cut_tile;
-  uint32_t cut_need;
-};
-
+// Top-k selection, one work-group per row (select_row, stream_device.h).
 __global__ __launch_bounds__(kBlock) void stream_select_kernel(SelectParams Q) {
   __shared__ SelectSmem sm;
-  const int row = blockIdx.x, V = Q.vocab, k = Q.k;
-  const int lane = lane_id(), wave = wave_id(), tid = threadIdx.x;
-  const RowRef r{as_global(Q.in + (int64_t)row * V), V, Q.vec_ok != 0};
-  const gptr<float> vo = as_global(Q.values + (int64_t)row * k);
-  const gptr<int32_t> io = as_global(Q.indices + (int64_t)row * k);
-  Red acc = red_zero();
-  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool in = valid && idx + e < V;
-      acc.mx = max(acc.mx, in ? signed_key(v[e]) : 0u);
-      acc.s0 += (in && isnan(v[e])) ? 1u : 0u;
-    }
-  });
-  const Red s0 = block_reduce(acc, sm.red);
-  if (s0.s0 != 0u) {
-    for (int j = tid; j < k; j += kBlock) {
-      vo[j] = __uint_as_float(0x7FC00000u);
-      io[j] = -1;
-    }
-    if (Q.row_status && tid == 0) Q.row_status[row] = 1;
-    return;
-  }
-  // the k-th largest key (k <= V); keys of real values are >= 1
-  const uint32_t tau = threshold_search<false, true>(r, 0u, s0.mx + 1u, (uint32_t)k, 0.0, sm.red);
-
-  // per tile: values equal to tau; above tau over the row
-  const int n_tiles = (V + kTile - 1) / kTile;
-  uint32_t gt = 0u;
-  for (int t = wave; t < n_tiles; t += kWaves) {
-    const int64_t base = (int64_t)t * kTile;
-    uint32_t eq = 0u;
-#pragma unroll
-    for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
-      const int64_t idx = base + q * (kWave * 4) + lane * 4;
-      load4(r, idx, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = idx + e < V ? signed_key(v[e]) : 0u;
-        eq += key == tau ? 1u : 0u;
-        gt += key > tau ? 1u : 0u;
-      }
-    }
-    eq = wave_sum(eq);
-    if (lane == 0) sm.ties[t] = eq;
-  }
-  Red cg = red_zero();
-  cg.s0 = gt;
-  const uint32_t above = block_reduce(cg, sm.red).s0;  // (its barriers also publish ties[])
-  if (wave == 0) {
-    // the tile where the ties still needed (k - above, in index order) end
-    const uint32_t need = (uint32_t)k - above;
-    uint32_t carry = 0u;
-    bool found = false;
-    for (int base = 0; base < n_tiles && !found; base += kWave) {
-      const int t = base + lane;
-      const uint32_t c = t < n_tiles ? sm.ties[t] : 0u;
-      const uint32_t incl = wave_incl_scan(c) + carry;
-      const uint64_t hit = __ballot(t < n_tiles && incl >= need && c > 0u);
-      if (hit) {
-        const int l = __ffsll((long long)hit) - 1;
-        if (lane == 0) {
-          sm.cut_tile = (uint32_t)(base + l);
-          sm.cut_need = need - (lane_value(incl, l) - lane_value(c, l));
-        }
-        found = true;
-      }
-      carry = lane63(incl);
-    }
-    if (!found && lane == 0) {  // need == 0 cannot happen (count(key >= tau) >= k > above)
-      sm.cut_tile = 0u;
-      sm.cut_need = 0u;
-    }
-    if (lane == 0) sm.n = 0u;
-  }
-  __syncthreads();
-  const uint32_t cut = sm.cut_tile, cneed = sm.cut_need;
-
-  // gather: every value above tau; the ties of tiles before the cut; the
-  // first cneed ties (index order) of the cut tile
-  for (int t = wave; t < n_tiles; t += kWaves) {
-    const int64_t base = (int64_t)t * kTile;
-    uint32_t tie_carry = 0u;
-#pragma unroll
-    for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
-      const int64_t idx = base + q * (kWave * 4) + lane * 4;
-      load4(r, idx, v);
-      uint32_t key[4];
-      uint32_t my_ties = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[e] = idx + e < V ? signed_key(v[e]) : 0u;
-        my_ties += key[e] == tau ? 1u : 0u;
-      }
-      const uint32_t tincl = wave_incl_scan(my_ties);
-      uint32_t trank = tie_carry + tincl - my_ties;  // ties before this lane's first value
-      bool take[4];
-      uint32_t cnt = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool tie = key[e] == tau;
-        take[e] = key[e] > tau || (tie && ((uint32_t)t < cut || ((uint32_t)t == cut && trank < cneed)));
-        trank += tie ? 1u : 0u;
-        cnt += take[e] ? 1u : 0u;
-      }
-      tie_carry += lane63(tincl);
-      const uint32_t cincl = wave_incl_scan(cnt);
-      uint32_t pos = 0u;
-      if (lane == kWave - 1 && cincl > 0u) pos = atomicAdd(&sm.n, cincl);
-      pos = __shfl(pos, kWave - 1) + cincl - cnt;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (take[e] && pos < (uint32_t)kSelectMax)
-          sm.ent[pos] = ((uint64_t)key[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(idx + e));
-        pos += take[e] ? 1u : 0u;
-      }
-    }
-  }
-  __syncthreads();
-  // pad to a power of two with zeros (below every real entry), then sort
-  uint32_t P = 1u;
-  while (P < (uint32_t)k) P <<= 1;
-  for (uint32_t j = (uint32_t)k + tid; j < P; j += kBlock) sm.ent[j] = 0ull;
-  __syncthreads();
-  for (uint32_t size = 2u; size <= P; size <<= 1) {
-    for (uint32_t stride = size >> 1; stride > 0u; stride >>= 1) {
-      for (uint32_t t = tid; t < P / 2u; t += kBlock) {
-        const uint32_t i = 2u * t - (t & (stride - 1u));
-        const uint32_t j = i + stride;
-        const uint64_t a = sm.ent[i], b = sm.ent[j];
-        const bool up = (i & size) != 0u;  // this block ascending (the final block descends)
-        if (up ? (a > b) : (a < b)) {
-          sm.ent[i] = b;
-          sm.ent[j] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // the values themselves are read back by index (the key folds -0.0 into +0.0)
-  for (int j = tid; j < k; j += kBlock) {
-    const int32_t ix = (int32_t)(0xFFFFFFFFu - (uint32_t)sm.ent[j]);
-    vo[j] = r.x[ix];
-    io[j] = ix;
-  }
-  if (Q.row_status && tid == 0) Q.row_status[row] = 0;
+  select_row(Q, blockIdx.x, sm);
 }
 
 // Probabilities from logits, one work-group per row, three passes: the

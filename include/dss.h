@@ -140,6 +140,7 @@ extern "C" {
 #define DSS_OP_TOP_K_MASK_LOGITS 7
 #define DSS_OP_TOP_K_TOP_P_FROM_LOGITS 8
 #define DSS_OP_SOFTMAX           9
+#define DSS_OP_TOP_K_SELECT     10
 
 /* Inverse-transform sampling from each output's row ([Blog "逆变换采样"],
  * [Expl "不带过滤时：inverse transform sampling"]): u ~ U[0,1) (draw r = 0),
@@ -267,10 +268,15 @@ int dss_top_k_top_p_sampling_from_logits(const float* logits, int32_t rows, int3
  * [rows, k] device arrays.  Any float32 input (probabilities or logits,
  * +-inf allowed); a NaN makes the row invalid (NaN values, index -1,
  * row_status 1, nullable).  1 <= k <= vocab, else DSS_ERR_INVALID_ARG;
- * k > 4096 is DSS_ERR_UNSUPPORTED.  No workspace; flags are reserved (pass
- * 0).  One work-group per row. */
+ * k > 4096 is DSS_ERR_UNSUPPORTED.  For k <= 2048 on 16-byte aligned rows
+ * of at least 1024 values the split engine runs (one read of the row, the
+ * top-k set gathered as in sampling, then sorted); it needs the workspace of
+ * dss_workspace_size(DSS_OP_TOP_K_SELECT, rows, vocab, rows, flags).
+ * Otherwise, or with DSS_FLAG_STREAMING, one work-group per row (no
+ * workspace).  Other flags are ignored. */
 int dss_top_k(const float* x, int32_t rows, int32_t vocab, int32_t k, float* values,
-              int32_t* indices, uint8_t* row_status, uint32_t flags, void* stream);
+              int32_t* indices, uint8_t* row_status, uint32_t flags, void* workspace,
+              size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace an op needs for these sizes and flags (0 if none). */
 size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,

@@ -58,7 +58,8 @@ def test_header_constants_match_binding():
             "top_p_renorm_probs": "DSS_OP_TOP_P_RENORM",
             "top_k_mask_logits": "DSS_OP_TOP_K_MASK_LOGITS",
             "top_k_top_p_sampling_from_logits": "DSS_OP_TOP_K_TOP_P_FROM_LOGITS",
-            "softmax": "DSS_OP_SOFTMAX"}[op]) == i
+            "softmax": "DSS_OP_SOFTMAX",
+            "top_k": "DSS_OP_TOP_K_SELECT"}[op]) == i
 
 
 def _plain(lib, probs=FAKE, rows=1, vocab=8, indices=NULL, n=1, samples=FAKE, flags=0,
@@ -138,8 +139,9 @@ def test_workspace_size_and_strings():
 def test_top_k_selection_validation():
     lib = _lib.load()
 
-    def call(x=FAKE, rows=1, vocab=8, k=3, values=FAKE, indices=FAKE, flags=0):
-        return lib.dss_top_k(x, rows, vocab, k, values, indices, NULL, flags, NULL)
+    def call(x=FAKE, rows=1, vocab=8, k=3, values=FAKE, indices=FAKE, flags=0, ws=NULL,
+             ws_bytes=0):
+        return lib.dss_top_k(x, rows, vocab, k, values, indices, NULL, flags, ws, ws_bytes, NULL)
     assert call(x=NULL) == _lib.DSS_ERR_INVALID_ARG
     assert call(values=NULL) == _lib.DSS_ERR_INVALID_ARG
     assert call(indices=NULL) == _lib.DSS_ERR_INVALID_ARG
@@ -149,6 +151,16 @@ def test_top_k_selection_validation():
     assert call(flags=0x100) == _lib.DSS_ERR_INVALID_ARG
     assert call(vocab=10000, k=4097) == _lib.DSS_ERR_UNSUPPORTED
     assert call(x=NULL, values=NULL, indices=NULL, rows=0) == _lib.DSS_OK
+    # B=64, V=151936: the split engine (k <= 2048) needs its hand-off area;
+    # the one-work-group path (k above 2048, or STREAMING) needs none
+    need = lib.dss_workspace_size(10, 64, 151936, 64, 0)
+    assert need > 0
+    assert lib.dss_workspace_size(10, 64, 151936, 64, _lib.DSS_FLAG_STREAMING) == 0
+    assert call(rows=64, vocab=151936, k=50) == _lib.DSS_ERR_WORKSPACE
+    assert call(rows=64, vocab=151936, k=50, ws=FAKE, ws_bytes=need - 1) == _lib.DSS_ERR_WORKSPACE
+    for kw in (dict(k=3000), dict(k=50, flags=_lib.DSS_FLAG_STREAMING),
+               dict(k=50, ws=FAKE, ws_bytes=need)):
+        assert call(rows=64, vocab=151936, **kw) != _lib.DSS_ERR_WORKSPACE, kw
 
 
 def test_logits_sampling_validation():

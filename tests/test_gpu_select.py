@@ -1,6 +1,11 @@
 """GPU parity of top-k selection (values and indices) against the oracle:
 bit-exact values and exact indices (values descending, equal values by
-ascending index, -0.0 equal to +0.0; [Expl] "选择 top-k 值本身")."""
+ascending index, -0.0 equal to +0.0; [Expl] "选择 top-k 值本身").
+
+k <= 2048 on aligned rows of >= 1024 values runs the split engine (its
+top-k set sorted); rows whose lists overflow (flat rows, huge tie groups)
+fall back inside that kernel to the one-work-group selection, which also
+serves k > 2048, unaligned rows and DSS_FLAG_STREAMING."""
 
 import numpy as np
 import pytest
@@ -28,11 +33,24 @@ def _check(x, k, vals, idx, status=None):
             assert status[r] == 0
 
 
-@pytest.mark.parametrize("k", [1, 50, 1024, 4096])
+@pytest.mark.parametrize("k", [1, 50, 1024, 2048, 2049, 4096])
 def test_top_k_full_size_logits(k):
     x = si.logits_rows(np.random.default_rng(k), 64, 151936, 2.0)
     vals, idx = dss.top_k(gpu(x), k)
     _check(x, k, host(vals), host(idx))
+
+
+@pytest.mark.parametrize("k", [1, 64, 257, 2048])
+def test_top_k_split_and_streaming_agree(k):
+    """The two engines on the same rows (every tie rule exercised by rows of
+    few distinct values), bit for bit, and both against the oracle."""
+    rng = np.random.default_rng(40 + k)
+    x = (rng.integers(-50, 50, size=(16, 32768)) / 8.0).astype(np.float32)
+    a = dss.top_k(gpu(x), k)
+    b = dss.top_k(gpu(x), k, flags=dss.DSS_FLAG_STREAMING)
+    for u, v in zip(a, b):
+        assert np.array_equal(host(u).view(np.uint32), host(v).view(np.uint32))
+    _check(x, k, host(a[0]), host(a[1]))
 
 
 def test_top_k_probabilities():
