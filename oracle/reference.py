@@ -47,6 +47,19 @@ Readings of the pages (each also listed in the design doc):
 * R19 top-k selection ([Expl] "选择 top-k 值本身": values and indices, not a
   sample): the k largest values of a row in descending order, equal values
   by ascending index, -0.0 equal to +0.0; a NaN makes the row invalid.
+* R20 chain speculative verification ([Blog] "社区采用和其他应用" names chain
+  speculative sampling as a use of the same rejection sampling and gives no
+  algorithm; the standard one, Leviathan, Kalman & Matias 2023 and Chen et
+  al. 2023, is taken): for j = 0 .. n-1 in order the draft token d_j is
+  accepted iff u_j * q_j(d_j) < p_j(d_j), u_j the row's draw j; at the first
+  rejection j* the emitted token is one inverse-transform draw (draw n) from
+  the residual max(0, p_j* - q_j*), taken exactly, or from p_j* when that
+  residual is zero everywhere; with every draft accepted a bonus token is
+  drawn (draw n) from p_n.  Output: d_0 .. d_{j*-1}, the drawn token, then
+  -1; accepted = j* (n with the bonus).  Invalid (all -1, accepted 0): a
+  draft id outside [0, V), a sign bit / NaN / inf in an examined p_j(d_j) or
+  q_j(d_j) or anywhere in the rows the final draw reads, or a zero total in
+  the row it draws from.
 * R17 the "joint" order ([Blog] footnote on the filter options; [Expl]
   "Top-k 与 top-p 的组合顺序会改变分布") checks the top-k and the top-p
   condition together in every rejection round; the top-p condition then
@@ -357,6 +370,71 @@ def top_k_select(row, k):
     key = row.astype(np.float64) + 0.0            # -0.0 -> +0.0
     order = np.lexsort((np.arange(row.size), -key))[:int(k)]
     return True, row[order], order.astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# chain speculative verification (R20)
+# ----------------------------------------------------------------------------
+
+def _finite_nonneg(values):
+    """No sign bit (negative or -0.0), NaN or inf among float32 values."""
+    bits = np.atleast_1d(np.asarray(values, dtype=np.float32)).view(np.uint32)
+    return not np.any(bits >= np.uint32(0x7F800000))
+
+
+def draw_from_units(units, a53):
+    """Inverse transform on exact weights: the first index whose prefix
+    exceeds floor(u * Z), u = a53 / 2**53 (the rule of ``CdfTable``); -1 when
+    the total is zero."""
+    prefix = list(accumulate(units))
+    if not prefix or prefix[-1] == 0:
+        return -1
+    thr = (int(a53) * prefix[-1]) >> 53
+    return bisect_right(prefix, thr)
+
+
+def chain_speculative(draft_probs, draft_ids, target_probs, a53s):
+    """One row of chain speculative verification (R20).
+
+    draft_probs [n, V] (q), draft_ids [n], target_probs [n + 1, V] (p), all
+    float32 / integer; a53s: the n + 1 draws (53-bit integers) of the row,
+    draw j for the acceptance test at position j, draw n for the final
+    token.  Returns (valid, tokens [n + 1] int32, accepted).
+    """
+    q = np.asarray(draft_probs, dtype=np.float32)
+    p = np.asarray(target_probs, dtype=np.float32)
+    ids = np.asarray(draft_ids).astype(np.int64)
+    n, V = q.shape
+    bad = (False, np.full(n + 1, -1, dtype=np.int32), 0)
+    out = []
+    for j in range(n):
+        d = int(ids[j])
+        if not 0 <= d < V:
+            return bad
+        pj, qj = p[j, d], q[j, d]
+        if not (_finite_nonneg(pj) and _finite_nonneg(qj)):
+            return bad
+        # u * q < p with u = a / 2**53, in integers
+        (qu,), (pu,) = exact_units([qj]), exact_units([pj])
+        if int(a53s[j]) * qu < pu << 53:
+            out.append(d)
+            continue
+        if not (_finite_nonneg(p[j]) and _finite_nonneg(q[j])):
+            return bad
+        res = [max(0, a - b) for a, b in zip(exact_units(p[j]), exact_units(q[j]))]
+        if sum(res) == 0:
+            res = exact_units(p[j])
+        tok = draw_from_units(res, a53s[n])
+        if tok < 0:
+            return bad
+        out += [tok] + [-1] * (n - j)
+        return True, np.array(out, dtype=np.int32), j
+    if not _finite_nonneg(p[n]):
+        return bad
+    tok = draw_from_units(exact_units(p[n]), a53s[n])
+    if tok < 0:
+        return bad
+    return True, np.array(out + [tok], dtype=np.int32), n
 
 
 # ----------------------------------------------------------------------------

@@ -495,3 +495,155 @@ def test_batch_thresholds_indices():
                                num_outputs=4)
     assert out[0] == (True, 0.5) and out[1] == (True, np.float32(0.7))
     assert out[2] == (False, None) and out[3] == (False, None)
+
+
+# ----------------------------------------------------------------------------
+# chain speculative verification (R20)
+# ----------------------------------------------------------------------------
+
+def _emitted_law_grid(q0, p0, p1, N=4096):
+    """Law of the first emitted token of a one-draft chain, the draft drawn
+    from q0, both uniforms integrated on an N-point midpoint grid: the oracle
+    is called as a black box, once per (draft, grid point)."""
+    V = q0.size
+    grid = [((2 * i + 1) << 52) // N for i in range(N)]  # (i + 1/2) / N * 2**53
+    q = q0[None, :]
+    p = np.stack([p0, p1])
+    law = np.zeros(V)
+    for d in range(V):
+        if q0[d] == 0:
+            continue
+        acc = 0
+        rej_any = None
+        for a in grid:
+            ok, tok, n_acc = ref.chain_speculative(q, [d], p, [a, grid[0]])
+            assert ok
+            if n_acc == 1:
+                assert tok[0] == d
+                acc += 1
+            else:
+                rej_any = a
+        law[d] += float(q0[d]) * acc / N
+        if rej_any is not None:
+            res = np.zeros(V)
+            for b in grid:
+                ok, tok, n_acc = ref.chain_speculative(q, [d], p, [rej_any, b])
+                assert ok and n_acc == 0 and tok[1] == -1
+                res[tok[0]] += 1.0 / N
+            law += float(q0[d]) * (N - acc) / N * res
+    return law
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_chain_speculative_preserves_target_law(case):
+    """Leviathan, Kalman & Matias 2023 (Theorem / appendix A.1), Chen et al.
+    2023 (Theorem 1): with the draft drawn from q, the emitted token is
+    distributed exactly as p.  A wrong acceptance test or a residual other
+    than max(0, p - q) moves the law by far more than the grid error."""
+    rng = np.random.default_rng(500 + case)
+    V = 6
+    q0 = rng.dirichlet(np.ones(V) * 0.7).astype(np.float32)
+    p0 = rng.dirichlet(np.ones(V) * 0.7).astype(np.float32)
+    if case == 2:
+        q0[3] = 0.0                          # a token the draft never proposes
+        p0[5] = 0.0                          # and one the target never emits
+        q0 = (q0 / q0.astype(np.float64).sum()).astype(np.float32)
+        p0 = (p0 / p0.astype(np.float64).sum()).astype(np.float32)
+    p1 = rng.dirichlet(np.ones(V)).astype(np.float32)
+    law = _emitted_law_grid(q0, p0, p1)
+    target = p0.astype(np.float64) / p0.astype(np.float64).sum()
+    # the draft law is q0 / sum(q0), which sums to one up to float32 rounding
+    assert np.abs(law / law.sum() - target).max() < 3.0 / 4096, (law, target)
+
+
+def test_chain_speculative_identical_models_accept_everything():
+    """q = p: u * q < p for every u < 1, so every draft is accepted and the
+    bonus token is the inverse-transform draw from p_n."""
+    rng = np.random.default_rng(7)
+    n, V = 5, 40
+    p = rng.dirichlet(np.ones(V), size=n + 1).astype(np.float32)
+    ids = rng.integers(0, V, size=n)
+    for a_fin in (0, 1 << 52, (1 << 53) - 1):
+        a53s = [int(x) for x in rng.integers(0, 1 << 53, size=n, dtype=np.uint64)] + [a_fin]
+        ok, tok, acc = ref.chain_speculative(p[:n], ids, p, a53s)
+        assert ok and acc == n
+        assert list(tok[:n]) == list(ids)
+        assert tok[n] == ref.CdfTable(p[n], p[n] > 0).draw(a_fin)
+
+
+def test_chain_speculative_one_hot_draft():
+    """q_0 = e_d: the draft is accepted iff u < p(d); on rejection the
+    residual max(0, p - e_d) is p without token d (closed form)."""
+    p0 = np.array([0.125, 0.5, 0.25, 0.125], dtype=np.float32)
+    p = np.stack([p0, p0])
+    q = np.zeros((1, 4), dtype=np.float32)
+    d = 1
+    q[0, d] = 1.0
+    half = 1 << 52                                    # u = 1/2 = p(d)
+    assert ref.chain_speculative(q, [d], p, [half - 1, 0])[2] == 1
+    ok, tok, acc = ref.chain_speculative(q, [d], p, [half, 0])
+    assert ok and acc == 0
+    without = p0.copy()
+    without[d] = 0
+    for a in (0, 1 << 51, 3 << 51, (1 << 53) - 1):
+        tok = ref.chain_speculative(q, [d], p, [half, a])[1]
+        assert tok[0] == ref.CdfTable(without, without > 0).draw(a)
+        assert tok[0] != d
+
+
+def test_chain_speculative_zero_target_and_zero_residual():
+    """p(d) = 0 rejects for every u (even u = 0); a residual that is zero
+    everywhere (p <= q, an unnormalised p) falls back to a draw from p."""
+    q = np.array([[0.25, 0.25, 0.5]], dtype=np.float32)
+    p = np.array([[0.0, 0.5, 0.5], [1.0, 0.0, 0.0]], dtype=np.float32)
+    ok, tok, acc = ref.chain_speculative(q, [0], p, [0, 0])
+    assert ok and acc == 0 and tok[0] in (1, 2)
+    ph_ = np.array([[0.125, 0.125, 0.25]], dtype=np.float32)   # p = q / 2
+    pp = np.concatenate([ph_, p[1:]])
+    ok, tok, acc = ref.chain_speculative(q, [2], pp, [1 << 52, 1 << 52])  # u = 1/2: rejected
+    assert ok and acc == 0
+    assert tok[0] == ref.CdfTable(ph_[0], ph_[0] > 0).draw(1 << 52)
+    assert ref.chain_speculative(q, [2], pp, [(1 << 52) - 1, 0])[2] == 1
+
+
+def test_chain_speculative_two_positions_monte_carlo():
+    """A chain of two drafts with the drafts drawn from q: the token emitted
+    at position 1, given position 0 accepted its draft, follows p_1; the
+    bonus, given both accepted, follows p_2 (chi-square, 20000 chains)."""
+    rng = np.random.default_rng(11)
+    V = 5
+    q = rng.dirichlet(np.ones(V), size=2).astype(np.float32)
+    p = rng.dirichlet(np.ones(V), size=3).astype(np.float32)
+    pos1, bonus = np.zeros(V), np.zeros(V)
+    cq = np.cumsum(q.astype(np.float64), axis=1)
+    for _ in range(20000):
+        ids = [min(int(np.searchsorted(cq[j], rng.random() * cq[j, -1], side="right")), V - 1)
+               for j in range(2)]
+        a53s = [int(x) for x in rng.integers(0, 1 << 53, size=3, dtype=np.uint64)]
+        ok, tok, acc = ref.chain_speculative(q, ids, p, a53s)
+        assert ok
+        if acc >= 1:
+            pos1[tok[1]] += 1
+        if acc == 2:
+            bonus[tok[2]] += 1
+    for counts, row in ((pos1, p[1]), (bonus, p[2])):
+        expect = counts.sum() * row.astype(np.float64) / row.astype(np.float64).sum()
+        assert stats.chisquare(counts, expect).pvalue > 1e-3
+
+
+def test_chain_speculative_invalid_rows():
+    q = np.array([[0.5, 0.5, 0.0]], dtype=np.float32)
+    p = np.array([[0.25, 0.75, 0.0], [0.5, 0.5, 0.0]], dtype=np.float32)
+    for ids in ([-1], [3]):                                  # draft id outside [0, V)
+        assert not ref.chain_speculative(q, ids, p, [0, 0])[0]
+    pn = p.copy()
+    pn[0, 2] = np.nan                                        # in the rejected row
+    assert not ref.chain_speculative(q, [0], pn, [(1 << 53) - 1, 0])[0]
+    assert ref.chain_speculative(q, [0], pn, [0, 0])[0]      # accepted: row not read
+    pz = p.copy()
+    pz[1, 2] = -0.0                                          # in the bonus row
+    assert not ref.chain_speculative(q, [0], pz, [0, 0])[0]
+    p0 = p.copy()
+    p0[1] = 0.0                                              # bonus row with no mass
+    ok, tok, acc = ref.chain_speculative(q, [0], p0, [0, 0])
+    assert not ok and list(tok) == [-1, -1] and acc == 0
