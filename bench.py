@@ -203,6 +203,20 @@ def extra_configs(dss, si, lib, dev):
     for kk in (50, 1024):
         out[f"logits B=64 V=151936 top_k selection (k={kk}; values + indices)"] = entry(
             kernel_times(lib, lambda: dss.top_k(Lg, kk), 50), B * V * 4 + B * kk * 8)
+    # chain speculative verification: one read of the two rows a rejection
+    # draws from (p_j*, q_j*), or of p_n for the bonus token, per row
+    w = si.speculative()
+    Q, Ids, Pt = g(w["q"]), g(w["ids"]), g(w["p"])
+    Sd = g(w["seeds"].view(np.int64))
+    t = kernel_times(lib, lambda: dss.chain_speculative_sampling(Q, Ids, Pt, seed=Sd, offset=0), 50)
+    _, acc = dss.chain_speculative_sampling(Q, Ids, Pt, seed=Sd, offset=0)
+    acc = acc.cpu().numpy()
+    nd = w["ids"].shape[1]
+    Vs = w["p"].shape[2]
+    nbytes = int(sum(8 * Vs if a < nd else 4 * Vs for a in acc))
+    out["speculative B=64 n=4 V=151936 chain_speculative_sampling"] = entry(
+        t, nbytes, mean_accepted=float(acc.mean()), rejected_rows=int((acc < nd).sum()))
+    del Q, Pt
     w = si.latency()
     P = g(w["probs"])
     t = kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_probs(P, 50, 0.9, seed=3,

@@ -24,7 +24,7 @@ __all__ = [
     "sampling_from_probs", "top_k_sampling_from_probs", "top_p_sampling_from_probs",
     "min_p_sampling_from_probs", "top_k_top_p_sampling_from_probs",
     "top_k_renorm_probs", "top_p_renorm_probs", "top_k_mask_logits",
-    "softmax", "top_k_top_p_sampling_from_logits", "top_k",
+    "softmax", "top_k_top_p_sampling_from_logits", "top_k", "chain_speculative_sampling",
     "DssError", "DSS_FLAG_FROM_ZERO", "DSS_FLAG_STREAMING", "DSS_FLAG_ORDER_JOINT",
     "DSS_FLAG_SINGLE_PIVOT",
 ]
@@ -230,6 +230,47 @@ def top_k(x, k, *, return_status=False, flags=0):
                                  indices.data_ptr(), _ptr(status), flags, ws, ws_bytes,
                                  _stream(device)), "top_k")
     return (values, indices, status) if return_status else (values, indices)
+
+
+def chain_speculative_sampling(draft_probs, draft_token_ids, target_probs, *, seed=None,
+                               offset=0, return_valid=False, flags=0):
+    """Verify a chain of draft tokens per row against the target model.
+
+    draft_probs [rows, n, vocab] float32, draft_token_ids [rows, n] int32,
+    target_probs [rows, n + 1, vocab] float32.  Returns (tokens [rows, n + 1]
+    int32: the accepted drafts, then the residual or bonus token, then -1;
+    accepted [rows] int32) and, with return_valid, valid [rows] uint8."""
+    def _chk(t, name, dtype, dims):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype
+                and t.dim() == dims and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dtype} {dims}-D GPU tensor")
+    _chk(target_probs, "target_probs", torch.float32, 3)
+    _chk(draft_probs, "draft_probs", torch.float32, 3)
+    _chk(draft_token_ids, "draft_token_ids", torch.int32, 2)
+    rows, n1, vocab = target_probs.shape
+    n = n1 - 1
+    device = target_probs.device
+    if tuple(draft_probs.shape) != (rows, n, vocab) or tuple(draft_token_ids.shape) != (rows, n) \
+            or draft_probs.device != device or draft_token_ids.device != device:
+        raise ValueError("draft_probs [rows, n, vocab] and draft_token_ids [rows, n] must "
+                         "match target_probs [rows, n + 1, vocab] on one device")
+    if seed is None:
+        seed = int(torch.randint(0, 2**62, (1,)).item())
+    seed_arr, seed_val = _rng(seed, rows, device, "seed")
+    off_arr, off_val = _rng(offset, rows, device, "offset")
+    tokens = torch.empty(rows, n + 1, dtype=torch.int32, device=device)
+    accepted = torch.empty(rows, dtype=torch.int32, device=device)
+    valid = torch.empty(rows, dtype=torch.uint8, device=device) if return_valid else None
+    lib = _lib.load()
+    ws, ws_bytes = _workspace(device, lib.dss_workspace_size(
+        OP_IDS["chain_speculative_sampling"], rows, vocab, n, flags))
+    with torch.cuda.device(device):
+        _lib.check(lib.dss_chain_speculative_sampling(
+            draft_probs.data_ptr(), draft_token_ids.data_ptr(), target_probs.data_ptr(), rows, n,
+            vocab, _ptr(seed_arr), seed_val, _ptr(off_arr), off_val, tokens.data_ptr(),
+            accepted.data_ptr(), _ptr(valid), flags, ws, ws_bytes, _stream(device)),
+            "chain_speculative_sampling")
+    return (tokens, accepted, valid) if return_valid else (tokens, accepted)
 
 
 def top_k_mask_logits(logits, top_k, *, out=None, return_status=False, flags=0):

@@ -35,6 +35,7 @@ OP_IDS = {
     "top_k_top_p_sampling_from_logits": 8,
     "softmax": 9,
     "top_k": 10,
+    "chain_speculative_sampling": 11,
 }
 
 _P = ctypes.c_void_p
@@ -61,6 +62,8 @@ SIGNATURES = {
     "dss_top_k": ([_P, _I32, _I32, _I32, _P, _P, _P, _U32, _P, _SZ, _P], ctypes.c_int),
     "dss_top_k_top_p_sampling_from_logits": (_HEAD + [_P, _I32, _P, _F32, _P, _F32] + _TAIL,
                                              ctypes.c_int),
+    "dss_chain_speculative_sampling": ([_P, _P, _P, _I32, _I32, _I32, _P, _U64, _P, _U64,
+                                        _P, _P, _P, _U32, _P, _SZ, _P], ctypes.c_int),
     "dss_workspace_size": ([_I32, _I32, _I32, _I32, _U32], ctypes.c_size_t),
     "dss_strerror": ([_I32], ctypes.c_char_p),
     "dss_version": ([], ctypes.c_int32),

@@ -321,6 +321,33 @@ DSS_EXPORT int dss_top_k(const float* x, int32_t rows, int32_t vocab, int32_t k,
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 
+DSS_EXPORT int dss_chain_speculative_sampling(
+    const float* draft_probs, const int32_t* draft_token_ids, const float* target_probs,
+    int32_t rows, int32_t num_draft, int32_t vocab, const uint64_t* seed_arr, uint64_t seed,
+    const uint64_t* offset_arr, uint64_t offset, int32_t* output_tokens, int32_t* accepted,
+    uint8_t* valid, uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
+  if (rows < 0 || vocab <= 0 || num_draft < 0) return DSS_ERR_INVALID_ARG;
+  if (vocab > DSS_MAX_VOCAB || num_draft > dss::kSpecMaxN) return DSS_ERR_UNSUPPORTED;
+  if (rows == 0) return DSS_OK;
+  if (!target_probs || !output_tokens || !accepted) return DSS_ERR_INVALID_ARG;
+  if (num_draft > 0 && (!draft_probs || !draft_token_ids)) return DSS_ERR_INVALID_ARG;
+  const int vec = vocab % 4 == 0 && aligned16(target_probs) &&
+                  (num_draft == 0 || aligned16(draft_probs));
+  const dss::SpecPlan plan = dss::plan_spec(rows, vocab, num_draft, vec);
+  if (plan.W == 0) return DSS_ERR_UNSUPPORTED;
+  if (workspace_bytes < plan.workspace || (plan.workspace > 0 && !workspace))
+    return DSS_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+  const dss::SpecParams sp{draft_probs, draft_token_ids, target_probs, rows, num_draft, vocab,
+                           seed_arr, seed, offset_arr, offset, output_tokens, accepted, valid};
+  return dss::launch_spec(sp, plan, workspace, static_cast<hipStream_t>(stream),
+                          timing_events()) == hipSuccess
+             ? DSS_OK
+             : DSS_ERR_HIP;
+}
+
 DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                                      int32_t num_outputs, uint32_t flags) {
   // sized for 16-byte aligned rows; an unaligned call runs the streaming
@@ -331,6 +358,11 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
     if (rows <= 0) return 0;
     const int kind = op == DSS_OP_TOP_K_RENORM ? dss::kRenormTopK : dss::kMaskLogits;
     return dss::plan_split_renorm(kind, rows, vocab, flags, vec).workspace;
+  }
+  if (op == DSS_OP_CHAIN_SPECULATIVE) {
+    // num_outputs is the number of draft tokens per row here
+    if (rows <= 0) return 0;
+    return dss::plan_spec(rows, vocab, num_outputs, vec).workspace;
   }
   if (op == DSS_OP_TOP_K_SELECT) {
     if (rows <= 0) return 0;

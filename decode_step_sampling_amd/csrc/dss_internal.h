@@ -163,6 +163,38 @@ struct SelectParams {
   int32_t vec_ok;
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t s, const LaunchEvents& ev);
+
+// Chain speculative verification (spec_kernels.hip).
+constexpr int kSpecMaxN = 64;             // draft tokens per row (one lane each)
+constexpr int kSpecMaxW = 16;             // slices per row
+constexpr int kSpecRowsPerLaunch = 2048;  // the split engine's counter block
+struct SpecParams {
+  const float* q;          // [rows][n][vocab] draft probabilities
+  const int32_t* ids;      // [rows][n] draft tokens
+  const float* p;          // [rows][n + 1][vocab] target probabilities
+  int32_t rows, n, vocab;
+  const uint64_t* seed_arr;
+  uint64_t seed;
+  const uint64_t* offset_arr;
+  uint64_t offset;
+  int32_t* tokens;         // [rows][n + 1]
+  int32_t* accepted;       // [rows]
+  uint8_t* valid;          // [rows], nullable
+};
+struct SpecPlan {
+  int W;              // slices per row (0: not supported)
+  int Lv;             // slice length in 16-byte vectors
+  int CH;             // vectors of one wave's chunk
+  int per_launch;     // rows per launch
+  size_t workspace;   // bytes
+  uint32_t* ctr;      // [kSpecRowsPerLaunch] arrival counters (zero between calls)
+  uint32_t* gen;      // [kSpecRowsPerLaunch] generation numbers
+  uint32_t* hdr;      // [per_launch][W][4]
+  double* masses;     // [per_launch][W][16]
+};
+SpecPlan plan_spec(int rows, int vocab, int n, int vec_ok);
+hipError_t launch_spec(const SpecParams& sp, const SpecPlan& plan, void* workspace,
+                       hipStream_t s, const LaunchEvents& ev);
 // Top-k selection on the split engine (k <= 2048): the top-k set that the
 // engine gathers, sorted; rows whose lists overflow fall back to the
 // one-work-group selection inside the same kernel.  W == 0: not eligible.

@@ -141,6 +141,7 @@ extern "C" {
 #define DSS_OP_TOP_K_TOP_P_FROM_LOGITS 8
 #define DSS_OP_SOFTMAX           9
 #define DSS_OP_TOP_K_SELECT     10
+#define DSS_OP_CHAIN_SPECULATIVE 11  /* num_outputs = draft tokens per row */
 
 /* Inverse-transform sampling from each output's row ([Blog "逆变换采样"],
  * [Expl "不带过滤时：inverse transform sampling"]): u ~ U[0,1) (draw r = 0),
@@ -277,6 +278,38 @@ int dss_top_k_top_p_sampling_from_logits(const float* logits, int32_t rows, int3
 int dss_top_k(const float* x, int32_t rows, int32_t vocab, int32_t k, float* values,
               int32_t* indices, uint8_t* row_status, uint32_t flags, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/* Chain speculative verification ([Blog "社区采用和其他应用"] names chain
+ * speculative sampling as a use of the same rejection sampling; the pages
+ * give no algorithm, so the standard one is taken: Leviathan, Kalman &
+ * Matias 2023, Chen et al. 2023).  Row r holds num_draft draft tokens
+ * draft_token_ids[r, j] with draft distributions draft_probs[r, j, :] (q_j)
+ * and num_draft + 1 target distributions target_probs[r, j, :] (p_j), all
+ * C-contiguous device arrays, probabilities float32.  For j = 0, 1, ... the
+ * draft d_j is accepted iff u_j * q_j(d_j) < p_j(d_j) (decided exactly),
+ * u_j = draw r = j of the row's stream; at the first rejection j* one token
+ * is drawn (draw r = num_draft) by inverse transform from the residual
+ * max(0, p_j* - q_j*) (differences in float64), or from p_j* if that
+ * residual is zero everywhere; if every draft is accepted the bonus token is
+ * drawn (draw r = num_draft) from p_{num_draft}.  output_tokens[r, :]
+ * (num_draft + 1 entries) = d_0 .. d_{j*-1}, the drawn token, then -1;
+ * accepted[r] = j* (num_draft with the bonus); valid[r] = 1 (nullable).
+ * Seeds and offsets as in the sampling calls (per row).  A draft id outside
+ * [0, vocab), a negative / NaN / inf value among the examined p_j(d_j),
+ * q_j(d_j) or in the rows the final draw reads, or a final row with zero
+ * mass make the row invalid: tokens -1, accepted 0, valid 0.
+ * 0 <= num_draft <= 64, else DSS_ERR_UNSUPPORTED; vocab % 4 == 0 and 16-byte
+ * aligned probability arrays, else DSS_ERR_UNSUPPORTED.  Workspace:
+ * dss_workspace_size(DSS_OP_CHAIN_SPECULATIVE, rows, vocab, num_draft,
+ * flags); flags are reserved (pass 0).  Reads per row: 2 num_draft single
+ * values, then the one row (bonus) or two rows (residual) the draw needs. */
+int dss_chain_speculative_sampling(const float* draft_probs, const int32_t* draft_token_ids,
+                                   const float* target_probs, int32_t rows, int32_t num_draft,
+                                   int32_t vocab, const uint64_t* seed_arr, uint64_t seed,
+                                   const uint64_t* offset_arr, uint64_t offset,
+                                   int32_t* output_tokens, int32_t* accepted, uint8_t* valid,
+                                   uint32_t flags, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Bytes of workspace an op needs for these sizes and flags (0 if none). */
 size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,

@@ -21,12 +21,18 @@ Workloads (shapes, value distributions and parameter mixes as named):
   stress    B=512, V=256000 in three groups (171/171/170 rows): near-uniform
             (1 + U[-1e-3, 1e-3]) / V; peaked (0.99 at one random id, the rest
             equal); geometric chain p_i ~ (1 - 1e-6)^i; top_k=1000, top_p=0.95
+  speculative  B=64, n=4 draft tokens, V=151936: draft logits z_j ~ N(0, 2^2),
+            target logits z_j + N(0, 0.5^2) (position n: fresh N(0, 2^2)),
+            q_j = softmax(draft), p_j = softmax(target); draft tokens drawn
+            from q_j with numpy's generator (an input, not the verifier);
+            per-row seeds
 """
 
 import numpy as np
 
 BASE_SEED = 20261202
-CFG_IDS = {"small": 1, "renorm": 2, "latency": 3, "hetero": 4, "stress": 5}
+CFG_IDS = {"small": 1, "renorm": 2, "latency": 3, "hetero": 4, "stress": 5,
+           "speculative": 6}
 
 
 def rng_for(cfg, rep=0):
@@ -110,3 +116,25 @@ def logits_rows(rng, rows, vocab, sigma=2.0):
     """float32 logits z ~ N(0, sigma^2) for the logit-masking op."""
     return np.ascontiguousarray((rng.standard_normal((rows, vocab)) * sigma)
                                 .astype(np.float32))
+
+
+def speculative(rep=0, rows=64, n=4, vocab=151936, sigma=2.0, noise=0.5):
+    """Draft / target distributions and draft tokens for chain verification."""
+    rng = rng_for("speculative", rep)
+    zq = rng.standard_normal((rows, n, vocab)) * sigma
+    zp = np.empty((rows, n + 1, vocab))
+    zp[:, :n] = zq + rng.standard_normal((rows, n, vocab)) * noise
+    zp[:, n] = rng.standard_normal((rows, vocab)) * sigma
+
+    def sm(z):
+        z = z - z.max(axis=-1, keepdims=True)
+        e = np.exp(z)
+        return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+    q, p = sm(zq), sm(zp)
+    del zq, zp
+    cq = np.cumsum(q.astype(np.float64), axis=-1)
+    u = rng.random((rows, n, 1)) * cq[:, :, -1:]
+    ids = np.minimum((cq <= u).sum(axis=-1), vocab - 1).astype(np.int32)
+    return dict(q=np.ascontiguousarray(q), p=np.ascontiguousarray(p),
+                ids=np.ascontiguousarray(ids), seeds=seeds_for(rng, rows), offset=0)
+

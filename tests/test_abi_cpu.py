@@ -34,7 +34,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -59,7 +59,8 @@ def test_header_constants_match_binding():
             "top_k_mask_logits": "DSS_OP_TOP_K_MASK_LOGITS",
             "top_k_top_p_sampling_from_logits": "DSS_OP_TOP_K_TOP_P_FROM_LOGITS",
             "softmax": "DSS_OP_SOFTMAX",
-            "top_k": "DSS_OP_TOP_K_SELECT"}[op]) == i
+            "top_k": "DSS_OP_TOP_K_SELECT",
+            "chain_speculative_sampling": "DSS_OP_CHAIN_SPECULATIVE"}[op]) == i
 
 
 def _plain(lib, probs=FAKE, rows=1, vocab=8, indices=NULL, n=1, samples=FAKE, flags=0,
@@ -191,3 +192,33 @@ def test_binding_refuses_cpu_tensors():
         dss.sampling_from_probs(torch.ones(2, 8))
     with pytest.raises(ValueError):
         dss.top_p_renorm_probs(torch.ones(2, 8), 0.5)
+
+
+def test_chain_speculative_validation():
+    lib = _lib.load()
+
+    def call(q=FAKE, ids=FAKE, p=FAKE, rows=1, n=2, vocab=8, tokens=FAKE, acc=FAKE, flags=0,
+             ws=NULL, ws_bytes=0):
+        return lib.dss_chain_speculative_sampling(q, ids, p, rows, n, vocab, NULL, 1, NULL, 0,
+                                                  tokens, acc, NULL, flags, ws, ws_bytes, NULL)
+    assert call(p=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(tokens=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(acc=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(q=NULL) == _lib.DSS_ERR_INVALID_ARG          # drafts need their rows
+    assert call(ids=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(n=-1) == _lib.DSS_ERR_INVALID_ARG
+    assert call(vocab=0) == _lib.DSS_ERR_INVALID_ARG
+    assert call(flags=0x100) == _lib.DSS_ERR_INVALID_ARG
+    assert call(n=65) == _lib.DSS_ERR_UNSUPPORTED             # more drafts than one wave
+    assert call(vocab=6) == _lib.DSS_ERR_UNSUPPORTED          # rows not in 16-byte vectors
+    assert call(p=ctypes.c_void_p(20)) == _lib.DSS_ERR_UNSUPPORTED
+    assert call(rows=0, p=NULL, tokens=NULL, acc=NULL) == _lib.DSS_OK
+    # B=64, V=151936: W > 1, so the hand-off needs its workspace
+    need = lib.dss_workspace_size(11, 64, 151936, 4, 0)
+    assert need > 0
+    assert call(rows=64, n=4, vocab=151936) == _lib.DSS_ERR_WORKSPACE
+    assert call(rows=64, n=4, vocab=151936, ws=FAKE, ws_bytes=need - 1) == _lib.DSS_ERR_WORKSPACE
+    assert call(rows=64, n=4, vocab=151936, ws=FAKE, ws_bytes=need) != _lib.DSS_ERR_WORKSPACE
+    # n = 0 needs no draft arrays
+    assert call(q=NULL, ids=NULL, n=0, rows=64, vocab=151936, ws=FAKE,
+                ws_bytes=need) != _lib.DSS_ERR_INVALID_ARG
