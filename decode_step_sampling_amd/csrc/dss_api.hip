@@ -55,7 +55,10 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   if (num_outputs == 0) return DSS_OK;
   if (!probs || !samples) return DSS_ERR_INVALID_ARG;
   const int vec_ok = (vocab % 4 == 0) && aligned16(probs);
-  const dss::SplitPlan plan = dss::plan_split(eop, rows, vocab, num_outputs, flags, vec_ok);
+  dss::SplitPlan plan = dss::plan_split(eop, rows, vocab, num_outputs, flags, vec_ok);
+  if (plan.W > 0 && !top_k_arr && (eop == dss::kOpTopK || eop == dss::kOpTopKTopP) &&
+      (top_k > dss::kSplitKCapHost || (int64_t)top_k * plan.W > dss::kSplitScalarKW))
+    plan = dss::SplitPlan{0, 0, 0, 0, 0, 0};
   const dss::SplitPlan rplan = plan.W > 0 ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
                                           : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok);
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
@@ -382,9 +385,10 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
            align256((size_t)rows * (size_t)vocab * 4);
   }
   if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || num_outputs <= 0) return 0;
+  // top-k ops may run on either engine (the choice can depend on k)
   const dss::SplitPlan plan = dss::plan_split(op, rows, vocab, num_outputs, flags, vec);
-  if (plan.W > 0) return plan.workspace;
-  return dss::plan_resident(op, vocab, num_outputs, flags, vec).workspace;
+  const size_t res = dss::plan_resident(op, vocab, num_outputs, flags, vec).workspace;
+  return plan.W > 0 && plan.workspace > res ? plan.workspace : res;
 }
 
 DSS_EXPORT int32_t dss_set_timing_events(void* start, void* stop) {

@@ -117,7 +117,12 @@ hipError_t launch_split_renorm(int kind, const RenormParams& p, const SplitPlan&
 // per-row results (written before they are read).
 constexpr size_t kCtlRegionBytes = 16384;
 constexpr int kResidentSlots = 256;  // outputs (and work-groups) of one resident launch at most
-constexpr size_t kResidentSlotBytes = 35072;
+constexpr size_t kResidentSlotBytes = 67840;
+// A scalar top-k whose sets would crowd the split engine's lists goes to the
+// resident engine: k above the split cap (2048), or k * W above half of the
+// 8192 candidates a row's merge holds (flat rows would overflow them).
+constexpr int kSplitKCapHost = 2048;
+constexpr int kSplitScalarKW = 4096;
 constexpr int kResidentSegKeys = 8192;  // boundary-bin keys one work-group may publish
 constexpr size_t kFixedRegionBytes = kCtlRegionBytes + (size_t)kResidentSlots * kResidentSlotBytes +
                                      (size_t)kResidentSlots * kResidentSegKeys * 4;

@@ -54,11 +54,15 @@ constexpr uint64_t kSpinTicks = 5000000ull;  // 50 ms of the 100 MHz constant cl
 // Per-output control block in the workspace, zero between calls.
 struct RowSlot {
   uint32_t ctl[64];  // 0 barrier arrivals, 1 XCC ids (bit mask), 2 maximum pattern, 3 bad value
-  uint64_t h1[kRB1];
+  uint64_t h1[kRB1];  // mass histograms (integer significand sums) of the three levels
   uint64_t h2[kRB2];
   uint64_t h3[kRB3];
+  uint64_t k1[kRB1];  // count histograms of the three levels (top-k)
+  uint64_t k2[kRB2];
+  uint64_t k3[kRB3];
   double chunk[kRMaxW * kWaves];  // kept mass of every (slice, wave) range
 };
+constexpr int kRLevelWords = kRB1 + kRB2 + kRB3;  // one set of three histograms
 
 struct ResidentParams {
   int W;      // slices per output (a power of two)
@@ -132,9 +136,10 @@ __device__ __forceinline__ bool row_barrier(gptr<uint32_t> ctr, uint32_t target,
 
 // Leave the row after the last read of its slot.  The work-group that
 // leaves last (all W have passed `passed` barriers and then left) clears what
-// the row used and finally the arrival counter, so the slot is zero for the
-// next launch.  Every thread must call.
-__device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, int W, bool used_hist, ResSmem& sm) {
+// the row used (hist_words words of the histograms from h1 on) and finally
+// the arrival counter, so the slot is zero for the next launch.  Every
+// thread must call.
+__device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, int W, int hist_words, ResSmem& sm) {
   __syncthreads();
   const gptr<uint32_t> ctr = (gptr<uint32_t>)slot->ctl;
   if (threadIdx.x == 0) {
@@ -144,10 +149,8 @@ __device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, i
   __syncthreads();
   if (!sm.flag) return;
   const int t = threadIdx.x;
-  if (used_hist) {
-    const gptr<uint64_t> h = (gptr<uint64_t>)slot->h1;  // h1, h2, h3 are contiguous
-    for (int q = t; q < kRB1 + kRB2 + kRB3; q += kBlock) h[q] = 0ull;
-  }
+  const gptr<uint64_t> h = (gptr<uint64_t>)slot->h1;  // h1 .. k3 are contiguous
+  for (int q = t; q < hist_words; q += kBlock) h[q] = 0ull;
   if (t < kRMaxW * kWaves) ((gptr<double>)slot->chunk)[t] = 0.0;
   if (t >= 1 && t < 64) ctr[t] = 0u;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -421,11 +424,255 @@ __device__ __forceinline__ void res_invalid(const SampleParams& P, const RenormP
   }
 }
 
+// Load a row histogram g (NB bins) into sm.md: counts as they are, or
+// significand sums as masses (`exponent` < 0: level 1, bin b holds exponent
+// b >> 2).
+template <bool COUNT, int NB>
+__device__ __forceinline__ void load_level(gptr<uint64_t> g, int exponent, ResSmem& sm) {
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    const uint64_t x = __hip_atomic_load(g + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.md[b] = COUNT ? (double)x : bin_mass(x, exponent < 0 ? (uint32_t)b >> 2 : (uint32_t)exponent);
+  }
+}
+
+// Fold the LDS histogram copies of NB bins into sm.md (counts, or masses of
+// exponent e).
+template <bool COUNT, int NB>
+__device__ __forceinline__ void fold_level(ResSmem& sm, uint32_t exponent) {
+  constexpr int C = kRHistWords / NB;
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    uint64_t x = 0ull;
+#pragma unroll
+    for (int c = 0; c < C; ++c) x += sm.hh[b * C + c];
+    sm.md[b] = COUNT ? (double)x : bin_mass(x, exponent);
+  }
+}
+
+// One histogram entry of a value pattern: 1 (counts) or its significand.
+template <bool COUNT>
+__device__ __forceinline__ unsigned long long level_add(uint32_t key) {
+  return COUNT ? 1ull : (unsigned long long)sig_of(key);
+}
+
+// Exact threshold on the resident slices, for top-k (COUNT: the F4 note's
+// search on counts, section ⑤ with 1023 pivots per pass) and for top-p
+// inside a top-k set (masses): tau = the largest pattern t with F(t) >= need,
+// F(t) the count or the mass of the values x >= max(t, cut); pfrac >= 0 sets
+// need = pfrac * F(cut).  kept = F(tau).  Levels: bits [30:21] as a row
+// histogram, then inside the crossing bin bits [20:10] and [9:0], either as
+// two more row histograms or, when that bin holds at most kResidentSegKeys
+// values, from a key list that every work-group resolves alone.  Every
+// thread calls; false if a row barrier timed out.
+template <bool COUNT, int NV>
+__device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec, uint32_t cut,
+                                           double need_in, double pfrac, gptr<uint64_t> g1,
+                                           gptr<uint64_t> g2, gptr<uint64_t> g3,
+                                           gptr<uint32_t> ctl, gptr<uint32_t> seg_base, int li,
+                                           int s, int W, uint32_t& passed, ResSmem& sm,
+                                           uint32_t& tau, double& kept) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = r_uwave();
+  clear_lds_hist(sm);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const bool in = vbase + j * kWave < nvec;
+    const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (in && k4[e] >= cut)
+        atomicAdd(&sm.hh[min(k4[e] >> 21, (uint32_t)(kRB1 - 1)) * 8u + (uint32_t)(lane & 7)],
+                  level_add<COUNT>(k4[e]));
+  }
+  __syncthreads();
+  publish_hist<kRB1>(sm, g1);
+  __syncthreads();
+  clear_lds_hist(sm);
+  if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+  ++passed;
+  load_level<COUNT, kRB1>(g1, -1, sm);
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t b1;
+    double above, total;
+    mass_find<kRB1>(sm.md, need_in, pfrac, b1, above, total);
+    if (lane == 0) {
+      sm.res[0] = b1;
+      sm.resd[0] = above;
+      sm.resd[1] = total;
+      sm.resd[2] = pfrac >= 0.0 ? pfrac * total : need_in;
+    }
+  }
+  __syncthreads();
+  const uint32_t b1 = sm.res[0];
+  const double above1 = sm.resd[0], ftot = sm.resd[1], need = sm.resd[2];
+  const uint32_t e1 = b1 >> 2;
+  if (!COUNT && pfrac >= 1.0) {  // every value >= cut
+    tau = cut;
+    kept = ftot;
+    return true;
+  }
+  // values of the row in bin b1: the count itself, or at most the
+  // significand sum / 2^23 (normal numbers)
+  const bool use_list = COUNT ? sm.md[b1] <= (double)kResidentSegKeys
+                              : e1 >= 1u && ldexp(sm.md[b1], 127 - (int)e1) <= (double)kResidentSegKeys;
+  uint32_t pre2, b3;
+  double above2, above3, m3;
+  if (use_list) {
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const bool in = vbase + j * kWave < nvec;
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += (in && (k4[e] >> 21) == b1 && k4[e] >= cut) ? 1u : 0u;
+    }
+    uint32_t mine;
+    uint32_t pos = res_block_scan(cnt, mine, sm);
+    const gptr<uint32_t> seg = seg_base + (size_t)(li * W + s) * kResidentSegKeys;
+    if (cnt != 0u) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const bool in = vbase + j * kWave < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (in && (k4[e] >> 21) == b1 && k4[e] >= cut) seg[pos++] = k4[e];
+      }
+    }
+    if (tid == 0) __hip_atomic_store(ctl + 8 + s, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+    ++passed;
+    if (wave == 0) {
+      const uint32_t c = lane < W ? __hip_atomic_load(ctl + 8 + lane, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0u;
+      const uint32_t incl = wave_incl_scan(c);
+      if (lane <= kRMaxW) sm.off[lane] = incl - c;
+    }
+    __syncthreads();
+    const uint32_t n = sm.off[W];
+    constexpr int kPer = kResidentSegKeys / kBlock;
+    constexpr uint32_t kNone = 0xFFFFFFFFu;  // above every non-negative pattern
+    uint32_t kk[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const uint32_t g = (uint32_t)tid + (uint32_t)(q * kBlock);
+      int sl = 0;
+      for (int t = 1; t < W; ++t) sl = g >= sm.off[t] ? t : sl;
+      const uint32_t at = min(g - sm.off[sl], (uint32_t)(kResidentSegKeys - 1));
+      const uint32_t k = __hip_atomic_load(seg_base + (size_t)(li * W + sl) * kResidentSegKeys + at,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      kk[q] = g < n ? k : kNone;
+    }
+    // level 2 in LDS: bits [20:10], copy lane % 4
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (kk[q] != kNone)
+        atomicAdd(&sm.hh[((kk[q] >> 10) & (uint32_t)(kRB2 - 1)) * 4u + (uint32_t)(lane & 3)],
+                  level_add<COUNT>(kk[q]));
+    __syncthreads();
+    fold_level<COUNT, kRB2>(sm, e1);
+    __syncthreads();
+    clear_lds_hist(sm);
+    if (wave == 0) {
+      uint32_t b2;
+      double above, total;
+      mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+      if (lane == 0) {
+        sm.res[1] = b2;
+        sm.resd[0] = above;
+      }
+    }
+    __syncthreads();
+    pre2 = (b1 << 11) | sm.res[1];
+    above2 = sm.resd[0];
+    // level 3 in LDS: bits [9:0] of the keys with bits [30:10] == pre2
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (kk[q] != kNone && (kk[q] >> 10) == pre2)
+        atomicAdd(&sm.hh[(kk[q] & (uint32_t)(kRB3 - 1)) * 8u + (uint32_t)(lane & 7)],
+                  level_add<COUNT>(kk[q]));
+    __syncthreads();
+    fold_level<COUNT, kRB3>(sm, e1);
+    __syncthreads();
+  } else {
+    // level 2: values in bin b1, by bits [20:10], copy lane % 4
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const bool in = vbase + j * kWave < nvec;
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (in && (k4[e] >> 21) == b1 && k4[e] >= cut)
+          atomicAdd(&sm.hh[((k4[e] >> 10) & (uint32_t)(kRB2 - 1)) * 4u + (uint32_t)(lane & 3)],
+                    level_add<COUNT>(k4[e]));
+    }
+    __syncthreads();
+    publish_hist<kRB2>(sm, g2);
+    __syncthreads();
+    clear_lds_hist(sm);
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+    ++passed;
+    load_level<COUNT, kRB2>(g2, (int)e1, sm);
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t b2;
+      double above, total;
+      mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+      if (lane == 0) {
+        sm.res[1] = b2;
+        sm.resd[0] = above;
+      }
+    }
+    __syncthreads();
+    pre2 = (b1 << 11) | sm.res[1];
+    above2 = sm.resd[0];
+    // level 3: values with bits [30:10] == pre2, by bits [9:0], copy lane % 8
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const bool in = vbase + j * kWave < nvec;
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (in && (k4[e] >> 10) == pre2 && k4[e] >= cut)
+          atomicAdd(&sm.hh[(k4[e] & (uint32_t)(kRB3 - 1)) * 8u + (uint32_t)(lane & 7)],
+                    level_add<COUNT>(k4[e]));
+    }
+    __syncthreads();
+    publish_hist<kRB3>(sm, g3);
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+    ++passed;
+    load_level<COUNT, kRB3>(g3, (int)e1, sm);
+    __syncthreads();
+  }
+  if (wave == 0) {
+    uint32_t b;
+    double above, total;
+    mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b, above, total);
+    if (lane == 0) {
+      sm.res[2] = b;
+      sm.resd[0] = above;
+      sm.resd[1] = sm.md[b];
+    }
+  }
+  __syncthreads();
+  b3 = sm.res[2];
+  above3 = sm.resd[0];
+  m3 = sm.resd[1];
+  __syncthreads();
+  tau = (pre2 << 10) | b3;
+  kept = above1 + above2 + (above3 + m3);
+  return true;
+}
+
 template <int KIND, int OP, int NV>
 __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, RenormParams RP,
                                                           ResidentParams R) {
   __shared__ ResSmem sm;
-  constexpr bool kTopP = OP == kOpTopP;
+  constexpr bool kTopP = OP == kOpTopP;  // top-p alone: level-1 masses while the slice lands
+  constexpr bool kTopK = OP == kOpTopK || OP == kOpTopKTopP;
+  // histogram words the row's last work-group clears (masses, then counts)
+  constexpr int kHistWords = kTopK ? 2 * kRLevelWords : kTopP ? kRLevelWords : 0;
   const int W = R.W;
   const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
   const int li = (local / W) * 8 + xcd;  // the W slices of an output share b % 8
@@ -458,8 +705,9 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   // parameters (read before any store, so they are scalar loads)
   float prm = 0.0f;
   if (KIND == kResRenorm) prm = RP.top_p_arr ? as_global(RP.top_p_arr)[i] : RP.top_p;
-  else if (OP == kOpTopP) prm = P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
+  else if (OP == kOpTopP || OP == kOpTopKTopP) prm = P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
   else if (OP == kOpMinP) prm = P.min_p_arr ? as_global(P.min_p_arr)[i] : P.min_p;
+  const int kk = kTopK ? (P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k) : 1;
   const uint64_t seed = KIND != kResSample ? 0ull : P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
   const uint64_t offset =
       KIND != kResSample ? 0ull : P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
@@ -473,7 +721,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
                               ? (gptr<r_v4f>)as_global(RP.out + (int64_t)row * V + s0)
                               : (gptr<r_v4f>)nullptr;
 
-  if (!row_ok || isnan(prm)) {  // the same decision in every slice of the output
+  if (!row_ok || isnan(prm) || kk <= 0) {  // the same decision in every slice of the output
     res_invalid<KIND, NV>(P, RP, i, row, s, vbase, nvec, dst);
     return;
   }
@@ -548,7 +796,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   double zkept = 0.0;
   if (bad) {
     res_invalid<KIND, NV>(P, RP, i, row, s, vbase, nvec, dst);
-    row_leave(slot, passed, W, kTopP, sm);
+    row_leave(slot, passed, W, kHistWords, sm);
     return;
   }
 
@@ -737,6 +985,25 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     float f = (float)thr;
     if ((double)f < thr) f = __uint_as_float(bits_of(f) + 1u);
     tau = max(bits_of(f), 1u);
+  } else if (kTopK) {
+    // tau_k = the k-th largest pattern (ties kept), by counts; then, for
+    // top-k-then-top-p, the top-p threshold inside {x >= tau_k} by masses
+    uint32_t tk;
+    double cnt;
+    if (!res_search<true, NV>(v, vbase, nvec, 0u, (double)kk, -1.0, (gptr<uint64_t>)slot->k1,
+                              (gptr<uint64_t>)slot->k2, (gptr<uint64_t>)slot->k3, ctl,
+                              as_global(R.lists), li, s, W, passed, sm, tk, cnt))
+      return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+    tau = max(tk, 1u);  // zeros carry no mass
+    if (OP == kOpTopKTopP) {
+      uint32_t tp;
+      double zk;
+      if (!res_search<false, NV>(v, vbase, nvec, tau, 0.0, (double)pc, (gptr<uint64_t>)slot->h1,
+                                 (gptr<uint64_t>)slot->h2, (gptr<uint64_t>)slot->h3, ctl,
+                                 as_global(R.lists), li, s, W, passed, sm, tp, zk))
+        return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+      tau = max(tp, tau);
+    }
   }
 
   if (KIND == kResRenorm) {
@@ -750,7 +1017,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       if (vbase + j * kWave < nvec) dst[vbase + j * kWave] = o;
     }
     if (s == 0 && tid == 0 && RP.row_status) as_global(RP.row_status)[row] = 0;
-    row_leave(slot, passed, W, true, sm);
+    row_leave(slot, passed, W, kRLevelWords, sm);
     return;
   }
 
@@ -822,7 +1089,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       stream::write_sample(P, i, pos >= 0 ? s0 + pos : -1, pos >= 0 ? 1 : 0);
     }
   }
-  row_leave(slot, passed, W, kTopP, sm);
+  row_leave(slot, passed, W, kHistWords, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -921,7 +1188,7 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(SoftmaxParams Q, Reside
   if (gb != 0u || __popc(xm) != 1 || !(T > 0.0f) || T == __builtin_inff() ||
       zmax == -__builtin_inff()) {
     invalid();
-    row_leave(slot, 1u, W, false, sm);
+    row_leave(slot, 1u, W, 0, sm);
     return;
   }
   const double m = (double)zmax, it = 1.0 / (double)T;
@@ -966,7 +1233,7 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(SoftmaxParams Q, Reside
     chain = (double)o[0];
   }
   if (s == 0 && tid == 0 && Q.row_status) as_global(Q.row_status)[row] = 0;
-  row_leave(slot, 2u, W, false, sm);
+  row_leave(slot, 2u, W, 0, sm);
 }
 
 }  // namespace
@@ -1018,13 +1285,19 @@ hipError_t launch_res_one(const SampleParams& p, const RenormParams& rp, const S
 template <int KIND, int OP>
 hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const SplitPlan& plan,
                          void* ws, hipStream_t s, const LaunchEvents& ev) {
+  // the top-k searches keep more live state: their plans stop at eight loads
+  constexpr bool kTopKOp = OP == kOpTopK || OP == kOpTopKTopP;
   switch (plan.nv) {
     case 1: return launch_res_one<KIND, OP, 1>(p, rp, plan, ws, s, ev);
     case 2: return launch_res_one<KIND, OP, 2>(p, rp, plan, ws, s, ev);
     case 4: return launch_res_one<KIND, OP, 4>(p, rp, plan, ws, s, ev);
     case 8: return launch_res_one<KIND, OP, 8>(p, rp, plan, ws, s, ev);
-    case 10: return launch_res_one<KIND, OP, 10>(p, rp, plan, ws, s, ev);
-    default: return launch_res_one<KIND, OP, 12>(p, rp, plan, ws, s, ev);
+    case 10:
+      if constexpr (kTopKOp) return hipErrorInvalidValue;
+      else return launch_res_one<KIND, OP, 10>(p, rp, plan, ws, s, ev);
+    default:
+      if constexpr (kTopKOp) return hipErrorInvalidValue;
+      else return launch_res_one<KIND, OP, 12>(p, rp, plan, ws, s, ev);
   }
 }
 
@@ -1032,10 +1305,13 @@ hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const Sp
 
 SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok) {
   SplitPlan plan{0, 0, 0, 0, 0, 0};
-  if (op != kOpNone && op != kOpTopP && op != kOpMinP) return plan;
+  if (op != kOpNone && op != kOpTopP && op != kOpMinP && op != kOpTopK && op != kOpTopKTopP)
+    return plan;
   if (flags & (DSS_FLAG_STREAMING | DSS_FLAG_FROM_ZERO | DSS_FLAG_SINGLE_PIVOT)) return plan;
   if (!vec_ok || vocab < 1024 || num_outputs <= 0) return plan;
-  constexpr int kMaxSlice = kRMaxNv * 4 * kBlock;
+  // values a slice holds: 48 per thread, 32 for the top-k searches
+  const bool topk = op == kOpTopK || op == kOpTopKTopP;
+  const int kMaxSlice = (topk ? 8 : kRMaxNv) * 4 * kBlock;
   const int wmin = (vocab + kMaxSlice - 1) / kMaxSlice;
   if (wmin > kRMaxW) return plan;
   const int wt = (kResidentSlots + num_outputs - 1) / num_outputs;
@@ -1050,6 +1326,7 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
   if (W < wmin) return plan;
   int nv = (L / 4 + kBlock - 1) / kBlock;
   nv = nv <= 2 ? nv : nv <= 4 ? 4 : nv <= 8 ? 8 : nv <= 10 ? 10 : 12;
+  if (topk && nv > 8) return plan;
   plan.W = W;
   plan.L = L;
   plan.nv = nv;
@@ -1065,6 +1342,8 @@ hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan
   hipError_t e;
   if (op == kOpNone) e = launch_res_nv<kResSample, kOpNone>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopP) e = launch_res_nv<kResSample, kOpTopP>(p, rp, plan, workspace, s, ev);
+  else if (op == kOpTopK) e = launch_res_nv<kResSample, kOpTopK>(p, rp, plan, workspace, s, ev);
+  else if (op == kOpTopKTopP) e = launch_res_nv<kResSample, kOpTopKTopP>(p, rp, plan, workspace, s, ev);
   else e = launch_res_nv<kResSample, kOpMinP>(p, rp, plan, workspace, s, ev);
   // a device that cannot hold one group of work-groups at once: streaming engine
   if (e == hipErrorInvalidConfiguration) e = launch_stream_sample(op, p, s, ev);

@@ -1,0 +1,104 @@
+"""GPU parity of top-k and top-k-then-top-p sampling on the resident engine
+(a scalar k above the split engine's cap, or k * W above half of its
+candidate capacity): tau_k exactly by counts, the top-p cut inside the top-k
+set exactly by masses, then one draw in index order.  That is the oracle's
+CDF draw on the kept set, so tokens are compared exactly (up to float64
+prefix rounding at a boundary, ~1e-13 relative)."""
+
+import numpy as np
+import pytest
+
+import decode_step_sampling_amd as dss
+import synthetic_inputs as si
+from oracle import philox as ph
+from oracle import reference as ref
+from gpu_util import gpu, host, u64
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(kind, rows, V, rng):
+    if kind == "softmax":
+        return si.softmax_rows(rng, rows, V, 2.0)
+    if kind == "ties":                       # few distinct values, huge tie groups
+        x = rng.integers(1, 6, size=(rows, V)).astype(np.float64)
+    elif kind == "flat":                     # near-uniform (one level-1 bin)
+        x = 1.0 + rng.uniform(-1e-3, 1e-3, size=(rows, V))
+    else:                                    # geometric chain in index order
+        x = np.tile((1.0 - 1e-5) ** np.arange(V, dtype=np.float64), (rows, 1))
+    x /= x.sum(axis=1, keepdims=True)
+    return np.ascontiguousarray(x.astype(np.float32))
+
+
+def _table(row, op, k, p):
+    """The oracle's CDF draw on the kept set (``sample_by_cdf``), built once."""
+    valid, tau = ref.threshold(row, op, k=k, p=p)
+    assert valid
+    return ref.CdfTable(row, ref.support_mask(row, tau))
+
+
+def _call(op, P, k, p, n_per_row, rows, seed, offset):
+    idx = np.repeat(np.arange(rows, dtype=np.int32), n_per_row)
+    if op == "top_k":
+        out = dss.top_k_sampling_from_probs(P, k, indices=gpu(idx), seed=seed, offset=offset,
+                                            return_valid=True, return_rounds=True)
+    else:
+        out = dss.top_k_top_p_sampling_from_probs(P, k, p, indices=gpu(idx), seed=seed,
+                                                  offset=offset, return_valid=True,
+                                                  return_rounds=True)
+    return idx, [host(t) for t in out]
+
+
+@pytest.mark.parametrize("kind", ["softmax", "ties", "flat", "geometric"])
+@pytest.mark.parametrize("op", ["top_k", "top_k_top_p"])
+@pytest.mark.parametrize("k", [500, 3000, 70000])
+def test_token_exact(kind, op, k):
+    """Four rows of V=32768, one output each (W=16 slices, so k * W > 4096
+    even for k=500), 16 calls with offsets 0..15."""
+    rng = np.random.default_rng(sum(map(ord, kind + op)) + k)
+    rows, V = 4, 32768
+    probs = _rows(kind, rows, V, rng)
+    P = gpu(probs)
+    p = np.float32(0.8)
+    seed = 4242
+    tables = [_table(probs[i], op, k, p) for i in range(rows)]
+    for offset in range(16):
+        idx, (s, v, r) = _call(op, P, k, p, 1, rows, seed, offset)
+        assert (v == 1).all() and (r == 1).all()
+        for i in range(rows):
+            want = tables[i].draw(ph.draw_bits53(seed, offset, i, 0))
+            assert s[i] == want, (kind, op, k, offset, i, int(s[i]), want)
+
+
+def test_extremes_and_invalid():
+    rng = np.random.default_rng(9)
+    probs = si.softmax_rows(rng, 3, 8192, 2.0)
+    P = gpu(probs)
+    # k = 1 (the maximum), k = V and above (everything), p = 0 and p = 1
+    for k, p in ((1, 0.9), (8192, 0.5), (10**6, 1.0), (2500, 0.0)):
+        idx, (s, v, r) = _call("top_k_top_p", P, k, np.float32(p), 8, 3, 77, 0)
+        tables = [_table(probs[j], "top_k_top_p", k, np.float32(p)) for j in range(3)]
+        for i in range(idx.size):
+            assert s[i] == tables[idx[i]].draw(ph.draw_bits53(77, 0, i, 0)), (k, p, i)
+    # k <= 0 and a NaN p make the output invalid
+    for k, p in ((0, 0.5), (-3, 0.5), (3000, float("nan"))):
+        s, v = dss.top_k_top_p_sampling_from_probs(P, k, p, seed=1, return_valid=True)
+        assert (host(v) == 0).all() and (host(s) == -1).all()
+
+
+def test_stress_rows_full_size():
+    """The stress workload's near-uniform, peaked and geometric rows at
+    B=512, V=256000, k=1000, p=0.95 (k * W = 8000: resident engine), one
+    draw per row against the oracle's CDF draw."""
+    w = si.stress()
+    probs = w["probs"]
+    seeds = w["seeds"]
+    s, v, r = dss.top_k_top_p_sampling_from_probs(gpu(probs), 1000, 0.95, seed=u64(seeds),
+                                                  offset=5, return_valid=True, return_rounds=True)
+    s, v, r = host(s), host(v), host(r)
+    assert (v == 1).all() and (r == 1).all()
+    for row in range(0, probs.shape[0], 16):
+        want = ref.sample_by_cdf(probs[row], "top_k_top_p",
+                                 ph.draw_bits53(int(seeds[row]), 5, 0, 0), k=1000,
+                                 p=np.float32(0.95))
+        assert s[row] == want, (row, int(w["groups"][row]))
