@@ -1,5 +1,5 @@
-// Resident-slice engine: plain, top-p and min-p sampling, top-p
-// renormalisation.
+// Resident-slice engine: plain, top-p, min-p, top-k and top-k-then-top-p
+// sampling, top-p renormalisation.
 //
 // Top-p needs the row's total mass before any value can be classified, so a
 // slice cannot bound its candidates alone the way the split engine does for
@@ -28,9 +28,11 @@
 //
 // Plain sampling uses tau = the smallest positive pattern and min-p the
 // smallest float >= min_p * max (blog, min-p section), both known without a
-// histogram.  The walk visits values in a fixed order (slice, wave, load,
-// lane, element), not index order; every fixed order gives value x_i the
-// probability x_i / Z_kept.
+// histogram.  Top-k runs the same three levels on counts (tau_k = the k-th
+// largest pattern, ties kept) and top-k-then-top-p then the mass levels on
+// the values >= tau_k only, so the top-p target is p * Z_k.  Every wave owns
+// a contiguous range of its slice, so the walk visits values in index order:
+// the draw is the inverse transform of the kept set.
 //
 // Work-group b runs on XCD b % 8, so the W work-groups of output li are the
 // blocks with equal b % 8 (as in the split engine), and the row's counters
