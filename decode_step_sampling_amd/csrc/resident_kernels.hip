@@ -189,44 +189,6 @@ __device__ __forceinline__ void load_masses(gptr<uint64_t> g, int exponent, ResS
   }
 }
 
-// One wave: the largest bin b of md[0, NB) whose mass from the top,
-// M(b) = sum_{b' >= b} md[b'], reaches `need` (need = pfrac * total when
-// pfrac >= 0) and is positive; `above` = M(b + 1).  If rounding leaves every
-// M(b) below need, the lowest bin with mass is taken (everything kept).
-// Lane l sums the chunk of NB / 64 bins that is l-th from the top; a scan
-// over lanes finds the chunk and a scan over that chunk's bins the bin.
-template <int NB>
-__device__ __forceinline__ void mass_find(const double* md, double need, double pfrac, uint32_t& bin,
-                          double& above, double& total) {
-  constexpr int C = NB / kWave;
-  const int lane = lane_id();
-  const int c = kWave - 1 - lane;
-  double s = 0.0;
-#pragma unroll
-  for (int q = C - 1; q >= 0; --q) {
-    if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // four reads in flight at a time
-    s += md[c * C + q];
-  }
-  const double incl = wave_incl_scan(s);
-  const double excl = wave_excl_from_incl(incl);
-  total = lane63(incl);
-  if (pfrac >= 0.0) need = pfrac * total;
-  uint64_t hit = __ballot(incl >= need && incl > 0.0);
-  int L = hit ? r_first_lane(hit) : r_last_lane(__ballot(s > 0.0) | 1ull);
-  const bool fallback = hit == 0ull;
-  const int cc = kWave - 1 - L;
-  const double ex = lane_value(excl, L);
-  const double m = lane < C ? md[cc * C + C - 1 - lane] : 0.0;
-  const double incl2 = wave_incl_scan(m) + ex;
-  const double sh = wave_excl_from_incl(incl2);
-  const double excl2 = lane == 0 ? ex : sh;
-  uint64_t hit2 = fallback ? 0ull : __ballot(lane < C && incl2 >= need && incl2 > 0.0);
-  if (hit2 == 0ull) hit2 = 1ull << r_last_lane(__ballot(lane < C && m > 0.0) | 1ull);
-  const int Q = r_first_lane(hit2);
-  bin = (uint32_t)(cc * C + C - 1 - Q);
-  above = lane_value(excl2, Q);
-}
-
 // The slice is loaded so that wave w owns the contiguous vector range
 // [w * 64 * NV, (w + 1) * 64 * NV): its load j covers vectors
 // w * 64 * NV + 64 j + lane (64 consecutive 16-byte vectors, one coalesced
@@ -496,7 +458,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
   if (wave == 0) {
     uint32_t b1;
     double above, total;
-    mass_find<kRB1>(sm.md, need_in, pfrac, b1, above, total);
+    stream::mass_find<kRB1>(sm.md, need_in, pfrac, b1, above, total);
     if (lane == 0) {
       sm.res[0] = b1;
       sm.resd[0] = above;
@@ -579,7 +541,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     if (wave == 0) {
       uint32_t b2;
       double above, total;
-      mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+      stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
       if (lane == 0) {
         sm.res[1] = b2;
         sm.resd[0] = above;
@@ -620,7 +582,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     if (wave == 0) {
       uint32_t b2;
       double above, total;
-      mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+      stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
       if (lane == 0) {
         sm.res[1] = b2;
         sm.resd[0] = above;
@@ -650,7 +612,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
   if (wave == 0) {
     uint32_t b;
     double above, total;
-    mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b, above, total);
+    stream::mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b, above, total);
     if (lane == 0) {
       sm.res[2] = b;
       sm.resd[0] = above;
@@ -809,7 +771,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     if (wave == 0) {
       uint32_t b1;
       double above, total;
-      mass_find<kRB1>(sm.md, 0.0, (double)pc, b1, above, total);
+      stream::mass_find<kRB1>(sm.md, 0.0, (double)pc, b1, above, total);
       if (lane == 0) {
         sm.res[0] = b1;
         sm.resd[0] = above;
@@ -889,7 +851,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       if (wave == 0) {
         uint32_t b2;
         double above, total;
-        mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+        stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
         if (lane == 0) {
           sm.res[1] = b2;
           sm.resd[0] = above;
@@ -910,7 +872,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       if (wave == 0) {
         uint32_t b3;
         double above, total;
-        mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
+        stream::mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
         if (lane == 0) {
           sm.res[2] = b3;
           sm.resd[0] = above1 + above2 + (above + sm.md[b3]);
@@ -942,7 +904,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       if (wave == 0) {
         uint32_t b2;
         double above, total;
-        mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
+        stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
         if (lane == 0) {
           sm.res[1] = b2;
           sm.resd[0] = above;
@@ -971,7 +933,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       if (wave == 0) {
         uint32_t b3;
         double above, total;
-        mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
+        stream::mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
         if (lane == 0) {
           sm.res[2] = b3;
           sm.resd[0] = above1 + above2 + (above + sm.md[b3]);

@@ -110,6 +110,7 @@ struct SplitSmem {
     } b;
     stream::SampleSmem stream;   // streaming fallback
     stream::SelectSmem sel;      // streaming fallback of a selection
+    stream::RadixSmem radix;     // exact fallback of top-k sampling
   } u;
   alignas(16) uint32_t hist[H1::kWords];
   // fixed-point masses of the top-k entries above the boundary bin, per
@@ -1127,7 +1128,9 @@ __global__ __launch_bounds__(kBlock) void split_kernel(SampleParams P, SplitPara
   int i = 0;
   const int mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
   if (mode == kFallback) {
-    if constexpr (KIND == kKindSample) {
+    if constexpr (KIND == kKindSample && (OP == kOpTopK || OP == kOpTopKTopP)) {
+      stream::sample_row_exact<OP>(P, i, sm.u.radix);
+    } else if constexpr (KIND == kKindSample) {
       stream::sample_row<OP>(P, i, sm.u.stream);
     } else if constexpr (KIND == kKindSelect) {
       stream::select_row(Q, i, sm.u.sel);

@@ -605,6 +605,214 @@ __device__ __forceinline__ void renorm_row(const RenormParams& P, int row, RedSm
   if (P.row_status && threadIdx.x == 0) P.row_status[row] = 0;
 }
 
+// One wave: the largest bin b of md[0, NB) whose mass from the top,
+// M(b) = sum_{b' >= b} md[b'], reaches `need` (need = pfrac * total when
+// pfrac >= 0) and is positive; `above` = M(b + 1).  If rounding leaves every
+// M(b) below need, the lowest bin with mass is taken (everything kept).
+// Lane l sums the chunk of NB / 64 bins that is l-th from the top; a scan
+// over lanes finds the chunk and a scan over that chunk's bins the bin.
+template <int NB>
+__device__ __forceinline__ void mass_find(const double* md, double need, double pfrac, uint32_t& bin,
+                          double& above, double& total) {
+  constexpr int C = NB / kWave;
+  const int lane = lane_id();
+  const int c = kWave - 1 - lane;
+  double s = 0.0;
+#pragma unroll
+  for (int q = C - 1; q >= 0; --q) {
+    if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // four reads in flight at a time
+    s += md[c * C + q];
+  }
+  const double incl = wave_incl_scan(s);
+  const double excl = wave_excl_from_incl(incl);
+  total = lane63(incl);
+  if (pfrac >= 0.0) need = pfrac * total;
+  uint64_t hit = __ballot(incl >= need && incl > 0.0);
+  int L = hit ? (__ffsll((long long)hit) - 1) : (63 - __clzll((long long)(__ballot(s > 0.0) | 1ull)));
+  const bool fallback = hit == 0ull;
+  const int cc = kWave - 1 - L;
+  const double ex = lane_value(excl, L);
+  const double m = lane < C ? md[cc * C + C - 1 - lane] : 0.0;
+  const double incl2 = wave_incl_scan(m) + ex;
+  const double sh = wave_excl_from_incl(incl2);
+  const double excl2 = lane == 0 ? ex : sh;
+  uint64_t hit2 = fallback ? 0ull : __ballot(lane < C && incl2 >= need && incl2 > 0.0);
+  if (hit2 == 0ull) hit2 = 1ull << (63 - __clzll((long long)(__ballot(lane < C && m > 0.0) | 1ull)));
+  const int Q = __ffsll((long long)hit2) - 1;
+  bin = (uint32_t)(cc * C + C - 1 - Q);
+  above = lane_value(excl2, Q);
+}
+
+// ---- exact top-k / top-k-then-top-p sampling, one work-group per output ---
+//
+// The split engine's in-kernel fallback for rows it cannot bound (k above its
+// cap, flat rows, huge tie groups).  Instead of the rejection loop from
+// low = 0 (one pass per round, many rounds on rows whose kept set reaches
+// deep into a long tail) it finds the kept set exactly, as the resident
+// engine does, with passes over the row: tau_k by count histograms of bits
+// [30:21], [20:10] and [9:0] (the F4 note's threshold search on the bit
+// pattern, 1023 pivots per pass), the top-p cut inside {x >= tau_k} by the
+// same three levels on exact significand sums, then one inverse-transform
+// draw over {x >= tau} (blog, 逆变换采样): tile masses, then one tile.
+// About eight passes whatever the row.
+
+struct RadixSmem {
+  uint64_t hh[2048];   // one level's histogram (counts, or significand sums)
+  double md[2048];     // the level as counts or masses
+  SampleSmem s;        // tile masses and the locate() scratch
+  uint32_t res[4];
+  double resd[4];
+};
+
+__device__ __forceinline__ uint32_t radix_sig(uint32_t key) {
+  return (key & 0x7FFFFFu) | (key >= 0x800000u ? 0x800000u : 0u);
+}
+
+// One pass: the values with pattern >= cut and pattern >> hs == prefix, by
+// bin (pattern >> ls) & (NB - 1): counts, or 24-bit significand sums (each
+// bin one quarter-binade or part of one, so exact integers); folded into md
+// as counts or masses (exponent e; e < 0: level 1, bin b holds exponent
+// b >> 2).  Every thread calls.
+template <bool COUNT, int NB>
+__device__ __forceinline__ void radix_pass(const RowRef& r, uint32_t cut, int hs, uint32_t prefix,
+                                           int ls, int e, RadixSmem& sm) {
+  for (int b = threadIdx.x; b < NB; b += kBlock) sm.hh[b] = 0ull;
+  __syncthreads();
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t key = bits_of(v[q]);
+      if (valid && idx + q < r.V && key >= cut && (key >> hs) == prefix)
+        atomicAdd(&sm.hh[(key >> ls) & (uint32_t)(NB - 1)],
+                  COUNT ? 1ull : (unsigned long long)radix_sig(key));
+    }
+  });
+  __syncthreads();
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    const uint64_t x = sm.hh[b];
+    const uint32_t ex = e < 0 ? (uint32_t)b >> 2 : (uint32_t)e;
+    sm.md[b] = COUNT ? (double)x : ldexp((double)x, (int)max(ex, 1u) - 150);
+  }
+  __syncthreads();
+}
+
+// tau = the largest pattern t with F(t) >= need, F(t) the count (COUNT) or
+// mass of the values >= max(t, cut); pfrac >= 0 sets need = pfrac * F(cut).
+// kept = F(tau).  Every thread calls.
+template <bool COUNT>
+__device__ __forceinline__ void radix_search(const RowRef& r, uint32_t cut, double need_in,
+                                             double pfrac, RadixSmem& sm, uint32_t& tau,
+                                             double& kept) {
+  const int lane = lane_id(), wave = wave_id();
+  radix_pass<COUNT, 1024>(r, cut, 31, 0u, 21, -1, sm);
+  if (wave == 0) {
+    uint32_t b;
+    double above, total;
+    mass_find<1024>(sm.md, need_in, pfrac, b, above, total);
+    if (lane == 0) {
+      sm.res[0] = b;
+      sm.resd[0] = above;
+      sm.resd[1] = total;
+      sm.resd[2] = pfrac >= 0.0 ? pfrac * total : need_in;
+    }
+  }
+  __syncthreads();
+  const uint32_t b1 = sm.res[0];
+  const double above1 = sm.resd[0], ftot = sm.resd[1], need = sm.resd[2];
+  __syncthreads();
+  if (!COUNT && pfrac >= 1.0) {  // every value >= cut
+    tau = cut;
+    kept = ftot;
+    return;
+  }
+  const int e1 = (int)(b1 >> 2);
+  radix_pass<COUNT, 2048>(r, cut, 21, b1, 10, e1, sm);
+  if (wave == 0) {
+    uint32_t b;
+    double above, total;
+    mass_find<2048>(sm.md, need - above1, -1.0, b, above, total);
+    if (lane == 0) {
+      sm.res[1] = b;
+      sm.resd[0] = above;
+    }
+  }
+  __syncthreads();
+  const uint32_t pre2 = (b1 << 11) | sm.res[1];
+  const double above2 = sm.resd[0];
+  __syncthreads();
+  radix_pass<COUNT, 1024>(r, cut, 10, pre2, 0, e1, sm);
+  if (wave == 0) {
+    uint32_t b;
+    double above, total;
+    mass_find<1024>(sm.md, need - above1 - above2, -1.0, b, above, total);
+    if (lane == 0) {
+      sm.res[2] = b;
+      sm.resd[0] = above;
+      sm.resd[1] = sm.md[b];
+    }
+  }
+  __syncthreads();
+  tau = (pre2 << 10) | sm.res[2];
+  kept = above1 + above2 + (sm.resd[0] + sm.resd[1]);
+  __syncthreads();
+}
+
+// Output i by the exact passes above (OP: top-k or top-k-then-top-p, the
+// top-p target p * Z_k); rounds = 1.  Every thread calls.
+template <int OP>
+__device__ __forceinline__ void sample_row_exact(const SampleParams& P, int i, RadixSmem& sm) {
+  static_assert(OP == kOpTopK || OP == kOpTopKTopP, "top-k and top-k-then-top-p only");
+  const int lane = lane_id(), wave = wave_id();
+  const int row = P.indices ? as_global(P.indices)[i] : i;
+  const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
+  const float pp = OP == kOpTopKTopP ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
+  if (!(row >= 0 && row < P.rows) || k <= 0 || isnan(pp)) {  // block-uniform
+    if (threadIdx.x == 0) write_sample(P, i, -1, 0);
+    return;
+  }
+  const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
+  const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
+  const RowRef r{as_global(P.probs + (int64_t)row * P.vocab), P.vocab, P.vec_ok != 0};
+  const int n_tiles = (P.vocab + kTile - 1) / kTile;
+
+  // validity: a sign bit, inf or NaN anywhere, or nothing positive
+  Red acc = red_zero();
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc.mx = max(acc.mx, (valid && idx + q < r.V) ? bits_of(v[q]) : 0u);
+  });
+  const uint32_t maxbits = block_reduce(acc, sm.s.red).mx;
+  if (maxbits >= 0x7F800000u || maxbits == 0u) {
+    if (threadIdx.x == 0) write_sample(P, i, -1, 0);
+    return;
+  }
+  uint32_t tk;
+  double cnt;
+  radix_search<true>(r, 0u, (double)k, -1.0, sm, tk, cnt);
+  uint32_t tau = max(tk, 1u);  // zeros carry no mass
+  if (OP == kOpTopKTopP) {
+    uint32_t tp;
+    double zk;
+    radix_search<false>(r, tau, 0.0, (double)clamp01(pp), sm, tp, zk);
+    tau = max(tp, tau);
+  }
+  // one draw over {x >= tau} = {x > low}
+  const float low = __uint_as_float(tau - 1u);
+  uint32_t ca = 0u, cb = 0u;
+  pivot_pass(r, n_tiles, low, low, sm.s.tm[0], sm.s.tm[1], ca, cb);
+  __syncthreads();
+  if (wave == 0) {
+    const double z = tile_scan_total(sm.s.tm[0], n_tiles);
+    if (lane == 0) sm.s.bc_d[0] = z * draw_uniform(seed, offset, sid, 0u);
+  }
+  __syncthreads();
+  const double T = sm.s.bc_d[0];
+  __syncthreads();
+  const int tok = locate(r, sm.s.tm[0], n_tiles, T, low, sm.s);
+  if (threadIdx.x == 0) write_sample(P, i, tok, tok >= 0 ? 1 : 0);
+}
+
 // ---- top-k selection (explainer, 选择 top-k 值本身) ----------------------
 
 // A row with no top-k set (a NaN in it): NaN values, index -1, status 1.
