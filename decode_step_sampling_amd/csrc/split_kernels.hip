@@ -1128,7 +1128,8 @@ __global__ __launch_bounds__(kBlock) void split_kernel(SampleParams P, SplitPara
   int i = 0;
   const int mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
   if (mode == kFallback) {
-    if constexpr (KIND == kKindSample && (OP == kOpTopK || OP == kOpTopKTopP)) {
+    if constexpr (KIND == kKindSample &&
+                  (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint)) {
       stream::sample_row_exact<OP>(P, i, sm.u.radix);
     } else if constexpr (KIND == kKindSample) {
       stream::sample_row<OP>(P, i, sm.u.stream);

@@ -757,15 +757,19 @@ __device__ __forceinline__ void radix_search(const RowRef& r, uint32_t cut, doub
   __syncthreads();
 }
 
-// Output i by the exact passes above (OP: top-k or top-k-then-top-p, the
-// top-p target p * Z_k); rounds = 1.  Every thread calls.
+// Output i by the exact passes above (OP: top-k; top-k-then-top-p, whose
+// top-p target is p * Z_k; or the joint order, whose top-p cut is taken on
+// the whole row and the kept set is {x >= max(tau_k, tau_p)}); rounds = 1.
+// Every thread calls.
 template <int OP>
 __device__ __forceinline__ void sample_row_exact(const SampleParams& P, int i, RadixSmem& sm) {
-  static_assert(OP == kOpTopK || OP == kOpTopKTopP, "top-k and top-k-then-top-p only");
+  static_assert(OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint,
+                "the top-k filters only");
+  constexpr bool kP = OP == kOpTopKTopP || OP == kOpTopKTopPJoint;
   const int lane = lane_id(), wave = wave_id();
   const int row = P.indices ? as_global(P.indices)[i] : i;
   const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
-  const float pp = OP == kOpTopKTopP ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
+  const float pp = kP ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
   if (!(row >= 0 && row < P.rows) || k <= 0 || isnan(pp)) {  // block-uniform
     if (threadIdx.x == 0) write_sample(P, i, -1, 0);
     return;
@@ -791,10 +795,11 @@ __device__ __forceinline__ void sample_row_exact(const SampleParams& P, int i, R
   double cnt;
   radix_search<true>(r, 0u, (double)k, -1.0, sm, tk, cnt);
   uint32_t tau = max(tk, 1u);  // zeros carry no mass
-  if (OP == kOpTopKTopP) {
+  if (kP) {
+    // top-k first: the cut inside {x >= tau_k}; joint: on the whole row
     uint32_t tp;
     double zk;
-    radix_search<false>(r, tau, 0.0, (double)clamp01(pp), sm, tp, zk);
+    radix_search<false>(r, OP == kOpTopKTopP ? tau : 1u, 0.0, (double)clamp01(pp), sm, tp, zk);
     tau = max(tp, tau);
   }
   // one draw over {x >= tau} = {x > low}

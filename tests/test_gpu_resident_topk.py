@@ -104,7 +104,7 @@ def test_stress_rows_full_size():
         assert s[row] == want, (row, int(w["groups"][row]))
 
 
-@pytest.mark.parametrize("op", ["top_k", "top_k_top_p"])
+@pytest.mark.parametrize("op", ["top_k", "top_k_top_p", "top_k_top_p_joint"])
 def test_split_fallback_rows_token_exact(op):
     """Per-output k arrays keep a call on the split engine; its outputs with
     k above the cap (2048) fall back inside the kernel to the exact passes
@@ -123,9 +123,11 @@ def test_split_fallback_rows_token_exact(op):
             s, v, r = dss.top_k_sampling_from_probs(P, gpu(ks), seed=u64(seeds), offset=offset,
                                                     return_valid=True, return_rounds=True)
         else:
+            order = "joint" if op.endswith("joint") else "top_k_first"
             s, v, r = dss.top_k_top_p_sampling_from_probs(P, gpu(ks), gpu(ps), seed=u64(seeds),
                                                           offset=offset, return_valid=True,
-                                                          return_rounds=True)
+                                                          return_rounds=True,
+                                                          filter_apply_order=order)
         s, v, r = host(s), host(v), host(r)
         assert (v == 1).all()
         for i in range(rows):
