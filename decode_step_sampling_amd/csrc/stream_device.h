@@ -698,11 +698,14 @@ __device__ __forceinline__ void radix_pass(const RowRef& r, uint32_t cut, int hs
 
 // tau = the largest pattern t with F(t) >= need, F(t) the count (COUNT) or
 // mass of the values >= max(t, cut); pfrac >= 0 sets need = pfrac * F(cut).
-// kept = F(tau).  Every thread calls.
+// kept = F(tau).  A count search from cut = 0 also checks the row: a value
+// with the sign bit set is left out of the level-1 total, an inf or NaN
+// falls in the top four bins; either sets `bad` and ends the search.  Every
+// thread calls.
 template <bool COUNT>
 __device__ __forceinline__ void radix_search(const RowRef& r, uint32_t cut, double need_in,
                                              double pfrac, RadixSmem& sm, uint32_t& tau,
-                                             double& kept) {
+                                             double& kept, bool& bad) {
   const int lane = lane_id(), wave = wave_id();
   radix_pass<COUNT, 1024>(r, cut, 31, 0u, 21, -1, sm);
   if (wave == 0) {
@@ -711,6 +714,9 @@ __device__ __forceinline__ void radix_search(const RowRef& r, uint32_t cut, doub
     mass_find<1024>(sm.md, need_in, pfrac, b, above, total);
     if (lane == 0) {
       sm.res[0] = b;
+      sm.res[3] = (COUNT && cut == 0u &&
+                   (total < (double)r.V || sm.md[1020] + sm.md[1021] + sm.md[1022] + sm.md[1023] > 0.0))
+                      ? 1u : 0u;
       sm.resd[0] = above;
       sm.resd[1] = total;
       sm.resd[2] = pfrac >= 0.0 ? pfrac * total : need_in;
@@ -719,7 +725,9 @@ __device__ __forceinline__ void radix_search(const RowRef& r, uint32_t cut, doub
   __syncthreads();
   const uint32_t b1 = sm.res[0];
   const double above1 = sm.resd[0], ftot = sm.resd[1], need = sm.resd[2];
+  bad = sm.res[3] != 0u;
   __syncthreads();
+  if (bad) return;
   if (!COUNT && pfrac >= 1.0) {  // every value >= cut
     tau = cut;
     kept = ftot;
@@ -780,26 +788,22 @@ __device__ __forceinline__ void sample_row_exact(const SampleParams& P, int i, R
   const RowRef r{as_global(P.probs + (int64_t)row * P.vocab), P.vocab, P.vec_ok != 0};
   const int n_tiles = (P.vocab + kTile - 1) / kTile;
 
-  // validity: a sign bit, inf or NaN anywhere, or nothing positive
-  Red acc = red_zero();
-  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc.mx = max(acc.mx, (valid && idx + q < r.V) ? bits_of(v[q]) : 0u);
-  });
-  const uint32_t maxbits = block_reduce(acc, sm.s.red).mx;
-  if (maxbits >= 0x7F800000u || maxbits == 0u) {
+  // tau_k (the count search also rejects a row with a sign bit, inf or
+  // NaN; a row with nothing positive ends with an empty draw below)
+  uint32_t tk;
+  double cnt;
+  bool bad;
+  radix_search<true>(r, 0u, (double)k, -1.0, sm, tk, cnt, bad);
+  if (bad) {
     if (threadIdx.x == 0) write_sample(P, i, -1, 0);
     return;
   }
-  uint32_t tk;
-  double cnt;
-  radix_search<true>(r, 0u, (double)k, -1.0, sm, tk, cnt);
   uint32_t tau = max(tk, 1u);  // zeros carry no mass
   if (kP) {
     // top-k first: the cut inside {x >= tau_k}; joint: on the whole row
     uint32_t tp;
     double zk;
-    radix_search<false>(r, OP == kOpTopKTopP ? tau : 1u, 0.0, (double)clamp01(pp), sm, tp, zk);
+    radix_search<false>(r, OP == kOpTopKTopP ? tau : 1u, 0.0, (double)clamp01(pp), sm, tp, zk, bad);
     tau = max(tp, tau);
   }
   // one draw over {x >= tau} = {x > low}

@@ -138,3 +138,32 @@ def test_split_fallback_rows_token_exact(op):
                 want = _table(probs[i], op, int(ks[i]), ps[i]).draw(
                     ph.draw_bits53(int(seeds[i]), offset, 0, 0))
                 assert s[i] == want and r[i] == 1, (op, i, offset, int(s[i]), want)
+
+
+@pytest.mark.parametrize("op", ["top_k", "top_k_top_p", "top_k_top_p_joint"])
+def test_split_fallback_invalid_rows(op):
+    """Outputs with k above the split cap reach the exact fallback before any
+    validity check: a NaN, -0.0, a negative value, +inf or an all-zero row
+    must come out invalid there; a valid row beside them is unaffected."""
+    rng = np.random.default_rng(5)
+    V = 8192
+    probs = si.softmax_rows(rng, 6, V, 2.0)
+    probs[0, 17] = np.nan
+    probs[1, 3] = -0.0
+    probs[2, 4000] = -1e-3
+    probs[3, 9] = np.inf
+    probs[4, :] = 0.0
+    ks = np.full(6, 3000, dtype=np.int32)
+    ps = np.full(6, 0.9, dtype=np.float32)
+    P = gpu(probs)
+    if op == "top_k":
+        s, v = dss.top_k_sampling_from_probs(P, gpu(ks), seed=3, return_valid=True)
+    else:
+        order = "joint" if op.endswith("joint") else "top_k_first"
+        s, v = dss.top_k_top_p_sampling_from_probs(P, gpu(ks), gpu(ps), seed=3, return_valid=True,
+                                                   filter_apply_order=order)
+    s, v = host(s), host(v)
+    assert list(v) == [0, 0, 0, 0, 0, 1], list(v)
+    assert list(s[:5]) == [-1] * 5
+    want = _table(probs[5], op, 3000, ps[5]).draw(ph.draw_bits53(3, 0, 5, 0))
+    assert s[5] == want
