@@ -929,7 +929,8 @@ __device__ __forceinline__ void sort_desc(uint64_t* ent, uint32_t n, uint32_t P)
 }
 
 // The row's first k sorted entries (key << 32 | ~index): indices, and the
-// values read back by index (the key folds -0.0 into +0.0); status 0.
+// values, decoded from their signed-order keys; a zero key is read back from
+// the row, since -0.0 and +0.0 share it.  Status 0.
 __device__ __forceinline__ void select_write(const SelectParams& Q, int row, const uint64_t* ent) {
   const int k = Q.k;
   const gptr<const float> x = as_global(Q.in + (int64_t)row * Q.vocab);
@@ -937,9 +938,12 @@ __device__ __forceinline__ void select_write(const SelectParams& Q, int row, con
   const gptr<int32_t> io = as_global(Q.indices + (int64_t)row * k);
   for (int j = threadIdx.x; j < k; j += kBlock) {
     const uint32_t ix = ~(uint32_t)ent[j];
+    const uint32_t key = (uint32_t)(ent[j] >> 32);
     // (always a position of the row; the test keeps any read inside it)
     const bool in = ix < (uint32_t)Q.vocab;
-    vo[j] = in ? x[ix] : __uint_as_float(0x7FC00000u);
+    float val = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+    if (in && key == 0x80000000u) val = x[ix];
+    vo[j] = in ? val : __uint_as_float(0x7FC00000u);
     io[j] = in ? (int32_t)ix : -1;
   }
   if (Q.row_status && threadIdx.x == 0) Q.row_status[row] = 0;
