@@ -24,9 +24,11 @@
  * Workspace.  `workspace` / `workspace_bytes` is caller-owned device scratch
  *   of at least dss_workspace_size(...) bytes (NULL is fine when that is 0):
  *   the split-row engine's hand-off area (top-k and top-k-then-top-p
- *   sampling) and its per-row results (top-k renormalisation and top-k logit
- *   masking), and the resident engine's per-output control blocks and key
- *   lists (plain, top-p and min-p sampling, top-p renormalisation).  It must
+ *   sampling, top-k selection, chain speculative verification) and its
+ *   per-row results (top-k renormalisation and top-k logit masking), and the
+ *   resident engine's per-output control blocks and key lists (plain, top-p
+ *   and min-p sampling, top-p renormalisation, and top-k sampling with one
+ *   scalar k that would crowd the split engine's lists).  It must
  *   be zero-filled once when it is allocated; every call leaves its counters
  *   and control blocks at zero again when its kernels end (the rest is
  *   written before it is read), so a workspace can be reused by later calls
