@@ -48,6 +48,8 @@ constexpr int kRowCandMax = 8192; // entries of all slices of a row (the merge's
 constexpr int kKeptMax = 4096;    // entries of the top-k set (ties included)
 constexpr int kBndMax = 4096;     // entries in the boundary bin
 constexpr int kSplitKCap = 2048;
+static_assert(kSplitKCap == kSplitKCapHost, "the host routes on the same cap");
+static_assert(kSplitScalarKW == kRowCandMax / 2, "half of a row's merge capacity");
 constexpr int kMaxSlices = 16;    // a power of two
 constexpr int kHdrWords = 8;
 constexpr int kMassBins = 256;    // top-p start search: one mass bin per 8 histogram bins

@@ -676,20 +676,26 @@ __device__ __forceinline__ uint32_t radix_sig(uint32_t key) {
 template <bool COUNT, int NB>
 __device__ __forceinline__ void radix_pass(const RowRef& r, uint32_t cut, int hs, uint32_t prefix,
                                            int ls, int e, RadixSmem& sm) {
-  for (int b = threadIdx.x; b < NB; b += kBlock) sm.hh[b] = 0ull;
+  // 2048 / NB copies of every bin (lane parity picks one with two copies),
+  // so that lanes piling into one bin mostly hit different words
+  constexpr uint32_t C = 2048 / NB;
+  const uint32_t cp = (uint32_t)lane_id() & (C - 1u);
+  for (int b = threadIdx.x; b < 2048; b += kBlock) sm.hh[b] = 0ull;
   __syncthreads();
   for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t key = bits_of(v[q]);
       if (valid && idx + q < r.V && key >= cut && (key >> hs) == prefix)
-        atomicAdd(&sm.hh[(key >> ls) & (uint32_t)(NB - 1)],
+        atomicAdd(&sm.hh[((key >> ls) & (uint32_t)(NB - 1)) * C + cp],
                   COUNT ? 1ull : (unsigned long long)radix_sig(key));
     }
   });
   __syncthreads();
   for (int b = threadIdx.x; b < NB; b += kBlock) {
-    const uint64_t x = sm.hh[b];
+    uint64_t x = 0ull;
+#pragma unroll
+    for (uint32_t c = 0; c < C; ++c) x += sm.hh[b * C + c];
     const uint32_t ex = e < 0 ? (uint32_t)b >> 2 : (uint32_t)e;
     sm.md[b] = COUNT ? (double)x : ldexp((double)x, (int)max(ex, 1u) - 150);
   }
