@@ -647,3 +647,55 @@ def test_chain_speculative_invalid_rows():
     p0[1] = 0.0                                              # bonus row with no mass
     ok, tok, acc = ref.chain_speculative(q, [0], p0, [0, 0])
     assert not ok and list(tok) == [-1, -1] and acc == 0
+
+
+# ----------------------------------------------------------------------------
+# pivot2 = (pivot1 + high) / 2 (blog "双枢轴拒绝采样"), traced on the A..E
+# top-2 row of the explainer ("一个简化的 top-k 例子").  The output law does
+# not depend on where pivot2 sits, so only the trace of (low, high) can tell
+# the pages' midpoint from another one (e.g. (low + high) / 2).
+# ----------------------------------------------------------------------------
+
+class _Scripted:
+    """A draw stream that returns the given uniforms u as 53-bit integers."""
+
+    def __init__(self, us):
+        self.a53 = [int(u * 2.0**53) for u in us]
+
+    def next(self):
+        return self.a53.pop(0)
+
+
+def _mid(a, b):
+    return np.float32((np.float64(np.float32(a)) + np.float64(np.float32(b))) / 2)
+
+
+def test_dual_pivot_trace_first_draw_d():
+    """k = 2, first draw D (u = .87 lies in [F_C, F_D) = [.81, .93)):
+    pivot1 = .12 is rejected (three values exceed it); pivot2 = (.12 + .35) / 2
+    = .235 is rejected too (#{x > .235} = 2 is not below k), so low moves to
+    .235 and high stays .35; then A (u = .1 among A, B) is accepted."""
+    row = f32(golden("expl_top2_example.json")["probs"])
+    trace = []
+    j, rounds = ref.dual_pivot_sample(row, "top_k", _Scripted([0.87, 0.1]), k=2, trace=trace)
+    assert (j, rounds) == (0, 2)
+    assert trace == [(np.float32(0), np.float32(0.35)), (_mid(0.12, 0.35), np.float32(0.35))]
+    assert abs(float(trace[1][0]) - 0.235) < 1e-7
+
+
+def test_dual_pivot_trace_second_case():
+    """k = 3 (tau = .18), first draw E (u = .96): pivot1 = .07 is rejected
+    (four values exceed it) but pivot2 = (.07 + .35) / 2 = .21 passes
+    (#{x > .21} = 2 < 3), so (low, high) becomes (.07, .21).  The next draw
+    D (.12, u = .9 of the mass above .07) is rejected and pivot2 =
+    (.12 + .21) / 2 = .165 fails (#{x > .165} = 3), so low moves to .165;
+    then A is accepted."""
+    row = f32(golden("expl_top2_example.json")["probs"])
+    trace = []
+    j, rounds = ref.dual_pivot_sample(row, "top_k", _Scripted([0.96, 0.9, 0.05]), k=3,
+                                      trace=trace)
+    assert (j, rounds) == (0, 3)
+    assert trace[0] == (np.float32(0), np.float32(0.35))
+    assert trace[1] == (np.float32(0.07), _mid(0.07, 0.35))
+    assert trace[2] == (_mid(0.12, _mid(0.07, 0.35)), _mid(0.07, 0.35))
+    assert abs(float(trace[1][1]) - 0.21) < 1e-7 and abs(float(trace[2][0]) - 0.165) < 1e-7
