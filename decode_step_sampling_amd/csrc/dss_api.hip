@@ -99,11 +99,16 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace of the logits path: the engines' area (the softmax kernel's and
-// the sampling call's share one), then the probabilities.
+// the sampling call's share one), then the probabilities.  The probabilities
+// start past the fixed region (control words and resident slots) even when
+// neither engine needs it for this call, so a shared workspace keeps every
+// word that other calls expect at zero.
 size_t logits_engine_bytes(int32_t rows, int32_t vocab, int32_t num_outputs, uint32_t flags) {
   const size_t a = dss_workspace_size(DSS_OP_TOP_K_TOP_P, rows, vocab, num_outputs, flags);
   const size_t b = dss::plan_softmax(rows, vocab, flags, vocab % 4 == 0).workspace;
-  return align256(a > b ? a : b);
+  const size_t c = align256(dss::kFixedRegionBytes);
+  const size_t m = a > b ? a : b;
+  return align256(m > c ? m : c);
 }
 
 int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows, int32_t vocab,

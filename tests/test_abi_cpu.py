@@ -119,9 +119,12 @@ def test_workspace_size_and_strings():
         for rows, vocab, n in ((1, 8, 1), (64, 151936, 64), (512, 256000, 512), (0, 1, 0)):
             size = lib.dss_workspace_size(op, rows, vocab, n, 0)
             assert size >= 0
-            # the streaming engine needs none; the logits path still holds its probabilities
+            # the streaming engine needs none; the logits path still holds its
+            # probabilities, past the fixed region that other calls keep at zero
             probs_bytes = ((rows * vocab * 4 + 255) // 256) * 256 if op == 8 and n > 0 else 0
-            assert lib.dss_workspace_size(op, rows, vocab, n, _lib.DSS_FLAG_STREAMING) == probs_bytes
+            fixed = FIXED_REGION_BYTES if op == 8 and n > 0 else 0
+            assert lib.dss_workspace_size(op, rows, vocab, n, _lib.DSS_FLAG_STREAMING) == \
+                probs_bytes + fixed
     for code in (0, -1, -2, -3, -4, -5):
         assert _lib.strerror(code) not in ("", "unknown status")
     assert _lib.strerror(7) == "unknown status"
@@ -135,6 +138,27 @@ def test_workspace_size_and_strings():
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 6, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(18), 8, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 8, None, None) == _lib.DSS_ERR_INVALID_ARG
+
+
+# control words (16 KiB), 256 resident slots of 67,840 bytes, 256 key lists of
+# 8192 words: the region every call leaves at zero or owns
+FIXED_REGION_BYTES = 16384 + 256 * 67840 + 256 * 8192 * 4
+
+
+@pytest.mark.parametrize("flags", [0, _lib.DSS_FLAG_STREAMING, _lib.DSS_FLAG_FROM_ZERO,
+                                   _lib.DSS_FLAG_ORDER_JOINT])
+@pytest.mark.parametrize("rows,vocab,n", [(64, 151936, 64), (3, 50257, 5), (2, 1000, 2),
+                                          (1, 7, 1), (256, 128256, 512)])
+def test_logits_probabilities_never_overlap_the_fixed_region(flags, rows, vocab, n):
+    """The from-logits call places its probabilities at the end of its
+    workspace (size - the probabilities' bytes); that offset must lie past the
+    control words and resident slots for every shape and flag."""
+    lib = _lib.load()
+    size = lib.dss_workspace_size(8, rows, vocab, n, flags)
+    probs_bytes = ((rows * vocab * 4 + 255) // 256) * 256
+    assert size - probs_bytes >= FIXED_REGION_BYTES
+    # and the sampling call on those probabilities fits the engine part
+    assert size - probs_bytes >= lib.dss_workspace_size(4, rows, vocab, n, flags)
 
 
 def test_top_k_selection_validation():

@@ -145,3 +145,37 @@ def test_sampling_from_logits_invalid_rows():
     s, v = host(s), host(v)
     assert v[0] == 1 and s[0] >= 0
     assert list(v[1:]) == [0, 0] and list(s[1:]) == [-1, -1]
+
+
+@pytest.mark.parametrize("vocab,flags", [(151936, dss.DSS_FLAG_STREAMING), (50257, 0),
+                                         (151936, 0)])
+def test_logits_call_leaves_the_shared_workspace_usable(vocab, flags):
+    """A from-logits call writes its probabilities into the shared workspace;
+    the control words and resident slots that later calls expect at zero
+    must survive it (streaming or ragged shapes need no engine area of their
+    own).  The fused from-probs call and top-p sampling on the same cached
+    workspace afterwards must still give valid draws inside the kept sets."""
+    rng = np.random.default_rng(vocab + flags)
+    rows = 64
+    logits = si.logits_rows(rng, rows, vocab, 2.0)
+    kk = rng.integers(1, 1025, size=rows).astype(np.int32)
+    pp = rng.uniform(0.5, 0.95, size=rows).astype(np.float32)
+    s, v = dss.top_k_top_p_sampling_from_logits(gpu(logits), gpu(kk), gpu(pp), 1.0, seed=5,
+                                                offset=0, return_valid=True, flags=flags)
+    assert host(v).all()
+    w = si.renorm(rows=64, vocab=151936)
+    P = gpu(w["probs"])
+    for off in range(3):
+        s, v = dss.top_k_top_p_sampling_from_probs(P, gpu(w["top_k"]), gpu(w["top_p"]),
+                                                   seed=u64(w["seeds"]), offset=off,
+                                                   return_valid=True)
+        s2, v2 = dss.top_p_sampling_from_probs(P, gpu(w["top_p"]), seed=u64(w["seeds"]),
+                                               offset=off, return_valid=True)
+        s, v, s2, v2 = host(s), host(v), host(s2), host(v2)
+        assert v.all() and v2.all()
+        for r in range(0, 64, 7):
+            _, tau = ref.threshold(w["probs"][r], "top_k_top_p", k=w["top_k"][r],
+                                   p=w["top_p"][r])
+            assert ref.support_mask(w["probs"][r], tau)[s[r]]
+            _, tau = ref.threshold(w["probs"][r], "top_p", p=w["top_p"][r])
+            assert ref.support_mask(w["probs"][r], tau)[s2[r]]

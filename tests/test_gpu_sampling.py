@@ -209,6 +209,44 @@ def test_headline_support_full_size(order):
     assert rounds_all.min() >= 1 and rounds_all.max() < 64
 
 
+def test_headline_chi_square_at_full_size():
+    """The headline batch itself (B=64, V=151936, per-row k and p; the split
+    engine's W=4 plan, ten vectors per thread): 20000 separate calls with
+    offsets 0..19999, then a chi-square test (alpha = 1e-3) per row against
+    the oracle's target law ([Expl] "统计正确性应该怎样测试") on eight rows:
+    the largest k, the smallest and the largest p, the smallest k, and four
+    more.  A certified top-p start set too high or a dropped kept candidate
+    would leave tokens of the kept set undrawn, which only a distribution
+    test can see."""
+    w = si.renorm()
+    probs = w["probs"]
+    rows, V = probs.shape
+    ks, ps = w["top_k"], w["top_p"]
+    pick = [int(np.argmax(ks)), int(np.argmin(ps)), int(np.argmax(ps)), int(np.argmin(ks))]
+    for r in range(rows):
+        if len(set(pick)) >= 8:
+            break
+        pick.append(r)
+    pick = sorted(set(pick))
+    assert len(pick) == 8
+    P = gpu(probs)
+    k_t, p_t = gpu(ks), gpu(ps)
+    seeds = u64(w["seeds"])
+    draws = 20000
+    out = torch.empty(draws, rows, dtype=torch.int32, device="cuda:0")
+    for t in range(draws):
+        out[t] = dss.top_k_top_p_sampling_from_probs(P, k_t, p_t, seed=seeds, offset=t)
+    s = host(out)
+    for row in pick:
+        _, tau = ref.threshold(probs[row], "top_k_top_p", k=ks[row], p=ps[row])
+        support = ref.support_mask(probs[row], tau)
+        assert support[s[:, row]].all(), row
+        counts = np.bincount(s[:, row], minlength=V)
+        pval, tvd, cells = pooled_chi_square(counts[support],
+                                             ref.target_distribution(probs[row], tau)[support])
+        assert pval > 1e-3, (row, int(ks[row]), float(ps[row]), pval, tvd, cells)
+
+
 # ----------------------------------------------------------------------------
 # degenerate rows and parameters ("退化分布必须可报告")
 # ----------------------------------------------------------------------------
