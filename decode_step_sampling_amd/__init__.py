@@ -13,6 +13,8 @@ output parameters (``top_k``, ``top_p``, ``min_p``) are Python scalars or
 with one value per output, read as unsigned 64-bit.
 """
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -25,6 +27,7 @@ __all__ = [
     "min_p_sampling_from_probs", "top_k_top_p_sampling_from_probs",
     "top_k_renorm_probs", "top_p_renorm_probs", "top_k_mask_logits",
     "softmax", "top_k_top_p_sampling_from_logits", "top_k", "chain_speculative_sampling",
+    "workspace_status", "reset_workspace",
     "DssError", "DSS_FLAG_FROM_ZERO", "DSS_FLAG_STREAMING", "DSS_FLAG_ORDER_JOINT",
     "DSS_FLAG_SINGLE_PIVOT",
 ]
@@ -42,14 +45,47 @@ def _stream(device):
 
 
 def _workspace(device, nbytes):
-    """Zero-filled scratch kept per device; the kernels leave it zeroed."""
+    """Zero-filled scratch kept per (device, stream); the kernels leave it
+    zeroed.  Calls on different streams may run concurrently and so get
+    different buffers.  A buffer is allocated while its stream is current, so
+    the caching allocator hands its memory back only to work ordered after
+    the kernels that used it when it grows."""
     if nbytes == 0:
         return None, 0
-    buf = _workspaces.get(device)
+    key = (device, _stream(device))
+    buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        _workspaces[device] = buf
+        with torch.cuda.device(device):
+            buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
     return buf.data_ptr(), buf.numel()
+
+
+def workspace_status(device=None):
+    """Resident control blocks of this stream's cached workspace whose row
+    barrier was given up (dss_workspace_status): a list of slot numbers,
+    empty when the workspace is clean.  Waits for the stream."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    buf = _workspaces.get((device, _stream(device)))
+    if buf is None:
+        return []
+    flags = (ctypes.c_uint8 * 256)()
+    with torch.cuda.device(device):
+        n = _lib.load().dss_workspace_status(buf.data_ptr(), buf.numel(), flags, _stream(device))
+    if n < 0:
+        _lib.check(n, "workspace_status")
+    return [i for i in range(256) if flags[i]]
+
+
+def reset_workspace(device=None):
+    """Zero this stream's cached workspace again (after a resident wait gave
+    up: see workspace_status).  Enqueued on the current stream."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    buf = _workspaces.get((device, _stream(device)))
+    if buf is not None:
+        buf.zero_()
 
 
 def _check_rows(x, name):

@@ -1,4 +1,5 @@
-"""ctypes loader for libdss.so (the C ABI declared in include/dss.h).
+"""ctypes loader for libdss.so (the C ABI declared in include/dss.h and the
+measurement / test hooks of include/dss_hooks.h).
 
 The library is built in-tree by ``python -m decode_step_sampling_amd.build``.
 There is no fallback: if the library is missing, every op raises.
@@ -69,6 +70,8 @@ SIGNATURES = {
     "dss_version": ([], ctypes.c_int32),
     "dss_set_timing_events": ([_P, _P], ctypes.c_int32),
     "dss_stream_read_reference": ([_P, ctypes.c_int64, _P, _P], ctypes.c_int32),
+    "dss_set_spin_limit": ([_U64], ctypes.c_int32),
+    "dss_workspace_status": ([_P, _SZ, _P, _P], ctypes.c_int32),
 }
 
 _lib = None

@@ -15,6 +15,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<void*> g_ev_start{nullptr}, g_ev_stop{nullptr};  // dss_set_timing_events
+std::atomic<uint64_t> g_spin_ticks{dss::kDefaultSpinTicks};  // dss_set_spin_limit
 
 dss::LaunchEvents timing_events() {
   return dss::LaunchEvents{static_cast<hipEvent_t>(g_ev_start.load(std::memory_order_relaxed)),
@@ -151,6 +152,10 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
 }
 
 }  // namespace
+
+namespace dss {
+uint64_t spin_limit_ticks() { return g_spin_ticks.load(std::memory_order_relaxed); }
+}  // namespace dss
 
 DSS_EXPORT int dss_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
                                        const int32_t* indices, int32_t num_outputs,
@@ -401,6 +406,38 @@ DSS_EXPORT int32_t dss_set_timing_events(void* start, void* stop) {
   g_ev_start.store(start, std::memory_order_relaxed);
   g_ev_stop.store(stop, std::memory_order_relaxed);
   return DSS_OK;
+}
+
+DSS_EXPORT int32_t dss_set_spin_limit(uint64_t ticks) {
+  g_spin_ticks.store(ticks == UINT64_MAX ? dss::kDefaultSpinTicks : ticks,
+                     std::memory_order_relaxed);
+  return DSS_OK;
+}
+
+DSS_EXPORT int32_t dss_workspace_status(const void* workspace, size_t workspace_bytes,
+                                        uint8_t* broken, void* stream) {
+  if (workspace_bytes > 0 && workspace == nullptr) return DSS_ERR_INVALID_ARG;
+  const int slots = workspace_bytes >= dss::kFixedRegionBytes ? dss::kResidentSlots : 0;
+  if (broken) std::memset(broken, 0, dss::kResidentSlots);
+  if (slots == 0) return 0;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+  // the arrival counter of every resident slot (its first word), strided
+  uint32_t ctr[dss::kResidentSlots];
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpy2DAsync(ctr, sizeof(uint32_t),
+                       static_cast<const char*>(workspace) + dss::kCtlRegionBytes,
+                       dss::kResidentSlotBytes, sizeof(uint32_t), slots, hipMemcpyDeviceToHost,
+                       st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return DSS_ERR_HIP;
+  int n = 0;
+  for (int q = 0; q < slots; ++q) {
+    const bool b = (ctr[q] & 0x80000000u) != 0u;
+    n += b ? 1 : 0;
+    if (broken) broken[q] = b ? 1 : 0;
+  }
+  return n;
 }
 
 DSS_EXPORT int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max,

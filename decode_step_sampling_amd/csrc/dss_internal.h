@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "dss.h"
+#include "dss_hooks.h"
 
 namespace dss {
 
@@ -68,6 +69,11 @@ struct LaunchEvents {
   hipEvent_t start;
   hipEvent_t stop;
 };
+
+// Longest wait of a resident row barrier, in ticks of the 100 MHz constant
+// clock (dss_set_spin_limit; 50 ms unless changed).
+uint64_t spin_limit_ticks();
+constexpr uint64_t kDefaultSpinTicks = 5000000ull;
 
 // Launch kernel on stream s, attaching the dispatch events of ev that apply
 // (start if first, stop if last).

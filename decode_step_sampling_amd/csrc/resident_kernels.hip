@@ -39,7 +39,12 @@
 // live in that XCD's L2.  Every launch holds at most as many work-groups as
 // the device keeps resident at once, so no work-group waits on one that
 // cannot start; a spin that still runs out of time marks the output invalid
-// instead of hanging.
+// instead of hanging.  It also marks the slot's arrival counter broken (its
+// top bit, set by a compare-and-swap that fails if the barrier completes
+// meanwhile): every later arrival at that counter, in this launch or any
+// later one, fails at once, so a dirty slot is never counted as clean.  The
+// mark stays until the caller zeroes the workspace (dss_workspace_status
+// reports it).
 #include "stream_device.h"
 
 namespace dss {
@@ -51,7 +56,7 @@ constexpr int kRB1 = 1024;   // level 1: bits [30:21]
 constexpr int kRB2 = 2048;   // level 2: bits [20:10]
 constexpr int kRB3 = 1024;   // level 3: bits [9:0]
 constexpr int kRHistWords = 8192;  // LDS histogram words: bins x copies
-constexpr uint64_t kSpinTicks = 5000000ull;  // 50 ms of the 100 MHz constant clock
+constexpr uint32_t kBroken = 0x80000000u;    // arrival-counter mark of a barrier given up
 
 // Per-output control block in the workspace, zero between calls.
 struct RowSlot {
@@ -73,6 +78,7 @@ struct ResidentParams {
   int n_out;  // outputs of this launch
   RowSlot* slots;
   uint32_t* lists;  // [n_out * W][kResidentSegKeys] boundary-bin keys per work-group
+  uint64_t spin;    // ticks of the 100 MHz constant clock a row barrier waits at most
 };
 
 enum ResKind : int { kResSample = 0, kResRenorm = 1 };
@@ -114,21 +120,39 @@ __device__ __forceinline__ uint32_t max4(const float4& x) {
 
 // Arrive at the row barrier and wait until `target` arrivals are counted.
 // Every thread must call; each thread's earlier global stores and atomics are
-// complete (vmcnt 0) before thread 0 arrives.  False if the wait timed out.
-__device__ __forceinline__ bool row_barrier(gptr<uint32_t> ctr, uint32_t target, ResSmem& sm) {
+// complete (vmcnt 0) before thread 0 arrives.  False if the counter is
+// broken, or if the wait runs past `spin` ticks: the waiter then breaks the
+// counter itself, with a compare-and-swap on the count it last saw, so that
+// either the barrier completed first (the swap fails and the new count
+// passes) or every work-group that arrives later fails too.  Arrivals only
+// raise the count, so a barrier that was reached can no longer be broken.
+__device__ __forceinline__ bool row_barrier(gptr<uint32_t> ctr, uint32_t target, uint64_t spin,
+                                            ResSmem& sm) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (the clock starts before the arrival, so a limit of 0 gives up at once
+    // unless this arrival completes the barrier)
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    int ok = 1;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-        ok = 0;
+    uint32_t c = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    int ok = 0;
+    while (true) {
+      if (c & kBroken) break;
+      if (c >= target) {
+        ok = 1;
         break;
       }
+      if (__builtin_amdgcn_s_memrealtime() - t0 >= spin) {
+        uint32_t seen = c;
+        __hip_atomic_compare_exchange_strong(ctr, &seen, c | kBroken, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seen == c) break;  // broken by this work-group
+        c = seen;              // the count moved: examine it again
+        continue;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     sm.flag = ok;
   }
@@ -432,8 +456,8 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
                                            double need_in, double pfrac, gptr<uint64_t> g1,
                                            gptr<uint64_t> g2, gptr<uint64_t> g3,
                                            gptr<uint32_t> ctl, gptr<uint32_t> seg_base, int li,
-                                           int s, int W, uint32_t& passed, ResSmem& sm,
-                                           uint32_t& tau, double& kept) {
+                                           int s, int W, uint64_t spin, uint32_t& passed,
+                                           ResSmem& sm, uint32_t& tau, double& kept) {
   const int tid = threadIdx.x, lane = lane_id(), wave = r_uwave();
   clear_lds_hist(sm);
   __syncthreads();
@@ -451,7 +475,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
   publish_hist<kRB1>(sm, g1);
   __syncthreads();
   clear_lds_hist(sm);
-  if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+  if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
   ++passed;
   load_level<COUNT, kRB1>(g1, -1, sm);
   __syncthreads();
@@ -504,7 +528,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
       }
     }
     if (tid == 0) __hip_atomic_store(ctl + 8 + s, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
     ++passed;
     if (wave == 0) {
       const uint32_t c = lane < W ? __hip_atomic_load(ctl + 8 + lane, __ATOMIC_RELAXED,
@@ -575,7 +599,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     publish_hist<kRB2>(sm, g2);
     __syncthreads();
     clear_lds_hist(sm);
-    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
     ++passed;
     load_level<COUNT, kRB2>(g2, (int)e1, sm);
     __syncthreads();
@@ -604,7 +628,7 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     }
     __syncthreads();
     publish_hist<kRB3>(sm, g3);
-    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm)) return false;
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
     ++passed;
     load_level<COUNT, kRB3>(g3, (int)e1, sm);
     __syncthreads();
@@ -751,7 +775,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     __syncthreads();
     clear_lds_hist(sm);
   }
-  if (!row_barrier(ctl, (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+  if (!row_barrier(ctl, (uint32_t)W, R.spin, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
   passed = 1u;
   const uint32_t gmax = __hip_atomic_load(ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t xm = __hip_atomic_load(ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -814,7 +838,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
         }
       }
       if (tid == 0) __hip_atomic_store(ctl + 8 + s, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+      if (!row_barrier(ctl, 2u * (uint32_t)W, R.spin, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
       passed = 2u;
       // every work-group: all of the row's keys in bin b1 (at most kResidentSegKeys)
       if (wave == 0) {
@@ -897,7 +921,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       publish_hist<kRB2>(sm, (gptr<uint64_t>)slot->h2);
       __syncthreads();
       clear_lds_hist(sm);
-      if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+      if (!row_barrier(ctl, 2u * (uint32_t)W, R.spin, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
       passed = 2u;
       load_masses<kRB2>((gptr<uint64_t>)slot->h2, (int)(b1 >> 2), sm);
       __syncthreads();
@@ -926,7 +950,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       }
       __syncthreads();
       publish_hist<kRB3>(sm, (gptr<uint64_t>)slot->h3);
-      if (!row_barrier(ctl, 3u * (uint32_t)W, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+      if (!row_barrier(ctl, 3u * (uint32_t)W, R.spin, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
       passed = 3u;
       load_masses<kRB3>((gptr<uint64_t>)slot->h3, (int)(b1 >> 2), sm);
       __syncthreads();
@@ -956,7 +980,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     double cnt;
     if (!res_search<true, NV>(v, vbase, nvec, 0u, (double)kk, -1.0, (gptr<uint64_t>)slot->k1,
                               (gptr<uint64_t>)slot->k2, (gptr<uint64_t>)slot->k3, ctl,
-                              as_global(R.lists), li, s, W, passed, sm, tk, cnt))
+                              as_global(R.lists), li, s, W, R.spin, passed, sm, tk, cnt))
       return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
     tau = max(tk, 1u);  // zeros carry no mass
     if (OP == kOpTopKTopP) {
@@ -964,7 +988,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       double zk;
       if (!res_search<false, NV>(v, vbase, nvec, tau, 0.0, (double)pc, (gptr<uint64_t>)slot->h1,
                                  (gptr<uint64_t>)slot->h2, (gptr<uint64_t>)slot->h3, ctl,
-                                 as_global(R.lists), li, s, W, passed, sm, tp, zk))
+                                 as_global(R.lists), li, s, W, R.spin, passed, sm, tp, zk))
         return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
       tau = max(tp, tau);
     }
@@ -988,7 +1012,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   // ---- sampling: kept mass per (slice, wave), one draw, the owner walks -----
   if (OP != kOpNone) {
     publish_chunks();
-    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, sm))
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, R.spin, sm))
       return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
     ++passed;
   }
@@ -1144,7 +1168,7 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(SoftmaxParams Q, Reside
       if (vbase + j * kWave < nvec) dst[vbase + j * kWave] = o;
     if (s == 0 && tid == 0 && Q.row_status) as_global(Q.row_status)[row] = 1;
   };
-  if (!row_barrier(ctl, (uint32_t)W, sm)) return invalid();
+  if (!row_barrier(ctl, (uint32_t)W, R.spin, sm)) return invalid();
   const uint32_t gk = __hip_atomic_load(ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t gb = __hip_atomic_load(ctl + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t xm = __hip_atomic_load(ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1175,7 +1199,7 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(SoftmaxParams Q, Reside
     for (int w = 0; w < kWaves; ++w) z += sm.md[w];
     __hip_atomic_store((gptr<double>)slot->chunk + s, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (!row_barrier(ctl, 2u * (uint32_t)W, sm)) return invalid();
+  if (!row_barrier(ctl, 2u * (uint32_t)W, R.spin, sm)) return invalid();
   if (wave == 0) {
     const double z = lane < W ? __hip_atomic_load((gptr<double>)slot->chunk + lane, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT)
@@ -1228,6 +1252,7 @@ hipError_t launch_res_one(const SampleParams& p, const RenormParams& rp, const S
   R.W = plan.W;
   R.L = plan.L;
   R.slots = reinterpret_cast<RowSlot*>(static_cast<char*>(workspace) + kCtlRegionBytes);
+  R.spin = spin_limit_ticks();
   R.lists = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kCtlRegionBytes +
                                         (size_t)kResidentSlots * kResidentSlotBytes);
   // outputs per launch: whole groups of eight (one per XCD), all resident
@@ -1339,6 +1364,7 @@ hipError_t launch_softmax_nv(const SoftmaxParams& q, const SplitPlan& plan, void
   R.W = plan.W;
   R.L = plan.L;
   R.slots = reinterpret_cast<RowSlot*>(static_cast<char*>(workspace) + kCtlRegionBytes);
+  R.spin = spin_limit_ticks();
   R.lists = nullptr;
   const int per = min(plan.chunk, (cap / (8 * plan.W)) * 8);
   if (per <= 0) return hipErrorInvalidConfiguration;

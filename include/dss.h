@@ -40,9 +40,11 @@
  *   work-groups than the device keeps resident at once.  Work that runs
  *   concurrently on other streams can still hold compute units; a
  *   work-group that waits more than 50 ms reports its output invalid
- *   (sample -1, valid 0; renorm rows NaN) instead of hanging, and leaves its
- *   control block dirty (zero the workspace again before reusing it).
- *   Callers that overlap other kernels with these ops can pass
+ *   (sample -1, valid 0; renorm rows NaN) instead of hanging, and marks its
+ *   control block broken: every later output that uses that block comes
+ *   out invalid as well (never counted against stale state) until the
+ *   workspace is zero-filled again; dss_workspace_status reports such
+ *   blocks.  Callers that overlap other kernels with these ops can pass
  *   DSS_FLAG_STREAMING, whose engine never waits.
  *
  * Outputs of the sampling ops (length num_outputs):
@@ -317,25 +319,16 @@ int dss_chain_speculative_sampling(const float* draft_probs, const int32_t* draf
 size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
                           int32_t num_outputs, uint32_t flags);
 
-/* Profiling hook (not part of the sampling path).  With two hipEvent_t
- * handles (passed as void*, both non-NULL), every later call of this process
- * attaches them to its kernels as dispatch events (hipExtLaunchKernel): the
- * first kernel of the call records `start` when it begins executing, the
- * last records `stop` when it ends, so hipEventElapsedTime(start, stop) is
- * the call's kernel time as a kernel-trace profiler reports it.  (NULL,
- * NULL) switches the hook off.  Process-wide; the caller owns the events
- * and must keep them alive while the hook is on.  Returns DSS_ERR_INVALID_ARG
- * if exactly one handle is NULL. */
-int32_t dss_set_timing_events(void* start, void* stop);
-
-/* Measurement aid (not part of the sampling path): one plain streaming read
- * of n floats at x (device, 16-byte aligned, n a multiple of 4), five
- * 16-byte loads in flight per thread, folding the largest float32 bit
- * pattern into *out_max (device uint32, caller-initialised; atomicMax).
- * Its time is the read rate this GPU reaches for that many bytes, the
- * reference beside the sampling kernels' HBM fraction.  Enqueued on
- * `stream`.  DSS_ERR_INVALID_ARG for a bad size, pointer or alignment. */
-int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max, void* stream);
+/* State of a workspace's resident control blocks: the number of slots
+ * (0 .. 256) whose row barrier was given up (see "Co-residency" above);
+ * broken (nullable, host memory of 256 bytes) receives one flag per slot.
+ * Outputs that a later call maps to such a slot (output index modulo the
+ * launch's chunk) come out invalid until the workspace is zero-filled again.
+ * Reads the workspace on `stream` and waits for it (host-synchronous).
+ * Returns a negative status for a NULL workspace with nonzero size or a
+ * HIP failure; 0 for a workspace too small to hold the slots. */
+int32_t dss_workspace_status(const void* workspace, size_t workspace_bytes, uint8_t* broken,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* dss_strerror(int32_t status);

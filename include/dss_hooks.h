@@ -1,0 +1,51 @@
+/*
+ * dss_hooks.h -- measurement and test hooks of libdss.so.
+ *
+ * Not part of the sampling ops (include/dss.h): these calls exist so that a
+ * benchmark can time kernels without a profiler, compare the sampling
+ * kernels with a plain read of the same bytes, and so that tests can force
+ * the resident engine's bounded wait to give up while every kernel still
+ * exits normally.  All are process-wide and take effect for later calls.
+ */
+#ifndef DSS_HOOKS_H
+#define DSS_HOOKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Profiling hook (not part of the sampling path).  With two hipEvent_t
+ * handles (passed as void*, both non-NULL), every later call of this process
+ * attaches them to its kernels as dispatch events (hipExtLaunchKernel): the
+ * first kernel of the call records `start` when it begins executing, the
+ * last records `stop` when it ends, so hipEventElapsedTime(start, stop) is
+ * the call's kernel time as a kernel-trace profiler reports it.  (NULL,
+ * NULL) switches the hook off.  Process-wide; the caller owns the events
+ * and must keep them alive while the hook is on.  Returns DSS_ERR_INVALID_ARG
+ * if exactly one handle is NULL. */
+int32_t dss_set_timing_events(void* start, void* stop);
+
+/* Measurement aid (not part of the sampling path): one plain streaming read
+ * of n floats at x (device, 16-byte aligned, n a multiple of 4), five
+ * 16-byte loads in flight per thread, folding the largest float32 bit
+ * pattern into *out_max (device uint32, caller-initialised; atomicMax).
+ * Its time is the read rate this GPU reaches for that many bytes, the
+ * reference beside the sampling kernels' HBM fraction.  Enqueued on
+ * `stream`.  DSS_ERR_INVALID_ARG for a bad size, pointer or alignment. */
+int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max, void* stream);
+
+/* Longest wait of a resident row barrier, in ticks of the GPU's 100 MHz
+ * constant clock (default 5,000,000 = 50 ms).  UINT64_MAX restores the
+ * default.  A small limit makes waits give up (the output is reported
+ * invalid and its control block marked broken, see dss.h "Co-residency"):
+ * for tests of that path only.  Always DSS_OK. */
+int32_t dss_set_spin_limit(uint64_t ticks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSS_HOOKS_H */

@@ -15,13 +15,14 @@ from decode_step_sampling_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dss.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "dss_hooks.h")]
 
 NULL = None
 FAKE = 0x1000          # never dereferenced: validation fails before any use
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*|int32_t)\s+(dss_\w+)\s*\(",
                                  text, re.M)))
 
@@ -34,7 +35,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -138,6 +139,13 @@ def test_workspace_size_and_strings():
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 6, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(18), 8, out, None) == _lib.DSS_ERR_INVALID_ARG
     assert lib.dss_stream_read_reference(ctypes.c_void_p(16), 8, None, None) == _lib.DSS_ERR_INVALID_ARG
+    # workspace state: argument checks and workspaces too small to hold the
+    # resident slots need no HIP call
+    flags = (ctypes.c_uint8 * 256)()
+    assert lib.dss_workspace_status(None, 64, flags, None) == _lib.DSS_ERR_INVALID_ARG
+    assert lib.dss_workspace_status(None, 0, flags, None) == 0
+    assert lib.dss_workspace_status(ctypes.c_void_p(16), 4096, None, None) == 0
+    assert lib.dss_set_spin_limit(2**64 - 1) == _lib.DSS_OK   # restores the default
 
 
 # control words (16 KiB), 256 resident slots of 67,840 bytes, 256 key lists of
