@@ -56,6 +56,8 @@ SIGNATURES = {
     "dss_top_p_sampling_from_probs": (_HEAD + [_P, _F32] + _TAIL, ctypes.c_int),
     "dss_min_p_sampling_from_probs": (_HEAD + [_P, _F32] + _TAIL, ctypes.c_int),
     "dss_top_k_top_p_sampling_from_probs": (_HEAD + [_P, _I32, _P, _F32] + _TAIL, ctypes.c_int),
+    "dss_top_k_top_p_sampling_from_probs_noalloc": (_HEAD + [_P, _I32, _P, _F32, _P, _P, _P,
+                                                             _U32, _P], ctypes.c_int),
     "dss_top_k_renorm_probs": ([_P, _P, _I32, _I32, _P, _I32] + _RENORM_TAIL, ctypes.c_int),
     "dss_top_p_renorm_probs": ([_P, _P, _I32, _I32, _P, _F32] + _RENORM_TAIL, ctypes.c_int),
     "dss_top_k_mask_logits": ([_P, _P, _I32, _I32, _P, _I32] + _RENORM_TAIL, ctypes.c_int),

@@ -44,7 +44,8 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
                   int32_t top_k, const float* top_p_arr, float top_p, const float* min_p_arr,
                   float min_p, int32_t* samples, uint8_t* valid, int32_t* rounds, uint32_t flags,
                   void* workspace, size_t workspace_bytes, void* stream,
-                  const dss::LaunchEvents& ev, bool check_only = false) {
+                  const dss::LaunchEvents& ev, bool check_only = false,
+                  bool repair_slots = false) {
   if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
   // the joint order only exists for the combined filter; the engines know it
   // as an op of its own (the public op id still sizes the workspace)
@@ -90,6 +91,9 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.vec_ok = vec_ok;
   p.single_pivot = (flags & DSS_FLAG_SINGLE_PIVOT) ? 1 : 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (repair_slots && plan.W == 0 && rplan.W > 0 &&
+      dss::launch_resident_repair(workspace, st) != hipSuccess)
+    return DSS_ERR_HIP;
   const hipError_t e =
       plan.W > 0    ? dss::launch_split_sample(eop, p, plan, workspace, st, ev)
       : rplan.W > 0 ? dss::launch_resident_sample(eop, p, rplan, workspace, st, ev)
@@ -157,6 +161,30 @@ namespace dss {
 uint64_t spin_limit_ticks() { return g_spin_ticks.load(std::memory_order_relaxed); }
 }  // namespace dss
 
+// Scratch of the allocation-free entry point: one array per GPU the library
+// runs on, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// uses the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+}  // namespace
+
 DSS_EXPORT int dss_sampling_from_probs(const float* probs, int32_t rows, int32_t vocab,
                                        const int32_t* indices, int32_t num_outputs,
                                        const uint64_t* seed_arr, uint64_t seed,
@@ -217,6 +245,31 @@ DSS_EXPORT int dss_top_k_top_p_sampling_from_probs(
   return sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs, seed_arr,
                        seed, offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p, nullptr,
                        0.0f, samples, valid, rounds, flags, workspace, workspace_bytes, stream, timing_events());
+}
+
+DSS_EXPORT int dss_top_k_top_p_sampling_from_probs_noalloc(
+    const float* probs, int32_t rows, int32_t vocab, const int32_t* indices, int32_t num_outputs,
+    const uint64_t* seed_arr, uint64_t seed, const uint64_t* offset_arr, uint64_t offset,
+    const int32_t* top_k_arr, int32_t top_k, const float* top_p_arr, float top_p,
+    int32_t* samples, uint8_t* valid, int32_t* rounds, uint32_t flags, void* stream) {
+  // every host check of the call first (no HIP call; the workspace pointer
+  // is only tested for NULL there), then the scratch's size
+  const int chk = sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs,
+                                seed_arr, seed, offset_arr, offset, top_k_arr, top_k, top_p_arr,
+                                top_p, nullptr, 0.0f, samples, valid, rounds, flags,
+                                reinterpret_cast<void*>(static_cast<uintptr_t>(256)),
+                                SIZE_MAX, stream, timing_events(), true);
+  if (chk != DSS_OK || num_outputs == 0) return chk;
+  if (dss_workspace_size(DSS_OP_TOP_K_TOP_P, rows, vocab, num_outputs, flags) > kScratchBytes)
+    return DSS_ERR_WORKSPACE;
+  const int dev = check_device();
+  if (dev != DSS_OK) return dev;
+  void* ws = scratch_address();
+  if (ws == nullptr) return DSS_ERR_HIP;
+  return sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs, seed_arr, seed,
+                       offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p, nullptr, 0.0f,
+                       samples, valid, rounds, flags, ws, kScratchBytes, stream, timing_events(),
+                       false, true);
 }
 
 DSS_EXPORT int dss_top_k_renorm_probs(const float* probs, float* out, int32_t rows, int32_t vocab,

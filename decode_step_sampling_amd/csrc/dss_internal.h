@@ -141,6 +141,8 @@ hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan
                                   void* workspace, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_resident_renorm(const RenormParams& p, const SplitPlan& plan, void* workspace,
                                   hipStream_t s, const LaunchEvents& ev);
+// Zero the slots of workspace whose row barrier was given up (broken mark).
+hipError_t launch_resident_repair(void* workspace, hipStream_t s);
 
 // Probabilities from logits with a temperature, p = softmax(z / T) per row
 // (T per row or one scalar); invalid rows are NaN-filled with status 1.

@@ -1231,6 +1231,7 @@ namespace dss {
 namespace {
 
 static_assert(sizeof(RowSlot) == kResidentSlotBytes, "workspace layout of the resident engine");
+static_assert(sizeof(RowSlot) % 16 == 0, "slots cleared in 16-byte words");
 
 
 template <int KIND, int OP, int NV>
@@ -1323,6 +1324,28 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
   plan.handoff = kFixedRegionBytes;
   plan.workspace = kFixedRegionBytes;
   return plan;
+}
+
+namespace {
+// Zero every slot whose arrival counter carries the broken mark (a row
+// barrier given up in an earlier launch), for a workspace that no caller can
+// zero.  One work-group per slot; the kernels that use the slots come later
+// on the same stream, so no work-group of theirs can see a half-cleared slot.
+__global__ __launch_bounds__(256) void repair_kernel(RowSlot* slots) {
+  const gptr<RowSlot> slot = as_global(slots + blockIdx.x);
+  const uint32_t c = __hip_atomic_load((gptr<uint32_t>)slot->ctl, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  if (!(c & kBroken)) return;
+  uint4* w = reinterpret_cast<uint4*>(slots + blockIdx.x);
+  for (int q = threadIdx.x; q < (int)(sizeof(RowSlot) / 16); q += 256)
+    w[q] = make_uint4(0u, 0u, 0u, 0u);
+}
+}  // namespace
+
+hipError_t launch_resident_repair(void* workspace, hipStream_t s) {
+  RowSlot* slots = reinterpret_cast<RowSlot*>(static_cast<char*>(workspace) + kCtlRegionBytes);
+  hipLaunchKernelGGL(repair_kernel, dim3(kResidentSlots), dim3(256), 0, s, slots);
+  return hipGetLastError();
 }
 
 hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan& plan,

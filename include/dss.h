@@ -208,6 +208,33 @@ int dss_top_k_top_p_sampling_from_probs(const float* probs, int32_t rows, int32_
                                         uint32_t flags, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* Allocation-free variant of dss_top_k_top_p_sampling_from_probs, for
+ * callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, semantics and outputs (token for token: the same kernels
+ * and streams) without workspace / workspace_bytes; the kernels' scratch is
+ * a static device array of the library, 64 MiB on every GPU the library runs
+ * on, held until the process ends.  A call whose
+ * dss_workspace_size(DSS_OP_TOP_K_TOP_P, rows, vocab, num_outputs, flags)
+ * exceeds 64 MiB returns DSS_ERR_WORKSPACE before anything is enqueued (the
+ * headline shape, 64 rows of 151936, needs 34.2 MB; up to about 1000 slices
+ * of the split engine fit).  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); the first call on a device looks
+ * up the array's device address once.  Every call on one GPU shares the
+ * array: calls that overlap on one GPU (concurrent streams, threads) race
+ * and must be serialised by the caller.  The array is zero when the library
+ * loads and the kernels leave it so; a resident control block whose wait
+ * was given up ("Co-residency") is zeroed again by a small kernel before
+ * the next call that uses the resident engine. */
+int dss_top_k_top_p_sampling_from_probs_noalloc(const float* probs, int32_t rows, int32_t vocab,
+                                                const int32_t* indices, int32_t num_outputs,
+                                                const uint64_t* seed_arr, uint64_t seed,
+                                                const uint64_t* offset_arr, uint64_t offset,
+                                                const int32_t* top_k_arr, int32_t top_k,
+                                                const float* top_p_arr, float top_p,
+                                                int32_t* samples, uint8_t* valid, int32_t* rounds,
+                                                uint32_t flags, void* stream);
+
 /* Top-k renormalisation ([F4 §②-④], [Expl "只过滤/归一化"]):
  * out[r, i] = x_i / Z_kept if x_i >= tau_k else 0.  top_k_arr has `rows`
  * entries (per row).  out may equal probs (in place). */

@@ -35,7 +35,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -146,6 +146,25 @@ def test_workspace_size_and_strings():
     assert lib.dss_workspace_status(None, 0, flags, None) == 0
     assert lib.dss_workspace_status(ctypes.c_void_p(16), 4096, None, None) == 0
     assert lib.dss_set_spin_limit(2**64 - 1) == _lib.DSS_OK   # restores the default
+
+
+def test_noalloc_entry_point_validation():
+    """Host checks of the allocation-free call, before any HIP call: the
+    same argument checks as the workspace call, and shapes whose scratch
+    would exceed the library's 64 MiB static array are refused."""
+    lib = _lib.load()
+    fn = lib.dss_top_k_top_p_sampling_from_probs_noalloc
+
+    def call(probs=FAKE, rows=4, vocab=1000, n=4, indices=NULL, samples=FAKE, flags=0):
+        return fn(probs, rows, vocab, indices, n, NULL, 1, NULL, 0, NULL, 5, NULL, 0.9, samples,
+                  NULL, NULL, flags, NULL)
+    assert call(probs=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(samples=NULL) == _lib.DSS_ERR_INVALID_ARG
+    assert call(rows=3) == _lib.DSS_ERR_INVALID_ARG            # n != rows without indices
+    assert call(flags=0x100) == _lib.DSS_ERR_INVALID_ARG
+    assert call(vocab=_lib.DSS_MAX_VOCAB + 1) == _lib.DSS_ERR_UNSUPPORTED
+    assert call(probs=NULL, samples=NULL, rows=0, n=0) == _lib.DSS_OK
+    assert call(rows=4096, vocab=151936, n=4096) == _lib.DSS_ERR_WORKSPACE
 
 
 # control words (16 KiB), 256 resident slots of 67,840 bytes, 256 key lists of
