@@ -46,8 +46,15 @@ def _run(cmd, verbose):
     return res
 
 
-def build(verbose=False, jobs=8):
-    """Compile every source and link libdss.so (always rebuilds)."""
+STAMPS_LIB_PATH = os.path.join(PKG_DIR, "libdss_stamps.so")
+
+
+def build(verbose=False, jobs=8, stamps=False):
+    """Compile every source and link libdss.so (always rebuilds).
+
+    stamps=True builds the measurement variant libdss_stamps.so instead: the
+    same sources with DSS_PHASE_STAMPS defined, whose split-row sampling
+    kernel writes phase clock stamps (read by ``bench.py --phase-stamps``)."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     tmp = tempfile.mkdtemp(prefix="dss_build_")
@@ -56,7 +63,8 @@ def build(verbose=False, jobs=8):
         for src in sources():
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             objs.append(obj)
-            cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+            cmd = [HIPCC, *COMMON_FLAGS, *(["-DDSS_PHASE_STAMPS"] if stamps else []), "-c", src,
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
@@ -65,13 +73,14 @@ def build(verbose=False, jobs=8):
                 _wait(procs.pop(0))
         while procs:
             _wait(procs.pop(0))
-        out_tmp = LIB_PATH + ".tmp"
+        target = STAMPS_LIB_PATH if stamps else LIB_PATH
+        out_tmp = target + ".tmp"
         _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp],
              verbose)
-        os.replace(out_tmp, LIB_PATH)
+        os.replace(out_tmp, target)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB_PATH
+    return target
 
 
 def _wait(item):
@@ -83,4 +92,4 @@ def _wait(item):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, stamps="--stamps" in sys.argv))

@@ -184,11 +184,26 @@ __device__ __forceinline__ gptr<T> as_global(T* p) {
   return (gptr<T>)p;
 }
 
+// One value through a vector load (global_load), never a scalar load: its
+// wait sits at the first use of the value, not at a work-group barrier.
+template <typename T>
+__device__ __forceinline__ T vload(const T* p) {
+  return __hip_atomic_load(as_global(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // 16-byte global load (HIP's float4 cannot be copied out of another
 // address space, the native vector type can)
 __device__ __forceinline__ float4 load_f4(gptr<const float4> p) {
   typedef float v4f __attribute__((ext_vector_type(4)));
   const v4f x = *(gptr<const v4f>)p;
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
+// The same load marked non-temporal (read once, not kept in the caches):
+// for the one read of a row, which no later pass of the kernel reads again.
+__device__ __forceinline__ float4 load_f4_nt(gptr<const float4> p) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f x = __builtin_nontemporal_load((gptr<const v4f>)p);
   return make_float4(x.x, x.y, x.z, x.w);
 }
 

@@ -132,6 +132,13 @@ constexpr int kSplitScalarKW = 4096;
 constexpr int kResidentSegKeys = 8192;  // boundary-bin keys one work-group may publish
 constexpr size_t kFixedRegionBytes = kCtlRegionBytes + (size_t)kResidentSlots * kResidentSlotBytes +
                                      (size_t)kResidentSlots * kResidentSegKeys * 4;
+// The split-row hand-off area after the fixed region: per output and slice a
+// header of kSplitHdrWords words, then a list of kSplitListEntries entries;
+// at most kSplitChunk outputs per launch (the arrival counters and
+// generation numbers of the control region).
+constexpr int kSplitHdrWords = 32;
+constexpr int kSplitListEntries = 4096;
+constexpr int kSplitChunk = 2048;
 
 // Resident-slice engine (plain, top-p and min-p sampling; top-p
 // renormalisation): W work-groups per output on one XCD keep the row in

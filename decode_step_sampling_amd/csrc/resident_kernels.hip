@@ -131,9 +131,12 @@ __device__ __forceinline__ bool row_barrier(gptr<uint32_t> ctr, uint32_t target,
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (threadIdx.x == 0) {
-    // (the clock starts before the arrival, so a limit of 0 gives up at once
-    // unless this arrival completes the barrier)
+  if (threadIdx.x == 0 && spin == 0ull) {
+    // a limit of zero (a test setting) gives up on arrival: the counter is
+    // marked broken without being counted
+    __hip_atomic_fetch_or(ctr, kBroken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.flag = 0;
+  } else if (threadIdx.x == 0) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     uint32_t c = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     int ok = 0;
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   float4 v[NV];
   const int vbase = wave * (kWave * NV) + lane;  // this thread's vector of load 0
   auto issue = [&](int j) __attribute__((always_inline)) {
-    v[j] = load_f4(src + min(vbase + j * kWave, nvec - 1));
+    v[j] = load_f4_nt(src + min(vbase + j * kWave, nvec - 1));
   };
 #pragma unroll
   for (int j = 0; j < kInFlight; ++j) issue(j);
@@ -1116,7 +1119,7 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(SoftmaxParams Q, Reside
   const int vbase = wave * (kWave * NV) + lane;
   float4 v[NV];
   auto issue = [&](int j) __attribute__((always_inline)) {
-    v[j] = load_f4(src + min(vbase + j * kWave, nvec - 1));
+    v[j] = load_f4_nt(src + min(vbase + j * kWave, nvec - 1));
   };
 #pragma unroll
   for (int j = 0; j < kInFlight; ++j) issue(j);

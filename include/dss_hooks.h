@@ -29,8 +29,9 @@ extern "C" {
 int32_t dss_set_timing_events(void* start, void* stop);
 
 /* Measurement aid (not part of the sampling path): one plain streaming read
- * of n floats at x (device, 16-byte aligned, n a multiple of 4), five
- * 16-byte loads in flight per thread, folding the largest float32 bit
+ * of n floats at x (device, 16-byte aligned, n a multiple of 4): a
+ * grid-stride loop of up to 2048 work-groups of 256 threads, one 16-byte
+ * load per thread per iteration, folding the largest float32 bit
  * pattern into *out_max (device uint32, caller-initialised; atomicMax).
  * Its time is the read rate this GPU reaches for that many bytes, the
  * reference beside the sampling kernels' HBM fraction.  Enqueued on
@@ -40,8 +41,10 @@ int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max, 
 /* Longest wait of a resident row barrier, in ticks of the GPU's 100 MHz
  * constant clock (default 5,000,000 = 50 ms).  UINT64_MAX restores the
  * default.  A small limit makes waits give up (the output is reported
- * invalid and its control block marked broken, see dss.h "Co-residency"):
- * for tests of that path only.  Always DSS_OK. */
+ * invalid and its control block marked broken, see dss.h "Co-residency");
+ * 0 makes every resident barrier give up on arrival, so every output of a
+ * resident launch comes out invalid and every slot it used is marked
+ * broken.  For tests of that path only.  Always DSS_OK. */
 int32_t dss_set_spin_limit(uint64_t ticks);
 
 #ifdef __cplusplus
