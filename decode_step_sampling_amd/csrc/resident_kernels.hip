@@ -47,6 +47,24 @@
 // reports it).
 #include "stream_device.h"
 
+// Phase clock stamps of the resident sampling kernel, as in split_kernels.hip
+// (compiled in only with -DDSS_PHASE_STAMPS; dss_debug_set_stamps_resident).
+#ifdef DSS_PHASE_STAMPS
+__device__ unsigned long long* g_dss_stamps_res;
+extern "C" __attribute__((visibility("default"))) int dss_debug_set_stamps_resident(void* p) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_dss_stamps_res), &p, sizeof(p)) == hipSuccess ? 0 : -4;
+}
+#define DSS_RSTAMP(n)                                                              \
+  do {                                                                             \
+    if (threadIdx.x == 0 && g_dss_stamps_res)                                      \
+      g_dss_stamps_res[blockIdx.x * 32 + (n)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define DSS_RSTAMP(n) \
+  do {                \
+  } while (0)
+#endif
+
 namespace dss {
 namespace {
 
@@ -462,6 +480,9 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
                                            int s, int W, uint64_t spin, uint32_t& passed,
                                            ResSmem& sm, uint32_t& tau, double& kept) {
   const int tid = threadIdx.x, lane = lane_id(), wave = r_uwave();
+#ifdef DSS_PHASE_STAMPS
+  const uint32_t passed0 = passed;
+#endif
   clear_lds_hist(sm);
   __syncthreads();
 #pragma unroll
@@ -478,7 +499,9 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
   publish_hist<kRB1>(sm, g1);
   __syncthreads();
   clear_lds_hist(sm);
+  DSS_RSTAMP((COUNT ? 4 : 10) + 2 * (int)passed - 2 * (int)passed0);
   if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+  DSS_RSTAMP((COUNT ? 5 : 11) + 2 * (int)passed - 2 * (int)passed0);
   ++passed;
   load_level<COUNT, kRB1>(g1, -1, sm);
   __syncthreads();
@@ -531,7 +554,9 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
       }
     }
     if (tid == 0) __hip_atomic_store(ctl + 8 + s, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    DSS_RSTAMP((COUNT ? 4 : 10) + 2 * (int)passed - 2 * (int)passed0);
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+    DSS_RSTAMP((COUNT ? 5 : 11) + 2 * (int)passed - 2 * (int)passed0);
     ++passed;
     if (wave == 0) {
       const uint32_t c = lane < W ? __hip_atomic_load(ctl + 8 + lane, __ATOMIC_RELAXED,
@@ -602,7 +627,9 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     publish_hist<kRB2>(sm, g2);
     __syncthreads();
     clear_lds_hist(sm);
+    DSS_RSTAMP((COUNT ? 4 : 10) + 2 * (int)passed - 2 * (int)passed0);
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+    DSS_RSTAMP((COUNT ? 5 : 11) + 2 * (int)passed - 2 * (int)passed0);
     ++passed;
     load_level<COUNT, kRB2>(g2, (int)e1, sm);
     __syncthreads();
@@ -631,7 +658,9 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     }
     __syncthreads();
     publish_hist<kRB3>(sm, g3);
+    DSS_RSTAMP((COUNT ? 4 : 10) + 2 * (int)passed - 2 * (int)passed0);
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+    DSS_RSTAMP((COUNT ? 5 : 11) + 2 * (int)passed - 2 * (int)passed0);
     ++passed;
     load_level<COUNT, kRB3>(g3, (int)e1, sm);
     __syncthreads();
@@ -660,6 +689,7 @@ template <int KIND, int OP, int NV>
 __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, RenormParams RP,
                                                           ResidentParams R) {
   __shared__ ResSmem sm;
+  DSS_RSTAMP(0);
   constexpr bool kTopP = OP == kOpTopP;  // top-p alone: level-1 masses while the slice lands
   constexpr bool kTopK = OP == kOpTopK || OP == kOpTopKTopP;
   // histogram words the row's last work-group clears (masses, then counts)
@@ -778,7 +808,9 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     __syncthreads();
     clear_lds_hist(sm);
   }
+  DSS_RSTAMP(1);
   if (!row_barrier(ctl, (uint32_t)W, R.spin, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+  DSS_RSTAMP(2);
   passed = 1u;
   const uint32_t gmax = __hip_atomic_load(ctl + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t xm = __hip_atomic_load(ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1015,8 +1047,10 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   // ---- sampling: kept mass per (slice, wave), one draw, the owner walks -----
   if (OP != kOpNone) {
     publish_chunks();
+    DSS_RSTAMP(16);
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, R.spin, sm))
       return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
+    DSS_RSTAMP(17);
     ++passed;
   }
   // every work-group, wave 0: the chunk holding u * (total kept mass);
@@ -1080,6 +1114,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       stream::write_sample(P, i, pos >= 0 ? s0 + pos : -1, pos >= 0 ? 1 : 0);
     }
   }
+  DSS_RSTAMP(18);
   row_leave(slot, passed, W, kHistWords, sm);
 }
 
