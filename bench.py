@@ -16,6 +16,12 @@ Two timed loops on the same stream:
     (dss_set_timing_events, hipExtLaunchKernel start/stop events on the
     kernel itself) -> the average kernel duration, the figure a kernel-trace
     profiler reports, from which roofline.achieved is computed.
+Beside the headline: a plain read of the same cold batch (the achievable
+read rate), the other workloads (warm: one resident buffer; cold: 16
+rotating buffers), the latency row at 4, 8 and 16 slices per row, and the
+oracle timed on the host's cores (a process pool forked before the first GPU
+call).  ``--phase-stamps`` instead prints the per-phase timeline of the
+headline kernel from the measurement build libdss_stamps.so.
 Prints one JSON line on stdout; details go to stderr.
 """
 
@@ -68,32 +74,144 @@ def measured_traffic():
     return float(val.group(1))
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The oracle as it stands (sort-based filter + exact CDF draw), one core.
+# ----------------------------------------------------------------------------
+# the oracle on the host's cores
+# ----------------------------------------------------------------------------
 
-    Cycles over the 64 headline rows (a new stream per pass) for about
-    ``budget_s`` seconds of CPU work and reports draws per second.
-    """
+_CPU = {}   # workload arrays, set before the pool forks (shared copy-on-write)
+
+
+def _oracle_rows(task):
+    """Worker: the oracle on `count` outputs of one workload, starting at
+    output `start` (cycling); returns the number of outputs done."""
     from oracle import philox as ph
     from oracle import reference as ref
-    probs, ks, ps, seeds = w["probs"], w["top_k"], w["top_p"], w["seeds"]
-    rows = probs.shape[0]
-    t0 = time.perf_counter()
-    done = 0
-    while done < rows or time.perf_counter() - t0 < budget_s:
-        r = done % rows
-        ref.sample_by_cdf(probs[r], "top_k_top_p",
-                          ph.draw_bits53(int(seeds[r]), done // rows, 0, 0), k=ks[r], p=ps[r])
-        done += 1
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sampled rows cycling over the 64 headline rows (sort + exact "
-                      f"prefix + CDF draw per row), {dt:.1f} s single-threaded Python/numpy"}
+    name, start, count, rep = task
+    d = _CPU[name]
+    n = d["n"]
+    for t in range(start, start + count):
+        i = t % n
+        if name == "renorm":       # top-p and top-k renormalisation of one row
+            ref.top_p_renorm(d["probs"][i], d["top_p"][i])
+            ref.top_k_renorm(d["probs"][i], d["top_k"][i])
+            continue
+        row = d["probs"][d["row_of"][i]]
+        a53 = ph.draw_bits53(int(d["seeds"][i]), rep, 0, 0)
+        op = d["op"][i]
+        ref.sample_by_cdf(row, op, a53, k=d["k"][i], p=d["p"][i], min_p=d["mp"][i])
+    return count
+
+
+def cpu_workloads(si, names):
+    """The host arrays of each workload the oracle is timed on (output-major)."""
+    out = {}
+    for name in names:
+        if name == "headline":
+            w = si.renorm()
+            n = w["probs"].shape[0]
+            out[name] = dict(n=n, probs=w["probs"], row_of=np.arange(n), seeds=w["seeds"],
+                             op=["top_k_top_p"] * n, k=w["top_k"], p=w["top_p"], mp=[None] * n,
+                             vocab=w["probs"].shape[1], what="fused top-k/top-p draw per row")
+        elif name == "renorm":
+            w = si.renorm()
+            n = w["probs"].shape[0]
+            out[name] = dict(n=n, probs=w["probs"], top_p=w["top_p"], top_k=w["top_k"],
+                             vocab=w["probs"].shape[1],
+                             what="top_p_renorm + top_k_renorm of one row")
+        elif name == "latency":
+            w = si.latency()
+            out[name] = dict(n=1, probs=w["probs"], row_of=[0], seeds=w["seeds"],
+                             op=["top_k_top_p"], k=[w["top_k"]], p=[w["top_p"]], mp=[None],
+                             vocab=w["probs"].shape[1], what="fused top-k/top-p draw (k=50, p=0.9)")
+        elif name == "hetero":
+            w = si.hetero()
+            idx = w["indices"]
+            ops = [("top_k_top_p", "min_p", "none")[o] for o in w["op_of_output"]]
+            out[name] = dict(n=len(idx), probs=w["probs"], row_of=idx, seeds=w["seeds"], op=ops,
+                             k=w["top_k"][idx], p=w["top_p"][idx], mp=w["min_p"][idx],
+                             vocab=w["probs"].shape[1],
+                             what="one output of the mixed top-k/top-p, min-p, plain batch")
+        elif name == "stress":
+            w = si.stress()
+            n = w["probs"].shape[0]
+            out[name] = dict(n=n, probs=w["probs"], row_of=np.arange(n), seeds=w["seeds"],
+                             op=["top_k_top_p"] * n, k=[w["top_k"]] * n, p=[w["top_p"]] * n,
+                             mp=[None] * n, vocab=w["probs"].shape[1],
+                             what="fused top-k/top-p draw (k=1000, p=0.95)")
+    return out
+
+
+def cpu_pool():
+    """Worker processes for the oracle: one per core of the machine's CPU share
+    (at most 16), forked now, before any GPU call."""
+    import multiprocessing as mp
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    n = max(1, min(16, avail))
+    return mp.get_context("fork").Pool(n, initializer=_one_thread), n
+
+
+def _one_thread():
+    """Each oracle process runs single-threaded (no hidden thread pools)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pool, ncores, names, per_core=(("headline", 48), ("renorm", 8),
+                                                ("latency", 32), ("hetero", 24),
+                                                ("stress", 16))):
+    """The oracle as it stands (sort-based filter + exact CDF draw, or the
+    renormalisation), timed on the host: for every workload, five runs on all
+    `ncores` worker processes (each doing `count` outputs) and five on one,
+    the median of each; outputs per second and the equivalent GB/s of one
+    read of each output's row."""
+    import statistics
+    res = {}
+    pool.map(_oracle_rows, [("latency", 0, 1, 0)] * ncores, chunksize=1)   # imports in every worker
+    for name, count in per_core:
+        if name not in names:
+            continue
+        d = _CPU[name]
+        row_bytes = 4 * d["vocab"] * (2 if name == "renorm" else 1)
+
+        def timed(ntasks, rep):
+            tasks = [(name, (rep * 7919 + j * count) % d["n"], count, rep) for j in range(ntasks)]
+            t0 = time.perf_counter()
+            done = sum(pool.map(_oracle_rows, tasks, chunksize=1))
+            return done / (time.perf_counter() - t0)
+
+        multi = statistics.median(timed(ncores, r) for r in range(5))
+        single = statistics.median(timed(1, r) for r in range(5))
+        res[name] = {"all_cores": {"value": multi, "GBps": multi * row_bytes / 1e9},
+                     "one_core": {"value": single, "GBps": single * row_bytes / 1e9},
+                     "unit": "outputs/s", "sample": f"{count} outputs per process per run, "
+                     f"median of 5 runs ({d['what']})"}
+    return res
+
+
+QUICK = [False]   # --quick: a few calls per workload (for counter runs under a profiler)
 
 
 def kernel_times(lib, fn, reps, warm=2):
     """Per-call kernel time in us of fn() (dispatch-event hook), reps calls."""
     import torch
+    if QUICK[0]:
+        reps, warm = min(reps, 4), min(warm, 1)
     for _ in range(warm):
         fn()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -183,6 +301,24 @@ def extra_configs(dss, si, lib, dev):
         kernel_times(lib, lambda: dss.top_p_renorm_probs(P, p), 10), 2 * B * V * 4)
     out["renorm B=64 V=151936 top_k_renorm_probs"] = entry(
         kernel_times(lib, lambda: dss.top_k_renorm_probs(P, k), 50), 2 * B * V * 4)
+    # the same two ops cold: 16 rotating input buffers, 16 output buffers
+    Pc = [P.clone() for _ in range(N_BUFFERS)]
+    Oc = [torch.empty_like(P) for _ in range(N_BUFFERS)]
+    cnt = [0]
+
+    def rot(fn):
+        def step():
+            j = cnt[0] % N_BUFFERS
+            cnt[0] += 1
+            fn(Pc[j], Oc[j])
+        return step
+    out["renorm B=64 V=151936 top_p_renorm_probs, cold (16 buffers)"] = entry(
+        kernel_times(lib, rot(lambda x, o: dss.top_p_renorm_probs(x, p, out=o)), 50, 4),
+        2 * B * V * 4)
+    out["renorm B=64 V=151936 top_k_renorm_probs, cold (16 buffers)"] = entry(
+        kernel_times(lib, rot(lambda x, o: dss.top_k_renorm_probs(x, k, out=o)), 50, 4),
+        2 * B * V * 4)
+    del Pc, Oc
     L = g(si.logits_rows(np.random.default_rng(1), B, V))
     out["logits B=64 V=151936 top_k_mask_logits"] = entry(
         kernel_times(lib, lambda: dss.top_k_mask_logits(L, k), 50), 2 * B * V * 4)
@@ -223,7 +359,22 @@ def extra_configs(dss, si, lib, dev):
                                                                        offset=0), 1000, 20)
     out["latency B=1 V=151936 top_k_top_p (k=50, p=0.9), 1000 calls"] = entry(
         t, 151936 * 4, p50_us=float(np.percentile(t, 50)), p95_us=float(np.percentile(t, 95)),
-        p99_us=float(np.percentile(t, 99)))
+        p99_us=float(np.percentile(t, 99)), slices=16)
+    # the same row at other slice counts (dss_set_split_slices; the engine's
+    # own choice is 16, its largest; 32 slices of one row do not exist)
+    sweep = {}
+    for W in (4, 8, 16):
+        lib.dss_set_split_slices(W)
+        try:
+            t = kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_probs(
+                P, 50, 0.9, seed=3, offset=0), 1000, 20)
+        finally:
+            lib.dss_set_split_slices(0)
+        sweep[str(W)] = {"p50_us": float(np.percentile(t, 50)), "p95_us": float(np.percentile(t, 95)),
+                         "p99_us": float(np.percentile(t, 99)), "mean_us": float(t.mean())}
+    best = min(sweep, key=lambda x: sweep[x]["p50_us"])
+    out["latency B=1 V=151936 slices per row sweep (p50/p95/p99 over 1000 calls)"] = {
+        "slices": sweep, "best": int(best), "32": "not available (at most 16 slices per row)"}
     w = si.hetero()
     P = g(w["probs"])
     B, V = P.shape
@@ -242,6 +393,31 @@ def extra_configs(dss, si, lib, dev):
     out["hetero B=256 V=128256, 512 outputs, three calls per step"] = {
         "kernel_us": step, "algorithmic_bytes": 512 * V * 4,
         "hbm_frac": 512 * V * 4 / (step * 1e-6) / (HBM_PEAK_GBS * 1e9), "calls": parts}
+    # cold: every call of a step on the next of 16 rotating copies of the batch
+    Pc = [P.clone() for _ in range(N_BUFFERS)]
+    step, parts = 0.0, {}
+    for o, name in enumerate(("top_k_top_p", "min_p", "plain")):
+        sel = np.nonzero(op == o)[0]
+        I, S = g(idx[sel]), g(seeds[sel].view(np.int64))
+        K, Pp, M = g(w["top_k"][idx[sel]]), g(w["top_p"][idx[sel]]), g(w["min_p"][idx[sel]])
+        cnt = [o * 5]
+
+        def fn(o=o, I=I, S=S, K=K, Pp=Pp, M=M, cnt=cnt):
+            X = Pc[cnt[0] % N_BUFFERS]
+            cnt[0] += 1
+            if o == 0:
+                dss.top_k_top_p_sampling_from_probs(X, K, Pp, indices=I, seed=S, offset=0)
+            elif o == 1:
+                dss.min_p_sampling_from_probs(X, M, indices=I, seed=S, offset=0)
+            else:
+                dss.sampling_from_probs(X, indices=I, seed=S, offset=0)
+        t = kernel_times(lib, fn, 16, 1)
+        parts[name] = {"outputs": int(len(sel)), "kernel_us": float(t.mean())}
+        step += float(t.mean())
+    out["hetero B=256 V=128256, 512 outputs, three calls per step, cold (16 buffers)"] = {
+        "kernel_us": step, "algorithmic_bytes": 512 * V * 4,
+        "hbm_frac": 512 * V * 4 / (step * 1e-6) / (HBM_PEAK_GBS * 1e9), "calls": parts}
+    del Pc
     w = si.stress()
     P = g(w["probs"])
     B, V = P.shape
@@ -258,6 +434,16 @@ def extra_configs(dss, si, lib, dev):
                       "p99": float(np.percentile(x, 99)), "max": int(x.max())}
     out["stress B=512 V=256000 top_k_top_p (k=1000, p=0.95)"] = entry(t, B * V * 4,
                                                                       rounds=hist)
+    Pc = [P.clone() for _ in range(N_BUFFERS)]
+    cnt = [0]
+
+    def cold_stress():
+        X = Pc[cnt[0] % N_BUFFERS]
+        cnt[0] += 1
+        dss.top_k_top_p_sampling_from_probs(X, 1000, 0.95, seed=seeds, offset=0)
+    out["stress B=512 V=256000 top_k_top_p (k=1000, p=0.95), cold (16 buffers)"] = entry(
+        kernel_times(lib, cold_stress, 16, 1), B * V * 4)
+    del Pc
     # the pages' tail argument: rounds of the loop run from low = 0 with the
     # second pivot (dual) and without it (single), same rows, same streams
     cmp = {}
@@ -275,6 +461,83 @@ def extra_configs(dss, si, lib, dev):
     return out
 
 
+PHASES = [(1, "slice loads issued, histogram cleared"), (2, "provisional bound from 30% sample"),
+          (3, "slice landed (thread 0)"), (4, "certified slice bound"),
+          (6, "candidates extracted to LDS"), (7, "list + header stored, drained"),
+          (8, "arrival counted"), (9, "last arriver: headers read"),
+          (10, "last arriver: lists placed"), (11, "tau_k histogram"), (12, "tau_k bin found"),
+          (13, "top-k set partitioned"), (14, "tau_k in the boundary bin"),
+          (15, "top-p start certified"), (16, "dual-pivot loop done")]
+
+
+def phase_stamps(si, steps):
+    """Per-phase timeline of the headline kernel: the measurement build
+    libdss_stamps.so (DSS_PHASE_STAMPS: thread 0 of every work-group stores
+    the 100 MHz constant clock at each phase boundary) on the cold rotating
+    buffers; times from the kernel's first work-group start, averaged over
+    `steps` launches.  The stamps themselves cost about 0.1 us each."""
+    import ctypes
+    import torch
+    from decode_step_sampling_amd import _lib, build
+    path = build.STAMPS_LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m decode_step_sampling_amd.build --stamps`")
+    lib = ctypes.CDLL(path)
+    for name, (a, r) in _lib.SIGNATURES.items():
+        f = getattr(lib, name)
+        f.argtypes, f.restype = a, r
+    lib.dss_debug_set_stamps.argtypes = [ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    w = si.renorm()
+    B, V = w["probs"].shape
+    base = torch.from_numpy(w["probs"]).to(dev)
+    bufs = [base.clone() for _ in range(N_BUFFERS)]
+    k = torch.from_numpy(w["top_k"]).to(dev)
+    p = torch.from_numpy(w["top_p"]).to(dev)
+    seeds = torch.from_numpy(w["seeds"].view(np.int64)).to(dev)
+    samples = torch.empty(B, dtype=torch.int32, device=dev)
+    wsb = lib.dss_workspace_size(4, B, V, B, 0)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    st = torch.zeros(4096 * 32, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call(i):
+        r = lib.dss_top_k_top_p_sampling_from_probs(
+            bufs[i % N_BUFFERS].data_ptr(), B, V, None, B, seeds.data_ptr(), 0, None, i,
+            k.data_ptr(), 0, p.data_ptr(), 0.0, samples.data_ptr(), None, None, 0, ws.data_ptr(),
+            wsb, stream)
+        if r != 0:
+            raise RuntimeError(_lib.strerror(r))
+    for i in range(20):
+        call(i)
+    torch.cuda.synchronize()
+    rel = []
+    for rep in range(steps):
+        st.zero_()
+        lib.dss_debug_set_stamps(ctypes.c_void_p(st.data_ptr()))
+        call(100 + rep)
+        torch.cuda.synchronize()
+        lib.dss_debug_set_stamps(None)
+        a = st.cpu().numpy().reshape(-1, 32)[:256].astype(np.float64)
+        t0 = a[:, 0][a[:, 0] > 0].min()
+        rel.append(np.where(a > 0, (a - t0) * 0.01, np.nan))
+    R = np.stack(rel)
+    print("| phase (thread 0 of each work-group, after the step) | all work-groups, mean us "
+          "| last arriver (64), mean us |")
+    print("|---|---|---|")
+    last = ~np.isnan(R[:, :, 9])
+    for j, name in PHASES:
+        x = R[:, :, j]
+        lx = np.where(last, x, np.nan)
+        print(f"| {j:2d} {name} | {np.nanmean(x):.2f} | "
+              f"{np.nanmean(lx):.2f} |" if not np.all(np.isnan(lx)) else
+              f"| {j:2d} {name} | {np.nanmean(x):.2f} | - |")
+    ends = np.nanmax(R[:, :, 16], axis=1)
+    print(f"\nlast loop end (kernel end less the sample store), mean over {steps} launches: "
+          f"{ends.mean():.2f} us")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +548,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (other_configs)")
+    ap.add_argument("--quick", action="store_true",
+                    help="four timed calls per other workload (for counter runs under a profiler)")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="print the headline kernel's phase timeline (libdss_stamps.so) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -292,9 +559,20 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    QUICK[0] = args.quick
+    import synthetic_inputs as si
+    if args.phase_stamps:
+        phase_stamps(si, args.steps)
+        return
+    # the oracle's worker processes are forked before anything touches the GPU
+    pool = None
+    cpu_names = ("headline", "renorm", "latency", "hetero", "stress")
+    if not args.no_cpu:
+        _CPU.update(cpu_workloads(si, cpu_names))
+        pool, ncores = cpu_pool()
+
     import torch
     import decode_step_sampling_amd as dss
-    import synthetic_inputs as si
 
     flags = {"auto": 0, "streaming": dss.DSS_FLAG_STREAMING,
              "from_zero": dss.DSS_FLAG_FROM_ZERO}[args.engine]
@@ -372,6 +650,7 @@ def main():
         f"kernel {per_launch_ms * 1e3:.2f} us, per-step {ms_per_step * 1e3:.2f} us, "
         f"wall {wall * 1e6 / K:.1f} us/step; rounds histogram {dict(sorted(hist.items()))}")
 
+    traffic = measured_traffic() if args.engine == "auto" and not args.warm_cache else None
     out = {
         "metric": METRIC,
         "value": B / (ms_per_step * 1e-3),
@@ -393,8 +672,10 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if args.engine == "auto" and not args.warm_cache
-                     else None,
+                     "traffic": traffic,
+                     "traffic_source": (f"{TRAFFIC_FILE} (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                        f"kernel source hash {kernel_source_hash()})")
+                     if traffic is not None else None,
                      "kernel_us": per_launch_ms * 1e3,
                      "algorithmic_bytes": bytes_per_launch},
         "rounds_histogram": {str(kk): vv for kk, vv in sorted(hist.items())},
@@ -404,8 +685,18 @@ def main():
         del bufs
         torch.cuda.empty_cache()
         out["other_configs"] = extra_configs(dss, si, lib, dev)
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w)
+    if pool is not None:
+        res = cpu_baseline(pool, ncores, cpu_names)
+        pool.close()
+        pool.join()
+        h = res["headline"]
+        out["cpu_baseline"] = {
+            "value": h["all_cores"]["value"], "unit": "rows/s", "cores": ncores, "kind": "oracle",
+            "sample": f"{h['sample']}; the sort-based Python/numpy oracle in {ncores} worker "
+                      "processes (one per core of the box's CPU share, at most 16)",
+            "one_core": h["one_core"]["value"], "GBps": h["all_cores"]["GBps"],
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "configs": {n: res[n] for n in res if n != "headline"}}
     print(json.dumps(out), flush=True)
 
 

@@ -16,6 +16,7 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<void*> g_ev_start{nullptr}, g_ev_stop{nullptr};  // dss_set_timing_events
 std::atomic<uint64_t> g_spin_ticks{dss::kDefaultSpinTicks};  // dss_set_spin_limit
+std::atomic<int> g_split_slices{0};                            // dss_set_split_slices
 
 dss::LaunchEvents timing_events() {
   return dss::LaunchEvents{static_cast<hipEvent_t>(g_ev_start.load(std::memory_order_relaxed)),
@@ -159,6 +160,7 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
 
 namespace dss {
 uint64_t spin_limit_ticks() { return g_spin_ticks.load(std::memory_order_relaxed); }
+int forced_split_slices() { return g_split_slices.load(std::memory_order_relaxed); }
 }  // namespace dss
 
 // Scratch of the allocation-free entry point: one array per GPU the library
@@ -464,6 +466,13 @@ DSS_EXPORT int32_t dss_set_timing_events(void* start, void* stop) {
 DSS_EXPORT int32_t dss_set_spin_limit(uint64_t ticks) {
   g_spin_ticks.store(ticks == UINT64_MAX ? dss::kDefaultSpinTicks : ticks,
                      std::memory_order_relaxed);
+  return DSS_OK;
+}
+
+DSS_EXPORT int32_t dss_set_split_slices(int32_t slices) {
+  if (slices != 0 && (slices < 1 || slices > 16 || (slices & (slices - 1)) != 0))
+    return DSS_ERR_INVALID_ARG;
+  g_split_slices.store(slices, std::memory_order_relaxed);
   return DSS_OK;
 }
 

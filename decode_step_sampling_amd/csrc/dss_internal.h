@@ -74,6 +74,9 @@ struct LaunchEvents {
 // clock (dss_set_spin_limit; 50 ms unless changed).
 uint64_t spin_limit_ticks();
 constexpr uint64_t kDefaultSpinTicks = 5000000ull;
+// Slices per output the split engine must use (dss_set_split_slices; 0: its
+// own choice).
+int forced_split_slices();
 
 // Launch kernel on stream s, attaching the dispatch events of ev that apply
 // (start if first, stop if last).

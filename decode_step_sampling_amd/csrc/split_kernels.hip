@@ -917,9 +917,10 @@ SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flag
   const int wt = (256 + num_outputs - 1) / num_outputs;
   if (wmin > kMaxSlices) return plan;
   // W: a power of two, at least wmin, about 256 work-groups in all, at most
-  // kMaxSlices, and no empty slice
+  // kMaxSlices, and no empty slice (or the measurement hook's choice)
   int W = 1;
   while (W < wmin || (W * 2 <= kMaxSlices && W * 2 <= wt)) W *= 2;
+  if (forced_split_slices() > 0) W = max(forced_split_slices(), wmin);
   int L = 0;
   for (;; W /= 2) {
     L = ((vocab + 4 * W - 1) / (4 * W)) * 4;

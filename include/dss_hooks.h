@@ -47,6 +47,14 @@ int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max, 
  * broken.  For tests of that path only.  Always DSS_OK. */
 int32_t dss_set_spin_limit(uint64_t ticks);
 
+/* Slices per output of the split-row engine (a power of two, 1..16), for
+ * measuring other choices than its own (about 256 work-groups in all); 0
+ * restores its own choice.  A value the vocabulary needs more slices than
+ * is raised to that minimum; the engine still halves it while a slice would
+ * be empty.  Also applies to dss_workspace_size, so query the workspace
+ * after setting it.  DSS_ERR_INVALID_ARG for other values. */
+int32_t dss_set_split_slices(int32_t slices);
+
 #ifdef __cplusplus
 }
 #endif

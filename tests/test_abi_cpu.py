@@ -35,7 +35,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -146,6 +146,16 @@ def test_workspace_size_and_strings():
     assert lib.dss_workspace_status(None, 0, flags, None) == 0
     assert lib.dss_workspace_status(ctypes.c_void_p(16), 4096, None, None) == 0
     assert lib.dss_set_spin_limit(2**64 - 1) == _lib.DSS_OK   # restores the default
+    # forced split slices: powers of two up to 16, or 0; the workspace follows
+    for bad in (3, 32, -1):
+        assert lib.dss_set_split_slices(bad) == _lib.DSS_ERR_INVALID_ARG
+    auto = lib.dss_workspace_size(4, 1, 151936, 1, 0)
+    assert lib.dss_set_split_slices(4) == _lib.DSS_OK
+    try:
+        assert lib.dss_workspace_size(4, 1, 151936, 1, 0) < auto    # W=16 by default
+    finally:
+        assert lib.dss_set_split_slices(0) == _lib.DSS_OK
+    assert lib.dss_workspace_size(4, 1, 151936, 1, 0) == auto
 
 
 def test_noalloc_entry_point_validation():
