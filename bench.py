@@ -42,6 +42,7 @@ METRIC = "sampled rows/s + achieved HBM GB/s, fused top-k/top-p, B=64 V=151936 f
 HBM_PEAK_GBS = 8000.0
 N_BUFFERS = 16
 KERNEL_SOURCES = ["decode_step_sampling_amd/csrc/split_kernels.hip",
+                  "decode_step_sampling_amd/csrc/split_device.h",
                   "decode_step_sampling_amd/csrc/stream_device.h",
                   "decode_step_sampling_amd/csrc/dss_device.h",
                   "decode_step_sampling_amd/csrc/dss_internal.h"]
