@@ -639,6 +639,44 @@ def dual_pivot_law(row, op, k=None, p=None, min_p=None):
     return solve(np.float32(0.0), np.float32(row.max()))
 
 
+def dual_pivot_rounds_law(row, op, k=None, p=None, min_p=None):
+    """Exact law of the number of rounds ``dual_pivot_sample`` takes.
+
+    The same enumeration as ``dual_pivot_law`` ([Blog] "双枢轴拒绝采样":
+    draw above low, accept at f(pivot1) = 1, else move (low, high) by the
+    three cases), but every accepted path adds its probability to the count
+    of rounds it used.  Tiny vocabularies only.  Returns {rounds: Fraction}.
+    """
+    row = np.asarray(row, dtype=np.float32)
+    f = Predicate(row, op, k=k, p=p, min_p=min_p)
+    units = f.units
+    memo = {}
+
+    def solve(low, high):
+        key = (float(low), float(high))
+        if key in memo:
+            return memo[key]
+        cand = [i for i in range(row.size) if row[i] > low]
+        s = sum(units[i] for i in cand)
+        law = {}
+        for i in cand:
+            w = Fraction(units[i], s)
+            if w == 0:
+                continue
+            pivot1 = row[i]
+            if f(pivot1):
+                law[1] = law.get(1, Fraction(0)) + w
+                continue
+            pivot2 = pivot2_of(pivot1, high)
+            sub = solve(pivot1, pivot2) if f(pivot2) else solve(pivot2, high)
+            for r, q in sub.items():
+                law[r + 1] = law.get(r + 1, Fraction(0)) + w * q
+        memo[key] = law
+        return law
+
+    return solve(np.float32(0.0), np.float32(row.max()))
+
+
 # ----------------------------------------------------------------------------
 # batch helpers mirroring the library's calling convention
 # ----------------------------------------------------------------------------

@@ -10,6 +10,9 @@ Inputs come from synthetic_inputs (seeded); every RNG seed here is fixed, so
 the statistical tests are deterministic.
 """
 
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -391,3 +394,46 @@ def test_graph_capture_with_device_offsets():
                                                     offset=u64(np.full(8, step, np.uint64)))
         torch.cuda.synchronize()
         assert torch.equal(out, eager), step
+
+
+# ----------------------------------------------------------------------------
+# round counts against the exact law of the blog's procedure (tiny rows)
+# ----------------------------------------------------------------------------
+
+def _rounds_cases():
+    row = np.asarray(json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                                 "expl_top2_example.json")))["probs"],
+                     dtype=np.float32)
+    rng = np.random.default_rng(31)
+    rnd = rng.dirichlet(np.full(7, 0.6)).astype(np.float32)
+    return [("A..E top_k k=2", row, "top_k", {"k": 2, "p": np.float32(1.0), "mp": np.float32(0)}),
+            ("A..E top_k k=3", row, "top_k", {"k": 3, "p": np.float32(1.0), "mp": np.float32(0)}),
+            ("V=7 top_k_top_p k=4 p=0.7", rnd, "top_k_top_p",
+             {"k": 4, "p": np.float32(0.7), "mp": np.float32(0)}),
+            ("V=7 top_p p=0.8", rnd, "top_p", {"k": 7, "p": np.float32(0.8), "mp": np.float32(0)})]
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_rounds_histogram_matches_exact_law(case):
+    """20000 draws from low = 0 (DSS_FLAG_FROM_ZERO) on one tiny row: the
+    histogram of round counts against the exact law of the blog's dual-pivot
+    procedure (oracle enumeration), chi-square at alpha = 1e-3, and the mean
+    within 4 standard errors of the exact expectation."""
+    name, row, op, prm = _rounds_cases()[case]
+    n = 20000
+    P = gpu(row[None, :])
+    idx = gpu(np.zeros(n, dtype=np.int32))
+    s, v, r = OPS[op](P, prm, indices=idx, seed=99, offset=case, return_valid=True,
+                      return_rounds=True, flags=dss.DSS_FLAG_FROM_ZERO)
+    r, v = host(r), host(v)
+    assert (v == 1).all(), name
+    law = ref.dual_pivot_rounds_law(row, op, **_oracle_kw(op, prm))
+    top = max(max(law), int(r.max()))
+    counts = np.bincount(r, minlength=top + 1)[1:]
+    target = np.array([float(law.get(q, 0)) for q in range(1, top + 1)])
+    assert counts[target == 0].sum() == 0, (name, counts, target)
+    pval, _, _ = pooled_chi_square(counts, target)
+    assert pval > 1e-3, (name, counts, target)
+    mean = sum(q * float(w) for q, w in law.items())
+    var = sum(q * q * float(w) for q, w in law.items()) - mean * mean
+    assert abs(r.mean() - mean) <= 4 * np.sqrt(max(var, 1e-12) / n) + 1e-9, (name, r.mean(), mean)

@@ -699,3 +699,59 @@ def test_dual_pivot_trace_second_case():
     assert trace[1] == (np.float32(0.07), _mid(0.07, 0.35))
     assert trace[2] == (_mid(0.12, _mid(0.07, 0.35)), _mid(0.07, 0.35))
     assert abs(float(trace[1][1]) - 0.21) < 1e-7 and abs(float(trace[2][0]) - 0.165) < 1e-7
+
+
+# ----------------------------------------------------------------------------
+# the law of the round count, worked by hand on the A..E row of the explainer
+# ("一个简化的 top-k 例子") with the update of the blog ("双枢轴拒绝采样")
+# ----------------------------------------------------------------------------
+
+def test_rounds_law_top2_by_hand():
+    """k = 2: A or B is accepted at once (mass .63).  C, D or E is rejected,
+    and its pivot2 (.265, .235 or .21) still has two values above it, so low
+    moves to pivot2 with only A and B left: exactly two rounds (mass .37)."""
+    row = f32(golden("expl_top2_example.json")["probs"])
+    u = ref.exact_units(row)
+    z = sum(u)
+    law = ref.dual_pivot_rounds_law(row, "top_k", k=2)
+    assert law == {1: Fraction(u[0] + u[1], z), 2: Fraction(u[2] + u[3] + u[4], z)}
+    assert abs(float(law[2]) - 0.37) < 1e-7
+
+
+def test_rounds_law_top3_by_hand():
+    """k = 3: A, B, C accepted at once (.81).  D: pivot2 = .235 passes, so
+    (low, high) = (.12, .235) and A, B or C is taken next: two rounds.  E:
+    pivot2 = .21 passes, (low, high) = (.07, .21); next A, B, C (mass .81 of
+    .93) end at two rounds, D (.12 of .93) is rejected again, pivot2 = .165
+    fails, low = .165, and the third round accepts."""
+    row = f32(golden("expl_top2_example.json")["probs"])
+    u = ref.exact_units(row)
+    z = sum(u)
+    above07 = u[0] + u[1] + u[2] + u[3]
+    law = ref.dual_pivot_rounds_law(row, "top_k", k=3)
+    p_e = Fraction(u[4], z)
+    assert law == {1: Fraction(u[0] + u[1] + u[2], z),
+                   2: Fraction(u[3], z) + p_e * Fraction(u[0] + u[1] + u[2], above07),
+                   3: p_e * Fraction(u[3], above07)}
+    assert abs(float(law[3]) - 0.07 * 0.12 / 0.93) < 1e-7
+
+
+def test_rounds_law_sums_to_one_and_matches_expectation():
+    """On random tiny rows the round law is a probability law whose mean is
+    the expected round count of the exact output-law enumeration."""
+    rng = np.random.default_rng(17)
+    checked = 0
+    for row in _tiny_rows(5, 60):
+        if row.size > 7:
+            continue
+        k = int(rng.integers(1, row.size + 1))
+        p = float(np.float32(rng.uniform(0.2, 0.95)))
+        for op in ("top_k", "top_p", "top_k_top_p"):
+            law = ref.dual_pivot_rounds_law(row, op, k=k, p=p)
+            _, mean = ref.dual_pivot_law(row, op, k=k, p=p)
+            if not law:
+                continue
+            assert sum(law.values()) == 1
+            assert sum(r * q for r, q in law.items()) == mean
+            checked += 1
+    assert checked > 50
