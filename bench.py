@@ -334,9 +334,19 @@ def extra_configs(dss, si, lib, dev):
     Lg = g(si.logits_rows(np.random.default_rng(2), B, V, 2.0))
     out["logits B=64 V=151936 softmax (T=0.8)"] = entry(
         kernel_times(lib, lambda: dss.softmax(Lg, 0.8), 50), 2 * B * V * 4)
-    out["logits B=64 V=151936 top_k_top_p_sampling_from_logits (T=0.8; softmax + sampling kernels)"] = entry(
+    out["logits B=64 V=151936 top_k_top_p_sampling_from_logits (T=0.8; softmax fused into the sampling kernel)"] = entry(
         kernel_times(lib, lambda: dss.top_k_top_p_sampling_from_logits(Lg, k, p, 0.8, seed=1, offset=0), 50),
         B * V * 4)
+    Lc = [Lg.clone() for _ in range(N_BUFFERS)]
+    cnt = [0]
+
+    def logits_cold():
+        x = Lc[cnt[0] % N_BUFFERS]
+        cnt[0] += 1
+        dss.top_k_top_p_sampling_from_logits(x, k, p, 0.8, seed=1, offset=0)
+    out["logits B=64 V=151936 top_k_top_p_sampling_from_logits (T=0.8; fused), cold (16 buffers)"] = entry(
+        kernel_times(lib, logits_cold, 50, 4), B * V * 4)
+    del Lc
     for kk in (50, 1024):
         out[f"logits B=64 V=151936 top_k selection (k={kk}; values + indices)"] = entry(
             kernel_times(lib, lambda: dss.top_k(Lg, kk), 50), B * V * 4 + B * kk * 8)

@@ -46,7 +46,10 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
                   float min_p, int32_t* samples, uint8_t* valid, int32_t* rounds, uint32_t flags,
                   void* workspace, size_t workspace_bytes, void* stream,
                   const dss::LaunchEvents& ev, bool check_only = false,
-                  bool repair_slots = false) {
+                  bool repair_slots = false, const float* temp_arr = nullptr,
+                  float temp = 1.0f, float* prob_buf = nullptr) {
+  // prob_buf set: `probs` holds logits, sampled through softmax(z / T) on the
+  // split engine (the caller has checked that its plan applies)
   if (flags & ~DSS_FLAGS_ALL) return DSS_ERR_INVALID_ARG;
   // the joint order only exists for the combined filter; the engines know it
   // as an op of its own (the public op id still sizes the workspace)
@@ -91,7 +94,15 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   p.rounds = rounds;
   p.vec_ok = vec_ok;
   p.single_pivot = (flags & DSS_FLAG_SINGLE_PIVOT) ? 1 : 0;
+  p.temp_arr = temp_arr;
+  p.temp = temp;
+  p.prob_buf = prob_buf;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (prob_buf) {
+    if (plan.W == 0) return DSS_ERR_INVALID_ARG;
+    return dss::launch_split_logits(eop, p, plan, workspace, st, ev) == hipSuccess ? DSS_OK
+                                                                                 : DSS_ERR_HIP;
+  }
   if (repair_slots && plan.W == 0 && rplan.W > 0 &&
       dss::launch_resident_repair(workspace, st) != hipSuccess)
     return DSS_ERR_HIP;
@@ -103,6 +114,18 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Whether top-k-then-top-p sampling from logits runs fused on the split
+// engine (the plan sample_common would take for the same shape, sequential
+// order only); otherwise probabilities are written first and sampled.
+bool logits_fused(int32_t rows, int32_t vocab, int32_t num_outputs, const int32_t* top_k_arr,
+                  int32_t top_k, uint32_t flags, int vec_ok) {
+  if (flags & DSS_FLAG_ORDER_JOINT) return false;
+  const dss::SplitPlan plan =
+      dss::plan_split(dss::kOpTopKTopP, rows, vocab, num_outputs, flags, vec_ok);
+  if (plan.W == 0) return false;
+  return top_k_arr || (top_k <= dss::kSplitKCapHost && (int64_t)top_k * plan.W <= dss::kSplitScalarKW);
+}
 
 // Workspace of the logits path: the engines' area (the softmax kernel's and
 // the sampling call's share one), then the probabilities.  The probabilities
@@ -339,8 +362,17 @@ DSS_EXPORT int dss_top_k_top_p_sampling_from_logits(
                                          flags);
   if (workspace_bytes < need || !workspace) return DSS_ERR_WORKSPACE;
   float* probs = reinterpret_cast<float*>(static_cast<char*>(workspace) + eng);
-  // every check of the sampling call before anything is enqueued
   const dss::LaunchEvents ev = timing_events();
+  const int vec_ok = (vocab % 4 == 0) && aligned16(logits);
+  if (logits_fused(rows, vocab, num_outputs, top_k_arr, top_k, flags, vec_ok)) {
+    // one kernel: the softmax rides inside the split engine's pass (the
+    // probabilities area only takes rows that fall back)
+    return sample_common(dss::kOpTopKTopP, logits, rows, vocab, indices, num_outputs, seed_arr,
+                         seed, offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p, nullptr,
+                         0.0f, samples, valid, rounds, flags, workspace, eng, stream, ev, false,
+                         false, temperature_arr, temperature, probs);
+  }
+  // every check of the sampling call before anything is enqueued
   const int chk = sample_common(dss::kOpTopKTopP, probs, rows, vocab, indices, num_outputs, seed_arr,
                                 seed, offset_arr, offset, top_k_arr, top_k, top_p_arr, top_p,
                                 nullptr, 0.0f, samples, valid, rounds, flags, workspace, eng,
@@ -351,7 +383,6 @@ DSS_EXPORT int dss_top_k_top_p_sampling_from_logits(
   // probabilities into the workspace (invalid rows come out NaN-filled, which
   // the sampling call reports as invalid outputs), then the sampling call;
   // the timing events span both kernels
-  const int vec_ok = (vocab % 4 == 0) && aligned16(logits);
   const dss::SoftmaxParams q{logits, probs, rows, vocab, temperature_arr, temperature, nullptr,
                              vec_ok};
   const hipError_t e = dss::launch_softmax(q, dss::plan_softmax(rows, vocab, flags, vec_ok),
@@ -445,9 +476,11 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
     return dss::plan_softmax(rows, vocab, flags, vec).workspace;
   }
   if (op == DSS_OP_TOP_K_TOP_P_FROM_LOGITS) {
+    // the engines' area, then probabilities: one row per input row (written
+    // before sampling), or per output (the fused path's fallback rows)
     if (rows <= 0 || num_outputs <= 0) return 0;
-    return logits_engine_bytes(rows, vocab, num_outputs, flags) +
-           align256((size_t)rows * (size_t)vocab * 4);
+    const size_t n = (size_t)(rows > num_outputs ? rows : num_outputs);
+    return logits_engine_bytes(rows, vocab, num_outputs, flags) + align256(n * (size_t)vocab * 4);
   }
   if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || num_outputs <= 0) return 0;
   // top-k ops may run on either engine (the choice can depend on k)

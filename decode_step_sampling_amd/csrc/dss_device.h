@@ -223,4 +223,10 @@ __device__ __forceinline__ uint32_t signed_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// float32 value of a signed-order key (the inverse of signed_key; -0.0 comes
+// back as +0.0)
+__device__ __forceinline__ float from_signed_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 }  // namespace dss

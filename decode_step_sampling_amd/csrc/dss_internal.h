@@ -45,6 +45,11 @@ struct SampleParams {
   int32_t* rounds;
   int32_t vec_ok;   // rows may be read with 16-byte loads
   int32_t single_pivot;  // streaming loop: low <- pivot1 after each rejection
+  // sampling from logits (split engine): `probs` holds logits z, the filters
+  // apply to softmax(z / T), T per row (temp_arr) or one scalar
+  const float* temp_arr;
+  float temp;
+  float* prob_buf;  // [num_outputs][vocab] probabilities of an output that falls back
 };
 
 enum RenormKind : int { kRenormTopK = 0, kRenormTopP = 1, kMaskLogits = 2 };
@@ -110,6 +115,13 @@ struct SplitPlan {
 };
 SplitPlan plan_split(int op, int rows, int vocab, int num_outputs, uint32_t flags, int vec_ok);
 hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& plan,
+                               void* workspace, hipStream_t s, const LaunchEvents& ev);
+
+// Top-k-then-top-p sampling from logits on the split engine, softmax fused:
+// the slices' maxima and sums of exponentials ride with the hand-off, and
+// the finishing work-group turns the candidates into probabilities.  Plans
+// as plan_split; the workspace also holds p.prob_buf (logits_fallback_bytes).
+hipError_t launch_split_logits(int op, const SampleParams& p, const SplitPlan& plan,
                                void* workspace, hipStream_t s, const LaunchEvents& ev);
 
 // Split-row top-k renormalisation / logit masking (kind kRenormTopK or

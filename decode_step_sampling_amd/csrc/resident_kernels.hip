@@ -1129,10 +1129,6 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
 // row invalid (NaN-filled, status 1).
 // ---------------------------------------------------------------------------
 
-// float32 value of a signed-order key (the inverse of signed_key)
-__device__ __forceinline__ float from_signed_key(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 template <int NV>
 __global__ __launch_bounds__(kBlock) void softmax_kernel(SoftmaxParams Q, ResidentParams R) {

@@ -92,10 +92,15 @@ struct SplitParams {
 };
 
 // What the split engine computes: a sample; tau_k (and Z_k) for a top-k
-// renormalisation or a top-k logit mask, written by a second kernel; or the
+// renormalisation or a top-k logit mask, written by a second kernel; the
 // top-k values and indices themselves (selection: the top-k set, already in
-// LDS, sorted by key and index).
-enum SplitKind : int { kKindSample = 0, kKindRenorm = 1, kKindMask = 2, kKindSelect = 3 };
+// LDS, sorted by key and index); or a sample from logits, the softmax fused
+// in (kKindLogits: the slices rank logits by their signed-order keys and
+// publish their maxima; the finishing work-group turns its candidates into
+// the softmax's weights exp((z - m) / T) before the rest runs as for
+// kKindSample).
+enum SplitKind : int { kKindSample = 0, kKindRenorm = 1, kKindMask = 2, kKindSelect = 3,
+                       kKindLogits = 4 };
 
 // Order key of a value: the float32 bits for probabilities (non-negative,
 // F4 note §③), the signed-order key for logits (F4 note §⑧).
@@ -120,6 +125,7 @@ struct SplitSmem {
   // group of eight histogram bins (+ per-lane dummy slots)
   alignas(16) uint32_t mh[kMassBins + kWave];
   double draws[stream::kPreDraws];
+  double etab[64];                // logits: 2^(j / 64), j = 0 .. 63 (table_exp)
   uint32_t red[4][kWaves];        // per-wave partials of the block scans
   uint32_t wmax[kWaves];
   uint32_t wnan[kWaves];
@@ -137,6 +143,25 @@ static_assert(sizeof(SplitSmem) <= 160 * 1024, "LDS budget of one gfx950 work-gr
 
 enum SplitMode : int { kDone = 0, kFallback = 1 };
 
+// exp(x) in float64 for x <= 0 (0 below -745, and for -inf): x = n ln2/64 + r
+// with n = round(64 x / ln2) (the constant ln2/64 split in two so that n
+// times its first part is exact), |r| <= ln2/128, exp(r) by its Taylor
+// polynomial to degree 5 (truncation below 4e-17), times tab[n mod 64] =
+// 2^((n mod 64) / 64), scaled by 2^floor(n / 64).  Within about 2 ulp.
+__device__ __forceinline__ double table_exp(double x, const double* tab) {
+  if (!(x > -745.0)) return 0.0;
+  const double n = __builtin_rint(x * 0x1.71547652b82fep+6);  // 64 / ln2
+  const int ni = (int)n;
+  double r = __builtin_fma(-n, 0x1.62e42fefa0000p-7, x);
+  r = __builtin_fma(-n, 0x1.cf79abc9e3b3ap-46, r);
+  double p = __builtin_fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  p = __builtin_fma(p, r, 1.0 / 6.0);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return __builtin_ldexp(p * tab[ni & 63], ni >> 6);
+}
+
 // Everything but the streaming fallback; returns kFallback when the output
 // must be sampled by the streaming engine instead (one call site, below).
 // Reports output i (chunk-local li) invalid; every thread calls it.
@@ -148,19 +173,23 @@ __device__ __forceinline__ void split_invalid(const SampleParams& P, const Split
     return;
   }
   if (threadIdx.x != 0) return;
-  if (KIND == kKindSample) stream::write_sample(P, i, -1, 0);
+  if (KIND == kKindSample || KIND == kKindLogits) stream::write_sample(P, i, -1, 0);
   else as_global(S.r_status)[li] = 1;
 }
 
 template <int KIND, int OP, int NV>
 __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitParams& S,
                                            const SelectParams& Q, SplitSmem& sm, int& out_i) {
+  // sampling from logits (softmax fused)
+  constexpr bool kLogits = KIND == kKindLogits;
+  constexpr bool kSampling = KIND == kKindSample || kLogits;
   // logits, and any values to select from: signed-order keys
-  constexpr bool KEYS = KIND == kKindMask || KIND == kKindSelect;
+  constexpr bool KEYS = KIND == kKindMask || KIND == kKindSelect || kLogits;
   // top-k-then-top-p sampling keeps a mass histogram for the loop's start
   constexpr bool kJoint = OP == kOpTopKTopPJoint;
+  static_assert(!(kLogits && kJoint), "the joint order needs every probability's mass");
   constexpr bool kTopPPart = OP == kOpTopKTopP || kJoint;
-  constexpr bool kMass = KIND == kKindSample && kTopPPart;
+  constexpr bool kMass = kSampling && kTopPPart;
   static_assert(kMassBins + kWave <= kBlock, "one clearing store per thread");
   constexpr uint32_t kSh = KEYS ? 21u : 20u;  // top eleven bits of a key
   const int W = S.W;
@@ -194,7 +223,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   float4 v[NV];
   // (a row that a second kernel reads again, renormalisation and masking,
   // stays cacheable; every other kind reads it once: non-temporal)
-  constexpr bool kOnce = KIND == kKindSample || KIND == kKindSelect;
+  constexpr bool kOnce = KIND == kKindSample || KIND == kKindSelect || kLogits;
   auto issue = [&](int j) {
     const gptr<const float4> a = src + min(tid + j * kBlock, nvec - 1);
     v[j] = kOnce ? load_f4_nt(a) : load_f4(a);
@@ -214,12 +243,19 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       vload(P.seed_arr ? P.seed_arr + i : reinterpret_cast<const uint64_t*>(P.probs));
   const uint64_t off_raw =
       vload(P.offset_arr ? P.offset_arr + i : reinterpret_cast<const uint64_t*>(P.probs));
+  const float t_raw = kLogits ? vload(P.temp_arr ? P.temp_arr + (row_ok ? row : 0)
+                                                 : reinterpret_cast<const float*>(P.probs))
+                              : 1.0f;
 #pragma unroll
   for (int j = 0; j < kInFlight; ++j) issue(j);
   const int k = P.top_k_arr ? k_raw : P.top_k;
   const float pp = kTopPPart ? (P.top_p_arr ? pp_raw : P.top_p) : 0.0f;
-  const uint64_t seed = KIND != kKindSample ? 0ull : P.seed_arr ? seed_raw : P.seed;
-  const uint64_t offset = KIND != kKindSample ? 0ull : P.offset_arr ? off_raw : P.offset;
+  const uint64_t seed = !kSampling ? 0ull : P.seed_arr ? seed_raw : P.seed;
+  const uint64_t offset = !kSampling ? 0ull : P.offset_arr ? off_raw : P.offset;
+  // logits: the temperature, and its inverse as the oracle of the softmax
+  // takes it (t = (z - m) * (1 / T) in float64)
+  const float temp = kLogits ? (P.temp_arr ? t_raw : P.temp) : 1.0f;
+  const double itemp = kLogits ? 1.0 / (double)temp : 1.0;
 
   // while the slice is in flight: clear the histogram; wave 0 reads the
   // row's generation (used only when the slice publishes).  Nothing here
@@ -341,7 +377,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   DSS_STAMP(3);
   // the parameters' checks, once the slice has landed (every slice of the
   // output decides alike)
-  const bool ok = row_ok && k > 0 && (!kTopPPart || !isnan(pp));
+  const bool ok = row_ok && k > 0 && (!kTopPPart || !isnan(pp)) &&
+                  (!kLogits || (temp > 0.0f && temp != __builtin_inff()));
   if (!ok || k > kSplitKCap) {
     // no hand-off for this output: slice 0 answers alone
     if (s != 0) return kDone;
@@ -376,7 +413,9 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const uint32_t bnd = sm.res[0];
   const uint32_t smax = sm.res[1];
   // probabilities: a sign bit, an inf or a NaN somewhere; logits: a NaN
-  const bool bad = KEYS ? sm.res[2] != 0u : smax >= 0x7F800000u;
+  // (and, sampling from logits, a +inf)
+  const bool bad = KEYS ? (sm.res[2] != 0u || (kLogits && smax == 0xFF800000u))
+                        : smax >= 0x7F800000u;
   const bool fast = sm.res[3] != 0u;
 
   // The general path: the vectors with a value >= bnd (key > bnd), staged
@@ -456,15 +495,17 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   uint32_t tstar, gmax, ntot;
   if (W == 1) {
     // the whole row is in this work-group: full[] holds its list
-    if (bad || smax == 0u) {
+    // (logits: no finite value, the -inf key or below, is an invalid row)
+    if (bad || smax == 0u || (kLogits && smax <= 0x007FFFFFu)) {
       split_invalid<KIND>(P, S, Q, i, li);
       return kDone;
     }
     if (!publish) return kFallback;
     clear_hist<kHistBins>(sm.hist, tid, kBlock);
     if (kMass && tid < kMassBins + kWave) sm.mh[tid] = 0u;
-    if (KIND == kKindSample && wave == 1) fill_draws();
-    __syncthreads();  // histogram clears, draws
+    if (kSampling && wave == 1) fill_draws();
+    if (kLogits && wave == 2) sm.etab[lane] = exp2((double)lane * (1.0 / 64.0));
+    __syncthreads();  // histogram clears, draws, table
     tstar = bnd;
     gmax = smax;
     ntot = nlist;
@@ -539,7 +580,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       e8[q] = __hip_atomic_load(lst + min((uint32_t)(lt + q * gsz), spec - 1u), __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
     // while those reads are in flight, one wave computes the output's draws
-    if (KIND == kKindSample && wave == 1) fill_draws();
+    if (kSampling && wave == 1) fill_draws();
+    if (kLogits && wave == 2) sm.etab[lane] = exp2((double)lane * (1.0 / 64.0));
     if (wave == 0) {
       const uint32_t me = xcc_id();
       const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
@@ -566,7 +608,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       if (lane == 0) {
         uint32_t status = 0u;  // 0: go on, 1: invalid row, 2: fall back
         if (foreign) status = 2u;
-        else if (anybad || (!KEYS && gm == 0u)) status = 1u;
+        else if (anybad || (!KEYS && gm == 0u) || (kLogits && gm <= 0x007FFFFFu)) status = 1u;
         else if (ovf || all > (uint32_t)kRowCandMax) status = 2u;
         sm.res[2] = ts;
         sm.res[3] = all;
@@ -624,6 +666,23 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // one wave-uniform test, and everything inside is branch-free.
   constexpr int kMw = 16, kMt = kMw * kWave, kSlots = kRowCandMax / kMt, kGrp = 2;
   const bool worker = wave < kMw;
+  // logits: from here on entries carry the softmax's weights w = float32(
+  // exp((z - m) / T)), m the row's largest logit, so w is 1 at the maximum
+  // and a non-decreasing function of the logit key.  Top-k, top-p and the
+  // draw compare values only with each other and with fractions of their
+  // sums, so the normaliser S = sum_j w_j would cancel: it is never formed.
+  // The bound t* becomes w(t*): an entry >= t* has w >= w(t*) (keys below
+  // the -inf key are no logits: bound 0).
+  const uint32_t tkey = tstar;
+  const double lmax = kLogits ? (double)from_signed_key(gmax) : 0.0;
+  auto prob_bits = [&](uint32_t key) -> uint32_t {
+    const float w = (float)table_exp(((double)from_signed_key(key) - lmax) * itemp, sm.etab);
+    return bits_of(w);
+  };
+  if constexpr (kLogits) {
+    tstar = tkey <= 0x007FFFFFu ? 0u : prob_bits(tkey);
+    gmax = prob_bits(gmax);
+  }
   const uint32_t range = gmax - tstar;
   const uint32_t sh = range < (uint32_t)kHistBins ? 0u : 21u - (uint32_t)__clz((int)range);
   uint64_t en[kSlots];
@@ -636,8 +695,16 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       for (int q = q0; q < q0 + kGrp; ++q) {
         const uint32_t g = (uint32_t)(tid + q * kMt);
         en[q] = sm.full[g < ntot ? g : (uint32_t)(kRowCandMax + lane)];
-        const uint32_t x = (uint32_t)en[q];
-        kq[q] = (g < ntot && x >= tstar) ? (x - tstar) >> sh : 0xFFFFFFFFu;
+        uint32_t x = (uint32_t)en[q];
+        bool in = g < ntot && x >= tstar;
+        if constexpr (kLogits) {
+          // an entry at or above t* (keys), as its weight; zero ones carry no mass
+          in = g < ntot && x >= tkey;
+          x = in ? prob_bits(x) : 0u;
+          en[q] = (en[q] & 0xFFFFFFFF00000000ull) | x;
+          in = in && x >= tstar && x > 0u;
+        }
+        kq[q] = in ? (x - tstar) >> sh : 0xFFFFFFFFu;
       }
     }
   }
@@ -669,6 +736,9 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const uint32_t bin1 = sm.fres[0], above1 = sm.fres[1], nstar = sm.fres[2];
   if (nstar < (uint32_t)k && tstar > 0u) return kFallback;  // guard: fewer than k at or above t*
   const bool all_kept = nstar < (uint32_t)k;  // t* = 0 and k above the row's entry count
+  // logits: values below t* can round to p(t*) itself, so tau_k must lie
+  // strictly above p(t*); the boundary bin above the lowest one ensures it
+  if (kLogits && !all_kept && tstar > 0u && bin1 == 0u) return kFallback;
 
   // ---- the entries above bin1 into cand, those in bin1 into bnd (both in
   // (slot, thread) order, one packed scan) --------------------------------------
@@ -759,7 +829,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     stream::select_write(Q, i, sm.u.b.cand);
     return kDone;
   }
-  if (KIND != kKindSample) {
+  if (!kSampling) {
     // renormalisation / masking: tau_k, and the kept mass Z_k in a fixed order
     double zs = 0.0;
     if (KIND == kKindRenorm) {
@@ -815,7 +885,25 @@ __global__ __launch_bounds__(kBlock) void split_kernel(SampleParams P, SplitPara
   DSS_STAMP(0);
   const int mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
   if (mode == kFallback) {
-    if constexpr (KIND == kKindSample &&
+    if constexpr (KIND == kKindLogits) {
+      // the output's row as probabilities into its part of prob_buf (the
+      // one-work-group softmax), then the exact sampler on them
+      const int row = P.indices ? as_global(P.indices)[i] : i;
+      if (!(row >= 0 && row < P.rows)) {
+        if (threadIdx.x == 0) stream::write_sample(P, i, -1, 0);
+        return;
+      }
+      const float T = P.temp_arr ? as_global(P.temp_arr)[row] : P.temp;
+      stream::softmax_row(P.probs + (int64_t)row * P.vocab, P.prob_buf + (int64_t)i * P.vocab,
+                          P.vocab, T, P.vec_ok != 0, sm.u.stream.red);
+      __syncthreads();
+      SampleParams Q2 = P;
+      Q2.probs = P.prob_buf;
+      Q2.indices = nullptr;
+      Q2.rows = P.num_outputs;
+      Q2.vec_ok = P.vocab % 4 == 0;
+      stream::sample_row_exact<OP>(Q2, i, sm.u.radix);
+    } else if constexpr (KIND == kKindSample &&
                   (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint)) {
       stream::sample_row_exact<OP>(P, i, sm.u.radix);
     } else if constexpr (KIND == kKindSample) {
@@ -992,6 +1080,22 @@ hipError_t launch_split_sample(int op, const SampleParams& p, const SplitPlan& p
     } else {
       launch_nv<kKindSample, kOpTopKTopP>(plan.nv, p, sp, rp, s, ev, first, last);
     }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_split_logits(int op, const SampleParams& p, const SplitPlan& plan,
+                               void* workspace, hipStream_t s, const LaunchEvents& ev) {
+  if (op != kOpTopKTopP || !p.prob_buf) return hipErrorInvalidValue;
+  SplitParams sp = split_params(plan, workspace);
+  const RenormParams rp{};
+  for (int out0 = 0; out0 < p.num_outputs; out0 += plan.chunk) {
+    sp.out0 = out0;
+    sp.n_out = min(plan.chunk, p.num_outputs - out0);
+    const bool first = out0 == 0, last = out0 + plan.chunk >= p.num_outputs;
+    launch_nv<kKindLogits, kOpTopKTopP>(plan.nv, p, sp, rp, s, ev, first, last);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1094,5 +1094,50 @@ __device__ __forceinline__ void select_row(const SelectParams& Q, int row, Selec
   select_write(Q, row, sm.ent);
 }
 
+// Probabilities of one row from logits with a temperature (explainer,
+// 采样流水线究竟在计算什么), one work-group, three passes over the row: the
+// maximum m (and NaN / +inf), S = the sum of exp((z - m) * (1 / T)), then
+// out = float32(exp((z - m) * (1 / T)) / S), all in float64.  A NaN or +inf
+// logit, no finite logit, or T not a finite positive number NaN-fill the
+// row; returns whether it was valid.  Every thread calls.
+__device__ __forceinline__ bool softmax_row(const float* in, float* out_row, int V, float T, bool vec,
+                                   RedSmem& red) {
+  const RowRef r{as_global(in), V, vec};
+  const gptr<float> out = as_global(out_row);
+  Red acc = red_zero();
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = valid && idx + e < V;
+      acc.mx = max(acc.mx, ok ? signed_key(v[e]) : 0u);
+      acc.s0 += (ok && (isnan(v[e]) || v[e] == __builtin_inff())) ? 1u : 0u;
+    }
+  });
+  const Red s0 = block_reduce(acc, red);
+  const float zmax = from_signed_key(s0.mx);
+  const int nvec = (V + 3) / 4;
+  if (s0.s0 != 0u || !(T > 0.0f) || T == __builtin_inff() || zmax == -__builtin_inff()) {
+    const float qnan = __uint_as_float(0x7FC00000u);
+    const float o[4] = {qnan, qnan, qnan, qnan};
+    for (int f = threadIdx.x; f < nvec; f += kBlock) store4(out, V, vec, 4ll * f, o);
+    return false;
+  }
+  const double m = (double)zmax, it = 1.0 / (double)T;
+  Red sum = red_zero();
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sum.d0 += (valid && idx + e < V) ? exp(((double)v[e] - m) * it) : 0.0;
+  });
+  const double S = block_reduce(sum, red).d0;
+  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)(exp(((double)v[e] - m) * it) / S);
+    if (valid) store4(out, V, vec, idx, o);
+  });
+  return true;
+}
+
 }  // namespace stream
 }  // namespace dss

@@ -42,50 +42,15 @@ __global__ __launch_bounds__(kBlock) void stream_select_kernel(SelectParams Q) {
   select_row(Q, blockIdx.x, sm);
 }
 
-// Probabilities from logits, one work-group per row, three passes: the
-// maximum (and NaN / +inf), the sum of exp((z - m) / T), the write; the same
-// arithmetic as the resident kernel (explainer, 采样流水线究竟在计算什么).
+// Probabilities from logits, one work-group per row (softmax_row,
+// stream_device.h); the same arithmetic as the resident kernel.
 __global__ __launch_bounds__(kBlock) void stream_softmax_kernel(SoftmaxParams Q) {
   __shared__ RedSmem red;
-  const int row = blockIdx.x, V = Q.vocab;
-  const RowRef r{as_global(Q.in + (int64_t)row * V), V, Q.vec_ok != 0};
-  const gptr<float> out = as_global(Q.out + (int64_t)row * V);
+  const int row = blockIdx.x;
   const float T = Q.temp_arr ? Q.temp_arr[row] : Q.temp;
-  Red acc = red_zero();
-  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool in = valid && idx + e < V;
-      acc.mx = max(acc.mx, in ? signed_key(v[e]) : 0u);
-      acc.s0 += (in && (isnan(v[e]) || v[e] == __builtin_inff())) ? 1u : 0u;
-    }
-  });
-  const Red s0 = block_reduce(acc, red);
-  const uint32_t k = s0.mx;
-  const float zmax = __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-  const int nvec = (V + 3) / 4;
-  if (s0.s0 != 0u || !(T > 0.0f) || T == __builtin_inff() || zmax == -__builtin_inff()) {
-    const float qnan = __uint_as_float(0x7FC00000u);
-    const float o[4] = {qnan, qnan, qnan, qnan};
-    for (int f = threadIdx.x; f < nvec; f += kBlock) store4(out, V, Q.vec_ok != 0, 4ll * f, o);
-    if (Q.row_status && threadIdx.x == 0) Q.row_status[row] = 1;
-    return;
-  }
-  const double m = (double)zmax, it = 1.0 / (double)T;
-  Red sum = red_zero();
-  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sum.d0 += (valid && idx + e < V) ? exp(((double)v[e] - m) * it) : 0.0;
-  });
-  const double S = block_reduce(sum, red).d0;
-  for_each4(r, [&](int64_t idx, const float (&v)[4], bool valid) {
-    float o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (float)(exp(((double)v[e] - m) * it) / S);
-    if (valid) store4(out, V, Q.vec_ok != 0, idx, o);
-  });
-  if (Q.row_status && threadIdx.x == 0) Q.row_status[row] = 0;
+  const bool ok = softmax_row(Q.in + (int64_t)row * Q.vocab, Q.out + (int64_t)row * Q.vocab,
+                              Q.vocab, T, Q.vec_ok != 0, red);
+  if (Q.row_status && threadIdx.x == 0) Q.row_status[row] = ok ? 0 : 1;
 }
 
 }  // namespace

@@ -275,13 +275,30 @@ int dss_softmax(const float* logits, float* probs, int32_t rows, int32_t vocab,
                 const float* temperature_arr, float temperature, uint8_t* row_status,
                 uint32_t flags, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Fused top-k-then-top-p sampling from logits: dss_softmax with the given
- * temperature (temperature_arr per ROW, `rows` entries), then
- * dss_top_k_top_p_sampling_from_probs on those probabilities with the same
- * indices, seeds, parameters and flags.  The probabilities live in the
- * workspace (dss_workspace_size(DSS_OP_TOP_K_TOP_P_FROM_LOGITS, ...) bytes,
- * zero-filled once like every workspace).  Rows the softmax rejects give
- * invalid outputs. */
+/* Top-k-then-top-p sampling from logits with a temperature
+ * (temperature_arr per ROW, `rows` entries): the softmax of [Expl
+ * "采样流水线究竟在计算什么"] followed by the filters and the draw of
+ * dss_top_k_top_p_sampling_from_probs, with the same indices, seeds,
+ * parameters and flags.
+ * Sequential order (the default), on the split engine: one kernel.  Top-k,
+ * top-p and the draw compare values only with each other and with
+ * fractions of their sums, so they are unchanged when every value is scaled
+ * by one constant; the kernel ranks the logits themselves and applies the
+ * filters to the softmax's weights w_i = float32(exp((z_i - m) / T)) (m the
+ * row's largest logit) of its candidates only, never forming the normaliser
+ * S.  Kept sets equal those of the float32 probabilities w_i / S except
+ * where the one rounding of each makes or breaks a tie.
+ * The joint order, DSS_FLAG_STREAMING / FROM_ZERO / SINGLE_PIVOT, a ragged
+ * or unaligned row, and scalar k beyond the split engine's reach: dss_softmax
+ * into the workspace first, then the sampling call on those probabilities.
+ * An output the fused kernel cannot finish alone (k above 2048, overflowing
+ * candidate lists) gets its row's probabilities written to the workspace and
+ * is sampled exactly from them, inside the same kernel.
+ * A NaN or +inf logit, no finite logit, or a temperature that is not a
+ * finite positive number make the output invalid.  Workspace:
+ * dss_workspace_size(DSS_OP_TOP_K_TOP_P_FROM_LOGITS, ...) bytes (the
+ * engines' area, then max(rows, num_outputs) rows of probabilities),
+ * zero-filled once like every workspace. */
 int dss_top_k_top_p_sampling_from_logits(const float* logits, int32_t rows, int32_t vocab,
                                          const int32_t* indices, int32_t num_outputs,
                                          const uint64_t* seed_arr, uint64_t seed,

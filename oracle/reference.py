@@ -44,6 +44,14 @@ Readings of the pages (each also listed in the design doc):
   (an identity of the formula, needed for range); differences, scaling by
   1/T, exponentials and their sum in float64, each probability rounded once
   to float32; the probabilities then enter the filters like any input row.
+* R21 sampling from logits with the softmax fused (the library's default
+  for top-k-then-top-p from logits): top-k, top-p (R2) and the draw compare
+  values only with each other and with fractions of their sums, so scaling
+  every value by one constant changes none of them; the filters and the draw
+  then take the softmax's weights w_i = exp((z_i - m) * (1 / T)) in float64,
+  rounded once to float32 (w = 1 at the maximum), and the normaliser
+  S = sum_j w_j is never formed.  The kept set equals R18's except where the
+  one float32 rounding of w_i versus that of w_i / S makes or breaks a tie.
 * R19 top-k selection ([Expl] "选择 top-k 值本身": values and indices, not a
   sample): the k largest values of a row in descending order, equal values
   by ascending index, -0.0 equal to +0.0; a NaN makes the row invalid.
@@ -355,6 +363,23 @@ def softmax_row(z, temperature):
     e = np.exp(t)                                # -inf -> 0
     total = math.fsum(e.tolist())
     return True, (e / total).astype(np.float32)
+
+
+def softmax_weights(z, temperature):
+    """w_i = float32(exp((z_i - m) * (1 / T))), m = max_i z_i (R21): the
+    softmax of [Expl] "采样流水线究竟在计算什么" without its normaliser.
+    Returns (valid, w); invalid exactly when ``softmax_row`` is."""
+    z = np.asarray(z, dtype=np.float32)
+    t32 = np.float32(temperature)
+    if np.isnan(z).any() or np.isposinf(z).any() or not np.isfinite(z).any():
+        return False, None
+    if not (np.isfinite(t32) and t32 > 0):
+        return False, None
+    m = np.float64(z.max())
+    inv_t = 1.0 / np.float64(t32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        t = (z.astype(np.float64) - m) * inv_t
+    return True, np.exp(t).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------

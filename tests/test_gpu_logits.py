@@ -1,10 +1,14 @@
 """GPU parity of softmax with a temperature and of top-k-then-top-p sampling
 from logits (the step before the filters: [Expl] "采样流水线究竟在计算什么").
 
-Both sides compute p_i = float32(exp((z_i - m) / T) / S) with float64
-exponentials and sums (oracle: math.fsum; GPU: a fixed-order float64 sum),
-so a probability can differ only when e_i / S lies within ~1e-13 relative of
-a float32 rounding boundary: at most one ulp, and rarely.
+The softmax kernel and the oracle compute p_i = float32(exp((z_i - m) / T) /
+S) with float64 exponentials and sums (oracle: math.fsum; GPU: a fixed-order
+float64 sum), so a probability can differ only when e_i / S lies within
+~1e-13 relative of a float32 rounding boundary: at most one ulp, and rarely.
+Sampling from logits in the sequential order runs fused: the filters take
+the weights w_i = float32(exp((z_i - m) / T)) without the normaliser
+(oracle: softmax_weights, reading R21); the joint order, and outputs that
+fall back, take the probabilities.
 """
 
 import numpy as np
@@ -22,6 +26,16 @@ def _ulps(a, b):
     a = np.asarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
     b = np.asarray(b, dtype=np.float32).view(np.int32).astype(np.int64)
     return np.abs(a - b)
+
+
+def _kept(logits_row, T, op, k, p, fused=True):
+    """The oracle's kept set for sampling from logits: on the weights (the
+    fused path) or on the probabilities (the joint order, fallbacks)."""
+    ok, x = (ref.softmax_weights if fused else ref.softmax_row)(logits_row, T)
+    assert ok
+    valid, tau = ref.threshold(x, op, k=k, p=p)
+    assert valid
+    return x, tau, ref.support_mask(x, tau)
 
 
 def _check_softmax(got, logits, temps):
@@ -99,10 +113,7 @@ def test_sampling_from_logits_chi_square(small_logits, order):
     assert (v == 1).all()
     op = "top_k_top_p" if order == "top_k_first" else "top_k_top_p_joint"
     for r in range(rows):
-        ok, p = ref.softmax_row(logits[r], T)
-        valid, tau = ref.threshold(p, op, k=50, p=np.float32(0.9))
-        assert ok and valid
-        sup = ref.support_mask(p, tau)
+        p, tau, sup = _kept(logits[r], T, op, 50, np.float32(0.9), fused=order == "top_k_first")
         got = s[r * draws:(r + 1) * draws]
         assert sup[got].all(), "draw outside the kept set"
         counts = np.bincount(got, minlength=V)
@@ -117,12 +128,8 @@ def test_sampling_from_logits_full_size_support():
     rng = np.random.default_rng(11)
     logits = si.logits_rows(rng, 64, 151936, 2.0)
     temps = rng.uniform(0.6, 1.4, size=64).astype(np.float32)
-    supports = []
-    for r in range(64):
-        ok, p = ref.softmax_row(logits[r], temps[r])
-        valid, tau = ref.threshold(p, "top_k_top_p", k=w["top_k"][r], p=w["top_p"][r])
-        assert ok and valid
-        supports.append(ref.support_mask(p, tau))
+    supports = [_kept(logits[r], temps[r], "top_k_top_p", w["top_k"][r], w["top_p"][r])[2]
+                for r in range(64)]
     L, K, Pp, Tt = gpu(logits), gpu(w["top_k"]), gpu(w["top_p"]), gpu(temps)
     seeds = u64(w["seeds"])
     for call in range(10):
@@ -135,16 +142,75 @@ def test_sampling_from_logits_full_size_support():
 
 
 def test_sampling_from_logits_invalid_rows():
+    """A NaN or +inf logit, no finite logit, or a temperature that is not a
+    finite positive number make the output invalid (-1, valid 0)."""
     V = 2048
     rng = np.random.default_rng(5)
-    logits = si.logits_rows(rng, 3, V, 2.0)
+    logits = si.logits_rows(rng, 6, V, 2.0)
     logits[1, 7] = np.nan
-    temps = np.array([1.0, 1.0, 0.0], dtype=np.float32)
+    logits[3, 99] = np.inf
+    logits[4, :] = -np.inf
+    temps = np.array([1.0, 1.0, 0.0, 1.0, 1.0, np.inf], dtype=np.float32)
     s, v = dss.top_k_top_p_sampling_from_logits(gpu(logits), 20, 0.8, gpu(temps), seed=1,
                                                 return_valid=True)
     s, v = host(s), host(v)
     assert v[0] == 1 and s[0] >= 0
-    assert list(v[1:]) == [0, 0] and list(s[1:]) == [-1, -1]
+    assert list(v[1:]) == [0] * 5 and list(s[1:]) == [-1] * 5
+
+
+def test_fused_logits_edge_rows():
+    """The fused path (softmax inside the sampling pass) on rows that stress
+    it, B=8, V=151936: masked (-inf) entries, a first stretch of -inf in
+    every thread's first loads, one logit far above the rest (each thread's
+    running reference is raised), a huge spread where most candidates'
+    probabilities underflow to zero, a tiny temperature, and k above the
+    split engine's cap (that output falls back to probabilities written for
+    it, so its kept set is the probabilities').  Twenty calls: every draw
+    valid and inside the oracle's kept set."""
+    V, rows = 151936, 8
+    rng = np.random.default_rng(23)
+    logits = si.logits_rows(rng, rows, V, 2.0)
+    logits[0, rng.choice(V, 5000, replace=False)] = -np.inf
+    logits[1, :65536] = -np.inf
+    logits[2, 123] = 300.0
+    logits[3] *= 40.0
+    temps = np.ones(rows, dtype=np.float32)
+    temps[4] = 0.05
+    k = np.array([50, 300, 10, 1000, 40, 5000, 2048, 1], dtype=np.int32)
+    p = np.array([0.9, 0.95, 0.5, 0.99, 0.8, 0.7, 1.0, 0.3], dtype=np.float32)
+    sup = [_kept(logits[r], temps[r], "top_k_top_p", k[r], p[r], fused=k[r] <= 2048)[2]
+           for r in range(rows)]
+    L, K, Pp, Tt = gpu(logits), gpu(k), gpu(p), gpu(temps)
+    for call in range(20):
+        s, v = dss.top_k_top_p_sampling_from_logits(L, K, Pp, Tt, seed=5, offset=call,
+                                                    return_valid=True)
+        s, v = host(s), host(v)
+        assert (v == 1).all(), (call, v)
+        for r in range(rows):
+            assert sup[r][s[r]], (call, r, s[r])
+
+
+def test_fused_logits_chi_square_full_size():
+    """Distribution at the fused path's full-size launch (B=64, V=151936,
+    W=4): 4000 calls of the batch, the draws of rows 0-7 (per-row k and p of
+    the renorm workload, T = 0.8) against the oracle's p~ on the weights at
+    alpha = 1e-3."""
+    w = si.renorm()
+    rng = np.random.default_rng(13)
+    logits = si.logits_rows(rng, 64, 151936, 2.0)
+    T = 0.8
+    L, K, Pp = gpu(logits), gpu(w["top_k"]), gpu(w["top_p"])
+    draws = 4000
+    got = np.empty((draws, 8), dtype=np.int64)
+    for c in range(draws):
+        s = dss.top_k_top_p_sampling_from_logits(L, K, Pp, T, seed=77, offset=c)
+        got[c] = host(s)[:8]
+    for r in range(8):
+        pr, tau, sup = _kept(logits[r], T, "top_k_top_p", w["top_k"][r], w["top_p"][r])
+        assert sup[got[:, r]].all(), r
+        counts = np.bincount(got[:, r], minlength=151936)
+        pval, tvd, cells = pooled_chi_square(counts[sup], ref.target_distribution(pr, tau)[sup])
+        assert pval > 1e-3, (r, pval, tvd, cells)
 
 
 @pytest.mark.parametrize("vocab,flags", [(151936, dss.DSS_FLAG_STREAMING), (50257, 0),

@@ -240,6 +240,42 @@ def test_softmax_row_closed_forms_and_scipy():
         assert np.allclose(p, q, rtol=2 ** -23, atol=2.0 ** -149)
 
 
+def test_softmax_weights_closed_forms_and_scale_invariance():
+    """The unnormalised weights (R21): closed forms, w = 1 at the maximum,
+    w / sum(w) equal to the probabilities within float32 rounding, and the
+    kept set of top-k-then-top-p unchanged by the missing normaliser on rows
+    with well separated values (the filters compare values only with each
+    other and with fractions of their sums)."""
+    ok, w = ref.softmax_weights(f32([1.0, 0.0, -np.inf]), 1.0)
+    assert ok and w[0] == 1.0 and w[2] == 0.0
+    assert w[1] == np.float32(np.exp(-1.0))
+    ok, w = ref.softmax_weights(f32([0.0, -2.0]), 0.5)           # exp(-4)
+    assert w.tolist() == [1.0, float(np.float32(np.exp(-4.0)))]
+    rng = np.random.default_rng(37)
+    for _ in range(60):
+        z = f32(rng.normal(0, 3, size=int(rng.integers(2, 400))))
+        T = float(np.float32(rng.uniform(0.3, 2.0)))
+        ok, p = ref.softmax_row(z, T)
+        ok2, w = ref.softmax_weights(z, T)
+        assert ok and ok2 and w.max() == 1.0
+        q = w.astype(np.float64) / w.astype(np.float64).sum()
+        assert np.allclose(q, p, rtol=2 ** -21, atol=2.0 ** -140)
+        # separated values: no two weights within 1e-4 of each other
+        ws = np.sort(w[w > 0].astype(np.float64))
+        if ws.size > 1 and np.min(np.diff(ws) / ws[1:]) < 1e-4:
+            continue
+        k = int(rng.integers(1, z.size + 1))
+        pp = np.float32(rng.uniform(0.1, 0.99))
+        _, tp = ref.threshold(p, "top_k_top_p", k=k, p=pp)
+        _, tw = ref.threshold(w, "top_k_top_p", k=k, p=pp)
+        margin = ref.top_p_boundary_margin(p, pp, k=k)
+        if margin is not None and abs(margin) < 1e-5:
+            continue
+        assert np.array_equal(ref.support_mask(p, tp), ref.support_mask(w, tw))
+    assert ref.softmax_weights(f32([np.nan, 0.0]), 1.0) == (False, None)
+    assert ref.softmax_weights(f32([0.0, 1.0]), 0.0) == (False, None)
+
+
 def test_softmax_row_invalid_inputs():
     for z, T in ((f32([np.nan, 0.0]), 1.0), (f32([np.inf, 0.0]), 1.0),
                  (f32([-np.inf, -np.inf]), 1.0), (f32([0.0, 1.0]), 0.0),
