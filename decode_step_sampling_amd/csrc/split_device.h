@@ -91,7 +91,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total,
 // finds the chunk, a scan over that chunk's bins finds the bin.
 template <int NB>
 __device__ void wave_find(const uint32_t* hist, uint32_t need, uint32_t& bin, uint32_t& above,
-                          uint32_t& total) {
+                          uint32_t& total, uint32_t* in_bin = nullptr) {
   using H = Padded<NB>;
   static_assert(H::kChunk % 4 == 0 && H::kChunk <= kWave, "chunk of whole 16-byte reads");
   const int lane = lane_id();
@@ -108,6 +108,7 @@ __device__ void wave_find(const uint32_t* hist, uint32_t need, uint32_t& bin, ui
   if (m == 0ull) {
     bin = 0u;
     above = total - hist[0];
+    if (in_bin) *in_bin = hist[0];
     return;
   }
   const int L = first_lane(m);
@@ -118,6 +119,7 @@ __device__ void wave_find(const uint32_t* hist, uint32_t need, uint32_t& bin, ui
   const int L2 = first_lane(__ballot(lane < H::kChunk && incl2 >= need));
   bin = (uint32_t)(c * H::kChunk + H::kChunk - 1 - L2);
   above = lane_value(incl2 - h, L2);
+  if (in_bin) *in_bin = lane_value(h, L2);  // the found bin's own count
 }
 
 // ---------------------------------------------------------------------------

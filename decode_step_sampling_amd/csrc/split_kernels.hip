@@ -390,8 +390,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   }
   __syncthreads();
   if (wave == 0) {
-    uint32_t bin, above, total;
-    wave_find<kHistBins>(sm.hist, (uint32_t)k, bin, above, total);
+    uint32_t bin, above, total, nbin;
+    wave_find<kHistBins>(sm.hist, (uint32_t)k, bin, above, total, &nbin);
     const uint32_t smax = wave_max(lane < kWaves ? sm.wmax[lane] : 0u);
     const bool anynan = KEYS && __ballot(lane < kWaves && sm.wnan[lane] != 0u) != 0ull;
     const uint32_t bnd = total < (uint32_t)k ? 0u : bin << kSh;  // fewer than k vectors: all of it
@@ -401,6 +401,12 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       sm.res[1] = smax;
       sm.res[2] = anynan ? 1u : 0u;
       sm.res[3] = (J0 > 0 && tp <= bnd && !ovf) ? 1u : 0u;
+      sm.res[4] = bin;
+      sm.res[5] = above;
+      sm.res[6] = nbin;
+      // refine the bound (below) when its bin holds far more vectors than needed
+      sm.res[7] = (bnd > 0u && bin < (uint32_t)(kHistBins - 1) &&
+                   above + nbin > max(2u * (uint32_t)k, (uint32_t)k + 1024u)) ? 1u : 0u;
       if (kJoint) {
         double z = 0.0;
         for (int w = 0; w < kWaves; ++w) z += sm.wz[w];
@@ -409,6 +415,49 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
     }
   }
   __syncthreads();
+  // A bin holding far more vectors than the bound needs (flat rows, whose
+  // values share a few bins): histograms of the next bits of the vector
+  // maxima inside that bin (eleven, then the rest) narrow the bound the same
+  // certified way, so the slice publishes about k entries instead of most of
+  // the slice.  Each level counts into the same LDS histogram.
+  if (sm.res[7] != 0u) {  // block-uniform
+    uint32_t pre = sm.res[4], ab = sm.res[5], nb = sm.res[6];
+    uint32_t hsh = kSh;  // bits below the prefix
+    const uint32_t limit = max(2u * (uint32_t)k, (uint32_t)k + 1024u);
+#pragma unroll 1
+    for (int lev = 0; lev < 2 && ab + nb > limit && hsh > 0u; ++lev) {  // block-uniform
+      const uint32_t sh2 = hsh > 11u ? hsh - 11u : 0u;
+      const uint32_t mask = (1u << (hsh - sh2)) - 1u;
+      __syncthreads();
+      clear_hist<kHistBins>(sm.hist, tid, kBlock);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const uint32_t m = key[j] - 1u;
+        const bool hit = key[j] != 0u && (m >> hsh) == pre;
+        atomicAdd(&sm.hist[hit ? H1::at((m >> sh2) & mask) : pad], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t bin2, above2, total2, nbin2;
+        wave_find<kHistBins>(sm.hist, (uint32_t)k - ab, bin2, above2, total2, &nbin2);
+        if (lane == 0) {
+          const uint32_t p2 = (pre << (hsh - sh2)) | bin2;
+          const uint32_t b = p2 << sh2;
+          sm.res[0] = b;
+          sm.res[3] = (sm.res[3] != 0u && tp <= b) ? 1u : 0u;
+          sm.res[4] = p2;
+          sm.res[5] = ab + above2;
+          sm.res[6] = nbin2;
+        }
+      }
+      __syncthreads();
+      pre = sm.res[4];
+      ab = sm.res[5];
+      nb = sm.res[6];
+      hsh = sh2;
+    }
+  }
   DSS_STAMP(4);
   const uint32_t bnd = sm.res[0];
   const uint32_t smax = sm.res[1];

@@ -51,10 +51,10 @@ def _call(op, P, k, p, n_per_row, rows, seed, offset):
 
 @pytest.mark.parametrize("kind", ["softmax", "ties", "flat", "geometric"])
 @pytest.mark.parametrize("op", ["top_k", "top_k_top_p"])
-@pytest.mark.parametrize("k", [500, 3000, 70000])
+@pytest.mark.parametrize("k", [1000, 3000, 70000])
 def test_token_exact(kind, op, k):
     """Four rows of V=32768, one output each (W=16 slices, so k * W > 4096
-    even for k=500), 16 calls with offsets 0..15."""
+    even for k=1000), 16 calls with offsets 0..15."""
     rng = np.random.default_rng(sum(map(ord, kind + op)) + k)
     rows, V = 4, 32768
     probs = _rows(kind, rows, V, rng)
@@ -88,20 +88,30 @@ def test_extremes_and_invalid():
 
 def test_stress_rows_full_size():
     """The stress workload's near-uniform, peaked and geometric rows at
-    B=512, V=256000, k=1000, p=0.95 (k * W = 8000: resident engine), one
-    draw per row against the oracle's CDF draw."""
+    B=512, V=256000, p=0.95, with the workload's k=1000 (k * W = 8000) and
+    with k=2500 (above the split cap), both on the resident engine: one
+    draw per row against the oracle's CDF draw, and every draw inside the
+    kept set."""
     w = si.stress()
     probs = w["probs"]
     seeds = w["seeds"]
-    s, v, r = dss.top_k_top_p_sampling_from_probs(gpu(probs), 1000, 0.95, seed=u64(seeds),
+    P = gpu(probs)
+    s, v, r = dss.top_k_top_p_sampling_from_probs(P, 2500, 0.95, seed=u64(seeds),
                                                   offset=5, return_valid=True, return_rounds=True)
     s, v, r = host(s), host(v), host(r)
     assert (v == 1).all() and (r == 1).all()
     for row in range(0, probs.shape[0], 16):
         want = ref.sample_by_cdf(probs[row], "top_k_top_p",
-                                 ph.draw_bits53(int(seeds[row]), 5, 0, 0), k=1000,
+                                 ph.draw_bits53(int(seeds[row]), 5, 0, 0), k=2500,
                                  p=np.float32(0.95))
         assert s[row] == want, (row, int(w["groups"][row]))
+    s, v = dss.top_k_top_p_sampling_from_probs(P, 1000, 0.95, seed=u64(seeds), offset=6,
+                                               return_valid=True)
+    s, v = host(s), host(v)
+    assert (v == 1).all()
+    for row in range(3, probs.shape[0], 16):
+        _, tau = ref.threshold(probs[row], "top_k_top_p", k=1000, p=np.float32(0.95))
+        assert ref.support_mask(probs[row], tau)[s[row]], (row, int(w["groups"][row]))
 
 
 @pytest.mark.parametrize("op", ["top_k", "top_k_top_p", "top_k_top_p_joint"])

@@ -194,3 +194,40 @@ def test_workspace_shared_by_renorm_and_sampling():
             s, v = host(s), host(v)
             assert (v == 1).all(), (rows, V, call)
             assert all(sup[r][s[r]] for r in range(4)), (rows, V, call)
+
+
+@pytest.mark.parametrize("op", ["top_k", "top_k_top_p"])
+def test_split_flat_rows_refined_bound(op):
+    """Near-uniform and geometric rows with per-output k arrays (so the call
+    stays on the split engine): their vector maxima share one or a few
+    histogram bins, and the slices narrow their bounds with the next bits
+    of those bins.  Every draw valid and inside the oracle's kept set, and
+    the draws of one near-uniform row follow p~ (chi-square, alpha = 1e-3)."""
+    rng = np.random.default_rng(61)
+    rows, V = 8, 151936
+    x = np.empty((rows, V), dtype=np.float64)
+    x[:4] = 1.0 + rng.uniform(-1e-3, 1e-3, size=(4, V))
+    x[4:] = (1.0 - 2e-6) ** np.arange(V, dtype=np.float64)[None, :]
+    x /= x.sum(axis=1, keepdims=True)
+    probs = np.ascontiguousarray(x.astype(np.float32))
+    ks = np.array([200, 1000, 50, 2048, 300, 1000, 20, 2000], dtype=np.int32)
+    ps = np.array([0.9, 0.5, 1.0, 0.95, 0.8, 0.99, 0.3, 1.0], dtype=np.float32)
+    sup = _supports(probs, op, ks, ps)
+    P, K, Pp = gpu(probs), gpu(ks), gpu(ps)
+    for call in range(8):
+        s, v = _call(op, P, K, Pp, seed=3, offset=call, return_valid=True)
+        s, v = host(s), host(v)
+        assert (v == 1).all()
+        for r in range(rows):
+            assert sup[r][s[r]], (call, r)
+    # one near-uniform row, 20000 draws in one call
+    n = 20000
+    idx = np.zeros(n, dtype=np.int32)
+    s = host(_call(op, P, gpu(np.full(n, 200, dtype=np.int32)), gpu(np.full(n, 0.9, dtype=np.float32)),
+                   indices=gpu(idx), seed=11, offset=0))
+    valid, tau = ref.threshold(probs[0], op, k=200, p=np.float32(0.9))
+    s0 = ref.support_mask(probs[0], tau)
+    assert s0[s].all()
+    counts = np.bincount(s, minlength=V)
+    pval, tvd, cells = pooled_chi_square(counts[s0], ref.target_distribution(probs[0], tau)[s0])
+    assert pval > 1e-3, (pval, tvd, cells)
