@@ -102,6 +102,15 @@ struct SplitParams {
 enum SplitKind : int { kKindSample = 0, kKindRenorm = 1, kKindMask = 2, kKindSelect = 3,
                        kKindLogits = 4 };
 
+struct LkSmem {                  // the large-k merge (inside SplitSmem's union)
+  stream::SampleSmem s;          // tile masses and the locate() scratch
+  double md[kHistBins];          // the row's bin masses
+  unsigned long long hm[kHistBins];  // significand sums of one selection level
+  uint32_t nlist;                // keys gathered
+  uint32_t res[8];
+  double resd[4];
+};
+
 // Order key of a value: the float32 bits for probabilities (non-negative,
 // F4 note §③), the signed-order key for logits (F4 note §⑧).
 struct SplitSmem {
@@ -119,6 +128,11 @@ struct SplitSmem {
     stream::SampleSmem stream;   // streaming fallback
     stream::SelectSmem sel;      // streaming fallback of a selection
     stream::RadixSmem radix;     // exact fallback of top-k sampling
+    struct {                     // large k, a slice: count and significand-sum
+      uint32_t cnt[2][kHistBins];                 // histograms of bits [30:20],
+      unsigned long long mass[2][kHistBins];      // two copies (lane parity)
+    } lk;
+    LkSmem lm;                   // large k, the merge
   } u;
   alignas(16) uint32_t hist[H1::kWords];
   // fixed-point masses of the top-k entries above the boundary bin, per
@@ -141,7 +155,7 @@ struct SplitSmem {
 };
 static_assert(sizeof(SplitSmem) <= 160 * 1024, "LDS budget of one gfx950 work-group");
 
-enum SplitMode : int { kDone = 0, kFallback = 1 };
+enum SplitMode : int { kDone = 0, kFallback = 1, kLargeKMerge = 2 };
 
 // exp(x) in float64 for x <= 0 (0 below -745, and for -inf): x = n ln2/64 + r
 // with n = round(64 x / ln2) (the constant ln2/64 split in two so that n
@@ -175,6 +189,279 @@ __device__ __forceinline__ void split_invalid(const SampleParams& P, const Split
   if (threadIdx.x != 0) return;
   if (KIND == kKindSample || KIND == kKindLogits) stream::write_sample(P, i, -1, 0);
   else as_global(S.r_status)[li] = 1;
+}
+
+// ---- large k (above the candidate cap) -----------------------------------
+// Every slice counts its values and sums their 24-bit significands per bin
+// of bits [30:20] (one eighth of a binade: a bin's mass is an exact integer
+// times one power of two) and publishes the two histograms through the
+// hand-off area instead of a candidate list.  The last work-group of the row
+// adds them up and finds the bin b_k holding the k-th largest value (counts
+// from the top) and the bins the top-p cut can fall in; one pass over the
+// row gathers the keys of those bins, and two more histogram levels over
+// the gathered keys (bits [19:9], then [8:0]) give tau_k, Z_k and the top-p
+// cut exactly (the threshold search of the F4 note, §③, with 2047 pivots per
+// level); one more pass gives the kept mass of every tile for the draw
+// (blog, 逆变换采样).  Rows whose boundary bins hold more values than the
+// gather keeps go to the exact passes of the streaming engine.
+constexpr uint32_t kLargeList = 0xFFFFFFFEu;  // header count of a slice that published histograms
+constexpr uint32_t kLkGather = 16384;         // keys the merge gathers (LDS)
+
+
+// Inside the keys x of bin `bin` (x >> 20 == bin) with x >= cut: the largest
+// key t such that the values >= t number (COUNT) or weigh (mass in units of
+// the bin's power of two) at least `need`; need is at most what the bin
+// holds there.  Two levels, bits [19:9] then [8:0]; every thread calls.
+template <bool COUNT>
+__device__ uint32_t lk_select(const uint32_t* keys, uint32_t n, uint32_t bin, uint32_t cut,
+                              double need, uint32_t* hist, LkSmem& lm) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = uwave();
+  uint32_t s0 = 0u, s1 = 0u;
+  for (int lev = 0; lev < 2; ++lev) {
+    const uint32_t nb = lev == 0 ? 2048u : 512u;
+    const uint32_t hsh = lev == 0 ? 20u : 9u;  // the bits above this level's field
+    const uint32_t hval = lev == 0 ? bin : ((bin << 11) | s0);
+    const uint32_t fsh = lev == 0 ? 9u : 0u;   // the field's shift
+    for (uint32_t q = (uint32_t)tid; q < nb; q += kBlock) {
+      if (COUNT) hist[H1::at(q)] = 0u;
+      else lm.hm[q] = 0ull;
+    }
+    __syncthreads();
+    for (uint32_t c = (uint32_t)tid; c < n; c += kBlock) {
+      const uint32_t x = keys[c];
+      if ((x >> hsh) != hval || x < cut) continue;
+      const uint32_t q = (x >> fsh) & (nb - 1u);
+      if (COUNT) atomicAdd(&hist[H1::at(q)], 1u);
+      else atomicAdd(&lm.hm[q], (unsigned long long)stream::radix_sig(x));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // the largest sub-bin whose suffix (from the top) reaches need
+      double acc = 0.0, above = 0.0;
+      uint32_t found = 0xFFFFFFFFu;
+      for (int base = (int)nb - kWave; base >= 0 && found == 0xFFFFFFFFu; base -= kWave) {
+        const uint32_t q = (uint32_t)(base + kWave - 1 - lane);  // lane 0: the highest
+        const double v = COUNT ? (double)hist[H1::at(q)] : (double)lm.hm[q];
+        const double incl = acc + wave_incl_scan(v);
+        const uint64_t hit = __ballot(incl >= need && v > 0.0);
+        if (hit) {
+          const int L = first_lane(hit);
+          found = (uint32_t)lane_value((int)q, L);
+          above = lane_value(incl - v, L);
+        }
+        acc = lane63(incl);
+      }
+      if (found == 0xFFFFFFFFu) {  // rounding: the lowest sub-bin with anything in it
+        uint32_t lo = 0xFFFFFFFFu;
+        for (uint32_t q = (uint32_t)lane; q < nb; q += kWave) {
+          const double v = COUNT ? (double)hist[H1::at(q)] : (double)lm.hm[q];
+          lo = v > 0.0 ? min(lo, q) : lo;
+        }
+        found = wave_min(lo);
+        found = found == 0xFFFFFFFFu ? 0u : found;
+        above = 0.0;
+      }
+      if (lane == 0) {
+        lm.res[7] = found;
+        lm.resd[3] = above;
+      }
+    }
+    __syncthreads();
+    if (lev == 0) s0 = lm.res[7];
+    else s1 = lm.res[7];
+    need -= lm.resd[3];
+    __syncthreads();
+  }
+  return (bin << 20) | (s0 << 9) | s1;
+}
+
+// The merge's part.  Every thread calls; returns kFallback when the gather
+// would overflow.
+template <int OP>
+__device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitParams& S,
+                                             SplitSmem& sm, int i) {
+  const int W = S.W, li = i - S.out0;
+  const int row = P.indices ? as_global(P.indices)[i] : i;
+  const int k = P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k;
+  const float pp = OP == kOpTopK ? 0.0f : P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
+  const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
+  const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
+  const uint64_t* hbase = S.list + (int64_t)li * W * kListMax;
+  constexpr bool kJoint = OP == kOpTopKTopPJoint;
+  constexpr bool kTopPPart = OP == kOpTopKTopP || kJoint;
+  const int tid = threadIdx.x, lane = lane_id(), wave = uwave();
+  LkSmem& lm = sm.u.lm;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(sm.full);
+  static_assert(sizeof(sm.full) >= kLkGather * 4, "gathered keys fit full[]");
+  // the row's histograms: counts into the padded LDS histogram, masses as
+  // float64 (each bin's integer sum times its power of two)
+  for (int b = tid; b < kHistBins; b += kBlock) {
+    unsigned long long m = 0ull;
+    uint32_t c = 0u;
+    for (int q = 0; q < W; ++q) {
+      const gptr<const uint64_t> h = as_global(hbase + (size_t)q * kListMax);
+      m += __hip_atomic_load(h + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      c += __hip_atomic_load((gptr<const uint32_t>)(h + kHistBins) + b, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sm.hist[H1::at((uint32_t)b)] = c;
+    lm.md[b] = ldexp((double)m, (int)max((uint32_t)b >> 3, 1u) - 150);
+  }
+  if (tid == 0) lm.nlist = 0u;
+  __syncthreads();
+  const float pc = stream::clamp01(pp);
+  if (wave == 0) {
+    uint32_t bk, above, total, nbk;
+    wave_find<kHistBins>(sm.hist, (uint32_t)k, bk, above, total, &nbk);
+    const bool all = total < (uint32_t)k;  // every value kept by top-k
+    // masses above b_k (the top-k set's certain part), of b_k, of the row
+    double mab = 0.0, mtot = 0.0;
+    for (int b = lane; b < kHistBins; b += kWave) {
+      mab += b > (int)bk ? lm.md[b] : 0.0;
+      mtot += lm.md[b];
+    }
+    mab = wave_sum(mab);
+    mtot = wave_sum(mtot);
+    const double mbk = lm.md[bk];
+    // the bins the top-p cut can fall in, [plo, phi]
+    uint32_t plo = bk, phi = bk;
+    if (kTopPPart) {
+      const double zlo = kJoint ? mtot : (all ? mtot : mab);
+      const double zhi = kJoint ? mtot : (all ? mtot : mab + mbk);
+      uint32_t b1, b2;
+      double a1, a2, t1, t2;
+      // (b_k's mass left out for the top-k-first order: a target above the
+      // bins over b_k falls in b_k, mass_find then reports a lower bin)
+      if (!kJoint && !all) lm.md[bk] = 0.0;
+      stream::mass_find<kHistBins>(lm.md, (double)pc * zlo, -1.0, b1, a1, t1);
+      stream::mass_find<kHistBins>(lm.md, (double)pc * zhi, -1.0, b2, a2, t2);
+      if (!kJoint && !all) lm.md[bk] = mbk;
+      if (kJoint || all) {
+        phi = b1;
+        plo = b2;
+      } else {
+        phi = (double)pc * zlo <= mab && mab > 0.0 ? max(b1, bk) : bk;
+        plo = (double)pc * zhi <= mab && mab > 0.0 ? max(b2, bk) : bk;
+      }
+    }
+    // keys to gather: bin b_k (unless every value is kept) and [plo, phi]
+    uint32_t n = 0u;
+    for (int b = lane; b < kHistBins; b += kWave) {
+      const bool g = (!all && b == (int)bk) || (b >= (int)plo && b <= (int)phi);
+      n += g ? sm.hist[H1::at((uint32_t)b)] : 0u;
+    }
+    n = wave_sum(n);
+    if (lane == 0) {
+      lm.res[0] = bk;
+      lm.res[1] = above;
+      lm.res[2] = all ? 1u : 0u;
+      lm.res[3] = plo;
+      lm.res[4] = phi;
+      lm.res[5] = n;
+      lm.resd[0] = mab;
+      lm.resd[1] = mtot;
+    }
+  }
+  __syncthreads();
+  const uint32_t bk = lm.res[0], above = lm.res[1], plo = lm.res[3], phi = lm.res[4];
+  const bool all = lm.res[2] != 0u;
+  if (lm.res[5] > kLkGather) return kFallback;  // block-uniform
+  // gather: one pass over the row, a tile per wave
+  const stream::RowRef r{as_global(P.probs + (int64_t)row * P.vocab), P.vocab, P.vec_ok != 0};
+  const int n_tiles = (P.vocab + stream::kTile - 1) / stream::kTile;
+  for (int t = wave; t < n_tiles; t += kWaves) {
+    const int64_t tb = (int64_t)t * stream::kTile;
+    float vt[stream::kTileChunks][4];
+#pragma unroll
+    for (int q = 0; q < stream::kTileChunks; ++q)
+      stream::load4(r, tb + q * (kWave * 4) + lane * 4, vt[q]);
+#pragma unroll
+    for (int q = 0; q < stream::kTileChunks; ++q) {
+      const int64_t idx = tb + q * (kWave * 4) + lane * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = bits_of(vt[q][e]);
+        const uint32_t b = min(key >> 20, (uint32_t)(kHistBins - 1));
+        const bool g = idx + e < P.vocab && ((!all && b == bk) || (b >= plo && b <= phi));
+        const uint64_t m = __ballot(g);
+        if (m == 0ull) continue;  // wave-uniform
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&lm.nlist, (uint32_t)__popcll(m));
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        const uint32_t pos = base + rank_in(m);
+        if (g && pos < kLkGather) keys[pos] = key;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t n = min(lm.nlist, kLkGather);
+  // tau_k: the (k - above)-th largest key of bin b_k
+  const uint32_t tk = all ? 0u : lk_select<true>(keys, n, bk, 0u, (double)((uint32_t)k - above),
+                                                 sm.hist, lm);
+  // Z_k: the bins above b_k, then b_k's values >= tau_k (exact integer
+  // significand sums, below 2^53, so their float64 sum is exact)
+  double sk = 0.0;
+  for (uint32_t c = (uint32_t)tid; c < n; c += kBlock) {
+    const uint32_t x = keys[c];
+    sk += (!all && (x >> 20) == bk && x >= tk) ? (double)stream::radix_sig(x) : 0.0;
+  }
+  sk = wave_sum(sk);
+  if (lane == 0) sm.wz[wave] = sk;
+  __syncthreads();
+  if (tid == 0) {
+    double z = 0.0;
+    for (int w = 0; w < kWaves; ++w) z += sm.wz[w];
+    lm.resd[2] = all ? lm.resd[1] : lm.resd[0] + ldexp(z, (int)max(bk >> 3, 1u) - 150);
+  }
+  __syncthreads();
+  const double zk = lm.resd[2];
+  uint32_t tau = max(tk, 1u);  // zeros carry no mass
+  if (kTopPPart) {
+    // the cut: the smallest prefix (descending) whose mass reaches p * Z
+    // (Z_k, or the row's mass for the joint order).  Its bin: the bins
+    // above b_k count fully, b_k with its values >= tau_k (top-k first)
+    const double target = (double)pc * (kJoint ? lm.resd[1] : zk);
+    if (wave == 0) {
+      if (!kJoint && !all) lm.md[bk] = zk - lm.resd[0];
+      uint32_t bp;
+      double ab, tot;
+      stream::mass_find<kHistBins>(lm.md, target, -1.0, bp, ab, tot);
+      if (!kJoint && !all) bp = max(bp, bk);
+      if (lane == 0) {
+        lm.res[6] = bp;
+        lm.resd[3] = ab;
+      }
+    }
+    __syncthreads();
+    const uint32_t bp = lm.res[6];
+    const double ab = lm.resd[3];
+    // inside bin b_p (gathered: b_p lies in [plo, phi] or is b_k), by mass
+    // in units of the bin's power of two
+    const double unit = ldexp(1.0, (int)max(bp >> 3, 1u) - 150);
+    const double need = max((target - ab) / unit, 0.0);
+    const uint32_t tp = (bp >= plo && bp <= phi) || (!all && bp == bk)
+                            ? lk_select<false>(keys, n, bp, (!kJoint && bp == bk) ? tk : 0u, need,
+                                               sm.hist, lm)
+                            : tk;
+    tau = max(tau, tp);
+  }
+  // the kept mass of every tile, then one draw (rounds = 1: the blog's loop
+  // started just below tau, where every draw is accepted)
+  const float low = __uint_as_float(tau - 1u);
+  uint32_t ca = 0u, cb = 0u;
+  stream::pivot_pass(r, n_tiles, low, low, lm.s.tm[0], lm.s.tm[1], ca, cb);
+  __syncthreads();
+  if (wave == 0) {
+    const double z = stream::tile_scan_total(lm.s.tm[0], n_tiles);
+    if (lane == 0) lm.s.bc_d[0] = z * draw_uniform(seed, offset, sid, 0u);
+  }
+  __syncthreads();
+  const double T = lm.s.bc_d[0];
+  __syncthreads();
+  const int tok = stream::locate(r, lm.s.tm[0], n_tiles, T, low, lm.s);
+  if (threadIdx.x == 0) stream::write_sample(P, i, tok, tok >= 0 ? 1 : 0);
+  return kDone;
 }
 
 template <int KIND, int OP, int NV>
@@ -379,6 +666,83 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // output decides alike)
   const bool ok = row_ok && k > 0 && (!kTopPPart || !isnan(pp)) &&
                   (!kLogits || (temp > 0.0f && temp != __builtin_inff()));
+  constexpr bool kLargeK = KIND == kKindSample &&
+                           (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint);
+  if (kLargeK && ok && k > kSplitKCap && W > 1) {
+    // ---- large k: histograms instead of candidate lists (see large_k_merge)
+    auto& lk = sm.u.lk;
+    __syncthreads();  // every wave's staging stores (same LDS) and maxima are done
+    for (int q = tid; q < kHistBins; q += kBlock) {
+      lk.cnt[0][q] = lk.cnt[1][q] = 0u;
+      lk.mass[0][q] = lk.mass[1][q] = 0ull;
+    }
+    __syncthreads();
+    const int cp = lane & 1;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const bool in = tid + j * kBlock < nvec;
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!in) continue;
+        const uint32_t b = min(k4[e] >> 20, (uint32_t)(kHistBins - 1));
+        atomicAdd(&lk.cnt[cp][b], 1u);
+        atomicAdd(&lk.mass[cp][b], (unsigned long long)stream::radix_sig(k4[e]));
+      }
+    }
+    __syncthreads();
+    const gptr<uint64_t> dst = as_global(S.list + ((int64_t)li * W + s) * kListMax);
+    for (int q = tid; q < kHistBins; q += kBlock) {
+      dst[q] = lk.mass[0][q] + lk.mass[1][q];
+      ((gptr<uint32_t>)(dst + kHistBins))[q] = lk.cnt[0][q] + lk.cnt[1][q];
+    }
+    if (tid == 0) {
+      uint32_t smax = 0u;
+      for (int w = 0; w < kWaves; ++w) smax = max(smax, sm.wmax[w]);
+      const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + s) * kHdrWords);
+      h[0] = 0u;
+      h[1] = kLargeList;
+      h[2] = smax;
+      h[3] = gen;
+      h[4] = xcc_id();
+      h[5] = smax >= 0x7F800000u ? 1u : 0u;  // a sign bit, an inf or a NaN
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(as_global(S.ctr + li), 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      sm.flag = (old == (uint32_t)(W - 1));
+    }
+    __syncthreads();
+    if (!sm.flag) return kDone;
+    // the last slice: the headers (all written before their arrivals)
+    if (wave == 0) {
+      const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + (lane & (W - 1))) * kHdrWords);
+      const uint32_t hc = __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hb = __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool mine = lane < W;
+      const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
+      const bool foreign =
+          __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull;
+      const bool anybad = __ballot(mine && hb != 0u) != 0ull;
+      if (lane == 0) {
+        __hip_atomic_store(as_global(S.ctr + li), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.res[0] = foreign ? 2u : anybad ? 1u : 0u;
+      }
+    }
+    __syncthreads();
+    if (sm.res[0] == 1u) {
+      split_invalid<KIND>(P, S, Q, i, li);
+      return kDone;
+    }
+    if (sm.res[0] == 2u) return kFallback;
+    return kLargeKMerge;
+  }
   if (!ok || k > kSplitKCap) {
     // no hand-off for this output: slice 0 answers alone
     if (s != 0) return kDone;
@@ -932,7 +1296,11 @@ __global__ __launch_bounds__(kBlock) void split_kernel(SampleParams P, SplitPara
   __shared__ SplitSmem sm;
   int i = 0;
   DSS_STAMP(0);
-  const int mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
+  int mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
+  if constexpr (KIND == kKindSample &&
+                (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint)) {
+    if (mode == kLargeKMerge) mode = large_k_merge<OP>(P, S, sm, i);
+  }
   if (mode == kFallback) {
     if constexpr (KIND == kKindLogits) {
       // the output's row as probabilities into its part of prob_buf (the
