@@ -212,6 +212,40 @@ constexpr uint32_t kLkGather = 16384;         // keys the merge gathers (LDS)
 // key t such that the values >= t number (COUNT) or weigh (mass in units of
 // the bin's power of two) at least `need`; need is at most what the bin
 // holds there.  Two levels, bits [19:9] then [8:0]; every thread calls.
+// The row's bin masses are stored by column: bin b at (b mod 32) * 64 +
+// b / 32, so that lane l reading its 32 consecutive bins touches 64
+// consecutive words per read (no LDS bank conflicts).
+__device__ __forceinline__ uint32_t md_at(uint32_t b) { return (b & 31u) * 64u + (b >> 5); }
+
+// One wave: the largest bin b whose mass from the top, M(b) = sum of the
+// bins >= b, reaches `need` and is positive; above = M(b + 1).  If rounding
+// leaves every M(b) below need, the lowest bin with mass (mass_find of the
+// streaming engine, on the column layout).
+__device__ __forceinline__ void md_find(const double* md, double need, uint32_t& bin,
+                                        double& above) {
+  const int lane = lane_id();
+  const int c = kWave - 1 - lane;  // lane 0: the top chunk
+  double s = 0.0;
+#pragma unroll 8
+  for (int q = 31; q >= 0; --q) s += md[md_at((uint32_t)(c * 32 + q))];
+  const double incl = wave_incl_scan(s);
+  const double excl = wave_excl_from_incl(incl);
+  const uint64_t hit = __ballot(incl >= need && incl > 0.0);
+  const int L = hit ? first_lane(hit) : last_lane(__ballot(s > 0.0) | 1ull);
+  const bool fb = hit == 0ull;
+  const int cc = kWave - 1 - L;
+  const double ex = lane_value(excl, L);
+  const double m = lane < 32 ? md[md_at((uint32_t)(cc * 32 + 31 - lane))] : 0.0;
+  const double incl2 = wave_incl_scan(m) + ex;
+  const double sh = wave_excl_from_incl(incl2);
+  const double excl2 = lane == 0 ? ex : sh;
+  uint64_t hit2 = fb ? 0ull : __ballot(lane < 32 && incl2 >= need && incl2 > 0.0);
+  if (hit2 == 0ull) hit2 = 1ull << (63 - __clzll((long long)(__ballot(lane < 32 && m > 0.0) | 1ull)));
+  const int Q = first_lane(hit2);
+  bin = (uint32_t)(cc * 32 + 31 - Q);
+  above = lane_value(excl2, Q);
+}
+
 template <bool COUNT>
 __device__ uint32_t lk_select(const uint32_t* keys, uint32_t n, uint32_t bin, uint32_t cut,
                               double need, uint32_t* hist, LkSmem& lm) {
@@ -222,7 +256,7 @@ __device__ uint32_t lk_select(const uint32_t* keys, uint32_t n, uint32_t bin, ui
     const uint32_t hsh = lev == 0 ? 20u : 9u;  // the bits above this level's field
     const uint32_t hval = lev == 0 ? bin : ((bin << 11) | s0);
     const uint32_t fsh = lev == 0 ? 9u : 0u;   // the field's shift
-    for (uint32_t q = (uint32_t)tid; q < nb; q += kBlock) {
+    for (uint32_t q = (uint32_t)tid; q < (uint32_t)kHistBins; q += kBlock) {
       if (COUNT) hist[H1::at(q)] = 0u;
       else lm.hm[q] = 0ull;
     }
@@ -235,31 +269,21 @@ __device__ uint32_t lk_select(const uint32_t* keys, uint32_t n, uint32_t bin, ui
       else atomicAdd(&lm.hm[q], (unsigned long long)stream::radix_sig(x));
     }
     __syncthreads();
+    if (!COUNT) {  // the sums as float64 (exact below 2^53) in the column layout
+      for (uint32_t q = (uint32_t)tid; q < (uint32_t)kHistBins; q += kBlock)
+        lm.md[md_at(q)] = (double)lm.hm[q];
+      __syncthreads();
+    }
+    // the largest sub-bin whose suffix (from the top) reaches need
     if (wave == 0) {
-      // the largest sub-bin whose suffix (from the top) reaches need
-      double acc = 0.0, above = 0.0;
-      uint32_t found = 0xFFFFFFFFu;
-      for (int base = (int)nb - kWave; base >= 0 && found == 0xFFFFFFFFu; base -= kWave) {
-        const uint32_t q = (uint32_t)(base + kWave - 1 - lane);  // lane 0: the highest
-        const double v = COUNT ? (double)hist[H1::at(q)] : (double)lm.hm[q];
-        const double incl = acc + wave_incl_scan(v);
-        const uint64_t hit = __ballot(incl >= need && v > 0.0);
-        if (hit) {
-          const int L = first_lane(hit);
-          found = (uint32_t)lane_value((int)q, L);
-          above = lane_value(incl - v, L);
-        }
-        acc = lane63(incl);
-      }
-      if (found == 0xFFFFFFFFu) {  // rounding: the lowest sub-bin with anything in it
-        uint32_t lo = 0xFFFFFFFFu;
-        for (uint32_t q = (uint32_t)lane; q < nb; q += kWave) {
-          const double v = COUNT ? (double)hist[H1::at(q)] : (double)lm.hm[q];
-          lo = v > 0.0 ? min(lo, q) : lo;
-        }
-        found = wave_min(lo);
-        found = found == 0xFFFFFFFFu ? 0u : found;
-        above = 0.0;
+      uint32_t found;
+      double above;
+      if (COUNT) {
+        uint32_t ac, tot;
+        wave_find<kHistBins>(hist, (uint32_t)need, found, ac, tot);
+        above = (double)ac;
+      } else {
+        md_find(lm.md, need, found, above);
       }
       if (lane == 0) {
         lm.res[7] = found;
@@ -306,7 +330,7 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
                              __HIP_MEMORY_SCOPE_AGENT);
     }
     sm.hist[H1::at((uint32_t)b)] = c;
-    lm.md[b] = ldexp((double)m, (int)max((uint32_t)b >> 3, 1u) - 150);
+    lm.md[md_at((uint32_t)b)] = ldexp((double)m, (int)max((uint32_t)b >> 3, 1u) - 150);
   }
   if (tid == 0) lm.nlist = 0u;
   __syncthreads();
@@ -318,25 +342,25 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     // masses above b_k (the top-k set's certain part), of b_k, of the row
     double mab = 0.0, mtot = 0.0;
     for (int b = lane; b < kHistBins; b += kWave) {
-      mab += b > (int)bk ? lm.md[b] : 0.0;
-      mtot += lm.md[b];
+      mab += b > (int)bk ? lm.md[md_at((uint32_t)b)] : 0.0;
+      mtot += lm.md[md_at((uint32_t)b)];
     }
     mab = wave_sum(mab);
     mtot = wave_sum(mtot);
-    const double mbk = lm.md[bk];
+    const double mbk = lm.md[md_at(bk)];
     // the bins the top-p cut can fall in, [plo, phi]
     uint32_t plo = bk, phi = bk;
     if (kTopPPart) {
       const double zlo = kJoint ? mtot : (all ? mtot : mab);
       const double zhi = kJoint ? mtot : (all ? mtot : mab + mbk);
       uint32_t b1, b2;
-      double a1, a2, t1, t2;
+      double a1, a2;
       // (b_k's mass left out for the top-k-first order: a target above the
-      // bins over b_k falls in b_k, mass_find then reports a lower bin)
-      if (!kJoint && !all) lm.md[bk] = 0.0;
-      stream::mass_find<kHistBins>(lm.md, (double)pc * zlo, -1.0, b1, a1, t1);
-      stream::mass_find<kHistBins>(lm.md, (double)pc * zhi, -1.0, b2, a2, t2);
-      if (!kJoint && !all) lm.md[bk] = mbk;
+      // bins over b_k falls in b_k, md_find then reports a lower bin)
+      if (!kJoint && !all) lm.md[md_at(bk)] = 0.0;
+      md_find(lm.md, (double)pc * zlo, b1, a1);
+      md_find(lm.md, (double)pc * zhi, b2, a2);
+      if (!kJoint && !all) lm.md[md_at(bk)] = mbk;
       if (kJoint || all) {
         phi = b1;
         plo = b2;
@@ -367,30 +391,41 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
   const uint32_t bk = lm.res[0], above = lm.res[1], plo = lm.res[3], phi = lm.res[4];
   const bool all = lm.res[2] != 0u;
   if (lm.res[5] > kLkGather) return kFallback;  // block-uniform
-  // gather: one pass over the row, a tile per wave
+  // gather: one pass over the row (thread t the vectors t, t + 1024, ...,
+  // eight loads in flight), one slot reservation per wave and batch
   const stream::RowRef r{as_global(P.probs + (int64_t)row * P.vocab), P.vocab, P.vec_ok != 0};
   const int n_tiles = (P.vocab + stream::kTile - 1) / stream::kTile;
-  for (int t = wave; t < n_tiles; t += kWaves) {
-    const int64_t tb = (int64_t)t * stream::kTile;
-    float vt[stream::kTileChunks][4];
+  const int nvec4 = (P.vocab + 3) / 4;
+  constexpr int kGB = 8;
+  for (int f0 = tid; f0 - tid < nvec4; f0 += kBlock * kGB) {  // block-uniform bound
+    float vt[kGB][4];
+    stream::load4_batch<kGB>(r, [&](int u) { return 4ll * min(f0 + u * kBlock, nvec4 - 1); }, vt);
+    uint32_t cnt = 0u;
+    uint32_t gm = 0u;  // bit 4u + e: value e of load u is gathered
 #pragma unroll
-    for (int q = 0; q < stream::kTileChunks; ++q)
-      stream::load4(r, tb + q * (kWave * 4) + lane * 4, vt[q]);
-#pragma unroll
-    for (int q = 0; q < stream::kTileChunks; ++q) {
-      const int64_t idx = tb + q * (kWave * 4) + lane * 4;
+    for (int u = 0; u < kGB; ++u) {
+      const int64_t idx = 4ll * (f0 + u * kBlock);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = bits_of(vt[q][e]);
-        const uint32_t b = min(key >> 20, (uint32_t)(kHistBins - 1));
-        const bool g = idx + e < P.vocab && ((!all && b == bk) || (b >= plo && b <= phi));
-        const uint64_t m = __ballot(g);
-        if (m == 0ull) continue;  // wave-uniform
-        uint32_t base = 0u;
-        if (lane == 0) base = atomicAdd(&lm.nlist, (uint32_t)__popcll(m));
-        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-        const uint32_t pos = base + rank_in(m);
-        if (g && pos < kLkGather) keys[pos] = key;
+        const uint32_t b = min(bits_of(vt[u][e]) >> 20, (uint32_t)(kHistBins - 1));
+        const bool g = f0 + u * kBlock < nvec4 && idx + e < P.vocab &&
+                       ((!all && b == bk) || (b >= plo && b <= phi));
+        gm |= g ? 1u << (4 * u + e) : 0u;
+        cnt += g ? 1u : 0u;
+      }
+    }
+    const uint32_t incl = wave_incl_scan(cnt);
+    uint32_t base = 0u;
+    if (lane == kWave - 1 && incl > 0u) base = atomicAdd(&lm.nlist, incl);
+    base = lane_value(base, kWave - 1);
+    uint32_t pos = base + incl - cnt;
+#pragma unroll
+    for (int u = 0; u < kGB; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!((gm >> (4 * u + e)) & 1u)) continue;
+        if (pos < kLkGather) keys[pos] = bits_of(vt[u][e]);
+        ++pos;
       }
     }
   }
@@ -423,10 +458,10 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     // above b_k count fully, b_k with its values >= tau_k (top-k first)
     const double target = (double)pc * (kJoint ? lm.resd[1] : zk);
     if (wave == 0) {
-      if (!kJoint && !all) lm.md[bk] = zk - lm.resd[0];
+      if (!kJoint && !all) lm.md[md_at(bk)] = zk - lm.resd[0];
       uint32_t bp;
-      double ab, tot;
-      stream::mass_find<kHistBins>(lm.md, target, -1.0, bp, ab, tot);
+      double ab;
+      md_find(lm.md, target, bp, ab);
       if (!kJoint && !all) bp = max(bp, bk);
       if (lane == 0) {
         lm.res[6] = bp;
@@ -446,11 +481,36 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
                             : tk;
     tau = max(tau, tp);
   }
-  // the kept mass of every tile, then one draw (rounds = 1: the blog's loop
-  // started just below tau, where every draw is accepted)
+  // the kept mass of every tile (2048 values: a wave's 64 vectors of one
+  // load lie in one tile, eight waves cover it; their partial sums go to
+  // fixed slots and are added in order), then one draw (rounds = 1: the
+  // blog's loop started just below tau, where every draw is accepted)
   const float low = __uint_as_float(tau - 1u);
-  uint32_t ca = 0u, cb = 0u;
-  stream::pivot_pass(r, n_tiles, low, low, lm.s.tm[0], lm.s.tm[1], ca, cb);
+  double* part = reinterpret_cast<double*>(sm.full);  // [tile][8], the keys are done with
+  static_assert(sizeof(sm.full) >= stream::kMaxTiles * 8 * sizeof(double), "tile partials");
+  __syncthreads();
+  for (int f0 = tid; f0 - tid < nvec4; f0 += kBlock * kGB) {  // block-uniform bound
+    float vt[kGB][4];
+    stream::load4_batch<kGB>(r, [&](int u) { return 4ll * min(f0 + u * kBlock, nvec4 - 1); }, vt);
+#pragma unroll
+    for (int u = 0; u < kGB; ++u) {
+      const int f = f0 + u * kBlock;
+      double sv = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sv += (f < nvec4 && vt[u][e] > low) ? (double)vt[u][e] : 0.0;
+      sv = wave_sum(sv);
+      const int fw = f - lane;  // the wave's first vector of this load
+      if (lane == 0 && fw < nvec4) part[(fw >> 9) * 8 + ((fw >> 6) & 7)] = sv;
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < n_tiles; t += kBlock) {
+    double z = 0.0;
+    const int nw = min(8, ((nvec4 - t * 512) + 63) / 64);  // waves that covered tile t
+    for (int q = 0; q < nw; ++q) z += part[t * 8 + q];
+    lm.s.tm[0][t] = z;
+  }
   __syncthreads();
   if (wave == 0) {
     const double z = stream::tile_scan_total(lm.s.tm[0], n_tiles);

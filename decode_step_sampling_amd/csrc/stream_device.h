@@ -21,17 +21,33 @@ struct RowRef {
   bool vec;
 };
 
-// Values x[idx .. idx+3]; positions past the row end read as 0.
-__device__ __forceinline__ void load4(const RowRef& r, int64_t idx, float (&v)[4]) {
-  if (r.vec && idx + 3 < r.V) {
-    const float4 q = load_f4((gptr<const float4>)(r.x + idx));
-    v[0] = q.x;
-    v[1] = q.y;
-    v[2] = q.z;
-    v[3] = q.w;
+// N groups of four, group u at idx_of(u) (a multiple of 4; past the row end
+// reads as 0), every load issued before the first value is used.  The
+// choice between 16-byte and one-value loads is made once for the batch on
+// r.vec, which every lane shares: made per group and per lane, the two kinds
+// of load land in the same registers from two arms and the compiler waits
+// for each load before the next one is issued.
+template <int N, class I>
+__device__ __forceinline__ void load4_batch(const RowRef& r, I&& idx_of, float (&v)[N][4]) {
+  if (r.vec) {
+    // V % 4 == 0: a group is whole or lies wholly past the row end
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      const int64_t idx = idx_of(u);
+      const bool in = idx < r.V;
+      const float4 q = load_f4((gptr<const float4>)(r.x + (in ? idx : 0)));
+      v[u][0] = in ? q.x : 0.0f;
+      v[u][1] = in ? q.y : 0.0f;
+      v[u][2] = in ? q.z : 0.0f;
+      v[u][3] = in ? q.w : 0.0f;
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (idx + e < r.V) ? r.x[idx + e] : 0.0f;
+    for (int u = 0; u < N; ++u) {
+      const int64_t idx = idx_of(u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[u][e] = (idx + e < r.V) ? r.x[idx + e] : 0.0f;
+    }
   }
 }
 
@@ -49,20 +65,7 @@ __device__ __forceinline__ void for_each4(const RowRef& r, F&& body) {
   const int nvec = (r.V + 3) / 4;
   for (int f0 = threadIdx.x; f0 < nvec; f0 += kBlock * kBatch) {
     float v[kBatch][4];
-    if (r.vec) {
-      // V % 4 == 0 and a 16-byte aligned row: every clamped group is whole
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float4 q = load_f4((gptr<const float4>)(r.x + 4ll * min(f0 + u * kBlock, nvec - 1)));
-        v[u][0] = q.x;
-        v[u][1] = q.y;
-        v[u][2] = q.z;
-        v[u][3] = q.w;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) load4(r, 4ll * min(f0 + u * kBlock, nvec - 1), v[u]);
-    }
+    load4_batch<kBatch>(r, [&](int u) { return 4ll * min(f0 + u * kBlock, nvec - 1); }, v);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int f = f0 + u * kBlock;
@@ -261,8 +264,7 @@ __device__ inline int locate(const RowRef& r, const double* tm, int n_tiles, dou
       double run_carry = 0.0;
       int last_cand = -1;
       float vt[kTileChunks][4];  // the whole tile in flight at once
-#pragma unroll
-      for (int q = 0; q < kTileChunks; ++q) load4(r, tbase + q * (kWave * 4) + lane * 4, vt[q]);
+      load4_batch<kTileChunks>(r, [&](int q) { return tbase + q * (kWave * 4) + lane * 4; }, vt);
 #pragma unroll
       for (int q = 0; q < kTileChunks; ++q) {
         const int64_t idx = tbase + q * (kWave * 4) + lane * 4;
@@ -314,10 +316,11 @@ __device__ inline void pivot_pass(const RowRef& r, int n_tiles, float a, float b
   for (int t = wave_id(); t < n_tiles; t += kWaves) {
     const int64_t base = (int64_t)t * kTile;
     double sa = 0.0, sb = 0.0;
+    float vt[kTileChunks][4];
+    load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
 #pragma unroll
     for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
-      load4(r, base + q * (kWave * 4) + lane * 4, v);
+      const float (&v)[4] = vt[q];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // padding past the row end reads as 0, never above a pivot >= 0
@@ -400,10 +403,11 @@ __device__ __forceinline__ void sample_row(const SampleParams& P, int i, SampleS
   for (int t = wave; t < n_tiles; t += kWaves) {
     const int64_t base = (int64_t)t * kTile;
     double s = 0.0;
+    float vt[kTileChunks][4];
+    load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
 #pragma unroll
     for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
-      load4(r, base + q * (kWave * 4) + lane * 4, v);
+      const float (&v)[4] = vt[q];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         mbits = max(mbits, bits_of(v[e]));
@@ -999,11 +1003,12 @@ __device__ __forceinline__ void select_row(const SelectParams& Q, int row, Selec
   for (int t = wave; t < n_tiles; t += kWaves) {
     const int64_t base = (int64_t)t * kTile;
     uint32_t eq = 0u;
+    float vt[kTileChunks][4];
+    load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
 #pragma unroll
     for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
+      const float (&v)[4] = vt[q];
       const int64_t idx = base + q * (kWave * 4) + lane * 4;
-      load4(r, idx, v);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t key = idx + e < V ? signed_key(v[e]) : 0u;
@@ -1051,11 +1056,12 @@ __device__ __forceinline__ void select_row(const SelectParams& Q, int row, Selec
   for (int t = wave; t < n_tiles; t += kWaves) {
     const int64_t base = (int64_t)t * kTile;
     uint32_t tie_carry = 0u;
+    float vt[kTileChunks][4];
+    load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
 #pragma unroll
     for (int q = 0; q < kTileChunks; ++q) {
-      float v[4];
+      const float (&v)[4] = vt[q];
       const int64_t idx = base + q * (kWave * 4) + lane * 4;
-      load4(r, idx, v);
       uint32_t key[4];
       uint32_t my_ties = 0u;
 #pragma unroll
