@@ -89,6 +89,13 @@ struct SplitParams {
   uint32_t* r_tau;    // renorm / mask: [n_out] tau_k as an order key
   double* r_z;        // renorm: [n_out] kept mass Z_k
   uint8_t* r_status;  // renorm / mask: [n_out] 0 ok, 1 invalid row, 2 written already
+  // Finishing work-groups (sampling with per-output k over more than one
+  // wave of work-groups): the slices of an output with k above the
+  // candidate cap publish their histograms and leave; one work-group per
+  // output, placed after every slice in the grid, waits for them and merges.
+  int fin;         // 1: the grid ends with finishing work-groups
+  int nsb;         // work-groups of slices (the finishing ones start here)
+  uint64_t spin;   // ticks of the 100 MHz constant clock a finisher waits at most
 };
 
 // What the split engine computes: a sample; tau_k (and Z_k) for a top-k
@@ -106,6 +113,8 @@ struct LkSmem {                  // the large-k merge (inside SplitSmem's union)
   stream::SampleSmem s;          // tile masses and the locate() scratch
   double md[kHistBins];          // the row's bin masses
   unsigned long long hm[kHistBins];  // significand sums of one selection level
+  uint32_t tst[stream::kMaxTiles];  // per tile: where its gathered keys start,
+  uint32_t tcn[stream::kMaxTiles];  // and how many there are
   uint32_t nlist;                // keys gathered
   uint32_t res[8];
   double resd[4];
@@ -128,10 +137,9 @@ struct SplitSmem {
     stream::SampleSmem stream;   // streaming fallback
     stream::SelectSmem sel;      // streaming fallback of a selection
     stream::RadixSmem radix;     // exact fallback of top-k sampling
-    struct {                     // large k, a slice: count and significand-sum
-      uint32_t cnt[2][kHistBins];                 // histograms of bits [30:20],
-      unsigned long long mass[2][kHistBins];      // two copies (lane parity)
-    } lk;
+    struct {                     // large k, a slice: count and significand sum of
+      unsigned long long cm[2][kHistBins];  // each bin of bits [30:20] packed in one
+    } lk;                                   // word; two copies (lane parity)
     LkSmem lm;                   // large k, the merge
   } u;
   alignas(16) uint32_t hist[H1::kWords];
@@ -205,7 +213,13 @@ __device__ __forceinline__ void split_invalid(const SampleParams& P, const Split
 // (blog, 逆变换采样).  Rows whose boundary bins hold more values than the
 // gather keeps go to the exact passes of the streaming engine.
 constexpr uint32_t kLargeList = 0xFFFFFFFEu;  // header count of a slice that published histograms
+constexpr int kFinMinBlocks = 256;  // one work-group per compute unit on the whole chip
 constexpr uint32_t kLkGather = 16384;         // keys the merge gathers (LDS)
+// A slice's bin word: the count above this bit, the significand sum below
+// (a slice holds at most 10 vectors per thread, a copy half of them, each
+// significand below 2^24: sums below 2^44, counts below 2^20).
+constexpr int kLkCountShift = 44;
+static_assert(10 * 4 * kBlock / 2 <= (1 << 20) && 64 - kLkCountShift >= 20, "packed bin words");
 
 
 // Inside the keys x of bin `bin` (x >> 20 == bin) with x >= cut: the largest
@@ -317,7 +331,7 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
   const int tid = threadIdx.x, lane = lane_id(), wave = uwave();
   LkSmem& lm = sm.u.lm;
   uint32_t* keys = reinterpret_cast<uint32_t*>(sm.full);
-  static_assert(sizeof(sm.full) >= kLkGather * 4, "gathered keys fit full[]");
+  static_assert(sizeof(sm.full) >= (kLkGather + kWave) * 4, "gathered keys (+ dummies) fit full[]");
   // the row's histograms: counts into the padded LDS histogram, masses as
   // float64 (each bin's integer sum times its power of two)
   for (int b = tid; b < kHistBins; b += kBlock) {
@@ -339,11 +353,17 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     uint32_t bk, above, total, nbk;
     wave_find<kHistBins>(sm.hist, (uint32_t)k, bk, above, total, &nbk);
     const bool all = total < (uint32_t)k;  // every value kept by top-k
-    // masses above b_k (the top-k set's certain part), of b_k, of the row
+    // masses above b_k (the top-k set's certain part), of b_k, of the row;
+    // lane l sums the 32 bins of chunk 63 - l (one conflict-free row of the
+    // column layout per step, all reads independent)
+    const int ch = kWave - 1 - lane;
     double mab = 0.0, mtot = 0.0;
-    for (int b = lane; b < kHistBins; b += kWave) {
-      mab += b > (int)bk ? lm.md[md_at((uint32_t)b)] : 0.0;
-      mtot += lm.md[md_at((uint32_t)b)];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const uint32_t b = (uint32_t)(ch * 32 + q);
+      const double m = lm.md[md_at(b)];
+      mtot += m;
+      mab += b > bk ? m : 0.0;
     }
     mab = wave_sum(mab);
     mtot = wave_sum(mtot);
@@ -371,7 +391,9 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     }
     // keys to gather: bin b_k (unless every value is kept) and [plo, phi]
     uint32_t n = 0u;
-    for (int b = lane; b < kHistBins; b += kWave) {
+#pragma unroll
+    for (int q = 0; q < kHistBins / kWave; ++q) {
+      const int b = lane + q * kWave;
       const bool g = (!all && b == (int)bk) || (b >= (int)plo && b <= (int)phi);
       n += g ? sm.hist[H1::at((uint32_t)b)] : 0u;
     }
@@ -391,43 +413,68 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
   const uint32_t bk = lm.res[0], above = lm.res[1], plo = lm.res[3], phi = lm.res[4];
   const bool all = lm.res[2] != 0u;
   if (lm.res[5] > kLkGather) return kFallback;  // block-uniform
-  // gather: one pass over the row (thread t the vectors t, t + 1024, ...,
-  // eight loads in flight), one slot reservation per wave and batch
+  // One pass over the row, a wave per tile of 2048 values (eight 16-byte
+  // loads per lane).  The keys of the gathered bins go to keys[], each tile's in
+  // one block (lane order); the values above every gathered bin are kept
+  // whatever tau turns out to be (tau lies in a gathered bin), so their mass
+  // per tile is summed now (values below the gathered bins are below tau
+  // and never kept).
   const stream::RowRef r{as_global(P.probs + (int64_t)row * P.vocab), P.vocab, P.vec_ok != 0};
   const int n_tiles = (P.vocab + stream::kTile - 1) / stream::kTile;
-  const int nvec4 = (P.vocab + 3) / 4;
-  constexpr int kGB = 8;
-  for (int f0 = tid; f0 - tid < nvec4; f0 += kBlock * kGB) {  // block-uniform bound
-    float vt[kGB][4];
-    stream::load4_batch<kGB>(r, [&](int u) { return 4ll * min(f0 + u * kBlock, nvec4 - 1); }, vt);
-    uint32_t cnt = 0u;
-    uint32_t gm = 0u;  // bit 4u + e: value e of load u is gathered
+  const uint32_t gtop = all ? phi : max(phi, bk);     // the highest gathered bin
+  const uint32_t cert = ((gtop + 1u) << 20) - 1u;     // keys above: kept
+  // gathered: keys in [lo1, lo1 + w1) (bins plo..phi) or [lo2, lo2 + w2) (bin b_k)
+  const uint32_t lo1 = plo << 20, w1 = (phi - plo + 1u) << 20;
+  const uint32_t lo2 = bk << 20, w2 = all ? 0u : 1u << 20;
+  constexpr int kC = stream::kTileChunks;
+  auto tile_load = [&](int t, float (&vt)[kC][4]) {
+    const int64_t tb = (int64_t)t * stream::kTile;
+    stream::load4_batch<kC, false>(r, [&](int q) { return tb + q * (kWave * 4) + lane * 4; }, vt);
+  };
+  auto tile_take = [&](int t, const float (&vt)[kC][4]) {
+    const int64_t tb = (int64_t)t * stream::kTile;
+    double cs = 0.0;
+    uint32_t cnt = 0u, gm = 0u;  // bit 4q + e: value e of load q is gathered
 #pragma unroll
-    for (int u = 0; u < kGB; ++u) {
-      const int64_t idx = 4ll * (f0 + u * kBlock);
+    for (int q = 0; q < kC; ++q) {
+      const int64_t idx = tb + q * (kWave * 4) + lane * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t b = min(bits_of(vt[u][e]) >> 20, (uint32_t)(kHistBins - 1));
-        const bool g = f0 + u * kBlock < nvec4 && idx + e < P.vocab &&
-                       ((!all && b == bk) || (b >= plo && b <= phi));
-        gm |= g ? 1u << (4 * u + e) : 0u;
+        const uint32_t x = bits_of(vt[q][e]);
+        const bool in = idx + e < P.vocab;
+        const bool g = in && (x - lo1 < w1 || x - lo2 < w2);
+        cs += (in && x > cert) ? (double)vt[q][e] : 0.0;
+        gm |= g ? 1u << (4 * q + e) : 0u;
         cnt += g ? 1u : 0u;
       }
     }
+    cs = wave_sum(cs);
     const uint32_t incl = wave_incl_scan(cnt);
+    const uint32_t tot = lane63(incl);
     uint32_t base = 0u;
-    if (lane == kWave - 1 && incl > 0u) base = atomicAdd(&lm.nlist, incl);
+    if (lane == kWave - 1 && tot > 0u) base = atomicAdd(&lm.nlist, tot);
     base = lane_value(base, kWave - 1);
+    // every value stored, the others into this lane's dummy slot past the keys
     uint32_t pos = base + incl - cnt;
 #pragma unroll
-    for (int u = 0; u < kGB; ++u) {
+    for (int q = 0; q < kC; ++q) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (!((gm >> (4 * u + e)) & 1u)) continue;
-        if (pos < kLkGather) keys[pos] = bits_of(vt[u][e]);
-        ++pos;
+        const bool g = (gm >> (4 * q + e)) & 1u;
+        keys[g && pos < kLkGather ? pos : kLkGather + (uint32_t)lane] = bits_of(vt[q][e]);
+        pos += g ? 1u : 0u;
       }
     }
+    if (lane == 0) {
+      lm.s.tm[1][t] = cs;
+      lm.tst[t] = base;
+      lm.tcn[t] = tot;
+    }
+  };
+  for (int t = wave; t < n_tiles; t += kWaves) {  // wave-uniform
+    float vt[kC][4];
+    tile_load(t, vt);
+    tile_take(t, vt);
   }
   __syncthreads();
   const uint32_t n = min(lm.nlist, kLkGather);
@@ -481,35 +528,20 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
                             : tk;
     tau = max(tau, tp);
   }
-  // the kept mass of every tile (2048 values: a wave's 64 vectors of one
-  // load lie in one tile, eight waves cover it; their partial sums go to
-  // fixed slots and are added in order), then one draw (rounds = 1: the
-  // blog's loop started just below tau, where every draw is accepted)
+  // the kept mass of every tile: the part above the gathered bins, plus the
+  // tile's gathered values >= tau (lane order inside the tile's block, fixed
+  // association), then one draw (rounds = 1: the blog's loop started just
+  // below tau, where every draw is accepted)
   const float low = __uint_as_float(tau - 1u);
-  double* part = reinterpret_cast<double*>(sm.full);  // [tile][8], the keys are done with
-  static_assert(sizeof(sm.full) >= stream::kMaxTiles * 8 * sizeof(double), "tile partials");
-  __syncthreads();
-  for (int f0 = tid; f0 - tid < nvec4; f0 += kBlock * kGB) {  // block-uniform bound
-    float vt[kGB][4];
-    stream::load4_batch<kGB>(r, [&](int u) { return 4ll * min(f0 + u * kBlock, nvec4 - 1); }, vt);
-#pragma unroll
-    for (int u = 0; u < kGB; ++u) {
-      const int f = f0 + u * kBlock;
-      double sv = 0.0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sv += (f < nvec4 && vt[u][e] > low) ? (double)vt[u][e] : 0.0;
-      sv = wave_sum(sv);
-      const int fw = f - lane;  // the wave's first vector of this load
-      if (lane == 0 && fw < nvec4) part[(fw >> 9) * 8 + ((fw >> 6) & 7)] = sv;
+  for (int t = wave; t < n_tiles; t += kWaves) {
+    const uint32_t t0 = lm.tst[t], tn = lm.tcn[t];
+    double us = 0.0;
+    for (uint32_t j = (uint32_t)lane; j < tn; j += kWave) {
+      const uint32_t x = keys[min(t0 + j, kLkGather - 1u)];
+      us += x >= tau ? (double)__uint_as_float(x) : 0.0;
     }
-  }
-  __syncthreads();
-  for (int t = tid; t < n_tiles; t += kBlock) {
-    double z = 0.0;
-    const int nw = min(8, ((nvec4 - t * 512) + 63) / 64);  // waves that covered tile t
-    for (int q = 0; q < nw; ++q) z += part[t * 8 + q];
-    lm.s.tm[0][t] = z;
+    us = wave_sum(us);
+    if (lane == 0) lm.s.tm[0][t] = lm.s.tm[1][t] + us;
   }
   __syncthreads();
   if (wave == 0) {
@@ -522,6 +554,77 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
   const int tok = stream::locate(r, lm.s.tm[0], n_tiles, T, low, lm.s);
   if (threadIdx.x == 0) stream::write_sample(P, i, tok, tok >= 0 ? 1 : 0);
   return kDone;
+}
+
+// A finishing work-group (see SplitParams::fin).  Every work-group of the
+// slices comes before it in the grid and the dispatcher starts work-groups
+// in grid order, so the slices it waits for are running or done and the
+// wait ends; it is bounded all the same (S.spin), and a finisher that gives
+// up samples the output with the exact streaming passes instead.  Either
+// way it takes the output's W arrivals off the counter and advances the
+// generation, so the counter is back at zero once every slice has arrived
+// (before the next launch on the stream starts).
+template <int OP>
+__device__ __forceinline__ int large_k_finish(const SampleParams& P, const SplitParams& S,
+                                              SplitSmem& sm, int& out_i) {
+  constexpr bool kTopPPart = OP == kOpTopKTopP || OP == kOpTopKTopPJoint;
+  const int W = S.W;
+  const int b = (int)blockIdx.x - S.nsb, xcd = b & 7, li = (b >> 3) * 8 + xcd;
+  if (li >= S.n_out) return kDone;
+  const int i = S.out0 + li;
+  out_i = i;
+  const int lane = lane_id(), wave = uwave();
+  const int row = P.indices ? as_global(P.indices)[i] : i;
+  const bool row_ok = row >= 0 && row < P.rows;
+  const int k = as_global(P.top_k_arr)[i];
+  const float pp = kTopPPart ? (P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p) : 0.0f;
+  // the slices' own test: any other output was answered by its slices
+  if (!(k > kSplitKCap && row_ok && !(kTopPPart && isnan(pp)))) return kDone;
+  const gptr<uint32_t> ctr = as_global(S.ctr + li);
+  if (threadIdx.x == 0) {
+    int ok = 0;
+    if (S.spin != 0ull) {  // (a limit of zero, a test setting, gives up at once)
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        const uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int32_t)c >= W) {
+          ok = 1;
+          break;
+        }
+        if (__builtin_amdgcn_s_memrealtime() - t0 >= S.spin) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    sm.flag = ok;
+  }
+  __syncthreads();
+  const bool arrived = sm.flag != 0;
+  if (wave == 0) {
+    // the headers (each written before its slice arrived)
+    const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + (lane & (W - 1))) * kHdrWords);
+    const bool mine = arrived && lane < W;
+    const uint32_t hc = mine ? __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    const uint32_t hg = mine ? __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    const uint32_t hx = mine ? __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    const uint32_t hb = mine ? __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    const uint32_t mygen = __hip_atomic_load(as_global(S.gen + li), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool foreign =
+        __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull;
+    const bool anybad = __ballot(mine && hb != 0u) != 0ull;
+    if (lane == 0) {
+      __hip_atomic_fetch_sub(ctr, (uint32_t)W, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.res[0] = !arrived || foreign ? 2u : anybad ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t st = sm.res[0];
+  __syncthreads();
+  if (st == 1u) {
+    if (threadIdx.x == 0) stream::write_sample(P, i, -1, 0);
+    return kDone;
+  }
+  return st == 0u ? kLargeKMerge : kFallback;
 }
 
 template <int KIND, int OP, int NV>
@@ -542,7 +645,12 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   const int W = S.W;
   const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
   const int li = (local / W) * 8 + xcd;  // the W slices of an output share b % 8
-  const int s = local % W;
+  // The dispatcher hands an XCD's work-groups to its shader engines in turn
+  // and waits, in order, for a compute unit of the engine whose turn it is.
+  // Without the rotation slice s of every output would land on engine s % 4,
+  // and the long-running last arrivers (often the same slice index) would
+  // fill one engine while the others idle and every later work-group waits.
+  const int s = (local % W + local / W) % W;
   if (li >= S.n_out) return kDone;
   const int i = S.out0 + li;
   out_i = i;
@@ -603,6 +711,104 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // takes it (t = (z - m) * (1 / T) in float64)
   const float temp = kLogits ? (P.temp_arr ? t_raw : P.temp) : 1.0f;
   const double itemp = kLogits ? 1.0 / (double)temp : 1.0;
+
+  // ---- large k: histograms instead of candidate lists (see large_k_merge).
+  // Decided as soon as the parameters arrive, before the landing loop, so
+  // that this path and the candidate path never hold their registers at once.
+  constexpr bool kLargeK = KIND == kKindSample &&
+                           (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint);
+  if (kLargeK && W > 1 && k > kSplitKCap && row_ok && !(kTopPPart && isnan(pp))) {
+    auto& lk = sm.u.lk;
+    for (int q = tid; q < kHistBins; q += kBlock) lk.cm[0][q] = lk.cm[1][q] = 0ull;
+    uint32_t gen = 0u;
+    if (wave == 0 && lane == 0)
+      gen = __hip_atomic_load(as_global(S.gen + li), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int cp = lane & 1;
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (j + kInFlight < NV) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + kInFlight);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool in = tid + j * kBlock < nvec;
+      // one vector at a time (the compiler would otherwise work ahead on
+      // all of them and run out of registers)
+      float4 x = v[j];
+      asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+      const uint32_t k4[4] = {bits_of(x.x), bits_of(x.y), bits_of(x.z), bits_of(x.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!in) continue;
+        mx = max(mx, k4[e]);
+        const uint32_t b = min(k4[e] >> 20, (uint32_t)(kHistBins - 1));
+        atomicAdd(&lk.cm[cp][b], (1ull << kLkCountShift) | stream::radix_sig(k4[e]));
+      }
+    }
+    mx = wave_max(mx);
+    if (lane == 0) sm.wmax[wave] = mx;
+    __syncthreads();
+    const gptr<uint64_t> dst = as_global(S.list + ((int64_t)li * W + s) * kListMax);
+    for (int q = tid; q < kHistBins; q += kBlock) {
+      const unsigned long long a = lk.cm[0][q], c = lk.cm[1][q];
+      constexpr unsigned long long kM = (1ull << kLkCountShift) - 1ull;
+      dst[q] = (a & kM) + (c & kM);
+      ((gptr<uint32_t>)(dst + kHistBins))[q] = (uint32_t)((a >> kLkCountShift) + (c >> kLkCountShift));
+    }
+    if (tid == 0) {
+      uint32_t smax = 0u;
+      for (int w = 0; w < kWaves; ++w) smax = max(smax, sm.wmax[w]);
+      const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + s) * kHdrWords);
+      h[0] = 0u;
+      h[1] = kLargeList;
+      h[2] = smax;
+      h[3] = gen;
+      h[4] = xcc_id();
+      h[5] = smax >= 0x7F800000u ? 1u : 0u;  // a sign bit, an inf or a NaN
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (S.fin) {  // the output's finishing work-group merges
+      if (tid == 0)
+        __hip_atomic_fetch_add(as_global(S.ctr + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return kDone;
+    }
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(as_global(S.ctr + li), 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      sm.flag = (old == (uint32_t)(W - 1));
+    }
+    __syncthreads();
+    if (!sm.flag) return kDone;
+    // the last slice: the headers (all written before their arrivals)
+    if (wave == 0) {
+      const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + (lane & (W - 1))) * kHdrWords);
+      const uint32_t hc = __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hb = __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool mine = lane < W;
+      const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
+      const bool foreign =
+          __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull;
+      const bool anybad = __ballot(mine && hb != 0u) != 0ull;
+      if (lane == 0) {
+        __hip_atomic_store(as_global(S.ctr + li), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.res[0] = foreign ? 2u : anybad ? 1u : 0u;
+      }
+    }
+    __syncthreads();
+    if (sm.res[0] == 1u) {
+      split_invalid<KIND>(P, S, Q, i, li);
+      return kDone;
+    }
+    if (sm.res[0] == 2u) return kFallback;
+    return kLargeKMerge;
+  }
 
   // while the slice is in flight: clear the histogram; wave 0 reads the
   // row's generation (used only when the slice publishes).  Nothing here
@@ -726,83 +932,6 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
   // output decides alike)
   const bool ok = row_ok && k > 0 && (!kTopPPart || !isnan(pp)) &&
                   (!kLogits || (temp > 0.0f && temp != __builtin_inff()));
-  constexpr bool kLargeK = KIND == kKindSample &&
-                           (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint);
-  if (kLargeK && ok && k > kSplitKCap && W > 1) {
-    // ---- large k: histograms instead of candidate lists (see large_k_merge)
-    auto& lk = sm.u.lk;
-    __syncthreads();  // every wave's staging stores (same LDS) and maxima are done
-    for (int q = tid; q < kHistBins; q += kBlock) {
-      lk.cnt[0][q] = lk.cnt[1][q] = 0u;
-      lk.mass[0][q] = lk.mass[1][q] = 0ull;
-    }
-    __syncthreads();
-    const int cp = lane & 1;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const bool in = tid + j * kBlock < nvec;
-      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (!in) continue;
-        const uint32_t b = min(k4[e] >> 20, (uint32_t)(kHistBins - 1));
-        atomicAdd(&lk.cnt[cp][b], 1u);
-        atomicAdd(&lk.mass[cp][b], (unsigned long long)stream::radix_sig(k4[e]));
-      }
-    }
-    __syncthreads();
-    const gptr<uint64_t> dst = as_global(S.list + ((int64_t)li * W + s) * kListMax);
-    for (int q = tid; q < kHistBins; q += kBlock) {
-      dst[q] = lk.mass[0][q] + lk.mass[1][q];
-      ((gptr<uint32_t>)(dst + kHistBins))[q] = lk.cnt[0][q] + lk.cnt[1][q];
-    }
-    if (tid == 0) {
-      uint32_t smax = 0u;
-      for (int w = 0; w < kWaves; ++w) smax = max(smax, sm.wmax[w]);
-      const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + s) * kHdrWords);
-      h[0] = 0u;
-      h[1] = kLargeList;
-      h[2] = smax;
-      h[3] = gen;
-      h[4] = xcc_id();
-      h[5] = smax >= 0x7F800000u ? 1u : 0u;  // a sign bit, an inf or a NaN
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(as_global(S.ctr + li), 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-      sm.flag = (old == (uint32_t)(W - 1));
-    }
-    __syncthreads();
-    if (!sm.flag) return kDone;
-    // the last slice: the headers (all written before their arrivals)
-    if (wave == 0) {
-      const gptr<uint32_t> h = as_global(S.hdr + ((int64_t)li * W + (lane & (W - 1))) * kHdrWords);
-      const uint32_t hc = __hip_atomic_load(h + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t hg = __hip_atomic_load(h + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t hx = __hip_atomic_load(h + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t hb = __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool mine = lane < W;
-      const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
-      const bool foreign =
-          __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull;
-      const bool anybad = __ballot(mine && hb != 0u) != 0ull;
-      if (lane == 0) {
-        __hip_atomic_store(as_global(S.ctr + li), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm.res[0] = foreign ? 2u : anybad ? 1u : 0u;
-      }
-    }
-    __syncthreads();
-    if (sm.res[0] == 1u) {
-      split_invalid<KIND>(P, S, Q, i, li);
-      return kDone;
-    }
-    if (sm.res[0] == 2u) return kFallback;
-    return kLargeKMerge;
-  }
   if (!ok || k > kSplitKCap) {
     // no hand-off for this output: slice 0 answers alone
     if (s != 0) return kDone;
@@ -1355,8 +1484,19 @@ __global__ __launch_bounds__(kBlock) void split_kernel(SampleParams P, SplitPara
                                                        RenormParams RP, SelectParams Q) {
   __shared__ SplitSmem sm;
   int i = 0;
-  DSS_STAMP(0);
-  int mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
+  int mode = kDone;
+  bool finisher = false;
+  if constexpr (KIND == kKindSample &&
+                (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint)) {
+    if (S.fin && (int)blockIdx.x >= S.nsb) {
+      mode = large_k_finish<OP>(P, S, sm, i);
+      finisher = true;
+    }
+  }
+  if (!finisher) {
+    DSS_STAMP(0);
+    mode = split_sample<KIND, OP, NV>(P, S, Q, sm, i);
+  }
   if constexpr (KIND == kKindSample &&
                 (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint)) {
     if (mode == kLargeKMerge) mode = large_k_merge<OP>(P, S, sm, i);
@@ -1439,8 +1579,18 @@ void launch_one(const SampleParams& p, const SplitParams& sp, const RenormParams
                 const SelectParams& q, hipStream_t s, const LaunchEvents& ev, bool first,
                 bool last) {
   const int groups = (sp.n_out + 7) / 8;
-  const dim3 grid((unsigned)(groups * 8 * sp.W)), block(kBlock);
-  launch_kernel(split_kernel<KIND, OP, NV>, grid, block, s, ev, first, last, p, sp, rp, q);
+  SplitParams S = sp;
+  S.nsb = groups * 8 * sp.W;
+  // finishing work-groups: only where an output's k is read per output (it
+  // may exceed the cap) and the slices alone take more than one work-group
+  // per compute unit, so that a merge holding a compute unit would keep
+  // slices waiting
+  constexpr bool kTopKOps = KIND == kKindSample &&
+                            (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint);
+  S.fin = kTopKOps && p.top_k_arr != nullptr && sp.W > 1 && S.nsb > kFinMinBlocks ? 1 : 0;
+  S.spin = spin_limit_ticks();
+  const dim3 grid((unsigned)(S.nsb + (S.fin ? groups * 8 : 0))), block(kBlock);
+  launch_kernel(split_kernel<KIND, OP, NV>, grid, block, s, ev, first, last, p, S, rp, q);
 }
 
 template <int KIND, int OP>
@@ -1518,6 +1668,9 @@ SplitParams split_params(const SplitPlan& plan, void* workspace) {
   char* ws = static_cast<char*>(workspace);
   const size_t ch = (size_t)plan.chunk;
   SplitParams sp;
+  sp.fin = 0;
+  sp.nsb = 0;
+  sp.spin = 0ull;
   sp.W = plan.W;
   sp.wlog = 0;
   while ((1 << sp.wlog) < plan.W) ++sp.wlog;

@@ -27,19 +27,32 @@ struct RowRef {
 // r.vec, which every lane shares: made per group and per lane, the two kinds
 // of load land in the same registers from two arms and the compiler waits
 // for each load before the next one is issued.
-template <int N, class I>
+//
+// ZERO = false leaves the groups past the row end unspecified (the caller
+// masks them), so that no instruction waits for the loads here: a caller can
+// issue the next batch before it uses this one.
+template <int N, bool ZERO = true, class I>
 __device__ __forceinline__ void load4_batch(const RowRef& r, I&& idx_of, float (&v)[N][4]) {
   if (r.vec) {
-    // V % 4 == 0: a group is whole or lies wholly past the row end
+    // V % 4 == 0: a group is whole or lies wholly past the row end.  All
+    // loads first (from an address inside the row), the zeros after: a
+    // select next to each load would make the compiler wait for it there.
 #pragma unroll
     for (int u = 0; u < N; ++u) {
       const int64_t idx = idx_of(u);
-      const bool in = idx < r.V;
-      const float4 q = load_f4((gptr<const float4>)(r.x + (in ? idx : 0)));
-      v[u][0] = in ? q.x : 0.0f;
-      v[u][1] = in ? q.y : 0.0f;
-      v[u][2] = in ? q.z : 0.0f;
-      v[u][3] = in ? q.w : 0.0f;
+      const float4 q = load_f4((gptr<const float4>)(r.x + (idx < r.V ? idx : 0)));
+      v[u][0] = q.x;
+      v[u][1] = q.y;
+      v[u][2] = q.z;
+      v[u][3] = q.w;
+    }
+    if (ZERO) {
+#pragma unroll
+      for (int u = 0; u < N; ++u) {
+        const bool in = idx_of(u) < r.V;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[u][e] = in ? v[u][e] : 0.0f;
+      }
     }
   } else {
 #pragma unroll
