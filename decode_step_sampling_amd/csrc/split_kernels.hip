@@ -432,21 +432,23 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     stream::load4_batch<kC, false>(r, [&](int q) { return tb + q * (kWave * 4) + lane * 4; }, vt);
   };
   auto tile_take = [&](int t, const float (&vt)[kC][4]) {
-    const int64_t tb = (int64_t)t * stream::kTile;
+    // value e of load q is inside the row when q * 256 + e < lim
+    const int lim = min(P.vocab - t * stream::kTile, stream::kTile) - lane * 4;
     double cs = 0.0;
     uint32_t cnt = 0u, gm = 0u;  // bit 4q + e: value e of load q is gathered
 #pragma unroll
     for (int q = 0; q < kC; ++q) {
-      const int64_t idx = tb + q * (kWave * 4) + lane * 4;
+      float gs = 0.0f;  // a group's kept values in float32, then added in float64
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t x = bits_of(vt[q][e]);
-        const bool in = idx + e < P.vocab;
+        const bool in = q * (kWave * 4) + e < lim;
         const bool g = in && (x - lo1 < w1 || x - lo2 < w2);
-        cs += (in && x > cert) ? (double)vt[q][e] : 0.0;
+        gs += (in && x > cert) ? vt[q][e] : 0.0f;
         gm |= g ? 1u << (4 * q + e) : 0u;
         cnt += g ? 1u : 0u;
       }
+      cs += (double)gs;
     }
     cs = wave_sum(cs);
     const uint32_t incl = wave_incl_scan(cnt);
@@ -454,14 +456,17 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     uint32_t base = 0u;
     if (lane == kWave - 1 && tot > 0u) base = atomicAdd(&lm.nlist, tot);
     base = lane_value(base, kWave - 1);
-    // every value stored, the others into this lane's dummy slot past the keys
+    // every value stored, the others into this lane's dummy slot past the
+    // keys (the gathered ones number exactly n <= kLkGather, counted by the
+    // histograms, so their positions stay below kLkGather)
     uint32_t pos = base + incl - cnt;
 #pragma unroll
     for (int q = 0; q < kC; ++q) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool g = (gm >> (4 * q + e)) & 1u;
-        keys[g && pos < kLkGather ? pos : kLkGather + (uint32_t)lane] = bits_of(vt[q][e]);
+        keys[min(g ? pos : kLkGather + (uint32_t)lane, kLkGather + (uint32_t)lane)] =
+            bits_of(vt[q][e]);
         pos += g ? 1u : 0u;
       }
     }
