@@ -66,7 +66,7 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
       (top_k > dss::kSplitKCapHost || (int64_t)top_k * plan.W > dss::kSplitScalarKW))
     plan = dss::SplitPlan{0, 0, 0, 0, 0, 0};
   const dss::SplitPlan rplan = plan.W > 0 ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
-                                          : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok);
+                                          : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok, true);
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   if (check_only) return DSS_OK;

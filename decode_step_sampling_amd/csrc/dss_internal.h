@@ -158,7 +158,10 @@ constexpr int kSplitChunk = 2048;
 // Resident-slice engine (plain, top-p and min-p sampling; top-p
 // renormalisation): W work-groups per output on one XCD keep the row in
 // registers and meet at row barriers.  W == 0 means "not eligible".
-SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok);
+// sample: the plan of a sampling call (plain, top-p and min-p may then hold
+// 64 values per thread); renormalisation and the softmax keep at most 48
+SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok,
+                        bool sample = false);
 hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan& plan,
                                   void* workspace, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_resident_renorm(const RenormParams& p, const SplitPlan& plan, void* workspace,

@@ -70,6 +70,7 @@ namespace {
 
 constexpr int kRMaxW = 16;
 constexpr int kRMaxNv = 12;  // 16-byte loads per thread (48 values; more run out of registers)
+constexpr int kRWideNv = 16;  // plain, top-p and min-p sampling: 64 values per thread
 constexpr int kRB1 = 1024;   // level 1: bits [30:21]
 constexpr int kRB2 = 2048;   // level 2: bits [20:10]
 constexpr int kRB3 = 1024;   // level 3: bits [9:0]
@@ -1319,15 +1320,22 @@ hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const Sp
     case 10:
       if constexpr (kTopKOp) return hipErrorInvalidValue;
       else return launch_res_one<KIND, OP, 10>(p, rp, plan, ws, s, ev);
-    default:
+    case 12:
       if constexpr (kTopKOp) return hipErrorInvalidValue;
       else return launch_res_one<KIND, OP, 12>(p, rp, plan, ws, s, ev);
+    case 16:  // plain, top-p and min-p sampling only (plan_resident's wide plans)
+      if constexpr (KIND == kResSample && (OP == kOpNone || OP == kOpMinP || OP == kOpTopP))
+        return launch_res_one<KIND, OP, 16>(p, rp, plan, ws, s, ev);
+      else return hipErrorInvalidValue;
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok) {
+SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok,
+                        bool sample) {
   SplitPlan plan{0, 0, 0, 0, 0, 0};
   if (op != kOpNone && op != kOpTopP && op != kOpMinP && op != kOpTopK && op != kOpTopKTopP)
     return plan;
@@ -1336,8 +1344,13 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
   // values a slice holds: 48 per thread, 32 for the top-k searches
   const bool topk = op == kOpTopK || op == kOpTopKTopP;
   const int kMaxSlice = (topk ? 8 : kRMaxNv) * 4 * kBlock;
-  const int wmin = (vocab + kMaxSlice - 1) / kMaxSlice;
+  int wmin = (vocab + kMaxSlice - 1) / kMaxSlice;
   if (wmin > kRMaxW) return plan;
+  // plain, top-p and min-p sampling keep few other values live and may hold
+  // 64 values per thread: half the slices, so twice the outputs per launch
+  // when a batch needs more than one launch
+  const bool wide = sample && (op == kOpNone || op == kOpMinP || op == kOpTopP);
+  if (wide) wmin = (vocab + kRWideNv * 4 * kBlock - 1) / (kRWideNv * 4 * kBlock);
   const int wt = (kResidentSlots + num_outputs - 1) / num_outputs;
   // W: a power of two, at least wmin, about 256 work-groups in all, no empty slice
   int W = 1;
@@ -1349,7 +1362,7 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
   }
   if (W < wmin) return plan;
   int nv = (L / 4 + kBlock - 1) / kBlock;
-  nv = nv <= 2 ? nv : nv <= 4 ? 4 : nv <= 8 ? 8 : nv <= 10 ? 10 : 12;
+  nv = nv <= 2 ? nv : nv <= 4 ? 4 : nv <= 8 ? 8 : nv <= 10 ? 10 : nv <= 12 ? 12 : kRWideNv;
   if (topk && nv > 8) return plan;
   plan.W = W;
   plan.L = L;
