@@ -62,10 +62,10 @@ def small():
 # token-exact
 # ----------------------------------------------------------------------------
 
+@pytest.mark.parametrize("n", [48, 4096])  # (48: the resident engine; 64 and more stream)
 @pytest.mark.parametrize("flags", FLAG_SETS)
-def test_plain_sampling_token_exact(small, flags):
+def test_plain_sampling_token_exact(small, flags, n):
     probs = small["probs"]
-    n = 4096
     idx = (np.arange(n) % probs.shape[0]).astype(np.int32)
     seed, offset = 987654321, 7
     s, v, r = dss.sampling_from_probs(small["P"], indices=gpu(idx), seed=seed, offset=offset,
