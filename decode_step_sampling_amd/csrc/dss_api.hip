@@ -65,14 +65,20 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   if (plan.W > 0 && !top_k_arr && (eop == dss::kOpTopK || eop == dss::kOpTopKTopP) &&
       (top_k > dss::kSplitKCapHost || (int64_t)top_k * plan.W > dss::kSplitScalarKW))
     plan = dss::SplitPlan{0, 0, 0, 0, 0, 0};
-  // plain sampling of 64 outputs or more: one work-group per output reading
-  // its row twice (tile masses, then one tile) keeps HBM busier than the
-  // resident engine's row barriers (172 outputs of V = 128256: 19 vs 40 us;
-  // 64 of V = 151936: 14 vs 16 us); fewer outputs leave most of the chip idle
-  const bool plain_streams = eop == dss::kOpNone && num_outputs >= 64;
-  const dss::SplitPlan rplan = plan.W > 0 || plain_streams
-                                   ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
-                                   : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok, true);
+  dss::SplitPlan rplan = plan.W > 0 ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
+                                    : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok, true);
+  // Plain and min-p sampling of a batch the resident engine would take in
+  // more than one launch: one work-group per output keeps HBM busier than
+  // launches that each wait at row barriers.  Plain sampling reads the row
+  // twice (tile masses, then one tile); min-p reads it for the tile maxima
+  // and again only where a tile holds a kept value (172 / 185 outputs of
+  // V = 128256: 19 / 27 us instead of 41 / 44 us).  Batches that fit one
+  // launch (up to 64 outputs of V = 151936) stay resident, where the chip's
+  // every compute unit shares each row.
+  const bool wide_stream = rplan.W > 0 && rplan.chunk < num_outputs &&
+                           (eop == dss::kOpNone || eop == dss::kOpMinP);
+  const bool minp_streams = wide_stream && eop == dss::kOpMinP;
+  if (wide_stream) rplan = dss::SplitPlan{0, 0, 0, 0, 0, 0};
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   if (check_only) return DSS_OK;
@@ -113,9 +119,10 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
       dss::launch_resident_repair(workspace, st) != hipSuccess)
     return DSS_ERR_HIP;
   const hipError_t e =
-      plan.W > 0    ? dss::launch_split_sample(eop, p, plan, workspace, st, ev)
-      : rplan.W > 0 ? dss::launch_resident_sample(eop, p, rplan, workspace, st, ev)
-                    : dss::launch_stream_sample(eop, p, st, ev);
+      plan.W > 0     ? dss::launch_split_sample(eop, p, plan, workspace, st, ev)
+      : rplan.W > 0  ? dss::launch_resident_sample(eop, p, rplan, workspace, st, ev)
+      : minp_streams ? dss::launch_stream_minp(p, st, ev)
+                     : dss::launch_stream_sample(eop, p, st, ev);
   return e == hipSuccess ? DSS_OK : DSS_ERR_HIP;
 }
 

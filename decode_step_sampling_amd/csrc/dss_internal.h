@@ -99,6 +99,9 @@ inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t s, const 
 // Streaming engine: one 1024-thread work-group per output (or row), every
 // pass reads the row from global memory.  Returns a hipError_t.
 hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s, const LaunchEvents& ev);
+// min-p sampling in two reads of each row (per-tile maxima first; tiles that
+// hold no kept value are not read again), one draw, rounds = 1
+hipError_t launch_stream_minp(const SampleParams& p, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_stream_renorm(int kind, const RenormParams& p, hipStream_t s,
                                 const LaunchEvents& ev);
 

@@ -376,6 +376,86 @@ __device__ __forceinline__ void write_sample(const SampleParams& P, int i, int t
 }
 
 
+// Min-p sampling of output i in two reads of the row (every thread of the
+// work-group calls): per-tile maxima and the row maximum M, then the kept
+// mass {x >= min_p * M} (the product exact in float64) of every tile whose
+// maximum reaches the threshold (the others hold nothing kept and are not
+// read again), one draw and the walk of one tile in index order.  This is
+// the blog's loop started just below the threshold, where the first draw
+// is accepted (rounds = 1); the pages' loop from low = 0 stays with
+// sample_row.
+__device__ __forceinline__ void sample_row_minp(const SampleParams& P, int i, SampleSmem& sm) {
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int row = P.indices ? as_global(P.indices)[i] : i;
+  const float mp = P.min_p_arr ? as_global(P.min_p_arr)[i] : P.min_p;
+  if (!(row >= 0 && row < P.rows) || isnan(mp)) {  // block-uniform
+    if (threadIdx.x == 0) write_sample(P, i, -1, 0);
+    return;
+  }
+  const uint64_t seed = P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
+  const uint64_t offset = P.offset_arr ? as_global(P.offset_arr)[i] : P.offset;
+  const uint64_t sid = P.seed_arr ? 0ull : (uint64_t)i;
+  const RowRef r{as_global(P.probs + (int64_t)row * P.vocab), P.vocab, P.vec_ok != 0};
+  const int n_tiles = (P.vocab + kTile - 1) / kTile;
+
+  // pass 0: the maximum of every tile (bits; a sign bit, inf or NaN shows as
+  // a pattern >= 0x7F800000) into tm[1], the row's maximum
+  uint32_t mbits = 0u;
+  for (int t = wave; t < n_tiles; t += kWaves) {
+    const int64_t base = (int64_t)t * kTile;
+    float vt[kTileChunks][4];
+    load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
+    uint32_t tb = 0u;
+#pragma unroll
+    for (int q = 0; q < kTileChunks; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tb = max(tb, bits_of(vt[q][e]));
+    tb = wave_max(tb);
+    mbits = max(mbits, tb);
+    if (lane == 0) sm.tm[1][t] = tb < 0x7F800000u ? (double)__uint_as_float(tb) : 0.0;
+  }
+  Red red0 = red_zero();
+  red0.mx = mbits;
+  const uint32_t maxbits = block_reduce(red0, sm.red).mx;  // (its barriers publish tm[1])
+  // sign bit, inf or NaN anywhere, or nothing positive: invalid row
+  if (maxbits >= 0x7F800000u || maxbits == 0u) {
+    if (threadIdx.x == 0) write_sample(P, i, -1, 0);
+    return;
+  }
+  const double thr = (double)clamp01(mp) * (double)__uint_as_float(maxbits);
+  // pass 1: kept mass per tile, read only where the tile's maximum reaches thr
+  for (int t = wave; t < n_tiles; t += kWaves) {
+    double s = 0.0;
+    if (sm.tm[1][t] >= thr) {  // wave-uniform
+      const int64_t base = (int64_t)t * kTile;
+      float vt[kTileChunks][4];
+      load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
+#pragma unroll
+      for (int q = 0; q < kTileChunks; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += (double)vt[q][e] >= thr ? (double)vt[q][e] : 0.0;
+      s = wave_sum(s);
+    }
+    if (lane == 0) sm.tm[0][t] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const double z = tile_scan_total(sm.tm[0], n_tiles);
+    if (lane == 0) sm.bc_d[0] = z * draw_uniform(seed, offset, sid, 0u);
+  }
+  __syncthreads();
+  const double T = sm.bc_d[0];
+  __syncthreads();
+  // {x >= thr} = {x > low}: low is the float32 just below the smallest
+  // float32 >= thr (for thr = 0 the zeros, which carry no mass, are left out)
+  float f = (float)thr;
+  if ((double)f < thr) f = __uint_as_float(__float_as_uint(f) + 1u);
+  const float low = f > 0.0f ? __uint_as_float(__float_as_uint(f) - 1u) : 0.0f;
+  const int tok = locate(r, sm.tm[0], n_tiles, T, low, sm);
+  if (threadIdx.x == 0) write_sample(P, i, tok, tok >= 0 ? 1 : 0);
+}
+
 // Sample output i with the streaming engine; every thread of the
 // work-group must call this (it contains barriers).
 template <int OP>

@@ -30,6 +30,11 @@ __global__ __launch_bounds__(kBlock) void stream_sample_kernel(SampleParams P) {
   sample_row<OP>(P, blockIdx.x, sm);
 }
 
+__global__ __launch_bounds__(kBlock) void stream_minp_kernel(SampleParams P) {
+  __shared__ SampleSmem sm;
+  sample_row_minp(P, blockIdx.x, sm);
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kBlock) void stream_renorm_kernel(RenormParams P) {
   __shared__ RedSmem red;
@@ -70,6 +75,12 @@ hipError_t launch_stream_sample(int op, const SampleParams& p, hipStream_t s, co
       break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_minp(const SampleParams& p, hipStream_t s, const LaunchEvents& ev) {
+  const dim3 grid((unsigned)p.num_outputs), block(kBlock);
+  launch_kernel(stream_minp_kernel, grid, block, s, ev, true, true, p);
   return hipGetLastError();
 }
 

@@ -93,6 +93,34 @@ def test_plain_sampling_token_exact_full_vocab():
     assert np.array_equal(s, expect)
 
 
+@pytest.mark.parametrize("n", [48, 512])  # (48: the resident engine; 64 and more: two reads per row)
+def test_min_p_sampling_token_exact(n):
+    """Min-p draws the oracle's inverse-transform token over its kept set
+    {x >= min_p * max} in index order with the output's first draw, on
+    full-size rows with per-output min_p (some near 0, keeping much of the
+    row, some near 1)."""
+    w = si.renorm(rows=8)
+    probs = w["probs"]
+    rng = np.random.default_rng(11)
+    mp = rng.uniform(0.0, 0.3, size=n).astype(np.float32)
+    mp[::7] = np.float32(1e-4)
+    mp[3::7] = np.float32(1.0)
+    idx = (np.arange(n) % probs.shape[0]).astype(np.int32)
+    seeds = np.arange(77, 77 + n, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15)
+    offs = np.arange(n, dtype=np.uint64) * np.uint64(3)
+    s, v, r = dss.min_p_sampling_from_probs(gpu(probs), gpu(mp), indices=gpu(idx),
+                                            seed=u64(seeds), offset=u64(offs),
+                                            return_valid=True, return_rounds=True)
+    s, v, r = host(s), host(v), host(r)
+    assert (v == 1).all() and (r == 1).all()
+    for i in range(n):
+        row = probs[idx[i]]
+        valid, tau = ref.threshold(row, "min_p", min_p=mp[i])
+        assert valid
+        table = ref.CdfTable(row, ref.support_mask(row, tau))
+        assert s[i] == table.draw(ph.draw_bits53(int(seeds[i]), int(offs[i]), 0, 0)), (i, mp[i])
+
+
 @pytest.mark.parametrize("op", ["top_k", "top_p", "min_p", "top_k_top_p", "top_k_top_p_joint"])
 def test_rejection_loop_token_exact_from_zero(small, op):
     """From low = 0 the GPU loop and the oracle's step-by-step model of the
