@@ -332,72 +332,111 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
   LkSmem& lm = sm.u.lm;
   uint32_t* keys = reinterpret_cast<uint32_t*>(sm.full);
   static_assert(sizeof(sm.full) >= (kLkGather + kWave) * 4, "gathered keys (+ dummies) fit full[]");
-  // the row's histograms: counts into the padded LDS histogram, masses as
-  // float64 (each bin's integer sum times its power of two)
-  for (int b = tid; b < kHistBins; b += kBlock) {
-    unsigned long long m = 0ull;
-    uint32_t c = 0u;
+  // The row's histograms, thread t holding bins 2047 - 2t and 2046 - 2t:
+  // the exact integer masses into hm, then (one block scan from the top)
+  // suffix counts C[b] (values in bins >= b, C[2048] = 0, in full[]) and
+  // suffix masses M[b] (float64, fixed association, in md), so that every
+  // decision below is a lookup or a two-step ballot search.
+  uint32_t* sc = keys;  // [kHistBins + 1], free until the row pass
+  {
+    const uint32_t bh = (uint32_t)(kHistBins - 1 - 2 * tid), bl = bh - 1u;
+    unsigned long long mh = 0ull, ml = 0ull;
+    uint32_t ch = 0u, cl = 0u;
     for (int q = 0; q < W; ++q) {
       const gptr<const uint64_t> h = as_global(hbase + (size_t)q * kListMax);
-      m += __hip_atomic_load(h + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      c += __hip_atomic_load((gptr<const uint32_t>)(h + kHistBins) + b, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+      const gptr<const uint32_t> hc = (gptr<const uint32_t>)(h + kHistBins);
+      mh += __hip_atomic_load(h + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ml += __hip_atomic_load(h + bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ch += __hip_atomic_load(hc + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      cl += __hip_atomic_load(hc + bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    sm.hist[H1::at((uint32_t)b)] = c;
-    lm.md[md_at((uint32_t)b)] = ldexp((double)m, (int)max((uint32_t)b >> 3, 1u) - 150);
+    lm.hm[bh] = mh;
+    lm.hm[bl] = ml;
+    const double dh = ldexp((double)mh, (int)max(bh >> 3, 1u) - 150);
+    const double dl = ldexp((double)ml, (int)max(bl >> 3, 1u) - 150);
+    const uint32_t cp = ch + cl;
+    const double dp = dh + dl;
+    const uint32_t cin = wave_incl_scan(cp);
+    const double din = wave_incl_scan(dp);
+    if (lane == kWave - 1) {
+      sm.wcnt[wave] = cin;
+      sm.wz[wave] = din;
+    }
+    __syncthreads();
+    uint32_t cw = 0u;
+    double dw = 0.0;
+    for (int w2 = 0; w2 < wave; ++w2) {
+      cw += sm.wcnt[w2];
+      dw += sm.wz[w2];
+    }
+    const uint32_t cex = cw + cin - cp;
+    const double mtop = (dw + wave_excl_from_incl(din)) + dh;
+    sc[bh] = cex + ch;
+    sc[bl] = cex + cp;
+    lm.md[bh] = mtop;
+    lm.md[bl] = mtop + dl;
+    if (tid == 0) {
+      sc[kHistBins] = 0u;
+      lm.nlist = 0u;
+    }
   }
-  if (tid == 0) lm.nlist = 0u;
   __syncthreads();
   const float pc = stream::clamp01(pp);
-  if (wave == 0) {
-    uint32_t bk, above, total, nbk;
-    wave_find<kHistBins>(sm.hist, (uint32_t)k, bk, above, total, &nbk);
-    const bool all = total < (uint32_t)k;  // every value kept by top-k
-    // masses above b_k (the top-k set's certain part), of b_k, of the row;
-    // lane l sums the 32 bins of chunk 63 - l (one conflict-free row of the
-    // column layout per step, all reads independent)
-    const int ch = kWave - 1 - lane;
-    double mab = 0.0, mtot = 0.0;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const uint32_t b = (uint32_t)(ch * 32 + q);
-      const double m = lm.md[md_at(b)];
-      mtot += m;
-      mab += b > bk ? m : 0.0;
+  // M[b], with M[2048] = 0
+  auto msuf = [&](uint32_t b) { return b < (uint32_t)kHistBins ? lm.md[b] : 0.0; };
+  // the largest bin b >= lo whose suffix mass reaches need (and is positive);
+  // without one, the lowest bin holding mass.  One wave.
+  auto mfind = [&](double need, uint32_t lo) -> uint32_t {
+    const uint32_t c0 = max((uint32_t)lane * 32u, lo);
+    const double m0 = c0 < (uint32_t)kHistBins ? lm.md[c0] : 0.0;
+    const uint64_t m1 = __ballot((uint32_t)lane * 32u + 31u >= lo && m0 >= need && m0 > 0.0);
+    if (m1 != 0ull) {
+      const uint32_t L = (uint32_t)last_lane(m1);
+      const uint32_t b = L * 32u + (uint32_t)lane;
+      const double mb = lane < 32 ? lm.md[b] : 0.0;
+      const uint64_t m2 = __ballot(lane < 32 && b >= lo && mb >= need && mb > 0.0);
+      return L * 32u + (uint32_t)last_lane(m2);
     }
-    mab = wave_sum(mab);
-    mtot = wave_sum(mtot);
-    const double mbk = lm.md[md_at(bk)];
+    // lowest bin with mass: bin 0 if it holds some, else the lowest
+    // non-empty bin above it (every value there is positive)
+    if (lm.hm[0] > 0ull) return 0u;
+    const uint32_t need_c = sc[1];
+    const uint64_t n1 = __ballot(sc[(uint32_t)lane * 32u] >= need_c);
+    const uint32_t L = (uint32_t)last_lane(n1);
+    const uint64_t n2 = __ballot(lane < 32 && sc[L * 32u + (uint32_t)lane] >= need_c);
+    return max(L * 32u + (uint32_t)last_lane(n2), 1u);
+  };
+  if (wave == 0) {
+    const uint32_t total = sc[0];
+    const bool all = total < (uint32_t)k;  // every value kept by top-k
+    // b_k: the largest bin whose suffix count reaches k
+    uint32_t bk = 0u;
+    if (!all) {
+      const uint64_t m1 = __ballot(sc[(uint32_t)lane * 32u] >= (uint32_t)k);
+      const uint32_t L = (uint32_t)last_lane(m1);
+      const uint64_t m2 = __ballot(lane < 32 && sc[L * 32u + (uint32_t)lane] >= (uint32_t)k);
+      bk = L * 32u + (uint32_t)last_lane(m2);
+    }
+    const uint32_t above = sc[bk + 1u];
+    // masses above b_k (the top-k set's certain part), of b_k (exact), of the row
+    const double mab = msuf(bk + 1u), mtot = msuf(0u);
+    const double mbk = ldexp((double)lm.hm[bk], (int)max(bk >> 3, 1u) - 150);
     // the bins the top-p cut can fall in, [plo, phi]
     uint32_t plo = bk, phi = bk;
     if (kTopPPart) {
-      const double zlo = kJoint ? mtot : (all ? mtot : mab);
-      const double zhi = kJoint ? mtot : (all ? mtot : mab + mbk);
-      uint32_t b1, b2;
-      double a1, a2;
-      // (b_k's mass left out for the top-k-first order: a target above the
-      // bins over b_k falls in b_k, md_find then reports a lower bin)
-      if (!kJoint && !all) lm.md[md_at(bk)] = 0.0;
-      md_find(lm.md, (double)pc * zlo, b1, a1);
-      md_find(lm.md, (double)pc * zhi, b2, a2);
-      if (!kJoint && !all) lm.md[md_at(bk)] = mbk;
       if (kJoint || all) {
-        phi = b1;
-        plo = b2;
+        plo = phi = mfind((double)pc * mtot, 0u);
       } else {
-        phi = (double)pc * zlo <= mab && mab > 0.0 ? max(b1, bk) : bk;
-        plo = (double)pc * zhi <= mab && mab > 0.0 ? max(b2, bk) : bk;
+        // the top-k set's mass Z_k lies in [mab, mab + mbk]; a target the
+        // bins above b_k reach falls above b_k, any other in b_k
+        const double tlo = (double)pc * mab, thi = (double)pc * (mab + mbk);
+        phi = tlo <= mab && mab > 0.0 ? max(mfind(tlo, bk + 1u), bk) : bk;
+        plo = thi <= mab && mab > 0.0 ? max(mfind(thi, bk + 1u), bk) : bk;
       }
     }
     // keys to gather: bin b_k (unless every value is kept) and [plo, phi]
-    uint32_t n = 0u;
-#pragma unroll
-    for (int q = 0; q < kHistBins / kWave; ++q) {
-      const int b = lane + q * kWave;
-      const bool g = (!all && b == (int)bk) || (b >= (int)plo && b <= (int)phi);
-      n += g ? sm.hist[H1::at((uint32_t)b)] : 0u;
-    }
-    n = wave_sum(n);
+    const uint32_t n = (sc[plo] - sc[phi + 1u]) +
+                       (!all && (bk < plo || bk > phi) ? sc[bk] - sc[bk + 1u] : 0u);
     if (lane == 0) {
       lm.res[0] = bk;
       lm.res[1] = above;
@@ -510,11 +549,17 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     // above b_k count fully, b_k with its values >= tau_k (top-k first)
     const double target = (double)pc * (kJoint ? lm.resd[1] : zk);
     if (wave == 0) {
-      if (!kJoint && !all) lm.md[md_at(bk)] = zk - lm.resd[0];
+      // (top-k first: the bins above b_k count fully, b_k with its values
+      // >= tau_k, so a target beyond the bins above b_k falls in b_k)
       uint32_t bp;
       double ab;
-      md_find(lm.md, target, bp, ab);
-      if (!kJoint && !all) bp = max(bp, bk);
+      const double mab = lm.resd[0];
+      if (!kJoint && !all) {
+        bp = target <= mab && mab > 0.0 ? max(mfind(target, bk + 1u), bk) : bk;
+      } else {
+        bp = mfind(target, 0u);
+      }
+      ab = bp == bk && !kJoint && !all ? mab : msuf(bp + 1u);
       if (lane == 0) {
         lm.res[6] = bp;
         lm.resd[3] = ab;
