@@ -226,43 +226,11 @@ static_assert(10 * 4 * kBlock / 2 <= (1 << 20) && 64 - kLkCountShift >= 20, "pac
 // key t such that the values >= t number (COUNT) or weigh (mass in units of
 // the bin's power of two) at least `need`; need is at most what the bin
 // holds there.  Two levels, bits [19:9] then [8:0]; every thread calls.
-// The row's bin masses are stored by column: bin b at (b mod 32) * 64 +
-// b / 32, so that lane l reading its 32 consecutive bins touches 64
-// consecutive words per read (no LDS bank conflicts).
-__device__ __forceinline__ uint32_t md_at(uint32_t b) { return (b & 31u) * 64u + (b >> 5); }
-
-// One wave: the largest bin b whose mass from the top, M(b) = sum of the
-// bins >= b, reaches `need` and is positive; above = M(b + 1).  If rounding
-// leaves every M(b) below need, the lowest bin with mass (mass_find of the
-// streaming engine, on the column layout).
-__device__ __forceinline__ void md_find(const double* md, double need, uint32_t& bin,
-                                        double& above) {
-  const int lane = lane_id();
-  const int c = kWave - 1 - lane;  // lane 0: the top chunk
-  double s = 0.0;
-#pragma unroll 8
-  for (int q = 31; q >= 0; --q) s += md[md_at((uint32_t)(c * 32 + q))];
-  const double incl = wave_incl_scan(s);
-  const double excl = wave_excl_from_incl(incl);
-  const uint64_t hit = __ballot(incl >= need && incl > 0.0);
-  const int L = hit ? first_lane(hit) : last_lane(__ballot(s > 0.0) | 1ull);
-  const bool fb = hit == 0ull;
-  const int cc = kWave - 1 - L;
-  const double ex = lane_value(excl, L);
-  const double m = lane < 32 ? md[md_at((uint32_t)(cc * 32 + 31 - lane))] : 0.0;
-  const double incl2 = wave_incl_scan(m) + ex;
-  const double sh = wave_excl_from_incl(incl2);
-  const double excl2 = lane == 0 ? ex : sh;
-  uint64_t hit2 = fb ? 0ull : __ballot(lane < 32 && incl2 >= need && incl2 > 0.0);
-  if (hit2 == 0ull) hit2 = 1ull << (63 - __clzll((long long)(__ballot(lane < 32 && m > 0.0) | 1ull)));
-  const int Q = first_lane(hit2);
-  bin = (uint32_t)(cc * 32 + 31 - Q);
-  above = lane_value(excl2, Q);
-}
-
+// The mass levels search suffix sums from the top, kept in md in plain
+// bin order.
 template <bool COUNT>
 __device__ uint32_t lk_select(const uint32_t* keys, uint32_t n, uint32_t bin, uint32_t cut,
-                              double need, uint32_t* hist, LkSmem& lm) {
+                              double need, uint32_t* hist, LkSmem& lm, double* wz) {
   const int tid = threadIdx.x, lane = lane_id(), wave = uwave();
   uint32_t s0 = 0u, s1 = 0u;
   for (int lev = 0; lev < 2; ++lev) {
@@ -283,9 +251,19 @@ __device__ uint32_t lk_select(const uint32_t* keys, uint32_t n, uint32_t bin, ui
       else atomicAdd(&lm.hm[q], (unsigned long long)stream::radix_sig(x));
     }
     __syncthreads();
-    if (!COUNT) {  // the sums as float64 (exact below 2^53) in the column layout
-      for (uint32_t q = (uint32_t)tid; q < (uint32_t)kHistBins; q += kBlock)
-        lm.md[md_at(q)] = (double)lm.hm[q];
+    if (!COUNT) {
+      // suffix sums from the top (thread t: sub-bins 2047 - 2t, 2046 - 2t),
+      // integers below 2^53 and so exact in float64 whatever the order
+      const uint32_t bh = (uint32_t)(kHistBins - 1 - 2 * tid), bl = bh - 1u;
+      const double vh = (double)lm.hm[bh], vl = (double)lm.hm[bl];
+      const double vin = wave_incl_scan(vh + vl);
+      if (lane == kWave - 1) wz[wave] = vin;
+      __syncthreads();
+      double vw = 0.0;
+      for (int w2 = 0; w2 < wave; ++w2) vw += wz[w2];
+      const double top = vw + wave_excl_from_incl(vin) + vh;
+      lm.md[bh] = top;
+      lm.md[bl] = top + vl;
       __syncthreads();
     }
     // the largest sub-bin whose suffix (from the top) reaches need
@@ -297,7 +275,17 @@ __device__ uint32_t lk_select(const uint32_t* keys, uint32_t n, uint32_t bin, ui
         wave_find<kHistBins>(hist, (uint32_t)need, found, ac, tot);
         above = (double)ac;
       } else {
-        md_find(lm.md, need, found, above);
+        // (with a positive suffix; if none reaches need, the lowest sub-bin
+        // holding mass: the largest whose suffix is still the whole total)
+        const double m0 = lm.md[(uint32_t)lane * 32u];
+        const uint64_t m1 = __ballot(m0 >= need && m0 > 0.0);
+        const double tgt = m1 != 0ull ? need : lm.md[0];
+        const uint64_t mm = m1 != 0ull ? m1 : __ballot(m0 >= tgt);
+        const uint32_t L = (uint32_t)last_lane(mm | 1ull);
+        const double mb = lane < 32 ? lm.md[L * 32u + (uint32_t)lane] : 0.0;
+        const uint64_t m2 = __ballot(lane < 32 && mb >= tgt && (m1 == 0ull || mb > 0.0));
+        found = L * 32u + (uint32_t)last_lane(m2 | 1ull);
+        above = found + 1u < (uint32_t)kHistBins ? lm.md[found + 1u] : 0.0;
       }
       if (lane == 0) {
         lm.res[7] = found;
@@ -524,7 +512,7 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
   const uint32_t n = min(lm.nlist, kLkGather);
   // tau_k: the (k - above)-th largest key of bin b_k
   const uint32_t tk = all ? 0u : lk_select<true>(keys, n, bk, 0u, (double)((uint32_t)k - above),
-                                                 sm.hist, lm);
+                                                 sm.hist, lm, sm.wz);
   // Z_k: the bins above b_k, then b_k's values >= tau_k (exact integer
   // significand sums, below 2^53, so their float64 sum is exact)
   double sk = 0.0;
@@ -574,7 +562,7 @@ __device__ __forceinline__ int large_k_merge(const SampleParams& P, const SplitP
     const double need = max((target - ab) / unit, 0.0);
     const uint32_t tp = (bp >= plo && bp <= phi) || (!all && bp == bk)
                             ? lk_select<false>(keys, n, bp, (!kJoint && bp == bk) ? tk : 0u, need,
-                                               sm.hist, lm)
+                                               sm.hist, lm, sm.wz)
                             : tk;
     tau = max(tau, tp);
   }
