@@ -73,12 +73,41 @@ __device__ __forceinline__ void load4_batch(const RowRef& r, I&& idx_of, float (
 // reductions must ignore invalid groups, stores may repeat the last group's.
 // Values past the row end inside the last group read as 0.
 constexpr int kBatch = 8;
+// Values x[idx .. idx+3]; positions past the row end read as 0 (for rows
+// without 16-byte loads; batches of 16-byte loads go through load4_batch or
+// the branch on r.vec below).
+__device__ __forceinline__ void load4(const RowRef& r, int64_t idx, float (&v)[4]) {
+  if (r.vec && idx + 3 < r.V) {
+    const float4 q = load_f4((gptr<const float4>)(r.x + idx));
+    v[0] = q.x;
+    v[1] = q.y;
+    v[2] = q.z;
+    v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (idx + e < r.V) ? r.x[idx + e] : 0.0f;
+  }
+}
+
 template <class F>
 __device__ __forceinline__ void for_each4(const RowRef& r, F&& body) {
   const int nvec = (r.V + 3) / 4;
   for (int f0 = threadIdx.x; f0 < nvec; f0 += kBlock * kBatch) {
     float v[kBatch][4];
-    load4_batch<kBatch>(r, [&](int u) { return 4ll * min(f0 + u * kBlock, nvec - 1); }, v);
+    if (r.vec) {
+      // V % 4 == 0 and a 16-byte aligned row: every clamped group is whole
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float4 q = load_f4((gptr<const float4>)(r.x + 4ll * min(f0 + u * kBlock, nvec - 1)));
+        v[u][0] = q.x;
+        v[u][1] = q.y;
+        v[u][2] = q.z;
+        v[u][3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) load4(r, 4ll * min(f0 + u * kBlock, nvec - 1), v[u]);
+    }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int f = f0 + u * kBlock;
@@ -1096,17 +1125,21 @@ __device__ __forceinline__ void select_row(const SelectParams& Q, int row, Selec
   for (int t = wave; t < n_tiles; t += kWaves) {
     const int64_t base = (int64_t)t * kTile;
     uint32_t eq = 0u;
-    float vt[kTileChunks][4];
-    load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
+    // a quarter of a tile per batch (the selection kernels keep much else live)
+    for (int h = 0; h < kTileChunks; h += kTileChunks / 4) {
+      float vt[kTileChunks / 4][4];
+      load4_batch<kTileChunks / 4>(r, [&](int q) { return base + (h + q) * (kWave * 4) + lane * 4; },
+                                   vt);
 #pragma unroll
-    for (int q = 0; q < kTileChunks; ++q) {
-      const float (&v)[4] = vt[q];
-      const int64_t idx = base + q * (kWave * 4) + lane * 4;
+      for (int q = 0; q < kTileChunks / 4; ++q) {
+        const float (&v)[4] = vt[q];
+        const int64_t idx = base + (h + q) * (kWave * 4) + lane * 4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = idx + e < V ? signed_key(v[e]) : 0u;
-        eq += key == tau ? 1u : 0u;
-        gt += key > tau ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = idx + e < V ? signed_key(v[e]) : 0u;
+          eq += key == tau ? 1u : 0u;
+          gt += key > tau ? 1u : 0u;
+        }
       }
     }
     eq = wave_sum(eq);
@@ -1149,12 +1182,14 @@ __device__ __forceinline__ void select_row(const SelectParams& Q, int row, Selec
   for (int t = wave; t < n_tiles; t += kWaves) {
     const int64_t base = (int64_t)t * kTile;
     uint32_t tie_carry = 0u;
-    float vt[kTileChunks][4];
-    load4_batch<kTileChunks>(r, [&](int q) { return base + q * (kWave * 4) + lane * 4; }, vt);
+    for (int h = 0; h < kTileChunks; h += kTileChunks / 4) {
+    float vt[kTileChunks / 4][4];
+    load4_batch<kTileChunks / 4>(r, [&](int q) { return base + (h + q) * (kWave * 4) + lane * 4; },
+                                 vt);
 #pragma unroll
-    for (int q = 0; q < kTileChunks; ++q) {
+    for (int q = 0; q < kTileChunks / 4; ++q) {
       const float (&v)[4] = vt[q];
-      const int64_t idx = base + q * (kWave * 4) + lane * 4;
+      const int64_t idx = base + (h + q) * (kWave * 4) + lane * 4;
       uint32_t key[4];
       uint32_t my_ties = 0u;
 #pragma unroll
@@ -1184,6 +1219,7 @@ __device__ __forceinline__ void select_row(const SelectParams& Q, int row, Selec
           sm.ent[pos] = ((uint64_t)key[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(idx + e));
         pos += take[e] ? 1u : 0u;
       }
+    }
     }
   }
   __syncthreads();
