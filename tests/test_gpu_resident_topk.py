@@ -114,40 +114,47 @@ def test_stress_rows_full_size():
         assert ref.support_mask(probs[row], tau)[s[row]], (row, int(w["groups"][row]))
 
 
+@pytest.mark.parametrize("n_out", [8, 72])
 @pytest.mark.parametrize("op", ["top_k", "top_k_top_p", "top_k_top_p_joint"])
-def test_split_fallback_rows_token_exact(op):
+def test_split_fallback_rows_token_exact(op, n_out):
     """Per-output k arrays keep a call on the split engine; its outputs with
-    k above the cap (2048) fall back inside the kernel to the exact passes
-    (counts, then masses inside the top-k set, one draw in index order),
-    which equal the oracle's CDF draw; the other outputs are checked for
-    their kept set only."""
+    k above the cap (2048) take the histogram path (exact tau_k, Z_k and top-p
+    cut from the slices' histograms and the gathered boundary keys, one draw
+    over the tiles in index order), which equals the oracle's CDF draw; the
+    other outputs are checked for their kept set only.  8 outputs: the last
+    slice to arrive merges (16 slices each); 72 outputs: 288 slices, more
+    than one wave of work-groups, so finishing work-groups merge."""
     rng = np.random.default_rng(31)
     rows, V = 8, 32768
     probs = np.concatenate([si.softmax_rows(rng, 6, V, 2.0), _rows("flat", 2, V, rng)])
     ks = np.array([50, 3000, 10, 70000, 2049, 1, 5000, 1000], dtype=np.int32)
     ps = np.array([0.9, 0.7, 0.5, 0.95, 0.3, 1.0, 0.99, 0.6], dtype=np.float32)
-    seeds = (np.arange(rows, dtype=np.uint64) + np.uint64(7)) * np.uint64(0x9E3779B97F4A7C15)
+    idx = (np.arange(n_out) % rows).astype(np.int32)
+    seeds = (np.arange(n_out, dtype=np.uint64) + np.uint64(7)) * np.uint64(0x9E3779B97F4A7C15)
     P = gpu(probs)
-    for offset in range(8):
+    kk, pk = ks[idx], ps[idx]
+    tables = {i: _table(probs[i], op, int(ks[i]), ps[i]) for i in range(rows) if ks[i] > 2048}
+    for offset in range(8 if n_out == 8 else 3):
         if op == "top_k":
-            s, v, r = dss.top_k_sampling_from_probs(P, gpu(ks), seed=u64(seeds), offset=offset,
-                                                    return_valid=True, return_rounds=True)
+            s, v, r = dss.top_k_sampling_from_probs(P, gpu(kk), indices=gpu(idx), seed=u64(seeds),
+                                                    offset=offset, return_valid=True,
+                                                    return_rounds=True)
         else:
             order = "joint" if op.endswith("joint") else "top_k_first"
-            s, v, r = dss.top_k_top_p_sampling_from_probs(P, gpu(ks), gpu(ps), seed=u64(seeds),
-                                                          offset=offset, return_valid=True,
-                                                          return_rounds=True,
+            s, v, r = dss.top_k_top_p_sampling_from_probs(P, gpu(kk), gpu(pk), indices=gpu(idx),
+                                                          seed=u64(seeds), offset=offset,
+                                                          return_valid=True, return_rounds=True,
                                                           filter_apply_order=order)
         s, v, r = host(s), host(v), host(r)
         assert (v == 1).all()
-        for i in range(rows):
+        for j in range(n_out):
+            i = int(idx[j])
             kw = dict(k=int(ks[i]), p=ps[i])
             valid, tau = ref.threshold(probs[i], op, **kw)
-            assert ref.support_mask(probs[i], tau)[s[i]], (op, i, offset)
+            assert ref.support_mask(probs[i], tau)[s[j]], (op, j, offset)
             if ks[i] > 2048:
-                want = _table(probs[i], op, int(ks[i]), ps[i]).draw(
-                    ph.draw_bits53(int(seeds[i]), offset, 0, 0))
-                assert s[i] == want and r[i] == 1, (op, i, offset, int(s[i]), want)
+                want = tables[i].draw(ph.draw_bits53(int(seeds[j]), offset, 0, 0))
+                assert s[j] == want and r[j] == 1, (op, j, offset, int(s[j]), want)
 
 
 @pytest.mark.parametrize("op", ["top_k", "top_k_top_p", "top_k_top_p_joint"])
