@@ -74,6 +74,7 @@ SIGNATURES = {
     "dss_stream_read_reference": ([_P, ctypes.c_int64, _P, _P], ctypes.c_int32),
     "dss_set_spin_limit": ([_U64], ctypes.c_int32),
     "dss_set_split_slices": ([_I32], ctypes.c_int32),
+    "dss_set_handoff_test": ([_I32], ctypes.c_int32),
     "dss_workspace_status": ([_P, _SZ, _P, _P], ctypes.c_int32),
 }
 

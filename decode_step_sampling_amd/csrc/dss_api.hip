@@ -16,6 +16,7 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<void*> g_ev_start{nullptr}, g_ev_stop{nullptr};  // dss_set_timing_events
 std::atomic<uint64_t> g_spin_ticks{dss::kDefaultSpinTicks};  // dss_set_spin_limit
+std::atomic<int32_t> g_handoff_test{0};                       // dss_set_handoff_test
 std::atomic<int> g_split_slices{0};                            // dss_set_split_slices
 
 dss::LaunchEvents timing_events() {
@@ -196,6 +197,7 @@ int renorm_common(int kind, int op_id, const float* in, float* out, int32_t rows
 
 namespace dss {
 uint64_t spin_limit_ticks() { return g_spin_ticks.load(std::memory_order_relaxed); }
+int handoff_test_mode() { return g_handoff_test.load(std::memory_order_relaxed); }
 int forced_split_slices() { return g_split_slices.load(std::memory_order_relaxed); }
 }  // namespace dss
 
@@ -512,6 +514,12 @@ DSS_EXPORT int32_t dss_set_timing_events(void* start, void* stop) {
 DSS_EXPORT int32_t dss_set_spin_limit(uint64_t ticks) {
   g_spin_ticks.store(ticks == UINT64_MAX ? dss::kDefaultSpinTicks : ticks,
                      std::memory_order_relaxed);
+  return DSS_OK;
+}
+
+DSS_EXPORT int32_t dss_set_handoff_test(int32_t mode) {
+  if (mode != 0 && mode != 1) return DSS_ERR_INVALID_ARG;
+  g_handoff_test.store(mode, std::memory_order_relaxed);
   return DSS_OK;
 }
 

@@ -78,6 +78,9 @@ struct LaunchEvents {
 // Longest wait of a resident row barrier, in ticks of the 100 MHz constant
 // clock (dss_set_spin_limit; 50 ms unless changed).
 uint64_t spin_limit_ticks();
+// 1 (dss_set_handoff_test): every split-engine hand-off is treated as
+// foreign, so its outputs take the in-kernel fallback (a test setting)
+int handoff_test_mode();
 constexpr uint64_t kDefaultSpinTicks = 5000000ull;
 // Slices per output the split engine must use (dss_set_split_slices; 0: its
 // own choice).

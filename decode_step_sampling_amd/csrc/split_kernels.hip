@@ -96,6 +96,7 @@ struct SplitParams {
   int fin;         // 1: the grid ends with finishing work-groups
   int nsb;         // work-groups of slices (the finishing ones start here)
   uint64_t spin;   // ticks of the 100 MHz constant clock a finisher waits at most
+  int test_foreign;  // 1: every hand-off is treated as foreign (a test setting)
 };
 
 // What the split engine computes: a sample; tau_k (and Z_k) for a top-k
@@ -647,7 +648,8 @@ __device__ __forceinline__ int large_k_finish(const SampleParams& P, const Split
     const uint32_t hb = mine ? __hip_atomic_load(h + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     const uint32_t mygen = __hip_atomic_load(as_global(S.gen + li), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool foreign =
-        __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull;
+        __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull ||
+        S.test_foreign != 0;
     const bool anybad = __ballot(mine && hb != 0u) != 0ull;
     if (lane == 0) {
       __hip_atomic_fetch_sub(ctr, (uint32_t)W, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -831,7 +833,8 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
       const bool mine = lane < W;
       const uint32_t mygen = (uint32_t)__builtin_amdgcn_readfirstlane((int)gen);
       const bool foreign =
-          __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull;
+          __ballot(mine && (hg != mygen || hx != xcc_id() || hc != kLargeList)) != 0ull ||
+          S.test_foreign != 0;
       const bool anybad = __ballot(mine && hb != 0u) != 0ull;
       if (lane == 0) {
         __hip_atomic_store(as_global(S.ctr + li), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1230,7 +1233,7 @@ __device__ __forceinline__ int split_sample(const SampleParams& P, const SplitPa
         __hip_atomic_fetch_add(as_global(S.gen + li), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       const bool anybad = __ballot(mine && hb != 0u) != 0ull;
-      const bool foreign = __ballot(mine && (hg != mygen || hx != me)) != 0ull;
+      const bool foreign = __ballot(mine && (hg != mygen || hx != me)) != 0ull || S.test_foreign != 0;
       const bool ovf = __ballot(mine && hc > (uint32_t)kListMax) != 0ull;  // kNoList too
       const uint32_t cc = (mine && hc <= (uint32_t)kListMax) ? hc : 0u;
       const uint32_t incl = wave_incl_scan(cc);
@@ -1627,6 +1630,7 @@ void launch_one(const SampleParams& p, const SplitParams& sp, const RenormParams
                             (OP == kOpTopK || OP == kOpTopKTopP || OP == kOpTopKTopPJoint);
   S.fin = kTopKOps && p.top_k_arr != nullptr && sp.W > 1 && S.nsb > kFinMinBlocks ? 1 : 0;
   S.spin = spin_limit_ticks();
+  S.test_foreign = handoff_test_mode();
   const dim3 grid((unsigned)(S.nsb + (S.fin ? groups * 8 : 0))), block(kBlock);
   launch_kernel(split_kernel<KIND, OP, NV>, grid, block, s, ev, first, last, p, S, rp, q);
 }
@@ -1709,6 +1713,7 @@ SplitParams split_params(const SplitPlan& plan, void* workspace) {
   sp.fin = 0;
   sp.nsb = 0;
   sp.spin = 0ull;
+  sp.test_foreign = 0;
   sp.W = plan.W;
   sp.wlog = 0;
   while ((1 << sp.wlog) < plan.W) ++sp.wlog;

@@ -4,8 +4,8 @@
  * Not part of the sampling ops (include/dss.h): these calls exist so that a
  * benchmark can time kernels without a profiler, compare the sampling
  * kernels with a plain read of the same bytes, and so that tests can force
- * the resident engine's bounded wait to give up while every kernel still
- * exits normally.  All are process-wide and take effect for later calls.
+ * the bounded waits to give up and the split engine's hand-off checks to
+ * fail while every kernel still exits normally.  All are process-wide and take effect for later calls.
  */
 #ifndef DSS_HOOKS_H
 #define DSS_HOOKS_H
@@ -38,14 +38,24 @@ int32_t dss_set_timing_events(void* start, void* stop);
  * `stream`.  DSS_ERR_INVALID_ARG for a bad size, pointer or alignment. */
 int32_t dss_stream_read_reference(const float* x, int64_t n, uint32_t* out_max, void* stream);
 
-/* Longest wait of a resident row barrier, in ticks of the GPU's 100 MHz
- * constant clock (default 5,000,000 = 50 ms).  UINT64_MAX restores the
- * default.  A small limit makes waits give up (the output is reported
- * invalid and its control block marked broken, see dss.h "Co-residency");
- * 0 makes every resident barrier give up on arrival, so every output of a
- * resident launch comes out invalid and every slot it used is marked
- * broken.  For tests of that path only.  Always DSS_OK. */
+/* Longest wait of a resident row barrier, and of a split-engine finishing
+ * work-group for its slices, in ticks of the GPU's 100 MHz constant clock
+ * (default 5,000,000 = 50 ms).  UINT64_MAX restores the default.  A small
+ * limit makes waits give up: a resident output is reported invalid and its
+ * control block marked broken (see dss.h "Co-residency"); a finishing
+ * work-group samples its output with the exact one-work-group passes
+ * instead.  0 makes every such wait give up at once.  For tests of those
+ * paths only.  Always DSS_OK. */
 int32_t dss_set_spin_limit(uint64_t ticks);
+
+/* 1 makes every hand-off of the split-row engine look foreign (as if a
+ * slice's header carried another generation or XCD), so every output whose
+ * slices published lists or histograms is computed instead by the in-kernel
+ * fallback of one work-group (the exact passes for top-k sampling, the
+ * streaming engine otherwise); 0 restores normal hand-offs.  For tests that
+ * the fallback fires and is correct; process-wide.  DSS_ERR_INVALID_ARG for
+ * other values. */
+int32_t dss_set_handoff_test(int32_t mode);
 
 /* Slices per output of the split-row engine (a power of two, 1..16), for
  * measuring other choices than its own (about 256 work-groups in all); 0

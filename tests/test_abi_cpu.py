@@ -35,7 +35,7 @@ def header_macro(name):
 def test_library_exports_every_declared_function():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -146,6 +146,10 @@ def test_workspace_size_and_strings():
     assert lib.dss_workspace_status(None, 0, flags, None) == 0
     assert lib.dss_workspace_status(ctypes.c_void_p(16), 4096, None, None) == 0
     assert lib.dss_set_spin_limit(2**64 - 1) == _lib.DSS_OK   # restores the default
+    # forced foreign hand-offs: 0 or 1 only
+    for bad in (2, -1):
+        assert lib.dss_set_handoff_test(bad) == _lib.DSS_ERR_INVALID_ARG
+    assert lib.dss_set_handoff_test(0) == _lib.DSS_OK
     # forced split slices: powers of two up to 16, or 0; the workspace follows
     for bad in (3, 32, -1):
         assert lib.dss_set_split_slices(bad) == _lib.DSS_ERR_INVALID_ARG
