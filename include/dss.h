@@ -46,6 +46,13 @@
  *   workspace is zero-filled again; dss_workspace_status reports such
  *   blocks.  Callers that overlap other kernels with these ops can pass
  *   DSS_FLAG_STREAMING, whose engine never waits.
+ *   The split engine waits in one case only: with per-output k arrays, a
+ *   launch of more slices than one work-group per compute unit ends with one
+ *   finishing work-group per output that waits for that output's slices
+ *   (all placed before it in the grid) when its k is above 2048.  That wait
+ *   is bounded too (50 ms); a finisher that gives up samples its output
+ *   with the exact one-work-group passes instead, and leaves the control
+ *   words balanced for later calls.
  *
  * Outputs of the sampling ops (length num_outputs):
  *   samples[i]  token id in [0, vocab), or -1 when output i is invalid;
