@@ -69,6 +69,9 @@ namespace dss {
 namespace {
 
 constexpr int kRMaxW = 16;
+// The resident kernel's own op id for top-k then top-p by the one search on
+// (count, mass) pairs; calls with a scalar k up to kResidentSegKeys take it.
+constexpr int kOpResPairs = 16;
 constexpr int kRMaxNv = 12;  // 16-byte loads per thread (48 values; more run out of registers)
 constexpr int kRWideNv = 16;  // plain, top-p and min-p sampling: 64 values per thread
 constexpr int kRB1 = 1024;   // level 1: bits [30:21]
@@ -104,6 +107,7 @@ enum ResKind : int { kResSample = 0, kResRenorm = 1 };
 
 struct ResSmem {
   alignas(16) uint64_t hh[kRHistWords];  // histogram copies (lanes spread over copies)
+  uint64_t sink[kWave];                  // per-lane target of adds outside a histogram
   double md[kRB2];                       // bin masses of the level being searched
   uint32_t wmax[kWaves];
   uint32_t wbad[kWaves];
@@ -111,9 +115,19 @@ struct ResSmem {
   uint32_t off[kRMaxW + 1];       // list offsets of the slices
   uint32_t res[4];
   double resd[4];
+  double wsd[kWaves];  // per-wave sums of a bin search
+  double wsd2[kWaves];
+  double fab, ftot, fab2;  // a bin search's result: sums above the bin, total
+  uint32_t fbin;
+  uint32_t lcnt;  // keys this work-group has put into its list segment
   int flag;
+  // top-k then top-p in one search: masses of the level being searched, and
+  // those of levels one and two kept for the top-p cut
+  double mm[kRB2];
+  double m1[kRB1];
+  double m2[kRB2];
 };
-static_assert(sizeof(ResSmem) <= 96 * 1024, "LDS of the resident kernel");
+static_assert(sizeof(ResSmem) <= 136 * 1024, "LDS of the resident kernel");
 
 __device__ __forceinline__ int r_uwave() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -121,6 +135,14 @@ __device__ __forceinline__ uint32_t r_xcc_id() {
   return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
 }
 
+// A work-group-uniform value held in scalar registers.
+__device__ __forceinline__ uint32_t r_uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ double r_uniform(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ __forceinline__ int r_first_lane(uint64_t m) { return __ffsll((long long)m) - 1; }
 __device__ __forceinline__ int r_last_lane(uint64_t m) { return 63 - __clzll((long long)m); }
 
@@ -223,6 +245,114 @@ __device__ __forceinline__ void publish_hist(const ResSmem& sm, gptr<uint64_t> g
 __device__ __forceinline__ void clear_lds_hist(ResSmem& sm) {
   uint4* h4 = reinterpret_cast<uint4*>(sm.hh);
   for (int q = threadIdx.x; q < kRHistWords / 2; q += kBlock) h4[q] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Adds into the LDS histogram copies (C words per bin, copy lane % C) that
+// merge a thread's consecutive values landing in one bin into a single add:
+// rows with huge tie groups or a narrow value range send most of their values
+// to a few bins, where the adds of a work-group would otherwise queue on a few
+// LDS words.  Integer adds, so the merged sums are the same.  Values outside
+// the histogram (`on` false) form runs of their own that go to the lane's
+// sink word, so each value costs one compare-and-select and the only branch
+// is around the add that ends a run (per-value branches on the exec mask
+// would keep the work-group's one scalar unit busy instead).
+constexpr uint32_t kNoBin = 0xFFFFFFFFu;
+template <int C>
+struct HistRun {
+  uint32_t bin = kNoBin;
+  unsigned long long acc = 0ull;
+  __device__ __forceinline__ void flush(ResSmem& sm) {
+    const uint32_t lane = (uint32_t)lane_id();
+    uint64_t* const w =
+        bin != kNoBin ? &sm.hh[bin * (uint32_t)C + (lane & (uint32_t)(C - 1))] : &sm.sink[lane];
+    atomicAdd(reinterpret_cast<unsigned long long*>(w), acc);
+  }
+  __device__ __forceinline__ void put(ResSmem& sm, bool on, uint32_t b, unsigned long long add) {
+    const uint32_t bb = on ? b : kNoBin;
+    const bool chg = bb != bin;
+    if (chg) flush(sm);
+    acc = (chg ? 0ull : acc) + add;
+    bin = bb;
+  }
+};
+
+// The bin of sm.md (NB bins) where the mass from the top first reaches
+// `need` (pfrac >= 0: need = pfrac * total): the first bin from the top whose
+// inclusive suffix sum is >= need and > 0, or, when rounding or need > total
+// leaves no such bin, the lowest non-zero bin (bin NB - 1 if all are zero).
+// `above` is the sum of the bins above it (TWO: `above2` the same sum over
+// sm.mm).  All sixteen waves take part: each sums NB / 16 bins (one or two
+// per lane), one wave scan over the wave sums finds the crossing wave, and
+// that wave finds the bin.  Every thread calls and gets the result.
+template <int NB, bool TWO = false>
+__device__ __forceinline__ void res_find(ResSmem& sm, double need, double pfrac, uint32_t& bin,
+                                         double& above, double& total, double* above2 = nullptr) {
+  constexpr int PW = NB / kWaves, PL = PW / kWave;  // bins per wave, per lane
+  static_assert(PL == 1 || PL == 2, "one or two bins per lane");
+  const int lane = lane_id(), w = r_uwave();
+  double m[PL], n[PL];
+  double s = 0.0, s2 = 0.0;
+#pragma unroll
+  for (int q = 0; q < PL; ++q) {
+    const int b = NB - 1 - (w * PW + lane * PL + q);
+    m[q] = sm.md[b];
+    s += m[q];
+    if (TWO) {
+      n[q] = sm.mm[b];
+      s2 += n[q];
+    }
+  }
+  const double incl = wave_incl_scan(s);
+  const double incl2 = TWO ? wave_incl_scan(s2) : 0.0;
+  if (lane == kWave - 1) {
+    sm.wsd[w] = incl;
+    if (TWO) sm.wsd2[w] = incl2;
+  }
+  __syncthreads();
+  const double t = lane < kWaves ? sm.wsd[lane] : 0.0;
+  const double tincl = wave_incl_scan(t);
+  const double tincl2 = TWO ? wave_incl_scan(lane < kWaves ? sm.wsd2[lane] : 0.0) : 0.0;
+  const double tot = lane63(tincl);
+  if (pfrac >= 0.0) need = pfrac * tot;
+  const uint64_t hit = __ballot(lane < kWaves && tincl >= need && tincl > 0.0);
+  const bool fb = hit == 0ull;
+  const int wc = fb ? r_last_lane(__ballot(lane < kWaves && t > 0.0) | 1ull) : r_first_lane(hit);
+  if (w == wc) {
+    const double exw = wc == 0 ? 0.0 : lane_value(tincl, wc - 1);
+    const double in2 = incl + exw;
+    uint64_t h2 = fb ? 0ull : __ballot(in2 >= need && in2 > 0.0);
+    const bool lfb = h2 == 0ull;
+    if (lfb) h2 = 1ull << r_last_lane(__ballot(s > 0.0) | 1ull);
+    const int L = r_first_lane(h2);
+    const double ex2 = L == 0 ? exw : lane_value(in2, L - 1);
+    double ex3 = 0.0;
+    if (TWO) {
+      const double exw2 = wc == 0 ? 0.0 : lane_value(tincl2, wc - 1);
+      const double in3 = incl2 + exw2;
+      ex3 = L == 0 ? exw2 : lane_value(in3, L - 1);
+    }
+    if (lane == L) {
+      int q = 0;
+      double ab = ex2, ab2 = ex3;
+      if (PL == 2) {
+        const bool c0 = !lfb && ex2 + m[0] >= need && ex2 + m[0] > 0.0;
+        if (!c0 && (lfb ? m[PL - 1] > 0.0 : true)) {
+          q = 1;
+          ab = ex2 + m[0];
+          if (TWO) ab2 = ex3 + n[0];
+        }
+      }
+      sm.fbin = (uint32_t)(NB - 1 - (w * PW + L * PL + q));
+      sm.fab = ab;
+      sm.ftot = tot;
+      if (TWO) sm.fab2 = ab2;
+    }
+  }
+  __syncthreads();
+  bin = r_uniform(sm.fbin);
+  above = r_uniform(sm.fab);
+  total = r_uniform(sm.ftot);
+  if (TWO) *above2 = r_uniform(sm.fab2);
 }
 
 // Load the row's histogram g (NB bins) as masses into sm.md; `exponent` < 0:
@@ -486,15 +616,18 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
 #endif
   clear_lds_hist(sm);
   __syncthreads();
+  {
+    HistRun<8> run;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const bool in = vbase + j * kWave < nvec;
-    const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+    for (int j = 0; j < NV; ++j) {
+      fence_vec(v[j], run.acc);  // one load at a time (register pressure)
+      const bool in = vbase + j * kWave < nvec;
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (in && k4[e] >= cut)
-        atomicAdd(&sm.hh[min(k4[e] >> 21, (uint32_t)(kRB1 - 1)) * 8u + (uint32_t)(lane & 7)],
-                  level_add<COUNT>(k4[e]));
+      for (int e = 0; e < 4; ++e)
+        run.put(sm, in && k4[e] >= cut, min(k4[e] >> 21, (uint32_t)(kRB1 - 1)), level_add<COUNT>(k4[e]));
+    }
+    run.flush(sm);
   }
   __syncthreads();
   publish_hist<kRB1>(sm, g1);
@@ -506,20 +639,10 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
   ++passed;
   load_level<COUNT, kRB1>(g1, -1, sm);
   __syncthreads();
-  if (wave == 0) {
-    uint32_t b1;
-    double above, total;
-    stream::mass_find<kRB1>(sm.md, need_in, pfrac, b1, above, total);
-    if (lane == 0) {
-      sm.res[0] = b1;
-      sm.resd[0] = above;
-      sm.resd[1] = total;
-      sm.resd[2] = pfrac >= 0.0 ? pfrac * total : need_in;
-    }
-  }
-  __syncthreads();
-  const uint32_t b1 = sm.res[0];
-  const double above1 = sm.resd[0], ftot = sm.resd[1], need = sm.resd[2];
+  uint32_t b1;
+  double above1, ftot;
+  res_find<kRB1>(sm, need_in, pfrac, b1, above1, ftot);
+  const double need = pfrac >= 0.0 ? pfrac * ftot : need_in;
   const uint32_t e1 = b1 >> 2;
   if (!COUNT && pfrac >= 1.0) {  // every value >= cut
     tau = cut;
@@ -582,47 +705,50 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
       kk[q] = g < n ? k : kNone;
     }
     // level 2 in LDS: bits [20:10], copy lane % 4
+    {
+      HistRun<4> run;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (kk[q] != kNone)
-        atomicAdd(&sm.hh[((kk[q] >> 10) & (uint32_t)(kRB2 - 1)) * 4u + (uint32_t)(lane & 3)],
-                  level_add<COUNT>(kk[q]));
+      for (int q = 0; q < kPer; ++q)
+        run.put(sm, kk[q] != kNone, (kk[q] >> 10) & (uint32_t)(kRB2 - 1), level_add<COUNT>(kk[q]));
+      run.flush(sm);
+    }
     __syncthreads();
     fold_level<COUNT, kRB2>(sm, e1);
     __syncthreads();
     clear_lds_hist(sm);
-    if (wave == 0) {
+    {
       uint32_t b2;
-      double above, total;
-      stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
-      if (lane == 0) {
-        sm.res[1] = b2;
-        sm.resd[0] = above;
-      }
+      double total;
+      res_find<kRB2>(sm, need - above1, -1.0, b2, above2, total);
+      pre2 = (b1 << 11) | b2;
     }
-    __syncthreads();
-    pre2 = (b1 << 11) | sm.res[1];
-    above2 = sm.resd[0];
     // level 3 in LDS: bits [9:0] of the keys with bits [30:10] == pre2
+    {
+      HistRun<8> run;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (kk[q] != kNone && (kk[q] >> 10) == pre2)
-        atomicAdd(&sm.hh[(kk[q] & (uint32_t)(kRB3 - 1)) * 8u + (uint32_t)(lane & 7)],
-                  level_add<COUNT>(kk[q]));
+      for (int q = 0; q < kPer; ++q)
+        run.put(sm, kk[q] != kNone && (kk[q] >> 10) == pre2, kk[q] & (uint32_t)(kRB3 - 1),
+                level_add<COUNT>(kk[q]));
+      run.flush(sm);
+    }
     __syncthreads();
     fold_level<COUNT, kRB3>(sm, e1);
     __syncthreads();
   } else {
     // level 2: values in bin b1, by bits [20:10], copy lane % 4
+    {
+      HistRun<4> run;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const bool in = vbase + j * kWave < nvec;
-      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+      for (int j = 0; j < NV; ++j) {
+        fence_vec(v[j], run.acc);  // one load at a time (register pressure)
+        const bool in = vbase + j * kWave < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (in && (k4[e] >> 21) == b1 && k4[e] >= cut)
-          atomicAdd(&sm.hh[((k4[e] >> 10) & (uint32_t)(kRB2 - 1)) * 4u + (uint32_t)(lane & 3)],
-                    level_add<COUNT>(k4[e]));
+        for (int e = 0; e < 4; ++e)
+          run.put(sm, in && (k4[e] >> 21) == b1 && k4[e] >= cut, (k4[e] >> 10) & (uint32_t)(kRB2 - 1),
+                  level_add<COUNT>(k4[e]));
+      }
+      run.flush(sm);
     }
     __syncthreads();
     publish_hist<kRB2>(sm, g2);
@@ -634,28 +760,26 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     ++passed;
     load_level<COUNT, kRB2>(g2, (int)e1, sm);
     __syncthreads();
-    if (wave == 0) {
+    {
       uint32_t b2;
-      double above, total;
-      stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
-      if (lane == 0) {
-        sm.res[1] = b2;
-        sm.resd[0] = above;
-      }
+      double total;
+      res_find<kRB2>(sm, need - above1, -1.0, b2, above2, total);
+      pre2 = (b1 << 11) | b2;
     }
-    __syncthreads();
-    pre2 = (b1 << 11) | sm.res[1];
-    above2 = sm.resd[0];
     // level 3: values with bits [30:10] == pre2, by bits [9:0], copy lane % 8
+    {
+      HistRun<8> run;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const bool in = vbase + j * kWave < nvec;
-      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+      for (int j = 0; j < NV; ++j) {
+        fence_vec(v[j], run.acc);  // one load at a time (register pressure)
+        const bool in = vbase + j * kWave < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (in && (k4[e] >> 10) == pre2 && k4[e] >= cut)
-          atomicAdd(&sm.hh[(k4[e] & (uint32_t)(kRB3 - 1)) * 8u + (uint32_t)(lane & 7)],
-                    level_add<COUNT>(k4[e]));
+        for (int e = 0; e < 4; ++e)
+          run.put(sm, in && (k4[e] >> 10) == pre2 && k4[e] >= cut, k4[e] & (uint32_t)(kRB3 - 1),
+                  level_add<COUNT>(k4[e]));
+      }
+      run.flush(sm);
     }
     __syncthreads();
     publish_hist<kRB3>(sm, g3);
@@ -666,23 +790,306 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
     load_level<COUNT, kRB3>(g3, (int)e1, sm);
     __syncthreads();
   }
-  if (wave == 0) {
-    uint32_t b;
-    double above, total;
-    stream::mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b, above, total);
-    if (lane == 0) {
-      sm.res[2] = b;
-      sm.resd[0] = above;
-      sm.resd[1] = sm.md[b];
-    }
+  {
+    double total;
+    res_find<kRB3>(sm, need - above1 - above2, -1.0, b3, above3, total);
+    m3 = sm.md[b3];
   }
-  __syncthreads();
-  b3 = sm.res[2];
-  above3 = sm.resd[0];
-  m3 = sm.resd[1];
   __syncthreads();
   tau = (pre2 << 10) | b3;
   kept = above1 + above2 + (above3 + m3);
+  return true;
+}
+
+// ---- top-k then top-p in one search ------------------------------------------
+//
+// Every level histogram carries (count, significand sum) pairs packed in one
+// 64-bit word (count << 44 | sum: a row of fewer than 2^20 values cannot
+// carry out of either field), so the count search that pins tau_k also
+// yields the exact masses of every bin it visits.  Z_k is then known with
+// tau_k, and the top-p cut p * Z_k (which lies at or above tau_k) is found
+// from the same histograms: on the count search's own path (bins above the
+// path bin whole, the path bin with its part >= tau_k, lower bins nothing),
+// or, where it leaves that path, inside a bin that lies wholly above the
+// top-k boundary bin.  Fewer than k values lie above that boundary, and the
+// last round of the count search also puts them into a key list, so the
+// cut is finished in LDS without another row barrier.  Three row barriers
+// for both thresholds instead of up to six.
+constexpr int kPairShift = 44;
+constexpr uint64_t kSigMask = (1ull << kPairShift) - 1ull;
+constexpr int kListPer = kResidentSegKeys / kBlock;  // list keys per thread after a gather
+
+__device__ __forceinline__ unsigned long long pair_of(uint32_t key) {
+  return (1ull << kPairShift) | (unsigned long long)sig_of(key);
+}
+
+// Row histogram g (NB bins of pairs) into sm.md (counts) and sm.mm (masses,
+// exponent < 0: level 1, bin b holds exponent b >> 2); masses also to `save`.
+template <int NB>
+__device__ __forceinline__ void load_pairs(gptr<uint64_t> g, int exponent, ResSmem& sm, double* save) {
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    const uint64_t x = __hip_atomic_load(g + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const double m = bin_mass(x & kSigMask, exponent < 0 ? (uint32_t)b >> 2 : (uint32_t)exponent);
+    sm.md[b] = (double)(x >> kPairShift);
+    sm.mm[b] = m;
+    if (save) save[b] = m;
+  }
+}
+
+// The same from the LDS copies; MASS: masses into sm.md only.
+template <int NB, bool MASS>
+__device__ __forceinline__ void fold_pairs(ResSmem& sm, uint32_t exponent, double* save) {
+  constexpr int C = kRHistWords / NB;
+  for (int b = threadIdx.x; b < NB; b += kBlock) {
+    uint64_t x = 0ull;
+#pragma unroll
+    for (int c = 0; c < C; ++c) x += sm.hh[b * C + c];
+    const double m = bin_mass(x & kSigMask, exponent);
+    if (MASS) {
+      sm.md[b] = m;
+    } else {
+      sm.md[b] = (double)(x >> kPairShift);
+      sm.mm[b] = m;
+      if (save) save[b] = m;
+    }
+  }
+}
+
+// sm.md = a level's masses as far as they are kept: bins above bk whole,
+// bin bk `kept`, lower bins nothing.
+template <int NB>
+__device__ __forceinline__ void kept_masses(const double* src, uint32_t bk, double kept, ResSmem& sm) {
+  for (int b = threadIdx.x; b < NB; b += kBlock)
+    sm.md[b] = (uint32_t)b > bk ? src[b] : (uint32_t)b == bk ? kept : 0.0;
+}
+
+// Puts `key` into this work-group's list segment when `take` (in any order):
+// the lanes that take reserve their slots with one LDS add per wave.
+__device__ __forceinline__ void list_put(bool take, uint32_t key, gptr<uint32_t> seg, ResSmem& sm) {
+  const uint64_t m = __ballot(take);
+  if (m != 0ull) {
+    const int f = r_first_lane(m);
+    uint32_t base = 0u;
+    if (lane_id() == f) base = atomicAdd(&sm.lcnt, (uint32_t)__popcll(m));
+    base = __builtin_amdgcn_readlane(base, f);
+    const uint32_t pos =
+        base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (take && pos < (uint32_t)kResidentSegKeys) seg[pos] = key;
+  }
+}
+
+// Every work-group's list segment of the output into kk (kListPer keys per
+// thread, kNoBin past the end).  Every thread calls.
+__device__ __forceinline__ void read_list(uint32_t (&kk)[kListPer], gptr<uint32_t> ctl,
+                                          gptr<uint32_t> seg_base, int li, int W, ResSmem& sm) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = r_uwave();
+  if (wave == 0) {
+    const uint32_t c = lane < W ? min(__hip_atomic_load(ctl + 8 + lane, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT),
+                                      (uint32_t)kResidentSegKeys)
+                                : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (lane <= kRMaxW) sm.off[lane] = incl - c;
+  }
+  __syncthreads();
+  const uint32_t n = sm.off[W];
+#pragma unroll
+  for (int q = 0; q < kListPer; ++q) {
+    const uint32_t g = (uint32_t)tid + (uint32_t)(q * kBlock);
+    int sl = 0;
+    for (int t = 1; t < W; ++t) sl = g >= sm.off[t] ? t : sl;
+    const uint32_t at = min(g - sm.off[sl], (uint32_t)(kResidentSegKeys - 1));
+    const uint32_t k = __hip_atomic_load(seg_base + (size_t)(li * W + sl) * kResidentSegKeys + at,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    kk[q] = g < n ? k : kNoBin;
+  }
+}
+
+// One level over the list in LDS: the keys with key >> pshift == prefix, by
+// bits [20:10] (NB = 2048) or [9:0] (NB = 1024), into sm.md / sm.mm (MASS:
+// masses into sm.md).  Every thread calls.
+template <int NB, bool MASS>
+__device__ __forceinline__ void list_level(const uint32_t (&kk)[kListPer], uint32_t pshift,
+                                           uint32_t prefix, uint32_t exponent, ResSmem& sm,
+                                           double* save) {
+  constexpr int C = kRHistWords / NB;
+  constexpr uint32_t bshift = NB == kRB2 ? 10u : 0u;
+  clear_lds_hist(sm);
+  __syncthreads();
+  {
+    HistRun<C> run;
+#pragma unroll
+    for (int q = 0; q < kListPer; ++q)
+      run.put(sm, kk[q] != kNoBin && (kk[q] >> pshift) == prefix, (kk[q] >> bshift) & (uint32_t)(NB - 1),
+              pair_of(kk[q]));
+    run.flush(sm);
+  }
+  __syncthreads();
+  fold_pairs<NB, MASS>(sm, exponent, save);
+  __syncthreads();
+}
+
+// tau = the top-p threshold inside the top-k set: with tau_k the k-th
+// largest pattern (ties kept) and Z_k the mass of {x >= tau_k}, the largest
+// pattern t with mass(x >= t) >= p * Z_k (p >= 1: tau_k itself); kept = the
+// mass of {x >= tau}.  Same results as the count search followed by the
+// mass search with cut = max(tau_k, 1).  Needs k <= kResidentSegKeys.  Every
+// thread calls; false if a row barrier timed out.
+template <int NV>
+__device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nvec, int k, float pc,
+                                              gptr<uint64_t> g1, gptr<uint64_t> g2, gptr<uint64_t> g3,
+                                              gptr<uint32_t> ctl, gptr<uint32_t> seg_base, int li,
+                                              int s, int W, uint64_t spin, uint32_t& passed,
+                                              ResSmem& sm, uint32_t& tau, double& kept) {
+  const int tid = threadIdx.x;
+  const gptr<uint32_t> seg = seg_base + (size_t)(li * W + s) * kResidentSegKeys;
+  // ---- level 1: every value by bits [30:21] --------------------------------
+  clear_lds_hist(sm);
+  __syncthreads();
+  {
+    HistRun<8> run;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      fence_vec(v[j], run.acc);  // one load at a time (register pressure)
+      const bool in = vbase + j * kWave < nvec;
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) run.put(sm, in, min(k4[e] >> 21, (uint32_t)(kRB1 - 1)), pair_of(k4[e]));
+    }
+    run.flush(sm);
+  }
+  __syncthreads();
+  publish_hist<kRB1>(sm, g1);
+  __syncthreads();
+  clear_lds_hist(sm);
+  if (tid == 0) sm.lcnt = 0u;
+  DSS_RSTAMP(4);
+  if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+  DSS_RSTAMP(5);
+  ++passed;
+  load_pairs<kRB1>(g1, -1, sm, sm.m1);
+  __syncthreads();
+  uint32_t b1, b2, b3;
+  double cab1, cab2, cab3, mab1, mab2, mab3, tot;
+  res_find<kRB1, true>(sm, (double)k, -1.0, b1, cab1, tot, &mab1);
+  const uint32_t e1 = b1 >> 2;
+  // bin b1 and everything above it fit one list: gather them all now
+  const bool use_list = cab1 + sm.md[b1] <= (double)kResidentSegKeys;
+  uint32_t pre2;
+  if (use_list) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const bool in = vbase + j * kWave < nvec;
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) list_put(in && (k4[e] >> 21) >= b1, k4[e], seg, sm);
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(ctl + 8 + s, sm.lcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    DSS_RSTAMP(6);
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+    DSS_RSTAMP(7);
+    ++passed;
+    uint32_t kk[kListPer];
+    read_list(kk, ctl, seg_base, li, W, sm);
+    list_level<kRB2, false>(kk, 21u, b1, e1, sm, sm.m2);
+    res_find<kRB2, true>(sm, (double)k - cab1, -1.0, b2, cab2, tot, &mab2);
+    pre2 = (b1 << 11) | b2;
+    list_level<kRB3, false>(kk, 10u, pre2, e1, sm, nullptr);
+  } else {
+    // level 2: values in bin b1 by bits [20:10]
+    {
+      HistRun<4> run;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        fence_vec(v[j], run.acc);  // one load at a time (register pressure)
+        const bool in = vbase + j * kWave < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          run.put(sm, in && (k4[e] >> 21) == b1, (k4[e] >> 10) & (uint32_t)(kRB2 - 1), pair_of(k4[e]));
+      }
+      run.flush(sm);
+    }
+    __syncthreads();
+    publish_hist<kRB2>(sm, g2);
+    __syncthreads();
+    clear_lds_hist(sm);
+    DSS_RSTAMP(6);
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+    DSS_RSTAMP(7);
+    ++passed;
+    load_pairs<kRB2>(g2, (int)e1, sm, sm.m2);
+    __syncthreads();
+    res_find<kRB2, true>(sm, (double)k - cab1, -1.0, b2, cab2, tot, &mab2);
+    pre2 = (b1 << 11) | b2;
+    // level 3: values with bits [30:10] == pre2 by bits [9:0]; the values
+    // above that bin (fewer than k) into the list
+    {
+      HistRun<8> run;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        fence_vec(v[j], run.acc);  // one load at a time (register pressure)
+        const bool in = vbase + j * kWave < nvec;
+        const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          run.put(sm, in && (k4[e] >> 10) == pre2, k4[e] & (uint32_t)(kRB3 - 1), pair_of(k4[e]));
+          list_put(in && (k4[e] >> 10) > pre2, k4[e], seg, sm);
+        }
+      }
+      run.flush(sm);
+    }
+    __syncthreads();
+    publish_hist<kRB3>(sm, g3);
+    if (tid == 0) __hip_atomic_store(ctl + 8 + s, sm.lcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    DSS_RSTAMP(8);
+    if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
+    DSS_RSTAMP(9);
+    ++passed;
+    load_pairs<kRB3>(g3, (int)e1, sm, nullptr);
+    __syncthreads();
+  }
+  res_find<kRB3, true>(sm, (double)k - cab1 - cab2, -1.0, b3, cab3, tot, &mab3);
+  const uint32_t tk = max((pre2 << 10) | b3, 1u);  // zeros carry no mass
+  const double m3 = mab3 + sm.mm[b3];              // kept part of bin pre2
+  const double zk = mab1 + (mab2 + m3);
+  if (pc >= 1.0f) {
+    __syncthreads();
+    tau = tk;
+    kept = zk;
+    return true;
+  }
+  // ---- the top-p cut p * Z_k, from the top ----------------------------------
+  const double need = (double)pc * zk;
+  double ap1, ap2, ap3, t;
+  uint32_t p1, p2, p3;
+  kept_masses<kRB1>(sm.m1, b1, mab2 + m3, sm);
+  __syncthreads();
+  res_find<kRB1>(sm, need, -1.0, p1, ap1, t);
+  if (p1 == b1) {
+    kept_masses<kRB2>(sm.m2, b2, m3, sm);
+    __syncthreads();
+    res_find<kRB2>(sm, need - ap1, -1.0, p2, ap2, t);
+    if (p2 == b2) {
+      kept_masses<kRB3>(sm.mm, b3, sm.mm[b3], sm);
+      __syncthreads();
+    } else {  // inside L2 bin p2 > b2: every value there is in the list
+      uint32_t kk[kListPer];
+      read_list(kk, ctl, seg_base, li, W, sm);
+      list_level<kRB3, true>(kk, 10u, (b1 << 11) | p2, e1, sm, nullptr);
+    }
+  } else {  // inside L1 bin p1 > b1: every value there is in the list
+    uint32_t kk[kListPer];
+    read_list(kk, ctl, seg_base, li, W, sm);
+    list_level<kRB2, true>(kk, 21u, p1, p1 >> 2, sm, nullptr);
+    res_find<kRB2>(sm, need - ap1, -1.0, p2, ap2, t);
+    list_level<kRB3, true>(kk, 10u, (p1 << 11) | p2, p1 >> 2, sm, nullptr);
+  }
+  res_find<kRB3>(sm, need - ap1 - ap2, -1.0, p3, ap3, t);
+  tau = max((((p1 << 11) | p2) << 10) | p3, tk);
+  kept = ap1 + ap2 + (ap3 + sm.md[p3]);
+  __syncthreads();
   return true;
 }
 
@@ -692,7 +1099,8 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   __shared__ ResSmem sm;
   DSS_RSTAMP(0);
   constexpr bool kTopP = OP == kOpTopP;  // top-p alone: level-1 masses while the slice lands
-  constexpr bool kTopK = OP == kOpTopK || OP == kOpTopKTopP;
+  constexpr bool kPairs = OP == kOpResPairs;  // top-k then top-p, one search on pairs
+  constexpr bool kTopK = OP == kOpTopK || OP == kOpTopKTopP || kPairs;
   // histogram words the row's last work-group clears (masses, then counts)
   constexpr int kHistWords = kTopK ? 2 * kRLevelWords : kTopP ? kRLevelWords : 0;
   const int W = R.W;
@@ -727,7 +1135,8 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   // parameters (read before any store, so they are scalar loads)
   float prm = 0.0f;
   if (KIND == kResRenorm) prm = RP.top_p_arr ? as_global(RP.top_p_arr)[i] : RP.top_p;
-  else if (OP == kOpTopP || OP == kOpTopKTopP) prm = P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
+  else if (OP == kOpTopP || OP == kOpTopKTopP || kPairs)
+    prm = P.top_p_arr ? as_global(P.top_p_arr)[i] : P.top_p;
   else if (OP == kOpMinP) prm = P.min_p_arr ? as_global(P.min_p_arr)[i] : P.min_p;
   const int kk = kTopK ? (P.top_k_arr ? as_global(P.top_k_arr)[i] : P.top_k) : 1;
   const uint64_t seed = KIND != kResSample ? 0ull : P.seed_arr ? as_global(P.seed_arr)[i] : P.seed;
@@ -828,20 +1237,10 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     // ---- threshold search, three levels --------------------------------------
     load_masses<kRB1>((gptr<uint64_t>)slot->h1, -1, sm);
     __syncthreads();
-    if (wave == 0) {
-      uint32_t b1;
-      double above, total;
-      stream::mass_find<kRB1>(sm.md, 0.0, (double)pc, b1, above, total);
-      if (lane == 0) {
-        sm.res[0] = b1;
-        sm.resd[0] = above;
-        sm.resd[1] = total;
-        sm.resd[2] = (double)pc * total;
-      }
-    }
-    __syncthreads();
-    const uint32_t b1 = sm.res[0];
-    const double above1 = sm.resd[0], ztot = sm.resd[1], need = sm.resd[2];
+    uint32_t b1;
+    double above1, ztot;
+    res_find<kRB1>(sm, 0.0, (double)pc, b1, above1, ztot);
+    const double need = (double)pc * ztot;
     const uint32_t e1 = b1 >> 2;
     // the row's values in bin b1 number at most its significand sum / 2^23
     // (normal numbers): a small bin goes out as a key list instead of two
@@ -908,18 +1307,10 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       fold_masses<kRB2>(sm, e1);
       __syncthreads();
       clear_lds_hist(sm);
-      if (wave == 0) {
-        uint32_t b2;
-        double above, total;
-        stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
-        if (lane == 0) {
-          sm.res[1] = b2;
-          sm.resd[0] = above;
-        }
-      }
-      __syncthreads();
-      const uint32_t pre2 = (b1 << 11) | sm.res[1];
-      const double above2 = sm.resd[0];
+      uint32_t b2;
+      double above2, total2;
+      res_find<kRB2>(sm, need - above1, -1.0, b2, above2, total2);
+      const uint32_t pre2 = (b1 << 11) | b2;
       // level 3 in LDS: bits [9:0] of the keys with bits [30:10] == pre2
 #pragma unroll
       for (int q = 0; q < kPer; ++q)
@@ -929,18 +1320,13 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       __syncthreads();
       fold_masses<kRB3>(sm, e1);
       __syncthreads();
-      if (wave == 0) {
+      {
         uint32_t b3;
         double above, total;
-        stream::mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
-        if (lane == 0) {
-          sm.res[2] = b3;
-          sm.resd[0] = above1 + above2 + (above + sm.md[b3]);
-        }
+        res_find<kRB3>(sm, need - above1 - above2, -1.0, b3, above, total);
+        tau = (pre2 << 10) | b3;
+        zkept = above1 + above2 + (above + sm.md[b3]);
       }
-      __syncthreads();
-      tau = (pre2 << 10) | sm.res[2];
-      zkept = sm.resd[0];
     } else {
       // level 2: values in bin b1, by bits [20:10], copy lane % 4
 #pragma unroll
@@ -961,18 +1347,10 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       passed = 2u;
       load_masses<kRB2>((gptr<uint64_t>)slot->h2, (int)(b1 >> 2), sm);
       __syncthreads();
-      if (wave == 0) {
-        uint32_t b2;
-        double above, total;
-        stream::mass_find<kRB2>(sm.md, need - above1, -1.0, b2, above, total);
-        if (lane == 0) {
-          sm.res[1] = b2;
-          sm.resd[0] = above;
-        }
-      }
-      __syncthreads();
-      const uint32_t pre2 = (b1 << 11) | sm.res[1];
-      const double above2 = sm.resd[0];
+      uint32_t b2;
+      double above2, total2;
+      res_find<kRB2>(sm, need - above1, -1.0, b2, above2, total2);
+      const uint32_t pre2 = (b1 << 11) | b2;
       // level 3: values with bits [30:10] == pre2, by bits [9:0], copy lane % 8
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
@@ -990,18 +1368,13 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       passed = 3u;
       load_masses<kRB3>((gptr<uint64_t>)slot->h3, (int)(b1 >> 2), sm);
       __syncthreads();
-      if (wave == 0) {
+      {
         uint32_t b3;
         double above, total;
-        stream::mass_find<kRB3>(sm.md, need - above1 - above2, -1.0, b3, above, total);
-        if (lane == 0) {
-          sm.res[2] = b3;
-          sm.resd[0] = above1 + above2 + (above + sm.md[b3]);
-        }
+        res_find<kRB3>(sm, need - above1 - above2, -1.0, b3, above, total);
+        tau = (pre2 << 10) | b3;
+        zkept = above1 + above2 + (above + sm.md[b3]);
       }
-      __syncthreads();
-      tau = (pre2 << 10) | sm.res[2];
-      zkept = sm.resd[0];
     }
   } else if (OP == kOpMinP) {
     // the smallest float32 >= min_p * max (an exact double product)
@@ -1009,6 +1382,13 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     float f = (float)thr;
     if ((double)f < thr) f = __uint_as_float(bits_of(f) + 1u);
     tau = max(bits_of(f), 1u);
+  } else if (kPairs) {
+    // both thresholds from one search on (count, mass) pairs (k at most
+    // kResidentSegKeys, checked by the launcher)
+    if (!res_search_kp<NV>(v, vbase, nvec, kk, pc, (gptr<uint64_t>)slot->k1, (gptr<uint64_t>)slot->k2,
+                           (gptr<uint64_t>)slot->k3, ctl, as_global(R.lists), li, s, W, R.spin, passed,
+                           sm, tau, zkept))
+      return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
   } else if (kTopK) {
     // tau_k = the k-th largest pattern (ties kept), by counts; then, for
     // top-k-then-top-p, the top-p threshold inside {x >= tau_k} by masses
@@ -1311,7 +1691,7 @@ template <int KIND, int OP>
 hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const SplitPlan& plan,
                          void* ws, hipStream_t s, const LaunchEvents& ev) {
   // the top-k searches keep more live state: their plans stop at eight loads
-  constexpr bool kTopKOp = OP == kOpTopK || OP == kOpTopKTopP;
+  constexpr bool kTopKOp = OP == kOpTopK || OP == kOpTopKTopP || OP == kOpResPairs;
   switch (plan.nv) {
     case 1: return launch_res_one<KIND, OP, 1>(p, rp, plan, ws, s, ev);
     case 2: return launch_res_one<KIND, OP, 2>(p, rp, plan, ws, s, ev);
@@ -1402,6 +1782,8 @@ hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan
   if (op == kOpNone) e = launch_res_nv<kResSample, kOpNone>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopP) e = launch_res_nv<kResSample, kOpTopP>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopK) e = launch_res_nv<kResSample, kOpTopK>(p, rp, plan, workspace, s, ev);
+  else if (op == kOpTopKTopP && !p.top_k_arr && p.top_k <= kResidentSegKeys)
+    e = launch_res_nv<kResSample, kOpResPairs>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopKTopP) e = launch_res_nv<kResSample, kOpTopKTopP>(p, rp, plan, workspace, s, ev);
   else e = launch_res_nv<kResSample, kOpMinP>(p, rp, plan, workspace, s, ev);
   // a device that cannot hold one group of work-groups at once: streaming engine
