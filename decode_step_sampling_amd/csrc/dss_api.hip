@@ -67,7 +67,8 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
       (top_k > dss::kSplitKCapHost || (int64_t)top_k * plan.W > dss::kSplitScalarKW))
     plan = dss::SplitPlan{0, 0, 0, 0, 0, 0};
   dss::SplitPlan rplan = plan.W > 0 ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
-                                    : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok, true);
+                                    : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok, true,
+                                                         dss::resident_pairs(eop, top_k_arr, top_k));
   // Plain and min-p sampling of a batch the resident engine would take in
   // more than one launch: one work-group per output keeps HBM busier than
   // launches that each wait at row barriers.  Plain sampling reads the row

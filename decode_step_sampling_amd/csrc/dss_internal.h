@@ -165,9 +165,17 @@ constexpr int kSplitChunk = 2048;
 // renormalisation): W work-groups per output on one XCD keep the row in
 // registers and meet at row barriers.  W == 0 means "not eligible".
 // sample: the plan of a sampling call (plain, top-p and min-p may then hold
-// 64 values per thread); renormalisation and the softmax keep at most 48
+// 64 values per thread); renormalisation and the softmax keep at most 48.
+// pairs: top-k then top-p by the one search on (count, mass) pairs
+// (resident_pairs), which may hold 64 values per thread too.
 SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok,
-                        bool sample = false);
+                        bool sample = false, bool pairs = false);
+// Top-k then top-p on the resident engine by the one search on (count,
+// mass) pairs: a scalar k whose values above the top-k boundary bin (fewer
+// than k) fit one key list.
+inline bool resident_pairs(int op, const int32_t* top_k_arr, int top_k) {
+  return op == kOpTopKTopP && top_k_arr == nullptr && top_k <= kResidentSegKeys;
+}
 hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan& plan,
                                   void* workspace, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_resident_renorm(const RenormParams& p, const SplitPlan& plan, void* workspace,

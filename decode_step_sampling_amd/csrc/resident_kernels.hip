@@ -120,6 +120,8 @@ struct ResSmem {
   double fab, ftot, fab2;  // a bin search's result: sums above the bin, total
   uint32_t fbin;
   uint32_t lcnt;  // keys this work-group has put into its list segment
+  uint32_t bcnt;  // keys of one bin gathered from the list into bkeys
+  uint32_t bkeys[kWave];
   int flag;
   // top-k then top-p in one search: masses of the level being searched, and
   // those of levels one and two kept for the top-p cut
@@ -929,12 +931,71 @@ __device__ __forceinline__ void list_level(const uint32_t (&kk)[kListPer], uint3
   __syncthreads();
 }
 
+// The largest list key x with key >> pshift == prefix whose suffix mass
+// (the mass of those keys >= x) is >= need, and that mass, found by one wave
+// when the bin holds at most 64 of the list's keys (the keys share one
+// exponent, so every such sum is exact); when none reaches need (rounding)
+// the bin's smallest key.  False, with nothing found, when the bin holds no
+// key or more than 64.  Every thread calls.
+__device__ __forceinline__ bool bin_brute(const uint32_t (&kk)[kListPer], uint32_t pshift,
+                                          uint32_t prefix, double need, ResSmem& sm, uint32_t& tau,
+                                          double& mass) {
+  const int lane = lane_id(), wave = r_uwave();
+  if (threadIdx.x == 0) sm.bcnt = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kListPer; ++q) {
+    const bool take = kk[q] != kNoBin && (kk[q] >> pshift) == prefix;
+    const uint64_t m = __ballot(take);
+    if (m != 0ull) {
+      const int f = r_first_lane(m);
+      uint32_t base = 0u;
+      if (lane == f) base = atomicAdd(&sm.bcnt, (uint32_t)__popcll(m));
+      base = __builtin_amdgcn_readlane(base, f);
+      const uint32_t pos =
+          base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (take && pos < (uint32_t)kWave) sm.bkeys[pos] = kk[q];
+    }
+  }
+  __syncthreads();
+  const uint32_t n = r_uniform(sm.bcnt);
+  if (n == 0u || n > (uint32_t)kWave) return false;
+  if (wave == 0) {
+    const uint32_t x = (uint32_t)lane < n ? sm.bkeys[lane] : 0u;
+    const double vx = (uint32_t)lane < n ? (double)__uint_as_float(x) : 0.0;
+    double M = 0.0;
+    for (uint32_t u = 0; u < n; ++u) {
+      const uint32_t y = __builtin_amdgcn_readlane(x, (int)u);
+      const double vy = lane_value(vx, (int)u);
+      M += y >= x ? vy : 0.0;
+    }
+    const bool in = (uint32_t)lane < n;
+    const bool cand = in && M >= need;
+    const uint64_t hit = __ballot(cand);
+    // the largest candidate, or the smallest key
+    const uint32_t pickx = hit ? wave_max(cand ? x : 0u) : ~wave_max(in ? ~x : 0u);
+    const int at = r_first_lane(__ballot(in && x == pickx));
+    const double pm = lane_value(M, at);
+    if (lane == 0) {
+      sm.fbin = pickx;
+      sm.fab = pm;
+    }
+  }
+  __syncthreads();
+  tau = r_uniform(sm.fbin);
+  mass = r_uniform(sm.fab);
+  __syncthreads();
+  return true;
+}
+
 // tau = the top-p threshold inside the top-k set: with tau_k the k-th
 // largest pattern (ties kept) and Z_k the mass of {x >= tau_k}, the largest
 // pattern t with mass(x >= t) >= p * Z_k (p >= 1: tau_k itself); kept = the
 // mass of {x >= tau}.  Same results as the count search followed by the
-// mass search with cut = max(tau_k, 1).  Needs k <= kResidentSegKeys.  Every
-// thread calls; false if a row barrier timed out.
+// mass search with cut = max(tau_k, 1).  Needs k <= kResidentSegKeys and the
+// level-1 pairs of every slice in g1 (published before the first row
+// barrier, with sm.lcnt zero).  Every thread calls; false if a row barrier
+// timed out.
 template <int NV>
 __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nvec, int k, float pc,
                                               gptr<uint64_t> g1, gptr<uint64_t> g2, gptr<uint64_t> g3,
@@ -943,30 +1004,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
                                               ResSmem& sm, uint32_t& tau, double& kept) {
   const int tid = threadIdx.x;
   const gptr<uint32_t> seg = seg_base + (size_t)(li * W + s) * kResidentSegKeys;
-  // ---- level 1: every value by bits [30:21] --------------------------------
-  clear_lds_hist(sm);
-  __syncthreads();
-  {
-    HistRun<8> run;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      fence_vec(v[j], run.acc);  // one load at a time (register pressure)
-      const bool in = vbase + j * kWave < nvec;
-      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) run.put(sm, in, min(k4[e] >> 21, (uint32_t)(kRB1 - 1)), pair_of(k4[e]));
-    }
-    run.flush(sm);
-  }
-  __syncthreads();
-  publish_hist<kRB1>(sm, g1);
-  __syncthreads();
-  clear_lds_hist(sm);
-  if (tid == 0) sm.lcnt = 0u;
-  DSS_RSTAMP(4);
-  if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
-  DSS_RSTAMP(5);
-  ++passed;
+  // level 1 (every value by bits [30:21]) went into g1 as the slice landed
   load_pairs<kRB1>(g1, -1, sm, sm.m1);
   __syncthreads();
   uint32_t b1, b2, b3;
@@ -1077,11 +1115,25 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
     } else {  // inside L2 bin p2 > b2: every value there is in the list
       uint32_t kk[kListPer];
       read_list(kk, ctl, seg_base, li, W, sm);
+      uint32_t x;
+      double mx;
+      if (bin_brute(kk, 10u, (b1 << 11) | p2, need - ap1 - ap2, sm, x, mx)) {
+        tau = max(x, tk);
+        kept = ap1 + ap2 + mx;
+        return true;
+      }
       list_level<kRB3, true>(kk, 10u, (b1 << 11) | p2, e1, sm, nullptr);
     }
   } else {  // inside L1 bin p1 > b1: every value there is in the list
     uint32_t kk[kListPer];
     read_list(kk, ctl, seg_base, li, W, sm);
+    uint32_t x;
+    double mx;
+    if (bin_brute(kk, 21u, p1, need - ap1, sm, x, mx)) {
+      tau = max(x, tk);
+      kept = ap1 + mx;
+      return true;
+    }
     list_level<kRB2, true>(kk, 21u, p1, p1 >> 2, sm, nullptr);
     res_find<kRB2>(sm, need - ap1, -1.0, p2, ap2, t);
     list_level<kRB3, true>(kk, 10u, (p1 << 11) | p2, p1 >> 2, sm, nullptr);
@@ -1157,13 +1209,15 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     return;
   }
 
-  if (kTopP) clear_lds_hist(sm);
+  if (kTopP || kPairs) clear_lds_hist(sm);
   __syncthreads();
 
   // as each vector lands: its maximum pattern, and (top-p) its values'
   // significands added into bin bits[30:21] of the LDS histogram, copy
   // lane % 8, so that lanes hitting one bin mostly hit different words
+  // (top-k then top-p by pairs: the values' (count, significand) pairs)
   uint32_t mx = 0u;
+  HistRun<8> lrun;
   auto next = [&](int j) __attribute__((always_inline)) {
     if (j + kInFlight < NV) {
       __builtin_amdgcn_sched_barrier(0);
@@ -1183,8 +1237,14 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
         atomicAdd(&sm.hh[min(k4[e] >> 21, (uint32_t)(kRB1 - 1)) * 8u + (uint32_t)(lane & 7)],
                   (unsigned long long)sig_of(k4[e]));
     }
+    if (kPairs) {
+      const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lrun.put(sm, in, min(k4[e] >> 21, (uint32_t)(kRB1 - 1)), pair_of(k4[e]));
+    }
     next(j);
   }
+  if (kPairs) lrun.flush(sm);
   mx = wave_max(mx);
   if (lane == 0) sm.wmax[wave] = mx;
   __syncthreads();
@@ -1210,13 +1270,15 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   };
   if (OP == kOpNone && KIND == kResSample) publish_chunks();
   if (kTopP) publish_hist<kRB1>(sm, (gptr<uint64_t>)slot->h1);
+  if (kPairs) publish_hist<kRB1>(sm, (gptr<uint64_t>)slot->k1);
 
   uint32_t passed = 0u;
   // a wait that timed out: the output is reported invalid (every slice of
   // it times out too, its counters never reach the target)
-  if (kTopP) {
+  if (kTopP || kPairs) {
     __syncthreads();
     clear_lds_hist(sm);
+    if (tid == 0) sm.lcnt = 0u;
   }
   DSS_RSTAMP(1);
   if (!row_barrier(ctl, (uint32_t)W, R.spin, sm)) return res_invalid<KIND, NV>(P, RP, i, row, 0, vbase, nvec, dst);
@@ -1703,8 +1765,9 @@ hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const Sp
     case 12:
       if constexpr (kTopKOp) return hipErrorInvalidValue;
       else return launch_res_one<KIND, OP, 12>(p, rp, plan, ws, s, ev);
-    case 16:  // plain, top-p and min-p sampling only (plan_resident's wide plans)
-      if constexpr (KIND == kResSample && (OP == kOpNone || OP == kOpMinP || OP == kOpTopP))
+    case 16:  // plain, top-p, min-p and pair-search sampling only (plan_resident's wide plans)
+      if constexpr (KIND == kResSample &&
+                    (OP == kOpNone || OP == kOpMinP || OP == kOpTopP || OP == kOpResPairs))
         return launch_res_one<KIND, OP, 16>(p, rp, plan, ws, s, ev);
       else return hipErrorInvalidValue;
     default:
@@ -1715,7 +1778,7 @@ hipError_t launch_res_nv(const SampleParams& p, const RenormParams& rp, const Sp
 }  // namespace
 
 SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int vec_ok,
-                        bool sample) {
+                        bool sample, bool pairs) {
   SplitPlan plan{0, 0, 0, 0, 0, 0};
   if (op != kOpNone && op != kOpTopP && op != kOpMinP && op != kOpTopK && op != kOpTopKTopP)
     return plan;
@@ -1726,10 +1789,11 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
   const int kMaxSlice = (topk ? 8 : kRMaxNv) * 4 * kBlock;
   int wmin = (vocab + kMaxSlice - 1) / kMaxSlice;
   if (wmin > kRMaxW) return plan;
-  // plain, top-p and min-p sampling keep few other values live and may hold
-  // 64 values per thread: half the slices, so twice the outputs per launch
-  // when a batch needs more than one launch
-  const bool wide = sample && (op == kOpNone || op == kOpMinP || op == kOpTopP);
+  // plain, top-p and min-p sampling, and top-k then top-p by the pair
+  // search, keep few other values live and may hold 64 values per thread:
+  // half the slices, so twice the outputs per launch when a batch needs more
+  // than one launch
+  const bool wide = sample && (op == kOpNone || op == kOpMinP || op == kOpTopP || pairs);
   if (wide) wmin = (vocab + kRWideNv * 4 * kBlock - 1) / (kRWideNv * 4 * kBlock);
   const int wt = (kResidentSlots + num_outputs - 1) / num_outputs;
   // W: a power of two, at least wmin, about 256 work-groups in all, no empty slice
@@ -1743,7 +1807,10 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
   if (W < wmin) return plan;
   int nv = (L / 4 + kBlock - 1) / kBlock;
   nv = nv <= 2 ? nv : nv <= 4 ? 4 : nv <= 8 ? 8 : nv <= 10 ? 10 : nv <= 12 ? 12 : kRWideNv;
-  if (topk && nv > 8) return plan;
+  if (topk && nv > 8) {  // the pair search holds 64 values per thread, the others at most 32
+    if (!wide) return plan;
+    nv = kRWideNv;
+  }
   plan.W = W;
   plan.L = L;
   plan.nv = nv;
@@ -1782,7 +1849,7 @@ hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan
   if (op == kOpNone) e = launch_res_nv<kResSample, kOpNone>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopP) e = launch_res_nv<kResSample, kOpTopP>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopK) e = launch_res_nv<kResSample, kOpTopK>(p, rp, plan, workspace, s, ev);
-  else if (op == kOpTopKTopP && !p.top_k_arr && p.top_k <= kResidentSegKeys)
+  else if (resident_pairs(op, p.top_k_arr, p.top_k))
     e = launch_res_nv<kResSample, kOpResPairs>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopKTopP) e = launch_res_nv<kResSample, kOpTopKTopP>(p, rp, plan, workspace, s, ev);
   else e = launch_res_nv<kResSample, kOpMinP>(p, rp, plan, workspace, s, ev);
