@@ -1071,9 +1071,12 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
         const bool in = vbase + j * kWave < nvec;
         const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 4; ++e)
           run.put(sm, in && (k4[e] >> 10) == pre2, k4[e] & (uint32_t)(kRB3 - 1), pair_of(k4[e]));
-          list_put(in && (k4[e] >> 10) > pre2, k4[e], seg, sm);
+        // one vote per vector: listed values are few
+        if (__ballot(in && (max(max(k4[0], k4[1]), max(k4[2], k4[3])) >> 10) > pre2) != 0ull) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) list_put(in && (k4[e] >> 10) > pre2, k4[e], seg, sm);
         }
       }
       run.flush(sm);
