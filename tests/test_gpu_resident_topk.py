@@ -184,3 +184,92 @@ def test_split_fallback_invalid_rows(op):
     assert list(s[:5]) == [-1] * 5
     want = _table(probs[5], op, 3000, ps[5]).draw(ph.draw_bits53(3, 0, 5, 0))
     assert s[5] == want
+
+
+# ---- the pair search's branches (scalar k <= 8192 on the resident engine) ----
+
+def _branch(row, k, p):
+    """Where the top-p cut of top-k-then-top-p lies relative to the count
+    search's path, from the float32 bit patterns (level 1: bits [30:21],
+    level 2: [20:10]): ("list" if bin b1 and everything above it hold at
+    most 8192 values, else "rows"), ("on", "l1", "l2"), and the number of
+    values in the bin that holds the cut when it is off the path."""
+    keys = row.view(np.uint32)
+    tau_k = np.sort(keys)[::-1][k - 1]
+    valid, tau = ref.threshold(row, "top_k_top_p", k=k, p=np.float32(p))
+    assert valid
+    tp = np.float32(tau).view(np.uint32)
+    b1, p1 = tau_k >> 21, tp >> 21
+    path = "list" if np.sum(keys >> 21 >= b1) <= 8192 else "rows"
+    if p1 != b1:
+        return path, "l1", int(np.sum(keys >> 21 == p1))
+    if (tp >> 10) != (tau_k >> 10):
+        return path, "l2", int(np.sum(keys >> 10 == tp >> 10))
+    return path, "on", 0
+
+
+def _pair_rows(V, rng):
+    """Rows built so that the cut takes each branch; (row, k, p, expected)."""
+    out = []
+
+    def norm(x):
+        x = x / x.sum()
+        return np.ascontiguousarray(x.astype(np.float32))
+
+    # a few / many large values above a long flat tail: the cut lies in a
+    # level-1 bin above the boundary bin (row histograms for the count search)
+    for nbig, big, p in ((20, 1e-2, 0.5), (200, 1e-3, 0.5)):
+        x = (1.0 + rng.uniform(-0.3, 0.3, V)) * 1e-6
+        x[rng.choice(V, nbig, replace=False)] = big * (1 + np.arange(nbig) * 1e-4)
+        out.append((norm(x), 1000, p, ("rows", "l1", nbig)))
+    # 1000 values in one level-1 bin, the top few / many of them in a higher
+    # level-2 bin, and a tail far below: the count search lists bin b1, the
+    # cut is in a level-2 bin above the boundary's
+    for ntop, p in ((30, 0.02), (100, 0.05)):
+        x = rng.uniform(0.5, 1.5, V) * 1e-9
+        pos = rng.choice(V, 1000, replace=False)
+        x[pos[:ntop]] = 1.2 * (1 + np.arange(ntop) * 2.5e-7)
+        x[pos[ntop:]] = 1.1 * (1 + np.arange(1000 - ntop) * 2.5e-7)
+        out.append((norm(x), 1000, p, ("list", "l2", ntop)))
+    # the same over a dense level-1 bin (row histograms), the top values in a
+    # higher level-2 bin
+    for ntop, p in ((30, 0.02), (100, 0.05)):
+        x = 1.0 + rng.uniform(0.0, 0.05, V)
+        x[rng.choice(V, ntop, replace=False)] = 1.2 * (1 + np.arange(ntop) * 2.5e-7)
+        out.append((norm(x), 1000, p, ("rows", "l2", ntop)))
+    # on the path
+    out.append((norm(1.0 + rng.uniform(-1e-3, 1e-3, V)), 1000, 0.9, ("rows", "on", 0)))
+    return out
+
+
+def test_pair_search_branches_token_exact():
+    """Top-k-then-top-p with a scalar k (the one search on (count, mass)
+    pairs): rows whose top-p cut lies on the count search's path, in a
+    level-1 bin above the top-k boundary bin, or in a level-2 bin above it,
+    each with few (at most 64: one wave's exact suffix sums) or many listed
+    keys in that bin, with the count search on row histograms or on the
+    listed keys.  Every draw equals the oracle's CDF draw, over 8 offsets."""
+    rng = np.random.default_rng(77)
+    V = 32768
+    cases = _pair_rows(V, rng)
+    for row, k, p, want in cases:
+        got = _branch(row, k, p)
+        assert got[:2] == want[:2] and (got[2] <= 64) == (want[2] <= 64), (want, got)
+    probs = np.stack([c[0] for c in cases])
+    P = gpu(probs)
+    rows = probs.shape[0]
+    seed = 99
+    tables = [ref.CdfTable(c[0], ref.support_mask(c[0], ref.threshold(c[0], "top_k_top_p", k=c[1],
+                                                                         p=np.float32(c[2]))[1]))
+              for c in cases]
+    ps = np.array([c[2] for c in cases], dtype=np.float32)
+    for offset in range(8):
+        idx = np.arange(rows, dtype=np.int32)
+        s, v, r = dss.top_k_top_p_sampling_from_probs(P, 1000, gpu(ps), indices=gpu(idx), seed=seed,
+                                                      offset=offset, return_valid=True,
+                                                      return_rounds=True)
+        s, v, r = host(s), host(v), host(r)
+        assert (v == 1).all() and (r == 1).all()
+        for i in range(rows):
+            want_tok = tables[i].draw(ph.draw_bits53(seed, offset, i, 0))
+            assert s[i] == want_tok, (cases[i][3], offset, int(s[i]), want_tok)
