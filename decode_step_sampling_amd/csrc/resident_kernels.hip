@@ -30,9 +30,11 @@
 // smallest float >= min_p * max (blog, min-p section), both known without a
 // histogram.  Top-k runs the same three levels on counts (tau_k = the k-th
 // largest pattern, ties kept) and top-k-then-top-p then the mass levels on
-// the values >= tau_k only, so the top-p target is p * Z_k.  Every wave owns
-// a contiguous range of its slice, so the walk visits values in index order:
-// the draw is the inverse transform of the kept set.
+// the values >= tau_k only, so the top-p target is p * Z_k; with a scalar k
+// up to 8192 both thresholds come from one search whose histograms carry
+// (count, mass) pairs (res_search_kp).  Every wave owns a contiguous range
+// of its slice, so the walk visits values in index order: the draw is the
+// inverse transform of the kept set.
 //
 // Work-group b runs on XCD b % 8, so the W work-groups of output li are the
 // blocks with equal b % 8 (as in the split engine), and the row's counters
