@@ -239,6 +239,11 @@ def _pair_rows(V, rng):
         out.append((norm(x), 1000, p, ("rows", "l2", ntop)))
     # on the path
     out.append((norm(1.0 + rng.uniform(-1e-3, 1e-3, V)), 1000, 0.9, ("rows", "on", 0)))
+    # fewer positive values than k: tau_k is the zero pattern, every positive
+    # value is in the top-k set and the cut lies among them
+    x = np.zeros(V)
+    x[rng.choice(V, 500, replace=False)] = rng.uniform(0.5, 1.5, 500)
+    out.append((norm(x), 1000, 0.7, ("rows", "l1", 42)))
     return out
 
 
