@@ -210,10 +210,11 @@ __device__ __forceinline__ bool row_barrier(gptr<uint32_t> ctr, uint32_t target,
 
 // Leave the row after the last read of its slot.  The work-group that
 // leaves last (all W have passed `passed` barriers and then left) clears what
-// the row used (hist_words words of the histograms from h1 on) and finally
-// the arrival counter, so the slot is zero for the next launch.  Every
-// thread must call.
-__device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, int W, int hist_words, ResSmem& sm) {
+// the row used (hist_words words of the histograms from word hist_first of
+// h1 on) and finally the arrival counter, so the slot is zero for the next
+// launch.  Every thread must call.
+__device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, int W, int hist_words, ResSmem& sm,
+                                          int hist_first = 0) {
   __syncthreads();
   const gptr<uint32_t> ctr = (gptr<uint32_t>)slot->ctl;
   if (threadIdx.x == 0) {
@@ -223,7 +224,7 @@ __device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, i
   __syncthreads();
   if (!sm.flag) return;
   const int t = threadIdx.x;
-  const gptr<uint64_t> h = (gptr<uint64_t>)slot->h1;  // h1 .. k3 are contiguous
+  const gptr<uint64_t> h = (gptr<uint64_t>)slot->h1 + hist_first;  // h1 .. k3 are contiguous
   for (int q = t; q < hist_words; q += kBlock) h[q] = 0ull;
   if (t < kRMaxW * kWaves) ((gptr<double>)slot->chunk)[t] = 0.0;
   if (t >= 1 && t < 64) ctr[t] = 0u;
@@ -1158,8 +1159,10 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   constexpr bool kTopP = OP == kOpTopP;  // top-p alone: level-1 masses while the slice lands
   constexpr bool kPairs = OP == kOpResPairs;  // top-k then top-p, one search on pairs
   constexpr bool kTopK = OP == kOpTopK || OP == kOpTopKTopP || kPairs;
-  // histogram words the row's last work-group clears (masses, then counts)
-  constexpr int kHistWords = kTopK ? 2 * kRLevelWords : kTopP ? kRLevelWords : 0;
+  // histogram words the row's last work-group clears (masses, then counts;
+  // the pair search uses the count set only)
+  constexpr int kHistWords = kPairs ? kRLevelWords : kTopK ? 2 * kRLevelWords : kTopP ? kRLevelWords : 0;
+  constexpr int kHistFirst = kPairs ? kRLevelWords : 0;
   const int W = R.W;
   const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
   const int li = (local / W) * 8 + xcd;  // the W slices of an output share b % 8
@@ -1296,7 +1299,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   double zkept = 0.0;
   if (bad) {
     res_invalid<KIND, NV>(P, RP, i, row, s, vbase, nvec, dst);
-    row_leave(slot, passed, W, kHistWords, sm);
+    row_leave(slot, passed, W, kHistWords, sm, kHistFirst);
     return;
   }
 
@@ -1563,7 +1566,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     }
   }
   DSS_RSTAMP(18);
-  row_leave(slot, passed, W, kHistWords, sm);
+  row_leave(slot, passed, W, kHistWords, sm, kHistFirst);
 }
 
 // ---------------------------------------------------------------------------
