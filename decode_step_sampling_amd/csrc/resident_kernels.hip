@@ -123,6 +123,7 @@ struct ResSmem {
   uint32_t fbin;
   uint32_t lcnt;  // keys this work-group has put into its list segment
   uint32_t bcnt;  // keys of one bin gathered from the list into bkeys
+  double udraw;   // the output's uniform draw
   uint32_t bkeys[kWave];
   int flag;
   // top-k then top-p in one search: masses of the level being searched, and
@@ -137,6 +138,15 @@ __device__ __forceinline__ int r_uwave() { return __builtin_amdgcn_readfirstlane
 
 __device__ __forceinline__ uint32_t r_xcc_id() {
   return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID
+}
+
+// threadIdx.x, opaque to the compiler: per-thread LDS addresses derived from
+// it are then formed where they are used instead of being kept in registers
+// through the whole kernel.
+__device__ __forceinline__ int fresh_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
 }
 
 // A work-group-uniform value held in scalar registers.
@@ -239,7 +249,7 @@ __device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, i
 template <int NB>
 __device__ __forceinline__ void publish_hist(const ResSmem& sm, gptr<uint64_t> g) {
   constexpr int C = kRHistWords / NB;
-  for (int b = threadIdx.x; b < NB; b += kBlock) {
+  for (int b = fresh_tid(); b < NB; b += kBlock) {
     uint64_t s = 0ull;
 #pragma unroll
     for (int c = 0; c < C; ++c) s += sm.hh[b * C + c];
@@ -249,7 +259,7 @@ __device__ __forceinline__ void publish_hist(const ResSmem& sm, gptr<uint64_t> g
 
 __device__ __forceinline__ void clear_lds_hist(ResSmem& sm) {
   uint4* h4 = reinterpret_cast<uint4*>(sm.hh);
-  for (int q = threadIdx.x; q < kRHistWords / 2; q += kBlock) h4[q] = make_uint4(0u, 0u, 0u, 0u);
+  for (int q = fresh_tid(); q < kRHistWords / 2; q += kBlock) h4[q] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Adds into the LDS histogram copies (C words per bin, copy lane % C) that
@@ -828,24 +838,34 @@ __device__ __forceinline__ unsigned long long pair_of(uint32_t key) {
   return (1ull << kPairShift) | (unsigned long long)sig_of(key);
 }
 
+// The level masses kept for the top-p cut, chosen at compile time (a fixed
+// LDS offset rather than a pointer held in registers): 0 none / sm.mm,
+// 1 sm.m1, 2 sm.m2.
+template <int A>
+__device__ __forceinline__ double* level_array(ResSmem& sm) {
+  return A == 1 ? sm.m1 : A == 2 ? sm.m2 : sm.mm;
+}
+
+
 // Row histogram g (NB bins of pairs) into sm.md (counts) and sm.mm (masses,
-// exponent < 0: level 1, bin b holds exponent b >> 2); masses also to `save`.
-template <int NB>
-__device__ __forceinline__ void load_pairs(gptr<uint64_t> g, int exponent, ResSmem& sm, double* save) {
-  for (int b = threadIdx.x; b < NB; b += kBlock) {
+// exponent < 0: level 1, bin b holds exponent b >> 2); masses also into
+// level_array<SAVE> (SAVE != 0).
+template <int NB, int SAVE>
+__device__ __forceinline__ void load_pairs(gptr<uint64_t> g, int exponent, ResSmem& sm) {
+  for (int b = fresh_tid(); b < NB; b += kBlock) {
     const uint64_t x = __hip_atomic_load(g + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const double m = bin_mass(x & kSigMask, exponent < 0 ? (uint32_t)b >> 2 : (uint32_t)exponent);
     sm.md[b] = (double)(x >> kPairShift);
     sm.mm[b] = m;
-    if (save) save[b] = m;
+    if (SAVE != 0) level_array<SAVE>(sm)[b] = m;
   }
 }
 
 // The same from the LDS copies; MASS: masses into sm.md only.
-template <int NB, bool MASS>
-__device__ __forceinline__ void fold_pairs(ResSmem& sm, uint32_t exponent, double* save) {
+template <int NB, bool MASS, int SAVE>
+__device__ __forceinline__ void fold_pairs(ResSmem& sm, uint32_t exponent) {
   constexpr int C = kRHistWords / NB;
-  for (int b = threadIdx.x; b < NB; b += kBlock) {
+  for (int b = fresh_tid(); b < NB; b += kBlock) {
     uint64_t x = 0ull;
 #pragma unroll
     for (int c = 0; c < C; ++c) x += sm.hh[b * C + c];
@@ -855,17 +875,17 @@ __device__ __forceinline__ void fold_pairs(ResSmem& sm, uint32_t exponent, doubl
     } else {
       sm.md[b] = (double)(x >> kPairShift);
       sm.mm[b] = m;
-      if (save) save[b] = m;
+      if (SAVE != 0) level_array<SAVE>(sm)[b] = m;
     }
   }
 }
 
 // sm.md = a level's masses as far as they are kept: bins above bk whole,
 // bin bk `kept`, lower bins nothing.
-template <int NB>
-__device__ __forceinline__ void kept_masses(const double* src, uint32_t bk, double kept, ResSmem& sm) {
-  for (int b = threadIdx.x; b < NB; b += kBlock)
-    sm.md[b] = (uint32_t)b > bk ? src[b] : (uint32_t)b == bk ? kept : 0.0;
+template <int NB, int SRC>
+__device__ __forceinline__ void kept_masses(uint32_t bk, double kept, ResSmem& sm) {
+  for (int b = fresh_tid(); b < NB; b += kBlock)
+    sm.md[b] = (uint32_t)b > bk ? level_array<SRC>(sm)[b] : (uint32_t)b == bk ? kept : 0.0;
 }
 
 // Puts `key` into this work-group's list segment when `take` (in any order):
@@ -913,10 +933,9 @@ __device__ __forceinline__ void read_list(uint32_t (&kk)[kListPer], gptr<uint32_
 // One level over the list in LDS: the keys with key >> pshift == prefix, by
 // bits [20:10] (NB = 2048) or [9:0] (NB = 1024), into sm.md / sm.mm (MASS:
 // masses into sm.md).  Every thread calls.
-template <int NB, bool MASS>
+template <int NB, bool MASS, int SAVE>
 __device__ __forceinline__ void list_level(const uint32_t (&kk)[kListPer], uint32_t pshift,
-                                           uint32_t prefix, uint32_t exponent, ResSmem& sm,
-                                           double* save) {
+                                           uint32_t prefix, uint32_t exponent, ResSmem& sm) {
   constexpr int C = kRHistWords / NB;
   constexpr uint32_t bshift = NB == kRB2 ? 10u : 0u;
   clear_lds_hist(sm);
@@ -930,7 +949,7 @@ __device__ __forceinline__ void list_level(const uint32_t (&kk)[kListPer], uint3
     run.flush(sm);
   }
   __syncthreads();
-  fold_pairs<NB, MASS>(sm, exponent, save);
+  fold_pairs<NB, MASS, SAVE>(sm, exponent);
   __syncthreads();
 }
 
@@ -1008,7 +1027,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
   const int tid = threadIdx.x;
   const gptr<uint32_t> seg = seg_base + (size_t)(li * W + s) * kResidentSegKeys;
   // level 1 (every value by bits [30:21]) went into g1 as the slice landed
-  load_pairs<kRB1>(g1, -1, sm, sm.m1);
+  load_pairs<kRB1, 1>(g1, -1, sm);
   __syncthreads();
   uint32_t b1, b2, b3;
   double cab1, cab2, cab3, mab1, mab2, mab3, tot;
@@ -1033,10 +1052,10 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
     ++passed;
     uint32_t kk[kListPer];
     read_list(kk, ctl, seg_base, li, W, sm);
-    list_level<kRB2, false>(kk, 21u, b1, e1, sm, sm.m2);
+    list_level<kRB2, false, 2>(kk, 21u, b1, e1, sm);
     res_find<kRB2, true>(sm, (double)k - cab1, -1.0, b2, cab2, tot, &mab2);
     pre2 = (b1 << 11) | b2;
-    list_level<kRB3, false>(kk, 10u, pre2, e1, sm, nullptr);
+    list_level<kRB3, false, 0>(kk, 10u, pre2, e1, sm);
   } else {
     // level 2: values in bin b1 by bits [20:10]
     {
@@ -1060,7 +1079,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
     DSS_RSTAMP(7);
     ++passed;
-    load_pairs<kRB2>(g2, (int)e1, sm, sm.m2);
+    load_pairs<kRB2, 2>(g2, (int)e1, sm);
     __syncthreads();
     res_find<kRB2, true>(sm, (double)k - cab1, -1.0, b2, cab2, tot, &mab2);
     pre2 = (b1 << 11) | b2;
@@ -1091,7 +1110,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
     DSS_RSTAMP(9);
     ++passed;
-    load_pairs<kRB3>(g3, (int)e1, sm, nullptr);
+    load_pairs<kRB3, 0>(g3, (int)e1, sm);
     __syncthreads();
   }
   res_find<kRB3, true>(sm, (double)k - cab1 - cab2, -1.0, b3, cab3, tot, &mab3);
@@ -1108,15 +1127,15 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
   const double need = (double)pc * zk;
   double ap1, ap2, ap3, t;
   uint32_t p1, p2, p3;
-  kept_masses<kRB1>(sm.m1, b1, mab2 + m3, sm);
+  kept_masses<kRB1, 1>(b1, mab2 + m3, sm);
   __syncthreads();
   res_find<kRB1>(sm, need, -1.0, p1, ap1, t);
   if (p1 == b1) {
-    kept_masses<kRB2>(sm.m2, b2, m3, sm);
+    kept_masses<kRB2, 2>(b2, m3, sm);
     __syncthreads();
     res_find<kRB2>(sm, need - ap1, -1.0, p2, ap2, t);
     if (p2 == b2) {
-      kept_masses<kRB3>(sm.mm, b3, sm.mm[b3], sm);
+      kept_masses<kRB3, 0>(b3, sm.mm[b3], sm);
       __syncthreads();
     } else {  // inside L2 bin p2 > b2: every value there is in the list
       uint32_t kk[kListPer];
@@ -1128,7 +1147,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
         kept = ap1 + ap2 + mx;
         return true;
       }
-      list_level<kRB3, true>(kk, 10u, (b1 << 11) | p2, e1, sm, nullptr);
+      list_level<kRB3, true, 0>(kk, 10u, (b1 << 11) | p2, e1, sm);
     }
   } else {  // inside L1 bin p1 > b1: every value there is in the list
     uint32_t kk[kListPer];
@@ -1140,9 +1159,9 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
       kept = ap1 + mx;
       return true;
     }
-    list_level<kRB2, true>(kk, 21u, p1, p1 >> 2, sm, nullptr);
+    list_level<kRB2, true, 0>(kk, 21u, p1, p1 >> 2, sm);
     res_find<kRB2>(sm, need - ap1, -1.0, p2, ap2, t);
-    list_level<kRB3, true>(kk, 10u, (p1 << 11) | p2, p1 >> 2, sm, nullptr);
+    list_level<kRB3, true, 0>(kk, 10u, (p1 << 11) | p2, p1 >> 2, sm);
   }
   res_find<kRB3>(sm, need - ap1 - ap2, -1.0, p3, ap3, t);
   tau = max((((p1 << 11) | p2) << 10) | p3, tk);
@@ -1205,8 +1224,11 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   const uint64_t sid = (KIND == kResSample && P.seed_arr) ? 0ull : (uint64_t)i;
   const float pc = stream::clamp01(prm);
   // the output's draw, while the slice is in flight (only thread 0 uses it)
-  double u = 0.0;
-  if (KIND == kResSample && wave == 0) u = draw_uniform(seed, offset, sid, 0u);
+  // (kept in LDS until the draw rather than in registers through the searches)
+  if (KIND == kResSample && wave == 0) {
+    const double u = draw_uniform(seed, offset, sid, 0u);
+    if (lane == 0) sm.udraw = u;
+  }
 
   const gptr<r_v4f> dst = KIND == kResRenorm
                               ? (gptr<r_v4f>)as_global(RP.out + (int64_t)row * V + s0)
@@ -1519,7 +1541,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       ls += cmq[q];
     }
     const double incl = wave_incl_scan(ls);
-    const double T = u * lane63(incl);
+    const double T = sm.udraw * lane63(incl);
     const uint64_t hit = __ballot(ls > 0.0 && incl > T);
     const bool fallback = hit == 0ull;
     const int L = fallback ? r_last_lane(__ballot(ls > 0.0) | 1ull) : r_first_lane(hit);
