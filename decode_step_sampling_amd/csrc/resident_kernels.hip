@@ -837,6 +837,11 @@ constexpr int kListPer = kResidentSegKeys / kBlock;  // list keys per thread aft
 __device__ __forceinline__ unsigned long long pair_of(uint32_t key) {
   return (1ull << kPairShift) | (unsigned long long)sig_of(key);
 }
+// The same for a key inside a level-1 bin, whose values share one exponent:
+// hb is the bin's hidden bit (0x800000, or 0 for the subnormal bins).
+__device__ __forceinline__ unsigned long long pair_in(uint32_t key, uint32_t hb) {
+  return (1ull << kPairShift) | (unsigned long long)((key & 0x7FFFFFu) | hb);
+}
 
 // The level masses kept for the top-p cut, chosen at compile time (a fixed
 // LDS offset rather than a pointer held in registers): 0 none / sm.mm,
@@ -1033,6 +1038,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
   double cab1, cab2, cab3, mab1, mab2, mab3, tot;
   res_find<kRB1, true>(sm, (double)k, -1.0, b1, cab1, tot, &mab1);
   const uint32_t e1 = b1 >> 2;
+  const uint32_t hb1 = e1 >= 1u ? 0x800000u : 0u;  // hidden bit of bin b1's values
   // bin b1 and everything above it fit one list: gather them all now
   const bool use_list = cab1 + sm.md[b1] <= (double)kResidentSegKeys;
   uint32_t pre2;
@@ -1067,7 +1073,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
         const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          run.put(sm, in && (k4[e] >> 21) == b1, (k4[e] >> 10) & (uint32_t)(kRB2 - 1), pair_of(k4[e]));
+          run.put(sm, in && (k4[e] >> 21) == b1, (k4[e] >> 10) & (uint32_t)(kRB2 - 1), pair_in(k4[e], hb1));
       }
       run.flush(sm);
     }
@@ -1094,7 +1100,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
         const uint32_t k4[4] = {bits_of(v[j].x), bits_of(v[j].y), bits_of(v[j].z), bits_of(v[j].w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          run.put(sm, in && (k4[e] >> 10) == pre2, k4[e] & (uint32_t)(kRB3 - 1), pair_of(k4[e]));
+          run.put(sm, in && (k4[e] >> 10) == pre2, k4[e] & (uint32_t)(kRB3 - 1), pair_in(k4[e], hb1));
         // one vote per vector: listed values are few
         if (__ballot(in && (max(max(k4[0], k4[1]), max(k4[2], k4[3])) >> 10) > pre2) != 0ull) {
 #pragma unroll
