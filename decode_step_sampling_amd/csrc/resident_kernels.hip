@@ -246,10 +246,10 @@ __device__ __forceinline__ void row_leave(gptr<RowSlot> slot, uint32_t passed, i
 
 // Sum the LDS histogram copies of every bin and add the non-zero sums into
 // the row's global histogram g (NB bins, kRHistWords / NB copies per bin).
-template <int NB>
+template <int NB, bool OPAQUE = false>
 __device__ __forceinline__ void publish_hist(const ResSmem& sm, gptr<uint64_t> g) {
   constexpr int C = kRHistWords / NB;
-  for (int b = fresh_tid(); b < NB; b += kBlock) {
+  for (int b = OPAQUE ? fresh_tid() : (int)threadIdx.x; b < NB; b += kBlock) {
     uint64_t s = 0ull;
 #pragma unroll
     for (int c = 0; c < C; ++c) s += sm.hh[b * C + c];
@@ -257,9 +257,13 @@ __device__ __forceinline__ void publish_hist(const ResSmem& sm, gptr<uint64_t> g
   }
 }
 
+// (OPAQUE: the thread index through fresh_tid, for the kernels that would
+// otherwise keep the derived addresses in registers throughout)
+template <bool OPAQUE = false>
 __device__ __forceinline__ void clear_lds_hist(ResSmem& sm) {
   uint4* h4 = reinterpret_cast<uint4*>(sm.hh);
-  for (int q = fresh_tid(); q < kRHistWords / 2; q += kBlock) h4[q] = make_uint4(0u, 0u, 0u, 0u);
+  for (int q = OPAQUE ? fresh_tid() : (int)threadIdx.x; q < kRHistWords / 2; q += kBlock)
+    h4[q] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Adds into the LDS histogram copies (C words per bin, copy lane % C) that
@@ -368,6 +372,28 @@ __device__ __forceinline__ void res_find(ResSmem& sm, double need, double pfrac,
   above = r_uniform(sm.fab);
   total = r_uniform(sm.ftot);
   if (TWO) *above2 = r_uniform(sm.fab2);
+}
+
+// The same search by one wave (stream::mass_find; the other waves wait at
+// the barrier): cheaper where the search is not on the critical path of
+// many waves' work, as in top-p alone.
+template <int NB>
+__device__ __forceinline__ void res_find_w0(ResSmem& sm, double need, double pfrac, uint32_t& bin,
+                                            double& above, double& total) {
+  if (r_uwave() == 0) {
+    uint32_t b;
+    double a, t;
+    stream::mass_find<NB>(sm.md, need, pfrac, b, a, t);
+    if (lane_id() == 0) {
+      sm.fbin = b;
+      sm.fab = a;
+      sm.ftot = t;
+    }
+  }
+  __syncthreads();
+  bin = r_uniform(sm.fbin);
+  above = r_uniform(sm.fab);
+  total = r_uniform(sm.ftot);
 }
 
 // Load the row's histogram g (NB bins) as masses into sm.md; `exponent` < 0:
@@ -943,7 +969,7 @@ __device__ __forceinline__ void list_level(const uint32_t (&kk)[kListPer], uint3
                                            uint32_t prefix, uint32_t exponent, ResSmem& sm) {
   constexpr int C = kRHistWords / NB;
   constexpr uint32_t bshift = NB == kRB2 ? 10u : 0u;
-  clear_lds_hist(sm);
+  clear_lds_hist<true>(sm);
   __syncthreads();
   {
     HistRun<C> run;
@@ -1078,9 +1104,9 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
       run.flush(sm);
     }
     __syncthreads();
-    publish_hist<kRB2>(sm, g2);
+    publish_hist<kRB2, true>(sm, g2);
     __syncthreads();
-    clear_lds_hist(sm);
+    clear_lds_hist<true>(sm);
     DSS_RSTAMP(6);
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
     DSS_RSTAMP(7);
@@ -1110,7 +1136,7 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
       run.flush(sm);
     }
     __syncthreads();
-    publish_hist<kRB3>(sm, g3);
+    publish_hist<kRB3, true>(sm, g3);
     if (tid == 0) __hip_atomic_store(ctl + 8 + s, sm.lcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     DSS_RSTAMP(8);
     if (!row_barrier(ctl, (passed + 1u) * (uint32_t)W, spin, sm)) return false;
@@ -1245,7 +1271,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     return;
   }
 
-  if (kTopP || kPairs) clear_lds_hist(sm);
+  if (kTopP || kPairs) clear_lds_hist<kPairs>(sm);
   __syncthreads();
 
   // as each vector lands: its maximum pattern, and (top-p) its values'
@@ -1306,14 +1332,14 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
   };
   if (OP == kOpNone && KIND == kResSample) publish_chunks();
   if (kTopP) publish_hist<kRB1>(sm, (gptr<uint64_t>)slot->h1);
-  if (kPairs) publish_hist<kRB1>(sm, (gptr<uint64_t>)slot->k1);
+  if (kPairs) publish_hist<kRB1, true>(sm, (gptr<uint64_t>)slot->k1);
 
   uint32_t passed = 0u;
   // a wait that timed out: the output is reported invalid (every slice of
   // it times out too, its counters never reach the target)
   if (kTopP || kPairs) {
     __syncthreads();
-    clear_lds_hist(sm);
+    clear_lds_hist<kPairs>(sm);
     if (tid == 0) sm.lcnt = 0u;
   }
   DSS_RSTAMP(1);
@@ -1337,7 +1363,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
     __syncthreads();
     uint32_t b1;
     double above1, ztot;
-    res_find<kRB1>(sm, 0.0, (double)pc, b1, above1, ztot);
+    res_find_w0<kRB1>(sm, 0.0, (double)pc, b1, above1, ztot);
     const double need = (double)pc * ztot;
     const uint32_t e1 = b1 >> 2;
     // the row's values in bin b1 number at most its significand sum / 2^23
@@ -1407,7 +1433,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       clear_lds_hist(sm);
       uint32_t b2;
       double above2, total2;
-      res_find<kRB2>(sm, need - above1, -1.0, b2, above2, total2);
+      res_find_w0<kRB2>(sm, need - above1, -1.0, b2, above2, total2);
       const uint32_t pre2 = (b1 << 11) | b2;
       // level 3 in LDS: bits [9:0] of the keys with bits [30:10] == pre2
 #pragma unroll
@@ -1421,7 +1447,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       {
         uint32_t b3;
         double above, total;
-        res_find<kRB3>(sm, need - above1 - above2, -1.0, b3, above, total);
+        res_find_w0<kRB3>(sm, need - above1 - above2, -1.0, b3, above, total);
         tau = (pre2 << 10) | b3;
         zkept = above1 + above2 + (above + sm.md[b3]);
       }
@@ -1447,7 +1473,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       __syncthreads();
       uint32_t b2;
       double above2, total2;
-      res_find<kRB2>(sm, need - above1, -1.0, b2, above2, total2);
+      res_find_w0<kRB2>(sm, need - above1, -1.0, b2, above2, total2);
       const uint32_t pre2 = (b1 << 11) | b2;
       // level 3: values with bits [30:10] == pre2, by bits [9:0], copy lane % 8
 #pragma unroll
@@ -1469,7 +1495,7 @@ __global__ __launch_bounds__(kBlock) void resident_kernel(SampleParams P, Renorm
       {
         uint32_t b3;
         double above, total;
-        res_find<kRB3>(sm, need - above1 - above2, -1.0, b3, above, total);
+        res_find_w0<kRB3>(sm, need - above1 - above2, -1.0, b3, above, total);
         tau = (pre2 << 10) | b3;
         zkept = above1 + above2 + (above + sm.md[b3]);
       }
