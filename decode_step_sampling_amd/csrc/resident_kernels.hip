@@ -1159,13 +1159,25 @@ __device__ __forceinline__ bool res_search_kp(float4 (&v)[NV], int vbase, int nv
   const double need = (double)pc * zk;
   double ap1, ap2, ap3, t;
   uint32_t p1, p2, p3;
-  kept_masses<kRB1, 1>(b1, mab2 + m3, sm);
-  __syncthreads();
-  res_find<kRB1>(sm, need, -1.0, p1, ap1, t);
-  if (p1 == b1) {
-    kept_masses<kRB2, 2>(b2, m3, sm);
+  // on the path at a level when the mass above the path bin stays below the
+  // target (a comparison; the bin search runs only otherwise)
+  if (mab1 < need) {
+    p1 = b1;
+    ap1 = mab1;
+  } else {
+    kept_masses<kRB1, 1>(b1, mab2 + m3, sm);
     __syncthreads();
-    res_find<kRB2>(sm, need - ap1, -1.0, p2, ap2, t);
+    res_find<kRB1>(sm, need, -1.0, p1, ap1, t);
+  }
+  if (p1 == b1) {
+    if (ap1 + mab2 < need) {
+      p2 = b2;
+      ap2 = mab2;
+    } else {
+      kept_masses<kRB2, 2>(b2, m3, sm);
+      __syncthreads();
+      res_find<kRB2>(sm, need - ap1, -1.0, p2, ap2, t);
+    }
     if (p2 == b2) {
       kept_masses<kRB3, 0>(b3, sm.mm[b3], sm);
       __syncthreads();
