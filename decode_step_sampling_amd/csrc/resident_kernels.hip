@@ -854,8 +854,11 @@ __device__ __forceinline__ bool res_search(float4 (&v)[NV], int vbase, int nvec,
 // or, where it leaves that path, inside a bin that lies wholly above the
 // top-k boundary bin.  Fewer than k values lie above that boundary, and the
 // last round of the count search also puts them into a key list, so the
-// cut is finished in LDS without another row barrier.  Three row barriers
-// for both thresholds instead of up to six.
+// cut is finished in LDS without another row barrier.  Whether the cut
+// stays on the path at a level is a comparison of the mass above the path
+// bin with p * Z_k; the bin searches run only where it leaves.  Three row
+// barriers for both thresholds (the first one also level 1's, filled as the
+// slice lands) instead of up to seven.
 constexpr int kPairShift = 44;
 constexpr uint64_t kSigMask = (1ull << kPairShift) - 1ull;
 constexpr int kListPer = kResidentSegKeys / kBlock;  // list keys per thread after a gather
