@@ -68,7 +68,7 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
     plan = dss::SplitPlan{0, 0, 0, 0, 0, 0};
   dss::SplitPlan rplan = plan.W > 0 ? dss::SplitPlan{0, 0, 0, 0, 0, 0}
                                     : dss::plan_resident(eop, vocab, num_outputs, flags, vec_ok, true,
-                                                         dss::resident_pairs(eop, top_k_arr, top_k));
+                                                         dss::resident_pairs(eop, top_k_arr, top_k, vocab));
   // Plain and min-p sampling of a batch the resident engine would take in
   // more than one launch: one work-group per output keeps HBM busier than
   // launches that each wait at row barriers.  Plain sampling reads the row
@@ -83,6 +83,9 @@ int sample_common(int op, const float* probs, int32_t rows, int32_t vocab, const
   if (wide_stream) rplan = dss::SplitPlan{0, 0, 0, 0, 0, 0};
   const size_t need = dss_workspace_size(op, rows, vocab, num_outputs, flags);
   if (workspace_bytes < need || (need > 0 && !workspace)) return DSS_ERR_WORKSPACE;
+  // and whatever the chosen plan itself uses (never past the caller's buffer)
+  const size_t used = plan.W > 0 ? plan.workspace : rplan.W > 0 ? rplan.workspace : 0;
+  if (workspace_bytes < used || (used > 0 && !workspace)) return DSS_ERR_WORKSPACE;
   if (check_only) return DSS_OK;
   const int dev = check_device();
   if (dev != DSS_OK) return dev;
@@ -501,7 +504,14 @@ DSS_EXPORT size_t dss_workspace_size(int32_t op, int32_t rows, int32_t vocab,
   if (op < DSS_OP_SAMPLING || op > DSS_OP_TOP_K_TOP_P || num_outputs <= 0) return 0;
   // top-k ops may run on either engine (the choice can depend on k)
   const dss::SplitPlan plan = dss::plan_split(op, rows, vocab, num_outputs, flags, vec);
-  const size_t res = dss::plan_resident(op, vocab, num_outputs, flags, vec).workspace;
+  size_t res = dss::plan_resident(op, vocab, num_outputs, flags, vec).workspace;
+  // top-k then top-p with a scalar k may take the pair search's plans, which
+  // reach larger vocabularies
+  if (op == DSS_OP_TOP_K_TOP_P) {
+    const size_t rp =
+        dss::plan_resident(dss::kOpTopKTopP, vocab, num_outputs, flags, vec, true, true).workspace;
+    res = rp > res ? rp : res;
+  }
   return plan.W > 0 && plan.workspace > res ? plan.workspace : res;
 }
 

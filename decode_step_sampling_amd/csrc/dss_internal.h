@@ -172,9 +172,10 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
                         bool sample = false, bool pairs = false);
 // Top-k then top-p on the resident engine by the one search on (count,
 // mass) pairs: a scalar k whose values above the top-k boundary bin (fewer
-// than k) fit one key list.
-inline bool resident_pairs(int op, const int32_t* top_k_arr, int top_k) {
-  return op == kOpTopKTopP && top_k_arr == nullptr && top_k <= kResidentSegKeys;
+// than k) fit one key list, and a row of fewer than 2^20 values (a bin's
+// count fills 20 bits of the packed pair).
+inline bool resident_pairs(int op, const int32_t* top_k_arr, int top_k, int vocab) {
+  return op == kOpTopKTopP && top_k_arr == nullptr && top_k <= kResidentSegKeys && vocab < (1 << 20);
 }
 hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan& plan,
                                   void* workspace, hipStream_t s, const LaunchEvents& ev);

@@ -1865,7 +1865,10 @@ SplitPlan plan_resident(int op, int vocab, int num_outputs, uint32_t flags, int 
   const bool topk = op == kOpTopK || op == kOpTopKTopP;
   const int kMaxSlice = (topk ? 8 : kRMaxNv) * 4 * kBlock;
   int wmin = (vocab + kMaxSlice - 1) / kMaxSlice;
-  if (wmin > kRMaxW) return plan;
+  // (the pair search may hold 64 values per thread, so rows up to sixteen
+  // such slices stay resident)
+  constexpr int kWideSlice = kRWideNv * 4 * kBlock;
+  if ((pairs ? (vocab + kWideSlice - 1) / kWideSlice : wmin) > kRMaxW) return plan;
   // plain, top-p and min-p sampling, and top-k then top-p by the pair
   // search, keep few other values live and may hold 64 values per thread:
   // half the slices, so twice the outputs per launch when a batch needs more
@@ -1926,7 +1929,7 @@ hipError_t launch_resident_sample(int op, const SampleParams& p, const SplitPlan
   if (op == kOpNone) e = launch_res_nv<kResSample, kOpNone>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopP) e = launch_res_nv<kResSample, kOpTopP>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopK) e = launch_res_nv<kResSample, kOpTopK>(p, rp, plan, workspace, s, ev);
-  else if (resident_pairs(op, p.top_k_arr, p.top_k))
+  else if (resident_pairs(op, p.top_k_arr, p.top_k, p.vocab))
     e = launch_res_nv<kResSample, kOpResPairs>(p, rp, plan, workspace, s, ev);
   else if (op == kOpTopKTopP) e = launch_res_nv<kResSample, kOpTopKTopP>(p, rp, plan, workspace, s, ev);
   else e = launch_res_nv<kResSample, kOpMinP>(p, rp, plan, workspace, s, ev);

@@ -287,3 +287,24 @@ def test_chain_speculative_validation():
     # n = 0 needs no draft arrays
     assert call(q=NULL, ids=NULL, n=0, rows=64, vocab=151936, ws=FAKE,
                 ws_bytes=need) != _lib.DSS_ERR_INVALID_ARG
+
+
+def test_workspace_covers_the_pair_search_plans():
+    """Top-k then top-p with a scalar k may run the resident pair search,
+    whose plans reach vocabularies the other resident plans do not (up to
+    sixteen slices of 64 values per thread): the workspace size must cover
+    its fixed region there, and a call whose buffer is smaller than the plan
+    it would launch is refused before any HIP call."""
+    lib = _lib.load()
+    for vocab in (528384, 985600, 2**20 - 4):
+        size = lib.dss_workspace_size(4, 2, vocab, 2, 0)
+        assert size >= FIXED_REGION_BYTES, (vocab, size)
+        r = lib.dss_top_k_top_p_sampling_from_probs(FAKE, 2, vocab, NULL, 2, NULL, 1, NULL, 0,
+                                                    NULL, 1000, NULL, 0.9, FAKE, NULL, NULL, 0,
+                                                    FAKE, size - 1, NULL)
+        assert r == _lib.DSS_ERR_WORKSPACE, (vocab, r)
+        # no workspace at all (a size query of 0 once left callers passing none)
+        r = lib.dss_top_k_top_p_sampling_from_probs(FAKE, 2, vocab, NULL, 2, NULL, 1, NULL, 0,
+                                                    NULL, 1000, NULL, 0.9, FAKE, NULL, NULL, 0,
+                                                    NULL, 0, NULL)
+        assert r == _lib.DSS_ERR_WORKSPACE, (vocab, r)

@@ -278,3 +278,28 @@ def test_pair_search_branches_token_exact():
         for i in range(rows):
             want_tok = tables[i].draw(ph.draw_bits53(seed, offset, i, 0))
             assert s[i] == want_tok, (cases[i][3], offset, int(s[i]), want_tok)
+
+
+def test_largest_vocab():
+    """V = 2^20 - 4 (the pair search's largest rows: sixteen slices of 64
+    values per thread) is token-exact against the oracle's CDF draw on a
+    near-uniform and a softmax row; at V = 2^20 (DSS_MAX_VOCAB) a bin of a
+    near-uniform row would hold 2^20 values, more than a packed pair counts,
+    so such calls take another engine: every token there lies in the kept
+    set."""
+    rng = np.random.default_rng(1234)
+    for V, exact in ((2**20 - 4, True), (2**20, False)):
+        probs = np.stack([_rows("flat", 1, V, rng)[0], si.softmax_rows(rng, 1, V, 2.0)[0]])
+        P = gpu(probs)
+        k, p, seed = 1000, np.float32(0.9), 5
+        tables = [_table(probs[i], "top_k_top_p", k, p) for i in range(2)]
+        for offset in range(4):
+            s, v = dss.top_k_top_p_sampling_from_probs(P, k, p, seed=seed, offset=offset,
+                                                       return_valid=True)
+            s, v = host(s), host(v)
+            assert (v == 1).all()
+            for i in range(2):
+                _, tau = ref.threshold(probs[i], "top_k_top_p", k=k, p=p)
+                assert ref.support_mask(probs[i], tau)[s[i]], (V, i, offset)
+                if exact:
+                    assert s[i] == tables[i].draw(ph.draw_bits53(seed, offset, i, 0)), (V, i, offset)
