@@ -308,3 +308,36 @@ def test_workspace_covers_the_pair_search_plans():
                                                     NULL, 1000, NULL, 0.9, FAKE, NULL, NULL, 0,
                                                     NULL, 0, NULL)
         assert r == _lib.DSS_ERR_WORKSPACE, (vocab, r)
+
+
+def test_queried_workspace_always_suffices():
+    """A sampling call given exactly dss_workspace_size bytes is never refused
+    for its workspace, whatever engine and plan it would take (the call then
+    stops at the device check on a machine without a GPU)."""
+    import itertools
+    lib = _lib.load()
+
+    def call(op, rows, vocab, n, k, karr, flags, ws, wsb):
+        head = (FAKE, rows, vocab, FAKE if n != rows else NULL, n, NULL, 1, NULL, 0)
+        tail = (FAKE, NULL, NULL, flags, ws, wsb, NULL)
+        if op == 0:
+            return lib.dss_sampling_from_probs(*head, *tail)
+        if op == 1:
+            return lib.dss_top_k_sampling_from_probs(*head, karr, k, *tail)
+        if op == 2:
+            return lib.dss_top_p_sampling_from_probs(*head, NULL, 0.9, *tail)
+        if op == 3:
+            return lib.dss_min_p_sampling_from_probs(*head, NULL, 0.1, *tail)
+        return lib.dss_top_k_top_p_sampling_from_probs(*head, karr, k, NULL, 0.9, *tail)
+
+    shapes = itertools.product((1, 2, 4, 64, 300, 512),
+                               (1024, 32000, 50257, 151936, 256000, 528384, 2**20 - 4, 2**20))
+    for rows, vocab in shapes:
+        for op in range(5):
+            ks = ((50, NULL), (1000, NULL), (3000, NULL), (9000, NULL), (0, FAKE)) if op in (1, 4) \
+                else ((50, NULL),)
+            for n, (k, karr), flags in itertools.product((rows, 2 * rows), ks,
+                                                         (0, _lib.DSS_FLAG_STREAMING)):
+                need = lib.dss_workspace_size(op, rows, vocab, n, flags)
+                r = call(op, rows, vocab, n, k, karr, flags, FAKE if need else NULL, need)
+                assert r != _lib.DSS_ERR_WORKSPACE, (op, rows, vocab, n, k, karr is not NULL, flags)
