@@ -89,9 +89,10 @@ def test_extremes_and_invalid():
 def test_stress_rows_full_size():
     """The stress workload's near-uniform, peaked and geometric rows at
     B=512, V=256000, p=0.95, with the workload's k=1000 (k * W = 8000) and
-    with k=2500 (above the split cap), both on the resident engine: one
-    draw per row against the oracle's CDF draw, and every draw inside the
-    kept set."""
+    with k=2500 (above the split cap), both on the resident engine (the one
+    search on (count, mass) pairs, four slices of 64 values per thread,
+    eight launches): one draw per row against the oracle's CDF draw, every
+    16th row of each call."""
     w = si.stress()
     probs = w["probs"]
     seeds = w["seeds"]
@@ -110,8 +111,10 @@ def test_stress_rows_full_size():
     s, v = host(s), host(v)
     assert (v == 1).all()
     for row in range(3, probs.shape[0], 16):
-        _, tau = ref.threshold(probs[row], "top_k_top_p", k=1000, p=np.float32(0.95))
-        assert ref.support_mask(probs[row], tau)[s[row]], (row, int(w["groups"][row]))
+        want = ref.sample_by_cdf(probs[row], "top_k_top_p",
+                                 ph.draw_bits53(int(seeds[row]), 6, 0, 0), k=1000,
+                                 p=np.float32(0.95))
+        assert s[row] == want, (row, int(w["groups"][row]))
 
 
 @pytest.mark.parametrize("n_out", [8, 72])
