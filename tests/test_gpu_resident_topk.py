@@ -234,6 +234,15 @@ def _pair_rows(V, rng):
         x[pos[:ntop]] = 1.2 * (1 + np.arange(ntop) * 2.5e-7)
         x[pos[ntop:]] = 1.1 * (1 + np.arange(1000 - ntop) * 2.5e-7)
         out.append((norm(x), 1000, p, ("list", "l2", ntop)))
+    # a few / many large values above 2000 medium ones and a tail far below:
+    # the count search lists bin b1 and everything above it, the cut lies in
+    # a level-1 bin above the boundary's
+    for nbig, big, p in ((20, 1e-2, 0.5), (200, 1e-3, 0.5)):
+        x = rng.uniform(0.5, 1.5, V) * 1e-9
+        pos = rng.choice(V, nbig + 2000, replace=False)
+        x[pos[:nbig]] = big * (1 + np.arange(nbig) * 1e-4)
+        x[pos[nbig:]] = 1e-4 * (1 + np.arange(2000) * 1e-5)
+        out.append((norm(x), 1000, p, ("list", "l1", nbig)))
     # the same over a dense level-1 bin (row histograms), the top values in a
     # higher level-2 bin
     for ntop, p in ((30, 0.02), (100, 0.05)):
@@ -246,7 +255,7 @@ def _pair_rows(V, rng):
     # value is in the top-k set and the cut lies among them
     x = np.zeros(V)
     x[rng.choice(V, 500, replace=False)] = rng.uniform(0.5, 1.5, 500)
-    out.append((norm(x), 1000, 0.7, ("rows", "l1", 42)))
+    out.append((norm(x), 1000, 0.7, ("rows", "l1", 50)))
     return out
 
 
@@ -257,7 +266,7 @@ def test_pair_search_branches_token_exact():
     each with few (at most 64: one wave's exact suffix sums) or many listed
     keys in that bin, with the count search on row histograms or on the
     listed keys.  Every draw equals the oracle's CDF draw, over 8 offsets."""
-    rng = np.random.default_rng(77)
+    rng = np.random.default_rng(79)  # a seed whose rows each take the intended branch
     V = 32768
     cases = _pair_rows(V, rng)
     for row, k, p, want in cases:
